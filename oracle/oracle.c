@@ -1,0 +1,153 @@
+/*
+ * oracle.c -- fp64 CPU reference of the selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test-suite, the smoke check and the CPU baseline
+ * leg of the benchmark use it.  It shares no code, header, table or constant
+ * with the HIP library.
+ *
+ * What it computes (plain definition, no blocking, no reordering):
+ *
+ *   Page "SAMBA混合注意力状态空间模型" (metaphor-xennon.pages.dev), section
+ *   数学框架 -> Mamba层: the state update h_t = Ā_t h_{t-1} + B̄_t x_t and the
+ *   readout y_t = C_t h_t (the readout uses the state *after* the update of the
+ *   same step), with B_t, C_t and Δ_t selected from the input (the selection
+ *   equations below them).  The same page, section 实现细节 -> 模型配置, gives
+ *   an SSM state size of 16; this file accepts any size >= 1.
+ *
+ *   The pages never define Ā_t, B̄_t or the map τ_Δ, nor a skip or gate; the
+ *   paper's own Mamba subsection (hackernoon page, §2.1.1) has no body in the
+ *   excerpt.  This library adopts the usual Mamba reading:
+ *     Δ      = softplus(dt_raw + dt_bias)            (τ_Δ; dt_raw is given)
+ *     Ā[n]   = exp(Δ * A[d][n])                      (zero-order hold, A diagonal, negative real)
+ *     B̄x[n]  = Δ * B_t[n] * x_t                      (Euler step for the input)
+ *     y_t    = (sum_n C_t[n] h_t[n] + Dskip[d] x_t) * silu(z_t)
+ *   B_t and C_t are one vector per token shared by all channels.
+ *
+ *   Prefill over a packed stream of sequences: each sequence starts from its
+ *   own h0 row (zeros when h0 is NULL) and never sees another sequence's
+ *   state; its final state goes to its h_last row.  The decode step is the
+ *   loop body for a single token, reading and writing the state in place
+ *   (page 1, section 推理效率: prefill by forward(prompt), then one constant-
+ *   time state update per generated token).
+ *
+ * Everything is double precision with libm exp / log1p; build without
+ * fast-math.  OpenMP runs over independent (sequence, channel) recurrences;
+ * time always runs sequentially inside one recurrence.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* softplus(v) = log(1 + e^v), evaluated without overflow for large v. */
+static double softplus(double v) {
+  if (v > 0.0) return v + log1p(exp(-v));
+  return log1p(exp(v));
+}
+
+/* silu(z) = z * sigmoid(z) = z / (1 + e^{-z}). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * One token of one channel: update h[0..N) in place and return y.
+ *   xv, dtv, zv : this token's x, dt_raw, z at the channel
+ *   Bt, Ct      : this token's B and C vectors (length N)
+ *   Arow        : A[d][0..N)
+ */
+static double token_update(double* h, int64_t N, double xv, double dtv, double zv,
+                           const double* Bt, const double* Ct, const double* Arow,
+                           double dskip, double bias) {
+  const double delta = softplus(dtv + bias);
+  double acc = 0.0;
+  for (int64_t n = 0; n < N; ++n) {
+    const double abar = exp(delta * Arow[n]);
+    const double bbar_x = delta * Bt[n] * xv;
+    h[n] = abar * h[n] + bbar_x;
+    acc += Ct[n] * h[n];
+  }
+  return (acc + dskip * xv) * silu(zv);
+}
+
+/*
+ * Prefill over nseq sequences packed along the token axis.
+ *   seq_start [nseq+1] : token offsets, seq_start[0] = 0, ascending; seq s owns
+ *                        tokens [seq_start[s], seq_start[s+1]).
+ *   x, dt, z  [T][dim] , B, C [T][dstate] , A [dim][dstate], Dskip, dt_bias [dim]
+ *   h0        [nseq][dim][dstate] or NULL (zeros)
+ *   y         [T][dim] (written)
+ *   h_last    [nseq][dim][dstate] or NULL (not written)
+ * Returns 0, or -1 on invalid sizes / allocation failure.
+ */
+int oracle_scan_fwd(int64_t nseq, const int64_t* seq_start, int64_t dim, int64_t dstate,
+                    const double* x, const double* dt, const double* z,
+                    const double* B, const double* C,
+                    const double* A, const double* Dskip, const double* dt_bias,
+                    const double* h0, double* y, double* h_last, int nthreads) {
+  if (nseq < 0 || dim < 0 || dstate < 1 || !seq_start) return -1;
+  for (int64_t s = 0; s < nseq; ++s)
+    if (seq_start[s + 1] < seq_start[s]) return -1;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+#endif
+  for (int64_t s = 0; s < nseq; ++s) {
+    for (int64_t d = 0; d < dim; ++d) {
+      double* h = (double*)malloc((size_t)dstate * sizeof(double));
+      if (!h) { failed = 1; continue; }
+      for (int64_t n = 0; n < dstate; ++n)
+        h[n] = h0 ? h0[(s * dim + d) * dstate + n] : 0.0;
+      for (int64_t t = seq_start[s]; t < seq_start[s + 1]; ++t) {
+        y[t * dim + d] = token_update(h, dstate, x[t * dim + d], dt[t * dim + d], z[t * dim + d],
+                                      B + t * dstate, C + t * dstate, A + d * dstate,
+                                      Dskip[d], dt_bias[d]);
+      }
+      if (h_last)
+        for (int64_t n = 0; n < dstate; ++n) h_last[(s * dim + d) * dstate + n] = h[n];
+      free(h);
+    }
+  }
+  (void)nthreads;
+  return failed ? -1 : 0;
+}
+
+/*
+ * One decode step for `batch` independent sequences.
+ *   state [batch][dim][dstate] : read and written in place
+ *   x, dt, z [batch][dim], B, C [batch][dstate], A [dim][dstate], Dskip, dt_bias [dim]
+ *   y [batch][dim] (written)
+ */
+int oracle_scan_step(int64_t batch, int64_t dim, int64_t dstate, double* state,
+                     const double* x, const double* dt, const double* z,
+                     const double* B, const double* C,
+                     const double* A, const double* Dskip, const double* dt_bias,
+                     double* y, int nthreads) {
+  if (batch < 0 || dim < 0 || dstate < 1) return -1;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nthreads)
+#endif
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t d = 0; d < dim; ++d) {
+      y[b * dim + d] = token_update(state + (b * dim + d) * dstate, dstate, x[b * dim + d], dt[b * dim + d],
+                                    z[b * dim + d], B + b * dstate, C + b * dstate, A + d * dstate,
+                                    Dskip[d], dt_bias[d]);
+    }
+  }
+  (void)nthreads;
+  return 0;
+}
+
+/* Number of OpenMP threads a call with nthreads <= 0 would use. */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

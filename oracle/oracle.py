@@ -1,0 +1,126 @@
+"""Python front of the fp64 oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the CPU
+baseline leg of the benchmark; never by the library.  It converts arrays to
+float64, calls the C loop through ctypes and returns float64 results.  It
+imports nothing from the GPU package.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+HERE = Path(__file__).resolve().parent
+SRC = HERE / "oracle.c"
+LIB = HERE / "liboracle.so"
+CFLAGS = ["-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c99"]
+
+_lib = None
+
+
+def build(force: bool = True, src: Path = SRC, out: Path = LIB) -> Path:
+    """Compile oracle.c with gcc (no fast-math, no FP contraction)."""
+    if not force and out.exists() and out.stat().st_mtime >= src.stat().st_mtime:
+        return out
+    tmp = out.with_suffix(".so.tmp%d" % os.getpid())
+    subprocess.check_call(["gcc", *CFLAGS, "-o", str(tmp), str(src), "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: Path | None = None):
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(str(path)))
+    if _lib is None:
+        if not LIB.exists() or LIB.stat().st_mtime < SRC.stat().st_mtime:
+            build()
+        _lib = _bind(ctypes.CDLL(str(LIB)))
+    return _lib
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_scan_fwd.argtypes = [I64, P, I64, I64, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+    lib.oracle_scan_fwd.restype = ctypes.c_int
+    lib.oracle_scan_step.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+    lib.oracle_scan_step.restype = ctypes.c_int
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan_fwd(x, dt, z, B, C, A, D, dt_bias, h0=None, seq_start=None, nthreads: int = 0, lib=None):
+    """Selective scan prefill in fp64.
+
+    x, dt, z : [T][dim] (or [batch][L][dim] with seq_start None: equal-length rows)
+    B, C     : [T][dstate] (or [batch][L][dstate])
+    A        : [dim][dstate];  D, dt_bias : [dim]
+    h0       : [nseq][dim][dstate] or None
+    seq_start: [nseq+1] token offsets of a packed stream, or None
+    Returns (y [same leading shape as x], h_last [nseq][dim][dstate]).
+    """
+    lib = lib or load()
+    x = _f64(x)
+    shape = x.shape
+    if x.ndim == 3:
+        batch, L, dim = shape
+        if seq_start is None:
+            seq_start = np.arange(batch + 1, dtype=np.int64) * L
+        x = x.reshape(batch * L, dim)
+        dt, z = _f64(dt).reshape(batch * L, dim), _f64(z).reshape(batch * L, dim)
+        B, C = _f64(B).reshape(batch * L, -1), _f64(C).reshape(batch * L, -1)
+    else:
+        dim = shape[1]
+        if seq_start is None:
+            seq_start = np.array([0, shape[0]], dtype=np.int64)
+        dt, z, B, C = _f64(dt), _f64(z), _f64(B), _f64(C)
+    A, D, dt_bias = _f64(A), _f64(D), _f64(dt_bias)
+    dstate = A.shape[1]
+    T = x.shape[0]
+    seq_start = np.ascontiguousarray(np.asarray(seq_start, dtype=np.int64))
+    nseq = len(seq_start) - 1
+    assert seq_start[0] == 0 and seq_start[-1] == T
+    assert dt.shape == z.shape == (T, dim) and B.shape == C.shape == (T, dstate) and A.shape == (dim, dstate)
+    h0 = None if h0 is None else _f64(h0).reshape(nseq, dim, dstate)
+    y = np.empty((T, dim), dtype=np.float64)
+    h_last = np.empty((nseq, dim, dstate), dtype=np.float64)
+    rc = lib.oracle_scan_fwd(nseq, _ptr(seq_start), dim, dstate, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C),
+                             _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_last), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_fwd failed (%d)" % rc)
+    return y.reshape(shape), h_last
+
+
+def scan_step(state, x, dt, z, B, C, A, D, dt_bias, nthreads: int = 0, lib=None):
+    """One decode token in fp64; returns (y [batch][dim], new_state [batch][dim][dstate])."""
+    lib = lib or load()
+    st = _f64(state).copy()
+    x, dt, z, B, C = _f64(x), _f64(dt), _f64(z), _f64(B), _f64(C)
+    A, D, dt_bias = _f64(A), _f64(D), _f64(dt_bias)
+    batch, dim = x.shape
+    dstate = A.shape[1]
+    assert st.shape == (batch, dim, dstate) and B.shape == C.shape == (batch, dstate)
+    y = np.empty((batch, dim), dtype=np.float64)
+    rc = lib.oracle_scan_step(batch, dim, dstate, _ptr(st), _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C),
+                              _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(y), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_step failed (%d)" % rc)
+    return y, st
+
+
+def max_threads(lib=None) -> int:
+    return int((lib or load()).oracle_max_threads())

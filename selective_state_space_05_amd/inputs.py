@@ -1,0 +1,222 @@
+"""Seeded synthetic inputs for the selective scan.
+
+This module only draws random numbers and packs them; it holds none of the
+scan's arithmetic, so both the GPU tests/bench and the fp64 oracle can take
+their inputs from it without sharing any compute code.
+
+Recipe (every config; sizes differ):
+  * x, z, dt_raw ~ N(0, 1) per (token, channel)
+  * dt_bias[d] = log(expm1(U(1e-3, 1e-1)))  -> softplus(dt_bias) lies in [1e-3, 1e-1]
+  * A[d, n] = -exp(U(0, ln 16))             -> A in [-16, -1], diagonal, negative real
+  * B, C ~ N(0, 1) per (token, state)
+  * D[d] ~ U(0, 1)
+  * h0 = 0 unless a test asks for a random carry-in
+bf16 tensors are produced from fp32 draws by integer round-to-nearest-even, so
+the exact values the kernels read are known bit for bit on the host.
+
+Two back ends draw from the same recipe: NumPy (PCG64 seeded from
+SeedSequence([20240611, config, tensor_id])) for host-sized cases that the
+oracle checks whole, and torch generators on the device for the full-size
+workloads (their values differ from NumPy's but are equally seeded; full-size
+checks copy the sampled slices of the very same device tensors to the host).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+SEED_ROOT = 20240611
+TENSOR_IDS = {"x": 0, "z": 1, "dt": 2, "dt_init": 3, "A": 4, "B": 5, "C": 6, "D": 7,
+              "lengths": 8, "h0": 9}
+DECODE_RING_BASE = 100
+DSTATE = 16
+
+
+# --------------------------------------------------------------------------- #
+# bf16 helpers (bit manipulation only)
+# --------------------------------------------------------------------------- #
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """Round fp32 -> bf16 to nearest even; returns the uint16 bit patterns."""
+    bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    lsb = (bits >> np.uint32(16)) & np.uint32(1)
+    rounded = bits + np.uint32(0x7FFF) + lsb
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def f32_from_bf16_bits(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _rng(cfg_id: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, cfg_id, tensor_id])))
+
+
+def torch_seed(cfg_id: int, tensor_id: int) -> int:
+    """63-bit seed for a torch generator, derived from the same seed tree."""
+    s = np.random.SeedSequence([SEED_ROOT, cfg_id, tensor_id]).generate_state(1, np.uint64)[0]
+    return int(s) & ((1 << 63) - 1)
+
+
+# --------------------------------------------------------------------------- #
+# Workload descriptions
+# --------------------------------------------------------------------------- #
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload (sizes of the five standard configurations)."""
+    cfg_id: int
+    name: str
+    batch: int
+    seqlen: int
+    dim: int
+    dstate: int = DSTATE
+    in_dtype: str = "bf16"          # "bf16" or "f32" for x, dt, z, B, C
+    varlen_total: int = 0           # >0: packed variable-length stream of this many tokens
+    chunks: int = 1                 # >1: the prompt is fed as this many chained calls
+    decode_steps: int = 0           # >0: streaming decode after a prefill of `seqlen`
+    decode_ring: int = 0            # number of distinct per-step input sets
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    0: Workload(0, "scan_fwd B1 L256 D64 N16 fp32", 1, 256, 64, in_dtype="f32"),
+    1: Workload(1, "scan_fwd B1 L4096 D2048 N16 bf16", 1, 4096, 2048),
+    2: Workload(2, "scan_fwd varlen T32768 D4096 N16 bf16", 1, 32768, 4096, varlen_total=32768),
+    3: Workload(3, "scan_fwd L131072 D4096 N16 bf16 as 8x16384 chained", 1, 131072, 4096, chunks=8),
+    4: Workload(4, "scan_step B64 D4096 N16 after L2048 prefill, 65536 steps", 64, 2048, 4096,
+                decode_steps=65536, decode_ring=256),
+}
+
+
+def varlen_lengths(cfg_id: int, total: int, lo: int = 512, hi: int = 4096) -> np.ndarray:
+    """Integer lengths in [lo, hi] summing exactly to `total`.
+
+    Lengths are drawn U[lo, hi] while more than hi + lo tokens remain; the
+    remainder r is appended whole if r <= hi, else split into floor(r/2) and
+    ceil(r/2) (both >= hi/2 >= lo).
+    """
+    g = _rng(cfg_id, TENSOR_IDS["lengths"])
+    out = []
+    rem = total
+    while rem > hi + lo:
+        L = int(g.integers(lo, hi + 1))
+        out.append(L)
+        rem -= L
+    if rem <= hi:
+        out.append(rem)
+    else:
+        out.extend([rem // 2, rem - rem // 2])
+    arr = np.asarray(out, dtype=np.int64)
+    assert arr.sum() == total and arr.min() >= min(lo, total) and arr.max() <= hi
+    return arr
+
+
+def cu_from_lengths(lengths) -> np.ndarray:
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return cu
+
+
+# --------------------------------------------------------------------------- #
+# Parameters (always small: drawn with NumPy, fp32)
+# --------------------------------------------------------------------------- #
+def make_params(cfg_id: int, dim: int, dstate: int = DSTATE) -> dict:
+    """A [dim][dstate], D [dim], dt_bias [dim] as fp32 arrays."""
+    u = _rng(cfg_id, TENSOR_IDS["dt_init"]).uniform(1e-3, 1e-1, size=dim)
+    dt_bias = np.log(np.expm1(u)).astype(np.float32)
+    A = (-np.exp(_rng(cfg_id, TENSOR_IDS["A"]).uniform(0.0, math.log(16.0), size=(dim, dstate)))).astype(np.float32)
+    D = _rng(cfg_id, TENSOR_IDS["D"]).uniform(0.0, 1.0, size=dim).astype(np.float32)
+    return {"A": A, "D": D, "dt_bias": dt_bias}
+
+
+def make_h0(cfg_id: int, nseq: int, dim: int, dstate: int = DSTATE, scale: float = 1.0) -> np.ndarray:
+    return (scale * _rng(cfg_id, TENSOR_IDS["h0"]).standard_normal((nseq, dim, dstate))).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- #
+# NumPy back end (host-sized cases)
+# --------------------------------------------------------------------------- #
+def _normal(cfg_id: int, name: str, shape) -> np.ndarray:
+    return _rng(cfg_id, TENSOR_IDS[name]).standard_normal(shape, dtype=np.float32)
+
+
+def make_fwd_inputs_np(cfg_id: int, rows: int, dim: int, dstate: int = DSTATE,
+                       in_dtype: str = "bf16") -> dict:
+    """Token-major inputs for `rows` tokens (batch*seqlen, or a packed stream).
+
+    Returns the device-side representation (uint16 bf16 bits or fp32) under
+    x, dt, z, B, C and the exact fp32 values the kernels see under *_f32.
+    """
+    out = {}
+    for name, shape in (("x", (rows, dim)), ("z", (rows, dim)), ("dt", (rows, dim)),
+                        ("B", (rows, dstate)), ("C", (rows, dstate))):
+        v = _normal(cfg_id, name, shape)
+        if in_dtype == "bf16":
+            bits = bf16_bits_from_f32(v)
+            out[name] = bits
+            out[name + "_f32"] = f32_from_bf16_bits(bits)
+        elif in_dtype == "f32":
+            out[name] = v
+            out[name + "_f32"] = v
+        else:
+            raise ValueError(in_dtype)
+    out.update(make_params(cfg_id, dim, dstate))
+    return out
+
+
+def make_step_inputs_np(cfg_id: int, ring_index: int, batch: int, dim: int, dstate: int = DSTATE,
+                        in_dtype: str = "bf16") -> dict:
+    """One decode step's inputs (x, dt, z [batch][dim]; B, C [batch][dstate])."""
+    base = DECODE_RING_BASE + ring_index * 8
+    out = {}
+    for k, (name, shape) in enumerate((("x", (batch, dim)), ("z", (batch, dim)), ("dt", (batch, dim)),
+                                       ("B", (batch, dstate)), ("C", (batch, dstate)))):
+        v = _rng(cfg_id, base + k).standard_normal(shape, dtype=np.float32)
+        if in_dtype == "bf16":
+            bits = bf16_bits_from_f32(v)
+            out[name], out[name + "_f32"] = bits, f32_from_bf16_bits(bits)
+        else:
+            out[name], out[name + "_f32"] = v, v
+    return out
+
+
+# --------------------------------------------------------------------------- #
+# torch back end (full-size workloads, generated on the device)
+# --------------------------------------------------------------------------- #
+def _torch_normal(torch, shape, cfg_id: int, tensor_id: int, device, dtype):
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_seed(cfg_id, tensor_id))
+    v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return v.to(dtype)  # fp32 -> bf16 cast rounds to nearest even
+
+
+def make_fwd_inputs_torch(cfg_id: int, rows: int, dim: int, device, dstate: int = DSTATE,
+                          in_dtype: str = "bf16", tensor_offset: int = 0) -> dict:
+    """Device tensors x, dt, z [rows][dim], B, C [rows][dstate] (+ fp32 params).
+
+    `tensor_offset` shifts the seed ids so that chained chunks of one long
+    prompt get distinct draws.
+    """
+    import torch
+    dt_ = torch.bfloat16 if in_dtype == "bf16" else torch.float32
+    out = {}
+    for name, shape in (("x", (rows, dim)), ("z", (rows, dim)), ("dt", (rows, dim)),
+                        ("B", (rows, dstate)), ("C", (rows, dstate))):
+        out[name] = _torch_normal(torch, shape, cfg_id, TENSOR_IDS[name] + 1000 * tensor_offset, device, dt_)
+    p = make_params(cfg_id, dim, dstate)
+    for k, v in p.items():
+        out[k] = torch.from_numpy(v).to(device)
+    return out
+
+
+def make_step_ring_torch(cfg_id: int, ring: int, batch: int, dim: int, device, dstate: int = DSTATE) -> dict:
+    """`ring` decode input sets stacked on a leading axis: x, dt, z [ring][batch][dim], B, C [ring][batch][dstate]."""
+    import torch
+    out = {}
+    for k, (name, shape) in enumerate((("x", (ring, batch, dim)), ("z", (ring, batch, dim)),
+                                       ("dt", (ring, batch, dim)), ("B", (ring, batch, dstate)),
+                                       ("C", (ring, batch, dstate)))):
+        out[name] = _torch_normal(torch, shape, cfg_id, DECODE_RING_BASE + k, device, torch.bfloat16)
+    return out
