@@ -1,0 +1,279 @@
+"""Benchmark of the selective scan on one MI355X.
+
+Step = one pass of the long-prompt prefill: L = 131072 tokens, D = 4096
+channels, 16 states, bf16 I/O and fp32 state, fed as 8 chained calls of 16384
+tokens with the state carried h0 -> h_last between calls.  Inputs are seeded
+synthetic tensors already resident in HBM.  `value` is algorithmic GB/s of
+that prefill (bytes the method must move: x, dt, z in and y out, B and C per
+token, parameters, carry in and out).  The streaming decode (batch 64, D 4096,
+65536 consecutive single-token steps over a ring of 256 input sets, state from
+a 2048-token prefill) is reported in the same line under "decode".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "scan GB/s & tokens·channels/s at L=128K, % HBM roofline; decode steps/s"
+HBM_PEAK_GBS = 8000.0
+# VALU issue peak: 256 CUs x 4 SIMDs x 32 fp32 lanes/clock x 2.4 GHz (one slot = one full-rate fp32 lane op)
+VALU_PEAK_TSLOT = 256 * 4 * 32 * 2.4e9 / 1e12
+TRANS_SLOTS = 4            # a transcendental (exp2, log2, rcp) issues at a quarter of the fp32 rate
+# Algorithmic work of the plain sequential recurrence per (token, channel):
+#   16 states x (Δ*A mul, exp, Δx*B mul, state FMA, readout FMA) = 64 VALU + 16 transcendentals
+#   softplus(dt + bias): add, exp, log1p (~2 VALU + 2 transcendentals); Δ*x: 1; skip: 1 FMA;
+#   silu gate: exp, rcp, 2 VALU; gate multiply: 1; bf16 widen x3 + narrow x1: 4
+VALU_PER_TD = 64 + 2 + 1 + 1 + 2 + 1 + 4
+TRANS_PER_TD = 16 + 2 + 2
+SLOTS_PER_TD = VALU_PER_TD + TRANS_SLOTS * TRANS_PER_TD
+KERNEL_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_scan.hip"
+TRAFFIC_FILE = ROOT / "profiles" / "scan_fwd_L16384_D4096_traffic.json"
+
+
+def prefill_bytes(tokens: int, dim: int, io_bytes: int = 2, h0: bool = True, h_last: bool = True, n: int = 16) -> int:
+    b = tokens * dim * 4 * io_bytes          # x, dt, z in; y out
+    b += tokens * 2 * n * io_bytes           # B, C
+    b += dim * n * 4 + dim * 8               # A, D, dt_bias
+    b += (dim * n * 4 if h0 else 0) + (dim * n * 4 if h_last else 0)
+    return b
+
+
+def decode_bytes(batch: int, dim: int, n: int = 16) -> int:
+    return batch * dim * (2 * n * 4 + 4 * 2) + batch * 2 * n * 2 + dim * n * 4 + dim * 8
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if taken on this kernel source."""
+    try:
+        t = json.loads(TRAFFIC_FILE.read_text())
+    except Exception:
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def bench_prefill(steps: int, warmup: int):
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import scan as S
+
+    W = I.WORKLOADS[3]
+    L, D, n = W.seqlen, W.dim, W.chunks
+    cl = L // n
+    dev = torch.device("cuda:0")
+    inp = I.make_fwd_inputs_torch(3, L, D, dev)
+    y = torch.empty(L, D, dtype=torch.bfloat16, device=dev)
+    h0 = torch.zeros(1, D, 16, device=dev)
+    hb = [torch.empty(1, D, 16, device=dev) for _ in range(2)]
+    lib = S.load_library()
+    stream = torch.cuda.current_stream()
+    args = []
+    prev = h0
+    for i in range(n):
+        sl = slice(i * cl, (i + 1) * cl)
+        a = S.fwd_args(*(inp[k][sl].view(1, cl, -1) for k in ("x", "dt", "z", "B", "C")), inp["A"], inp["D"],
+                       inp["dt_bias"], y=y[sl].view(1, cl, D), h0=prev, h_last=hb[i % 2])
+        args.append(a)
+        prev = hb[i % 2]
+    plan = S.fwd_plan(*(inp[k][:cl].view(1, cl, -1) for k in ("x", "dt", "z", "B", "C")), inp["A"], inp["D"],
+                      inp["dt_bias"], y=y[:cl].view(1, cl, D), h0=h0, h_last=hb[0])
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def one_step():
+        for a in args:
+            st = lib.samba_scan_fwd(ctypes.byref(a), sh)
+            if st != 0:
+                raise S.SambaError(st, "samba_scan_fwd")
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        one_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    launch_ms = ms / n
+    tokens_ch = L * D
+    step_bytes = n * prefill_bytes(cl, D)
+    return {
+        "ms_per_step": ms,
+        "gbs": step_bytes / (ms * 1e-3) / 1e9,
+        "tokens_channels_per_s": tokens_ch / (ms * 1e-3),
+        "launch_ms": launch_ms,
+        "launch_td": cl * D,
+        "bytes_per_launch": prefill_bytes(cl, D),
+        "plan": {"time_slices": plan[0], "workgroups": plan[1], "threads_per_workgroup": plan[2]},
+    }
+
+
+def bench_decode(steps: int = 65536, ring: int = 256):
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import scan as S
+
+    W = I.WORKLOADS[4]
+    Bt, L, D = W.batch, W.seqlen, W.dim
+    dev = torch.device("cuda:0")
+    pre = I.make_fwd_inputs_torch(4, Bt * L, D, dev)
+    _, state = S.scan_fwd(*(pre[k].view(Bt, L, -1) for k in ("x", "dt", "z", "B", "C")), pre["A"], pre["D"],
+                          pre["dt_bias"])
+    del pre["x"], pre["dt"], pre["z"]
+    rg = I.make_step_ring_torch(4, ring, Bt, D, dev)
+    ys = torch.empty(ring, Bt, D, dtype=torch.bfloat16, device=dev)
+    lib = S.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    args = [S.step_args(state, rg["x"][r], rg["dt"][r], rg["z"][r], rg["B"][r], rg["C"][r], pre["A"], pre["D"],
+                        pre["dt_bias"], y=ys[r]) for r in range(ring)]
+    refs = [ctypes.byref(a) for a in args]
+    f = lib.samba_scan_step
+    for r in range(ring):
+        f(refs[r], sh)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(steps):
+        if f(refs[k & (ring - 1)], sh) != 0:
+            raise RuntimeError("samba_scan_step failed")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    us = ms * 1e3 / steps
+    out = {"steps": steps, "us_per_step": us, "steps_per_s": steps / (ms * 1e-3),
+           "gbs": decode_bytes(Bt, D) / (us * 1e-6) / 1e9}
+    out["hbm_frac"] = out["gbs"] / HBM_PEAK_GBS
+    # the same steps captured by the caller into a graph (one replay = one pass over the ring)
+    try:
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        with torch.cuda.stream(cs):
+            f(refs[0], ctypes.c_void_p(cs.cuda_stream))
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cs):
+            csh = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for r in range(ring):
+                f(refs[r], csh)
+        torch.cuda.synchronize()
+        reps = steps // ring
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gus = e0.elapsed_time(e1) * 1e3 / (reps * ring)
+        out["graph"] = {"us_per_step": gus, "steps_per_s": 1e6 / gus,
+                        "gbs": decode_bytes(Bt, D) / (gus * 1e-6) / 1e9}
+    except Exception as ex:  # graph capture is an optional, separately reported variant
+        out["graph"] = {"error": repr(ex)[:200]}
+    return out
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of the same prefill (first 16384-token call, some channels)."""
+    import numpy as np
+    import torch
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+
+    W = I.WORKLOADS[3]
+    cl, D = W.seqlen // W.chunks, W.dim
+    inp = I.make_fwd_inputs_torch(3, cl, D, "cpu")
+    P = I.make_params(3, D)
+    Bh, Ch = (inp[k].float().numpy() for k in ("B", "C"))
+    lib = O.load()
+    cores = O.max_threads(lib)
+
+    def run(C):
+        xs, ds, zs = (inp[k][:, :C].float().numpy() for k in ("x", "dt", "z"))
+        t0 = time.perf_counter()
+        O.scan_fwd(xs, ds, zs, Bh, Ch, P["A"][:C], P["D"][:C], P["dt_bias"][:C], h0=np.zeros((1, C, 16)), lib=lib)
+        return time.perf_counter() - t0
+
+    t = run(64)
+    C = int(min(D, max(64, 64 * target_s / max(t, 1e-3))))
+    C = max(64, (C // 64) * 64)
+    t = run(C)
+    gbs = prefill_bytes(cl, C) / t / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "first 16384-token call of the 131072-token prompt, %d of 4096 channels, fp64 oracle, %.1f s"
+                      % (C, t),
+            "tokens_channels_per_s": cl * C / t}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=65536)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    pf = bench_prefill(args.steps, args.warmup)
+    achieved = SLOTS_PER_TD * pf["launch_td"] / (pf["launch_ms"] * 1e-3) / 1e12
+    traffic = read_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(pf["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "long-prompt prefill L=131072 D=4096 N=16 as 8 chained calls of 16384 "
+                               "(h0 -> h_last), bf16 I/O, fp32 state", "seq_len": 131072, "dim": 4096,
+                   "dstate": 16, "chunks": 8, "io": "bf16"},
+        "tokens_channels_per_s": pf["tokens_channels_per_s"],
+        "hbm_frac": pf["gbs"] / HBM_PEAK_GBS,
+        "plan": pf["plan"],
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TSLOT, 2),
+                     "unit": "Tslot/s", "frac": round(achieved / VALU_PEAK_TSLOT, 4),
+                     "traffic": traffic, "kernel": "scan_fwd_kernel<bf16,bf16,W=%d>" % pf["plan"]["time_slices"],
+                     "launch_us": round(pf["launch_ms"] * 1e3, 2), "slots_per_token_channel": SLOTS_PER_TD,
+                     "algorithmic_bytes_per_launch": pf["bytes_per_launch"]},
+    }
+    if not args.no_decode:
+        dec = bench_decode(args.decode_steps)
+        dec["roofline"] = {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                           "kernel": "scan_step_kernel<bf16,bf16>"}
+        line["decode"] = dec
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

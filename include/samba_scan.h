@@ -1,0 +1,146 @@
+/*
+ * samba_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan.
+ *
+ * The operation (page "SAMBA混合注意力状态空间模型", metaphor-xennon.pages.dev,
+ * section 数学框架 -> Mamba层): a diagonal linear recurrence per channel,
+ *     h_t = Ā_t h_{t-1} + B̄_t x_t,   y_t = C_t h_t   (readout after the update),
+ * with B_t, C_t and Δ_t chosen from the input.  The pages leave Ā, B̄ and τ_Δ
+ * undefined; this library uses the Mamba reading, stated once here:
+ *     Δ      = softplus(dt_raw + dt_bias[d])
+ *     Ā[n]   = exp(Δ * A[d][n])          A diagonal, negative real (not checked)
+ *     B̄x[n]  = Δ * B_t[n] * x_t
+ *     y      = (sum_n C_t[n] h[n] + D[d] * x_t) * silu(z_t)
+ * State size: 16 per channel (same page, section 实现细节 -> 模型配置).
+ * Arithmetic is fp32 (state, discretisation, readout); x, dt, z, B, C are bf16
+ * or fp32; y is written as bf16 (round to nearest even) or fp32.
+ *
+ * Layout (all row-major, contiguous, token-major):
+ *     x, dt, z, y   [tokens][dim]        tokens = batch * seqlen (rows of batch b
+ *                                        are tokens b*seqlen .. b*seqlen+seqlen-1)
+ *     B, C          [tokens][16]         one vector per token, shared by all channels
+ *     A             [dim][16]  fp32      D, dt_bias  [dim] fp32
+ *     h0, h_last    [nseq][dim][16] fp32 (nseq = batch, or the cu_seqlens count)
+ *     state (step)  [batch][dim][16] fp32
+ *
+ * Ownership: every pointer (except the args struct itself) is a DEVICE pointer
+ * owned by the caller.  The library allocates no device memory, keeps no
+ * pointers after a call returns, and caches only per-device properties.
+ *
+ * Asynchrony: calls validate on the host, then enqueue kernels on `stream`
+ * (a hipStream_t passed as void*; NULL = the default stream) and return.
+ * Results are valid once the caller synchronises that stream.  Calls on one
+ * stream run in order; calls on different streams must not share outputs.
+ *
+ * Errors: all validation happens before anything is enqueued; on any error
+ * nothing is enqueued and no output is touched.  A failed launch returns
+ * SAMBA_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ * synchronisation.  No C++ exception crosses this interface.
+ */
+#ifndef SAMBA_SCAN_H
+#define SAMBA_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAMBA_SCAN_ABI_VERSION 1
+#define SAMBA_DSTATE 16
+
+typedef enum {
+  SAMBA_OK = 0,
+  SAMBA_ERR_NULL_ARG = 1,      /* a required pointer is NULL */
+  SAMBA_ERR_BAD_SHAPE = 2,     /* negative / inconsistent sizes, or varlen with batch != 1 */
+  SAMBA_ERR_BAD_DTYPE = 3,     /* in_dtype / y_dtype not a samba_dtype value */
+  SAMBA_ERR_MISALIGNED = 4,    /* a pointer violates its alignment rule (below) */
+  SAMBA_ERR_ALIASING = 5,      /* an output overlaps an input it must not overlap */
+  SAMBA_ERR_UNSUPPORTED = 6,   /* dstate != 16, or time_slices not 0/1/2/4/8 */
+  SAMBA_ERR_BAD_STRUCT = 7,    /* struct_size does not match this header */
+  SAMBA_ERR_HIP = 8            /* the HIP runtime refused the launch */
+} samba_status;
+
+typedef enum { SAMBA_F32 = 0, SAMBA_BF16 = 1 } samba_dtype;
+
+/*
+ * Prefill: scan every sequence from its carry-in h0 (zeros if NULL) over its
+ * tokens, write y for every token and, if h_last is not NULL, each sequence's
+ * final state.  "Unlimited streaming" (page 2 abstract; hackernoon page,
+ * abstract and §1) is served by chaining calls: pass one call's h_last as the
+ * next call's h0; the result equals one call over the concatenated tokens.
+ *
+ * Sequences: without cu_seqlens, `batch` rows of `seqlen` tokens each.  With
+ * cu_seqlens (device int32 [nseq+1], cu[0] = 0, ascending, cu[nseq] =
+ * seqlen), batch must be 1 and the `seqlen` tokens hold nseq packed
+ * sequences; each restarts from its own h0 row and writes its own h_last row.
+ * Out-of-range or descending offsets are clamped into [0, seqlen] on the
+ * device (memory-safe; results for such input are unspecified).
+ *
+ * Pointers: x, dt, z, B, C, y may be NULL only when there are no tokens.
+ * Alignment: B, C, A, h0, h_last 16 bytes; x, dt, z, y, D, dt_bias their
+ * element size.  h_last may equal h0 exactly (in-place carry); any other
+ * overlap of an output (y, h_last) with an input is SAMBA_ERR_ALIASING.
+ * time_slices: 0 lets the library choose how many waves split each time chunk
+ * of one channel tile (1, 2, 4 or 8); other values force it (testing and
+ * tuning; results agree to fp32 rounding, and are bitwise reproducible for a
+ * given choice).
+ */
+typedef struct {
+  uint32_t struct_size;        /* = sizeof(samba_scan_fwd_args) */
+  int32_t batch, seqlen, dim, dstate;
+  const int32_t* cu_seqlens;   /* optional, device */
+  int32_t nseq;                /* number of packed sequences when cu_seqlens != NULL */
+  int32_t in_dtype, y_dtype;   /* samba_dtype */
+  int32_t time_slices;         /* 0 = automatic */
+  const void *x, *dt, *z;
+  const void *B, *C;
+  const float *A, *D, *dt_bias;
+  const float* h0;             /* optional */
+  float* h_last;               /* optional */
+  void* y;
+} samba_scan_fwd_args;
+
+/*
+ * Decode: one token for each of `batch` sequences (page 1, section 推理效率:
+ * the per-token constant-time state update of generation).  The state is read
+ * and written IN PLACE; y gets one value per (sequence, channel).
+ * Alignment: state, B, C, A 16 bytes; others their element size.  y must not
+ * overlap state or any input.
+ */
+typedef struct {
+  uint32_t struct_size;        /* = sizeof(samba_scan_step_args) */
+  int32_t batch, dim, dstate;
+  int32_t in_dtype, y_dtype;
+  float* state;                /* [batch][dim][16], in place */
+  const void *x, *dt, *z;      /* [batch][dim] */
+  const void *B, *C;           /* [batch][16] */
+  const float *A, *D, *dt_bias;
+  void* y;                     /* [batch][dim] */
+} samba_scan_step_args;
+
+/* Enqueue a prefill scan.  See samba_scan_fwd_args. */
+samba_status samba_scan_fwd(const samba_scan_fwd_args* args, void* stream);
+
+/* Enqueue one decode step.  See samba_scan_step_args. */
+samba_status samba_scan_step(const samba_scan_step_args* args, void* stream);
+
+/*
+ * Host-only: validate `args` and report the launch the library would make on
+ * the current device (time slices per channel tile, workgroups, threads per
+ * workgroup).  Enqueues nothing.  Any of the out pointers may be NULL.
+ */
+samba_status samba_scan_fwd_plan(const samba_scan_fwd_args* args, int32_t* time_slices,
+                                 int32_t* workgroups, int32_t* threads_per_workgroup);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* samba_status_string(int status);
+
+/* SAMBA_SCAN_ABI_VERSION of the built library. */
+int samba_scan_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAMBA_SCAN_H */

@@ -1,0 +1,8 @@
+"""MI355X (gfx950) selective state-space scan: HIP kernels behind a C ABI.
+
+The library (libsamba_scan.so, built from csrc/samba_scan.hip) is loaded on
+first use by :mod:`selective_state_space_05_amd.scan`; importing this package
+does not load it, so the seeded input recipe (:mod:`.inputs`) is usable on
+hosts without the built library.
+"""
+__all__ = ["scan", "inputs"]

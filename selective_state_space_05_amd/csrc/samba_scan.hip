@@ -1,0 +1,693 @@
+// samba_scan.hip -- gfx950 (MI355X) kernels and the C ABI of the selective scan.
+//
+// Operation: page "SAMBA混合注意力状态空间模型" (metaphor-xennon.pages.dev),
+// section 数学框架 -> Mamba层: h_t = Ā_t h_{t-1} + B̄_t x_t, y_t = C_t h_t with
+// B_t, C_t, Δ_t chosen from the input.  Ā = exp(ΔA), B̄x = ΔBx, Δ = softplus(dt +
+// bias), y = (C.h + D x) silu(z) is the Mamba reading this library adopts (the
+// pages leave those maps undefined).  State size 16 (same page, 实现细节 ->
+// 模型配置).  Prefill is the page's forward(prompt); the decode step is its
+// per-token constant-time state update (section 推理效率).
+//
+// Work decomposition (both kernels): a channel's 16 states are split over a
+// quad of 4 lanes (4 states per lane), so a wave covers 16 channels.  B_t and
+// C_t are shared by all channels; they are staged once per wave into LDS as
+// fp32, so the per-lane work is only the recurrence itself.  The per-token
+// scalar work of a channel (softplus, skip, gate, conversions, load and store)
+// is spread over the quad: lane g of a quad owns tokens t with t % 4 == g of
+// each group of four, and broadcasts Δ and Δx to its quad with DPP.  The four
+// lanes' partial readouts are summed with a transposed quad reduction so that
+// each lane ends with the finished y of its own token.
+//
+// Prefill parallelism: (sequence x 16-channel tile) workgroups; when that is
+// too few to fill 256 CUs, W waves of a workgroup split each time chunk of
+// W*16 tokens into W slices.  Each wave runs its slice from a zero state,
+// keeping every Ā and B̄x it computed in registers and publishing the slice's
+// (product of Ā, local end state) pair through LDS; after one barrier each
+// wave folds its predecessors' pairs into its carry-in and replays the slice
+// from the registers (two FMAs per state and token, no second exp).  The carry
+// between chunks goes through LDS as well.  No state crosses workgroups, so no
+// workspace and no inter-workgroup synchronisation is needed.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "samba_scan.h"
+
+namespace {
+
+constexpr int kN = 16;         // states per channel
+constexpr int kSPL = 4;        // states per lane
+constexpr int kCPW = 16;       // channels per wave
+constexpr int kK = 16;         // tokens per wave slice (multiple of 4)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// ---------------------------------------------------------------------------
+// element access
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float ld_in(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_in(const uint16_t* p, int64_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((b >> 16) | 0x40u);  // keep NaN a NaN
+  b += 0x7fffu + ((b >> 16) & 1u);                                                     // round to nearest even
+  return static_cast<uint16_t>(b >> 16);
+}
+__device__ __forceinline__ void st_out(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st_out(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// scalar maps
+// ---------------------------------------------------------------------------
+// softplus(v) = log(1 + e^v).  log1p is formed as log(u) * e / (u - 1) with
+// u = 1 + e rounded (Goldberg's correction), which keeps full relative accuracy
+// for the small Δ this map produces; v > 20 returns v (the remainder is below
+// fp32 resolution).
+__device__ __forceinline__ float softplus_f32(float v) {
+  const float e = __builtin_amdgcn_exp2f(v * kLog2e);
+  const float u = 1.0f + e;
+  const float um1 = u - 1.0f;
+  const float lg = __builtin_amdgcn_logf(u) * kLn2;
+  const float r = (um1 == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(um1));
+  return (v > 20.0f) ? v : r;
+}
+
+// silu(z) = z / (1 + e^{-z})
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+
+// ---------------------------------------------------------------------------
+// quad (4-lane) exchanges through DPP quad_perm
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float qperm(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQXor1 = 0xB1;  // [1,0,3,2]
+constexpr int kQXor2 = 0x4E;  // [2,3,0,1]
+template <int Q>
+__device__ __forceinline__ float qbcast(float v) { return qperm<Q * 0x55>(v); }  // [Q,Q,Q,Q]
+
+// Lane g holds partial sums p[0..3] for the four tokens of a group; returns, on
+// lane g, the quad's total for token g.
+__device__ __forceinline__ float quad_transpose_sum(float p0, float p1, float p2, float p3, int g) {
+  const bool hi = (g & 2) != 0;
+  const float k0 = hi ? p2 : p0, s0 = hi ? p0 : p2;
+  const float k1 = hi ? p3 : p1, s1 = hi ? p1 : p3;
+  const float r0 = k0 + qperm<kQXor2>(s0);
+  const float r1 = k1 + qperm<kQXor2>(s1);
+  const bool odd = (g & 1) != 0;
+  const float k = odd ? r1 : r0, s = odd ? r0 : r1;
+  return k + qperm<kQXor1>(s);
+}
+
+__device__ __forceinline__ float quad_allsum(float v) {
+  v += qperm<kQXor1>(v);
+  v += qperm<kQXor2>(v);
+  return v;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// B/C staging: kK tokens x 16 states of B and of C -> fp32 LDS rows.
+// Rows at or beyond `nv` valid tokens are zero-filled.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void stage_bc(const uint16_t* B, const uint16_t* C, int64_t t0, int nv,
+                                         float* sB, float* sC, int lane) {
+  static_assert(kK == 16, "one 16-byte vector per lane covers 16 rows of B and C");
+  const int which = lane >> 5;
+  const int r = (lane & 31) >> 1;
+  const int half = lane & 1;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (r < nv) v = *reinterpret_cast<const uint4*>((which ? C : B) + (t0 + r) * kN + half * 8);
+  float* dst = (which ? sC : sB) + r * kN + half * 8;
+  reinterpret_cast<float4*>(dst)[0] = make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
+  reinterpret_cast<float4*>(dst)[1] = make_float4(bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w));
+}
+
+__device__ __forceinline__ void stage_bc(const float* B, const float* C, int64_t t0, int nv, float* sB,
+                                         float* sC, int lane) {
+  const int r = lane >> 2;
+  const int qt = lane & 3;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < nv) v = *reinterpret_cast<const float4*>((which ? C : B) + (t0 + r) * kN + qt * 4);
+    reinterpret_cast<float4*>((which ? sC : sB) + r * kN)[qt] = v;
+  }
+}
+
+// Block index -> logical index so that consecutive logical blocks (adjacent
+// channel tiles, which share 128-byte lines of x, dt, z, y) land on the same
+// XCD, given that the dispatcher deals blocks round-robin over the 8 XCDs.
+// A bijection on [0, n) whatever the dispatch order is.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int q = n >> 3, r = n & 7, xcd = bid & 7, slot = bid >> 3;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+struct FwdParams {
+  const void *x, *dt, *z, *B, *C;
+  const float *A, *Dskip, *bias;
+  const float* h0;
+  float* h_last;
+  void* y;
+  const int32_t* cu;
+  int64_t total_tokens;
+  int32_t seqlen;        // tokens per sequence when cu == nullptr
+  int32_t dim;
+  int32_t ntiles;        // ceil(dim / 16)
+  int32_t tiles_per_wg;  // waves of one workgroup that take consecutive tiles (W == 1 only)
+  int32_t ngroups;       // ceil(ntiles / tiles_per_wg)
+  int32_t nblocks;       // nseq * ngroups
+};
+
+// Per-lane setup shared by both prefill variants.
+struct LaneCtx {
+  int lane, g, c, d;
+  bool dvalid;
+  int64_t start, end;
+  float A2[kSPL];
+  float dsk, bias;
+  float hinit[kSPL];
+};
+
+template <typename Tin>
+__device__ __forceinline__ void load_slice(const FwdParams& p, const LaneCtx& L, int64_t t0, int nv,
+                                           float (&xv)[kK / 4], float (&zv)[kK / 4], float (&dl)[kK / 4],
+                                           float (&uu)[kK / 4]) {
+  const Tin* x = static_cast<const Tin*>(p.x);
+  const Tin* dt = static_cast<const Tin*>(p.dt);
+  const Tin* z = static_cast<const Tin*>(p.z);
+#pragma unroll
+  for (int j = 0; j < kK / 4; ++j) {
+    const int kk = 4 * j + L.g;
+    float xr = 0.f, dr = 0.f, zr = 0.f;
+    if (L.dvalid && kk < nv) {
+      const int64_t idx = (t0 + kk) * p.dim + L.d;
+      xr = ld_in(x, idx);
+      dr = ld_in(dt, idx);
+      zr = ld_in(z, idx);
+    }
+    xv[j] = xr;
+    zv[j] = zr;
+    const float delta = (L.dvalid && kk < nv) ? softplus_f32(dr + L.bias) : 0.0f;
+    dl[j] = delta;
+    uu[j] = delta * xr;
+  }
+}
+
+template <typename Tout>
+__device__ __forceinline__ void store_y(const FwdParams& p, const LaneCtx& L, int64_t t0, int kk, int nv,
+                                        float yraw, float xr, float zr) {
+  if (L.dvalid && kk < nv) {
+    const float yv = (yraw + L.dsk * xr) * silu_f32(zr);
+    st_out(static_cast<Tout*>(p.y), (t0 + kk) * p.dim + L.d, yv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill kernel.  W = waves splitting each time chunk (1 = plain sequential
+// scan); TPW = channel tiles per workgroup (W == 1 only).
+// ---------------------------------------------------------------------------
+template <typename Tin, typename Tout, int W, int TPW>
+__global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
+  static_assert(W == 1 || TPW == 1, "time slices and tile packing are exclusive");
+  constexpr int kWaves = W * TPW;
+  __shared__ float4 s_bc[kWaves][2][kK * kN / 4];                  // per-wave staged B, C (fp32)
+  __shared__ float4 s_agg[(W > 1) ? 2 : 1][W][2][64];              // slice (P, H) pairs, double buffered
+  __shared__ float4 s_carry[(W > 1) ? 2 : 1][64];                  // chunk carry, double buffered
+
+  const int wave = threadIdx.x >> 6;
+  const int logical = xcd_remap(blockIdx.x, p.nblocks);
+  const int s = logical / p.ngroups;
+  const int grp = logical - s * p.ngroups;
+  const int tile = (W == 1) ? grp * TPW + wave : grp;
+  if (W == 1 && tile >= p.ntiles) return;  // whole wave idle (no barriers in the W == 1 path)
+
+  LaneCtx L;
+  L.lane = threadIdx.x & 63;
+  L.g = L.lane & 3;
+  L.c = L.lane >> 2;
+  L.d = tile * kCPW + L.c;
+  L.dvalid = L.d < p.dim;
+  const int dc = L.dvalid ? L.d : p.dim - 1;
+  if (p.cu) {
+    int64_t a = p.cu[s], b = p.cu[s + 1];
+    a = a < 0 ? 0 : (a > p.total_tokens ? p.total_tokens : a);
+    b = b < a ? a : (b > p.total_tokens ? p.total_tokens : b);
+    L.start = a;
+    L.end = b;
+  } else {
+    L.start = static_cast<int64_t>(s) * p.seqlen;
+    L.end = L.start + p.seqlen;
+  }
+  {
+    const float4 a4 = reinterpret_cast<const float4*>(p.A + static_cast<int64_t>(dc) * kN)[L.g];
+    L.A2[0] = a4.x * kLog2e;
+    L.A2[1] = a4.y * kLog2e;
+    L.A2[2] = a4.z * kLog2e;
+    L.A2[3] = a4.w * kLog2e;
+  }
+  L.dsk = p.Dskip[dc];
+  L.bias = p.bias[dc];
+  if (p.h0) {
+    const float4 h4 = reinterpret_cast<const float4*>(p.h0 + (static_cast<int64_t>(s) * p.dim + dc) * kN)[L.g];
+    L.hinit[0] = h4.x; L.hinit[1] = h4.y; L.hinit[2] = h4.z; L.hinit[3] = h4.w;
+  } else {
+    L.hinit[0] = L.hinit[1] = L.hinit[2] = L.hinit[3] = 0.f;
+  }
+
+  const Tin* Bp = static_cast<const Tin*>(p.B);
+  const Tin* Cp = static_cast<const Tin*>(p.C);
+  float* sB = reinterpret_cast<float*>(s_bc[wave][0]);
+  float* sC = reinterpret_cast<float*>(s_bc[wave][1]);
+  const float4* sB4 = s_bc[wave][0];
+  const float4* sC4 = s_bc[wave][1];
+  float h[kSPL] = {L.hinit[0], L.hinit[1], L.hinit[2], L.hinit[3]};
+
+  if constexpr (W == 1) {
+    // ---------------- sequential scan over the whole sequence ----------------
+    for (int64_t t0 = L.start; t0 < L.end; t0 += kK) {
+      const int64_t rem = L.end - t0;
+      const int nv = rem < kK ? static_cast<int>(rem) : kK;
+      stage_bc(Bp, Cp, t0, nv, sB, sC, L.lane);
+      float xv[kK / 4], zv[kK / 4], dl[kK / 4], uu[kK / 4];
+      load_slice<Tin>(p, L, t0, nv, xv, zv, dl, uu);
+      wave_lds_sync();
+#pragma unroll
+      for (int j = 0; j < kK / 4; ++j) {
+        if (4 * j >= nv) break;
+        float pr[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float dk = (q == 0) ? qbcast<0>(dl[j]) : (q == 1) ? qbcast<1>(dl[j]) : (q == 2) ? qbcast<2>(dl[j]) : qbcast<3>(dl[j]);
+          const float uk = (q == 0) ? qbcast<0>(uu[j]) : (q == 1) ? qbcast<1>(uu[j]) : (q == 2) ? qbcast<2>(uu[j]) : qbcast<3>(uu[j]);
+          const float4 bv = sB4[(4 * j + q) * 4 + L.g];
+          const float4 cv = sC4[(4 * j + q) * 4 + L.g];
+          h[0] = fmaf(__builtin_amdgcn_exp2f(dk * L.A2[0]), h[0], uk * bv.x);
+          h[1] = fmaf(__builtin_amdgcn_exp2f(dk * L.A2[1]), h[1], uk * bv.y);
+          h[2] = fmaf(__builtin_amdgcn_exp2f(dk * L.A2[2]), h[2], uk * bv.z);
+          h[3] = fmaf(__builtin_amdgcn_exp2f(dk * L.A2[3]), h[3], uk * bv.w);
+          pr[q] = fmaf(cv.w, h[3], fmaf(cv.z, h[2], fmaf(cv.y, h[1], cv.x * h[0])));
+        }
+        const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
+        store_y<Tout>(p, L, t0, 4 * j + L.g, nv, yraw, xv[j], zv[j]);
+      }
+      wave_lds_sync();
+    }
+    if (p.h_last && L.dvalid)
+      reinterpret_cast<float4*>(p.h_last + (static_cast<int64_t>(s) * p.dim + L.d) * kN)[L.g] =
+          make_float4(h[0], h[1], h[2], h[3]);
+  } else {
+    // ---------------- time-sliced scan: W waves per chunk of W*kK tokens ----------------
+    const int64_t ntok = L.end - L.start;
+    const int64_t chunk = static_cast<int64_t>(W) * kK;
+    const int64_t nchunks = (ntok + chunk - 1) / chunk;
+    for (int64_t ci = 0; ci < nchunks; ++ci) {
+      const int buf = static_cast<int>(ci & 1);
+      const int64_t t0 = L.start + ci * chunk + static_cast<int64_t>(wave) * kK;
+      const int64_t rem = L.end - t0;
+      const int nv = rem <= 0 ? 0 : (rem < kK ? static_cast<int>(rem) : kK);
+      stage_bc(Bp, Cp, t0, nv, sB, sC, L.lane);
+      float xv[kK / 4], zv[kK / 4], dl[kK / 4], uu[kK / 4];
+      load_slice<Tin>(p, L, t0, nv, xv, zv, dl, uu);
+      wave_lds_sync();
+
+      // phase 1: local scan of the slice from zero; keep Ā and B̄x in registers
+      float ak[kK][kSPL], bk[kK][kSPL];
+      float H[kSPL] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < kK; ++k) {
+        const int j = k >> 2, q = k & 3;
+        const float dk = (q == 0) ? qbcast<0>(dl[j]) : (q == 1) ? qbcast<1>(dl[j]) : (q == 2) ? qbcast<2>(dl[j]) : qbcast<3>(dl[j]);
+        const float uk = (q == 0) ? qbcast<0>(uu[j]) : (q == 1) ? qbcast<1>(uu[j]) : (q == 2) ? qbcast<2>(uu[j]) : qbcast<3>(uu[j]);
+        const float4 bv = sB4[k * 4 + L.g];
+        ak[k][0] = __builtin_amdgcn_exp2f(dk * L.A2[0]);
+        ak[k][1] = __builtin_amdgcn_exp2f(dk * L.A2[1]);
+        ak[k][2] = __builtin_amdgcn_exp2f(dk * L.A2[2]);
+        ak[k][3] = __builtin_amdgcn_exp2f(dk * L.A2[3]);
+        bk[k][0] = uk * bv.x;
+        bk[k][1] = uk * bv.y;
+        bk[k][2] = uk * bv.z;
+        bk[k][3] = uk * bv.w;
+#pragma unroll
+        for (int i = 0; i < kSPL; ++i) H[i] = fmaf(ak[k][i], H[i], bk[k][i]);
+      }
+      // product of the slice's Ā = exp(A * sum of the slice's Δ)
+      float sd = 0.f;
+#pragma unroll
+      for (int j = 0; j < kK / 4; ++j) sd += dl[j];
+      sd = quad_allsum(sd);
+      s_agg[buf][wave][0][L.lane] = make_float4(__builtin_amdgcn_exp2f(L.A2[0] * sd), __builtin_amdgcn_exp2f(L.A2[1] * sd),
+                                                __builtin_amdgcn_exp2f(L.A2[2] * sd), __builtin_amdgcn_exp2f(L.A2[3] * sd));
+      s_agg[buf][wave][1][L.lane] = make_float4(H[0], H[1], H[2], H[3]);
+      __syncthreads();
+
+      // carry-in of this slice: chunk carry folded through the earlier slices
+      float hin[kSPL];
+      if (ci == 0) {
+#pragma unroll
+        for (int i = 0; i < kSPL; ++i) hin[i] = L.hinit[i];
+      } else {
+        const float4 cr = s_carry[buf ^ 1][L.lane];
+        hin[0] = cr.x; hin[1] = cr.y; hin[2] = cr.z; hin[3] = cr.w;
+      }
+      for (int w2 = 0; w2 < wave; ++w2) {
+        const float4 P = s_agg[buf][w2][0][L.lane];
+        const float4 Hs = s_agg[buf][w2][1][L.lane];
+        hin[0] = fmaf(P.x, hin[0], Hs.x);
+        hin[1] = fmaf(P.y, hin[1], Hs.y);
+        hin[2] = fmaf(P.z, hin[2], Hs.z);
+        hin[3] = fmaf(P.w, hin[3], Hs.w);
+      }
+
+      // phase 3: replay the slice from the true carry-in, read out, gate, store
+#pragma unroll
+      for (int i = 0; i < kSPL; ++i) h[i] = hin[i];
+#pragma unroll
+      for (int j = 0; j < kK / 4; ++j) {
+        float pr[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = 4 * j + q;
+          const float4 cv = sC4[k * 4 + L.g];
+#pragma unroll
+          for (int i = 0; i < kSPL; ++i) h[i] = fmaf(ak[k][i], h[i], bk[k][i]);
+          pr[q] = fmaf(cv.w, h[3], fmaf(cv.z, h[2], fmaf(cv.y, h[1], cv.x * h[0])));
+        }
+        if (4 * j < nv) {
+          const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
+          store_y<Tout>(p, L, t0, 4 * j + L.g, nv, yraw, xv[j], zv[j]);
+        }
+      }
+      if (wave == W - 1) s_carry[buf][L.lane] = make_float4(h[0], h[1], h[2], h[3]);
+      wave_lds_sync();
+    }
+    if (wave == W - 1 && p.h_last && L.dvalid)
+      reinterpret_cast<float4*>(p.h_last + (static_cast<int64_t>(s) * p.dim + L.d) * kN)[L.g] =
+          make_float4(h[0], h[1], h[2], h[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode step: one token per sequence; lane = (sequence, channel, state quarter).
+// ---------------------------------------------------------------------------
+struct StepParams {
+  float* state;
+  const void *x, *dt, *z, *B, *C;
+  const float *A, *Dskip, *bias;
+  void* y;
+  int64_t nquads;  // batch * dim
+  int32_t dim;
+};
+
+template <typename Tin>
+__device__ __forceinline__ void load4(const Tin* p, int64_t i, float (&v)[4]);
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, int64_t i, float (&v)[4]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p + i);
+  v[0] = bf_lo(w.x); v[1] = bf_hi(w.x); v[2] = bf_lo(w.y); v[3] = bf_hi(w.y);
+}
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, int64_t i, float (&v)[4]) {
+  const float4 w = *reinterpret_cast<const float4*>(p + i);
+  v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+}
+
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void scan_step_kernel(StepParams p) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t qd = gid >> 2;
+  const int g = static_cast<int>(gid & 3);
+  const bool valid = qd < p.nquads;
+  const int64_t qs = valid ? qd : p.nquads - 1;
+  const int64_t b = qs / p.dim;
+  const int d = static_cast<int>(qs - b * p.dim);
+
+  float4* st = reinterpret_cast<float4*>(p.state + qs * kN) + g;
+  const float4 h4 = *st;
+  const float4 a4 = reinterpret_cast<const float4*>(p.A + static_cast<int64_t>(d) * kN)[g];
+  const float xv = ld_in(static_cast<const Tin*>(p.x), qs);
+  const float dr = ld_in(static_cast<const Tin*>(p.dt), qs);
+  const float zv = ld_in(static_cast<const Tin*>(p.z), qs);
+  float Bv[4], Cv[4];
+  load4<Tin>(static_cast<const Tin*>(p.B), b * kN + 4 * g, Bv);
+  load4<Tin>(static_cast<const Tin*>(p.C), b * kN + 4 * g, Cv);
+
+  const float delta = softplus_f32(dr + p.bias[d]);
+  const float u = delta * xv;
+  float h[4] = {h4.x, h4.y, h4.z, h4.w};
+  const float A2[4] = {a4.x * kLog2e, a4.y * kLog2e, a4.z * kLog2e, a4.w * kLog2e};
+  float pr = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = fmaf(__builtin_amdgcn_exp2f(delta * A2[i]), h[i], u * Bv[i]);
+    pr = fmaf(Cv[i], h[i], pr);
+  }
+  pr = quad_allsum(pr);
+  if (valid) {
+    *st = make_float4(h[0], h[1], h[2], h[3]);
+    if (g == 0) st_out(static_cast<Tout*>(p.y), qs, (pr + p.Dskip[d] * xv) * silu_f32(zv));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t esize(int32_t dt) { return dt == SAMBA_BF16 ? 2 : 4; }
+bool dtype_ok(int32_t dt) { return dt == SAMBA_F32 || dt == SAMBA_BF16; }
+
+struct FwdPlan {
+  int W, tpw, threads, grid;
+  int64_t nseq;
+  FwdParams prm;
+};
+
+samba_status validate_fwd(const samba_scan_fwd_args* a, FwdPlan* plan) {
+  if (!a) return SAMBA_ERR_NULL_ARG;
+  if (a->struct_size != sizeof(samba_scan_fwd_args)) return SAMBA_ERR_BAD_STRUCT;
+  if (a->dstate != kN) return SAMBA_ERR_UNSUPPORTED;
+  if (!dtype_ok(a->in_dtype) || !dtype_ok(a->y_dtype)) return SAMBA_ERR_BAD_DTYPE;
+  if (a->batch < 0 || a->seqlen < 0 || a->dim < 1) return SAMBA_ERR_BAD_SHAPE;
+  const int ts = a->time_slices;
+  if (!(ts == 0 || ts == 1 || ts == 2 || ts == 4 || ts == 8)) return SAMBA_ERR_UNSUPPORTED;
+  int64_t nseq = a->batch;
+  if (a->cu_seqlens) {
+    if (a->batch != 1 || a->nseq < 1) return SAMBA_ERR_BAD_SHAPE;
+    nseq = a->nseq;
+    if (!aligned(a->cu_seqlens, 4)) return SAMBA_ERR_MISALIGNED;
+  }
+  const int64_t tokens = static_cast<int64_t>(a->batch) * a->seqlen;
+  if (!a->A || !a->D || !a->dt_bias) return SAMBA_ERR_NULL_ARG;
+  if (tokens > 0 && (!a->x || !a->dt || !a->z || !a->B || !a->C || !a->y)) return SAMBA_ERR_NULL_ARG;
+  const size_t ei = esize(a->in_dtype), eo = esize(a->y_dtype);
+  if (!aligned(a->x, ei) || !aligned(a->dt, ei) || !aligned(a->z, ei) || !aligned(a->y, eo)) return SAMBA_ERR_MISALIGNED;
+  if (!aligned(a->B, 16) || !aligned(a->C, 16) || !aligned(a->A, 16) || !aligned(a->h0, 16) ||
+      !aligned(a->h_last, 16) || !aligned(a->D, 4) || !aligned(a->dt_bias, 4))
+    return SAMBA_ERR_MISALIGNED;
+  // outputs must not overlap inputs (h_last == h0 exactly is allowed: in-place carry)
+  const size_t n_td = static_cast<size_t>(tokens) * a->dim;
+  const size_t n_state = static_cast<size_t>(nseq) * a->dim * kN * 4;
+  const void* ins[] = {a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias, a->h0, a->cu_seqlens};
+  const size_t insz[] = {n_td * ei, n_td * ei, n_td * ei, static_cast<size_t>(tokens) * kN * ei,
+                         static_cast<size_t>(tokens) * kN * ei, static_cast<size_t>(a->dim) * kN * 4,
+                         static_cast<size_t>(a->dim) * 4, static_cast<size_t>(a->dim) * 4, n_state,
+                         a->cu_seqlens ? static_cast<size_t>(nseq + 1) * 4 : 0};
+  for (int i = 0; i < 10; ++i) {
+    if (overlap(a->y, n_td * eo, ins[i], insz[i])) return SAMBA_ERR_ALIASING;
+    if (i != 8 && overlap(a->h_last, n_state, ins[i], insz[i])) return SAMBA_ERR_ALIASING;
+  }
+  if (a->h_last && a->h0 && a->h_last != a->h0 && overlap(a->h_last, n_state, a->h0, n_state))
+    return SAMBA_ERR_ALIASING;
+  if (overlap(a->y, n_td * eo, a->h_last, n_state)) return SAMBA_ERR_ALIASING;
+
+  if (!plan) return SAMBA_OK;
+  const int ntiles = (a->dim + kCPW - 1) / kCPW;
+  int W = ts;
+  if (W == 0) {
+    // Enough waves for two per SIMD (4 SIMDs per CU) without slicing?  Otherwise
+    // split time, but never into slices that the average sequence cannot fill.
+    const int64_t target = static_cast<int64_t>(device_cu_count()) * 8;
+    const int64_t base = nseq * ntiles;
+    const int64_t avg_len = nseq > 0 ? tokens / nseq : 0;
+    W = 1;
+    while (W < 8 && base * W < target && static_cast<int64_t>(W) * 2 * kK <= avg_len) W *= 2;
+  }
+  const int tpw = (W == 1) ? 4 : 1;
+  const int ngroups = (ntiles + tpw - 1) / tpw;
+  FwdParams& p = plan->prm;
+  p.x = a->x; p.dt = a->dt; p.z = a->z; p.B = a->B; p.C = a->C;
+  p.A = a->A; p.Dskip = a->D; p.bias = a->dt_bias;
+  p.h0 = a->h0; p.h_last = a->h_last; p.y = a->y;
+  p.cu = a->cu_seqlens;
+  p.total_tokens = tokens;
+  p.seqlen = a->seqlen;
+  p.dim = a->dim;
+  p.ntiles = ntiles;
+  p.tiles_per_wg = tpw;
+  p.ngroups = ngroups;
+  const int64_t nblocks = nseq * ngroups;
+  if (nblocks > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  p.nblocks = static_cast<int32_t>(nblocks);
+  plan->W = W;
+  plan->tpw = tpw;
+  plan->threads = 64 * W * tpw;
+  plan->grid = static_cast<int>(nblocks);
+  plan->nseq = nseq;
+  return SAMBA_OK;
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_fwd(const FwdPlan& pl, hipStream_t st) {
+  const dim3 grid(pl.grid), block(pl.threads);
+  switch (pl.W) {
+    case 1: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 1, 4>), grid, block, 0, st, pl.prm); break;
+    case 2: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 2, 1>), grid, block, 0, st, pl.prm); break;
+    case 4: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 4, 1>), grid, block, 0, st, pl.prm); break;
+    default: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 8, 1>), grid, block, 0, st, pl.prm); break;
+  }
+  return hipGetLastError();
+}
+
+samba_status validate_step(const samba_scan_step_args* a) {
+  if (!a) return SAMBA_ERR_NULL_ARG;
+  if (a->struct_size != sizeof(samba_scan_step_args)) return SAMBA_ERR_BAD_STRUCT;
+  if (a->dstate != kN) return SAMBA_ERR_UNSUPPORTED;
+  if (!dtype_ok(a->in_dtype) || !dtype_ok(a->y_dtype)) return SAMBA_ERR_BAD_DTYPE;
+  if (a->batch < 0 || a->dim < 1) return SAMBA_ERR_BAD_SHAPE;
+  if (!a->A || !a->D || !a->dt_bias) return SAMBA_ERR_NULL_ARG;
+  if (a->batch > 0 && (!a->state || !a->x || !a->dt || !a->z || !a->B || !a->C || !a->y)) return SAMBA_ERR_NULL_ARG;
+  const size_t ei = esize(a->in_dtype), eo = esize(a->y_dtype);
+  if (!aligned(a->state, 16) || !aligned(a->B, 16) || !aligned(a->C, 16) || !aligned(a->A, 16) ||
+      !aligned(a->x, ei) || !aligned(a->dt, ei) || !aligned(a->z, ei) || !aligned(a->y, eo) ||
+      !aligned(a->D, 4) || !aligned(a->dt_bias, 4))
+    return SAMBA_ERR_MISALIGNED;
+  const size_t nbd = static_cast<size_t>(a->batch) * a->dim;
+  const size_t n_state = nbd * kN * 4;
+  const void* ins[] = {a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias};
+  const size_t insz[] = {nbd * ei, nbd * ei, nbd * ei, static_cast<size_t>(a->batch) * kN * ei,
+                         static_cast<size_t>(a->batch) * kN * ei, static_cast<size_t>(a->dim) * kN * 4,
+                         static_cast<size_t>(a->dim) * 4, static_cast<size_t>(a->dim) * 4};
+  for (int i = 0; i < 8; ++i) {
+    if (overlap(a->y, nbd * eo, ins[i], insz[i])) return SAMBA_ERR_ALIASING;
+    if (overlap(a->state, n_state, ins[i], insz[i])) return SAMBA_ERR_ALIASING;
+  }
+  if (overlap(a->y, nbd * eo, a->state, n_state)) return SAMBA_ERR_ALIASING;
+  return SAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+samba_status samba_scan_fwd(const samba_scan_fwd_args* args, void* stream) {
+  FwdPlan pl;
+  const samba_status st = validate_fwd(args, &pl);
+  if (st != SAMBA_OK) return st;
+  if (pl.grid == 0) return SAMBA_OK;  // no sequences
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (args->in_dtype == SAMBA_BF16)
+    e = (args->y_dtype == SAMBA_BF16) ? launch_fwd<uint16_t, uint16_t>(pl, s) : launch_fwd<uint16_t, float>(pl, s);
+  else
+    e = (args->y_dtype == SAMBA_BF16) ? launch_fwd<float, uint16_t>(pl, s) : launch_fwd<float, float>(pl, s);
+  return e == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
+}
+
+samba_status samba_scan_fwd_plan(const samba_scan_fwd_args* args, int32_t* time_slices, int32_t* workgroups,
+                                 int32_t* threads_per_workgroup) {
+  FwdPlan pl;
+  const samba_status st = validate_fwd(args, &pl);
+  if (st != SAMBA_OK) return st;
+  if (time_slices) *time_slices = pl.W;
+  if (workgroups) *workgroups = pl.grid;
+  if (threads_per_workgroup) *threads_per_workgroup = pl.threads;
+  return SAMBA_OK;
+}
+
+samba_status samba_scan_step(const samba_scan_step_args* args, void* stream) {
+  const samba_status st = validate_step(args);
+  if (st != SAMBA_OK) return st;
+  const int64_t nquads = static_cast<int64_t>(args->batch) * args->dim;
+  if (nquads == 0) return SAMBA_OK;
+  const int64_t threads = nquads * 4;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  StepParams p;
+  p.state = args->state;
+  p.x = args->x; p.dt = args->dt; p.z = args->z; p.B = args->B; p.C = args->C;
+  p.A = args->A; p.Dskip = args->D; p.bias = args->dt_bias;
+  p.y = args->y;
+  p.nquads = nquads;
+  p.dim = args->dim;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  if (args->in_dtype == SAMBA_BF16) {
+    if (args->y_dtype == SAMBA_BF16) hipLaunchKernelGGL((scan_step_kernel<uint16_t, uint16_t>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_step_kernel<uint16_t, float>), grid, block, 0, s, p);
+  } else {
+    if (args->y_dtype == SAMBA_BF16) hipLaunchKernelGGL((scan_step_kernel<float, uint16_t>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((scan_step_kernel<float, float>), grid, block, 0, s, p);
+  }
+  return hipGetLastError() == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
+}
+
+const char* samba_status_string(int status) {
+  switch (status) {
+    case SAMBA_OK: return "ok";
+    case SAMBA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case SAMBA_ERR_BAD_SHAPE: return "invalid or inconsistent sizes";
+    case SAMBA_ERR_BAD_DTYPE: return "unsupported dtype code";
+    case SAMBA_ERR_MISALIGNED: return "pointer misaligned";
+    case SAMBA_ERR_ALIASING: return "an output overlaps an input";
+    case SAMBA_ERR_UNSUPPORTED: return "unsupported configuration (dstate must be 16; time_slices 0/1/2/4/8)";
+    case SAMBA_ERR_BAD_STRUCT: return "argument struct size mismatch (header/library version skew)";
+    case SAMBA_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int samba_scan_abi_version(void) { return SAMBA_SCAN_ABI_VERSION; }
+
+}  // extern "C"
