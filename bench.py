@@ -68,7 +68,7 @@ def read_traffic():
     return t.get("bytes_per_launch")
 
 
-def bench_prefill(steps: int, warmup: int):
+def bench_prefill(steps: int, warmup: int, time_slices: int = 0):
     import torch
     from selective_state_space_05_amd import inputs as I
     from selective_state_space_05_amd import scan as S
@@ -88,11 +88,11 @@ def bench_prefill(steps: int, warmup: int):
     for i in range(n):
         sl = slice(i * cl, (i + 1) * cl)
         a = S.fwd_args(*(inp[k][sl].view(1, cl, -1) for k in ("x", "dt", "z", "B", "C")), inp["A"], inp["D"],
-                       inp["dt_bias"], y=y[sl].view(1, cl, D), h0=prev, h_last=hb[i % 2])
+                       inp["dt_bias"], y=y[sl].view(1, cl, D), h0=prev, h_last=hb[i % 2], time_slices=time_slices)
         args.append(a)
         prev = hb[i % 2]
     plan = S.fwd_plan(*(inp[k][:cl].view(1, cl, -1) for k in ("x", "dt", "z", "B", "C")), inp["A"], inp["D"],
-                      inp["dt_bias"], y=y[:cl].view(1, cl, D), h0=h0, h_last=hb[0])
+                      inp["dt_bias"], y=y[:cl].view(1, cl, D), h0=h0, h_last=hb[0], time_slices=time_slices)
     sh = ctypes.c_void_p(stream.cuda_stream)
 
     def one_step():
@@ -190,6 +190,16 @@ def bench_decode(steps: int = 65536, ring: int = 256):
     return out
 
 
+def copy_probe(nbytes: int = 512 << 20, reps: int = 3):
+    """A plain device-to-device copy of known size; its FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").uniform_()
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(target_s: float = 12.0):
     """The fp64 oracle on a bounded sample of the same prefill (first 16384-token call, some channels)."""
     import numpy as np
@@ -230,13 +240,18 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=65536)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--time-slices", type=int, default=0, help="force the prefill's waves per time chunk (0 = auto)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 512 MiB device copy (untimed), the reference kernel for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
-    pf = bench_prefill(args.steps, args.warmup)
+    pf = bench_prefill(args.steps, args.warmup, args.time_slices)
+    if args.copy_probe:
+        copy_probe()
     achieved = SLOTS_PER_TD * pf["launch_td"] / (pf["launch_ms"] * 1e-3) / 1e12
     traffic = read_traffic()
     line = {

@@ -56,7 +56,7 @@ typedef enum {
   SAMBA_ERR_BAD_DTYPE = 3,     /* in_dtype / y_dtype not a samba_dtype value */
   SAMBA_ERR_MISALIGNED = 4,    /* a pointer violates its alignment rule (below) */
   SAMBA_ERR_ALIASING = 5,      /* an output overlaps an input it must not overlap */
-  SAMBA_ERR_UNSUPPORTED = 6,   /* dstate != 16, or time_slices not 0/1/2/4/8 */
+  SAMBA_ERR_UNSUPPORTED = 6,   /* dstate != 16, or time_slices not 0/1/2/4/8/16 */
   SAMBA_ERR_BAD_STRUCT = 7,    /* struct_size does not match this header */
   SAMBA_ERR_HIP = 8            /* the HIP runtime refused the launch */
 } samba_status;
@@ -82,7 +82,7 @@ typedef enum { SAMBA_F32 = 0, SAMBA_BF16 = 1 } samba_dtype;
  * element size.  h_last may equal h0 exactly (in-place carry); any other
  * overlap of an output (y, h_last) with an input is SAMBA_ERR_ALIASING.
  * time_slices: 0 lets the library choose how many waves split each time chunk
- * of one channel tile (1, 2, 4 or 8); other values force it (testing and
+ * of one channel tile (1, 2, 4, 8 or 16); other values force it (testing and
  * tuning; results agree to fp32 rounding, and are bitwise reproducible for a
  * given choice).
  */

@@ -41,29 +41,25 @@ namespace {
 constexpr int kN = 16;         // states per channel
 constexpr int kSPL = 4;        // states per lane
 constexpr int kCPW = 16;       // channels per wave
-constexpr int kK = 16;         // tokens per wave slice (multiple of 4)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
 // ---------------------------------------------------------------------------
-// element access
+// element access and conversion
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float ld_in(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ld_in(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
-  uint32_t b = __float_as_uint(v);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((b >> 16) | 0x40u);  // keep NaN a NaN
-  b += 0x7fffu + ((b >> 16) & 1u);                                                     // round to nearest even
-  return static_cast<uint16_t>(b >> 16);
-}
-__device__ __forceinline__ void st_out(float* p, int64_t i, float v) { p[i] = v; }
-__device__ __forceinline__ void st_out(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
-
+__device__ __forceinline__ float widen(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+__device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (the gfx950 conversion instruction)
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+__device__ __forceinline__ void st_out(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st_out(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 
 // ---------------------------------------------------------------------------
 // scalar maps
@@ -97,6 +93,15 @@ constexpr int kQXor1 = 0xB1;  // [1,0,3,2]
 constexpr int kQXor2 = 0x4E;  // [2,3,0,1]
 template <int Q>
 __device__ __forceinline__ float qbcast(float v) { return qperm<Q * 0x55>(v); }  // [Q,Q,Q,Q]
+__device__ __forceinline__ float qbcast_dyn(float v, int q) {
+  // q is a compile-time constant after unrolling; the switch folds away
+  switch (q) {
+    case 0: return qbcast<0>(v);
+    case 1: return qbcast<1>(v);
+    case 2: return qbcast<2>(v);
+    default: return qbcast<3>(v);
+  }
+}
 
 // Lane g holds partial sums p[0..3] for the four tokens of a group; returns, on
 // lane g, the quad's total for token g.
@@ -124,32 +129,54 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ---------------------------------------------------------------------------
-// B/C staging: kK tokens x 16 states of B and of C -> fp32 LDS rows.
-// Rows at or beyond `nv` valid tokens are zero-filled.
+// buffer access: a wave-uniform resource (base, byte count) in SGPRs plus a
+// 32-bit per-lane byte offset.  Reads at or beyond the byte count return 0 and
+// writes there are dropped, so a resource that ends at the current sequence's
+// last token makes ragged tails free of per-lane predicates.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void stage_bc(const uint16_t* B, const uint16_t* C, int64_t t0, int nv,
-                                         float* sB, float* sC, int lane) {
-  static_assert(kK == 16, "one 16-byte vector per lane covers 16 rows of B and C");
-  const int which = lane >> 5;
-  const int r = (lane & 31) >> 1;
-  const int half = lane & 1;
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (r < nv) v = *reinterpret_cast<const uint4*>((which ? C : B) + (t0 + r) * kN + half * 8);
-  float* dst = (which ? sC : sB) + r * kN + half * 8;
-  reinterpret_cast<float4*>(dst)[0] = make_float4(bf_lo(v.x), bf_hi(v.x), bf_lo(v.y), bf_hi(v.y));
-  reinterpret_cast<float4*>(dst)[1] = make_float4(bf_lo(v.z), bf_hi(v.z), bf_lo(v.w), bf_hi(v.w));
-}
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped, unswizzled) buffer
 
-__device__ __forceinline__ void stage_bc(const float* B, const float* C, int64_t t0, int nv, float* sB,
-                                         float* sC, int lane) {
-  const int r = lane >> 2;
-  const int qt = lane & 3;
-#pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < nv) v = *reinterpret_cast<const float4*>((which ? C : B) + (t0 + r) * kN + qt * 4);
-    reinterpret_cast<float4*>((which ? sC : sB) + r * kN)[qt] = v;
+template <typename T>
+__device__ __forceinline__ rsrc_t make_rsrc_bytes(const T* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                          kRsrcWord3);
+}
+// Resource over `rows` rows of `row_elems` elements; rows <= 0 gives an empty
+// resource, and byte counts beyond 32 bits saturate (offsets stay 32-bit).
+// 32-bit arithmetic throughout, so the wave-uniform values stay in SGPRs.
+template <typename T>
+__device__ __forceinline__ rsrc_t make_rsrc_rows(const T* base, int rows, uint32_t row_elems) {
+  const uint32_t row_bytes = row_elems * static_cast<uint32_t>(sizeof(T));
+  const uint32_t max_rows = 0xffffffffu / row_bytes;
+  const uint32_t bytes = rows <= 0 ? 0u
+                         : (static_cast<uint32_t>(rows) >= max_rows ? 0xffffffffu : static_cast<uint32_t>(rows) * row_bytes);
+  return make_rsrc_bytes(base, bytes);
+}
+__device__ __forceinline__ void bload(rsrc_t r, uint32_t off, uint16_t& v) {
+  v = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ void bload(rsrc_t r, uint32_t off, float& v) {
+  v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <int NW>
+__device__ __forceinline__ void bload_words(rsrc_t r, uint32_t off, uint32_t (&w)[NW]) {
+  static_assert(NW == 1 || NW == 2 || NW == 4, "4, 8 or 16 bytes");
+  if constexpr (NW == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (NW == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
   }
+}
+__device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, float v, float*) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, float v, uint16_t*) {
+  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
 }
 
 // Block index -> logical index so that consecutive logical blocks (adjacent
@@ -177,7 +204,21 @@ struct FwdParams {
   int32_t nblocks;       // nseq * ngroups
 };
 
-// Per-lane setup shared by both prefill variants.
+// ---------------------------------------------------------------------------
+// One slice = K consecutive tokens (K = 8 or 16) of a 16-channel tile.
+// Lane g of a quad owns tokens 4j+g (j < K/4) for x, dt, z, y.  B and C rows
+// of the slice (K x 16 values each) are spread over the wave, E = K/4 values of
+// each per lane, and widened once into fp32 LDS rows (stage_bc).
+// ---------------------------------------------------------------------------
+template <typename Tin, int K>
+struct RawSlice {
+  static constexpr int kE = K / 4;                                            // B (and C) values per lane
+  static constexpr int kWords = kE * static_cast<int>(sizeof(Tin)) / 4;       // as 32-bit words
+  Tin x[K / 4], dt[K / 4], z[K / 4];
+  uint32_t bw[kWords], cw[kWords];
+};
+
+template <typename Tin, typename Tout, int K>
 struct LaneCtx {
   int lane, g, c, d;
   bool dvalid;
@@ -185,67 +226,156 @@ struct LaneCtx {
   float A2[kSPL];
   float dsk, bias;
   float hinit[kSPL];
+  uint32_t in_off[K / 4];   // byte offsets of this lane's x/dt/z elements from a slice's first row
+  uint32_t out_off[K / 4];  // same for y
+  uint32_t bc_off;          // byte offset of this lane's B/C values from a slice's first row
+  int bc_lds;               // float index of those values in an LDS [K][16] tile
 };
 
-template <typename Tin>
-__device__ __forceinline__ void load_slice(const FwdParams& p, const LaneCtx& L, int64_t t0, int nv,
-                                           float (&xv)[kK / 4], float (&zv)[kK / 4], float (&dl)[kK / 4],
-                                           float (&uu)[kK / 4]) {
-  const Tin* x = static_cast<const Tin*>(p.x);
-  const Tin* dt = static_cast<const Tin*>(p.dt);
-  const Tin* z = static_cast<const Tin*>(p.z);
+// Issue the loads of the slice starting at token row t0 (all buffer loads).
+template <typename Tin, typename Tout, int K>
+__device__ __forceinline__ void load_raw(const FwdParams& p, const LaneCtx<Tin, Tout, K>& L, int64_t t0,
+                                         RawSlice<Tin, K>& r) {
+  // tokens left in this sequence (wave-uniform; a sequence is < 2^31 tokens)
+  const int rem = static_cast<int>(L.end - t0 > 0x7fffffff ? 0x7fffffff : (L.end - t0 < 0 ? 0 : L.end - t0));
+  const int64_t row0 = t0 * p.dim;
+  const uint32_t dim = static_cast<uint32_t>(p.dim);
+  const rsrc_t rx = make_rsrc_rows(static_cast<const Tin*>(p.x) + row0, rem, dim);
+  const rsrc_t rd = make_rsrc_rows(static_cast<const Tin*>(p.dt) + row0, rem, dim);
+  const rsrc_t rz = make_rsrc_rows(static_cast<const Tin*>(p.z) + row0, rem, dim);
 #pragma unroll
-  for (int j = 0; j < kK / 4; ++j) {
-    const int kk = 4 * j + L.g;
-    float xr = 0.f, dr = 0.f, zr = 0.f;
-    if (L.dvalid && kk < nv) {
-      const int64_t idx = (t0 + kk) * p.dim + L.d;
-      xr = ld_in(x, idx);
-      dr = ld_in(dt, idx);
-      zr = ld_in(z, idx);
+  for (int j = 0; j < K / 4; ++j) {
+    bload(rx, L.in_off[j], r.x[j]);
+    bload(rd, L.in_off[j], r.dt[j]);
+    bload(rz, L.in_off[j], r.z[j]);
+  }
+  const rsrc_t rb = make_rsrc_rows(static_cast<const Tin*>(p.B) + t0 * kN, rem, kN);
+  const rsrc_t rc = make_rsrc_rows(static_cast<const Tin*>(p.C) + t0 * kN, rem, kN);
+  bload_words(rb, L.bc_off, r.bw);
+  bload_words(rc, L.bc_off, r.cw);
+}
+
+template <typename Tin, int K>
+__device__ __forceinline__ void widen_words(const uint32_t (&w)[RawSlice<Tin, K>::kWords], float (&v)[K / 4]) {
+  if constexpr (sizeof(Tin) == 2) {
+#pragma unroll
+    for (int i = 0; i < RawSlice<Tin, K>::kWords; ++i) {
+      v[2 * i] = bf_lo(w[i]);
+      v[2 * i + 1] = bf_hi(w[i]);
     }
-    xv[j] = xr;
-    zv[j] = zr;
-    const float delta = (L.dvalid && kk < nv) ? softplus_f32(dr + L.bias) : 0.0f;
-    dl[j] = delta;
-    uu[j] = delta * xr;
+  } else {
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) v[i] = __uint_as_float(w[i]);
   }
 }
 
-template <typename Tout>
-__device__ __forceinline__ void store_y(const FwdParams& p, const LaneCtx& L, int64_t t0, int kk, int nv,
-                                        float yraw, float xr, float zr) {
-  if (L.dvalid && kk < nv) {
-    const float yv = (yraw + L.dsk * xr) * silu_f32(zr);
-    st_out(static_cast<Tout*>(p.y), (t0 + kk) * p.dim + L.d, yv);
+template <int E>
+__device__ __forceinline__ void lds_put(float* dst, const float (&v)[E]) {
+  if constexpr (E == 2) {
+    *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
   }
+}
+
+template <typename Tin, typename Tout, int K>
+__device__ __forceinline__ void stage_bc(const RawSlice<Tin, K>& r, const LaneCtx<Tin, Tout, K>& L, float* sB,
+                                         float* sC) {
+  float v[K / 4];
+  widen_words<Tin, K>(r.bw, v);
+  lds_put<K / 4>(sB + L.bc_lds, v);
+  widen_words<Tin, K>(r.cw, v);
+  lds_put<K / 4>(sC + L.bc_lds, v);
+}
+
+// Widen a slice's own tokens and discretise: Δ = softplus(dt + bias), u = Δ x.
+template <typename Tin, typename Tout, int K>
+__device__ __forceinline__ void decode_raw(const RawSlice<Tin, K>& r, const LaneCtx<Tin, Tout, K>& L, int nv,
+                                           float (&xv)[K / 4], float (&zv)[K / 4], float (&dl)[K / 4],
+                                           float (&uu)[K / 4]) {
+#pragma unroll
+  for (int j = 0; j < K / 4; ++j) {
+    const bool ok = L.dvalid && (4 * j + L.g) < nv;
+    const float xr = widen(r.x[j]);
+    xv[j] = xr;
+    zv[j] = widen(r.z[j]);
+    const float delta = ok ? softplus_f32(widen(r.dt[j]) + L.bias) : 0.0f;
+    dl[j] = delta;
+    uu[j] = ok ? delta * xr : 0.0f;
+  }
+}
+
+// Share each lane's (Δ, Δx) with its quad through LDS: lane g of channel c
+// writes token 4j+g's pair; every lane of the quad then reads the four pairs of
+// group j with two 16-byte reads (no cross-lane VALU work).
+template <int K>
+__device__ __forceinline__ void publish_du(float4 (*du)[kCPW][2], int c, int g, const float (&dl)[K / 4],
+                                           const float (&uu)[K / 4]) {
+#pragma unroll
+  for (int j = 0; j < K / 4; ++j)
+    reinterpret_cast<float2*>(du[j][c])[g] = make_float2(dl[j], uu[j]);
+}
+__device__ __forceinline__ void fetch_du(const float4 (*du)[kCPW][2], int j, int c, float (&dk)[4], float (&uk)[4]) {
+  const float4 a = du[j][c][0], b = du[j][c][1];
+  dk[0] = a.x; uk[0] = a.y; dk[1] = a.z; uk[1] = a.w;
+  dk[2] = b.x; uk[2] = b.y; dk[3] = b.z; uk[3] = b.w;
+}
+
+template <int K>
+__device__ __forceinline__ int slice_len(int64_t rem) {
+  return rem <= 0 ? 0 : (rem < K ? static_cast<int>(rem) : K);
+}
+
+// y of token 4j+g: skip, gate, round, store (tokens past the sequence end are
+// outside the resource and dropped by the hardware).
+template <typename Tin, typename Tout, int K>
+__device__ __forceinline__ void store_y(const LaneCtx<Tin, Tout, K>& L, rsrc_t ry, int j, float yraw, float xr,
+                                        float zr) {
+  const float yv = (yraw + L.dsk * xr) * silu_f32(zr);
+  if (L.dvalid) bstore(ry, L.out_off[j], yv, static_cast<Tout*>(nullptr));
 }
 
 // ---------------------------------------------------------------------------
 // Prefill kernel.  W = waves splitting each time chunk (1 = plain sequential
-// scan); TPW = channel tiles per workgroup (W == 1 only).
+// scan); TPW = channel tiles per workgroup (W == 1 only); K = tokens per wave
+// slice (8 or 16).
 // ---------------------------------------------------------------------------
-template <typename Tin, typename Tout, int W, int TPW>
+template <typename Tin, typename Tout, int W, int TPW, int K>
 __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
   static_assert(W == 1 || TPW == 1, "time slices and tile packing are exclusive");
+  static_assert(K == 8 || K == 16, "slice length");
   constexpr int kWaves = W * TPW;
-  __shared__ float4 s_bc[kWaves][2][kK * kN / 4];                  // per-wave staged B, C (fp32)
+  __shared__ float4 s_bc[kWaves][2][K * kN / 4];                   // per-wave staged B, C (fp32)
+  __shared__ float4 s_du[kWaves][K / 4][kCPW][2];                  // per-wave (Δ, Δx) of each group's 4 tokens
   __shared__ float4 s_agg[(W > 1) ? 2 : 1][W][2][64];              // slice (P, H) pairs, double buffered
   __shared__ float4 s_carry[(W > 1) ? 2 : 1][64];                  // chunk carry, double buffered
 
-  const int wave = threadIdx.x >> 6;
+  // wave index, declared wave-uniform so that everything derived from it lives in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int logical = xcd_remap(blockIdx.x, p.nblocks);
   const int s = logical / p.ngroups;
   const int grp = logical - s * p.ngroups;
   const int tile = (W == 1) ? grp * TPW + wave : grp;
   if (W == 1 && tile >= p.ntiles) return;  // whole wave idle (no barriers in the W == 1 path)
 
-  LaneCtx L;
+  LaneCtx<Tin, Tout, K> L;
   L.lane = threadIdx.x & 63;
   L.g = L.lane & 3;
   L.c = L.lane >> 2;
   L.d = tile * kCPW + L.c;
   L.dvalid = L.d < p.dim;
+  {
+    const uint32_t dim = static_cast<uint32_t>(p.dim);
+    const uint32_t e0 = static_cast<uint32_t>(L.g) * dim + static_cast<uint32_t>(L.d);
+#pragma unroll
+    for (int j = 0; j < K / 4; ++j) {
+      L.in_off[j] = (e0 + static_cast<uint32_t>(j) * 4u * dim) * static_cast<uint32_t>(sizeof(Tin));
+      L.out_off[j] = (e0 + static_cast<uint32_t>(j) * 4u * dim) * static_cast<uint32_t>(sizeof(Tout));
+    }
+    constexpr int E = K / 4, lanes_per_row = kN / E;
+    L.bc_lds = (L.lane / lanes_per_row) * kN + (L.lane % lanes_per_row) * E;
+    L.bc_off = static_cast<uint32_t>(L.bc_lds) * static_cast<uint32_t>(sizeof(Tin));
+  }
   const int dc = L.dvalid ? L.d : p.dim - 1;
   if (p.cu) {
     int64_t a = p.cu[s], b = p.cu[s + 1];
@@ -273,71 +403,102 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
     L.hinit[0] = L.hinit[1] = L.hinit[2] = L.hinit[3] = 0.f;
   }
 
-  const Tin* Bp = static_cast<const Tin*>(p.B);
-  const Tin* Cp = static_cast<const Tin*>(p.C);
   float* sB = reinterpret_cast<float*>(s_bc[wave][0]);
   float* sC = reinterpret_cast<float*>(s_bc[wave][1]);
   const float4* sB4 = s_bc[wave][0];
   const float4* sC4 = s_bc[wave][1];
   float h[kSPL] = {L.hinit[0], L.hinit[1], L.hinit[2], L.hinit[3]};
+  Tout* const yout = static_cast<Tout*>(p.y);
 
   if constexpr (W == 1) {
     // ---------------- sequential scan over the whole sequence ----------------
-    for (int64_t t0 = L.start; t0 < L.end; t0 += kK) {
-      const int64_t rem = L.end - t0;
-      const int nv = rem < kK ? static_cast<int>(rem) : kK;
-      stage_bc(Bp, Cp, t0, nv, sB, sC, L.lane);
-      float xv[kK / 4], zv[kK / 4], dl[kK / 4], uu[kK / 4];
-      load_slice<Tin>(p, L, t0, nv, xv, zv, dl, uu);
+    // One slice of K tokens per step; the next slice's loads are issued first
+    // (into the other register set: the loop body is instantiated twice).
+    // Loop bookkeeping stays in 32-bit scalars (a sequence is < 2^31 tokens):
+    // 64-bit compares would go through VGPRs and force waits on in-flight loads.
+    const int ntok = static_cast<int>(L.end - L.start);
+    auto step = [&](int i0, const RawSlice<Tin, K>& cur, RawSlice<Tin, K>& nxt) {
+      const int64_t t0 = L.start + i0;
+      const int nv = ntok - i0 < K ? ntok - i0 : K;
+      load_raw<Tin, Tout, K>(p, L, t0 + K, nxt);
+      stage_bc<Tin, Tout, K>(cur, L, sB, sC);
+      float xv[K / 4], zv[K / 4], dl[K / 4], uu[K / 4];
+      decode_raw<Tin, Tout, K>(cur, L, nv, xv, zv, dl, uu);
+      publish_du<K>(s_du[wave], L.c, L.g, dl, uu);
+      const rsrc_t ry = make_rsrc_rows(yout + t0 * p.dim, ntok - i0, static_cast<uint32_t>(p.dim));
       wave_lds_sync();
 #pragma unroll
-      for (int j = 0; j < kK / 4; ++j) {
+      for (int j = 0; j < K / 4; ++j) {
         if (4 * j >= nv) break;
+        float4 bv[4], cv[4];
+        float dk[4], uk[4];
+        fetch_du(s_du[wave], j, L.c, dk, uk);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bv[q] = sB4[(4 * j + q) * 4 + L.g];
+          cv[q] = sC4[(4 * j + q) * 4 + L.g];
+        }
         float pr[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float dk = (q == 0) ? qbcast<0>(dl[j]) : (q == 1) ? qbcast<1>(dl[j]) : (q == 2) ? qbcast<2>(dl[j]) : qbcast<3>(dl[j]);
-          const float uk = (q == 0) ? qbcast<0>(uu[j]) : (q == 1) ? qbcast<1>(uu[j]) : (q == 2) ? qbcast<2>(uu[j]) : qbcast<3>(uu[j]);
-          const float4 bv = sB4[(4 * j + q) * 4 + L.g];
-          const float4 cv = sC4[(4 * j + q) * 4 + L.g];
-          h[0] = fmaf(__builtin_amdgcn_exp2f(dk * L.A2[0]), h[0], uk * bv.x);
-          h[1] = fmaf(__builtin_amdgcn_exp2f(dk * L.A2[1]), h[1], uk * bv.y);
-          h[2] = fmaf(__builtin_amdgcn_exp2f(dk * L.A2[2]), h[2], uk * bv.z);
-          h[3] = fmaf(__builtin_amdgcn_exp2f(dk * L.A2[3]), h[3], uk * bv.w);
-          pr[q] = fmaf(cv.w, h[3], fmaf(cv.z, h[2], fmaf(cv.y, h[1], cv.x * h[0])));
+          h[0] = fmaf(__builtin_amdgcn_exp2f(dk[q] * L.A2[0]), h[0], uk[q] * bv[q].x);
+          h[1] = fmaf(__builtin_amdgcn_exp2f(dk[q] * L.A2[1]), h[1], uk[q] * bv[q].y);
+          h[2] = fmaf(__builtin_amdgcn_exp2f(dk[q] * L.A2[2]), h[2], uk[q] * bv[q].z);
+          h[3] = fmaf(__builtin_amdgcn_exp2f(dk[q] * L.A2[3]), h[3], uk[q] * bv[q].w);
+          pr[q] = fmaf(cv[q].w, h[3], fmaf(cv[q].z, h[2], fmaf(cv[q].y, h[1], cv[q].x * h[0])));
         }
         const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
-        store_y<Tout>(p, L, t0, 4 * j + L.g, nv, yraw, xv[j], zv[j]);
+        store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
       }
       wave_lds_sync();
+    };
+    RawSlice<Tin, K> ra, rb;
+    load_raw<Tin, Tout, K>(p, L, L.start, ra);
+    for (int i0 = 0; i0 < ntok; i0 += 2 * K) {
+      step(i0, ra, rb);
+      if (i0 + K < ntok) step(i0 + K, rb, ra);
     }
     if (p.h_last && L.dvalid)
       reinterpret_cast<float4*>(p.h_last + (static_cast<int64_t>(s) * p.dim + L.d) * kN)[L.g] =
           make_float4(h[0], h[1], h[2], h[3]);
   } else {
-    // ---------------- time-sliced scan: W waves per chunk of W*kK tokens ----------------
-    const int64_t ntok = L.end - L.start;
-    const int64_t chunk = static_cast<int64_t>(W) * kK;
-    const int64_t nchunks = (ntok + chunk - 1) / chunk;
-    for (int64_t ci = 0; ci < nchunks; ++ci) {
-      const int buf = static_cast<int>(ci & 1);
-      const int64_t t0 = L.start + ci * chunk + static_cast<int64_t>(wave) * kK;
-      const int64_t rem = L.end - t0;
-      const int nv = rem <= 0 ? 0 : (rem < kK ? static_cast<int>(rem) : kK);
-      stage_bc(Bp, Cp, t0, nv, sB, sC, L.lane);
-      float xv[kK / 4], zv[kK / 4], dl[kK / 4], uu[kK / 4];
-      load_slice<Tin>(p, L, t0, nv, xv, zv, dl, uu);
+    // ---------------- time-sliced scan: W waves per chunk of W*K tokens ----------------
+    // 32-bit loop bookkeeping (see the sequential path)
+    const int ntok = static_cast<int>(L.end - L.start);
+    constexpr int chunk = W * K;
+    const int nchunks = (ntok + chunk - 1) / chunk;
+    const int my0 = wave * K;  // this wave's slice in chunk 0, relative to the sequence start
+    // the carry into chunk 0 is h0: seed the "previous chunk" carry slot with it
+    if (wave == W - 1) s_carry[1][L.lane] = make_float4(L.hinit[0], L.hinit[1], L.hinit[2], L.hinit[3]);
+
+    auto chunk_step = [&](int ci, const RawSlice<Tin, K>& cur, RawSlice<Tin, K>& nxt) {
+      const int buf = ci & 1;
+      const int i0 = my0 + ci * chunk;
+      const int64_t t0 = L.start + i0;
+      const int nv = ntok - i0 <= 0 ? 0 : (ntok - i0 < K ? ntok - i0 : K);
+      load_raw<Tin, Tout, K>(p, L, t0 + chunk, nxt);  // prefetch this wave's slice of the next chunk
+      stage_bc<Tin, Tout, K>(cur, L, sB, sC);
+      float xv[K / 4], zv[K / 4], dl[K / 4], uu[K / 4];
+      decode_raw<Tin, Tout, K>(cur, L, nv, xv, zv, dl, uu);
+      publish_du<K>(s_du[wave], L.c, L.g, dl, uu);
       wave_lds_sync();
 
       // phase 1: local scan of the slice from zero; keep Ā and B̄x in registers
-      float ak[kK][kSPL], bk[kK][kSPL];
+      float ak[K][kSPL], bk[K][kSPL];
       float H[kSPL] = {0.f, 0.f, 0.f, 0.f};
+      float4 bq[4];
+      float dq[4], uq[4];
 #pragma unroll
-      for (int k = 0; k < kK; ++k) {
+      for (int k = 0; k < K; ++k) {
         const int j = k >> 2, q = k & 3;
-        const float dk = (q == 0) ? qbcast<0>(dl[j]) : (q == 1) ? qbcast<1>(dl[j]) : (q == 2) ? qbcast<2>(dl[j]) : qbcast<3>(dl[j]);
-        const float uk = (q == 0) ? qbcast<0>(uu[j]) : (q == 1) ? qbcast<1>(uu[j]) : (q == 2) ? qbcast<2>(uu[j]) : qbcast<3>(uu[j]);
-        const float4 bv = sB4[k * 4 + L.g];
+        if (q == 0) {
+          fetch_du(s_du[wave], j, L.c, dq, uq);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bq[r] = sB4[(k + r) * 4 + L.g];  // the group's B rows, read together
+        }
+        const float dk = dq[q];
+        const float uk = uq[q];
+        const float4 bv = bq[q];
         ak[k][0] = __builtin_amdgcn_exp2f(dk * L.A2[0]);
         ak[k][1] = __builtin_amdgcn_exp2f(dk * L.A2[1]);
         ak[k][2] = __builtin_amdgcn_exp2f(dk * L.A2[2]);
@@ -352,7 +513,7 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
       // product of the slice's Ā = exp(A * sum of the slice's Δ)
       float sd = 0.f;
 #pragma unroll
-      for (int j = 0; j < kK / 4; ++j) sd += dl[j];
+      for (int j = 0; j < K / 4; ++j) sd += dl[j];
       sd = quad_allsum(sd);
       s_agg[buf][wave][0][L.lane] = make_float4(__builtin_amdgcn_exp2f(L.A2[0] * sd), __builtin_amdgcn_exp2f(L.A2[1] * sd),
                                                 __builtin_amdgcn_exp2f(L.A2[2] * sd), __builtin_amdgcn_exp2f(L.A2[3] * sd));
@@ -361,10 +522,7 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
 
       // carry-in of this slice: chunk carry folded through the earlier slices
       float hin[kSPL];
-      if (ci == 0) {
-#pragma unroll
-        for (int i = 0; i < kSPL; ++i) hin[i] = L.hinit[i];
-      } else {
+      {
         const float4 cr = s_carry[buf ^ 1][L.lane];
         hin[0] = cr.x; hin[1] = cr.y; hin[2] = cr.z; hin[3] = cr.w;
       }
@@ -378,26 +536,37 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
       }
 
       // phase 3: replay the slice from the true carry-in, read out, gate, store
+      const rsrc_t ry = make_rsrc_rows(yout + t0 * p.dim, ntok - i0, static_cast<uint32_t>(p.dim));
 #pragma unroll
       for (int i = 0; i < kSPL; ++i) h[i] = hin[i];
 #pragma unroll
-      for (int j = 0; j < kK / 4; ++j) {
+      for (int j = 0; j < K / 4; ++j) {
         float pr[4];
+        float4 cq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cq[q] = sC4[(4 * j + q) * 4 + L.g];  // the group's C rows, read together
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int k = 4 * j + q;
-          const float4 cv = sC4[k * 4 + L.g];
+          const float4 cv = cq[q];
 #pragma unroll
           for (int i = 0; i < kSPL; ++i) h[i] = fmaf(ak[k][i], h[i], bk[k][i]);
           pr[q] = fmaf(cv.w, h[3], fmaf(cv.z, h[2], fmaf(cv.y, h[1], cv.x * h[0])));
         }
         if (4 * j < nv) {
           const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
-          store_y<Tout>(p, L, t0, 4 * j + L.g, nv, yraw, xv[j], zv[j]);
+          store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
         }
       }
       if (wave == W - 1) s_carry[buf][L.lane] = make_float4(h[0], h[1], h[2], h[3]);
       wave_lds_sync();
+    };
+
+    RawSlice<Tin, K> ra, rb;
+    load_raw<Tin, Tout, K>(p, L, L.start + my0, ra);
+    for (int ci = 0; ci < nchunks; ci += 2) {
+      chunk_step(ci, ra, rb);
+      if (ci + 1 < nchunks) chunk_step(ci + 1, rb, ra);
     }
     if (wave == W - 1 && p.h_last && L.dvalid)
       reinterpret_cast<float4*>(p.h_last + (static_cast<int64_t>(s) * p.dim + L.d) * kN)[L.g] =
@@ -498,6 +667,10 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 size_t esize(int32_t dt) { return dt == SAMBA_BF16 ? 2 : 4; }
 bool dtype_ok(int32_t dt) { return dt == SAMBA_F32 || dt == SAMBA_BF16; }
 
+// Tokens per wave slice: 16 keeps the replay registers of two waves per SIMD;
+// 16-wave workgroups (four per SIMD) use 8 to stay within 128 VGPRs.
+int slice_tokens(int W) { return W >= 16 ? 8 : 16; }
+
 struct FwdPlan {
   int W, tpw, threads, grid;
   int64_t nseq;
@@ -511,7 +684,7 @@ samba_status validate_fwd(const samba_scan_fwd_args* a, FwdPlan* plan) {
   if (!dtype_ok(a->in_dtype) || !dtype_ok(a->y_dtype)) return SAMBA_ERR_BAD_DTYPE;
   if (a->batch < 0 || a->seqlen < 0 || a->dim < 1) return SAMBA_ERR_BAD_SHAPE;
   const int ts = a->time_slices;
-  if (!(ts == 0 || ts == 1 || ts == 2 || ts == 4 || ts == 8)) return SAMBA_ERR_UNSUPPORTED;
+  if (!(ts == 0 || ts == 1 || ts == 2 || ts == 4 || ts == 8 || ts == 16)) return SAMBA_ERR_UNSUPPORTED;
   int64_t nseq = a->batch;
   if (a->cu_seqlens) {
     if (a->batch != 1 || a->nseq < 1) return SAMBA_ERR_BAD_SHAPE;
@@ -546,13 +719,16 @@ samba_status validate_fwd(const samba_scan_fwd_args* a, FwdPlan* plan) {
   const int ntiles = (a->dim + kCPW - 1) / kCPW;
   int W = ts;
   if (W == 0) {
-    // Enough waves for two per SIMD (4 SIMDs per CU) without slicing?  Otherwise
-    // split time, but never into slices that the average sequence cannot fill.
-    const int64_t target = static_cast<int64_t>(device_cu_count()) * 8;
+    // Enough (sequence, tile) waves for two per SIMD: plain sequential scan.
+    // Otherwise aim at four waves per SIMD by splitting time, but never into
+    // slices that the average sequence cannot fill.
+    const int64_t cus = device_cu_count();
     const int64_t base = nseq * ntiles;
     const int64_t avg_len = nseq > 0 ? tokens / nseq : 0;
     W = 1;
-    while (W < 8 && base * W < target && static_cast<int64_t>(W) * 2 * kK <= avg_len) W *= 2;
+    if (base < cus * 8) {
+      while (W < 16 && base * W < cus * 16 && static_cast<int64_t>(W) * 2 * slice_tokens(W * 2) <= avg_len) W *= 2;
+    }
   }
   const int tpw = (W == 1) ? 4 : 1;
   const int ngroups = (ntiles + tpw - 1) / tpw;
@@ -582,10 +758,11 @@ template <typename Tin, typename Tout>
 hipError_t launch_fwd(const FwdPlan& pl, hipStream_t st) {
   const dim3 grid(pl.grid), block(pl.threads);
   switch (pl.W) {
-    case 1: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 1, 4>), grid, block, 0, st, pl.prm); break;
-    case 2: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 2, 1>), grid, block, 0, st, pl.prm); break;
-    case 4: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 4, 1>), grid, block, 0, st, pl.prm); break;
-    default: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 8, 1>), grid, block, 0, st, pl.prm); break;
+    case 1: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 1, 4, 16>), grid, block, 0, st, pl.prm); break;
+    case 2: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 2, 1, 16>), grid, block, 0, st, pl.prm); break;
+    case 4: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 4, 1, 16>), grid, block, 0, st, pl.prm); break;
+    case 8: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 8, 1, 16>), grid, block, 0, st, pl.prm); break;
+    default: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 16, 1, 8>), grid, block, 0, st, pl.prm); break;
   }
   return hipGetLastError();
 }
@@ -681,7 +858,7 @@ const char* samba_status_string(int status) {
     case SAMBA_ERR_BAD_DTYPE: return "unsupported dtype code";
     case SAMBA_ERR_MISALIGNED: return "pointer misaligned";
     case SAMBA_ERR_ALIASING: return "an output overlaps an input";
-    case SAMBA_ERR_UNSUPPORTED: return "unsupported configuration (dstate must be 16; time_slices 0/1/2/4/8)";
+    case SAMBA_ERR_UNSUPPORTED: return "unsupported configuration (dstate must be 16; time_slices 0/1/2/4/8/16)";
     case SAMBA_ERR_BAD_STRUCT: return "argument struct size mismatch (header/library version skew)";
     case SAMBA_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";

@@ -110,7 +110,7 @@ FWD_CASES = {
     "neg_seqlen": (lambda a: setattr(a, "seqlen", -5), 2),
     "zero_dim": (lambda a: setattr(a, "dim", 0), 2),
     "time_slices": (lambda a: setattr(a, "time_slices", 3), 6),
-    "time_slices_16": (lambda a: setattr(a, "time_slices", 16), 6),
+    "time_slices_32": (lambda a: setattr(a, "time_slices", 32), 6),
     "null_x": (lambda a: setattr(a, "x", None), 1),
     "null_A": (lambda a: setattr(a, "A", None), 1),
     "null_y": (lambda a: setattr(a, "y", None), 1),
@@ -187,7 +187,7 @@ def test_step_empty_batch_is_noop(lib):
 def test_plan_low_parallelism_splits_time(lib):
     a = fwd_ok(batch=1, seqlen=16384, dim=4096)
     st, w, g, t = plan(lib, a)
-    assert st == 0 and w == 8 and g == 256 and t == 512
+    assert st == 0 and w == 16 and g == 256 and t == 1024
 
 
 def test_plan_batched_runs_sequential(lib):
@@ -203,7 +203,7 @@ def test_plan_short_sequences_limit_slices(lib):
 
 
 def test_plan_forced_slices(lib):
-    for ts in (1, 2, 4, 8):
+    for ts in (1, 2, 4, 8, 16):
         a = fwd_ok(batch=1, seqlen=1000, dim=100)
         a.time_slices = ts
         st, w, g, t = plan(lib, a)

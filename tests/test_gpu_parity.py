@@ -83,6 +83,8 @@ SMALL = [
     (2, 1, 16, "bf16", "f32", 0, 1.0),      # single token
     (3, 5, 40, "bf16", "f32", 1, 0.5),      # ragged tokens (< 4) and channels (not a multiple of 16)
     (1, 130, 33, "bf16", "f32", 8, 1.0),    # ragged last chunk with 8 slices
+    (1, 300, 33, "bf16", "f32", 16, 1.0),   # 16 slices of 8 tokens, ragged
+    (3, 1000, 48, "bf16", "f32", 16, 1.0),
     (2, 1000, 48, "bf16", "f32", 1, 1.0),
     (2, 1000, 48, "bf16", "f32", 2, 1.0),
     (2, 1000, 48, "bf16", "f32", 4, 1.0),
@@ -117,9 +119,9 @@ def test_empty_sequence_copies_carry():
 def test_time_slices_agree():
     """Every slicing of the time axis gives the same result to fp32 rounding."""
     outs = {}
-    for ts in (1, 2, 4, 8):
+    for ts in (1, 2, 4, 8, 16):
         outs[ts] = run_case(1, 2000, 64, "bf16", "f32", ts, 1.0, cfg=1)
-    for ts in (2, 4, 8):
+    for ts in (2, 4, 8, 16):
         assert norm_err(outs[ts]["y"], outs[1]["y"]) < 1e-5
         assert norm_err(outs[ts]["h"], outs[1]["h"]) < 1e-5
 
@@ -127,7 +129,7 @@ def test_time_slices_agree():
 def test_delta_to_zero_carry_pin():
     """dt_raw = -40 makes Δ ~ 1e-18: h_last must equal h0 and y_t = (C_t.h0 + D x_t) silu(z_t).
     Away from the first token only a correct carry (across slices, chunks and waves) gives this."""
-    for ts in (1, 8):
+    for ts in (1, 8, 16):
         r = run_case(2, 1000, 32, "bf16", "f32", ts, 1.0, dt_override=-40.0)
         inp, h0 = r["inp"], r["h0"]
         C = inp["C_f32"].reshape(2, 1000, 16).astype(np.float64)
@@ -192,7 +194,7 @@ def test_varlen_small_with_empty_sequences():
     x, dt, z = (dev_in(inp[k], "bf16") for k in ("x", "dt", "z"))
     B, C = (dev_in(inp[k], "bf16") for k in ("B", "C"))
     A, Dv, bias = (torch.from_numpy(inp[k]).to(DEV) for k in ("A", "D", "dt_bias"))
-    for ts in (0, 1, 4):
+    for ts in (0, 1, 4, 16):
         y, hl = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=torch.from_numpy(h0).to(DEV),
                            cu_seqlens=torch.from_numpy(cu).to(DEV), y_dtype=torch.float32, time_slices=ts)
         torch.cuda.synchronize()
