@@ -41,6 +41,10 @@ namespace {
 constexpr int kN = 16;         // states per channel
 constexpr int kSPL = 4;        // states per lane
 constexpr int kCPW = 16;       // channels per wave
+#ifndef SAMBA_STEP_QPT
+#define SAMBA_STEP_QPT 4
+#endif
+constexpr int kStepQPT = SAMBA_STEP_QPT;  // quads per thread of the decode step on large batches
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -582,7 +586,7 @@ struct StepParams {
   const void *x, *dt, *z, *B, *C;
   const float *A, *Dskip, *bias;
   void* y;
-  int64_t nquads;  // batch * dim
+  int32_t batch;
   int32_t dim;
 };
 
@@ -599,40 +603,55 @@ __device__ __forceinline__ void load4<float>(const float* p, int64_t i, float (&
   v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
 }
 
-template <typename Tin, typename Tout>
+// A workgroup of 256 threads = 64 channel quads covers channels
+// [64*bx, 64*bx+64) for QPT consecutive sequences [QPT*by, QPT*by+QPT): each
+// thread loads its channel's A, dt_bias and D once and reuses them for all its
+// sequences; each round of a wave touches 1 KB of contiguous state.  All
+// rounds' loads are issued before any compute.
+template <typename Tin, typename Tout, int QPT>
 __global__ __launch_bounds__(256) void scan_step_kernel(StepParams p) {
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t qd = gid >> 2;
-  const int g = static_cast<int>(gid & 3);
-  const bool valid = qd < p.nquads;
-  const int64_t qs = valid ? qd : p.nquads - 1;
-  const int64_t b = qs / p.dim;
-  const int d = static_cast<int>(qs - b * p.dim);
-
-  float4* st = reinterpret_cast<float4*>(p.state + qs * kN) + g;
-  const float4 h4 = *st;
-  const float4 a4 = reinterpret_cast<const float4*>(p.A + static_cast<int64_t>(d) * kN)[g];
-  const float xv = ld_in(static_cast<const Tin*>(p.x), qs);
-  const float dr = ld_in(static_cast<const Tin*>(p.dt), qs);
-  const float zv = ld_in(static_cast<const Tin*>(p.z), qs);
-  float Bv[4], Cv[4];
-  load4<Tin>(static_cast<const Tin*>(p.B), b * kN + 4 * g, Bv);
-  load4<Tin>(static_cast<const Tin*>(p.C), b * kN + 4 * g, Cv);
-
-  const float delta = softplus_f32(dr + p.bias[d]);
-  const float u = delta * xv;
-  float h[4] = {h4.x, h4.y, h4.z, h4.w};
-  const float A2[4] = {a4.x * kLog2e, a4.y * kLog2e, a4.z * kLog2e, a4.w * kLog2e};
-  float pr = 0.f;
+  const int g = threadIdx.x & 3;
+  const int d = blockIdx.x * 64 + (threadIdx.x >> 2);
+  const bool dvalid = d < p.dim;
+  const int dc = dvalid ? d : p.dim - 1;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * QPT;
+  const float4 a4 = reinterpret_cast<const float4*>(p.A + static_cast<int64_t>(dc) * kN)[g];
+  const float bias = p.bias[dc];
+  const float dsk = p.Dskip[dc];
+  float4 h4[QPT];
+  float xv[QPT], dr[QPT], zv[QPT], Bv[QPT][4], Cv[QPT][4];
+  int64_t qs[QPT];
+  bool valid[QPT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = fmaf(__builtin_amdgcn_exp2f(delta * A2[i]), h[i], u * Bv[i]);
-    pr = fmaf(Cv[i], h[i], pr);
+  for (int r = 0; r < QPT; ++r) {
+    const int64_t b = b0 + r;
+    valid[r] = dvalid && b < p.batch;
+    const int64_t bc = b < p.batch ? b : p.batch - 1;
+    qs[r] = bc * p.dim + dc;
+    h4[r] = reinterpret_cast<const float4*>(p.state + qs[r] * kN)[g];
+    xv[r] = ld_in(static_cast<const Tin*>(p.x), qs[r]);
+    dr[r] = ld_in(static_cast<const Tin*>(p.dt), qs[r]);
+    zv[r] = ld_in(static_cast<const Tin*>(p.z), qs[r]);
+    load4<Tin>(static_cast<const Tin*>(p.B), bc * kN + 4 * g, Bv[r]);
+    load4<Tin>(static_cast<const Tin*>(p.C), bc * kN + 4 * g, Cv[r]);
   }
-  pr = quad_allsum(pr);
-  if (valid) {
-    *st = make_float4(h[0], h[1], h[2], h[3]);
-    if (g == 0) st_out(static_cast<Tout*>(p.y), qs, (pr + p.Dskip[d] * xv) * silu_f32(zv));
+  const float A2[4] = {a4.x * kLog2e, a4.y * kLog2e, a4.z * kLog2e, a4.w * kLog2e};
+#pragma unroll
+  for (int r = 0; r < QPT; ++r) {
+    const float delta = softplus_f32(dr[r] + bias);
+    const float u = delta * xv[r];
+    float h[4] = {h4[r].x, h4[r].y, h4[r].z, h4[r].w};
+    float pr = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = fmaf(__builtin_amdgcn_exp2f(delta * A2[i]), h[i], u * Bv[r][i]);
+      pr = fmaf(Cv[r][i], h[i], pr);
+    }
+    pr = quad_allsum(pr);
+    if (valid[r]) {
+      reinterpret_cast<float4*>(p.state + qs[r] * kN)[g] = make_float4(h[0], h[1], h[2], h[3]);
+      if (g == 0) st_out(static_cast<Tout*>(p.y), qs[r], (pr + dsk * xv[r]) * silu_f32(zv[r]));
+    }
   }
 }
 
@@ -828,24 +847,33 @@ samba_status samba_scan_step(const samba_scan_step_args* args, void* stream) {
   if (st != SAMBA_OK) return st;
   const int64_t nquads = static_cast<int64_t>(args->batch) * args->dim;
   if (nquads == 0) return SAMBA_OK;
-  const int64_t threads = nquads * 4;
-  const int64_t blocks = (threads + 255) / 256;
-  if (blocks > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  // sequences per thread: more than one once the batch is large enough to
+  // keep every CU busy (A, dt_bias and D are then loaded once per channel)
+  const int qpt = (args->batch >= 2 * kStepQPT &&
+                   static_cast<int64_t>((args->dim + 63) / 64) * (args->batch / kStepQPT) >= device_cu_count() * 2)
+                      ? kStepQPT : 1;
+  const int64_t gx = (args->dim + 63) / 64, gy = (static_cast<int64_t>(args->batch) + qpt - 1) / qpt;
+  if (gy > 65535) return SAMBA_ERR_BAD_SHAPE;
   StepParams p;
   p.state = args->state;
   p.x = args->x; p.dt = args->dt; p.z = args->z; p.B = args->B; p.C = args->C;
   p.A = args->A; p.Dskip = args->D; p.bias = args->dt_bias;
   p.y = args->y;
-  p.nquads = nquads;
+  p.batch = args->batch;
   p.dim = args->dim;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  if (args->in_dtype == SAMBA_BF16) {
-    if (args->y_dtype == SAMBA_BF16) hipLaunchKernelGGL((scan_step_kernel<uint16_t, uint16_t>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_step_kernel<uint16_t, float>), grid, block, 0, s, p);
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy)), block(256);
+  const bool bi = args->in_dtype == SAMBA_BF16, bo = args->y_dtype == SAMBA_BF16;
+  if (qpt == 1) {
+    if (bi) { if (bo) hipLaunchKernelGGL((scan_step_kernel<uint16_t, uint16_t, 1>), grid, block, 0, s, p);
+              else hipLaunchKernelGGL((scan_step_kernel<uint16_t, float, 1>), grid, block, 0, s, p); }
+    else { if (bo) hipLaunchKernelGGL((scan_step_kernel<float, uint16_t, 1>), grid, block, 0, s, p);
+           else hipLaunchKernelGGL((scan_step_kernel<float, float, 1>), grid, block, 0, s, p); }
   } else {
-    if (args->y_dtype == SAMBA_BF16) hipLaunchKernelGGL((scan_step_kernel<float, uint16_t>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((scan_step_kernel<float, float>), grid, block, 0, s, p);
+    if (bi) { if (bo) hipLaunchKernelGGL((scan_step_kernel<uint16_t, uint16_t, kStepQPT>), grid, block, 0, s, p);
+              else hipLaunchKernelGGL((scan_step_kernel<uint16_t, float, kStepQPT>), grid, block, 0, s, p); }
+    else { if (bo) hipLaunchKernelGGL((scan_step_kernel<float, uint16_t, kStepQPT>), grid, block, 0, s, p);
+           else hipLaunchKernelGGL((scan_step_kernel<float, float, kStepQPT>), grid, block, 0, s, p); }
   }
   return hipGetLastError() == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
 }

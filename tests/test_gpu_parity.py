@@ -230,6 +230,24 @@ def test_step_matches_oracle_and_fwd():
     check_fp32(host(st).reshape(Bt, -1), ho.reshape(Bt, -1), "step state")
 
 
+def test_step_many_sequences_ragged():
+    """A batch large enough for several sequences per thread, with ragged batch and channel counts."""
+    Bt, D = 130, 2000
+    g = np.random.default_rng(7)
+    p = I.make_params(1, D)
+    st0 = (0.5 * g.standard_normal((Bt, D, 16))).astype(np.float32)
+    s = I.make_step_inputs_np(1, 0, Bt, D)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    bf = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+    st = T(st0)
+    y = S.scan_step(st, bf(s["x"]), bf(s["dt"]), bf(s["z"]), bf(s["B"]), bf(s["C"]), T(p["A"]), T(p["D"]),
+                    T(p["dt_bias"]), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yo, so = O.scan_step(st0, s["x_f32"], s["dt_f32"], s["z_f32"], s["B_f32"], s["C_f32"], p["A"], p["D"], p["dt_bias"])
+    check_fp32(host(y), yo, "step ragged y", np.arange(Bt + 1))
+    check_fp32(host(st).reshape(Bt, -1), so.reshape(Bt, -1), "step ragged state")
+
+
 def test_step_fp32_io_and_ragged_dim():
     Bt, D = 3, 37
     g = np.random.default_rng(5)
