@@ -68,16 +68,20 @@ __device__ __forceinline__ void st_out(uint16_t* p, int64_t i, float v) { p[i] =
 // ---------------------------------------------------------------------------
 // scalar maps
 // ---------------------------------------------------------------------------
-// softplus(v) = log(1 + e^v).  log1p is formed as log(u) * e / (u - 1) with
-// u = 1 + e rounded (Goldberg's correction), which keeps full relative accuracy
-// for the small Δ this map produces; v > 20 returns v (the remainder is below
-// fp32 resolution).
+// softplus(v) = log(1 + e^v) with e = e^v and u = fl(1 + e).  log(1 + e) =
+// log(u) + log((1 + e) / u), and (1 + e) - u = e - (u - 1) exactly when e < 1
+// (u - 1 is then exact), so the rounding of u is undone by the first-order term
+// (e - (u - 1)) / u, with 1/u taken as 2 - u (error (u-1)^2 relative to a term
+// already below one ulp).  For e >= 1 the rounding of u costs at most 2^-24
+// relative and is left alone; v > 20 returns v (the remainder is below fp32
+// resolution).  Full relative accuracy for the small Δ this map produces, with
+// two transcendental instructions (exp2, log2).
 __device__ __forceinline__ float softplus_f32(float v) {
   const float e = __builtin_amdgcn_exp2f(v * kLog2e);
   const float u = 1.0f + e;
-  const float um1 = u - 1.0f;
-  const float lg = __builtin_amdgcn_logf(u) * kLn2;
-  const float r = (um1 == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(um1));
+  const float lost = e - (u - 1.0f);
+  const float inv_u = (e < 1.0f) ? (2.0f - u) : 0.0f;
+  const float r = fmaf(__builtin_amdgcn_logf(u), kLn2, lost * inv_u);
   return (v > 20.0f) ? v : r;
 }
 
@@ -118,6 +122,22 @@ __device__ __forceinline__ float quad_transpose_sum(float p0, float p1, float p2
   const bool odd = (g & 1) != 0;
   const float k = odd ? r1 : r0, s = odd ? r0 : r1;
   return k + qperm<kQXor1>(s);
+}
+
+// Same result through LDS (no DPP, no selects): lane g stores its partial of
+// token q at red[c][q][g]; lane g then reads the four partials of token g.
+__device__ __forceinline__ float quad_transpose_sum_lds(float4 (*red)[4], int c, int g, float p0, float p1, float p2,
+                                                        float p3) {
+  float* row = reinterpret_cast<float*>(red[c]);
+  row[0 * 4 + g] = p0;
+  row[1 * 4 + g] = p1;
+  row[2 * 4 + g] = p2;
+  row[3 * 4 + g] = p3;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float4 v = red[c][g];
+  return (v.x + v.y) + (v.z + v.w);
 }
 
 __device__ __forceinline__ float quad_allsum(float v) {
@@ -303,8 +323,9 @@ __device__ __forceinline__ void decode_raw(const RawSlice<Tin, K>& r, const Lane
     const float xr = widen(r.x[j]);
     xv[j] = xr;
     zv[j] = widen(r.z[j]);
-    const float delta = ok ? softplus_f32(widen(r.dt[j]) + L.bias) : 0.0f;
-    dl[j] = delta;
+    // computed on every lane and then masked: branching would not skip any work
+    const float delta = softplus_f32(widen(r.dt[j]) + L.bias);
+    dl[j] = ok ? delta : 0.0f;
     uu[j] = ok ? delta * xr : 0.0f;
   }
 }
@@ -351,6 +372,7 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
   constexpr int kWaves = W * TPW;
   __shared__ float4 s_bc[kWaves][2][K * kN / 4];                   // per-wave staged B, C (fp32)
   __shared__ float4 s_du[kWaves][K / 4][kCPW][2];                  // per-wave (Δ, Δx) of each group's 4 tokens
+  __shared__ float4 s_red[kWaves][kCPW][4];                        // per-wave readout partials of one group
   __shared__ float4 s_agg[(W > 1) ? 2 : 1][W][2][64];              // slice (P, H) pairs, double buffered
   __shared__ float4 s_carry[(W > 1) ? 2 : 1][64];                  // chunk carry, double buffered
 
@@ -451,7 +473,7 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
           h[3] = fmaf(__builtin_amdgcn_exp2f(dk[q] * L.A2[3]), h[3], uk[q] * bv[q].w);
           pr[q] = fmaf(cv[q].w, h[3], fmaf(cv[q].z, h[2], fmaf(cv[q].y, h[1], cv[q].x * h[0])));
         }
-        const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
+        const float yraw = quad_transpose_sum_lds(s_red[wave], L.c, L.g, pr[0], pr[1], pr[2], pr[3]);
         store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
       }
       wave_lds_sync();
@@ -489,7 +511,7 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
 
       // phase 1: local scan of the slice from zero; keep Ā and B̄x in registers
       float ak[K][kSPL], bk[K][kSPL];
-      float H[kSPL] = {0.f, 0.f, 0.f, 0.f};
+      float H[kSPL];
       float4 bq[4];
       float dq[4], uq[4];
 #pragma unroll
@@ -512,7 +534,7 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
         bk[k][2] = uk * bv.z;
         bk[k][3] = uk * bv.w;
 #pragma unroll
-        for (int i = 0; i < kSPL; ++i) H[i] = fmaf(ak[k][i], H[i], bk[k][i]);
+        for (int i = 0; i < kSPL; ++i) H[i] = (k == 0) ? bk[0][i] : fmaf(ak[k][i], H[i], bk[k][i]);  // from a zero state
       }
       // product of the slice's Ā = exp(A * sum of the slice's Δ)
       float sd = 0.f;
@@ -558,7 +580,7 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
           pr[q] = fmaf(cv.w, h[3], fmaf(cv.z, h[2], fmaf(cv.y, h[1], cv.x * h[0])));
         }
         if (4 * j < nv) {
-          const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
+          const float yraw = quad_transpose_sum_lds(s_red[wave], L.c, L.g, pr[0], pr[1], pr[2], pr[3]);
           store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
         }
       }
@@ -629,9 +651,11 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepParams p) {
     const int64_t bc = b < p.batch ? b : p.batch - 1;
     qs[r] = bc * p.dim + dc;
     h4[r] = reinterpret_cast<const float4*>(p.state + qs[r] * kN)[g];
-    xv[r] = ld_in(static_cast<const Tin*>(p.x), qs[r]);
-    dr[r] = ld_in(static_cast<const Tin*>(p.dt), qs[r]);
-    zv[r] = ld_in(static_cast<const Tin*>(p.z), qs[r]);
+    // per-step inputs and y are touched once: non-temporal, so they do not
+    // displace the state (which stays cache-resident from step to step)
+    xv[r] = widen(__builtin_nontemporal_load(static_cast<const Tin*>(p.x) + qs[r]));
+    dr[r] = widen(__builtin_nontemporal_load(static_cast<const Tin*>(p.dt) + qs[r]));
+    zv[r] = widen(__builtin_nontemporal_load(static_cast<const Tin*>(p.z) + qs[r]));
     load4<Tin>(static_cast<const Tin*>(p.B), bc * kN + 4 * g, Bv[r]);
     load4<Tin>(static_cast<const Tin*>(p.C), bc * kN + 4 * g, Cv[r]);
   }
@@ -650,7 +674,11 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepParams p) {
     pr = quad_allsum(pr);
     if (valid[r]) {
       reinterpret_cast<float4*>(p.state + qs[r] * kN)[g] = make_float4(h[0], h[1], h[2], h[3]);
-      if (g == 0) st_out(static_cast<Tout*>(p.y), qs[r], (pr + dsk * xv[r]) * silu_f32(zv[r]));
+      if (g == 0) {
+        const float yv = (pr + dsk * xv[r]) * silu_f32(zv[r]);
+        if constexpr (sizeof(Tout) == 2) __builtin_nontemporal_store(f32_to_bf16(yv), static_cast<uint16_t*>(p.y) + qs[r]);
+        else __builtin_nontemporal_store(yv, static_cast<float*>(p.y) + qs[r]);
+      }
     }
   }
 }
