@@ -226,6 +226,15 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
     out_d["bytes_per_launch"] = out_d["FETCH_SIZE"]["bytes_per_launch"] + out_d["WRITE_SIZE"]["bytes_per_launch"]
     W = 16384
     out_d["algorithmic_bytes_per_launch"] = prefill_bytes(W, 4096)
+    run = "python3 <repo>/bench.py --steps 1 --warmup 0 --no-decode --no-cpu --copy-probe"
+    out_d["command"] = [
+        f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {run}",
+        f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {run}",
+        f"python bench.py --pmc-summary {fetch_dir} {write_dir} {out}",
+    ]
+    out_d["note"] = ("FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by the ratio of the known size "
+                     "of the plain 512 MiB device copy in the same run to what the counter reports for it "
+                     "(FETCH_SIZE reads half, WRITE_SIZE exact).")
     Path(out).write_text(json.dumps(out_d, indent=1) + "\n")
     print(json.dumps(out_d))
 

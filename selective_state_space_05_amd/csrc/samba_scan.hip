@@ -99,33 +99,10 @@ __device__ __forceinline__ float qperm(float v) {
 }
 constexpr int kQXor1 = 0xB1;  // [1,0,3,2]
 constexpr int kQXor2 = 0x4E;  // [2,3,0,1]
-template <int Q>
-__device__ __forceinline__ float qbcast(float v) { return qperm<Q * 0x55>(v); }  // [Q,Q,Q,Q]
-__device__ __forceinline__ float qbcast_dyn(float v, int q) {
-  // q is a compile-time constant after unrolling; the switch folds away
-  switch (q) {
-    case 0: return qbcast<0>(v);
-    case 1: return qbcast<1>(v);
-    case 2: return qbcast<2>(v);
-    default: return qbcast<3>(v);
-  }
-}
-
 // Lane g holds partial sums p[0..3] for the four tokens of a group; returns, on
-// lane g, the quad's total for token g.
-__device__ __forceinline__ float quad_transpose_sum(float p0, float p1, float p2, float p3, int g) {
-  const bool hi = (g & 2) != 0;
-  const float k0 = hi ? p2 : p0, s0 = hi ? p0 : p2;
-  const float k1 = hi ? p3 : p1, s1 = hi ? p1 : p3;
-  const float r0 = k0 + qperm<kQXor2>(s0);
-  const float r1 = k1 + qperm<kQXor2>(s1);
-  const bool odd = (g & 1) != 0;
-  const float k = odd ? r1 : r0, s = odd ? r0 : r1;
-  return k + qperm<kQXor1>(s);
-}
-
-// Same result through LDS (no DPP, no selects): lane g stores its partial of
-// token q at red[c][q][g]; lane g then reads the four partials of token g.
+// lane g, the quad's total for token g.  The exchange goes through LDS (no DPP,
+// no selects): lane g stores its partial of token q at red[c][q][g], then reads
+// the four partials of token g.
 __device__ __forceinline__ float quad_transpose_sum_lds(float4 (*red)[4], int c, int g, float p0, float p1, float p2,
                                                         float p3) {
   float* row = reinterpret_cast<float*>(red[c]);
