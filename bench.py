@@ -112,6 +112,16 @@ def bench_prefill(steps: int, warmup: int, time_slices: int = 0):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     launch_ms = ms / n
+    # per-call durations (each call bracketed by its own events), after the interval timing above
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n * steps + 1)]
+    evs[0].record(stream)
+    for s in range(steps):
+        for i, a in enumerate(args):
+            if lib.samba_scan_fwd(ctypes.byref(a), sh) != 0:
+                raise RuntimeError("samba_scan_fwd failed")
+            evs[s * n + i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(n * steps))
     tokens_ch = L * D
     step_bytes = n * prefill_bytes(cl, D)
     return {
@@ -122,6 +132,7 @@ def bench_prefill(steps: int, warmup: int, time_slices: int = 0):
         "launch_td": cl * D,
         "bytes_per_launch": prefill_bytes(cl, D),
         "plan": {"time_slices": plan[0], "workgroups": plan[1], "threads_per_workgroup": plan[2]},
+        "call_us": {"median": per_call[len(per_call) // 2], "min": per_call[0], "calls": len(per_call)},
     }
 
 
@@ -239,6 +250,27 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
     print(json.dumps(out_d))
 
 
+def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Measured device-to-device copy rate (bytes read + bytes written per second, GB/s): the practical HBM
+    ceiling the algorithmic rates are also compared with."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def copy_probe(nbytes: int = 512 << 20, reps: int = 3):
     """A plain device-to-device copy of known size; its FETCH_SIZE / WRITE_SIZE per dispatch calibrate the counters."""
     import torch
@@ -283,6 +315,34 @@ def cpu_baseline(max_oracle_s: float = 30.0):
             "tokens_channels_per_s": done * cl * D / spent}
 
 
+def cpu_baseline_decode(steps: int = 1024, max_oracle_s: float = 15.0):
+    """The fp64 oracle's decode step on the full batch-64, D-4096 state, chained over the first `steps`
+    steps of the input ring (stopping early past ~max_oracle_s); steps/s is extrapolated from that sample."""
+    import numpy as np
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+
+    W = I.WORKLOADS[4]
+    Bt, D, R = W.batch, W.dim, W.decode_ring
+    P = I.make_params(4, D)
+    lib = O.load()
+    state = np.zeros((Bt, D, 16))
+    ring = [I.make_step_inputs_np(4, r, Bt, D) for r in range(min(R, 16))]
+    spent, done = 0.0, 0
+    for k in range(steps):
+        s = ring[k % len(ring)]
+        t0 = time.perf_counter()
+        _, state = O.scan_step(state, s["x_f32"], s["dt_f32"], s["z_f32"], s["B_f32"], s["C_f32"], P["A"], P["D"],
+                               P["dt_bias"], lib=lib)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent > max_oracle_s:
+            break
+    return {"value": done / spent, "unit": "steps/s", "cores": O.max_threads(lib), "kind": "oracle",
+            "sample": "first %d of the 65536 steps (batch 64, D 4096, fp64 state), extrapolated to steps/s; "
+                      "%.1f s of oracle time" % (done, spent)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +366,7 @@ def main():
         sys.exit(2)
 
     pf = bench_prefill(args.steps, args.warmup, args.time_slices)
+    ceiling = copy_ceiling()
     if args.copy_probe:
         copy_probe()
     achieved = SLOTS_PER_TD * pf["launch_td"] / (pf["launch_ms"] * 1e-3) / 1e12
@@ -328,7 +389,10 @@ def main():
                    "dstate": 16, "chunks": 8, "io": "bf16"},
         "tokens_channels_per_s": pf["tokens_channels_per_s"],
         "hbm_frac": pf["gbs"] / HBM_PEAK_GBS,
+        "copy_ceiling_gbs": round(ceiling, 1),
+        "copy_frac": pf["gbs"] / ceiling,
         "plan": pf["plan"],
+        "call_us": pf["call_us"],
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TSLOT, 2),
                      "unit": "Tslot/s", "frac": round(achieved / VALU_PEAK_TSLOT, 4),
                      "traffic": traffic, "kernel": "scan_fwd_kernel<bf16,bf16,W=%d>" % pf["plan"]["time_slices"],
@@ -340,9 +404,12 @@ def main():
         dec["roofline"] = {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
                            "kernel": "scan_step_kernel<bf16,bf16>"}
+        dec["copy_frac"] = dec["gbs"] / ceiling
         line["decode"] = dec
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
+        if not args.no_decode:
+            line["cpu_baseline"]["decode"] = cpu_baseline_decode()
     print(json.dumps(line), flush=True)
 
 

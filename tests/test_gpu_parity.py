@@ -356,40 +356,71 @@ def test_full_cfg3_chained_128k():
 
 
 def test_full_cfg4_decode_65536_steps():
-    """B = 64, D = 4096: prefill 2048 tokens, then 65536 steps over a ring of 256 input sets."""
+    """B = 64, D = 4096: prefill 2048 tokens, then 65536 steps over a ring of 256 input sets.
+
+    Checked: the full state [64][4096][16] after 1024 steps, and, on all 64
+    sequences x 64 sampled channels, the state after all 65536 steps and the y
+    of the last 256 steps.  The oracle side runs the step tokens through its
+    chained forward scan (its step loop equals its forward scan: pinned in the
+    oracle tests), in sequence groups and time chunks that bound host memory."""
     W = I.WORKLOADS[4]
     Bt, L, D, steps, R = W.batch, W.seqlen, W.dim, W.decode_steps, W.decode_ring
+    early = 1024
     pre = I.make_fwd_inputs_torch(4, Bt * L, D, DEV)
     P = I.make_params(4, D)
     A, Dv, bias = pre["A"], pre["D"], pre["dt_bias"]
     _, state = S.scan_fwd(*(pre[k].view(Bt, L, -1) for k in ("x", "dt", "z", "B", "C")), A, Dv, bias)
     ring = I.make_step_ring_torch(4, R, Bt, D, DEV)
     ys = torch.empty(R, Bt, D, dtype=torch.bfloat16, device=DEV)
+    state_early = None
     for k in range(steps):
         r = k % R
         S.scan_step(state, ring["x"][r], ring["dt"][r], ring["z"][r], ring["B"][r], ring["C"][r], A, Dv, bias,
                     y=ys[r])
+        if k == early - 1:
+            state_early = state.clone()
     torch.cuda.synchronize()
-    bsel = np.array([0, 17, 40, 63])
-    dsel = sample_channels(D, 12, 44)
-    # oracle: prefill of the sampled sequences/channels, then every step
-    bt, dtt = torch.from_numpy(bsel).to(DEV), torch.from_numpy(dsel).to(DEV)
-    sub = {k: pre[k].view(Bt, L, -1).index_select(0, bt) for k in ("x", "dt", "z", "B", "C")}
-    xo, do_, zo = (host(sub[k].index_select(2, dtt)) for k in ("x", "dt", "z"))
-    _, so = O.scan_fwd(xo, do_, zo, host(sub["B"]), host(sub["C"]), P["A"][dsel], P["D"][dsel], P["dt_bias"][dsel])
-    rx, rd, rz = (host(ring[k].index_select(1, bt).index_select(2, dtt)) for k in ("x", "dt", "z"))
-    rB, rC = (host(ring[k].index_select(1, bt)) for k in ("B", "C"))
+    say("cfg4: GPU steps done")
+
+    def ring_tokens(t, first, count, bsl, dsl=None):
+        """Step inputs of steps first..first+count-1 as a token axis: [sequences][count][cols]."""
+        v = t[:, bsl] if dsl is None else t[:, bsl][:, :, dsl]
+        idx = torch.arange(first, first + count, device=DEV) % R
+        return host(v.index_select(0, idx).transpose(0, 1).contiguous())
+
+    # full state after `early` steps: oracle prefill + `early` step tokens, 8 sequences at a time
     lib = O.load()
-    yo_last = np.zeros((R, len(bsel), len(dsel)))
-    for k in range(steps):
-        r = k % R
-        yk, so = O.scan_step(so, rx[r], rd[r], rz[r], rB[r], rC[r], P["A"][dsel], P["D"][dsel], P["dt_bias"][dsel],
-                             nthreads=1, lib=lib)
-        if k >= steps - R:
-            yo_last[r] = yk
-    yg = host(ys.index_select(1, bt).index_select(2, dtt))
-    e1 = check_bf16_y(yg.transpose(1, 0, 2).reshape(len(bsel) * R, -1), yo_last.transpose(1, 0, 2).reshape(
-        len(bsel) * R, -1), "cfg4 last-256-steps bf16 y", np.arange(len(bsel) + 1) * R)
-    sg = host(state.index_select(0, bt).index_select(1, dtt))
-    e2 = check_fp32(sg.reshape(len(bsel), -1), so.reshape(len(bsel), -1), "cfg4 state after 65536 steps")
+    so_pre = np.empty((Bt, D, 16))
+    worst = 0.0
+    for g0 in range(0, Bt, 8):
+        bs = slice(g0, g0 + 8)
+        sub = {k: pre[k].view(Bt, L, -1)[bs] for k in ("x", "dt", "z", "B", "C")}
+        _, hp = O.scan_fwd(*(host(sub[k]) for k in ("x", "dt", "z", "B", "C")), P["A"], P["D"], P["dt_bias"],
+                           lib=lib)
+        so_pre[bs] = hp
+        _, he = O.scan_fwd(*(ring_tokens(ring[k], 0, early, bs) for k in ("x", "dt", "z", "B", "C")), P["A"],
+                           P["D"], P["dt_bias"], h0=hp, lib=lib)
+        ge = host(state_early[bs])
+        worst = max(worst, check_fp32(ge.reshape(8, -1), he.reshape(8, -1), "cfg4 full state after %d steps" % early,
+                                      np.arange(9)))
+    say("cfg4: full state after %d steps err %.3e" % (early, worst))
+
+    # 64 sequences x 64 sampled channels through all steps
+    dsel = sample_channels(D, 64, 44)
+    dtt = torch.from_numpy(dsel).to(DEV)
+    bs = slice(0, Bt)
+    so = so_pre[:, dsel]
+    chunk = 4096
+    yo_last = None
+    for c0 in range(0, steps, chunk):
+        toks = [ring_tokens(ring[k], c0, chunk, bs, dtt) for k in ("x", "dt", "z")]
+        toks += [ring_tokens(ring[k], c0, chunk, bs) for k in ("B", "C")]
+        yk, so = O.scan_fwd(*toks, P["A"][dsel], P["D"][dsel], P["dt_bias"][dsel], h0=so, lib=lib)
+        if c0 + chunk == steps:
+            yo_last = yk[:, chunk - R:]  # [seq][last R steps][ch]; step k uses ring slot k % R
+    yg = host(ys.index_select(2, dtt)).transpose(1, 0, 2)  # [seq][ring slot][ch]
+    e1 = check_bf16_y(yg.reshape(Bt * R, -1), yo_last.reshape(Bt * R, -1), "cfg4 last-256-steps bf16 y",
+                      np.arange(Bt + 1) * R)
+    sg = host(state.index_select(1, dtt))
+    e2 = check_fp32(sg.reshape(Bt, -1), so.reshape(Bt, -1), "cfg4 state after 65536 steps", np.arange(Bt + 1))
     say("cfg4: bf16 ratio %.3f state err %.3e" % (e1, e2))
