@@ -31,6 +31,9 @@
  *   (page 1, section 推理效率: prefill by forward(prompt), then one constant-
  *   time state update per generated token).
  *
+ * The gradients of the prefill (oracle_scan_bwd) are the reverse-mode
+ * derivative of exactly that loop; the formulas stand above the function.
+ *
  * Everything is double precision with libm exp / log1p; build without
  * fast-math.  OpenMP runs over independent (sequence, channel) recurrences;
  * time always runs sequentially inside one recurrence.
@@ -141,6 +144,143 @@ int oracle_scan_step(int64_t batch, int64_t dim, int64_t dstate, double* state,
   }
   (void)nthreads;
   return 0;
+}
+
+/*
+ * Gradients of the prefill: reverse-mode differentiation of exactly the loop
+ * oracle_scan_fwd runs (the pages train Samba with this scan: page
+ * "SAMBA混合注意力状态空间模型", 实现细节 -> 训练配置; the hackernoon page,
+ * §2.1.2, names Mamba's selective scan as the training-time kernel).  For the
+ * loss L = sum_t,d dy[t][d] y[t][d] + sum_s,d,n dh_last[s][d][n] h_last[s][d][n]:
+ *
+ *   per token t of sequence s, channel d (v = dt_raw + bias, Δ = softplus(v)):
+ *     r_t      = sum_n C_t[n] h_t[n] + Dskip x_t          (pre-gate output)
+ *     dr_t     = dy_t silu(z_t)
+ *     dz_t     = dy_t r_t silu'(z_t),   silu'(z) = σ(z) (1 + z (1 - σ(z)))
+ *     g_t[n]   = dr_t C_t[n] + Ā_{t+1}[n] g_{t+1}[n]       (adjoint of h_t; the
+ *                term after the last token is dh_last)
+ *     dx_t     = dr_t Dskip + Δ_t sum_n g_t[n] B_t[n]
+ *     dΔ_t     = sum_n g_t[n] (A[n] Ā_t[n] h_{t-1}[n] + B_t[n] x_t)
+ *     ddt_t    = dΔ_t σ(v)                                 (softplus' = σ)
+ *     dB_t[n] += g_t[n] Δ_t x_t,   dC_t[n] += dr_t h_t[n]  (summed over d)
+ *     dA[d][n]+= g_t[n] Δ_t Ā_t[n] h_{t-1}[n], dDskip[d] += dr_t x_t,
+ *     ddt_bias[d] += ddt_t                                 (summed over t, s)
+ *   dh0[s][d][n] = Ā_first[n] g_first[n]  (dh_last for an empty sequence).
+ *
+ *   dy [T][dim]; dh_last [nseq][dim][dstate] or NULL (zeros); h0 as in the
+ *   forward.  Outputs: dx, ddt, dz [T][dim]; dB, dC [T][dstate]; dA
+ *   [dim][dstate]; dDskip, ddt_bias [dim]; dh0 [nseq][dim][dstate] or NULL.
+ * Each (sequence, channel) runs its forward loop (keeping every state) and
+ * then the reverse loop.  OpenMP spreads channels; each thread sums its dB and
+ * dC into a private buffer, added up in thread order at the end.
+ */
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+int oracle_scan_bwd(int64_t nseq, const int64_t* seq_start, int64_t dim, int64_t dstate,
+                    const double* x, const double* dt, const double* z,
+                    const double* B, const double* C,
+                    const double* A, const double* Dskip, const double* dt_bias,
+                    const double* h0, const double* dy, const double* dh_last,
+                    double* dx, double* ddt, double* dz, double* dB, double* dC,
+                    double* dA, double* dDskip, double* ddt_bias, double* dh0, int nthreads) {
+  if (nseq < 0 || dim < 0 || dstate < 1 || !seq_start) return -1;
+  for (int64_t s = 0; s < nseq; ++s)
+    if (seq_start[s + 1] < seq_start[s]) return -1;
+  const int64_t T = seq_start[nseq];
+  int64_t maxlen = 0;
+  for (int64_t s = 0; s < nseq; ++s)
+    if (seq_start[s + 1] - seq_start[s] > maxlen) maxlen = seq_start[s + 1] - seq_start[s];
+  int nt = 1;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  nt = nthreads;
+#endif
+  double** priv = (double**)calloc((size_t)nt, sizeof(double*));
+  if (!priv) return -1;
+  int failed = 0;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nt) reduction(| : failed)
+#endif
+  {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    double* acc = (double*)calloc((size_t)(2 * T * dstate + 1), sizeof(double));  /* dB, then dC */
+    double* hs = (double*)malloc((size_t)((maxlen + 1) * dstate) * sizeof(double));
+    double* g = (double*)malloc((size_t)dstate * sizeof(double));
+    priv[tid] = acc;
+    if (!acc || !hs || !g) failed = 1;
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+    for (int64_t d = 0; d < dim; ++d) {
+      if (!acc || !hs || !g) continue;
+      const double* Arow = A + d * dstate;
+      for (int64_t n = 0; n < dstate; ++n) dA[d * dstate + n] = 0.0;
+      dDskip[d] = 0.0;
+      ddt_bias[d] = 0.0;
+      for (int64_t s = 0; s < nseq; ++s) {
+        const int64_t t0 = seq_start[s], len = seq_start[s + 1] - t0;
+        /* forward: hs[i] = state before token i (hs[0] = h0), hs[i+1] = after it */
+        for (int64_t n = 0; n < dstate; ++n) hs[n] = h0 ? h0[(s * dim + d) * dstate + n] : 0.0;
+        for (int64_t i = 0; i < len; ++i) {
+          const int64_t t = t0 + i;
+          const double delta = softplus(dt[t * dim + d] + dt_bias[d]);
+          for (int64_t n = 0; n < dstate; ++n)
+            hs[(i + 1) * dstate + n] = exp(delta * Arow[n]) * hs[i * dstate + n] +
+                                       delta * B[t * dstate + n] * x[t * dim + d];
+        }
+        /* reverse: g carries Ā_{t+1} g_{t+1} (dh_last after the last token) */
+        for (int64_t n = 0; n < dstate; ++n) g[n] = dh_last ? dh_last[(s * dim + d) * dstate + n] : 0.0;
+        for (int64_t i = len - 1; i >= 0; --i) {
+          const int64_t t = t0 + i;
+          const double xv = x[t * dim + d], zv = z[t * dim + d], v = dt[t * dim + d] + dt_bias[d];
+          const double delta = softplus(v);
+          const double sz = sigmoid(zv);
+          const double* hcur = hs + (i + 1) * dstate;
+          const double* hprev = hs + i * dstate;
+          double r = Dskip[d] * xv;
+          for (int64_t n = 0; n < dstate; ++n) r += C[t * dstate + n] * hcur[n];
+          const double dyv = dy[t * dim + d];
+          const double dr = dyv * zv * sz;
+          dz[t * dim + d] = dyv * r * sz * (1.0 + zv * (1.0 - sz));
+          double dxv = dr * Dskip[d], ddelta = 0.0;
+          for (int64_t n = 0; n < dstate; ++n) {
+            const double gt = g[n] + dr * C[t * dstate + n];
+            const double abar = exp(delta * Arow[n]);
+            acc[t * dstate + n] += gt * delta * xv;
+            acc[T * dstate + t * dstate + n] += dr * hcur[n];
+            dxv += gt * delta * B[t * dstate + n];
+            ddelta += gt * (Arow[n] * abar * hprev[n] + B[t * dstate + n] * xv);
+            dA[d * dstate + n] += gt * delta * abar * hprev[n];
+            g[n] = abar * gt;
+          }
+          dx[t * dim + d] = dxv;
+          ddt[t * dim + d] = ddelta * sigmoid(v);
+          ddt_bias[d] += ddt[t * dim + d];
+          dDskip[d] += dr * xv;
+        }
+        if (dh0)
+          for (int64_t n = 0; n < dstate; ++n) dh0[(s * dim + d) * dstate + n] = g[n];
+      }
+    }
+    free(hs);
+    free(g);
+  }
+  if (!failed) {
+    for (int64_t i = 0; i < T * dstate; ++i) { dB[i] = 0.0; dC[i] = 0.0; }
+    for (int k = 0; k < nt; ++k) {
+      if (!priv[k]) continue;
+      for (int64_t i = 0; i < T * dstate; ++i) {
+        dB[i] += priv[k][i];
+        dC[i] += priv[k][T * dstate + i];
+      }
+    }
+  }
+  for (int k = 0; k < nt; ++k) free(priv[k]);
+  free(priv);
+  return failed ? -1 : 0;
 }
 
 /* Number of OpenMP threads a call with nthreads <= 0 would use. */

@@ -51,6 +51,8 @@ def _bind(lib):
     lib.oracle_scan_fwd.restype = ctypes.c_int
     lib.oracle_scan_step.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_scan_step.restype = ctypes.c_int
+    lib.oracle_scan_bwd.argtypes = [I64, P, I64, I64] + [P] * 20 + [ctypes.c_int]
+    lib.oracle_scan_bwd.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -103,6 +105,56 @@ def scan_fwd(x, dt, z, B, C, A, D, dt_bias, h0=None, seq_start=None, nthreads: i
     if rc != 0:
         raise RuntimeError("oracle_scan_fwd failed (%d)" % rc)
     return y.reshape(shape), h_last
+
+
+def scan_bwd(x, dt, z, B, C, A, D, dt_bias, dy, h0=None, dh_last=None, seq_start=None, nthreads: int = 0,
+             lib=None):
+    """Gradients of scan_fwd's outputs (y, h_last) in fp64, for upstream gradients dy (shaped like y) and
+    dh_last ([nseq][dim][dstate] or None = zeros).
+
+    Returns a dict: dx, ddt, dz (shaped like x), dB, dC (shaped like B), dA [dim][dstate], dD, ddt_bias [dim],
+    dh0 [nseq][dim][dstate] (the gradient of h0, whether h0 was given or zero).
+    """
+    lib = lib or load()
+    x = _f64(x)
+    shape, bshape = x.shape, np.shape(B)
+    if x.ndim == 3:
+        batch, L, dim = shape
+        if seq_start is None:
+            seq_start = np.arange(batch + 1, dtype=np.int64) * L
+        x = x.reshape(batch * L, dim)
+        dt, z, dy = (_f64(a).reshape(batch * L, dim) for a in (dt, z, dy))
+        B, C = _f64(B).reshape(batch * L, -1), _f64(C).reshape(batch * L, -1)
+    else:
+        dim = shape[1]
+        if seq_start is None:
+            seq_start = np.array([0, shape[0]], dtype=np.int64)
+        dt, z, dy, B, C = _f64(dt), _f64(z), _f64(dy), _f64(B), _f64(C)
+    A, D, dt_bias = _f64(A), _f64(D), _f64(dt_bias)
+    dstate = A.shape[1]
+    T = x.shape[0]
+    seq_start = np.ascontiguousarray(np.asarray(seq_start, dtype=np.int64))
+    nseq = len(seq_start) - 1
+    assert seq_start[0] == 0 and seq_start[-1] == T
+    assert dt.shape == z.shape == dy.shape == (T, dim) and B.shape == C.shape == (T, dstate)
+    h0 = None if h0 is None else _f64(h0).reshape(nseq, dim, dstate)
+    dh_last = None if dh_last is None else _f64(dh_last).reshape(nseq, dim, dstate)
+    out = {k: np.empty((T, dim)) for k in ("dx", "ddt", "dz")}
+    out.update({k: np.empty((T, dstate)) for k in ("dB", "dC")})
+    out["dA"] = np.empty((dim, dstate))
+    out["dD"], out["ddt_bias"] = np.empty(dim), np.empty(dim)
+    out["dh0"] = np.empty((nseq, dim, dstate))
+    rc = lib.oracle_scan_bwd(nseq, _ptr(seq_start), dim, dstate, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C),
+                             _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(dy), _ptr(dh_last),
+                             *(_ptr(out[k]) for k in ("dx", "ddt", "dz", "dB", "dC", "dA", "dD", "ddt_bias", "dh0")),
+                             int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_bwd failed (%d)" % rc)
+    for k in ("dx", "ddt", "dz"):
+        out[k] = out[k].reshape(shape)
+    for k in ("dB", "dC"):
+        out[k] = out[k].reshape(bshape)
+    return out
 
 
 def scan_step(state, x, dt, z, B, C, A, D, dt_bias, nthreads: int = 0, lib=None):
