@@ -7,7 +7,9 @@ synthetic tensors already resident in HBM.  `value` is algorithmic GB/s of
 that prefill (bytes the method must move: x, dt, z in and y out, B and C per
 token, parameters, carry in and out).  The streaming decode (batch 64, D 4096,
 65536 consecutive single-token steps over a ring of 256 input sets, state from
-a 2048-token prefill) is reported in the same line under "decode".
+a 2048-token prefill) is reported in the same line under "decode", and the
+backward on the training shape (batch 4 x 4096 tokens, D 4096: gradients of
+every input, forward states recomputed inside the call) under "backward".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
 """
@@ -37,8 +39,16 @@ TRANS_SLOTS = 4            # a transcendental (exp2, log2, rcp) issues at a quar
 VALU_PER_TD = 64 + 2 + 1 + 1 + 2 + 1 + 4
 TRANS_PER_TD = 16 + 2 + 2
 SLOTS_PER_TD = VALU_PER_TD + TRANS_SLOTS * TRANS_PER_TD
+# Backward, per (token, channel), the plain algorithm: per state the forward recompute (Δ*A mul, exp, Δx*B mul,
+# state FMA), the readout FMA of r, and the reverse step (adjoint FMA, Ā*h_prev, g*u, dA FMA, dΔ FMA, dx FMA,
+# dB and dC products, adjoint decay, and the two channel-sum adds of dB and dC) = 16 x (15 VALU + 1 exp);
+# per token and channel: softplus (2 transcendentals), sigmoid(v) and sigmoid(z) (2 each), silu' and dr, dz,
+# dx, ddt, the dD and ddt_bias sums, 4 bf16 widenings and 3 narrowings (~20 VALU).
+BWD_VALU_PER_TD = 16 * 15 + 20
+BWD_TRANS_PER_TD = 16 + 6
+BWD_SLOTS_PER_TD = BWD_VALU_PER_TD + TRANS_SLOTS * BWD_TRANS_PER_TD
 KERNEL_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_scan.hip"
-TRAFFIC_FILE = ROOT / "profiles" / "scan_fwd_L16384_D4096_traffic.json"
+TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_fwd_L16384_D4096_bwd_B4_L4096_D4096.json"
 
 
 def prefill_bytes(tokens: int, dim: int, io_bytes: int = 2, h0: bool = True, h_last: bool = True, n: int = 16) -> int:
@@ -46,6 +56,15 @@ def prefill_bytes(tokens: int, dim: int, io_bytes: int = 2, h0: bool = True, h_l
     b += tokens * 2 * n * io_bytes           # B, C
     b += dim * n * 4 + dim * 8               # A, D, dt_bias
     b += (dim * n * 4 if h0 else 0) + (dim * n * 4 if h_last else 0)
+    return b
+
+
+def bwd_bytes(tokens: int, dim: int, nseq: int, io_bytes: int = 2, n: int = 16) -> int:
+    b = tokens * dim * 7 * io_bytes          # x, dt, z, dy in; dx, ddt, dz out
+    b += tokens * 2 * n * io_bytes           # B, C in
+    b += tokens * 2 * n * 4                  # dB, dC out (fp32)
+    b += dim * n * 4 * 2 + dim * 8 * 2       # A, D, dt_bias in; dA, dD, ddt_bias out
+    b += nseq * dim * n * 4                  # dh0 out
     return b
 
 
@@ -57,14 +76,17 @@ def kernel_hash() -> str:
     return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if taken on this kernel source."""
+def read_traffic(part: str = "forward"):
+    """HBM bytes per launch (forward prefill kernel) or per call (backward) from the committed rocprofv3
+    counter runs, if they were taken on this kernel source."""
     try:
         t = json.loads(TRAFFIC_FILE.read_text())
     except Exception:
         return None
     if t.get("kernel_source_sha256_16") != kernel_hash():
         return None
+    if part == "backward":
+        return t.get("backward", {}).get("bytes_per_call")
     return t.get("bytes_per_launch")
 
 
@@ -136,6 +158,59 @@ def bench_prefill(steps: int, warmup: int, time_slices: int = 0):
     }
 
 
+def bench_backward(steps: int = 10, warmup: int = 5):
+    """samba_scan_bwd on the training shape: batch 4 x 4096 tokens, D 4096, bf16, no carries in or out."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import scan as S
+
+    W = I.WORKLOADS[5]
+    Bt, L, D = W.batch, W.seqlen, W.dim
+    dev = torch.device("cuda:0")
+    inp = I.make_fwd_inputs_torch(5, Bt * L, D, dev)
+    ex = I.make_bwd_extra_torch(5, Bt * L, D, Bt, dev)
+    shp, bshp = (Bt, L, D), (Bt, L, 16)
+    x, dt, z, dy = (t.view(shp) for t in (inp["x"], inp["dt"], inp["z"], ex["dy"]))
+    B, C = inp["B"].view(bshp), inp["C"].view(bshp)
+    out = {k: torch.empty_like(x) for k in ("dx", "ddt", "dz")}
+    out["dB"], out["dC"] = (torch.empty(bshp, dtype=torch.float32, device=dev) for _ in range(2))
+    out["dA"] = torch.empty(D, 16, dtype=torch.float32, device=dev)
+    out["dD"], out["ddt_bias"] = (torch.empty(D, dtype=torch.float32, device=dev) for _ in range(2))
+    out["dh0"] = torch.empty(Bt, D, 16, dtype=torch.float32, device=dev)
+    a = S.bwd_args(x, dt, z, B, C, inp["A"], inp["D"], inp["dt_bias"], dy, **out)
+    ws = torch.empty(S.bwd_workspace_bytes(a), dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    lib = S.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def call():
+        st = lib.samba_scan_bwd(ctypes.byref(a), sh)
+        if st != 0:
+            raise S.SambaError(st, "samba_scan_bwd")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    td = Bt * L * D
+    nbytes = bwd_bytes(Bt * L, D, Bt)
+    slots = BWD_SLOTS_PER_TD * td / (ms * 1e-3) / 1e12
+    return {"workload": "backward B=4 L=4096 D=4096 N=16 bf16 (training shape), all gradients",
+            "steps": steps, "ms_per_call": ms, "tokens_channels_per_s": td / (ms * 1e-3),
+            "gbs": nbytes / (ms * 1e-3) / 1e9, "algorithmic_bytes": nbytes, "workspace_bytes": ws.numel(),
+            "roofline": {"bound": "alu", "achieved": round(slots, 3), "peak": round(VALU_PEAK_TSLOT, 2),
+                         "unit": "Tslot/s", "frac": round(slots / VALU_PEAK_TSLOT, 4), "traffic": None,
+                         "kernel": "samba_scan_bwd call (checkpoint + backward + finish kernels)",
+                         "slots_per_token_channel": BWD_SLOTS_PER_TD}}
+
+
 def bench_decode(steps: int = 65536, ring: int = 256):
     import torch
     from selective_state_space_05_amd import inputs as I
@@ -203,8 +278,10 @@ def bench_decode(steps: int = 65536, ring: int = 256):
 
 def pmc_summary(fetch_dir: str, write_dir: str, out: str):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; CSV output) of
-    `bench.py --steps 1 --warmup 0 --no-decode --no-cpu --copy-probe` into the
-    per-launch HBM byte summary bench.py reports as roofline.traffic.
+    `bench.py --steps 1 --warmup 0 --no-decode --no-cpu --bwd-steps 1 --copy-probe`
+    into the per-launch HBM byte summary bench.py reports as roofline.traffic
+    (prefill kernel) and backward.roofline.traffic (the three kernels of one
+    backward call).
 
     Each counter is scaled by what it reads for the plain 512 MiB copy of the
     same run (expected 512 MiB fetched and 512 MiB written per dispatch)."""
@@ -220,32 +297,45 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
                 vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
 
+    def pick(vals, *parts):
+        keys = [k for k in vals if all(p in k for p in parts)]
+        assert len(keys) == 1, (parts, keys)
+        return keys[0]
+
+    sel = {"fwd": ("scan_fwd_kernel", ", false>"), "ckpt": ("scan_fwd_kernel", ", true>"),
+           "bwd": ("scan_bwd_kernel<",), "finish": ("scan_bwd_finish_kernel",)}
     out_d = {"kernel_source_sha256_16": kernel_hash(), "unit": "bytes per launch"}
-    scan_key = None
+    got = {k: {} for k in sel}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = per_kernel(d, counter)
         copy = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs]
-        big = max(copy)  # the 512 MiB dispatches (the run also has small copies)
-        expected_kib = (512 << 20) / 1024.0
-        scale = expected_kib / big
-        scans = {k: vs for k, vs in vals.items() if "scan_fwd_kernel" in k}
-        scan_key = max(scans, key=lambda k: len(scans[k]))
-        kib = statistics.median(scans[scan_key])
-        out_d[counter] = {"raw_kib_per_dispatch": kib, "copy_raw_kib_per_dispatch": big, "scale": scale,
-                          "bytes_per_launch": kib * scale * 1024.0}
-    out_d["kernel"] = scan_key[:120]
+        # the 512 MiB probe: the smallest of the large copies (a run may also hold small copies and, when the
+        # copy-ceiling measurement ran, 1 GiB copies)
+        big = min(v for v in copy if v > 0.25 * max(copy))
+        scale = (512 << 20) / 1024.0 / big
+        for name, parts in sel.items():
+            key = pick(vals, *parts)
+            kib = statistics.median(vals[key])
+            got[name][counter] = {"raw_kib_per_dispatch": kib, "scale": scale, "bytes_per_launch": kib * scale * 1024.0,
+                                  "kernel": key[:120]}
+        out_d[counter] = dict(got["fwd"][counter], copy_raw_kib_per_dispatch=big)
+        del out_d[counter]["kernel"]
+    out_d["kernel"] = got["fwd"]["FETCH_SIZE"]["kernel"]
     out_d["bytes_per_launch"] = out_d["FETCH_SIZE"]["bytes_per_launch"] + out_d["WRITE_SIZE"]["bytes_per_launch"]
-    W = 16384
-    out_d["algorithmic_bytes_per_launch"] = prefill_bytes(W, 4096)
-    run = "python3 <repo>/bench.py --steps 1 --warmup 0 --no-decode --no-cpu --copy-probe"
+    out_d["algorithmic_bytes_per_launch"] = prefill_bytes(16384, 4096)
+    bw = {name: {"kernel": got[name]["FETCH_SIZE"]["kernel"], "fetch": got[name]["FETCH_SIZE"]["bytes_per_launch"],
+                 "write": got[name]["WRITE_SIZE"]["bytes_per_launch"]} for name in ("ckpt", "bwd", "finish")}
+    out_d["backward"] = {"kernels": bw, "bytes_per_call": sum(v["fetch"] + v["write"] for v in bw.values()),
+                         "algorithmic_bytes_per_call": bwd_bytes(4 * 4096, 4096, 4)}
+    run = "python3 <repo>/bench.py --steps 1 --warmup 0 --no-decode --no-cpu --bwd-steps 1 --copy-probe"
     out_d["command"] = [
         f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {run}",
         f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {run}",
         f"python bench.py --pmc-summary {fetch_dir} {write_dir} {out}",
     ]
-    out_d["note"] = ("FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by the ratio of the known size "
-                     "of the plain 512 MiB device copy in the same run to what the counter reports for it "
-                     "(FETCH_SIZE reads half, WRITE_SIZE exact).")
+    out_d["note"] = ("FETCH_SIZE and WRITE_SIZE are KiB per dispatch (median over the run's dispatches of each "
+                     "kernel); each is scaled by the ratio of the known size of the plain 512 MiB device copy in "
+                     "the same run to what the counter reports for it (FETCH_SIZE reads half, WRITE_SIZE exact).")
     Path(out).write_text(json.dumps(out_d, indent=1) + "\n")
     print(json.dumps(out_d))
 
@@ -315,6 +405,36 @@ def cpu_baseline(max_oracle_s: float = 30.0):
             "tokens_channels_per_s": done * cl * D / spent}
 
 
+def cpu_baseline_backward(max_oracle_s: float = 30.0):
+    """The fp64 oracle's gradients on the same training-shape backward (all 4 sequences, all channels)."""
+    import numpy as np
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+
+    W = I.WORKLOADS[5]
+    Bt, L, D = W.batch, W.seqlen, W.dim
+    P = I.make_params(5, D)
+    lib = O.load()
+    inp = I.make_fwd_inputs_torch(5, Bt * L, D, "cpu")
+    ex = I.make_bwd_extra_torch(5, Bt * L, D, Bt, "cpu")
+    arrs = [inp[k].double().numpy() for k in ("x", "dt", "z", "B", "C")]
+    dy = ex["dy"].double().numpy()
+    ss = np.arange(Bt + 1, dtype=np.int64) * L
+    # one sequence first: stop there if the whole would exceed the time budget
+    t0 = time.perf_counter()
+    O.scan_bwd(*(a[:L] for a in arrs), P["A"], P["D"], P["dt_bias"], dy[:L], seq_start=ss[:2], lib=lib)
+    one = time.perf_counter() - t0
+    if one * Bt <= max_oracle_s:
+        t0 = time.perf_counter()
+        O.scan_bwd(*arrs, P["A"], P["D"], P["dt_bias"], dy, seq_start=ss, lib=lib)
+        spent, nseq = time.perf_counter() - t0, Bt
+    else:
+        spent, nseq = one, 1
+    return {"value": nseq * L * D / spent, "unit": "tokens*channels/s", "cores": O.max_threads(lib),
+            "kind": "oracle", "sample": "%d of the 4 sequences (4096 tokens, all 4096 channels), fp64 oracle "
+                                        "gradients, %.1f s" % (nseq, spent)}
+
+
 def cpu_baseline_decode(steps: int = 1024, max_oracle_s: float = 15.0):
     """The fp64 oracle's decode step on the full batch-64, D-4096 state, chained over the first `steps`
     steps of the input ring (stopping early past ~max_oracle_s); steps/s is extrapolated from that sample."""
@@ -351,6 +471,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=65536)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
+    ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--time-slices", type=int, default=0, help="force the prefill's waves per time chunk (0 = auto)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (untimed), the reference kernel for HBM byte counters")
@@ -366,7 +488,8 @@ def main():
         sys.exit(2)
 
     pf = bench_prefill(args.steps, args.warmup, args.time_slices)
-    ceiling = copy_ceiling()
+    # (counter runs skip the ceiling measurement: its 1 GiB copies are not needed there)
+    ceiling = None if args.copy_probe else copy_ceiling()
     if args.copy_probe:
         copy_probe()
     achieved = SLOTS_PER_TD * pf["launch_td"] / (pf["launch_ms"] * 1e-3) / 1e12
@@ -389,8 +512,8 @@ def main():
                    "dstate": 16, "chunks": 8, "io": "bf16"},
         "tokens_channels_per_s": pf["tokens_channels_per_s"],
         "hbm_frac": pf["gbs"] / HBM_PEAK_GBS,
-        "copy_ceiling_gbs": round(ceiling, 1),
-        "copy_frac": pf["gbs"] / ceiling,
+        "copy_ceiling_gbs": round(ceiling, 1) if ceiling else None,
+        "copy_frac": pf["gbs"] / ceiling if ceiling else None,
         "plan": pf["plan"],
         "call_us": pf["call_us"],
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TSLOT, 2),
@@ -404,12 +527,17 @@ def main():
         dec["roofline"] = {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
                            "kernel": "scan_step_kernel<bf16,bf16>"}
-        dec["copy_frac"] = dec["gbs"] / ceiling
+        dec["copy_frac"] = dec["gbs"] / ceiling if ceiling else None
         line["decode"] = dec
+    if not args.no_bwd:
+        line["backward"] = bench_backward(args.bwd_steps)
+        line["backward"]["roofline"]["traffic"] = read_traffic("backward")
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
         if not args.no_decode:
             line["cpu_baseline"]["decode"] = cpu_baseline_decode()
+        if not args.no_bwd:
+            line["cpu_baseline"]["backward"] = cpu_baseline_backward()
     print(json.dumps(line), flush=True)
 
 

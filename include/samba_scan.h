@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SAMBA_SCAN_ABI_VERSION 1
+#define SAMBA_SCAN_ABI_VERSION 2
 #define SAMBA_DSTATE 16
 
 typedef enum {
@@ -58,7 +58,8 @@ typedef enum {
   SAMBA_ERR_ALIASING = 5,      /* an output overlaps an input it must not overlap */
   SAMBA_ERR_UNSUPPORTED = 6,   /* dstate != 16, or time_slices not 0/1/2/4/8/16 */
   SAMBA_ERR_BAD_STRUCT = 7,    /* struct_size does not match this header */
-  SAMBA_ERR_HIP = 8            /* the HIP runtime refused the launch */
+  SAMBA_ERR_HIP = 8,           /* the HIP runtime refused the launch */
+  SAMBA_ERR_WORKSPACE = 9      /* workspace NULL, too small or misaligned (backward) */
 } samba_status;
 
 typedef enum { SAMBA_F32 = 0, SAMBA_BF16 = 1 } samba_dtype;
@@ -118,6 +119,67 @@ typedef struct {
   const float *A, *D, *dt_bias;
   void* y;                     /* [batch][dim] */
 } samba_scan_step_args;
+
+/*
+ * Backward of the prefill: gradients of every input of samba_scan_fwd for the
+ * loss sum(dy * y) + sum(dh_last * h_last), i.e. the reverse-mode derivative
+ * of the operation above (the pages train Samba with this scan: page 1,
+ * section 实现细节 -> 训练配置; hackernoon page, §2.1.2).  Per token t of a
+ * sequence and channel d, with v = dt_raw + dt_bias, Δ = softplus(v) and
+ * r = sum_n C_t[n] h_t[n] + D x_t:
+ *     g_t[n]  = dr_t C_t[n] + Ā_{t+1}[n] g_{t+1}[n]   adjoint of h_t (dh_last after the last token)
+ *     dr_t    = dy_t silu(z_t);       dz_t = dy_t r_t silu'(z_t)
+ *     dx_t    = dr_t D + Δ_t sum_n g_t[n] B_t[n]
+ *     ddt_t   = sigmoid(v) sum_n g_t[n] (A[n] Ā_t[n] h_{t-1}[n] + B_t[n] x_t)
+ *     dB_t[n] = sum_d g_t[n] Δ_t x_t,   dC_t[n] = sum_d dr_t h_t[n]
+ *     dA[d][n] = sum g_t[n] Δ_t Ā_t[n] h_{t-1}[n],  dD[d] = sum dr_t x_t,  ddt_bias[d] = sum ddt_t
+ *     dh0[n]  = Ā_first[n] g_first[n]   (dh_last for an empty sequence)
+ * The forward states are recomputed inside the call (from x, dt, B and h0);
+ * nothing from a previous samba_scan_fwd call is needed.
+ *
+ * Shapes and dtypes: x, dt, z, B, C, cu_seqlens, A, D, dt_bias, h0 exactly as
+ * for samba_scan_fwd (in_dtype).  dy [tokens][dim] and the outputs dx, ddt, dz
+ * [tokens][dim] have in_dtype too.  dB, dC [tokens][16], dA [dim][16], dD,
+ * ddt_bias [dim] are fp32 and are overwritten (not accumulated).  dh_last
+ * (input) and dh0 (output) are fp32 [nseq][dim][16] and optional (NULL:
+ * zeros / not written).  Alignment: as for the forward, plus dB, dC, dA,
+ * dh_last, dh0 16 bytes, dy/dx/ddt/dz their element size, workspace 256
+ * bytes.  No output may overlap an input or another output.
+ *
+ * Workspace: caller-owned device memory of at least
+ * samba_scan_bwd_workspace_size() bytes (checkpointed states every 8 tokens,
+ * per-tile partial sums of dB and dC, per-sequence partial sums of dA, dD and
+ * ddt_bias).  Calls that overlap in time must use different workspaces.
+ * time_slices: 0 = automatic, else 1, 2, 4 or 8 waves per time chunk of a
+ * channel tile (results agree to fp32 rounding; bitwise reproducible for a
+ * given choice).
+ */
+typedef struct {
+  uint32_t struct_size;        /* = sizeof(samba_scan_bwd_args) */
+  int32_t batch, seqlen, dim, dstate;
+  const int32_t* cu_seqlens;   /* optional, device */
+  int32_t nseq;
+  int32_t in_dtype;            /* x, dt, z, B, C, dy, dx, ddt, dz */
+  int32_t time_slices;         /* 0 = automatic */
+  const void *x, *dt, *z;
+  const void *B, *C;
+  const float *A, *D, *dt_bias;
+  const float* h0;             /* optional */
+  const void* dy;
+  const float* dh_last;        /* optional */
+  void *dx, *ddt, *dz;
+  float *dB, *dC;
+  float *dA, *dD, *ddt_bias;
+  float* dh0;                  /* optional */
+  void* workspace;
+  size_t workspace_bytes;
+} samba_scan_bwd_args;
+
+/* Host-only: bytes of workspace samba_scan_bwd needs for these sizes (pointers are not examined). */
+samba_status samba_scan_bwd_workspace_size(const samba_scan_bwd_args* args, size_t* bytes);
+
+/* Enqueue the backward.  See samba_scan_bwd_args. */
+samba_status samba_scan_bwd(const samba_scan_bwd_args* args, void* stream);
 
 /* Enqueue a prefill scan.  See samba_scan_fwd_args. */
 samba_status samba_scan_fwd(const samba_scan_fwd_args* args, void* stream);

@@ -195,6 +195,7 @@ struct FwdParams {
   const float* h0;
   float* h_last;
   void* y;
+  float* ckpt;           // checkpoint variant: state before every 8th token of each sequence
   const int32_t* cu;
   int64_t total_tokens;
   int32_t seqlen;        // tokens per sequence when cu == nullptr
@@ -337,12 +338,18 @@ __device__ __forceinline__ void store_y(const LaneCtx<Tin, Tout, K>& L, rsrc_t r
   if (L.dvalid) bstore(ry, L.out_off[j], yv, static_cast<Tout*>(nullptr));
 }
 
+// Checkpoint slot of the state before token 8*j of the sequence that starts
+// at token row `start` and is the s-th one: (start / 8) + s + j.  Distinct
+// sequences never share a slot, and all slots fit in tokens / 8 + nseq + 1.
+__device__ __forceinline__ int64_t ckpt_slot(int64_t start, int s, int j) { return (start >> 3) + s + j; }
+
 // ---------------------------------------------------------------------------
 // Prefill kernel.  W = waves splitting each time chunk (1 = plain sequential
 // scan); TPW = channel tiles per workgroup (W == 1 only); K = tokens per wave
-// slice (8 or 16).
+// slice (8 or 16).  kCkpt: instead of y, write the state before every 8th
+// token of each sequence to p.ckpt (the backward's recomputation points).
 // ---------------------------------------------------------------------------
-template <typename Tin, typename Tout, int W, int TPW, int K>
+template <typename Tin, typename Tout, int W, int TPW, int K, bool kCkpt = false>
 __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
   static_assert(W == 1 || TPW == 1, "time slices and tile packing are exclusive");
   static_assert(K == 8 || K == 16, "slice length");
@@ -412,6 +419,12 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
   const float4* sC4 = s_bc[wave][1];
   float h[kSPL] = {L.hinit[0], L.hinit[1], L.hinit[2], L.hinit[3]};
   Tout* const yout = static_cast<Tout*>(p.y);
+  // checkpoint of the state before token i (a multiple of 8) of this sequence
+  auto put_ckpt = [&](int i, const float (&hv)[kSPL]) {
+    if (L.dvalid)
+      reinterpret_cast<float4*>(p.ckpt + (ckpt_slot(L.start, s, i >> 3) * p.dim + L.d) * kN)[L.g] =
+          make_float4(hv[0], hv[1], hv[2], hv[3]);
+  };
 
   if constexpr (W == 1) {
     // ---------------- sequential scan over the whole sequence ----------------
@@ -428,11 +441,17 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
       float xv[K / 4], zv[K / 4], dl[K / 4], uu[K / 4];
       decode_raw<Tin, Tout, K>(cur, L, nv, xv, zv, dl, uu);
       publish_du<K>(s_du[wave], L.c, L.g, dl, uu);
-      const rsrc_t ry = make_rsrc_rows(yout + t0 * p.dim, ntok - i0, static_cast<uint32_t>(p.dim));
+      // (the checkpoint variant writes no y: an empty resource)
+      const rsrc_t ry = make_rsrc_rows(kCkpt ? yout : yout + t0 * p.dim, kCkpt ? 0 : ntok - i0,
+                                       static_cast<uint32_t>(p.dim));
+      if constexpr (kCkpt) put_ckpt(i0, h);
       wave_lds_sync();
 #pragma unroll
       for (int j = 0; j < K / 4; ++j) {
         if (4 * j >= nv) break;
+        if constexpr (kCkpt && K == 16) {
+          if (j == 2) put_ckpt(i0 + 8, h);
+        }
         float4 bv[4], cv[4];
         float dk[4], uk[4];
         fetch_du(s_du[wave], j, L.c, dk, uk);
@@ -450,8 +469,10 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
           h[3] = fmaf(__builtin_amdgcn_exp2f(dk[q] * L.A2[3]), h[3], uk[q] * bv[q].w);
           pr[q] = fmaf(cv[q].w, h[3], fmaf(cv[q].z, h[2], fmaf(cv[q].y, h[1], cv[q].x * h[0])));
         }
-        const float yraw = quad_transpose_sum_lds(s_red[wave], L.c, L.g, pr[0], pr[1], pr[2], pr[3]);
-        store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
+        if constexpr (!kCkpt) {
+          const float yraw = quad_transpose_sum_lds(s_red[wave], L.c, L.g, pr[0], pr[1], pr[2], pr[3]);
+          store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
+        }
       }
       wave_lds_sync();
     };
@@ -539,11 +560,18 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
       }
 
       // phase 3: replay the slice from the true carry-in, read out, gate, store
-      const rsrc_t ry = make_rsrc_rows(yout + t0 * p.dim, ntok - i0, static_cast<uint32_t>(p.dim));
+      const rsrc_t ry = make_rsrc_rows(kCkpt ? yout : yout + t0 * p.dim, kCkpt ? 0 : ntok - i0,
+                                       static_cast<uint32_t>(p.dim));
+      if constexpr (kCkpt) {
+        if (nv > 0) put_ckpt(i0, hin);
+      }
 #pragma unroll
       for (int i = 0; i < kSPL; ++i) h[i] = hin[i];
 #pragma unroll
       for (int j = 0; j < K / 4; ++j) {
+        if constexpr (kCkpt && K == 16) {
+          if (j == 2 && nv > 8) put_ckpt(i0 + 8, h);
+        }
         float pr[4];
         float4 cq[4];
 #pragma unroll
@@ -556,9 +584,11 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
           for (int i = 0; i < kSPL; ++i) h[i] = fmaf(ak[k][i], h[i], bk[k][i]);
           pr[q] = fmaf(cv.w, h[3], fmaf(cv.z, h[2], fmaf(cv.y, h[1], cv.x * h[0])));
         }
-        if (4 * j < nv) {
-          const float yraw = quad_transpose_sum_lds(s_red[wave], L.c, L.g, pr[0], pr[1], pr[2], pr[3]);
-          store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
+        if constexpr (!kCkpt) {
+          if (4 * j < nv) {
+            const float yraw = quad_transpose_sum_lds(s_red[wave], L.c, L.g, pr[0], pr[1], pr[2], pr[3]);
+            store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
+          }
         }
       }
       if (wave == W - 1) s_carry[buf][L.lane] = make_float4(h[0], h[1], h[2], h[3]);
@@ -575,6 +605,347 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
       reinterpret_cast<float4*>(p.h_last + (static_cast<int64_t>(s) * p.dim + L.d) * kN)[L.g] =
           make_float4(h[0], h[1], h[2], h[3]);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Backward (gradients of the prefill).  Per sequence and channel the adjoint
+// g_t = dr_t C_t + Ā_{t+1} g_{t+1} runs from the last token to the first, and
+// every gradient term of token t needs g_t together with the forward states
+// h_{t-1}, h_t.  Decomposition (same lanes as the forward: a quad of lanes per
+// channel, 4 states per lane, 16 channels per wave):
+//   * the forward states are recomputed from checkpoints (the state before
+//     every 8th token, written by the forward kernel's checkpoint variant);
+//   * a workgroup owns one (sequence, 16-channel tile); its W waves split each
+//     time chunk of 8W tokens into slices of 8, and chunks run from the end of
+//     the sequence to its start;
+//   * each wave recomputes its slice forward from its checkpoint, keeping Ā_t
+//     and h_t in registers, and in the same sweep forms the slice's adjoint
+//     transfer pair (P = product of Ā, Ĝ = sum_t (prod_{r<=t} Ā_r) dr_t C_t):
+//     Ĝ is the adjoint leaving the slice's start when none enters its end;
+//   * after one barrier each wave folds the later slices' pairs into the
+//     adjoint entering the chunk, then runs the reverse sweep, where every
+//     gradient term is formed; the leftmost wave's result is the adjoint
+//     entering the previous chunk (LDS, double buffered);
+//   * dB_t and dC_t are sums over all channels: each wave sums its 16 channels
+//     through LDS and writes one partial row per token and tile; dA, dD and
+//     ddt_bias are summed over the sequence in registers and written per
+//     sequence; a final kernel adds the partials in a fixed order (no atomics,
+//     bitwise reproducible).
+// ---------------------------------------------------------------------------
+constexpr int kBK = 8;      // tokens per backward slice = checkpoint interval
+constexpr int kParW = 20;   // per-sequence partial row: dA[16], dD, ddt_bias, 2 pad (16-byte rows)
+
+struct BwdParams {
+  const void *x, *dt, *z, *B, *C, *dy;
+  const float *A, *Dskip, *bias;
+  const float* dh_last;
+  const float* ckpt;      // [slots][dim][16]
+  void *dx, *ddt, *dz;
+  float* dbc;             // [ntiles][total_tokens][32]: per-tile dB (0..15) and dC (16..31)
+  float* dpar;            // [nseq][dim][kParW]
+  float* dh0;
+  const int32_t* cu;
+  int64_t total_tokens;
+  int32_t seqlen, dim, ntiles, nblocks;
+};
+
+template <typename T, int W>
+__global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
+  constexpr int K = kBK;
+  __shared__ float4 s_bc[W][2][K * kN / 4];   // B, C rows of the slice (fp32)
+  __shared__ float4 s_sc[W][K][kCPW];         // per token and channel: (Δ, Δx, dr, 0)
+  __shared__ float4 s_red[W][kCPW][4];        // quad transposed sums
+  __shared__ float s_dbc[W][2][kCPW][32];     // two tokens' dB/dC partials of each channel
+  __shared__ float4 s_agg[2][W][2][64];       // slice (P, Ĝ), double buffered
+  __shared__ float4 s_carry[2][64];           // adjoint entering a chunk from the right, double buffered
+  __shared__ float4 s_fin[W][64];             // end of sequence: per-wave dA
+  __shared__ float2 s_fin2[W][kCPW];          // end of sequence: per-wave (dD, ddt_bias)
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int logical = xcd_remap(blockIdx.x, p.nblocks);
+  const int s = logical / p.ntiles;
+  const int tile = logical - s * p.ntiles;
+  const int lane = threadIdx.x & 63, g = lane & 3, c = lane >> 2;
+  const int d = tile * kCPW + c;
+  const bool dvalid = d < p.dim;
+  const int dc = dvalid ? d : p.dim - 1;
+  int64_t start, end;
+  if (p.cu) {
+    int64_t a = p.cu[s], b = p.cu[s + 1];
+    a = a < 0 ? 0 : (a > p.total_tokens ? p.total_tokens : a);
+    b = b < a ? a : (b > p.total_tokens ? p.total_tokens : b);
+    start = a;
+    end = b;
+  } else {
+    start = static_cast<int64_t>(s) * p.seqlen;
+    end = start + p.seqlen;
+  }
+  const int ntok = static_cast<int>(end - start);
+  float A2[kSPL], Ar[kSPL];
+  {
+    const float4 a4 = reinterpret_cast<const float4*>(p.A + static_cast<int64_t>(dc) * kN)[g];
+    Ar[0] = a4.x; Ar[1] = a4.y; Ar[2] = a4.z; Ar[3] = a4.w;
+#pragma unroll
+    for (int i = 0; i < kSPL; ++i) A2[i] = Ar[i] * kLog2e;
+  }
+  const float dsk = p.Dskip[dc], bias = p.bias[dc];
+  const uint32_t dim = static_cast<uint32_t>(p.dim);
+  uint32_t in_off[K / 4];
+#pragma unroll
+  for (int j = 0; j < K / 4; ++j)
+    in_off[j] = ((static_cast<uint32_t>(4 * j + g)) * dim + static_cast<uint32_t>(d)) * static_cast<uint32_t>(sizeof(T));
+  const int bc_lds = (lane >> 3) * kN + (lane & 7) * 2;   // 2 of the 8 x 16 B (and C) values per lane
+  const uint32_t bc_off = static_cast<uint32_t>(bc_lds) * static_cast<uint32_t>(sizeof(T));
+  float* sB = reinterpret_cast<float*>(s_bc[wave][0]);
+  float* sC = reinterpret_cast<float*>(s_bc[wave][1]);
+  const float4* sB4 = s_bc[wave][0];
+  const float4* sC4 = s_bc[wave][1];
+
+  // adjoint entering the sequence's last token from the right: dh_last
+  float gh[kSPL] = {0.f, 0.f, 0.f, 0.f};
+  if (p.dh_last) {
+    const float4 v = reinterpret_cast<const float4*>(p.dh_last + (static_cast<int64_t>(s) * p.dim + dc) * kN)[g];
+    gh[0] = v.x; gh[1] = v.y; gh[2] = v.z; gh[3] = v.w;
+  }
+  if (wave == 0) s_carry[1][lane] = make_float4(gh[0], gh[1], gh[2], gh[3]);
+
+  constexpr int chunk = W * K;
+  const int nchunks = (ntok + chunk - 1) / chunk;
+  float dAacc[kSPL] = {0.f, 0.f, 0.f, 0.f};
+  float dDacc = 0.f, dbacc = 0.f;
+
+  for (int it = 0; it < nchunks; ++it) {
+    const int ci = nchunks - 1 - it;
+    const int buf = it & 1;
+    const int i0 = ci * chunk + wave * K;
+    const int rem = ntok - i0;
+    const int nv = rem <= 0 ? 0 : (rem < K ? rem : K);
+    const int64_t t0 = start + i0;
+    const int64_t row0 = t0 * p.dim;
+
+    // ---- loads: this lane's tokens of x, dt, z, dy; the slice's B, C; the checkpoint
+    T xr[K / 4], dtr[K / 4], zr[K / 4], dyr[K / 4];
+    uint32_t bw[RawSlice<T, K>::kWords], cw[RawSlice<T, K>::kWords];
+    {
+      const rsrc_t rx = make_rsrc_rows(static_cast<const T*>(p.x) + row0, rem, dim);
+      const rsrc_t rd = make_rsrc_rows(static_cast<const T*>(p.dt) + row0, rem, dim);
+      const rsrc_t rz = make_rsrc_rows(static_cast<const T*>(p.z) + row0, rem, dim);
+      const rsrc_t ry = make_rsrc_rows(static_cast<const T*>(p.dy) + row0, rem, dim);
+#pragma unroll
+      for (int j = 0; j < K / 4; ++j) {
+        bload(rx, in_off[j], xr[j]);
+        bload(rd, in_off[j], dtr[j]);
+        bload(rz, in_off[j], zr[j]);
+        bload(ry, in_off[j], dyr[j]);
+      }
+      const rsrc_t rb = make_rsrc_rows(static_cast<const T*>(p.B) + t0 * kN, rem, kN);
+      const rsrc_t rc = make_rsrc_rows(static_cast<const T*>(p.C) + t0 * kN, rem, kN);
+      bload_words(rb, bc_off, bw);
+      bload_words(rc, bc_off, cw);
+    }
+    float hs[kSPL] = {0.f, 0.f, 0.f, 0.f};
+    if (nv > 0) {
+      const float4 v = reinterpret_cast<const float4*>(
+          p.ckpt + (ckpt_slot(start, s, i0 >> 3) * p.dim + dc) * kN)[g];
+      hs[0] = v.x; hs[1] = v.y; hs[2] = v.z; hs[3] = v.w;
+    }
+    {
+      float v[K / 4];
+      widen_words<T, K>(bw, v);
+      lds_put<K / 4>(sB + bc_lds, v);
+      widen_words<T, K>(cw, v);
+      lds_put<K / 4>(sC + bc_lds, v);
+    }
+    // ---- per-token scalars of this lane's tokens (4j + g)
+    float xk[K / 4], dyk[K / 4], dlk[K / 4], drk[K / 4], sigv[K / 4], dsl[K / 4];
+#pragma unroll
+    for (int j = 0; j < K / 4; ++j) {
+      const bool ok = dvalid && (4 * j + g) < nv;
+      const float xv = widen(xr[j]), zv = widen(zr[j]), dyv = widen(dyr[j]);
+      const float v = widen(dtr[j]) + bias;
+      const float delta = softplus_f32(v);
+      const float sz = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zv * kLog2e));
+      sigv[j] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
+      dsl[j] = sz * fmaf(zv, 1.0f - sz, 1.0f);
+      xk[j] = xv;
+      dyk[j] = dyv;
+      dlk[j] = ok ? delta : 0.0f;
+      drk[j] = ok ? dyv * zv * sz : 0.0f;
+      s_sc[wave][4 * j + g][c] = make_float4(dlk[j], ok ? delta * xv : 0.0f, drk[j], 0.0f);
+    }
+    wave_lds_sync();
+
+    // ---- forward recompute of the slice; adjoint transfer pair (P, Ĝ)
+    float ak[K][kSPL], hk[K][kSPL];
+    float P[kSPL], G[kSPL];
+    float rr[K / 4];
+#pragma unroll
+    for (int jj = 0; jj < K / 4; ++jj) {
+      float pr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = 4 * jj + q;
+        const float4 sc = s_sc[wave][k][c];
+        const float4 bv = sB4[k * 4 + g], cv = sC4[k * 4 + g];
+        const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+        const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < kSPL; ++i) {
+          ak[k][i] = __builtin_amdgcn_exp2f(sc.x * A2[i]);
+          const float prev = (k == 0) ? hs[i] : hk[k - 1][i];
+          hk[k][i] = fmaf(ak[k][i], prev, sc.y * bb[i]);
+          P[i] = (k == 0) ? ak[k][i] : P[i] * ak[k][i];
+          const float drc = sc.z * cc[i];
+          G[i] = (k == 0) ? P[i] * drc : fmaf(P[i], drc, G[i]);
+          acc = fmaf(cc[i], hk[k][i], acc);
+        }
+        pr[q] = acc;
+      }
+      rr[jj] = quad_transpose_sum_lds(s_red[wave], c, g, pr[0], pr[1], pr[2], pr[3]);
+    }
+    s_agg[buf][wave][0][lane] = make_float4(P[0], P[1], P[2], P[3]);
+    s_agg[buf][wave][1][lane] = make_float4(G[0], G[1], G[2], G[3]);
+    __syncthreads();
+
+    // ---- adjoint entering this slice's end: fold the later slices into the chunk's incoming adjoint
+    {
+      const float4 v = s_carry[buf ^ 1][lane];
+      gh[0] = v.x; gh[1] = v.y; gh[2] = v.z; gh[3] = v.w;
+    }
+    for (int w2 = W - 1; w2 > wave; --w2) {
+      const float4 P2 = s_agg[buf][w2][0][lane];
+      const float4 G2 = s_agg[buf][w2][1][lane];
+      gh[0] = fmaf(P2.x, gh[0], G2.x);
+      gh[1] = fmaf(P2.y, gh[1], G2.y);
+      gh[2] = fmaf(P2.z, gh[2], G2.z);
+      gh[3] = fmaf(P2.w, gh[3], G2.w);
+    }
+
+    // ---- reverse sweep: every gradient term
+    const int prow = rem < 0 ? 0 : rem;
+    const rsrc_t rbc = make_rsrc_rows(p.dbc + (static_cast<int64_t>(tile) * p.total_tokens + t0) * 32, prow, 32u);
+    float sau_t[K / 4], sgb_t[K / 4];
+#pragma unroll
+    for (int jj = K / 4 - 1; jj >= 0; --jj) {
+      float sau[4], sgb[4];
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        const int k = 4 * jj + q;
+        const float4 sc = s_sc[wave][k][c];
+        const float4 bv = sB4[k * 4 + g], cv = sC4[k * 4 + g];
+        const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+        const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
+        float sa = 0.f, sb = 0.f, db[4], dcv[4];
+#pragma unroll
+        for (int i = 0; i < kSPL; ++i) {
+          const float gi = fmaf(sc.z, cc[i], gh[i]);
+          const float prev = (k == 0) ? hs[i] : hk[k - 1][i];
+          const float gu = gi * (ak[k][i] * prev);
+          dAacc[i] = fmaf(gu, sc.x, dAacc[i]);
+          sa = fmaf(gu, Ar[i], sa);
+          sb = fmaf(gi, bb[i], sb);
+          db[i] = gi * sc.y;
+          dcv[i] = sc.z * hk[k][i];
+          gh[i] = ak[k][i] * gi;
+        }
+        sau[q] = sa;
+        sgb[q] = sb;
+        // this token's dB / dC partials of the wave's 16 channels
+        float* row = s_dbc[wave][k & 1][c];
+        *reinterpret_cast<float4*>(row + 4 * g) = make_float4(db[0], db[1], db[2], db[3]);
+        *reinterpret_cast<float4*>(row + 16 + 4 * g) = make_float4(dcv[0], dcv[1], dcv[2], dcv[3]);
+        if ((k & 1) == 0) {
+          // tokens k (lanes 0..31) and k+1 (lanes 32..63): sum output (lane & 31) over the 16 channels
+          wave_lds_sync();
+          const int tt = lane >> 5, o = lane & 31;
+          float acc = 0.f;
+#pragma unroll
+          for (int c2 = 0; c2 < kCPW; ++c2) acc += s_dbc[wave][tt][c2][o];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rbc,
+                                                static_cast<uint32_t>(((k + tt) * 32 + o) * 4), 0, 0);
+          wave_lds_sync();
+        }
+      }
+      sau_t[jj] = quad_transpose_sum_lds(s_red[wave], c, g, sau[0], sau[1], sau[2], sau[3]);
+      sgb_t[jj] = quad_transpose_sum_lds(s_red[wave], c, g, sgb[0], sgb[1], sgb[2], sgb[3]);
+    }
+
+    // ---- per-token outputs of this lane's tokens
+    {
+      const rsrc_t ox = make_rsrc_rows(static_cast<T*>(p.dx) + row0, rem, dim);
+      const rsrc_t od = make_rsrc_rows(static_cast<T*>(p.ddt) + row0, rem, dim);
+      const rsrc_t oz = make_rsrc_rows(static_cast<T*>(p.dz) + row0, rem, dim);
+#pragma unroll
+      for (int j = 0; j < K / 4; ++j) {
+        const bool ok = dvalid && (4 * j + g) < nv;
+        const float r = fmaf(dsk, xk[j], rr[j]);
+        const float dzv = dyk[j] * r * dsl[j];
+        const float dxv = fmaf(drk[j], dsk, dlk[j] * sgb_t[j]);
+        const float ddtv = fmaf(sgb_t[j], xk[j], sau_t[j]) * sigv[j];
+        if (ok) {
+          dDacc = fmaf(drk[j], xk[j], dDacc);
+          dbacc += ddtv;
+          bstore(ox, in_off[j], dxv, static_cast<T*>(nullptr));
+          bstore(od, in_off[j], ddtv, static_cast<T*>(nullptr));
+          bstore(oz, in_off[j], dzv, static_cast<T*>(nullptr));
+        }
+      }
+    }
+    if (wave == 0) s_carry[buf][lane] = make_float4(gh[0], gh[1], gh[2], gh[3]);
+    wave_lds_sync();
+  }
+
+  // ---- end of the sequence: dh0 (wave 0 holds the adjoint leaving the first token), parameter partials
+  if (wave == 0 && p.dh0 && dvalid)
+    reinterpret_cast<float4*>(p.dh0 + (static_cast<int64_t>(s) * p.dim + d) * kN)[g] =
+        make_float4(gh[0], gh[1], gh[2], gh[3]);
+  dDacc = quad_allsum(dDacc);
+  dbacc = quad_allsum(dbacc);
+  s_fin[wave][lane] = make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
+  if (g == 0) s_fin2[wave][c] = make_float2(dDacc, dbacc);
+  __syncthreads();
+  if (wave == 0 && dvalid) {
+    float4 a = s_fin[0][lane];
+    float2 b = s_fin2[0][c];
+#pragma unroll
+    for (int w2 = 1; w2 < W; ++w2) {
+      const float4 a2 = s_fin[w2][lane];
+      const float2 b2 = s_fin2[w2][c];
+      a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+      b.x += b2.x; b.y += b2.y;
+    }
+    float* row = p.dpar + (static_cast<int64_t>(s) * p.dim + d) * kParW;
+    reinterpret_cast<float4*>(row)[g] = a;
+    if (g == 0) { row[16] = b.x; row[17] = b.y; }
+  }
+}
+
+// dB, dC: sum of the per-tile partial rows; dA, dD, ddt_bias: sum of the
+// per-sequence partial rows.  One thread per output element, fixed order.
+__global__ __launch_bounds__(256) void scan_bwd_finish_kernel(const float* dbc, const float* dpar, float* dB, float* dC,
+                                                              float* dA, float* dD, float* dbias, int64_t total_tokens,
+                                                              int32_t ntiles, int32_t nseq, int32_t dim) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n1 = total_tokens * 32;
+  if (idx < n1) {
+    float acc = 0.f;
+    for (int t = 0; t < ntiles; ++t) acc += dbc[static_cast<int64_t>(t) * n1 + idx];
+    const int64_t row = idx >> 5;
+    const int o = static_cast<int>(idx & 31);
+    if (o < 16) dB[row * 16 + o] = acc;
+    else dC[row * 16 + (o - 16)] = acc;
+    return;
+  }
+  const int64_t i2 = idx - n1;
+  if (i2 >= static_cast<int64_t>(dim) * 18) return;
+  const int64_t dd = i2 / 18;
+  const int q = static_cast<int>(i2 - dd * 18);
+  float acc = 0.f;
+  for (int s2 = 0; s2 < nseq; ++s2) acc += dpar[(static_cast<int64_t>(s2) * dim + dd) * kParW + q];
+  if (q < 16) dA[dd * 16 + q] = acc;
+  else if (q == 16) dD[dd] = acc;
+  else dbias[dd] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -701,6 +1072,51 @@ struct FwdPlan {
   FwdParams prm;
 };
 
+// Waves per time chunk.  Enough (sequence, tile) waves for two per SIMD:
+// plain sequential scan.  Otherwise aim at four waves per SIMD by splitting
+// time, but never into slices that the average sequence cannot fill.
+int choose_time_slices(int64_t nseq, int64_t ntiles, int64_t tokens, int wmax, int (*slice)(int)) {
+  const int64_t cus = device_cu_count();
+  const int64_t base = nseq * ntiles;
+  const int64_t avg_len = nseq > 0 ? tokens / nseq : 0;
+  int W = 1;
+  if (base < cus * 8) {
+    while (W < wmax && base * W < cus * 16 && static_cast<int64_t>(W) * 2 * slice(W * 2) <= avg_len) W *= 2;
+  }
+  return W;
+}
+
+samba_status make_fwd_plan(const void* x, const void* dt, const void* z, const void* B, const void* C, const float* A,
+                           const float* D, const float* bias, const float* h0, const int32_t* cu, int64_t nseq,
+                           int32_t batch, int32_t seqlen, int32_t dim, int ts, FwdPlan* plan) {
+  const int64_t tokens = static_cast<int64_t>(batch) * seqlen;
+  const int ntiles = (dim + kCPW - 1) / kCPW;
+  const int W = ts ? ts : choose_time_slices(nseq, ntiles, tokens, 16, slice_tokens);
+  const int tpw = (W == 1) ? 4 : 1;
+  const int ngroups = (ntiles + tpw - 1) / tpw;
+  FwdParams& p = plan->prm;
+  p = FwdParams{};
+  p.x = x; p.dt = dt; p.z = z; p.B = B; p.C = C;
+  p.A = A; p.Dskip = D; p.bias = bias;
+  p.h0 = h0;
+  p.cu = cu;
+  p.total_tokens = tokens;
+  p.seqlen = seqlen;
+  p.dim = dim;
+  p.ntiles = ntiles;
+  p.tiles_per_wg = tpw;
+  p.ngroups = ngroups;
+  const int64_t nblocks = nseq * ngroups;
+  if (nblocks > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  p.nblocks = static_cast<int32_t>(nblocks);
+  plan->W = W;
+  plan->tpw = tpw;
+  plan->threads = 64 * W * tpw;
+  plan->grid = static_cast<int>(nblocks);
+  plan->nseq = nseq;
+  return SAMBA_OK;
+}
+
 samba_status validate_fwd(const samba_scan_fwd_args* a, FwdPlan* plan) {
   if (!a) return SAMBA_ERR_NULL_ARG;
   if (a->struct_size != sizeof(samba_scan_fwd_args)) return SAMBA_ERR_BAD_STRUCT;
@@ -740,42 +1156,8 @@ samba_status validate_fwd(const samba_scan_fwd_args* a, FwdPlan* plan) {
   if (overlap(a->y, n_td * eo, a->h_last, n_state)) return SAMBA_ERR_ALIASING;
 
   if (!plan) return SAMBA_OK;
-  const int ntiles = (a->dim + kCPW - 1) / kCPW;
-  int W = ts;
-  if (W == 0) {
-    // Enough (sequence, tile) waves for two per SIMD: plain sequential scan.
-    // Otherwise aim at four waves per SIMD by splitting time, but never into
-    // slices that the average sequence cannot fill.
-    const int64_t cus = device_cu_count();
-    const int64_t base = nseq * ntiles;
-    const int64_t avg_len = nseq > 0 ? tokens / nseq : 0;
-    W = 1;
-    if (base < cus * 8) {
-      while (W < 16 && base * W < cus * 16 && static_cast<int64_t>(W) * 2 * slice_tokens(W * 2) <= avg_len) W *= 2;
-    }
-  }
-  const int tpw = (W == 1) ? 4 : 1;
-  const int ngroups = (ntiles + tpw - 1) / tpw;
-  FwdParams& p = plan->prm;
-  p.x = a->x; p.dt = a->dt; p.z = a->z; p.B = a->B; p.C = a->C;
-  p.A = a->A; p.Dskip = a->D; p.bias = a->dt_bias;
-  p.h0 = a->h0; p.h_last = a->h_last; p.y = a->y;
-  p.cu = a->cu_seqlens;
-  p.total_tokens = tokens;
-  p.seqlen = a->seqlen;
-  p.dim = a->dim;
-  p.ntiles = ntiles;
-  p.tiles_per_wg = tpw;
-  p.ngroups = ngroups;
-  const int64_t nblocks = nseq * ngroups;
-  if (nblocks > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
-  p.nblocks = static_cast<int32_t>(nblocks);
-  plan->W = W;
-  plan->tpw = tpw;
-  plan->threads = 64 * W * tpw;
-  plan->grid = static_cast<int>(nblocks);
-  plan->nseq = nseq;
-  return SAMBA_OK;
+  return make_fwd_plan(a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias, a->h0, a->cu_seqlens, nseq,
+                       a->batch, a->seqlen, a->dim, ts, plan);
 }
 
 template <typename Tin, typename Tout>
@@ -787,6 +1169,149 @@ hipError_t launch_fwd(const FwdPlan& pl, hipStream_t st) {
     case 4: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 4, 1, 16>), grid, block, 0, st, pl.prm); break;
     case 8: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 8, 1, 16>), grid, block, 0, st, pl.prm); break;
     default: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 16, 1, 8>), grid, block, 0, st, pl.prm); break;
+  }
+  return hipGetLastError();
+}
+
+template <typename Tin>
+hipError_t launch_ckpt(const FwdPlan& pl, hipStream_t st) {
+  const dim3 grid(pl.grid), block(pl.threads);
+  switch (pl.W) {
+    case 1: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 1, 4, 16, true>), grid, block, 0, st, pl.prm); break;
+    case 2: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 2, 1, 16, true>), grid, block, 0, st, pl.prm); break;
+    case 4: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 4, 1, 16, true>), grid, block, 0, st, pl.prm); break;
+    case 8: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 8, 1, 16, true>), grid, block, 0, st, pl.prm); break;
+    default: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 16, 1, 8, true>), grid, block, 0, st, pl.prm); break;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// backward host side
+// ---------------------------------------------------------------------------
+struct BwdPlan {
+  int W;                    // backward waves per workgroup
+  int64_t nseq, tokens;
+  int ntiles;
+  size_t off_dbc, off_dpar, bytes;  // workspace layout: checkpoints at 0, then dB/dC partials, then parameter partials
+  FwdPlan ck;               // checkpoint pass
+  BwdParams prm;
+};
+
+size_t round256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+int bwd_slice(int) { return kBK; }
+
+samba_status bwd_layout(int64_t nseq, int64_t tokens, int32_t dim, BwdPlan* pl) {
+  const int64_t ntiles = (dim + kCPW - 1) / kCPW;
+  const int64_t slots = tokens / kBK + nseq + 1;
+  const size_t ck = round256(static_cast<size_t>(slots) * dim * kN * 4);
+  const size_t dbc = round256(static_cast<size_t>(ntiles) * tokens * 32 * 4);
+  const size_t dpar = round256(static_cast<size_t>(nseq) * dim * kParW * 4);
+  pl->nseq = nseq;
+  pl->tokens = tokens;
+  pl->ntiles = static_cast<int>(ntiles);
+  pl->off_dbc = ck;
+  pl->off_dpar = ck + dbc;
+  pl->bytes = ck + dbc + dpar;
+  return SAMBA_OK;
+}
+
+samba_status bwd_shape(const samba_scan_bwd_args* a, int64_t* nseq) {
+  if (!a) return SAMBA_ERR_NULL_ARG;
+  if (a->struct_size != sizeof(samba_scan_bwd_args)) return SAMBA_ERR_BAD_STRUCT;
+  if (a->dstate != kN) return SAMBA_ERR_UNSUPPORTED;
+  if (!dtype_ok(a->in_dtype)) return SAMBA_ERR_BAD_DTYPE;
+  if (a->batch < 0 || a->seqlen < 0 || a->dim < 1) return SAMBA_ERR_BAD_SHAPE;
+  const int ts = a->time_slices;
+  if (!(ts == 0 || ts == 1 || ts == 2 || ts == 4 || ts == 8)) return SAMBA_ERR_UNSUPPORTED;
+  *nseq = a->batch;
+  if (a->cu_seqlens) {
+    if (a->batch != 1 || a->nseq < 1) return SAMBA_ERR_BAD_SHAPE;
+    *nseq = a->nseq;
+  }
+  return SAMBA_OK;
+}
+
+samba_status validate_bwd(const samba_scan_bwd_args* a, BwdPlan* plan) {
+  int64_t nseq = 0;
+  samba_status st = bwd_shape(a, &nseq);
+  if (st != SAMBA_OK) return st;
+  if (a->cu_seqlens && !aligned(a->cu_seqlens, 4)) return SAMBA_ERR_MISALIGNED;
+  const int64_t tokens = static_cast<int64_t>(a->batch) * a->seqlen;
+  if (!a->A || !a->D || !a->dt_bias || !a->dA || !a->dD || !a->ddt_bias) return SAMBA_ERR_NULL_ARG;
+  if (tokens > 0 && (!a->x || !a->dt || !a->z || !a->B || !a->C || !a->dy || !a->dx || !a->ddt || !a->dz ||
+                     !a->dB || !a->dC))
+    return SAMBA_ERR_NULL_ARG;
+  const size_t ei = esize(a->in_dtype);
+  const void* elem[] = {a->x, a->dt, a->z, a->dy, a->dx, a->ddt, a->dz};
+  for (const void* q : elem)
+    if (!aligned(q, ei)) return SAMBA_ERR_MISALIGNED;
+  const void* a16[] = {a->B, a->C, a->A, a->h0, a->dh_last, a->dB, a->dC, a->dA, a->dh0};
+  for (const void* q : a16)
+    if (!aligned(q, 16)) return SAMBA_ERR_MISALIGNED;
+  const void* a4[] = {a->D, a->dt_bias, a->dD, a->ddt_bias};
+  for (const void* q : a4)
+    if (!aligned(q, 4)) return SAMBA_ERR_MISALIGNED;
+  BwdPlan local;
+  BwdPlan* pl = plan ? plan : &local;
+  bwd_layout(nseq, tokens, a->dim, pl);
+  if (!a->workspace || a->workspace_bytes < pl->bytes) return SAMBA_ERR_WORKSPACE;
+  if (!aligned(a->workspace, 256)) return SAMBA_ERR_WORKSPACE;
+  // no output may overlap an input or another output
+  const size_t n_td = static_cast<size_t>(tokens) * a->dim, n_tn = static_cast<size_t>(tokens) * kN;
+  const size_t n_dn = static_cast<size_t>(a->dim) * kN * 4, n_d = static_cast<size_t>(a->dim) * 4;
+  const size_t n_state = static_cast<size_t>(nseq) * a->dim * kN * 4;
+  const void* ins[] = {a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias, a->h0, a->dy, a->dh_last, a->cu_seqlens};
+  const size_t insz[] = {n_td * ei, n_td * ei, n_td * ei, n_tn * ei, n_tn * ei, n_dn, n_d, n_d, n_state, n_td * ei,
+                         n_state, a->cu_seqlens ? static_cast<size_t>(nseq + 1) * 4 : 0};
+  const void* outs[] = {a->dx, a->ddt, a->dz, a->dB, a->dC, a->dA, a->dD, a->ddt_bias, a->dh0, a->workspace};
+  const size_t outsz[] = {n_td * ei, n_td * ei, n_td * ei, n_tn * 4, n_tn * 4, n_dn, n_d, n_d, n_state, pl->bytes};
+  for (int i = 0; i < 10; ++i) {
+    for (int j = 0; j < 12; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return SAMBA_ERR_ALIASING;
+    for (int j = i + 1; j < 10; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return SAMBA_ERR_ALIASING;
+  }
+  if (!plan) return SAMBA_OK;
+
+  // checkpoint pass: the forward kernel's checkpoint variant, its own launch plan
+  st = make_fwd_plan(a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias, a->h0, a->cu_seqlens, nseq, a->batch,
+                     a->seqlen, a->dim, 0, &pl->ck);
+  if (st != SAMBA_OK) return st;
+  char* ws = static_cast<char*>(a->workspace);
+  pl->ck.prm.ckpt = reinterpret_cast<float*>(ws);
+  const int ts = a->time_slices;
+  pl->W = ts ? ts : choose_time_slices(nseq, pl->ntiles, tokens, 8, bwd_slice);
+  const int64_t nblocks = nseq * pl->ntiles;
+  if (nblocks > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  BwdParams& p = pl->prm;
+  p = BwdParams{};
+  p.x = a->x; p.dt = a->dt; p.z = a->z; p.B = a->B; p.C = a->C; p.dy = a->dy;
+  p.A = a->A; p.Dskip = a->D; p.bias = a->dt_bias;
+  p.dh_last = a->dh_last;
+  p.ckpt = reinterpret_cast<const float*>(ws);
+  p.dx = a->dx; p.ddt = a->ddt; p.dz = a->dz;
+  p.dbc = reinterpret_cast<float*>(ws + pl->off_dbc);
+  p.dpar = reinterpret_cast<float*>(ws + pl->off_dpar);
+  p.dh0 = a->dh0;
+  p.cu = a->cu_seqlens;
+  p.total_tokens = tokens;
+  p.seqlen = a->seqlen;
+  p.dim = a->dim;
+  p.ntiles = pl->ntiles;
+  p.nblocks = static_cast<int32_t>(nblocks);
+  return SAMBA_OK;
+}
+
+template <typename T>
+hipError_t launch_bwd_kernel(const BwdPlan& pl, hipStream_t st) {
+  const dim3 grid(pl.prm.nblocks), block(64 * pl.W);
+  switch (pl.W) {
+    case 1: hipLaunchKernelGGL((scan_bwd_kernel<T, 1>), grid, block, 0, st, pl.prm); break;
+    case 2: hipLaunchKernelGGL((scan_bwd_kernel<T, 2>), grid, block, 0, st, pl.prm); break;
+    case 4: hipLaunchKernelGGL((scan_bwd_kernel<T, 4>), grid, block, 0, st, pl.prm); break;
+    default: hipLaunchKernelGGL((scan_bwd_kernel<T, 8>), grid, block, 0, st, pl.prm); break;
   }
   return hipGetLastError();
 }
@@ -826,6 +1351,8 @@ samba_status samba_scan_fwd(const samba_scan_fwd_args* args, void* stream) {
   FwdPlan pl;
   const samba_status st = validate_fwd(args, &pl);
   if (st != SAMBA_OK) return st;
+  pl.prm.h_last = args->h_last;
+  pl.prm.y = args->y;
   if (pl.grid == 0) return SAMBA_OK;  // no sequences
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -845,6 +1372,40 @@ samba_status samba_scan_fwd_plan(const samba_scan_fwd_args* args, int32_t* time_
   if (workgroups) *workgroups = pl.grid;
   if (threads_per_workgroup) *threads_per_workgroup = pl.threads;
   return SAMBA_OK;
+}
+
+samba_status samba_scan_bwd_workspace_size(const samba_scan_bwd_args* args, size_t* bytes) {
+  int64_t nseq = 0;
+  const samba_status st = bwd_shape(args, &nseq);
+  if (st != SAMBA_OK) return st;
+  if (!bytes) return SAMBA_ERR_NULL_ARG;
+  BwdPlan pl;
+  bwd_layout(nseq, static_cast<int64_t>(args->batch) * args->seqlen, args->dim, &pl);
+  *bytes = pl.bytes;
+  return SAMBA_OK;
+}
+
+samba_status samba_scan_bwd(const samba_scan_bwd_args* args, void* stream) {
+  BwdPlan pl;
+  const samba_status st = validate_bwd(args, &pl);
+  if (st != SAMBA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = args->in_dtype == SAMBA_BF16;
+  if (pl.prm.nblocks > 0) {
+    if (pl.tokens > 0) {
+      const hipError_t e = bf ? launch_ckpt<uint16_t>(pl.ck, s) : launch_ckpt<float>(pl.ck, s);
+      if (e != hipSuccess) return SAMBA_ERR_HIP;
+    }
+    const hipError_t e = bf ? launch_bwd_kernel<uint16_t>(pl, s) : launch_bwd_kernel<float>(pl, s);
+    if (e != hipSuccess) return SAMBA_ERR_HIP;
+  }
+  const int64_t nout = pl.tokens * 32 + static_cast<int64_t>(args->dim) * 18;
+  const int64_t blocks = (nout + 255) / 256;
+  if (blocks > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(scan_bwd_finish_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, pl.prm.dbc,
+                     pl.prm.dpar, args->dB, args->dC, args->dA, args->dD, args->ddt_bias, pl.tokens, pl.ntiles,
+                     static_cast<int32_t>(pl.nseq), args->dim);
+  return hipGetLastError() == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
 }
 
 samba_status samba_scan_step(const samba_scan_step_args* args, void* stream) {
@@ -894,6 +1455,7 @@ const char* samba_status_string(int status) {
     case SAMBA_ERR_UNSUPPORTED: return "unsupported configuration (dstate must be 16; time_slices 0/1/2/4/8/16)";
     case SAMBA_ERR_BAD_STRUCT: return "argument struct size mismatch (header/library version skew)";
     case SAMBA_ERR_HIP: return "HIP runtime error at launch";
+    case SAMBA_ERR_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
     default: return "unknown status";
   }
 }

@@ -11,6 +11,9 @@ Recipe (every config; sizes differ):
   * B, C ~ N(0, 1) per (token, state)
   * D[d] ~ U(0, 1)
   * h0 = 0 unless a test asks for a random carry-in
+  * backward: upstream gradients dy ~ N(0, 1) per (token, channel) (in the
+    input dtype) and, where a test asks for one, dh_last ~ N(0, 1) per
+    (sequence, channel, state)
 bf16 tensors are produced from fp32 draws by integer round-to-nearest-even, so
 the exact values the kernels read are known bit for bit on the host.
 
@@ -29,7 +32,7 @@ import numpy as np
 
 SEED_ROOT = 20240611
 TENSOR_IDS = {"x": 0, "z": 1, "dt": 2, "dt_init": 3, "A": 4, "B": 5, "C": 6, "D": 7,
-              "lengths": 8, "h0": 9}
+              "lengths": 8, "h0": 9, "dy": 10, "dh_last": 11}
 DECODE_RING_BASE = 100
 DSTATE = 16
 
@@ -87,6 +90,8 @@ WORKLOADS = {
     3: Workload(3, "scan_fwd L131072 D4096 N16 bf16 as 8x16384 chained", 1, 131072, 4096, chunks=8),
     4: Workload(4, "scan_step B64 D4096 N16 after L2048 prefill, 65536 steps", 64, 2048, 4096,
                 decode_steps=65536, decode_ring=256),
+    # training shape: context 4096, batch 4 per device (page 1, 实现细节 -> 训练配置)
+    5: Workload(5, "scan_bwd B4 L4096 D4096 N16 bf16", 4, 4096, 4096),
 }
 
 
@@ -209,6 +214,31 @@ def make_fwd_inputs_torch(cfg_id: int, rows: int, dim: int, device, dstate: int 
     for k, v in p.items():
         out[k] = torch.from_numpy(v).to(device)
     return out
+
+
+def make_bwd_extra_np(cfg_id: int, rows: int, dim: int, nseq: int, dstate: int = DSTATE,
+                      in_dtype: str = "bf16") -> dict:
+    """Upstream gradients for the backward: dy [rows][dim] (input dtype, plus dy_f32) and dh_last
+    [nseq][dim][dstate] fp32."""
+    v = _normal(cfg_id, "dy", (rows, dim))
+    out = {}
+    if in_dtype == "bf16":
+        out["dy"] = bf16_bits_from_f32(v)
+        out["dy_f32"] = f32_from_bf16_bits(out["dy"])
+    else:
+        out["dy"], out["dy_f32"] = v, v
+    out["dh_last"] = _normal(cfg_id, "dh_last", (nseq, dim, dstate))
+    return out
+
+
+def make_bwd_extra_torch(cfg_id: int, rows: int, dim: int, nseq: int, device, dstate: int = DSTATE,
+                         in_dtype: str = "bf16") -> dict:
+    """Device upstream gradients: dy [rows][dim] (input dtype), dh_last [nseq][dim][dstate] fp32."""
+    import torch
+    dt_ = torch.bfloat16 if in_dtype == "bf16" else torch.float32
+    return {"dy": _torch_normal(torch, (rows, dim), cfg_id, TENSOR_IDS["dy"], device, dt_),
+            "dh_last": _torch_normal(torch, (nseq, dim, dstate), cfg_id, TENSOR_IDS["dh_last"], device,
+                                     torch.float32)}
 
 
 def make_step_ring_torch(cfg_id: int, ring: int, batch: int, dim: int, device, dstate: int = DSTATE) -> dict:

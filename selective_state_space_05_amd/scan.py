@@ -11,14 +11,14 @@ from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "libsamba_scan.so"
 DSTATE = 16
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 SAMBA_F32, SAMBA_BF16 = 0, 1
 STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE", 3: "SAMBA_ERR_BAD_DTYPE",
                 4: "SAMBA_ERR_MISALIGNED", 5: "SAMBA_ERR_ALIASING", 6: "SAMBA_ERR_UNSUPPORTED",
-                7: "SAMBA_ERR_BAD_STRUCT", 8: "SAMBA_ERR_HIP"}
-EXPORTED = ("samba_scan_fwd", "samba_scan_step", "samba_scan_fwd_plan", "samba_status_string",
-            "samba_scan_abi_version")
+                7: "SAMBA_ERR_BAD_STRUCT", 8: "SAMBA_ERR_HIP", 9: "SAMBA_ERR_WORKSPACE"}
+EXPORTED = ("samba_scan_fwd", "samba_scan_step", "samba_scan_fwd_plan", "samba_scan_bwd",
+            "samba_scan_bwd_workspace_size", "samba_status_string", "samba_scan_abi_version")
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -37,6 +37,16 @@ class StepArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("batch", _I32), ("dim", _I32), ("dstate", _I32),
                 ("in_dtype", _I32), ("y_dtype", _I32), ("state", _P), ("x", _P), ("dt", _P), ("z", _P),
                 ("B", _P), ("C", _P), ("A", _P), ("D", _P), ("dt_bias", _P), ("y", _P)]
+
+
+class BwdArgs(ctypes.Structure):
+    """Mirror of samba_scan_bwd_args."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("batch", _I32), ("seqlen", _I32), ("dim", _I32),
+                ("dstate", _I32), ("cu_seqlens", _P), ("nseq", _I32), ("in_dtype", _I32), ("time_slices", _I32),
+                ("x", _P), ("dt", _P), ("z", _P), ("B", _P), ("C", _P), ("A", _P), ("D", _P), ("dt_bias", _P),
+                ("h0", _P), ("dy", _P), ("dh_last", _P), ("dx", _P), ("ddt", _P), ("dz", _P), ("dB", _P),
+                ("dC", _P), ("dA", _P), ("dD", _P), ("ddt_bias", _P), ("dh0", _P), ("workspace", _P),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class SambaError(RuntimeError):
@@ -65,6 +75,10 @@ def load_library(path: Path | str | None = None):
     lib.samba_scan_fwd_plan.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                         ctypes.POINTER(_I32)]
     lib.samba_scan_fwd_plan.restype = ctypes.c_int
+    lib.samba_scan_bwd.argtypes = [ctypes.POINTER(BwdArgs), _P]
+    lib.samba_scan_bwd.restype = ctypes.c_int
+    lib.samba_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.samba_scan_bwd_workspace_size.restype = ctypes.c_int
     lib.samba_status_string.argtypes = [ctypes.c_int]
     lib.samba_status_string.restype = ctypes.c_char_p
     lib.samba_scan_abi_version.restype = ctypes.c_int
@@ -206,3 +220,75 @@ def scan_step(state, x, dt, z, B, C, A, D, dt_bias, *, y=None, y_dtype=None, str
     if st != 0:
         raise SambaError(st, "samba_scan_step")
     return y
+
+
+def bwd_args(x, dt, z, B, C, A, D, dt_bias, dy, *, dx, ddt, dz, dB, dC, dA, dD, ddt_bias, h0=None, dh_last=None,
+             dh0=None, cu_seqlens=None, workspace=None, time_slices: int = 0) -> BwdArgs:
+    """Fill a samba_scan_bwd_args from tensors (shapes as in scan_bwd)."""
+    if x.dim() == 3:
+        batch, seqlen, dim = x.shape
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens needs packed [tokens][dim] inputs")
+        nseq = 0
+    elif x.dim() == 2:
+        seqlen, dim = x.shape
+        batch = 1
+        nseq = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    else:
+        raise ValueError("x must be [batch][seqlen][dim] or [tokens][dim]")
+    a = BwdArgs()
+    a.struct_size = ctypes.sizeof(BwdArgs)
+    a.batch, a.seqlen, a.dim, a.dstate = batch, seqlen, dim, A.shape[-1]
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.nseq = nseq
+    a.in_dtype = _dtype_code(x)
+    a.time_slices = int(time_slices)
+    a.x, a.dt, a.z, a.B, a.C = _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C)
+    a.A, a.D, a.dt_bias, a.h0 = _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(h0)
+    a.dy, a.dh_last = _ptr(dy), _ptr(dh_last)
+    a.dx, a.ddt, a.dz, a.dB, a.dC = _ptr(dx), _ptr(ddt), _ptr(dz), _ptr(dB), _ptr(dC)
+    a.dA, a.dD, a.ddt_bias, a.dh0 = _ptr(dA), _ptr(dD), _ptr(ddt_bias), _ptr(dh0)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return a
+
+
+def bwd_workspace_bytes(a: BwdArgs) -> int:
+    n = ctypes.c_size_t()
+    st = load_library().samba_scan_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if st != 0:
+        raise SambaError(st, "samba_scan_bwd_workspace_size")
+    return n.value
+
+
+def scan_bwd(x, dt, z, B, C, A, D, dt_bias, dy, *, h0=None, dh_last=None, cu_seqlens=None, workspace=None,
+             want_dh0: bool = True, time_slices: int = 0, stream=None):
+    """Gradients of scan_fwd through samba_scan_bwd.
+
+    Inputs as for scan_fwd, plus dy (shaped like y, same dtype as x) and dh_last ([nseq][dim][16] fp32 or None).
+    `workspace` is a device tensor (any dtype) of at least the size the library asks for, or None (allocated
+    here).  Returns a dict: dx, ddt, dz (like x), dB, dC (like B, fp32), dA [dim][16], dD, ddt_bias [dim] and
+    dh0 [nseq][dim][16] (fp32; None unless want_dh0).
+    """
+    import torch
+    _check_dev(x, dt, z, B, C, A, D, dt_bias, dy, h0, dh_last, cu_seqlens, workspace)
+    dev = x.device
+    dim = x.shape[-1]
+    nseq = x.shape[0] if cu_seqlens is None and x.dim() == 3 else (
+        cu_seqlens.numel() - 1 if cu_seqlens is not None else 1)
+    out = {k: torch.empty_like(x) for k in ("dx", "ddt", "dz")}
+    out["dB"] = torch.empty(B.shape, dtype=torch.float32, device=dev)
+    out["dC"] = torch.empty(C.shape, dtype=torch.float32, device=dev)
+    out["dA"] = torch.empty((dim, DSTATE), dtype=torch.float32, device=dev)
+    out["dD"] = torch.empty(dim, dtype=torch.float32, device=dev)
+    out["ddt_bias"] = torch.empty(dim, dtype=torch.float32, device=dev)
+    out["dh0"] = torch.empty((nseq, dim, DSTATE), dtype=torch.float32, device=dev) if want_dh0 else None
+    a = bwd_args(x, dt, z, B, C, A, D, dt_bias, dy, h0=h0, dh_last=dh_last, cu_seqlens=cu_seqlens,
+                 time_slices=time_slices, **out)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(a), 1), dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    st = load_library().samba_scan_bwd(ctypes.byref(a), _P(_stream_handle(stream)))
+    if st != 0:
+        raise SambaError(st, "samba_scan_bwd")
+    return out

@@ -42,15 +42,19 @@ def test_abi_version_and_state_size(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         assert lib.samba_status_string(code)
     assert lib.samba_status_string(12345) == b"unknown status"
+
+
+STRUCTS = (("samba_scan_fwd_args", S.FwdArgs), ("samba_scan_step_args", S.StepArgs),
+           ("samba_scan_bwd_args", S.BwdArgs))
 
 
 def test_struct_layout_matches_header(tmp_path):
     """Compile a C probe against the header and compare sizeof/offsetof with the ctypes mirrors."""
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "samba_scan.h"', 'int main(void) {']
-    for cname, py in (("samba_scan_fwd_args", S.FwdArgs), ("samba_scan_step_args", S.StepArgs)):
+    for cname, py in STRUCTS:
         lines.append('printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
         for f, _ in py._fields_:
             lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
@@ -60,7 +64,7 @@ def test_struct_layout_matches_header(tmp_path):
     exe = tmp_path / "probe"
     subprocess.check_call(["gcc", "-std=c99", "-I", str(ROOT / "include"), "-o", str(exe), str(src)])
     got = dict(l.split() for l in subprocess.check_output([str(exe)]).decode().splitlines())
-    for cname, py in (("samba_scan_fwd_args", S.FwdArgs), ("samba_scan_step_args", S.StepArgs)):
+    for cname, py in STRUCTS:
         assert int(got[cname]) == ctypes.sizeof(py)
         for f, _ in py._fields_:
             assert int(got["%s.%s" % (cname, f)]) == getattr(py, f).offset, (cname, f)
@@ -209,3 +213,80 @@ def test_plan_forced_slices(lib):
         st, w, g, t = plan(lib, a)
         assert st == 0 and w == ts
         assert g == (7 if ts > 1 else 2) and t == (64 * ts if ts > 1 else 256)
+
+
+# --------------------------------------------------------------------------- #
+# backward: workspace size and validation
+# --------------------------------------------------------------------------- #
+def bwd_ok(batch=2, seqlen=100, dim=64, in_dtype=S.SAMBA_BF16):
+    a = S.BwdArgs()
+    a.struct_size = ctypes.sizeof(S.BwdArgs)
+    a.batch, a.seqlen, a.dim, a.dstate = batch, seqlen, dim, 16
+    a.in_dtype = in_dtype
+    gb = 1 << 30
+    names = ("x", "dt", "z", "B", "C", "A", "D", "dt_bias", "h0", "dy", "dh_last", "dx", "ddt", "dz", "dB", "dC",
+             "dA", "dD", "ddt_bias", "dh0", "workspace")
+    for i, n in enumerate(names):
+        setattr(a, n, BASE + i * gb)
+    a.workspace_bytes = 1 << 29
+    return a
+
+
+def ws_bytes(lib, a):
+    n = ctypes.c_size_t()
+    st = lib.samba_scan_bwd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+def r256(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("batch,seqlen,dim", [(2, 100, 64), (4, 4096, 4096), (1, 0, 16), (3, 7, 40)])
+def test_bwd_workspace_size(lib, batch, seqlen, dim):
+    """checkpoints (state before every 8th token of each sequence) + per-tile dB/dC partial rows +
+    per-sequence parameter partial rows, each rounded up to 256 bytes."""
+    a = bwd_ok(batch, seqlen, dim)
+    st, n = ws_bytes(lib, a)
+    tokens, tiles = batch * seqlen, (dim + 15) // 16
+    want = r256((tokens // 8 + batch + 1) * dim * 64) + r256(tiles * tokens * 128) + r256(batch * dim * 80)
+    assert st == 0 and n == want
+
+
+BWD_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 8), 7),
+    "dstate": (lambda a: setattr(a, "dstate", 4), 6),
+    "in_dtype": (lambda a: setattr(a, "in_dtype", 2), 3),
+    "neg_seqlen": (lambda a: setattr(a, "seqlen", -1), 2),
+    "time_slices_16": (lambda a: setattr(a, "time_slices", 16), 6),
+    "time_slices_3": (lambda a: setattr(a, "time_slices", 3), 6),
+    "null_dy": (lambda a: setattr(a, "dy", None), 1),
+    "null_dB": (lambda a: setattr(a, "dB", None), 1),
+    "null_dA": (lambda a: setattr(a, "dA", None), 1),
+    "null_workspace": (lambda a: setattr(a, "workspace", None), 9),
+    "small_workspace": (lambda a: setattr(a, "workspace_bytes", 1024), 9),
+    "misaligned_workspace": (lambda a: setattr(a, "workspace", a.workspace + 64), 9),
+    "misaligned_dB": (lambda a: setattr(a, "dB", a.dB + 4), 4),
+    "misaligned_dh_last": (lambda a: setattr(a, "dh_last", a.dh_last + 8), 4),
+    "misaligned_dx": (lambda a: setattr(a, "dx", a.dx + 1), 4),
+    "dx_overlaps_x": (lambda a: setattr(a, "dx", a.x + 2), 5),
+    "dB_overlaps_dC": (lambda a: setattr(a, "dB", a.dC + 16), 5),
+    "workspace_overlaps_dy": (lambda a: setattr(a, "workspace", a.dy), 5),
+    "dh0_overlaps_h0": (lambda a: setattr(a, "dh0", a.h0), 5),
+    "varlen_batch": (lambda a: (setattr(a, "cu_seqlens", BASE + 40 * (1 << 30)), setattr(a, "nseq", 3)), 2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_CASES))
+def test_bwd_rejects(lib, name):
+    a = bwd_ok()
+    mutate, code = BWD_CASES[name]
+    mutate(a)
+    assert lib.samba_scan_bwd(ctypes.byref(a), None) == code
+
+
+def test_bwd_null_args(lib):
+    assert lib.samba_scan_bwd(None, None) == 1
+    n = ctypes.c_size_t()
+    assert lib.samba_scan_bwd_workspace_size(None, ctypes.byref(n)) == 1
+    assert lib.samba_scan_bwd_workspace_size(ctypes.byref(bwd_ok()), None) == 1
