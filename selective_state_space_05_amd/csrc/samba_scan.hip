@@ -100,12 +100,27 @@ __device__ __forceinline__ float qperm(float v) {
 constexpr int kQXor1 = 0xB1;  // [1,0,3,2]
 constexpr int kQXor2 = 0x4E;  // [2,3,0,1]
 // Lane g holds partial sums p[0..3] for the four tokens of a group; returns, on
-// lane g, the quad's total for token g.  The exchange goes through LDS (no DPP,
-// no selects): lane g stores its partial of token q at red[c][q][g], then reads
-// the four partials of token g.
-__device__ __forceinline__ float quad_transpose_sum_lds(float4 (*red)[4], int c, int g, float p0, float p1, float p2,
+// lane g, the quad's total for token g.  Register-only version: two exchange
+// rounds of a transposed butterfly (6 selects, 3 DPP adds), no LDS traffic.
+__device__ __forceinline__ float quad_transpose_sum(float p0, float p1, float p2, float p3, int g) {
+  const bool hi = (g & 2) != 0;
+  const float k0 = hi ? p2 : p0, s0 = hi ? p0 : p2;
+  const float k1 = hi ? p3 : p1, s1 = hi ? p1 : p3;
+  const float r0 = k0 + qperm<kQXor2>(s0);
+  const float r1 = k1 + qperm<kQXor2>(s1);
+  const bool odd = (g & 1) != 0;
+  const float k = odd ? r1 : r0, s = odd ? r0 : r1;
+  return k + qperm<kQXor1>(s);
+}
+
+// Same result through LDS (no DPP, no selects): lane g stores its partial of
+// token q at red[c][q][g], then reads the four partials of token g.  A
+// channel's row is 20 floats (16 used), so the four single-float writes of a
+// wave hit 32 distinct banks.
+constexpr int kRedRow = 20;
+__device__ __forceinline__ float quad_transpose_sum_lds(float* red, int c, int g, float p0, float p1, float p2,
                                                         float p3) {
-  float* row = reinterpret_cast<float*>(red[c]);
+  float* row = red + c * kRedRow;
   row[0 * 4 + g] = p0;
   row[1 * 4 + g] = p1;
   row[2 * 4 + g] = p2;
@@ -113,7 +128,7 @@ __device__ __forceinline__ float quad_transpose_sum_lds(float4 (*red)[4], int c,
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const float4 v = red[c][g];
+  const float4 v = reinterpret_cast<const float4*>(row)[g];
   return (v.x + v.y) + (v.z + v.w);
 }
 
@@ -356,7 +371,7 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
   constexpr int kWaves = W * TPW;
   __shared__ float4 s_bc[kWaves][2][K * kN / 4];                   // per-wave staged B, C (fp32)
   __shared__ float4 s_du[kWaves][K / 4][kCPW][2];                  // per-wave (Δ, Δx) of each group's 4 tokens
-  __shared__ float4 s_red[kWaves][kCPW][4];                        // per-wave readout partials of one group
+  __shared__ float s_red[kWaves][kCPW * kRedRow];                  // per-wave readout partials of one group
   __shared__ float4 s_agg[(W > 1) ? 2 : 1][W][2][64];              // slice (P, H) pairs, double buffered
   __shared__ float4 s_carry[(W > 1) ? 2 : 1][64];                  // chunk carry, double buffered
 
@@ -634,6 +649,10 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
 // ---------------------------------------------------------------------------
 constexpr int kBK = 8;      // tokens per backward slice = checkpoint interval
 constexpr int kParW = 20;   // per-sequence partial row: dA[16], dD, ddt_bias, 2 pad (16-byte rows)
+// dB/dC channel-sum scratch: dB of channel c at [16c, 16c+16), dC at kDbcOff + 16c.  Each lane's float4
+// writes are contiguous across the wave, and the 16-float shift of the dC block puts a half-wave's reads
+// of dB (lanes 0..15) and dC (lanes 16..31) on different banks.
+constexpr int kDbcOff = kCPW * kN + 16;
 
 struct BwdParams {
   const void *x, *dt, *z, *B, *C, *dy;
@@ -652,14 +671,13 @@ struct BwdParams {
 template <typename T, int W>
 __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
   constexpr int K = kBK;
+  // LDS, per wave (9 KiB) plus 2 KiB per workgroup: four 4-wave workgroups fit a CU.
   __shared__ float4 s_bc[W][2][K * kN / 4];   // B, C rows of the slice (fp32)
-  __shared__ float4 s_sc[W][K][kCPW];         // per token and channel: (Δ, Δx, dr, 0)
-  __shared__ float4 s_red[W][kCPW][4];        // quad transposed sums
-  __shared__ float s_dbc[W][2][kCPW][32];     // two tokens' dB/dC partials of each channel
-  __shared__ float4 s_agg[2][W][2][64];       // slice (P, Ĝ), double buffered
+  __shared__ float4 s_sc[W][K][kCPW];         // per token and channel: (Δ, Δx, dr, 0), masked
+  __shared__ float4 s_tok[W][K / 4][64];      // this lane's tokens: (x, dy, sigmoid(v), silu'(z))
+  __shared__ float s_red[W][kDbcOff + kCPW * kN];   // one token's dB [channel][16], then dC [channel][16]
+  __shared__ float4 s_agg[W][2][64];          // slice (P, Ĝ); after the last chunk: per-wave parameter sums
   __shared__ float4 s_carry[2][64];           // adjoint entering a chunk from the right, double buffered
-  __shared__ float4 s_fin[W][64];             // end of sequence: per-wave dA
-  __shared__ float2 s_fin2[W][kCPW];          // end of sequence: per-wave (dD, ddt_bias)
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int logical = xcd_remap(blockIdx.x, p.nblocks);
@@ -681,12 +699,10 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
     end = start + p.seqlen;
   }
   const int ntok = static_cast<int>(end - start);
-  float A2[kSPL], Ar[kSPL];
+  float A2[kSPL];   // A * log2(e); the dΔ sum is taken against A2 and rescaled by ln 2 per token
   {
     const float4 a4 = reinterpret_cast<const float4*>(p.A + static_cast<int64_t>(dc) * kN)[g];
-    Ar[0] = a4.x; Ar[1] = a4.y; Ar[2] = a4.z; Ar[3] = a4.w;
-#pragma unroll
-    for (int i = 0; i < kSPL; ++i) A2[i] = Ar[i] * kLog2e;
+    A2[0] = a4.x * kLog2e; A2[1] = a4.y * kLog2e; A2[2] = a4.z * kLog2e; A2[3] = a4.w * kLog2e;
   }
   const float dsk = p.Dskip[dc], bias = p.bias[dc];
   const uint32_t dim = static_cast<uint32_t>(p.dim);
@@ -696,10 +712,12 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
     in_off[j] = ((static_cast<uint32_t>(4 * j + g)) * dim + static_cast<uint32_t>(d)) * static_cast<uint32_t>(sizeof(T));
   const int bc_lds = (lane >> 3) * kN + (lane & 7) * 2;   // 2 of the 8 x 16 B (and C) values per lane
   const uint32_t bc_off = static_cast<uint32_t>(bc_lds) * static_cast<uint32_t>(sizeof(T));
+  const uint32_t ck_off = (static_cast<uint32_t>(dc) * kN + 4u * static_cast<uint32_t>(g)) * 4u;
   float* sB = reinterpret_cast<float*>(s_bc[wave][0]);
   float* sC = reinterpret_cast<float*>(s_bc[wave][1]);
   const float4* sB4 = s_bc[wave][0];
   const float4* sC4 = s_bc[wave][1];
+  float* red = s_red[wave];
 
   // adjoint entering the sequence's last token from the right: dh_last
   float gh[kSPL] = {0.f, 0.f, 0.f, 0.f};
@@ -743,11 +761,13 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
       bload_words(rb, bc_off, bw);
       bload_words(rc, bc_off, cw);
     }
-    float hs[kSPL] = {0.f, 0.f, 0.f, 0.f};
-    if (nv > 0) {
-      const float4 v = reinterpret_cast<const float4*>(
-          p.ckpt + (ckpt_slot(start, s, i0 >> 3) * p.dim + dc) * kN)[g];
-      hs[0] = v.x; hs[1] = v.y; hs[2] = v.z; hs[3] = v.w;
+    float hs[kSPL];
+    {
+      // checkpoint row of this slice (an empty resource past the sequence end: reads give 0)
+      const rsrc_t rk = make_rsrc_rows(p.ckpt + ckpt_slot(start, s, i0 >> 3) * p.dim * kN, nv > 0 ? 1 : 0, dim * kN);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ck_off, 0, 0);
+      hs[0] = __uint_as_float(v[0]); hs[1] = __uint_as_float(v[1]);
+      hs[2] = __uint_as_float(v[2]); hs[3] = __uint_as_float(v[3]);
     }
     {
       float v[K / 4];
@@ -756,8 +776,7 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
       widen_words<T, K>(cw, v);
       lds_put<K / 4>(sC + bc_lds, v);
     }
-    // ---- per-token scalars of this lane's tokens (4j + g)
-    float xk[K / 4], dyk[K / 4], dlk[K / 4], drk[K / 4], sigv[K / 4], dsl[K / 4];
+    // ---- per-token scalars of this lane's tokens (4j + g), parked in LDS until the outputs
 #pragma unroll
     for (int j = 0; j < K / 4; ++j) {
       const bool ok = dvalid && (4 * j + g) < nv;
@@ -765,47 +784,64 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
       const float v = widen(dtr[j]) + bias;
       const float delta = softplus_f32(v);
       const float sz = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zv * kLog2e));
-      sigv[j] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
-      dsl[j] = sz * fmaf(zv, 1.0f - sz, 1.0f);
-      xk[j] = xv;
-      dyk[j] = dyv;
-      dlk[j] = ok ? delta : 0.0f;
-      drk[j] = ok ? dyv * zv * sz : 0.0f;
-      s_sc[wave][4 * j + g][c] = make_float4(dlk[j], ok ? delta * xv : 0.0f, drk[j], 0.0f);
+      const float sigv = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-v * kLog2e));
+      s_tok[wave][j][lane] = make_float4(xv, dyv, sigv, sz * fmaf(zv, 1.0f - sz, 1.0f));
+      s_sc[wave][4 * j + g][c] = make_float4(ok ? delta : 0.0f, ok ? delta * xv : 0.0f, ok ? dyv * zv * sz : 0.0f, 0.0f);
     }
     wave_lds_sync();
 
-    // ---- forward recompute of the slice; adjoint transfer pair (P, Ĝ)
-    float ak[K][kSPL], hk[K][kSPL];
+    // ---- forward recompute of the slice; adjoint transfer pair (P, Ĝ).  Ā_t and h_t of the
+    // second half of the slice stay in registers; the first half is recomputed (same operations,
+    // same order, so bit for bit the same values) after the second half's reverse sweep: half the
+    // replay registers, so four waves fit a SIMD.
+    constexpr int H = K / 2;
+    float ak[H][kSPL], hk[H][kSPL];   // tokens H..K-1 during the first reverse half, 0..H-1 after
+    float hmid[kSPL];                 // state after token H-1
     float P[kSPL], G[kSPL];
     float rr[K / 4];
+    auto fwd_token = [&](int k, const float (&prev)[kSPL], float (&a)[kSPL], float (&h)[kSPL], float4& cv_out) {
+      const float4 sc = s_sc[wave][k][c];
+      const float4 bv = sB4[k * 4 + g];
+      cv_out = sC4[k * 4 + g];
+      const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-    for (int jj = 0; jj < K / 4; ++jj) {
-      float pr[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = 4 * jj + q;
-        const float4 sc = s_sc[wave][k][c];
-        const float4 bv = sB4[k * 4 + g], cv = sC4[k * 4 + g];
-        const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
-        const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < kSPL; ++i) {
-          ak[k][i] = __builtin_amdgcn_exp2f(sc.x * A2[i]);
-          const float prev = (k == 0) ? hs[i] : hk[k - 1][i];
-          hk[k][i] = fmaf(ak[k][i], prev, sc.y * bb[i]);
-          P[i] = (k == 0) ? ak[k][i] : P[i] * ak[k][i];
-          const float drc = sc.z * cc[i];
-          G[i] = (k == 0) ? P[i] * drc : fmaf(P[i], drc, G[i]);
-          acc = fmaf(cc[i], hk[k][i], acc);
-        }
-        pr[q] = acc;
+      for (int i = 0; i < kSPL; ++i) {
+        a[i] = __builtin_amdgcn_exp2f(sc.x * A2[i]);
+        h[i] = fmaf(a[i], prev[i], sc.y * bb[i]);
       }
-      rr[jj] = quad_transpose_sum_lds(s_red[wave], c, g, pr[0], pr[1], pr[2], pr[3]);
+      return sc;
+    };
+    {
+      float hcur[kSPL] = {hs[0], hs[1], hs[2], hs[3]};
+#pragma unroll
+      for (int jj = 0; jj < K / 4; ++jj) {
+        float pr[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = 4 * jj + q;
+          float a[kSPL], h[kSPL];
+          float4 cv;
+          const float4 sc = fwd_token(k, hcur, a, h, cv);
+          const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
+          float acc = 0.f;
+#pragma unroll
+          for (int i = 0; i < kSPL; ++i) {
+            P[i] = (k == 0) ? a[i] : P[i] * a[i];
+            const float drc = sc.z * cc[i];
+            G[i] = (k == 0) ? P[i] * drc : fmaf(P[i], drc, G[i]);
+            acc = fmaf(cc[i], h[i], acc);
+            hcur[i] = h[i];
+            if (k >= H) { ak[k - H][i] = a[i]; hk[k - H][i] = h[i]; }
+            if (k == H - 1) hmid[i] = h[i];
+          }
+          pr[q] = acc;
+        }
+        rr[jj] = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], g);
+      }
     }
-    s_agg[buf][wave][0][lane] = make_float4(P[0], P[1], P[2], P[3]);
-    s_agg[buf][wave][1][lane] = make_float4(G[0], G[1], G[2], G[3]);
+    __syncthreads();  // every wave has finished reading the previous chunk's pairs
+    s_agg[wave][0][lane] = make_float4(P[0], P[1], P[2], P[3]);
+    s_agg[wave][1][lane] = make_float4(G[0], G[1], G[2], G[3]);
     __syncthreads();
 
     // ---- adjoint entering this slice's end: fold the later slices into the chunk's incoming adjoint
@@ -814,8 +850,8 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
       gh[0] = v.x; gh[1] = v.y; gh[2] = v.z; gh[3] = v.w;
     }
     for (int w2 = W - 1; w2 > wave; --w2) {
-      const float4 P2 = s_agg[buf][w2][0][lane];
-      const float4 G2 = s_agg[buf][w2][1][lane];
+      const float4 P2 = s_agg[w2][0][lane];
+      const float4 G2 = s_agg[w2][1][lane];
       gh[0] = fmaf(P2.x, gh[0], G2.x);
       gh[1] = fmaf(P2.y, gh[1], G2.y);
       gh[2] = fmaf(P2.z, gh[2], G2.z);
@@ -825,50 +861,79 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
     // ---- reverse sweep: every gradient term
     const int prow = rem < 0 ? 0 : rem;
     const rsrc_t rbc = make_rsrc_rows(p.dbc + (static_cast<int64_t>(tile) * p.total_tokens + t0) * 32, prow, 32u);
+    const int half = lane >> 5, o = lane & 31;
+    const int obase = (o >> 4) * kDbcOff + (o & 15);   // output o = kind * 16 + n
     float sau_t[K / 4], sgb_t[K / 4];
+    // one token k of the reverse sweep, with Ā_k, h_{k-1} and h_k; returns its (Σ g A2 Ā h_{k-1}, Σ g B) partials
+    auto rev_token = [&](int k, const float (&a)[kSPL], const float (&hprev)[kSPL], const float (&hc)[kSPL],
+                         float& sa, float& sb) {
+      const float4 sc = s_sc[wave][k][c];
+      const float4 bv = sB4[k * 4 + g], cv = sC4[k * 4 + g];
+      const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+      const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
+      float db[4], dcv[4];
+      sa = 0.f;
+      sb = 0.f;
 #pragma unroll
-    for (int jj = K / 4 - 1; jj >= 0; --jj) {
+      for (int i = 0; i < kSPL; ++i) {
+        const float gi = fmaf(sc.z, cc[i], gh[i]);
+        const float gu = gi * (a[i] * hprev[i]);
+        dAacc[i] = fmaf(gu, sc.x, dAacc[i]);
+        sa = fmaf(gu, A2[i], sa);
+        sb = fmaf(gi, bb[i], sb);
+        db[i] = gi * sc.y;
+        dcv[i] = sc.z * hc[i];
+        gh[i] = a[i] * gi;
+      }
+      // this token's dB / dC summed over the wave's 16 channels: lanes 0..31 take channels 0..7 and
+      // lanes 32..63 channels 8..15 of output (lane & 31); one lane swap adds the halves
+      *reinterpret_cast<float4*>(red + c * kN + 4 * g) = make_float4(db[0], db[1], db[2], db[3]);
+      *reinterpret_cast<float4*>(red + kDbcOff + c * kN + 4 * g) = make_float4(dcv[0], dcv[1], dcv[2], dcv[3]);
+      wave_lds_sync();
+      float acc = 0.f;
+#pragma unroll
+      for (int c2 = 0; c2 < kCPW / 2; ++c2) acc += red[obase + (8 * half + c2) * kN];
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
+      acc += __uint_as_float(sw[1]);   // lanes 0..31: + the value of lane + 32
+      if (half == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rbc, static_cast<uint32_t>((k * 32 + o) * 4),
+                                              0, 0);
+    };
+    static_assert(H == 4, "one quad group per half");
+    // second half (tokens K-1 .. H) from the registers
+    {
       float sau[4], sgb[4];
 #pragma unroll
       for (int q = 3; q >= 0; --q) {
-        const int k = 4 * jj + q;
-        const float4 sc = s_sc[wave][k][c];
-        const float4 bv = sB4[k * 4 + g], cv = sC4[k * 4 + g];
-        const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
-        const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
-        float sa = 0.f, sb = 0.f, db[4], dcv[4];
+        const int k = H + q;
+        float hp[kSPL];
 #pragma unroll
-        for (int i = 0; i < kSPL; ++i) {
-          const float gi = fmaf(sc.z, cc[i], gh[i]);
-          const float prev = (k == 0) ? hs[i] : hk[k - 1][i];
-          const float gu = gi * (ak[k][i] * prev);
-          dAacc[i] = fmaf(gu, sc.x, dAacc[i]);
-          sa = fmaf(gu, Ar[i], sa);
-          sb = fmaf(gi, bb[i], sb);
-          db[i] = gi * sc.y;
-          dcv[i] = sc.z * hk[k][i];
-          gh[i] = ak[k][i] * gi;
-        }
-        sau[q] = sa;
-        sgb[q] = sb;
-        // this token's dB / dC partials of the wave's 16 channels
-        float* row = s_dbc[wave][k & 1][c];
-        *reinterpret_cast<float4*>(row + 4 * g) = make_float4(db[0], db[1], db[2], db[3]);
-        *reinterpret_cast<float4*>(row + 16 + 4 * g) = make_float4(dcv[0], dcv[1], dcv[2], dcv[3]);
-        if ((k & 1) == 0) {
-          // tokens k (lanes 0..31) and k+1 (lanes 32..63): sum output (lane & 31) over the 16 channels
-          wave_lds_sync();
-          const int tt = lane >> 5, o = lane & 31;
-          float acc = 0.f;
-#pragma unroll
-          for (int c2 = 0; c2 < kCPW; ++c2) acc += s_dbc[wave][tt][c2][o];
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rbc,
-                                                static_cast<uint32_t>(((k + tt) * 32 + o) * 4), 0, 0);
-          wave_lds_sync();
-        }
+        for (int i = 0; i < kSPL; ++i) hp[i] = (q == 0) ? hmid[i] : hk[q - 1][i];
+        rev_token(k, ak[q], hp, hk[q], sau[q], sgb[q]);
       }
-      sau_t[jj] = quad_transpose_sum_lds(s_red[wave], c, g, sau[0], sau[1], sau[2], sau[3]);
-      sgb_t[jj] = quad_transpose_sum_lds(s_red[wave], c, g, sgb[0], sgb[1], sgb[2], sgb[3]);
+      sau_t[1] = quad_transpose_sum(sau[0], sau[1], sau[2], sau[3], g);
+      sgb_t[1] = quad_transpose_sum(sgb[0], sgb[1], sgb[2], sgb[3], g);
+    }
+    // first half (tokens H-1 .. 0): recompute from the checkpoint, then reverse
+    {
+      float hcur[kSPL] = {hs[0], hs[1], hs[2], hs[3]};
+#pragma unroll
+      for (int k = 0; k < H; ++k) {
+        float4 cv;
+        fwd_token(k, hcur, ak[k], hk[k], cv);
+#pragma unroll
+        for (int i = 0; i < kSPL; ++i) hcur[i] = hk[k][i];
+      }
+      float sau[4], sgb[4];
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        float hp[kSPL];
+#pragma unroll
+        for (int i = 0; i < kSPL; ++i) hp[i] = (q == 0) ? hs[i] : hk[q - 1][i];
+        rev_token(q, ak[q], hp, hk[q], sau[q], sgb[q]);
+      }
+      sau_t[0] = quad_transpose_sum(sau[0], sau[1], sau[2], sau[3], g);
+      sgb_t[0] = quad_transpose_sum(sgb[0], sgb[1], sgb[2], sgb[3], g);
     }
 
     // ---- per-token outputs of this lane's tokens
@@ -879,12 +944,14 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < K / 4; ++j) {
         const bool ok = dvalid && (4 * j + g) < nv;
-        const float r = fmaf(dsk, xk[j], rr[j]);
-        const float dzv = dyk[j] * r * dsl[j];
-        const float dxv = fmaf(drk[j], dsk, dlk[j] * sgb_t[j]);
-        const float ddtv = fmaf(sgb_t[j], xk[j], sau_t[j]) * sigv[j];
+        const float4 tk = s_tok[wave][j][lane];           // x, dy, sigmoid(v), silu'(z)
+        const float4 sc = s_sc[wave][4 * j + g][c];       // Δ, Δx, dr (masked)
+        const float r = fmaf(dsk, tk.x, rr[j]);
+        const float dzv = tk.y * r * tk.w;
+        const float dxv = fmaf(sc.z, dsk, sc.x * sgb_t[j]);
+        const float ddtv = fmaf(sgb_t[j], tk.x, sau_t[j] * kLn2) * tk.z;
         if (ok) {
-          dDacc = fmaf(drk[j], xk[j], dDacc);
+          dDacc = fmaf(sc.z, tk.x, dDacc);
           dbacc += ddtv;
           bstore(ox, in_off[j], dxv, static_cast<T*>(nullptr));
           bstore(od, in_off[j], ddtv, static_cast<T*>(nullptr));
@@ -902,16 +969,17 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
         make_float4(gh[0], gh[1], gh[2], gh[3]);
   dDacc = quad_allsum(dDacc);
   dbacc = quad_allsum(dbacc);
-  s_fin[wave][lane] = make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
-  if (g == 0) s_fin2[wave][c] = make_float2(dDacc, dbacc);
+  __syncthreads();  // the last chunk's folds are done with s_agg
+  s_agg[wave][0][lane] = make_float4(dAacc[0], dAacc[1], dAacc[2], dAacc[3]);
+  s_agg[wave][1][lane] = make_float4(dDacc, dbacc, 0.f, 0.f);
   __syncthreads();
   if (wave == 0 && dvalid) {
-    float4 a = s_fin[0][lane];
-    float2 b = s_fin2[0][c];
+    float4 a = s_agg[0][0][lane];
+    float4 b = s_agg[0][1][lane];
 #pragma unroll
     for (int w2 = 1; w2 < W; ++w2) {
-      const float4 a2 = s_fin[w2][lane];
-      const float2 b2 = s_fin2[w2][c];
+      const float4 a2 = s_agg[w2][0][lane];
+      const float4 b2 = s_agg[w2][1][lane];
       a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
       b.x += b2.x; b.y += b2.y;
     }
@@ -1062,9 +1130,11 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 size_t esize(int32_t dt) { return dt == SAMBA_BF16 ? 2 : 4; }
 bool dtype_ok(int32_t dt) { return dt == SAMBA_F32 || dt == SAMBA_BF16; }
 
-// Tokens per wave slice: 16 keeps the replay registers of two waves per SIMD;
-// 16-wave workgroups (four per SIMD) use 8 to stay within 128 VGPRs.
-int slice_tokens(int W) { return W >= 16 ? 8 : 16; }
+// Tokens per wave slice.  Time-sliced variants keep 2*K*4 replay values per
+// lane in registers: K = 8 stays within 128 VGPRs (four waves per SIMD); 16
+// would halve the occupancy.  The sequential variant keeps no replay
+// registers and takes 16.
+int slice_tokens(int W) { return W >= 2 ? 8 : 16; }
 
 struct FwdPlan {
   int W, tpw, threads, grid;
@@ -1165,9 +1235,9 @@ hipError_t launch_fwd(const FwdPlan& pl, hipStream_t st) {
   const dim3 grid(pl.grid), block(pl.threads);
   switch (pl.W) {
     case 1: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 1, 4, 16>), grid, block, 0, st, pl.prm); break;
-    case 2: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 2, 1, 16>), grid, block, 0, st, pl.prm); break;
-    case 4: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 4, 1, 16>), grid, block, 0, st, pl.prm); break;
-    case 8: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 8, 1, 16>), grid, block, 0, st, pl.prm); break;
+    case 2: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 2, 1, 8>), grid, block, 0, st, pl.prm); break;
+    case 4: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 4, 1, 8>), grid, block, 0, st, pl.prm); break;
+    case 8: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 8, 1, 8>), grid, block, 0, st, pl.prm); break;
     default: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 16, 1, 8>), grid, block, 0, st, pl.prm); break;
   }
   return hipGetLastError();
@@ -1178,9 +1248,9 @@ hipError_t launch_ckpt(const FwdPlan& pl, hipStream_t st) {
   const dim3 grid(pl.grid), block(pl.threads);
   switch (pl.W) {
     case 1: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 1, 4, 16, true>), grid, block, 0, st, pl.prm); break;
-    case 2: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 2, 1, 16, true>), grid, block, 0, st, pl.prm); break;
-    case 4: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 4, 1, 16, true>), grid, block, 0, st, pl.prm); break;
-    case 8: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 8, 1, 16, true>), grid, block, 0, st, pl.prm); break;
+    case 2: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 2, 1, 8, true>), grid, block, 0, st, pl.prm); break;
+    case 4: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 4, 1, 8, true>), grid, block, 0, st, pl.prm); break;
+    case 8: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 8, 1, 8, true>), grid, block, 0, st, pl.prm); break;
     default: hipLaunchKernelGGL((scan_fwd_kernel<Tin, float, 16, 1, 8, true>), grid, block, 0, st, pl.prm); break;
   }
   return hipGetLastError();

@@ -201,9 +201,11 @@ def test_plan_batched_runs_sequential(lib):
 
 
 def test_plan_short_sequences_limit_slices(lib):
-    a = fwd_ok(batch=1, seqlen=20, dim=64)
-    st, w, g, t = plan(lib, a)
-    assert st == 0 and w == 1
+    """Time is split only into slices (8 tokens each) that the average sequence fills at least twice over."""
+    for seqlen, want in ((12, 1), (20, 2), (40, 4)):
+        a = fwd_ok(batch=1, seqlen=seqlen, dim=64)
+        st, w, g, t = plan(lib, a)
+        assert st == 0 and w == want, (seqlen, w)
 
 
 def test_plan_forced_slices(lib):
