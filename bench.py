@@ -202,8 +202,36 @@ def bench_backward(steps: int = 10, warmup: int = 5):
     td = Bt * L * D
     nbytes = bwd_bytes(Bt * L, D, Bt)
     slots = BWD_SLOTS_PER_TD * td / (ms * 1e-3) / 1e12
+
+    # training route: the forward writes y and the checkpoints; the backward reuses them
+    y = torch.empty_like(x)
+    ck = S.alloc_ckpt(x)
+    fa = S.fwd_args(x, dt, z, B, C, inp["A"], inp["D"], inp["dt_bias"], y=y)
+    fc = S.fwd_args(x, dt, z, B, C, inp["A"], inp["D"], inp["dt_bias"], y=y, h_ckpt=ck)
+    bc = S.bwd_args(x, dt, z, B, C, inp["A"], inp["D"], inp["dt_bias"], dy, h_ckpt=ck, **out)
+    bc.workspace, bc.workspace_bytes = ws.data_ptr(), ws.numel()
+
+    def timed(args, fn):
+        for _ in range(warmup):
+            fn(ctypes.byref(args), sh)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            if fn(ctypes.byref(args), sh) != 0:
+                raise RuntimeError("call failed")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    fwd_ms = timed(fa, lib.samba_scan_fwd)
+    fwd_ck_ms = timed(fc, lib.samba_scan_fwd)
+    bwd_ck_ms = timed(bc, lib.samba_scan_bwd)
     return {"workload": "backward B=4 L=4096 D=4096 N=16 bf16 (training shape), all gradients",
             "steps": steps, "ms_per_call": ms, "tokens_channels_per_s": td / (ms * 1e-3),
+            "training_route": {"fwd_ms": fwd_ms, "fwd_with_checkpoints_ms": fwd_ck_ms,
+                               "bwd_from_checkpoints_ms": bwd_ck_ms,
+                               "fwd_plus_bwd_ms": fwd_ck_ms + bwd_ck_ms,
+                               "fwd_plus_self_contained_bwd_ms": fwd_ms + ms},
             "gbs": nbytes / (ms * 1e-3) / 1e9, "algorithmic_bytes": nbytes, "workspace_bytes": ws.numel(),
             "roofline": {"bound": "alu", "achieved": round(slots, 3), "peak": round(VALU_PEAK_TSLOT, 2),
                          "unit": "Tslot/s", "frac": round(slots / VALU_PEAK_TSLOT, 4), "traffic": None,

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SAMBA_SCAN_ABI_VERSION 2
+#define SAMBA_SCAN_ABI_VERSION 3
 #define SAMBA_DSTATE 16
 
 typedef enum {
@@ -86,6 +86,14 @@ typedef enum { SAMBA_F32 = 0, SAMBA_BF16 = 1 } samba_dtype;
  * of one channel tile (1, 2, 4, 8 or 16); other values force it (testing and
  * tuning; results agree to fp32 rounding, and are bitwise reproducible for a
  * given choice).
+ *
+ * h_ckpt (optional output, fp32, 16-byte aligned): the state before every 8th
+ * token of each sequence, for a later samba_scan_bwd of the same inputs (a
+ * training forward keeps them instead of the backward recomputing them).  The
+ * state before token 8j of sequence s (first token row start_s) is slot
+ * floor(start_s / 8) + s + j of an array [slots][dim][16], slots = tokens / 8 +
+ * nseq + 1 (samba_scan_ckpt_bytes); slots no sequence uses are not written.
+ * It must not overlap any other argument.
  */
 typedef struct {
   uint32_t struct_size;        /* = sizeof(samba_scan_fwd_args) */
@@ -100,6 +108,7 @@ typedef struct {
   const float* h0;             /* optional */
   float* h_last;               /* optional */
   void* y;
+  float* h_ckpt;               /* optional: states every 8 tokens, for the backward */
 } samba_scan_fwd_args;
 
 /*
@@ -134,8 +143,10 @@ typedef struct {
  *     dB_t[n] = sum_d g_t[n] Δ_t x_t,   dC_t[n] = sum_d dr_t h_t[n]
  *     dA[d][n] = sum g_t[n] Δ_t Ā_t[n] h_{t-1}[n],  dD[d] = sum dr_t x_t,  ddt_bias[d] = sum ddt_t
  *     dh0[n]  = Ā_first[n] g_first[n]   (dh_last for an empty sequence)
- * The forward states are recomputed inside the call (from x, dt, B and h0);
- * nothing from a previous samba_scan_fwd call is needed.
+ * The forward states are recomputed inside the call from x, dt, B and h0, or,
+ * when h_ckpt is given, from those checkpoints: the h_ckpt a samba_scan_fwd
+ * call wrote for the same x, dt, B, h0 and sequences (with time_slices 0 on
+ * both sides the two routes give bitwise the same gradients).
  *
  * Shapes and dtypes: x, dt, z, B, C, cu_seqlens, A, D, dt_bias, h0 exactly as
  * for samba_scan_fwd (in_dtype).  dy [tokens][dim] and the outputs dx, ddt, dz
@@ -147,9 +158,9 @@ typedef struct {
  * bytes.  No output may overlap an input or another output.
  *
  * Workspace: caller-owned device memory of at least
- * samba_scan_bwd_workspace_size() bytes (checkpointed states every 8 tokens,
- * per-tile partial sums of dB and dC, per-sequence partial sums of dA, dD and
- * ddt_bias).  Calls that overlap in time must use different workspaces.
+ * samba_scan_bwd_workspace_size() bytes (checkpointed states every 8 tokens
+ * unless h_ckpt is given, per-tile partial sums of dB and dC, per-sequence
+ * partial sums of dA, dD and ddt_bias).  Calls that overlap in time must use different workspaces.
  * time_slices: 0 = automatic, else 1, 2, 4 or 8 waves per time chunk of a
  * channel tile (results agree to fp32 rounding; bitwise reproducible for a
  * given choice).
@@ -167,6 +178,7 @@ typedef struct {
   const float* h0;             /* optional */
   const void* dy;
   const float* dh_last;        /* optional */
+  const float* h_ckpt;         /* optional: checkpoints from samba_scan_fwd (see there) */
   void *dx, *ddt, *dz;
   float *dB, *dC;
   float *dA, *dD, *ddt_bias;
@@ -175,7 +187,12 @@ typedef struct {
   size_t workspace_bytes;
 } samba_scan_bwd_args;
 
-/* Host-only: bytes of workspace samba_scan_bwd needs for these sizes (pointers are not examined). */
+/* Host-only: bytes of the h_ckpt array for these sizes (nseq = batch without cu_seqlens):
+ * (batch * seqlen / 8 + nseq + 1) * dim * 16 * 4. */
+samba_status samba_scan_ckpt_bytes(int32_t batch, int32_t seqlen, int32_t nseq, int32_t dim, size_t* bytes);
+
+/* Host-only: bytes of workspace samba_scan_bwd needs for these sizes and for whether h_ckpt is given
+ * (no other pointer is examined). */
 samba_status samba_scan_bwd_workspace_size(const samba_scan_bwd_args* args, size_t* bytes);
 
 /* Enqueue the backward.  See samba_scan_bwd_args. */

@@ -459,13 +459,13 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
       // (the checkpoint variant writes no y: an empty resource)
       const rsrc_t ry = make_rsrc_rows(kCkpt ? yout : yout + t0 * p.dim, kCkpt ? 0 : ntok - i0,
                                        static_cast<uint32_t>(p.dim));
-      if constexpr (kCkpt) put_ckpt(i0, h);
+      if (kCkpt || p.ckpt) put_ckpt(i0, h);
       wave_lds_sync();
 #pragma unroll
       for (int j = 0; j < K / 4; ++j) {
         if (4 * j >= nv) break;
-        if constexpr (kCkpt && K == 16) {
-          if (j == 2) put_ckpt(i0 + 8, h);
+        if constexpr (K == 16) {
+          if ((kCkpt || p.ckpt) && j == 2) put_ckpt(i0 + 8, h);
         }
         float4 bv[4], cv[4];
         float dk[4], uk[4];
@@ -577,15 +577,15 @@ __global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
       // phase 3: replay the slice from the true carry-in, read out, gate, store
       const rsrc_t ry = make_rsrc_rows(kCkpt ? yout : yout + t0 * p.dim, kCkpt ? 0 : ntok - i0,
                                        static_cast<uint32_t>(p.dim));
-      if constexpr (kCkpt) {
+      if (kCkpt || p.ckpt) {
         if (nv > 0) put_ckpt(i0, hin);
       }
 #pragma unroll
       for (int i = 0; i < kSPL; ++i) h[i] = hin[i];
 #pragma unroll
       for (int j = 0; j < K / 4; ++j) {
-        if constexpr (kCkpt && K == 16) {
-          if (j == 2 && nv > 8) put_ckpt(i0 + 8, h);
+        if constexpr (K == 16) {
+          if ((kCkpt || p.ckpt) && j == 2 && nv > 8) put_ckpt(i0 + 8, h);
         }
         float pr[4];
         float4 cq[4];
@@ -1128,6 +1128,11 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 size_t esize(int32_t dt) { return dt == SAMBA_BF16 ? 2 : 4; }
+
+// Bytes of a checkpoint array: slots = tokens / 8 + nseq + 1 (see ckpt_slot), dim x 16 fp32 each.
+size_t ckpt_bytes(int64_t tokens, int64_t nseq, int64_t dim) {
+  return static_cast<size_t>(tokens / 8 + nseq + 1) * static_cast<size_t>(dim) * kN * 4;
+}
 bool dtype_ok(int32_t dt) { return dt == SAMBA_F32 || dt == SAMBA_BF16; }
 
 // Tokens per wave slice.  Time-sliced variants keep 2*K*4 replay values per
@@ -1207,7 +1212,7 @@ samba_status validate_fwd(const samba_scan_fwd_args* a, FwdPlan* plan) {
   const size_t ei = esize(a->in_dtype), eo = esize(a->y_dtype);
   if (!aligned(a->x, ei) || !aligned(a->dt, ei) || !aligned(a->z, ei) || !aligned(a->y, eo)) return SAMBA_ERR_MISALIGNED;
   if (!aligned(a->B, 16) || !aligned(a->C, 16) || !aligned(a->A, 16) || !aligned(a->h0, 16) ||
-      !aligned(a->h_last, 16) || !aligned(a->D, 4) || !aligned(a->dt_bias, 4))
+      !aligned(a->h_last, 16) || !aligned(a->h_ckpt, 16) || !aligned(a->D, 4) || !aligned(a->dt_bias, 4))
     return SAMBA_ERR_MISALIGNED;
   // outputs must not overlap inputs (h_last == h0 exactly is allowed: in-place carry)
   const size_t n_td = static_cast<size_t>(tokens) * a->dim;
@@ -1224,6 +1229,13 @@ samba_status validate_fwd(const samba_scan_fwd_args* a, FwdPlan* plan) {
   if (a->h_last && a->h0 && a->h_last != a->h0 && overlap(a->h_last, n_state, a->h0, n_state))
     return SAMBA_ERR_ALIASING;
   if (overlap(a->y, n_td * eo, a->h_last, n_state)) return SAMBA_ERR_ALIASING;
+  if (a->h_ckpt) {
+    const size_t n_ck = ckpt_bytes(tokens, nseq, a->dim);
+    for (int i = 0; i < 10; ++i)
+      if (overlap(a->h_ckpt, n_ck, ins[i], insz[i])) return SAMBA_ERR_ALIASING;
+    if (overlap(a->h_ckpt, n_ck, a->y, n_td * eo) || overlap(a->h_ckpt, n_ck, a->h_last, n_state))
+      return SAMBA_ERR_ALIASING;
+  }
 
   if (!plan) return SAMBA_OK;
   return make_fwd_plan(a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias, a->h0, a->cu_seqlens, nseq,
@@ -1272,10 +1284,9 @@ size_t round256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 int bwd_slice(int) { return kBK; }
 
-samba_status bwd_layout(int64_t nseq, int64_t tokens, int32_t dim, BwdPlan* pl) {
+samba_status bwd_layout(int64_t nseq, int64_t tokens, int32_t dim, bool own_ckpt, BwdPlan* pl) {
   const int64_t ntiles = (dim + kCPW - 1) / kCPW;
-  const int64_t slots = tokens / kBK + nseq + 1;
-  const size_t ck = round256(static_cast<size_t>(slots) * dim * kN * 4);
+  const size_t ck = own_ckpt ? round256(ckpt_bytes(tokens, nseq, dim)) : 0;
   const size_t dbc = round256(static_cast<size_t>(ntiles) * tokens * 32 * 4);
   const size_t dpar = round256(static_cast<size_t>(nseq) * dim * kParW * 4);
   pl->nseq = nseq;
@@ -1317,7 +1328,7 @@ samba_status validate_bwd(const samba_scan_bwd_args* a, BwdPlan* plan) {
   const void* elem[] = {a->x, a->dt, a->z, a->dy, a->dx, a->ddt, a->dz};
   for (const void* q : elem)
     if (!aligned(q, ei)) return SAMBA_ERR_MISALIGNED;
-  const void* a16[] = {a->B, a->C, a->A, a->h0, a->dh_last, a->dB, a->dC, a->dA, a->dh0};
+  const void* a16[] = {a->B, a->C, a->A, a->h0, a->dh_last, a->h_ckpt, a->dB, a->dC, a->dA, a->dh0};
   for (const void* q : a16)
     if (!aligned(q, 16)) return SAMBA_ERR_MISALIGNED;
   const void* a4[] = {a->D, a->dt_bias, a->dD, a->ddt_bias};
@@ -1325,20 +1336,22 @@ samba_status validate_bwd(const samba_scan_bwd_args* a, BwdPlan* plan) {
     if (!aligned(q, 4)) return SAMBA_ERR_MISALIGNED;
   BwdPlan local;
   BwdPlan* pl = plan ? plan : &local;
-  bwd_layout(nseq, tokens, a->dim, pl);
+  bwd_layout(nseq, tokens, a->dim, a->h_ckpt == nullptr, pl);
   if (!a->workspace || a->workspace_bytes < pl->bytes) return SAMBA_ERR_WORKSPACE;
   if (!aligned(a->workspace, 256)) return SAMBA_ERR_WORKSPACE;
   // no output may overlap an input or another output
   const size_t n_td = static_cast<size_t>(tokens) * a->dim, n_tn = static_cast<size_t>(tokens) * kN;
   const size_t n_dn = static_cast<size_t>(a->dim) * kN * 4, n_d = static_cast<size_t>(a->dim) * 4;
   const size_t n_state = static_cast<size_t>(nseq) * a->dim * kN * 4;
-  const void* ins[] = {a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias, a->h0, a->dy, a->dh_last, a->cu_seqlens};
+  const void* ins[] = {a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias, a->h0, a->dy, a->dh_last, a->cu_seqlens,
+                       a->h_ckpt};
   const size_t insz[] = {n_td * ei, n_td * ei, n_td * ei, n_tn * ei, n_tn * ei, n_dn, n_d, n_d, n_state, n_td * ei,
-                         n_state, a->cu_seqlens ? static_cast<size_t>(nseq + 1) * 4 : 0};
+                         n_state, a->cu_seqlens ? static_cast<size_t>(nseq + 1) * 4 : 0,
+                         a->h_ckpt ? ckpt_bytes(tokens, nseq, a->dim) : 0};
   const void* outs[] = {a->dx, a->ddt, a->dz, a->dB, a->dC, a->dA, a->dD, a->ddt_bias, a->dh0, a->workspace};
   const size_t outsz[] = {n_td * ei, n_td * ei, n_td * ei, n_tn * 4, n_tn * 4, n_dn, n_d, n_d, n_state, pl->bytes};
   for (int i = 0; i < 10; ++i) {
-    for (int j = 0; j < 12; ++j)
+    for (int j = 0; j < 13; ++j)
       if (overlap(outs[i], outsz[i], ins[j], insz[j])) return SAMBA_ERR_ALIASING;
     for (int j = i + 1; j < 10; ++j)
       if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return SAMBA_ERR_ALIASING;
@@ -1350,7 +1363,8 @@ samba_status validate_bwd(const samba_scan_bwd_args* a, BwdPlan* plan) {
                      a->seqlen, a->dim, 0, &pl->ck);
   if (st != SAMBA_OK) return st;
   char* ws = static_cast<char*>(a->workspace);
-  pl->ck.prm.ckpt = reinterpret_cast<float*>(ws);
+  float* ckpt = a->h_ckpt ? const_cast<float*>(a->h_ckpt) : reinterpret_cast<float*>(ws);
+  pl->ck.prm.ckpt = ckpt;
   const int ts = a->time_slices;
   pl->W = ts ? ts : choose_time_slices(nseq, pl->ntiles, tokens, 8, bwd_slice);
   const int64_t nblocks = nseq * pl->ntiles;
@@ -1360,7 +1374,7 @@ samba_status validate_bwd(const samba_scan_bwd_args* a, BwdPlan* plan) {
   p.x = a->x; p.dt = a->dt; p.z = a->z; p.B = a->B; p.C = a->C; p.dy = a->dy;
   p.A = a->A; p.Dskip = a->D; p.bias = a->dt_bias;
   p.dh_last = a->dh_last;
-  p.ckpt = reinterpret_cast<const float*>(ws);
+  p.ckpt = ckpt;
   p.dx = a->dx; p.ddt = a->ddt; p.dz = a->dz;
   p.dbc = reinterpret_cast<float*>(ws + pl->off_dbc);
   p.dpar = reinterpret_cast<float*>(ws + pl->off_dpar);
@@ -1423,6 +1437,7 @@ samba_status samba_scan_fwd(const samba_scan_fwd_args* args, void* stream) {
   if (st != SAMBA_OK) return st;
   pl.prm.h_last = args->h_last;
   pl.prm.y = args->y;
+  pl.prm.ckpt = args->h_ckpt;
   if (pl.grid == 0) return SAMBA_OK;  // no sequences
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -1450,8 +1465,15 @@ samba_status samba_scan_bwd_workspace_size(const samba_scan_bwd_args* args, size
   if (st != SAMBA_OK) return st;
   if (!bytes) return SAMBA_ERR_NULL_ARG;
   BwdPlan pl;
-  bwd_layout(nseq, static_cast<int64_t>(args->batch) * args->seqlen, args->dim, &pl);
+  bwd_layout(nseq, static_cast<int64_t>(args->batch) * args->seqlen, args->dim, args->h_ckpt == nullptr, &pl);
   *bytes = pl.bytes;
+  return SAMBA_OK;
+}
+
+samba_status samba_scan_ckpt_bytes(int32_t batch, int32_t seqlen, int32_t nseq, int32_t dim, size_t* bytes) {
+  if (!bytes) return SAMBA_ERR_NULL_ARG;
+  if (batch < 0 || seqlen < 0 || nseq < 0 || dim < 1) return SAMBA_ERR_BAD_SHAPE;
+  *bytes = ckpt_bytes(static_cast<int64_t>(batch) * seqlen, nseq, dim);
   return SAMBA_OK;
 }
 
@@ -1462,7 +1484,7 @@ samba_status samba_scan_bwd(const samba_scan_bwd_args* args, void* stream) {
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = args->in_dtype == SAMBA_BF16;
   if (pl.prm.nblocks > 0) {
-    if (pl.tokens > 0) {
+    if (pl.tokens > 0 && !args->h_ckpt) {
       const hipError_t e = bf ? launch_ckpt<uint16_t>(pl.ck, s) : launch_ckpt<float>(pl.ck, s);
       if (e != hipSuccess) return SAMBA_ERR_HIP;
     }

@@ -11,14 +11,15 @@ from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "libsamba_scan.so"
 DSTATE = 16
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 SAMBA_F32, SAMBA_BF16 = 0, 1
 STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE", 3: "SAMBA_ERR_BAD_DTYPE",
                 4: "SAMBA_ERR_MISALIGNED", 5: "SAMBA_ERR_ALIASING", 6: "SAMBA_ERR_UNSUPPORTED",
                 7: "SAMBA_ERR_BAD_STRUCT", 8: "SAMBA_ERR_HIP", 9: "SAMBA_ERR_WORKSPACE"}
 EXPORTED = ("samba_scan_fwd", "samba_scan_step", "samba_scan_fwd_plan", "samba_scan_bwd",
-            "samba_scan_bwd_workspace_size", "samba_status_string", "samba_scan_abi_version")
+            "samba_scan_bwd_workspace_size", "samba_scan_ckpt_bytes", "samba_status_string",
+            "samba_scan_abi_version")
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -29,7 +30,7 @@ class FwdArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("batch", _I32), ("seqlen", _I32), ("dim", _I32),
                 ("dstate", _I32), ("cu_seqlens", _P), ("nseq", _I32), ("in_dtype", _I32), ("y_dtype", _I32),
                 ("time_slices", _I32), ("x", _P), ("dt", _P), ("z", _P), ("B", _P), ("C", _P), ("A", _P),
-                ("D", _P), ("dt_bias", _P), ("h0", _P), ("h_last", _P), ("y", _P)]
+                ("D", _P), ("dt_bias", _P), ("h0", _P), ("h_last", _P), ("y", _P), ("h_ckpt", _P)]
 
 
 class StepArgs(ctypes.Structure):
@@ -44,7 +45,7 @@ class BwdArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("batch", _I32), ("seqlen", _I32), ("dim", _I32),
                 ("dstate", _I32), ("cu_seqlens", _P), ("nseq", _I32), ("in_dtype", _I32), ("time_slices", _I32),
                 ("x", _P), ("dt", _P), ("z", _P), ("B", _P), ("C", _P), ("A", _P), ("D", _P), ("dt_bias", _P),
-                ("h0", _P), ("dy", _P), ("dh_last", _P), ("dx", _P), ("ddt", _P), ("dz", _P), ("dB", _P),
+                ("h0", _P), ("dy", _P), ("dh_last", _P), ("h_ckpt", _P), ("dx", _P), ("ddt", _P), ("dz", _P), ("dB", _P),
                 ("dC", _P), ("dA", _P), ("dD", _P), ("ddt_bias", _P), ("dh0", _P), ("workspace", _P),
                 ("workspace_bytes", ctypes.c_size_t)]
 
@@ -79,6 +80,8 @@ def load_library(path: Path | str | None = None):
     lib.samba_scan_bwd.restype = ctypes.c_int
     lib.samba_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(BwdArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.samba_scan_bwd_workspace_size.restype = ctypes.c_int
+    lib.samba_scan_ckpt_bytes.argtypes = [_I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.samba_scan_ckpt_bytes.restype = ctypes.c_int
     lib.samba_status_string.argtypes = [ctypes.c_int]
     lib.samba_status_string.restype = ctypes.c_char_p
     lib.samba_scan_abi_version.restype = ctypes.c_int
@@ -128,8 +131,30 @@ def _stream_handle(stream):
     return s.cuda_stream
 
 
+def _seq_shape(x, cu_seqlens):
+    """(batch, seqlen, dim, nseq) of the token layout."""
+    if x.dim() == 3:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens needs packed [tokens][dim] inputs")
+        return x.shape[0], x.shape[1], x.shape[2], x.shape[0]
+    if x.dim() == 2:
+        return 1, x.shape[0], x.shape[1], (1 if cu_seqlens is None else cu_seqlens.numel() - 1)
+    raise ValueError("x must be [batch][seqlen][dim] or [tokens][dim]")
+
+
+def alloc_ckpt(x, cu_seqlens=None):
+    """An h_ckpt array for these inputs: fp32 [slots][dim][16], slots = tokens/8 + nseq + 1."""
+    import torch
+    batch, seqlen, dim, nseq = _seq_shape(x, cu_seqlens)
+    n = ctypes.c_size_t()
+    st = load_library().samba_scan_ckpt_bytes(batch, seqlen, nseq, dim, ctypes.byref(n))
+    if st != 0:
+        raise SambaError(st, "samba_scan_ckpt_bytes")
+    return torch.empty(n.value // (DSTATE * 4 * dim), dim, DSTATE, dtype=torch.float32, device=x.device)
+
+
 def fwd_args(x, dt, z, B, C, A, D, dt_bias, *, y, h0=None, h_last=None, cu_seqlens=None,
-             time_slices: int = 0) -> FwdArgs:
+             time_slices: int = 0, h_ckpt=None) -> FwdArgs:
     """Fill a samba_scan_fwd_args from tensors (shapes as in scan_fwd)."""
     if x.dim() == 3:
         batch, seqlen, dim = x.shape
@@ -153,11 +178,12 @@ def fwd_args(x, dt, z, B, C, A, D, dt_bias, *, y, h0=None, h_last=None, cu_seqle
     a.x, a.dt, a.z, a.B, a.C = _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C)
     a.A, a.D, a.dt_bias = _ptr(A), _ptr(D), _ptr(dt_bias)
     a.h0, a.h_last, a.y = _ptr(h0), _ptr(h_last), _ptr(y)
+    a.h_ckpt = _ptr(h_ckpt)
     return a
 
 
 def scan_fwd(x, dt, z, B, C, A, D, dt_bias, *, h0=None, h_last=None, y=None, return_last_state: bool = True,
-             cu_seqlens=None, y_dtype=None, time_slices: int = 0, stream=None):
+             cu_seqlens=None, y_dtype=None, time_slices: int = 0, h_ckpt=None, stream=None):
     """Selective-scan prefill through samba_scan_fwd.
 
     x, dt, z : [batch][seqlen][dim]  (or [tokens][dim] with cu_seqlens)   bf16 or fp32
@@ -165,10 +191,11 @@ def scan_fwd(x, dt, z, B, C, A, D, dt_bias, *, h0=None, h_last=None, y=None, ret
     A        : [dim][16] fp32;  D, dt_bias : [dim] fp32
     h0       : [nseq][dim][16] fp32 or None (zeros)
     cu_seqlens: int32 [nseq+1] device tensor of packed sequence offsets, or None
+    h_ckpt   : optional output from alloc_ckpt(x, cu_seqlens): states every 8 tokens, for scan_bwd
     Returns (y, h_last); h_last is None when neither given nor requested.
     """
     import torch
-    _check_dev(x, dt, z, B, C, A, D, dt_bias, h0, h_last, y, cu_seqlens)
+    _check_dev(x, dt, z, B, C, A, D, dt_bias, h0, h_last, y, cu_seqlens, h_ckpt)
     if y is None:
         y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
     if h_last is None and return_last_state:
@@ -176,7 +203,7 @@ def scan_fwd(x, dt, z, B, C, A, D, dt_bias, *, h0=None, h_last=None, y=None, ret
             cu_seqlens.numel() - 1 if cu_seqlens is not None else 1)
         h_last = torch.empty((nseq, x.shape[-1], DSTATE), dtype=torch.float32, device=x.device)
     a = fwd_args(x, dt, z, B, C, A, D, dt_bias, y=y, h0=h0, h_last=h_last, cu_seqlens=cu_seqlens,
-                 time_slices=time_slices)
+                 time_slices=time_slices, h_ckpt=h_ckpt)
     st = load_library().samba_scan_fwd(ctypes.byref(a), _P(_stream_handle(stream)))
     if st != 0:
         raise SambaError(st, "samba_scan_fwd")
@@ -223,7 +250,7 @@ def scan_step(state, x, dt, z, B, C, A, D, dt_bias, *, y=None, y_dtype=None, str
 
 
 def bwd_args(x, dt, z, B, C, A, D, dt_bias, dy, *, dx, ddt, dz, dB, dC, dA, dD, ddt_bias, h0=None, dh_last=None,
-             dh0=None, cu_seqlens=None, workspace=None, time_slices: int = 0) -> BwdArgs:
+             dh0=None, cu_seqlens=None, workspace=None, time_slices: int = 0, h_ckpt=None) -> BwdArgs:
     """Fill a samba_scan_bwd_args from tensors (shapes as in scan_bwd)."""
     if x.dim() == 3:
         batch, seqlen, dim = x.shape
@@ -245,7 +272,7 @@ def bwd_args(x, dt, z, B, C, A, D, dt_bias, dy, *, dx, ddt, dz, dB, dC, dA, dD, 
     a.time_slices = int(time_slices)
     a.x, a.dt, a.z, a.B, a.C = _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C)
     a.A, a.D, a.dt_bias, a.h0 = _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(h0)
-    a.dy, a.dh_last = _ptr(dy), _ptr(dh_last)
+    a.dy, a.dh_last, a.h_ckpt = _ptr(dy), _ptr(dh_last), _ptr(h_ckpt)
     a.dx, a.ddt, a.dz, a.dB, a.dC = _ptr(dx), _ptr(ddt), _ptr(dz), _ptr(dB), _ptr(dC)
     a.dA, a.dD, a.ddt_bias, a.dh0 = _ptr(dA), _ptr(dD), _ptr(ddt_bias), _ptr(dh0)
     a.workspace = _ptr(workspace)
@@ -262,16 +289,17 @@ def bwd_workspace_bytes(a: BwdArgs) -> int:
 
 
 def scan_bwd(x, dt, z, B, C, A, D, dt_bias, dy, *, h0=None, dh_last=None, cu_seqlens=None, workspace=None,
-             want_dh0: bool = True, time_slices: int = 0, stream=None):
+             want_dh0: bool = True, time_slices: int = 0, h_ckpt=None, stream=None):
     """Gradients of scan_fwd through samba_scan_bwd.
 
     Inputs as for scan_fwd, plus dy (shaped like y, same dtype as x) and dh_last ([nseq][dim][16] fp32 or None).
     `workspace` is a device tensor (any dtype) of at least the size the library asks for, or None (allocated
-    here).  Returns a dict: dx, ddt, dz (like x), dB, dC (like B, fp32), dA [dim][16], dD, ddt_bias [dim] and
+    here).  h_ckpt: the checkpoints a scan_fwd of the same inputs wrote (skips their recomputation), or None.
+    Returns a dict: dx, ddt, dz (like x), dB, dC (like B, fp32), dA [dim][16], dD, ddt_bias [dim] and
     dh0 [nseq][dim][16] (fp32; None unless want_dh0).
     """
     import torch
-    _check_dev(x, dt, z, B, C, A, D, dt_bias, dy, h0, dh_last, cu_seqlens, workspace)
+    _check_dev(x, dt, z, B, C, A, D, dt_bias, dy, h0, dh_last, cu_seqlens, workspace, h_ckpt)
     dev = x.device
     dim = x.shape[-1]
     nseq = x.shape[0] if cu_seqlens is None and x.dim() == 3 else (
@@ -284,7 +312,7 @@ def scan_bwd(x, dt, z, B, C, A, D, dt_bias, dy, *, h0=None, dh_last=None, cu_seq
     out["ddt_bias"] = torch.empty(dim, dtype=torch.float32, device=dev)
     out["dh0"] = torch.empty((nseq, dim, DSTATE), dtype=torch.float32, device=dev) if want_dh0 else None
     a = bwd_args(x, dt, z, B, C, A, D, dt_bias, dy, h0=h0, dh_last=dh_last, cu_seqlens=cu_seqlens,
-                 time_slices=time_slices, **out)
+                 time_slices=time_slices, h_ckpt=h_ckpt, **out)
     if workspace is None:
         workspace = torch.empty(max(bwd_workspace_bytes(a), 1), dtype=torch.uint8, device=dev)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()

@@ -126,6 +126,9 @@ FWD_CASES = {
     "y_overlaps_x": (lambda a: setattr(a, "y", a.x + 64), 5),
     "h_last_overlaps_h0": (lambda a: setattr(a, "h_last", a.h0 + 64), 5),
     "h_last_overlaps_A": (lambda a: setattr(a, "h_last", a.A), 5),
+    "misaligned_h_ckpt": (lambda a: setattr(a, "h_ckpt", BASE + 12 * (1 << 30) + 8), 4),
+    "h_ckpt_overlaps_x": (lambda a: setattr(a, "h_ckpt", a.x + 64), 5),
+    "h_ckpt_overlaps_y": (lambda a: setattr(a, "h_ckpt", a.y), 5),
     "varlen_batch": (lambda a: (setattr(a, "cu_seqlens", BASE + 11 * (1 << 30)), setattr(a, "nseq", 3)), 2),
     "varlen_nseq0": (lambda a: (setattr(a, "batch", 1), setattr(a, "cu_seqlens", BASE + 11 * (1 << 30)),
                                 setattr(a, "nseq", 0)), 2),
@@ -276,6 +279,8 @@ BWD_CASES = {
     "workspace_overlaps_dy": (lambda a: setattr(a, "workspace", a.dy), 5),
     "dh0_overlaps_h0": (lambda a: setattr(a, "dh0", a.h0), 5),
     "varlen_batch": (lambda a: (setattr(a, "cu_seqlens", BASE + 40 * (1 << 30)), setattr(a, "nseq", 3)), 2),
+    "misaligned_h_ckpt": (lambda a: setattr(a, "h_ckpt", BASE + 41 * (1 << 30) + 4), 4),
+    "h_ckpt_overlaps_dx": (lambda a: setattr(a, "h_ckpt", a.dx), 5),
 }
 
 
@@ -285,6 +290,24 @@ def test_bwd_rejects(lib, name):
     mutate, code = BWD_CASES[name]
     mutate(a)
     assert lib.samba_scan_bwd(ctypes.byref(a), None) == code
+
+
+def test_ckpt_bytes(lib):
+    """h_ckpt holds slots = tokens/8 + nseq + 1 rows of dim x 16 fp32 states."""
+    n = ctypes.c_size_t()
+    for batch, seqlen, nseq, dim in ((4, 4096, 4, 4096), (1, 100, 7, 40), (2, 0, 2, 16)):
+        assert lib.samba_scan_ckpt_bytes(batch, seqlen, nseq, dim, ctypes.byref(n)) == 0
+        assert n.value == (batch * seqlen // 8 + nseq + 1) * dim * 64
+    assert lib.samba_scan_ckpt_bytes(1, 8, 1, 0, ctypes.byref(n)) == 2
+    assert lib.samba_scan_ckpt_bytes(1, 8, 1, 8, None) == 1
+
+
+def test_bwd_workspace_without_checkpoint_section(lib):
+    a = bwd_ok(4, 4096, 4096)
+    st, full = ws_bytes(lib, a)
+    a.h_ckpt = BASE + 42 * (1 << 30)
+    st2, small = ws_bytes(lib, a)
+    assert st == st2 == 0 and full - small == r256((4 * 4096 // 8 + 4 + 1) * 4096 * 64)
 
 
 def test_bwd_null_args(lib):

@@ -185,3 +185,55 @@ def test_bwd_full_training_shape():
                    host(ex["dy"]), seq_start=np.arange(Bt + 1, dtype=np.int64) * L)
     gh = {k: host(v).reshape(o[k].shape) for k, v in g.items() if v is not None}
     check_all(gh, o, np.arange(Bt + 1, dtype=np.int64) * L, "bf16", "full B4 L4096 D4096")
+
+
+@pytest.mark.parametrize("lengths", [None, [37, 0, 100, 8, 1, 0, 64]])
+def test_forward_checkpoints_feed_the_backward(lengths):
+    """samba_scan_fwd with h_ckpt: y and h_last unchanged (bitwise); every checkpoint is the oracle's state
+    before that token; the backward fed these checkpoints equals the self-contained backward (bitwise)."""
+    D, cfg = 40, 0
+    if lengths is None:
+        batch, L = 2, 100
+        rows, nseq = batch * L, batch
+        seq_start = np.arange(batch + 1, dtype=np.int64) * L
+        shp, bshp = (batch, L, D), (batch, L, 16)
+    else:
+        rows, nseq = int(sum(lengths)), len(lengths)
+        seq_start = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+        shp, bshp = (rows, D), (rows, 16)
+    say("case: forward checkpoints -> backward, %s" % ("B2 L100" if lengths is None else lengths))
+    inp = I.make_fwd_inputs_np(cfg, rows, D, in_dtype="bf16")
+    ex = I.make_bwd_extra_np(cfg, rows, D, nseq)
+    h0 = I.make_h0(cfg, nseq, D, scale=1.0)
+    x, dt, z, dy = (dev_in(a, "bf16").reshape(shp) for a in (inp["x"], inp["dt"], inp["z"], ex["dy"]))
+    B, C = (dev_in(inp[k], "bf16").reshape(bshp) for k in ("B", "C"))
+    A, Dv, bias = (torch.from_numpy(inp[k]).to(DEV) for k in ("A", "D", "dt_bias"))
+    cu = torch.from_numpy(seq_start.astype(np.int32)).to(DEV) if lengths is not None else None
+    h0t, dhl = torch.from_numpy(h0).to(DEV), torch.from_numpy(ex["dh_last"]).to(DEV)
+    y1, hl1 = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=h0t, cu_seqlens=cu)
+    ck = S.alloc_ckpt(x, cu)
+    y2, hl2 = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=h0t, cu_seqlens=cu, h_ckpt=ck)
+    g1 = S.scan_bwd(x, dt, z, B, C, A, Dv, bias, dy, h0=h0t, dh_last=dhl, cu_seqlens=cu)
+    g2 = S.scan_bwd(x, dt, z, B, C, A, Dv, bias, dy, h0=h0t, dh_last=dhl, cu_seqlens=cu, h_ckpt=ck)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(hl1, hl2)
+    for k, v in g1.items():
+        assert torch.equal(v, g2[k]), "backward with forward checkpoints differs: " + k
+    ckh = host(ck)
+    worst = 0.0
+    for s_ in range(nseq):
+        a, b = int(seq_start[s_]), int(seq_start[s_ + 1])
+        for j in range((b - a + 7) // 8):
+            slot = a // 8 + s_ + j
+            if j == 0:
+                ref = h0[s_].astype(np.float64)
+            else:
+                e = a + 8 * j
+                _, ref = O.scan_fwd(inp["x_f32"].reshape(rows, D)[a:e], inp["dt_f32"].reshape(rows, D)[a:e],
+                                    inp["z_f32"].reshape(rows, D)[a:e], inp["B_f32"].reshape(rows, 16)[a:e],
+                                    inp["C_f32"].reshape(rows, 16)[a:e], inp["A"], inp["D"], inp["dt_bias"],
+                                    h0=h0[s_:s_ + 1])
+                ref = ref[0]
+            worst = max(worst, check_fp32(ckh[slot].reshape(1, -1), ref.reshape(1, -1),
+                                          "checkpoint s=%d j=%d" % (s_, j)))
+    say("forward checkpoints: worst state error %.2e" % worst)
