@@ -283,6 +283,38 @@ int oracle_scan_bwd(int64_t nseq, const int64_t* seq_start, int64_t dim, int64_t
   return failed ? -1 : 0;
 }
 
+/*
+ * Selection projections (page "SAMBA混合注意力状态空间模型", 数学框架 -> Mamba层:
+ * B_t, C_t and the argument of τ_Δ are linear maps of x_t).  The three maps are
+ * the rows of one matrix W [dim + 2*dstate][dim] (one output feature per row,
+ * as a linear layer stores its weight): rows 0..dim-1 give dt_raw (Linear_Δ,
+ * full rank), the next dstate rows B_t (Linear_B), the last dstate rows C_t
+ * (Linear_C).  No bias: τ_Δ's bias is the scan's dt_bias.
+ *   out[t][j] = sum_k x[t][k] * W[j][k];  dt = out[:, :dim], B = out[:, dim:dim+dstate],
+ *   C = out[:, dim+dstate:]
+ * x [T][dim]; dt [T][dim], B and C [T][dstate] (written).  OpenMP over tokens.
+ */
+int oracle_proj(int64_t T, int64_t dim, int64_t dstate, const double* x, const double* W,
+                double* dt, double* B, double* C, int nthreads) {
+  if (T < 0 || dim < 1 || dstate < 1) return -1;
+  const int64_t nout = dim + 2 * dstate;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+#endif
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t j = 0; j < nout; ++j) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < dim; ++k) acc += x[t * dim + k] * W[j * dim + k];
+      if (j < dim) dt[t * dim + j] = acc;
+      else if (j < dim + dstate) B[t * dstate + (j - dim)] = acc;
+      else C[t * dstate + (j - dim - dstate)] = acc;
+    }
+  }
+  (void)nthreads;
+  return 0;
+}
+
 /* Number of OpenMP threads a call with nthreads <= 0 would use. */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

@@ -53,6 +53,8 @@ def _bind(lib):
     lib.oracle_scan_step.restype = ctypes.c_int
     lib.oracle_scan_bwd.argtypes = [I64, P, I64, I64] + [P] * 20 + [ctypes.c_int]
     lib.oracle_scan_bwd.restype = ctypes.c_int
+    lib.oracle_proj.argtypes = [I64, I64, I64, P, P, P, P, P, ctypes.c_int]
+    lib.oracle_proj.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -155,6 +157,20 @@ def scan_bwd(x, dt, z, B, C, A, D, dt_bias, dy, h0=None, dh_last=None, seq_start
     for k in ("dB", "dC"):
         out[k] = out[k].reshape(bshape)
     return out
+
+
+def proj(x, W, dstate: int = 16, nthreads: int = 0, lib=None):
+    """Selection projections in fp64: x [T][dim], W [dim + 2*dstate][dim] -> (dt_raw [T][dim], B, C [T][dstate])."""
+    lib = lib or load()
+    x, W = _f64(x), _f64(W)
+    T, dim = x.shape
+    assert W.shape == (dim + 2 * dstate, dim)
+    dt = np.empty((T, dim))
+    B, C = np.empty((T, dstate)), np.empty((T, dstate))
+    rc = lib.oracle_proj(T, dim, dstate, _ptr(x), _ptr(W), _ptr(dt), _ptr(B), _ptr(C), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_proj failed (%d)" % rc)
+    return dt, B, C
 
 
 def scan_step(state, x, dt, z, B, C, A, D, dt_bias, nthreads: int = 0, lib=None):
