@@ -29,6 +29,7 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "scan GB/s & tokens·channels/s at L=128K, % HBM roofline; decode steps/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak (no sparsity)
 # VALU issue peak: 256 CUs x 4 SIMDs x 32 fp32 lanes/clock x 2.4 GHz (one slot = one full-rate fp32 lane op)
 VALU_PEAK_TSLOT = 256 * 4 * 32 * 2.4e9 / 1e12
 TRANS_SLOTS = 4            # a transcendental (exp2, log2, rcp) issues at a quarter of the fp32 rate
@@ -237,6 +238,62 @@ def bench_backward(steps: int = 10, warmup: int = 5):
                          "unit": "Tslot/s", "frac": round(slots / VALU_PEAK_TSLOT, 4), "traffic": None,
                          "kernel": "samba_scan_bwd call (checkpoint + backward + finish kernels)",
                          "slots_per_token_channel": BWD_SLOTS_PER_TD}}
+
+
+def bench_proj(steps: int = 20, warmup: int = 5):
+    """samba_proj on the long-prompt chunk: 16384 tokens, D 4096 -> dt_raw, B, C (bf16 out)."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import scan as S
+
+    T, D, N = 16384, 4096, 16
+    dev = torch.device("cuda:0")
+    x = I.make_fwd_inputs_torch(3, T, D, dev)["x"]
+    W = I.make_proj_weight_torch(3, D, dev)
+    dt = torch.empty(T, D, dtype=torch.bfloat16, device=dev)
+    B = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    C = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+    a = S.proj_args(x, W, dt=dt, B=B, C=C)
+    lib = S.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    for _ in range(warmup):
+        lib.samba_proj(ctypes.byref(a), sh)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        if lib.samba_proj(ctypes.byref(a), sh) != 0:
+            raise RuntimeError("samba_proj failed")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * T * (D + 2 * N) * D
+    tf = flops / (ms * 1e-3) / 1e12
+    nbytes = (T * D + (D + 2 * N) * D + T * (D + 2 * N)) * 2
+    return {"workload": "selection projections x[16384][4096] W[4128][4096] bf16 -> dt_raw, B, C (bf16)",
+            "steps": steps, "ms_per_call": ms, "tflops": tf, "tokens_per_s": T / (ms * 1e-3),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "proj_kernel<bf16> (v_mfma_f32_32x32x16_bf16)", "flops_per_call": flops,
+                         "algorithmic_bytes_per_call": nbytes}}
+
+
+def cpu_baseline_proj(rows: int = 64):
+    """The fp64 oracle's projections on `rows` tokens of the same shape (D 4096), extrapolated to TFLOP/s."""
+    import numpy as np
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+
+    D = 4096
+    x = I.make_fwd_inputs_np(3, rows, D, in_dtype="bf16")["x_f32"]
+    W = I.make_proj_weight_np(3, D)["W_f32"]
+    lib = O.load()
+    t0 = time.perf_counter()
+    O.proj(x, W, lib=lib)
+    spent = time.perf_counter() - t0
+    return {"value": 2.0 * rows * (D + 32) * D / spent / 1e12, "unit": "TFLOP/s", "cores": O.max_threads(lib),
+            "kind": "oracle", "sample": "%d of the 16384 tokens, all 4128 outputs, fp64 oracle, %.1f s" % (rows, spent)}
 
 
 def bench_decode(steps: int = 65536, ring: int = 256):
@@ -501,6 +558,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     ap.add_argument("--bwd-steps", type=int, default=10)
+    ap.add_argument("--no-proj", action="store_true", help="skip the selection-projection leg")
     ap.add_argument("--time-slices", type=int, default=0, help="force the prefill's waves per time chunk (0 = auto)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (untimed), the reference kernel for HBM byte counters")
@@ -557,6 +615,8 @@ def main():
                            "kernel": "scan_step_kernel<bf16,bf16>"}
         dec["copy_frac"] = dec["gbs"] / ceiling if ceiling else None
         line["decode"] = dec
+    if not args.no_proj:
+        line["projections"] = bench_proj()
     if not args.no_bwd:
         line["backward"] = bench_backward(args.bwd_steps)
         line["backward"]["roofline"]["traffic"] = read_traffic("backward")
@@ -566,6 +626,8 @@ def main():
             line["cpu_baseline"]["decode"] = cpu_baseline_decode()
         if not args.no_bwd:
             line["cpu_baseline"]["backward"] = cpu_baseline_backward()
+        if not args.no_proj:
+            line["cpu_baseline"]["projections"] = cpu_baseline_proj()
     print(json.dumps(line), flush=True)
 
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SAMBA_SCAN_ABI_VERSION 3
+#define SAMBA_SCAN_ABI_VERSION 4
 #define SAMBA_DSTATE 16
 
 typedef enum {
@@ -197,6 +197,34 @@ samba_status samba_scan_bwd_workspace_size(const samba_scan_bwd_args* args, size
 
 /* Enqueue the backward.  See samba_scan_bwd_args. */
 samba_status samba_scan_bwd(const samba_scan_bwd_args* args, void* stream);
+
+/*
+ * Selection projections (page "SAMBA混合注意力状态空间模型", 数学框架 -> Mamba层:
+ * B_t = Linear_B(x_t), C_t = Linear_C(x_t), and Linear_Δ(x_t) inside τ_Δ): the
+ * three linear maps that produce the scan's dt, B and C from its input x, as
+ * one bf16 GEMM on the matrix cores with fp32 accumulation.
+ *     out[t][j] = sum_k x[t][k] * W[j][k],  j < dim + 2*dstate
+ *     dt[t][j] = out[t][j] (j < dim);  B[t][n] = out[t][dim + n];  C[t][n] = out[t][dim + dstate + n]
+ * W [dim + 2*dstate][dim] holds the maps as rows (one output feature per row,
+ * as a linear layer stores its weight): Linear_Δ (dim rows, full rank), then
+ * Linear_B, then Linear_C.  No bias (τ_Δ's bias is dt_bias of the scan).
+ * x [tokens][dim] and W are bf16 (in_dtype must be SAMBA_BF16), 16-byte
+ * aligned, dim a multiple of 8; dt [tokens][dim], B and C [tokens][dstate]
+ * are written in out_dtype (bf16 round to nearest even, or fp32), aligned to
+ * their element size, and must not overlap x, W or each other.  The outputs
+ * feed samba_scan_fwd / samba_scan_bwd directly (same layouts).
+ */
+typedef struct {
+  uint32_t struct_size;        /* = sizeof(samba_proj_args) */
+  int32_t tokens, dim, dstate;
+  int32_t in_dtype, out_dtype;
+  const void* x;               /* [tokens][dim] bf16 */
+  const void* W;               /* [dim + 2*dstate][dim] bf16 */
+  void *dt, *B, *C;            /* [tokens][dim], [tokens][dstate], [tokens][dstate] */
+} samba_proj_args;
+
+/* Enqueue the selection projections.  See samba_proj_args. */
+samba_status samba_proj(const samba_proj_args* args, void* stream);
 
 /* Enqueue a prefill scan.  See samba_scan_fwd_args. */
 samba_status samba_scan_fwd(const samba_scan_fwd_args* args, void* stream);

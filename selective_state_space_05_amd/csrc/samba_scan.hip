@@ -1100,6 +1100,142 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Selection projections: [dt_raw | B | C] = x W^T, one bf16 GEMM on the matrix
+// cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  x [T][dim] and W
+// [dim + 2N][dim] are both K-contiguous.  A 256-thread workgroup computes a
+// 128 x 128 output tile: its four waves own 64 x 64 quadrants (2 x 2 MFMA
+// blocks of 32 x 32).  K advances 64 at a time through double-buffered LDS
+// tiles (rows padded to 144 bytes so that the 16-byte fragment reads of 8
+// consecutive rows hit distinct banks); the next step's global loads are
+// issued before the current step's MFMAs.  Tiles are ordered in groups of 8
+// row tiles so that workgroups running together on one XCD share their A and
+// B tiles in L2.  Operand layouts (checked on the device): lane l holds
+// A[l % 32][8 (l / 32) + 0..7] and B[8 (l / 32) + 0..7][l % 32]; result
+// element e of lane l is D[8 (e / 4) + 4 (l / 32) + e % 4][l % 32].
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kPM = 128, kPN = 128, kPK = 64;
+constexpr int kPRow = kPK + 8;      // LDS row stride in bf16 (144 bytes)
+constexpr int kPGroup = 8;          // row tiles per ordering group
+
+struct ProjParams {
+  const uint16_t* x;    // [T][dim]
+  const uint16_t* W;    // [nout][dim]
+  void *dt, *B, *C;
+  int32_t T, dim, dstate, nout, mtiles, ntiles, nblocks;
+};
+
+template <typename Tout>
+__device__ __forceinline__ void proj_store(const ProjParams& p, int t, int j, float v) {
+  if (t >= p.T || j >= p.nout) return;
+  if (j < p.dim) st_out(static_cast<Tout*>(p.dt), static_cast<int64_t>(t) * p.dim + j, v);
+  else if (j < p.dim + p.dstate) st_out(static_cast<Tout*>(p.B), static_cast<int64_t>(t) * p.dstate + (j - p.dim), v);
+  else st_out(static_cast<Tout*>(p.C), static_cast<int64_t>(t) * p.dstate + (j - p.dim - p.dstate), v);
+}
+
+template <typename Tout>
+__global__ __launch_bounds__(256) void proj_kernel(ProjParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kPM * kPRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kPN * kPRow];
+  const int logical = xcd_remap(blockIdx.x, p.nblocks);
+  // grouped order: kPGroup row tiles x all column tiles per group
+  const int per_group = kPGroup * p.ntiles;
+  const int grp = logical / per_group;
+  const int first_m = grp * kPGroup;
+  const int gm = (p.mtiles - first_m) < kPGroup ? (p.mtiles - first_m) : kPGroup;
+  const int within = logical - grp * per_group;
+  const int mt = first_m + within % gm;
+  const int nt = within / gm;
+  const int m0 = mt * kPM, n0 = nt * kPN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const uint32_t row_bytes = static_cast<uint32_t>(p.dim) * 2u;
+  const rsrc_t rx = make_rsrc_rows(p.x + static_cast<int64_t>(m0) * p.dim, p.T - m0 < kPM ? p.T - m0 : kPM,
+                                   static_cast<uint32_t>(p.dim));
+  const rsrc_t rw = make_rsrc_rows(p.W + static_cast<int64_t>(n0) * p.dim, p.nout - n0 < kPN ? p.nout - n0 : kPN,
+                                   static_cast<uint32_t>(p.dim));
+  // this thread's four 16-byte chunks of each tile: row = q / 8, chunk c = q % 8 (8 bf16 each)
+  uint32_t goff[4];
+  int lofs[4], kc[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int q = tid + 256 * r;
+    const int row = q >> 3, c = q & 7;
+    goff[r] = static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(c) * 16u;
+    lofs[r] = row * kPRow + c * 8;
+    kc[r] = c * 8;
+  }
+  uint4 ra[4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool in = k0 + kc[r] < p.dim;   // K tail: chunks past dim read as zeros
+      const uint32_t off = goff[r] + static_cast<uint32_t>(k0) * 2u;
+      const auto va = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      const auto vb = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
+      ra[r] = in ? make_uint4(va[0], va[1], va[2], va[3]) : make_uint4(0u, 0u, 0u, 0u);
+      rb[r] = in ? make_uint4(vb[0], vb[1], vb[2], vb[3]) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<uint4*>(&sA[buf][lofs[r]]) = ra[r];
+      *reinterpret_cast<uint4*>(&sW[buf][lofs[r]]) = rb[r];
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = (p.dim + kPK - 1) / kPK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int fr = lane & 31, fk = (lane >> 5) * 8;   // fragment row and k offset of this lane
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nk) gload((ks + 1) * kPK);
+#pragma unroll
+    for (int kk = 0; kk < kPK / 16; ++kk) {
+      bf16x8_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][(64 * wm + 32 * i + fr) * kPRow + 16 * kk + fk]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(&sW[buf][(64 * wn + 32 * j + fr) * kPRow + 16 * kk + fk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (ks + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  // epilogue: element e of lane l is row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32 of its block
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int n = 64 * wn + 32 * j + (lane & 31);
+        proj_store<Tout>(p, m0 + m, n0 + n, acc[i][j][e]);
+      }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 int device_cu_count() {
@@ -1497,6 +1633,47 @@ samba_status samba_scan_bwd(const samba_scan_bwd_args* args, void* stream) {
   hipLaunchKernelGGL(scan_bwd_finish_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, pl.prm.dbc,
                      pl.prm.dpar, args->dB, args->dC, args->dA, args->dD, args->ddt_bias, pl.tokens, pl.ntiles,
                      static_cast<int32_t>(pl.nseq), args->dim);
+  return hipGetLastError() == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
+}
+
+samba_status samba_proj(const samba_proj_args* a, void* stream) {
+  if (!a) return SAMBA_ERR_NULL_ARG;
+  if (a->struct_size != sizeof(samba_proj_args)) return SAMBA_ERR_BAD_STRUCT;
+  if (a->in_dtype != SAMBA_BF16 || !dtype_ok(a->out_dtype)) return SAMBA_ERR_BAD_DTYPE;
+  if (a->tokens < 0 || a->dim < 8 || a->dstate < 1) return SAMBA_ERR_BAD_SHAPE;
+  if (a->dim % 8 != 0) return SAMBA_ERR_BAD_SHAPE;
+  const int64_t nout = static_cast<int64_t>(a->dim) + 2 * static_cast<int64_t>(a->dstate);
+  if (nout > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  if (!a->W) return SAMBA_ERR_NULL_ARG;
+  if (a->tokens > 0 && (!a->x || !a->dt || !a->B || !a->C)) return SAMBA_ERR_NULL_ARG;
+  const size_t eo = esize(a->out_dtype);
+  if (!aligned(a->x, 16) || !aligned(a->W, 16) || !aligned(a->dt, eo) || !aligned(a->B, eo) || !aligned(a->C, eo))
+    return SAMBA_ERR_MISALIGNED;
+  const size_t T = static_cast<size_t>(a->tokens), dim = static_cast<size_t>(a->dim), n = static_cast<size_t>(a->dstate);
+  const void* outs[] = {a->dt, a->B, a->C};
+  const size_t outsz[] = {T * dim * eo, T * n * eo, T * n * eo};
+  const void* ins[] = {a->x, a->W};
+  const size_t insz[] = {T * dim * 2, static_cast<size_t>(nout) * dim * 2};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 2; ++j)
+      if (overlap(outs[i], outsz[i], ins[j], insz[j])) return SAMBA_ERR_ALIASING;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outsz[i], outs[j], outsz[j])) return SAMBA_ERR_ALIASING;
+  }
+  if (a->tokens == 0) return SAMBA_OK;
+  ProjParams p;
+  p.x = static_cast<const uint16_t*>(a->x);
+  p.W = static_cast<const uint16_t*>(a->W);
+  p.dt = a->dt; p.B = a->B; p.C = a->C;
+  p.T = a->tokens; p.dim = a->dim; p.dstate = a->dstate; p.nout = static_cast<int32_t>(nout);
+  p.mtiles = (a->tokens + kPM - 1) / kPM;
+  p.ntiles = static_cast<int32_t>((nout + kPN - 1) / kPN);
+  const int64_t nblocks = static_cast<int64_t>(p.mtiles) * p.ntiles;
+  if (nblocks > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  p.nblocks = static_cast<int32_t>(nblocks);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a->out_dtype == SAMBA_BF16) hipLaunchKernelGGL(proj_kernel<uint16_t>, dim3(p.nblocks), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(proj_kernel<float>, dim3(p.nblocks), dim3(256), 0, s, p);
   return hipGetLastError() == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
 }
 

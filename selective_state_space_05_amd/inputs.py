@@ -11,6 +11,8 @@ Recipe (every config; sizes differ):
   * B, C ~ N(0, 1) per (token, state)
   * D[d] ~ U(0, 1)
   * h0 = 0 unless a test asks for a random carry-in
+  * selection projections: W [dim + 2N][dim] ~ N(0, 1/dim) (a linear layer's
+    scale, so dt_raw, B and C come out ~N(0, 1) like the scan's own inputs)
   * backward: upstream gradients dy ~ N(0, 1) per (token, channel) (in the
     input dtype) and, where a test asks for one, dh_last ~ N(0, 1) per
     (sequence, channel, state)
@@ -32,7 +34,7 @@ import numpy as np
 
 SEED_ROOT = 20240611
 TENSOR_IDS = {"x": 0, "z": 1, "dt": 2, "dt_init": 3, "A": 4, "B": 5, "C": 6, "D": 7,
-              "lengths": 8, "h0": 9, "dy": 10, "dh_last": 11}
+              "lengths": 8, "h0": 9, "dy": 10, "dh_last": 11, "W_sel": 12}
 DECODE_RING_BASE = 100
 DSTATE = 16
 
@@ -239,6 +241,20 @@ def make_bwd_extra_torch(cfg_id: int, rows: int, dim: int, nseq: int, device, ds
     return {"dy": _torch_normal(torch, (rows, dim), cfg_id, TENSOR_IDS["dy"], device, dt_),
             "dh_last": _torch_normal(torch, (nseq, dim, dstate), cfg_id, TENSOR_IDS["dh_last"], device,
                                      torch.float32)}
+
+
+def make_proj_weight_np(cfg_id: int, dim: int, dstate: int = DSTATE) -> dict:
+    """Selection-projection weight W [dim + 2*dstate][dim] as bf16 bits (W) and their fp32 values (W_f32)."""
+    v = (_normal(cfg_id, "W_sel", (dim + 2 * dstate, dim)) / np.float32(math.sqrt(dim))).astype(np.float32)
+    bits = bf16_bits_from_f32(v)
+    return {"W": bits, "W_f32": f32_from_bf16_bits(bits)}
+
+
+def make_proj_weight_torch(cfg_id: int, dim: int, device, dstate: int = DSTATE):
+    """Device bf16 W [dim + 2*dstate][dim] ~ N(0, 1/dim)."""
+    import torch
+    w = _torch_normal(torch, (dim + 2 * dstate, dim), cfg_id, TENSOR_IDS["W_sel"], device, torch.float32)
+    return (w / math.sqrt(dim)).to(torch.bfloat16)
 
 
 def make_step_ring_torch(cfg_id: int, ring: int, batch: int, dim: int, device, dstate: int = DSTATE) -> dict:

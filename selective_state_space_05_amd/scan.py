@@ -11,14 +11,14 @@ from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "libsamba_scan.so"
 DSTATE = 16
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 SAMBA_F32, SAMBA_BF16 = 0, 1
 STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE", 3: "SAMBA_ERR_BAD_DTYPE",
                 4: "SAMBA_ERR_MISALIGNED", 5: "SAMBA_ERR_ALIASING", 6: "SAMBA_ERR_UNSUPPORTED",
                 7: "SAMBA_ERR_BAD_STRUCT", 8: "SAMBA_ERR_HIP", 9: "SAMBA_ERR_WORKSPACE"}
 EXPORTED = ("samba_scan_fwd", "samba_scan_step", "samba_scan_fwd_plan", "samba_scan_bwd",
-            "samba_scan_bwd_workspace_size", "samba_scan_ckpt_bytes", "samba_status_string",
+            "samba_scan_bwd_workspace_size", "samba_scan_ckpt_bytes", "samba_proj", "samba_status_string",
             "samba_scan_abi_version")
 
 _P = ctypes.c_void_p
@@ -48,6 +48,12 @@ class BwdArgs(ctypes.Structure):
                 ("h0", _P), ("dy", _P), ("dh_last", _P), ("h_ckpt", _P), ("dx", _P), ("ddt", _P), ("dz", _P), ("dB", _P),
                 ("dC", _P), ("dA", _P), ("dD", _P), ("ddt_bias", _P), ("dh0", _P), ("workspace", _P),
                 ("workspace_bytes", ctypes.c_size_t)]
+
+
+class ProjArgs(ctypes.Structure):
+    """Mirror of samba_proj_args."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("tokens", _I32), ("dim", _I32), ("dstate", _I32),
+                ("in_dtype", _I32), ("out_dtype", _I32), ("x", _P), ("W", _P), ("dt", _P), ("B", _P), ("C", _P)]
 
 
 class SambaError(RuntimeError):
@@ -82,6 +88,8 @@ def load_library(path: Path | str | None = None):
     lib.samba_scan_bwd_workspace_size.restype = ctypes.c_int
     lib.samba_scan_ckpt_bytes.argtypes = [_I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_size_t)]
     lib.samba_scan_ckpt_bytes.restype = ctypes.c_int
+    lib.samba_proj.argtypes = [ctypes.POINTER(ProjArgs), _P]
+    lib.samba_proj.restype = ctypes.c_int
     lib.samba_status_string.argtypes = [ctypes.c_int]
     lib.samba_status_string.restype = ctypes.c_char_p
     lib.samba_scan_abi_version.restype = ctypes.c_int
@@ -320,3 +328,33 @@ def scan_bwd(x, dt, z, B, C, A, D, dt_bias, dy, *, h0=None, dh_last=None, cu_seq
     if st != 0:
         raise SambaError(st, "samba_scan_bwd")
     return out
+
+
+def proj_args(x, W, *, dt, B, C) -> ProjArgs:
+    """Fill a samba_proj_args: x [tokens][dim] bf16, W [dim + 2*dstate][dim] bf16; outputs as in proj."""
+    a = ProjArgs()
+    a.struct_size = ctypes.sizeof(ProjArgs)
+    a.tokens, a.dim = x.shape[0], x.shape[1]
+    a.dstate = (W.shape[0] - x.shape[1]) // 2
+    a.in_dtype = _dtype_code(x)
+    a.out_dtype = _dtype_code(dt)
+    a.x, a.W, a.dt, a.B, a.C = _ptr(x), _ptr(W), _ptr(dt), _ptr(B), _ptr(C)
+    return a
+
+
+def proj(x, W, *, out_dtype=None, dt=None, B=None, C=None, stream=None):
+    """Selection projections through samba_proj: x [tokens][dim] bf16 and W [dim + 2*dstate][dim] bf16 ->
+    (dt_raw [tokens][dim], B [tokens][dstate], C [tokens][dstate]) in out_dtype (default bf16)."""
+    import torch
+    _check_dev(x, W, dt, B, C)
+    T, dim = x.shape
+    N = (W.shape[0] - dim) // 2
+    od = out_dtype or torch.bfloat16
+    dt = torch.empty(T, dim, dtype=od, device=x.device) if dt is None else dt
+    B = torch.empty(T, N, dtype=od, device=x.device) if B is None else B
+    C = torch.empty(T, N, dtype=od, device=x.device) if C is None else C
+    a = proj_args(x, W, dt=dt, B=B, C=C)
+    st = load_library().samba_proj(ctypes.byref(a), _P(_stream_handle(stream)))
+    if st != 0:
+        raise SambaError(st, "samba_proj")
+    return dt, B, C

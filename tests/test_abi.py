@@ -48,7 +48,7 @@ def test_status_strings(lib):
 
 
 STRUCTS = (("samba_scan_fwd_args", S.FwdArgs), ("samba_scan_step_args", S.StepArgs),
-           ("samba_scan_bwd_args", S.BwdArgs))
+           ("samba_scan_bwd_args", S.BwdArgs), ("samba_proj_args", S.ProjArgs))
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -315,3 +315,47 @@ def test_bwd_null_args(lib):
     n = ctypes.c_size_t()
     assert lib.samba_scan_bwd_workspace_size(None, ctypes.byref(n)) == 1
     assert lib.samba_scan_bwd_workspace_size(ctypes.byref(bwd_ok()), None) == 1
+
+
+# --------------------------------------------------------------------------- #
+# selection projections: validation
+# --------------------------------------------------------------------------- #
+def proj_ok(tokens=100, dim=64, dstate=16):
+    a = S.ProjArgs()
+    a.struct_size = ctypes.sizeof(S.ProjArgs)
+    a.tokens, a.dim, a.dstate = tokens, dim, dstate
+    a.in_dtype, a.out_dtype = S.SAMBA_BF16, S.SAMBA_BF16
+    gb = 1 << 30
+    a.x, a.W, a.dt, a.B, a.C = BASE, BASE + gb, BASE + 2 * gb, BASE + 3 * gb, BASE + 4 * gb
+    return a
+
+
+PROJ_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 4), 7),
+    "f32_inputs": (lambda a: setattr(a, "in_dtype", S.SAMBA_F32), 3),
+    "out_dtype": (lambda a: setattr(a, "out_dtype", 9), 3),
+    "dim_not_multiple_of_8": (lambda a: setattr(a, "dim", 60), 2),
+    "neg_tokens": (lambda a: setattr(a, "tokens", -1), 2),
+    "zero_dstate": (lambda a: setattr(a, "dstate", 0), 2),
+    "null_W": (lambda a: setattr(a, "W", None), 1),
+    "null_dt": (lambda a: setattr(a, "dt", None), 1),
+    "misaligned_x": (lambda a: setattr(a, "x", a.x + 8), 4),
+    "misaligned_dt": (lambda a: setattr(a, "dt", a.dt + 1), 4),
+    "dt_overlaps_x": (lambda a: setattr(a, "dt", a.x + 64), 5),
+    "B_overlaps_C": (lambda a: setattr(a, "B", a.C + 2), 5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PROJ_CASES))
+def test_proj_rejects(lib, name):
+    a = proj_ok()
+    mutate, code = PROJ_CASES[name]
+    mutate(a)
+    assert lib.samba_proj(ctypes.byref(a), None) == code
+
+
+def test_proj_no_tokens_is_noop(lib):
+    a = proj_ok(tokens=0)
+    a.x = a.dt = a.B = a.C = None
+    assert lib.samba_proj(ctypes.byref(a), None) == 0
+    assert lib.samba_proj(None, None) == 1
