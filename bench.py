@@ -49,7 +49,7 @@ BWD_VALU_PER_TD = 16 * 15 + 20
 BWD_TRANS_PER_TD = 16 + 6
 BWD_SLOTS_PER_TD = BWD_VALU_PER_TD + TRANS_SLOTS * BWD_TRANS_PER_TD
 KERNEL_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_scan.hip"
-TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_fwd_L16384_D4096_bwd_B4_L4096_D4096.json"
+TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_fwd_step_bwd_proj.json"
 
 
 def prefill_bytes(tokens: int, dim: int, io_bytes: int = 2, h0: bool = True, h_last: bool = True, n: int = 16) -> int:
@@ -78,8 +78,8 @@ def kernel_hash() -> str:
 
 
 def read_traffic(part: str = "forward"):
-    """HBM bytes per launch (forward prefill kernel) or per call (backward) from the committed rocprofv3
-    counter runs, if they were taken on this kernel source."""
+    """HBM bytes per launch (forward, decode_step, projections) or per call (backward) from the committed
+    rocprofv3 counter runs, if they were taken on this kernel source."""
     try:
         t = json.loads(TRAFFIC_FILE.read_text())
     except Exception:
@@ -88,7 +88,7 @@ def read_traffic(part: str = "forward"):
         return None
     if part == "backward":
         return t.get("backward", {}).get("bytes_per_call")
-    return t.get("bytes_per_launch")
+    return t.get(part, {}).get("bytes_per_launch")
 
 
 def bench_prefill(steps: int, warmup: int, time_slices: int = 0):
@@ -361,15 +361,17 @@ def bench_decode(steps: int = 65536, ring: int = 256):
     return out
 
 
-def pmc_summary(fetch_dir: str, write_dir: str, out: str):
-    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; CSV output) of
-    `bench.py --steps 1 --warmup 0 --no-decode --no-cpu --bwd-steps 1 --copy-probe`
-    into the per-launch HBM byte summary bench.py reports as roofline.traffic
-    (prefill kernel) and backward.roofline.traffic (the three kernels of one
-    backward call).
+PMC_RUN = ("python3 <repo>/bench.py --steps 1 --warmup 0 --decode-steps 256 --no-cpu --bwd-steps 1 "
+           "--proj-steps 1 --copy-probe")
 
-    Each counter is scaled by what it reads for the plain 512 MiB copy of the
-    same run (expected 512 MiB fetched and 512 MiB written per dispatch)."""
+
+def pmc_summary(fetch_dir: str, write_dir: str, out: str):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; CSV output) of PMC_RUN into the per-launch HBM
+    byte summary bench.py reports as `traffic`: the prefill kernel, the decode step, the three kernels of
+    one backward call, and the projection GEMM.
+
+    Each counter is scaled by what it reads for the plain 512 MiB copy of the same run (expected 512 MiB
+    fetched and 512 MiB written per dispatch); values are the median over each kernel's dispatches."""
     import csv
     import glob
     import statistics
@@ -387,40 +389,43 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
         assert len(keys) == 1, (parts, keys)
         return keys[0]
 
-    sel = {"fwd": ("scan_fwd_kernel", ", false>"), "ckpt": ("scan_fwd_kernel", ", true>"),
-           "bwd": ("scan_bwd_kernel<",), "finish": ("scan_bwd_finish_kernel",)}
-    out_d = {"kernel_source_sha256_16": kernel_hash(), "unit": "bytes per launch"}
+    sel = {"fwd": ("scan_fwd_kernel", "16, 1, 8, false>"), "step": ("scan_step_kernel<unsigned short, unsigned short",),
+           "ckpt": ("scan_fwd_kernel", ", true>"), "bwd": ("scan_bwd_kernel<",), "finish": ("scan_bwd_finish_kernel",),
+           "proj": ("proj_kernel<unsigned short",)}
     got = {k: {} for k in sel}
+    scales = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = per_kernel(d, counter)
         copy = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs]
-        # the 512 MiB probe: the smallest of the large copies (a run may also hold small copies and, when the
-        # copy-ceiling measurement ran, 1 GiB copies)
+        # the 512 MiB probe: the smallest of the large copies (a run may also hold small copies)
         big = min(v for v in copy if v > 0.25 * max(copy))
         scale = (512 << 20) / 1024.0 / big
+        scales[counter] = {"copy_raw_kib_per_dispatch": big, "scale": scale}
         for name, parts in sel.items():
             key = pick(vals, *parts)
             kib = statistics.median(vals[key])
-            got[name][counter] = {"raw_kib_per_dispatch": kib, "scale": scale, "bytes_per_launch": kib * scale * 1024.0,
-                                  "kernel": key[:120]}
-        out_d[counter] = dict(got["fwd"][counter], copy_raw_kib_per_dispatch=big)
-        del out_d[counter]["kernel"]
-    out_d["kernel"] = got["fwd"]["FETCH_SIZE"]["kernel"]
-    out_d["bytes_per_launch"] = out_d["FETCH_SIZE"]["bytes_per_launch"] + out_d["WRITE_SIZE"]["bytes_per_launch"]
-    out_d["algorithmic_bytes_per_launch"] = prefill_bytes(16384, 4096)
-    bw = {name: {"kernel": got[name]["FETCH_SIZE"]["kernel"], "fetch": got[name]["FETCH_SIZE"]["bytes_per_launch"],
-                 "write": got[name]["WRITE_SIZE"]["bytes_per_launch"]} for name in ("ckpt", "bwd", "finish")}
-    out_d["backward"] = {"kernels": bw, "bytes_per_call": sum(v["fetch"] + v["write"] for v in bw.values()),
-                         "algorithmic_bytes_per_call": bwd_bytes(4 * 4096, 4096, 4)}
-    run = "python3 <repo>/bench.py --steps 1 --warmup 0 --no-decode --no-cpu --bwd-steps 1 --copy-probe"
+            got[name][counter] = {"kernel": key[:120], "raw_kib_per_dispatch": kib, "bytes": kib * scale * 1024.0}
+
+    def entry(name, algorithmic):
+        f, w = got[name]["FETCH_SIZE"]["bytes"], got[name]["WRITE_SIZE"]["bytes"]
+        return {"kernel": got[name]["FETCH_SIZE"]["kernel"], "fetch_bytes": f, "write_bytes": w,
+                "bytes_per_launch": f + w, "algorithmic_bytes_per_launch": algorithmic}
+
+    out_d = {"kernel_source_sha256_16": kernel_hash(), "unit": "bytes per launch", "calibration": scales,
+             "forward": entry("fwd", prefill_bytes(16384, 4096)),
+             "decode_step": entry("step", decode_bytes(64, 4096)),
+             "backward": {"kernels": {n: entry(n, None) for n in ("ckpt", "bwd", "finish")},
+                          "algorithmic_bytes_per_call": bwd_bytes(4 * 4096, 4096, 4)},
+             "projections": entry("proj", (16384 * 4096 + 4128 * 4096 + 16384 * 4128) * 2)}
+    out_d["backward"]["bytes_per_call"] = sum(v["bytes_per_launch"] for v in out_d["backward"]["kernels"].values())
     out_d["command"] = [
-        f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {run}",
-        f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {run}",
+        f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {PMC_RUN}",
+        f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {PMC_RUN}",
         f"python bench.py --pmc-summary {fetch_dir} {write_dir} {out}",
     ]
-    out_d["note"] = ("FETCH_SIZE and WRITE_SIZE are KiB per dispatch (median over the run's dispatches of each "
-                     "kernel); each is scaled by the ratio of the known size of the plain 512 MiB device copy in "
-                     "the same run to what the counter reports for it (FETCH_SIZE reads half, WRITE_SIZE exact).")
+    out_d["note"] = ("FETCH_SIZE and WRITE_SIZE are KiB per dispatch (median over each kernel's dispatches), each "
+                     "scaled by the ratio of the known size of the plain 512 MiB device copy in the same run to what "
+                     "the counter reports for it (FETCH_SIZE reads half, WRITE_SIZE exact).")
     Path(out).write_text(json.dumps(out_d, indent=1) + "\n")
     print(json.dumps(out_d))
 
@@ -559,6 +564,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--no-proj", action="store_true", help="skip the selection-projection leg")
+    ap.add_argument("--proj-steps", type=int, default=20)
     ap.add_argument("--time-slices", type=int, default=0, help="force the prefill's waves per time chunk (0 = auto)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (untimed), the reference kernel for HBM byte counters")
@@ -611,12 +617,13 @@ def main():
     if not args.no_decode:
         dec = bench_decode(args.decode_steps)
         dec["roofline"] = {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                           "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_step"),
                            "kernel": "scan_step_kernel<bf16,bf16>"}
         dec["copy_frac"] = dec["gbs"] / ceiling if ceiling else None
         line["decode"] = dec
     if not args.no_proj:
-        line["projections"] = bench_proj()
+        line["projections"] = bench_proj(args.proj_steps)
+        line["projections"]["roofline"]["traffic"] = read_traffic("projections")
     if not args.no_bwd:
         line["backward"] = bench_backward(args.bwd_steps)
         line["backward"]["roofline"]["traffic"] = read_traffic("backward")
