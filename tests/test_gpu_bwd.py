@@ -237,3 +237,30 @@ def test_forward_checkpoints_feed_the_backward(lengths):
             worst = max(worst, check_fp32(ckh[slot].reshape(1, -1), ref.reshape(1, -1),
                                           "checkpoint s=%d j=%d" % (s_, j)))
     say("forward checkpoints: worst state error %.2e" % worst)
+
+
+def test_bwd_chained_calls_equal_one_call():
+    """Two chained calls (h_last of the first is h0 of the second) differentiate like one call: the
+    second call's dh0 fed as the first call's dh_last gives the one-call gradients (to fp32 rounding)."""
+    L, cut, D = 600, 256, 48
+    say("case: bwd chained calls L%d cut %d D%d" % (L, cut, D))
+    inp = I.make_fwd_inputs_torch(2, L, D, DEV)
+    ex = I.make_bwd_extra_torch(2, L, D, 1, DEV)
+    h0 = torch.randn(1, D, 16, device=DEV)
+    keys = ("x", "dt", "z", "B", "C")
+    full = [inp[k].view(1, L, -1) for k in keys]
+    first = [inp[k][:cut].view(1, cut, -1) for k in keys]
+    second = [inp[k][cut:].view(1, L - cut, -1) for k in keys]
+    P = (inp["A"], inp["D"], inp["dt_bias"])
+    one = S.scan_bwd(*full, *P, ex["dy"].view(1, L, -1), h0=h0, dh_last=ex["dh_last"])
+    _, hmid = S.scan_fwd(*first, *P, h0=h0)
+    g2 = S.scan_bwd(*second, *P, ex["dy"][cut:].view(1, L - cut, -1), h0=hmid, dh_last=ex["dh_last"])
+    g1 = S.scan_bwd(*first, *P, ex["dy"][:cut].view(1, cut, -1), h0=h0, dh_last=g2["dh0"])
+    torch.cuda.synchronize()
+    for k in ("dx", "ddt", "dz", "dB", "dC"):
+        cat = torch.cat([g1[k], g2[k]], dim=1)
+        e = check_fp32(host(cat).reshape(L, -1), host(one[k]).reshape(L, -1), "chained " + k, trip=BWD_TRIP)
+        say("  %s %.2e" % (k, e))
+    for k in ("dA", "dD", "ddt_bias"):
+        check_fp32(host(g1[k] + g2[k]).reshape(1, -1), host(one[k]).reshape(1, -1), "chained " + k, trip=BWD_TRIP)
+    check_fp32(host(g1["dh0"]).reshape(1, -1), host(one["dh0"]).reshape(1, -1), "chained dh0", trip=BWD_TRIP)
