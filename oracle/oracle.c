@@ -1,5 +1,6 @@
 /*
- * oracle.c -- fp64 CPU reference of the selective state-space scan.
+ * oracle.c -- fp64 CPU reference of the selective state-space scan and of
+ * sliding-window attention.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file: only the test-suite, the smoke check and the CPU baseline
@@ -33,6 +34,10 @@
  *
  * The gradients of the prefill (oracle_scan_bwd) are the reverse-mode
  * derivative of exactly that loop; the formulas stand above the function.
+ *
+ * The other layer of the hybrid, sliding-window attention (oracle_swa), is
+ * the definition written out per query: rotate, score the visible keys,
+ * softmax, weight the values (its reading stands above the function).
  *
  * Everything is double precision with libm exp / log1p; build without
  * fast-math.  OpenMP runs over independent (sequence, channel) recurrences;
@@ -313,6 +318,78 @@ int oracle_proj(int64_t T, int64_t dim, int64_t dstate, const double* x, const d
   }
   (void)nthreads;
   return 0;
+}
+
+/*
+ * Sliding-window attention (page "SAMBA混合注意力状态空间模型", 数学框架 -> 滑动窗口注意力:
+ * softmax(Q K^T / sqrt(d_k) + M) V with the window mask M; the hackernoon page, §2.1.2: window w, RoPE
+ * relative positions inside the window).  Reading: causal, query i sees keys j with i - window <= j <= i
+ * of its own sequence; RoPE rotates the pairs (c, c + hd/2) of q and k by the token's position inside its
+ * sequence with the given tables (cos, sin [positions][hd/2]); NULL tables: no rotation.
+ *   q, k, v, o [T][H][hd]; sequences as in oracle_scan_fwd (seq_start [nseq+1]).
+ * Each (sequence, head, query) is one plain loop: rotate, score every visible key, softmax (maximum
+ * subtracted), weighted sum of v.  OpenMP spreads (head, query) pairs.
+ */
+static void rope_rotate(const double* x, double* out, int64_t hd, const double* cs, const double* sn) {
+  const int64_t half = hd / 2;
+  for (int64_t c = 0; c < half; ++c) {
+    out[c] = x[c] * cs[c] - x[c + half] * sn[c];
+    out[c + half] = x[c + half] * cs[c] + x[c] * sn[c];
+  }
+}
+
+int oracle_swa(int64_t nseq, const int64_t* seq_start, int64_t H, int64_t hd, int64_t window,
+               const double* q, const double* k, const double* v, const double* rope_cos, const double* rope_sin,
+               double* o, int nthreads) {
+  if (nseq < 0 || H < 1 || hd < 2 || (hd & 1) || window < 0 || !seq_start) return -1;
+  if ((rope_cos == NULL) != (rope_sin == NULL)) return -1;
+  for (int64_t s = 0; s < nseq; ++s)
+    if (seq_start[s + 1] < seq_start[s]) return -1;
+  const int64_t T = seq_start[nseq];
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic, 16) num_threads(nthreads) reduction(| : failed)
+#endif
+  for (int64_t h = 0; h < H; ++h) {
+    for (int64_t i = 0; i < T; ++i) {
+      int64_t s = 0;
+      while (seq_start[s + 1] <= i) ++s;
+      const int64_t t0 = seq_start[s];
+      const int64_t jlo = (i - window > t0) ? i - window : t0;
+      const int64_t nkeys = i - jlo + 1;
+      double* buf = (double*)malloc((size_t)(2 * hd + nkeys) * sizeof(double));
+      if (!buf) { failed = 1; continue; }
+      double* qr = buf;
+      double* kr = buf + hd;
+      double* sc = buf + 2 * hd;
+      const double* qi = q + (i * H + h) * hd;
+      if (rope_cos) rope_rotate(qi, qr, hd, rope_cos + (i - t0) * (hd / 2), rope_sin + (i - t0) * (hd / 2));
+      else for (int64_t c = 0; c < hd; ++c) qr[c] = qi[c];
+      double mx = -INFINITY;
+      for (int64_t j = jlo; j <= i; ++j) {
+        const double* kj = k + (j * H + h) * hd;
+        if (rope_cos) rope_rotate(kj, kr, hd, rope_cos + (j - t0) * (hd / 2), rope_sin + (j - t0) * (hd / 2));
+        else for (int64_t c = 0; c < hd; ++c) kr[c] = kj[c];
+        double dot = 0.0;
+        for (int64_t c = 0; c < hd; ++c) dot += qr[c] * kr[c];
+        sc[j - jlo] = dot / sqrt((double)hd);
+        if (sc[j - jlo] > mx) mx = sc[j - jlo];
+      }
+      double den = 0.0;
+      for (int64_t j = 0; j < nkeys; ++j) { sc[j] = exp(sc[j] - mx); den += sc[j]; }
+      double* oi = o + (i * H + h) * hd;
+      for (int64_t c = 0; c < hd; ++c) oi[c] = 0.0;
+      for (int64_t j = jlo; j <= i; ++j) {
+        const double w = sc[j - jlo] / den;
+        const double* vj = v + (j * H + h) * hd;
+        for (int64_t c = 0; c < hd; ++c) oi[c] += w * vj[c];
+      }
+      free(buf);
+    }
+  }
+  (void)nthreads;
+  return failed ? -1 : 0;
 }
 
 /* Number of OpenMP threads a call with nthreads <= 0 would use. */

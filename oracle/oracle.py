@@ -55,6 +55,8 @@ def _bind(lib):
     lib.oracle_scan_bwd.restype = ctypes.c_int
     lib.oracle_proj.argtypes = [I64, I64, I64, P, P, P, P, P, ctypes.c_int]
     lib.oracle_proj.restype = ctypes.c_int
+    lib.oracle_swa.argtypes = [I64, P, I64, I64, I64, P, P, P, P, P, P, ctypes.c_int]
+    lib.oracle_swa.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -171,6 +173,36 @@ def proj(x, W, dstate: int = 16, nthreads: int = 0, lib=None):
     if rc != 0:
         raise RuntimeError("oracle_proj failed (%d)" % rc)
     return dt, B, C
+
+
+def swa(q, k, v, window: int, rope_cos=None, rope_sin=None, seq_start=None, nthreads: int = 0, lib=None):
+    """Causal sliding-window attention in fp64.  q, k, v: [T][H][hd] (or [batch][L][H][hd]); rope tables
+    [positions][hd/2] or None.  Query i sees keys i-window .. i of its own sequence.  Returns o like q."""
+    lib = lib or load()
+    q = _f64(q)
+    shape = q.shape
+    if q.ndim == 4:
+        b, L, H, hd = shape
+        if seq_start is None:
+            seq_start = np.arange(b + 1, dtype=np.int64) * L
+        q = q.reshape(b * L, H, hd)
+        k, v = _f64(k).reshape(b * L, H, hd), _f64(v).reshape(b * L, H, hd)
+    else:
+        H, hd = shape[1], shape[2]
+        if seq_start is None:
+            seq_start = np.array([0, shape[0]], dtype=np.int64)
+        k, v = _f64(k), _f64(v)
+    T = q.shape[0]
+    seq_start = np.ascontiguousarray(np.asarray(seq_start, dtype=np.int64))
+    assert seq_start[0] == 0 and seq_start[-1] == T and k.shape == v.shape == q.shape
+    cs = None if rope_cos is None else _f64(rope_cos)
+    sn = None if rope_sin is None else _f64(rope_sin)
+    o = np.empty_like(q)
+    rc = lib.oracle_swa(len(seq_start) - 1, _ptr(seq_start), H, hd, int(window), _ptr(q), _ptr(k), _ptr(v), _ptr(cs),
+                        _ptr(sn), _ptr(o), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_swa failed (%d)" % rc)
+    return o.reshape(shape)
 
 
 def scan_step(state, x, dt, z, B, C, A, D, dt_bias, nthreads: int = 0, lib=None):
