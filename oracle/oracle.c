@@ -338,13 +338,61 @@ static void rope_rotate(const double* x, double* out, int64_t hd, const double* 
   }
 }
 
-int oracle_swa(int64_t nseq, const int64_t* seq_start, int64_t H, int64_t hd, int64_t window,
-               const double* q, const double* k, const double* v, const double* rope_cos, const double* rope_sin,
-               double* o, int nthreads) {
+/* One (head, query) of oracle_swa: the query is row i of the packed stream, t0 its sequence's first row. */
+static int swa_query(int64_t i, int64_t t0, int64_t h, int64_t H, int64_t hd, int64_t window, const double* q,
+                     const double* k, const double* v, const double* rope_cos, const double* rope_sin, double* o) {
+  const int64_t jlo = (i - window > t0) ? i - window : t0;
+  const int64_t nkeys = i - jlo + 1;
+  double* buf = (double*)malloc((size_t)(2 * hd + nkeys) * sizeof(double));
+  if (!buf) return -1;
+  double* qr = buf;
+  double* kr = buf + hd;
+  double* sc = buf + 2 * hd;
+  const double* qi = q + (i * H + h) * hd;
+  if (rope_cos) rope_rotate(qi, qr, hd, rope_cos + (i - t0) * (hd / 2), rope_sin + (i - t0) * (hd / 2));
+  else for (int64_t c = 0; c < hd; ++c) qr[c] = qi[c];
+  double mx = -INFINITY;
+  for (int64_t j = jlo; j <= i; ++j) {
+    const double* kj = k + (j * H + h) * hd;
+    if (rope_cos) rope_rotate(kj, kr, hd, rope_cos + (j - t0) * (hd / 2), rope_sin + (j - t0) * (hd / 2));
+    else for (int64_t c = 0; c < hd; ++c) kr[c] = kj[c];
+    double dot = 0.0;
+    for (int64_t c = 0; c < hd; ++c) dot += qr[c] * kr[c];
+    sc[j - jlo] = dot / sqrt((double)hd);
+    if (sc[j - jlo] > mx) mx = sc[j - jlo];
+  }
+  double den = 0.0;
+  for (int64_t j = 0; j < nkeys; ++j) { sc[j] = exp(sc[j] - mx); den += sc[j]; }
+  double* oi = o + (i * H + h) * hd;
+  for (int64_t c = 0; c < hd; ++c) oi[c] = 0.0;
+  for (int64_t j = jlo; j <= i; ++j) {
+    const double w = sc[j - jlo] / den;
+    const double* vj = v + (j * H + h) * hd;
+    for (int64_t c = 0; c < hd; ++c) oi[c] += w * vj[c];
+  }
+  free(buf);
+  return 0;
+}
+
+static int swa_check(int64_t nseq, const int64_t* seq_start, int64_t H, int64_t hd, int64_t window,
+                     const double* rope_cos, const double* rope_sin) {
   if (nseq < 0 || H < 1 || hd < 2 || (hd & 1) || window < 0 || !seq_start) return -1;
   if ((rope_cos == NULL) != (rope_sin == NULL)) return -1;
   for (int64_t s = 0; s < nseq; ++s)
     if (seq_start[s + 1] < seq_start[s]) return -1;
+  return 0;
+}
+
+static int64_t seq_of_row(const int64_t* seq_start, int64_t i) {
+  int64_t s = 0;
+  while (seq_start[s + 1] <= i) ++s;
+  return s;
+}
+
+int oracle_swa(int64_t nseq, const int64_t* seq_start, int64_t H, int64_t hd, int64_t window,
+               const double* q, const double* k, const double* v, const double* rope_cos, const double* rope_sin,
+               double* o, int nthreads) {
+  if (swa_check(nseq, seq_start, H, hd, window, rope_cos, rope_sin) != 0) return -1;
   const int64_t T = seq_start[nseq];
   int failed = 0;
 #ifdef _OPENMP
@@ -353,43 +401,49 @@ int oracle_swa(int64_t nseq, const int64_t* seq_start, int64_t H, int64_t hd, in
 #endif
   for (int64_t h = 0; h < H; ++h) {
     for (int64_t i = 0; i < T; ++i) {
-      int64_t s = 0;
-      while (seq_start[s + 1] <= i) ++s;
-      const int64_t t0 = seq_start[s];
-      const int64_t jlo = (i - window > t0) ? i - window : t0;
-      const int64_t nkeys = i - jlo + 1;
-      double* buf = (double*)malloc((size_t)(2 * hd + nkeys) * sizeof(double));
-      if (!buf) { failed = 1; continue; }
-      double* qr = buf;
-      double* kr = buf + hd;
-      double* sc = buf + 2 * hd;
-      const double* qi = q + (i * H + h) * hd;
-      if (rope_cos) rope_rotate(qi, qr, hd, rope_cos + (i - t0) * (hd / 2), rope_sin + (i - t0) * (hd / 2));
-      else for (int64_t c = 0; c < hd; ++c) qr[c] = qi[c];
-      double mx = -INFINITY;
-      for (int64_t j = jlo; j <= i; ++j) {
-        const double* kj = k + (j * H + h) * hd;
-        if (rope_cos) rope_rotate(kj, kr, hd, rope_cos + (j - t0) * (hd / 2), rope_sin + (j - t0) * (hd / 2));
-        else for (int64_t c = 0; c < hd; ++c) kr[c] = kj[c];
-        double dot = 0.0;
-        for (int64_t c = 0; c < hd; ++c) dot += qr[c] * kr[c];
-        sc[j - jlo] = dot / sqrt((double)hd);
-        if (sc[j - jlo] > mx) mx = sc[j - jlo];
-      }
-      double den = 0.0;
-      for (int64_t j = 0; j < nkeys; ++j) { sc[j] = exp(sc[j] - mx); den += sc[j]; }
-      double* oi = o + (i * H + h) * hd;
-      for (int64_t c = 0; c < hd; ++c) oi[c] = 0.0;
-      for (int64_t j = jlo; j <= i; ++j) {
-        const double w = sc[j - jlo] / den;
-        const double* vj = v + (j * H + h) * hd;
-        for (int64_t c = 0; c < hd; ++c) oi[c] += w * vj[c];
-      }
-      free(buf);
+      const int64_t t0 = seq_start[seq_of_row(seq_start, i)];
+      if (swa_query(i, t0, h, H, hd, window, q, k, v, rope_cos, rope_sin, o) != 0) failed = 1;
     }
   }
   (void)nthreads;
   return failed ? -1 : 0;
+}
+
+/* oracle_swa for the listed query rows only (all heads); other rows of o are left as they are. */
+int oracle_swa_rows(int64_t nseq, const int64_t* seq_start, int64_t H, int64_t hd, int64_t window,
+                    const double* q, const double* k, const double* v, const double* rope_cos,
+                    const double* rope_sin, const int64_t* rows, int64_t nrows, double* o, int nthreads) {
+  if (swa_check(nseq, seq_start, H, hd, window, rope_cos, rope_sin) != 0 || nrows < 0 || (nrows && !rows)) return -1;
+  const int64_t T = seq_start[nseq];
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= T) return -1;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+#endif
+  for (int64_t r = 0; r < nrows; ++r) {
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t i = rows[r];
+      const int64_t t0 = seq_start[seq_of_row(seq_start, i)];
+      if (swa_query(i, t0, h, H, hd, window, q, k, v, rope_cos, rope_sin, o) != 0) failed = 1;
+    }
+  }
+  (void)nthreads;
+  return failed ? -1 : 0;
+}
+
+/* RoPE alone: rotate x [T][H][hd] row t by position pos[t] of the tables (as inside oracle_swa). */
+int oracle_rope(int64_t T, int64_t H, int64_t hd, const double* x, const int64_t* pos, const double* rope_cos,
+                const double* rope_sin, double* out) {
+  if (T < 0 || H < 1 || hd < 2 || (hd & 1) || !pos || !rope_cos || !rope_sin) return -1;
+  for (int64_t t = 0; t < T; ++t) {
+    if (pos[t] < 0) return -1;
+    for (int64_t h = 0; h < H; ++h)
+      rope_rotate(x + (t * H + h) * hd, out + (t * H + h) * hd, hd, rope_cos + pos[t] * (hd / 2),
+                  rope_sin + pos[t] * (hd / 2));
+  }
+  return 0;
 }
 
 /* Number of OpenMP threads a call with nthreads <= 0 would use. */

@@ -57,6 +57,10 @@ def _bind(lib):
     lib.oracle_proj.restype = ctypes.c_int
     lib.oracle_swa.argtypes = [I64, P, I64, I64, I64, P, P, P, P, P, P, ctypes.c_int]
     lib.oracle_swa.restype = ctypes.c_int
+    lib.oracle_swa_rows.argtypes = [I64, P, I64, I64, I64, P, P, P, P, P, P, I64, P, ctypes.c_int]
+    lib.oracle_swa_rows.restype = ctypes.c_int
+    lib.oracle_rope.argtypes = [I64, I64, I64, P, P, P, P, P]
+    lib.oracle_rope.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -175,9 +179,11 @@ def proj(x, W, dstate: int = 16, nthreads: int = 0, lib=None):
     return dt, B, C
 
 
-def swa(q, k, v, window: int, rope_cos=None, rope_sin=None, seq_start=None, nthreads: int = 0, lib=None):
+def swa(q, k, v, window: int, rope_cos=None, rope_sin=None, seq_start=None, rows=None, nthreads: int = 0,
+        lib=None):
     """Causal sliding-window attention in fp64.  q, k, v: [T][H][hd] (or [batch][L][H][hd]); rope tables
-    [positions][hd/2] or None.  Query i sees keys i-window .. i of its own sequence.  Returns o like q."""
+    [positions][hd/2] or None.  Query i sees keys i-window .. i of its own sequence.  Returns o like q;
+    with `rows` (packed row indices) only those rows are computed and the others are NaN."""
     lib = lib or load()
     q = _f64(q)
     shape = q.shape
@@ -197,12 +203,34 @@ def swa(q, k, v, window: int, rope_cos=None, rope_sin=None, seq_start=None, nthr
     assert seq_start[0] == 0 and seq_start[-1] == T and k.shape == v.shape == q.shape
     cs = None if rope_cos is None else _f64(rope_cos)
     sn = None if rope_sin is None else _f64(rope_sin)
-    o = np.empty_like(q)
-    rc = lib.oracle_swa(len(seq_start) - 1, _ptr(seq_start), H, hd, int(window), _ptr(q), _ptr(k), _ptr(v), _ptr(cs),
-                        _ptr(sn), _ptr(o), int(nthreads))
+    if rows is None:
+        o = np.empty_like(q)
+        rc = lib.oracle_swa(len(seq_start) - 1, _ptr(seq_start), H, hd, int(window), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(cs), _ptr(sn), _ptr(o), int(nthreads))
+    else:
+        o = np.full_like(q, np.nan)
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        rc = lib.oracle_swa_rows(len(seq_start) - 1, _ptr(seq_start), H, hd, int(window), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(cs), _ptr(sn), _ptr(r), len(r), _ptr(o), int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_swa failed (%d)" % rc)
     return o.reshape(shape)
+
+
+def rope(x, rope_cos, rope_sin, positions, lib=None):
+    """RoPE alone in fp64: x [T][H][hd], row t rotated by table row positions[t]."""
+    lib = lib or load()
+    x = _f64(x)
+    T, H, hd = x.shape
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64))
+    assert pos.shape == (T,)
+    cs, sn = _f64(rope_cos), _f64(rope_sin)
+    assert pos.size == 0 or (pos.max() < cs.shape[0])
+    out = np.empty_like(x)
+    rc = lib.oracle_rope(T, H, hd, _ptr(x), _ptr(pos), _ptr(cs), _ptr(sn), _ptr(out))
+    if rc != 0:
+        raise RuntimeError("oracle_rope failed (%d)" % rc)
+    return out
 
 
 def scan_step(state, x, dt, z, B, C, A, D, dt_bias, nthreads: int = 0, lib=None):

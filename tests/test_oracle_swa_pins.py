@@ -13,7 +13,10 @@ inside the window).  Pins:
     picks the one highest-scoring visible key and ignores a higher one just outside the window;
   * RoPE depends on relative positions only: shifting every position by the same amount leaves the output
     unchanged, and keys rotated at the query's position instead of their own (a plausible slip) do not;
-  * packed sequences equal separate calls; heads are independent.
+  * packed sequences equal separate calls; heads are independent; a subset of query rows equals the same
+    rows of the full call;
+  * RoPE alone (oracle_rope, the rotation used inside oracle_swa) keeps each pair's norm, adds angles, is the
+    identity at angle 0 and turns (1, 0) into (0, 1) at a quarter turn.
 A mutation test plants mistakes in copies of the oracle and checks that the pins reject every one.
 """
 import math
@@ -155,6 +158,43 @@ def test_packed_equals_separate_and_heads_independent(oracle_lib):
     np.testing.assert_array_equal(op, o[:, perm])
 
 
+def test_rope_alone_is_a_rotation_by_position(oracle_lib):
+    # rotation is orthogonal pairwise (norms of (x[c], x[c+hd/2]) kept), angle-additive (table rows a, b, a+b),
+    # the identity at angle 0, and a quarter turn maps (1, 0) to (0, 1)
+    g = np.random.default_rng(11)
+    T, H, hd = 6, 2, 8
+    x = g.standard_normal((T, H, hd))
+    cos, sin = rope_tables(64, hd)
+    pos = np.array([0, 1, 5, 9, 30, 63])
+    r = O.rope(x, cos, sin, pos, lib=oracle_lib)
+    half = hd // 2
+    np.testing.assert_allclose(r[..., :half] ** 2 + r[..., half:] ** 2, x[..., :half] ** 2 + x[..., half:] ** 2,
+                               rtol=1e-12)
+    np.testing.assert_array_equal(r[0], x[0])
+    a, b = 9, 30
+    twice = O.rope(O.rope(x, cos, sin, np.full(T, a), lib=oracle_lib), cos, sin, np.full(T, b), lib=oracle_lib)
+    c2, s2 = rope_tables(a + b + 1, hd)
+    once = O.rope(x, c2, s2, np.full(T, a + b), lib=oracle_lib)
+    np.testing.assert_allclose(twice, once, rtol=1e-12, atol=1e-12)
+    quarter_c, quarter_s = np.zeros((1, 1)), np.ones((1, 1))
+    e = np.array([[[1.0, 0.0]]])
+    np.testing.assert_array_equal(O.rope(e, quarter_c, quarter_s, [0], lib=oracle_lib), [[[0.0, 1.0]]])
+
+
+def test_rows_subset_matches_full(oracle_lib):
+    g = np.random.default_rng(12)
+    lengths, H, hd, w = (9, 14), 2, 8, 5
+    T = sum(lengths)
+    q, k, v = (g.standard_normal((T, H, hd)) for _ in range(3))
+    cos, sin = rope_tables(max(lengths), hd)
+    st = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    full = O.swa(q, k, v, w, cos, sin, seq_start=st, lib=oracle_lib)
+    rows = [0, 8, 9, 15, 22]
+    part = O.swa(q, k, v, w, cos, sin, seq_start=st, rows=rows, lib=oracle_lib)
+    np.testing.assert_array_equal(part[rows], full[rows])
+    assert np.isnan(np.delete(part, rows, axis=0)).all()
+
+
 def test_rejects_bad_arguments(oracle_lib):
     q = np.zeros((4, 1, 3))
     with pytest.raises(RuntimeError):
@@ -189,7 +229,7 @@ SWA_MUTANTS = {
     "keys_at_query_position": ("rope_cos + (j - t0) * (hd / 2), rope_sin + (j - t0) * (hd / 2)",
                                "rope_cos + (i - t0) * (hd / 2), rope_sin + (i - t0) * (hd / 2)"),
     "no_max_subtracted": ("sc[j] = exp(sc[j] - mx);", "sc[j] = exp(sc[j]);"),
-    "sequences_leak": ("const int64_t t0 = seq_start[s];", "const int64_t t0 = 0;"),
+    "sequences_leak": ("  while (seq_start[s + 1] <= i) ++s;\n  return s;", "  while (seq_start[s + 1] <= i) ++s;\n  return 0;"),
     "unnormalised": ("const double w = sc[j - jlo] / den;", "const double w = sc[j - jlo];"),
     "value_of_query": ("const double* vj = v + (j * H + h) * hd;", "const double* vj = v + (i * H + h) * hd;"),
 }
