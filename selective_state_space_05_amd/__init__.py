@@ -1,8 +1,10 @@
-"""MI355X (gfx950) selective state-space scan: HIP kernels behind a C ABI.
+"""MI355X (gfx950) selective state-space scan and sliding-window attention:
+HIP kernels behind a C ABI.
 
-The library (libsamba_scan.so, built from csrc/samba_scan.hip) is loaded on
-first use by :mod:`selective_state_space_05_amd.scan`; importing this package
+The library (libsamba_scan.so, built from csrc/samba_scan.hip and
+csrc/samba_swa.hip) is loaded on first use by
+:mod:`selective_state_space_05_amd.scan` (and :mod:`.swa`); importing this package
 does not load it, so the seeded input recipe (:mod:`.inputs`) is usable on
 hosts without the built library.
 """
-__all__ = ["scan", "inputs"]
+__all__ = ["scan", "swa", "inputs"]

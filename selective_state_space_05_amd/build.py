@@ -1,4 +1,5 @@
-"""Builds libsamba_scan.so in-tree with hipcc for gfx950.
+"""Builds libsamba_scan.so in-tree with hipcc for gfx950 (the scan and the
+sliding-window attention kernels, one library).
 
 Usage:  python -m selective_state_space_05_amd.build   (always recompiles)
 """
@@ -11,8 +12,8 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SRC = PKG / "csrc" / "samba_scan.hip"
-HEADER = ROOT / "include" / "samba_scan.h"
+SRCS = (PKG / "csrc" / "samba_scan.hip", PKG / "csrc" / "samba_swa.hip")
+HEADERS = (ROOT / "include" / "samba_scan.h", ROOT / "include" / "samba_swa.h")
 LIB = PKG / "libsamba_scan.so"
 
 HIPCC_FLAGS = [
@@ -37,7 +38,7 @@ def hipcc() -> str:
 def build(out: Path = LIB, extra=()) -> Path:
     """Compile the HIP library (kernels + C ABI) into `out`."""
     tmp = out.with_suffix(".so.tmp%d" % os.getpid())
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", str(ROOT / "include"), "-o", str(tmp), str(SRC)]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", str(ROOT / "include"), "-o", str(tmp), *(str(p) for p in SRCS)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)

@@ -5,6 +5,11 @@ scan's arithmetic, so both the GPU tests/bench and the fp64 oracle can take
 their inputs from it without sharing any compute code.
 
 Recipe (every config; sizes differ):
+  * attention: q, k, v ~ N(0, 1) per (token, head, feature), rounded to bf16;
+    RoPE tables cos/sin of p * 10000^(-2c / head_dim) (the layer's fixed
+    parameter, computed in float64 and handed to both sides: fp64 to the
+    oracle, rounded to fp32 for the library); decode positions drawn
+    uniformly from a range the test names
   * x, z, dt_raw ~ N(0, 1) per (token, channel)
   * dt_bias[d] = log(expm1(U(1e-3, 1e-1)))  -> softplus(dt_bias) lies in [1e-3, 1e-1]
   * A[d, n] = -exp(U(0, ln 16))             -> A in [-16, -1], diagonal, negative real
@@ -34,7 +39,9 @@ import numpy as np
 
 SEED_ROOT = 20240611
 TENSOR_IDS = {"x": 0, "z": 1, "dt": 2, "dt_init": 3, "A": 4, "B": 5, "C": 6, "D": 7,
-              "lengths": 8, "h0": 9, "dy": 10, "dh_last": 11, "W_sel": 12}
+              "lengths": 8, "h0": 9, "dy": 10, "dh_last": 11, "W_sel": 12, "q": 13, "k": 14, "v": 15,
+              "pos": 16}
+ROPE_BASE = 10000.0
 DECODE_RING_BASE = 100
 DSTATE = 16
 
@@ -94,6 +101,12 @@ WORKLOADS = {
                 decode_steps=65536, decode_ring=256),
     # training shape: context 4096, batch 4 per device (page 1, 实现细节 -> 训练配置)
     5: Workload(5, "scan_bwd B4 L4096 D4096 N16 bf16", 4, 4096, 4096),
+    # sliding-window attention of Samba-3.8B (hidden 3072 = 24 heads x 128, window 2048: page 1,
+    # 实现细节 -> 模型配置) on the training shape, and its decode step over a full window
+    6: Workload(6, "swa_fwd B4 L4096 H24 hd128 w2048 bf16", 4, 4096, 3072,
+                extra={"heads": 24, "head_dim": 128, "window": 2048}),
+    7: Workload(7, "swa_decode B64 H24 hd128 w2048 cache 2049 bf16", 64, 1, 3072,
+                extra={"heads": 24, "head_dim": 128, "window": 2048, "cache_len": 2049, "pos": 4096}),
 }
 
 
@@ -266,3 +279,37 @@ def make_step_ring_torch(cfg_id: int, ring: int, batch: int, dim: int, device, d
                                        ("C", (ring, batch, dstate)))):
         out[name] = _torch_normal(torch, shape, cfg_id, DECODE_RING_BASE + k, device, torch.bfloat16)
     return out
+
+
+# --------------------------------------------------------------------------- #
+# sliding-window attention
+# --------------------------------------------------------------------------- #
+def rope_tables(npos: int, head_dim: int, base: float = ROPE_BASE):
+    """(cos, sin) float64 [npos][head_dim / 2] of the angles p * base^(-2c / head_dim): the layer's RoPE
+    parameter, an input to both the library and the oracle."""
+    ang = np.arange(npos, dtype=np.float64)[:, None] * base ** (-2.0 * np.arange(head_dim // 2)[None, :] / head_dim)
+    return np.cos(ang), np.sin(ang)
+
+
+def make_swa_inputs_np(cfg_id: int, rows: int, heads: int, head_dim: int, q_scale: float = 1.0) -> dict:
+    """q, k, v [rows][heads][head_dim] as bf16 bits, with their exact fp32 values under *_f32."""
+    out = {}
+    for name in ("q", "k", "v"):
+        v = _normal(cfg_id, name, (rows, heads, head_dim))
+        if name == "q" and q_scale != 1.0:
+            v = (v * np.float32(q_scale)).astype(np.float32)
+        bits = bf16_bits_from_f32(v)
+        out[name], out[name + "_f32"] = bits, f32_from_bf16_bits(bits)
+    return out
+
+
+def make_swa_inputs_torch(cfg_id: int, rows: int, heads: int, head_dim: int, device) -> dict:
+    """Device bf16 q, k, v [rows][heads][head_dim] ~ N(0, 1)."""
+    import torch
+    return {name: _torch_normal(torch, (rows, heads, head_dim), cfg_id, TENSOR_IDS[name], device, torch.bfloat16)
+            for name in ("q", "k", "v")}
+
+
+def make_positions_np(cfg_id: int, n: int, lo: int, hi: int) -> np.ndarray:
+    """n decode positions drawn uniformly from [lo, hi] (int32)."""
+    return _rng(cfg_id, TENSOR_IDS["pos"]).integers(lo, hi + 1, size=n).astype(np.int32)

@@ -12,19 +12,24 @@ from pathlib import Path
 import pytest
 
 from selective_state_space_05_amd import scan as S
+from selective_state_space_05_amd import swa as W
 
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "samba_scan.h"
+HEADERS = sorted((ROOT / "include").glob("*.h"))
 
 
 @pytest.fixture(scope="module")
 def lib():
-    return S.load_library()
+    return W.load_library()
 
 
 def header_functions():
-    txt = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"\b(samba_\w+)\s*\(", txt)))
+    names = set()
+    for h in HEADERS:
+        txt = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
+        names |= set(re.findall(r"\b(samba_\w+)\s*\(", txt))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(lib):
@@ -48,12 +53,14 @@ def test_status_strings(lib):
 
 
 STRUCTS = (("samba_scan_fwd_args", S.FwdArgs), ("samba_scan_step_args", S.StepArgs),
-           ("samba_scan_bwd_args", S.BwdArgs), ("samba_proj_args", S.ProjArgs))
+           ("samba_scan_bwd_args", S.BwdArgs), ("samba_proj_args", S.ProjArgs), ("samba_rope_args", W.RopeArgs),
+           ("samba_swa_fwd_args", W.SwaFwdArgs), ("samba_swa_decode_args", W.SwaDecodeArgs))
 
 
 def test_struct_layout_matches_header(tmp_path):
     """Compile a C probe against the header and compare sizeof/offsetof with the ctypes mirrors."""
-    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "samba_scan.h"', 'int main(void) {']
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "samba_scan.h"', '#include "samba_swa.h"',
+             'int main(void) {']
     for cname, py in STRUCTS:
         lines.append('printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
         for f, _ in py._fields_:
@@ -359,3 +366,141 @@ def test_proj_no_tokens_is_noop(lib):
     a.x = a.dt = a.B = a.C = None
     assert lib.samba_proj(ctypes.byref(a), None) == 0
     assert lib.samba_proj(None, None) == 1
+
+
+# --------------------------------------------------------------------------- #
+# sliding-window attention: validation
+# --------------------------------------------------------------------------- #
+GB = 1 << 30
+
+
+def rope_ok(batch=2, seqlen=100, heads=4, hd=128):
+    a = W.RopeArgs()
+    a.struct_size = ctypes.sizeof(W.RopeArgs)
+    a.batch, a.seqlen, a.heads, a.head_dim = batch, seqlen, heads, hd
+    a.cos, a.sin, a.npos = BASE, BASE + GB, 4096
+    a.q_in, a.k_in, a.q_out, a.k_out = BASE + 2 * GB, BASE + 3 * GB, BASE + 4 * GB, BASE + 5 * GB
+    return a
+
+
+ROPE_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 4), 7),
+    "neg_batch": (lambda a: setattr(a, "batch", -1), 2),
+    "zero_heads": (lambda a: setattr(a, "heads", 0), 2),
+    "head_dim_not_16": (lambda a: setattr(a, "head_dim", 72), 2),
+    "zero_npos": (lambda a: setattr(a, "npos", 0), 2),
+    "varlen_batch": (lambda a: (setattr(a, "cu_seqlens", BASE + 6 * GB), setattr(a, "nseq", 2)), 2),
+    "varlen_nseq0": (lambda a: (setattr(a, "batch", 1), setattr(a, "cu_seqlens", BASE + 6 * GB)), 2),
+    "null_cos": (lambda a: setattr(a, "cos", None), 1),
+    "q_in_without_out": (lambda a: setattr(a, "q_out", None), 1),
+    "k_out_without_in": (lambda a: setattr(a, "k_in", None), 1),
+    "misaligned_q": (lambda a: setattr(a, "q_in", a.q_in + 2), 4),
+    "misaligned_sin": (lambda a: setattr(a, "sin", a.sin + 4), 4),
+    "q_out_overlaps_k_in": (lambda a: setattr(a, "q_out", a.k_in + 256), 5),
+    "k_out_shifted_on_k_in": (lambda a: setattr(a, "k_out", a.k_in + 16), 5),
+    "q_out_overlaps_k_out": (lambda a: setattr(a, "q_out", a.k_out), 5),
+    "k_out_overlaps_cos": (lambda a: setattr(a, "k_out", a.cos), 5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROPE_CASES))
+def test_rope_rejects(lib, name):
+    a = rope_ok()
+    mutate, code = ROPE_CASES[name]
+    mutate(a)
+    assert lib.samba_rope(ctypes.byref(a), None) == code
+
+
+def test_rope_noops(lib):
+    a = rope_ok(seqlen=0)
+    a.q_in = a.k_in = a.q_out = a.k_out = None
+    assert lib.samba_rope(ctypes.byref(a), None) == 0
+    a = rope_ok()
+    a.q_in = a.k_in = a.q_out = a.k_out = None   # nothing to rotate
+    assert lib.samba_rope(ctypes.byref(a), None) == 0
+    assert lib.samba_rope(None, None) == 1
+
+
+def swa_ok(batch=2, seqlen=300, heads=4, hd=128, out_dtype=S.SAMBA_BF16):
+    a = W.SwaFwdArgs()
+    a.struct_size = ctypes.sizeof(W.SwaFwdArgs)
+    a.batch, a.seqlen, a.heads, a.head_dim = batch, seqlen, heads, hd
+    a.window, a.out_dtype = 64, out_dtype
+    a.q, a.k, a.v, a.o = BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB
+    return a
+
+
+SWA_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 4), 7),
+    "head_dim_64": (lambda a: setattr(a, "head_dim", 64), 6),
+    "neg_window": (lambda a: setattr(a, "window", -1), 2),
+    "zero_heads": (lambda a: setattr(a, "heads", 0), 2),
+    "too_many_heads": (lambda a: setattr(a, "heads", 5000), 2),
+    "neg_seqlen": (lambda a: setattr(a, "seqlen", -1), 2),
+    "out_dtype": (lambda a: setattr(a, "out_dtype", 5), 3),
+    "varlen_batch": (lambda a: (setattr(a, "cu_seqlens", BASE + 5 * GB), setattr(a, "nseq", 2)), 2),
+    "null_v": (lambda a: setattr(a, "v", None), 1),
+    "null_o": (lambda a: setattr(a, "o", None), 1),
+    "misaligned_k": (lambda a: setattr(a, "k", a.k + 8), 4),
+    "misaligned_o_f32": (lambda a: (setattr(a, "out_dtype", S.SAMBA_F32), setattr(a, "o", a.o + 2)), 4),
+    "o_overlaps_q": (lambda a: setattr(a, "o", a.q + 128), 5),
+    "o_overlaps_v": (lambda a: setattr(a, "o", a.v), 5),
+    "o_overlaps_cu": (lambda a: (setattr(a, "batch", 1), setattr(a, "cu_seqlens", a.o + 64), setattr(a, "nseq", 2)), 5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SWA_CASES))
+def test_swa_fwd_rejects(lib, name):
+    a = swa_ok()
+    mutate, code = SWA_CASES[name]
+    mutate(a)
+    assert lib.samba_swa_fwd(ctypes.byref(a), None) == code
+
+
+def test_swa_fwd_no_tokens_is_noop(lib):
+    a = swa_ok(seqlen=0)
+    a.q = a.k = a.v = a.o = None
+    assert lib.samba_swa_fwd(ctypes.byref(a), None) == 0
+    assert lib.samba_swa_fwd(None, None) == 1
+
+
+def dec_ok(batch=4, heads=4, hd=128, window=64, cache_len=65):
+    a = W.SwaDecodeArgs()
+    a.struct_size = ctypes.sizeof(W.SwaDecodeArgs)
+    a.batch, a.heads, a.head_dim, a.window, a.cache_len = batch, heads, hd, window, cache_len
+    a.out_dtype = S.SAMBA_BF16
+    a.pos, a.q, a.k, a.v = BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB
+    a.k_cache, a.v_cache, a.o = BASE + 4 * GB, BASE + 5 * GB, BASE + 6 * GB
+    return a
+
+
+DEC_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 4), 7),
+    "head_dim_64": (lambda a: setattr(a, "head_dim", 64), 6),
+    "cache_shorter_than_window": (lambda a: setattr(a, "cache_len", 64), 2),
+    "neg_window": (lambda a: setattr(a, "window", -1), 2),
+    "zero_heads": (lambda a: setattr(a, "heads", 0), 2),
+    "out_dtype": (lambda a: setattr(a, "out_dtype", 3), 3),
+    "null_pos": (lambda a: setattr(a, "pos", None), 1),
+    "null_k_cache": (lambda a: setattr(a, "k_cache", None), 1),
+    "misaligned_v_cache": (lambda a: setattr(a, "v_cache", a.v_cache + 8), 4),
+    "misaligned_pos": (lambda a: setattr(a, "pos", a.pos + 2), 4),
+    "o_overlaps_q": (lambda a: setattr(a, "o", a.q), 5),
+    "k_cache_overlaps_v_cache": (lambda a: setattr(a, "k_cache", a.v_cache + 256), 5),
+    "v_cache_overlaps_v": (lambda a: setattr(a, "v_cache", a.v - 256), 5),
+    "o_overlaps_pos": (lambda a: setattr(a, "o", a.pos), 5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEC_CASES))
+def test_swa_decode_rejects(lib, name):
+    a = dec_ok()
+    mutate, code = DEC_CASES[name]
+    mutate(a)
+    assert lib.samba_swa_decode(ctypes.byref(a), None) == code
+
+
+def test_swa_decode_empty_batch_is_noop(lib):
+    a = dec_ok(batch=0)
+    a.pos = a.q = a.k = a.v = a.k_cache = a.v_cache = a.o = None
+    assert lib.samba_swa_decode(ctypes.byref(a), None) == 0
