@@ -50,6 +50,25 @@ BWD_TRANS_PER_TD = 16 + 6
 BWD_SLOTS_PER_TD = BWD_VALU_PER_TD + TRANS_SLOTS * BWD_TRANS_PER_TD
 KERNEL_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_scan.hip"
 TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_fwd_step_bwd_proj.json"
+SWA_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_swa.hip"
+SWA_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_swa.json"
+
+
+def visible_keys(L: int, window: int) -> int:
+    """Sum over the queries of one L-token sequence of the keys each sees (min(i + 1, window + 1))."""
+    m = min(L, window + 1)
+    return m * (m + 1) // 2 + (L - m) * (window + 1)
+
+
+def swa_flops(batch: int, L: int, heads: int, hd: int, window: int) -> int:
+    """Algorithmic flops of the attention: per visible (query, key) pair a q.k dot and a p*v axpy of hd each."""
+    return 4 * hd * heads * batch * visible_keys(L, window)
+
+
+def swa_decode_bytes(batch: int, heads: int, hd: int, window: int) -> int:
+    """Bytes one decode step must move: the window's cached keys and values (window rows each), the new q, k,
+    v rows in, k and v written to the cache, o out (bf16)."""
+    return batch * heads * hd * 2 * (2 * window + 3 + 2 + 1)
 
 
 def prefill_bytes(tokens: int, dim: int, io_bytes: int = 2, h0: bool = True, h_last: bool = True, n: int = 16) -> int:
@@ -75,6 +94,22 @@ def decode_bytes(batch: int, dim: int, n: int = 16) -> int:
 
 def kernel_hash() -> str:
     return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+
+
+def swa_hash() -> str:
+    return hashlib.sha256(SWA_SRC.read_bytes()).hexdigest()[:16]
+
+
+def read_swa_traffic(part: str):
+    """HBM bytes per launch of the attention kernels (prefill, decode) from the committed counter runs, if
+    they were taken on this kernel source."""
+    try:
+        t = json.loads(SWA_TRAFFIC_FILE.read_text())
+    except Exception:
+        return None
+    if t.get("kernel_source_sha256_16") != swa_hash():
+        return None
+    return t.get(part, {}).get("bytes_per_launch")
 
 
 def read_traffic(part: str = "forward"):
@@ -361,6 +396,173 @@ def bench_decode(steps: int = 65536, ring: int = 256):
     return out
 
 
+def _timed(fn, steps: int, stream):
+    """Average ms of `steps` calls of fn() between two events on `stream`."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_swa(steps: int = 20, warmup: int = 5):
+    """The sliding-window attention layer of Samba-3.8B on the training shape: batch 4 x 4096 tokens, 24 heads
+    of 128, window 2048, bf16 q/k/v/o.  One layer pass = RoPE of q and k, then the attention."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import swa as W
+
+    wl = I.WORKLOADS[6]
+    B, L, H, hd, w = wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.extra["window"]
+    dev = torch.device("cuda:0")
+    t = I.make_swa_inputs_torch(6, B * L, H, hd, dev)
+    q, k, v = (t[n].view(B, L, H, hd) for n in ("q", "k", "v"))
+    c, s_ = I.rope_tables(L, hd)
+    ct = torch.from_numpy(c.astype("float32")).to(dev)
+    st = torch.from_numpy(s_.astype("float32")).to(dev)
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
+    o = torch.empty_like(q)
+    ra = W.rope_args(q, k, ct, st, q_out=qr, k_out=kr)
+    fa = W.fwd_args(qr, kr, v, w, o=o)
+    lib = W.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    rr, fr = ctypes.byref(ra), ctypes.byref(fa)
+
+    def rope():
+        if lib.samba_rope(rr, sh) != 0:
+            raise RuntimeError("samba_rope failed")
+
+    def att():
+        if lib.samba_swa_fwd(fr, sh) != 0:
+            raise RuntimeError("samba_swa_fwd failed")
+
+    def layer():
+        rope()
+        att()
+
+    for _ in range(warmup):
+        layer()
+    torch.cuda.synchronize()
+    ms_layer = _timed(layer, steps, stream)
+    ms_att = _timed(att, steps, stream)
+    ms_rope = _timed(rope, steps, stream)
+    flops = swa_flops(B, L, H, hd, w)
+    tf = flops / (ms_att * 1e-3) / 1e12
+    return {"workload": "sliding-window attention B=%d L=%d heads=%d head_dim=%d window=%d bf16, RoPE + "
+                        "attention (Samba-3.8B layer, training shape)" % (B, L, H, hd, w),
+            "steps": steps, "ms_per_layer": ms_layer, "tokens_per_s": B * L / (ms_layer * 1e-3),
+            "attention_ms": ms_att, "rope_ms": ms_rope, "tflops": tf,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": read_swa_traffic("prefill"),
+                         "kernel": "swa_fwd_kernel<bf16> (v_mfma_f32_32x32x16_bf16)", "flops_per_launch": flops,
+                         "launch_us": round(ms_att * 1e3, 2),
+                         "algorithmic_bytes_per_launch": 4 * B * L * H * hd * 2}}
+
+
+def bench_swa_decode(steps: int = 200, warmup: int = 20):
+    """One decode step of the attention layer for 64 sequences at position 4096 (a full 2048-token window in
+    a 2049-slot ring cache): RoPE of the new q and k, then the attention over the cache."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import swa as W
+
+    wl = I.WORKLOADS[7]
+    B, H, hd, w, cl, P = (wl.batch, wl.extra["heads"], wl.extra["head_dim"], wl.extra["window"],
+                          wl.extra["cache_len"], wl.extra["pos"])
+    dev = torch.device("cuda:0")
+    t = I.make_swa_inputs_torch(7, B * (cl + 1), H, hd, dev)
+    kc = t["k"][:B * cl].view(B, cl, H, hd).permute(0, 2, 1, 3).contiguous()
+    vc = t["v"][:B * cl].view(B, cl, H, hd).permute(0, 2, 1, 3).contiguous()
+    q, k, v = (t[n][B * cl:].view(B, 1, H, hd) for n in ("q", "k", "v"))
+    del t
+    c, s_ = I.rope_tables(P + 1, hd)
+    ct = torch.from_numpy(c.astype("float32")).to(dev)
+    st = torch.from_numpy(s_.astype("float32")).to(dev)
+    pos = torch.full((B,), P, dtype=torch.int32, device=dev)
+    qr, kr = torch.empty_like(q), torch.empty_like(k)
+    o = torch.empty(B, H, hd, dtype=torch.bfloat16, device=dev)
+    ra = W.rope_args(q, k, ct, st, q_out=qr, k_out=kr, pos0=pos)
+    da = W.decode_args(qr.view(B, H, hd), kr.view(B, H, hd), v.view(B, H, hd), kc, vc, pos, w, o=o)
+    lib = W.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    rr, dr = ctypes.byref(ra), ctypes.byref(da)
+
+    def att():
+        if lib.samba_swa_decode(dr, sh) != 0:
+            raise RuntimeError("samba_swa_decode failed")
+
+    def step():
+        if lib.samba_rope(rr, sh) != 0:
+            raise RuntimeError("samba_rope failed")
+        att()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = _timed(step, steps, stream)
+    ms_att = _timed(att, steps, stream)
+    nbytes = swa_decode_bytes(B, H, hd, w)
+    gbs = nbytes / (ms_att * 1e-3) / 1e9
+    return {"workload": "attention decode step: batch %d, heads %d x %d, window %d, ring cache of %d slots, "
+                        "position %d, bf16" % (B, H, hd, w, cl, P),
+            "steps": steps, "us_per_step": ms_step * 1e3, "steps_per_s": 1e3 / ms_step,
+            "attention_us": ms_att * 1e3, "gbs": gbs,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_swa_traffic("decode"),
+                         "kernel": "swa_decode_kernel<bf16>", "launch_us": round(ms_att * 1e3, 2),
+                         "algorithmic_bytes_per_launch": nbytes}}
+
+
+def cpu_baseline_swa(rows: int = 256):
+    """The fp64 oracle's attention for `rows` query rows of one 4096-token sequence (all 24 heads, full
+    2048-token windows), in TFLOP/s of the same algorithmic count."""
+    import numpy as np
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+
+    wl = I.WORKLOADS[6]
+    L, H, hd, w = wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.extra["window"]
+    inp = I.make_swa_inputs_np(6, L, H, hd)
+    c, s_ = I.rope_tables(L, hd)
+    sel = np.linspace(w, L - 1, rows).astype(np.int64)
+    lib = O.load()
+    t0 = time.perf_counter()
+    O.swa(inp["q_f32"], inp["k_f32"], inp["v_f32"], w, c, s_, rows=sel, lib=lib)
+    spent = time.perf_counter() - t0
+    flops = 4.0 * hd * H * rows * (w + 1)
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": O.max_threads(lib), "kind": "oracle",
+            "sample": "%d query rows (full windows) of one 4096-token sequence, 24 heads, fp64 oracle with "
+                      "RoPE, %.1f s" % (rows, spent)}
+
+
+def cpu_baseline_swa_decode(seqs: int = 16):
+    """The fp64 oracle's decode output (last row of a full window) for `seqs` of the 64 sequences,
+    extrapolated to steps/s of the whole batch."""
+    import numpy as np
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+
+    wl = I.WORKLOADS[7]
+    B, H, hd, w, P = wl.batch, wl.extra["heads"], wl.extra["head_dim"], wl.extra["window"], wl.extra["pos"]
+    c, s_ = I.rope_tables(P + 1, hd)
+    lib = O.load()
+    spent = 0.0
+    for b in range(seqs):
+        inp = I.make_swa_inputs_np(700 + b, w + 1, H, hd)
+        t0 = time.perf_counter()
+        O.swa(inp["q_f32"], inp["k_f32"], inp["v_f32"], w, c[P - w:], s_[P - w:], rows=[w], lib=lib)
+        spent += time.perf_counter() - t0
+    per_step = spent / seqs * B
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": O.max_threads(lib), "kind": "oracle",
+            "sample": "%d of the 64 sequences' last rows (2049-token windows, 24 heads, fp64 oracle with RoPE), "
+                      "extrapolated to the batch; %.2f s" % (seqs, spent)}
+
+
 PMC_RUN = ("python3 <repo>/bench.py --steps 1 --warmup 0 --decode-steps 256 --no-cpu --bwd-steps 1 "
            "--proj-steps 1 --copy-probe")
 
@@ -565,6 +767,11 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--no-proj", action="store_true", help="skip the selection-projection leg")
     ap.add_argument("--proj-steps", type=int, default=20)
+    ap.add_argument("--no-swa", action="store_true", help="skip the sliding-window attention legs")
+    ap.add_argument("--swa-steps", type=int, default=20)
+    ap.add_argument("--swa-decode-steps", type=int, default=200)
+    ap.add_argument("--swa-only", action="store_true",
+                    help="run only the attention legs (and the copy probe with --copy-probe): counter runs")
     ap.add_argument("--time-slices", type=int, default=0, help="force the prefill's waves per time chunk (0 = auto)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (untimed), the reference kernel for HBM byte counters")
@@ -578,6 +785,14 @@ def main():
         print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.swa_only:
+        out = {"attention": bench_swa(args.swa_steps, min(args.warmup, 5)),
+               "attention_decode": bench_swa_decode(args.swa_decode_steps, min(args.warmup, 20))}
+        if args.copy_probe:
+            copy_probe()
+        print(json.dumps(out), flush=True)
+        return
 
     pf = bench_prefill(args.steps, args.warmup, args.time_slices)
     # (counter runs skip the ceiling measurement: its 1 GiB copies are not needed there)
@@ -627,6 +842,10 @@ def main():
     if not args.no_bwd:
         line["backward"] = bench_backward(args.bwd_steps)
         line["backward"]["roofline"]["traffic"] = read_traffic("backward")
+    if not args.no_swa:
+        line["attention"] = bench_swa(args.swa_steps)
+        line["attention_decode"] = bench_swa_decode(args.swa_decode_steps)
+        line["attention_decode"]["copy_frac"] = line["attention_decode"]["gbs"] / ceiling if ceiling else None
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
         if not args.no_decode:
@@ -635,6 +854,9 @@ def main():
             line["cpu_baseline"]["backward"] = cpu_baseline_backward()
         if not args.no_proj:
             line["cpu_baseline"]["projections"] = cpu_baseline_proj()
+        if not args.no_swa:
+            line["cpu_baseline"]["attention"] = cpu_baseline_swa()
+            line["cpu_baseline"]["attention_decode"] = cpu_baseline_swa_decode()
     print(json.dumps(line), flush=True)
 
 

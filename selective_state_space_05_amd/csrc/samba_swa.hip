@@ -40,6 +40,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "samba_swa.h"
 
 namespace {
@@ -55,7 +57,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kHD = 128;                // head size served by the attention kernels
 constexpr int kQB = 128;                // queries per prefill workgroup
 constexpr int kKB = 64;                 // keys per prefill tile
-constexpr int kRopeTok = 64;            // tokens per RoPE workgroup
+constexpr float kRescale = 8.0f;        // exp2 units a score may exceed the softmax reference by
+constexpr int kRopeShift = 3;           // 8 tokens per RoPE workgroup (thousands of workgroups in flight)
+constexpr int kRopeTok = 1 << kRopeShift;
 
 // Resource over `rows` rows of row_bytes; rows <= 0 gives an empty resource (loads return 0, stores are
 // dropped), byte counts beyond 32 bits saturate.
@@ -161,16 +165,17 @@ __device__ __forceinline__ void rope_rows(const uint16_t* in, uint16_t* out, int
   *reinterpret_cast<uint4*>(out + off + half) = make_uint4(rb[0], rb[1], rb[2], rb[3]);
 }
 
-// One workgroup per 64 tokens of one sequence; a work item is (token, head, 8 rotation pairs).
+// One workgroup per 8 tokens of one sequence; a work item is (token, head, 8 rotation pairs).
 __global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
-  const SeqBlock sb = locate(p.cu, p.nseq, p.total, p.seqlen, p.per_seq, blockIdx.x, 6);
+  const SeqBlock sb = locate(p.cu, p.nseq, p.total, p.seqlen, p.per_seq, blockIdx.x, kRopeShift);
   if (sb.j < 0 || sb.j * kRopeTok >= sb.len) return;
   const int first = sb.j * kRopeTok;
   const int ntok = (sb.len - first) < kRopeTok ? sb.len - first : kRopeTok;
   const int half = p.hd >> 1, cph = half >> 3, per_tok = p.heads * cph;
   int32_t base_pos = first;
   if (p.pos0) {
-    const int s = p.cu ? seq_of_block(p.cu, p.nseq, blockIdx.x, 6, p.total) : static_cast<int>(blockIdx.x) / p.per_seq;
+    const int s = p.cu ? seq_of_block(p.cu, p.nseq, blockIdx.x, kRopeShift, p.total)
+                       : static_cast<int>(blockIdx.x) / p.per_seq;
     base_pos += p.pos0[s];
   }
   for (int it = threadIdx.x; it < ntok * per_tok; it += blockDim.x) {
@@ -212,7 +217,7 @@ __device__ __forceinline__ int key_slot(int k) { return (k & ~12) | ((k & 4) << 
 
 template <typename Tout>
 __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKB * kHD];   // [key][hd], group g at g ^ (key & 7)
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKB * kHD];   // [key][hd], group g at g ^ (key & 15)
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kHD * kKB];   // [hd][slot], group g at g ^ vswz(hd)
   const int logical = xcd_remap(blockIdx.x, p.nqb * p.heads);
   const int head = logical / p.nqb;
@@ -235,6 +240,7 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
   const bool wave_live = q_lo < len;
   const int q_hi = wave_live ? ((len - q_lo) < 32 ? len - 1 : q_lo + 31) : q_lo;
   const int qp = q_lo + ql;   // this lane's query
+  // q fragments, multiplied by log2(e) / sqrt(head size) and rounded to bf16: scores come out in exp2 units
   bf16x8_t qf[8];
   {
     const rsrc_t rq = rsrc_rows(p.q + (sb.t0 + q_lo) * p.heads * kHD + head_off, wave_live ? q_hi - q_lo + 1 : 0,
@@ -242,7 +248,12 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const uint4 w = ld16(rq, static_cast<uint32_t>(ql) * row_bytes + (16 * jj + 8 * hf) * 2);
-      qf[jj] = __builtin_bit_cast(bf16x8_t, w);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qf[jj][2 * i] = static_cast<__bf16>(bf_lo(ws[i]) * p.c);
+        qf[jj][2 * i + 1] = static_cast<__bf16>(bf_hi(ws[i]) * p.c);
+      }
     }
   }
 
@@ -260,25 +271,24 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
     for (int i = 0; i < 4; ++i) vr[i] = ld16(rv, static_cast<uint32_t>(4 * sr + i) * row_bytes + sg * 16);
   };
   const int vslot = key_slot(4 * sr);
-  auto lstore = [&](int buf) {
+  auto lstore = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = sr + 16 * r;
-      *reinterpret_cast<uint4*>(&sK[buf][row * kHD + ((sg ^ (row & 7)) << 3)]) = kr[r];
+      *reinterpret_cast<uint4*>(&sK[buf][row * kHD + ((sg ^ (row & 15)) << 3)]) = kr[r];
     }
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const int row = 8 * sg + d;
       const int w = d >> 1;
       const uint32_t a0 = (&vr[0].x)[w], a1 = (&vr[1].x)[w], a2 = (&vr[2].x)[w], a3 = (&vr[3].x)[w];
+      // bf16 number d of keys 4 sr + 0..3, packed in key order (byte select: low or high halves)
+      constexpr uint32_t kLoHalves = 0x05040100u, kHiHalves = 0x07060302u;
+      const uint32_t sel = (d & 1) ? kHiHalves : kLoHalves;
       uint2 pk;
-      if (d & 1) {
-        pk.x = (a0 >> 16) | (a1 & 0xffff0000u);
-        pk.y = (a2 >> 16) | (a3 & 0xffff0000u);
-      } else {
-        pk.x = (a0 & 0xffffu) | (a1 << 16);
-        pk.y = (a2 & 0xffffu) | (a3 << 16);
-      }
+      pk.x = __builtin_amdgcn_perm(a1, a0, sel);
+      pk.y = __builtin_amdgcn_perm(a3, a2, sel);
       *reinterpret_cast<uint2*>(&sV[buf][row * kKB + (((vslot >> 3) ^ vswz(row)) << 3) + (vslot & 7)]) = pk;
     }
   };
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
   // fragment offsets (elements) of this lane
   int koff[8], voff[2][4];
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) koff[jj] = ql * kHD + (((2 * jj + hf) ^ (ql & 7)) << 3);
+  for (int jj = 0; jj < 8; ++jj) koff[jj] = ql * kHD + (((2 * jj + hf) ^ (ql & 15)) << 3);
 #pragma unroll
   for (int par = 0; par < 2; ++par)
 #pragma unroll
@@ -297,15 +307,21 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
   for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[hb][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c = p.c;
+  // Softmax reference per lane (exp2 units): the scores of a tile are formed relative to it (the MFMA
+  // accumulators start at -m_ref), and it is moved only when a score exceeds it by more than kRescale (or
+  // before the lane has seen any key), so the rescaling of the output is rare.  Any reference gives the same
+  // result once the output is divided by the sum; keeping the maximum within 2^kRescale of it bounds the
+  // probabilities by 2^kRescale and keeps the largest one >= 1.
+  float m_ref = -INFINITY, l_run = 0.f;
+  f32x16_t cneg;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) cneg[e] = 0.f;
 
-  auto compute = [&](int buf, int kt, bool need_mask) {
+  auto compute = [&](auto bufc, int kt, bool need_mask) {
+    constexpr int buf = decltype(bufc)::value;
     const uint16_t* K = sK[buf];
     const uint16_t* Vt = sV[buf];
-    f32x16_t s0, s1;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) { s0[e] = 0.f; s1[e] = 0.f; }
+    f32x16_t s0 = cneg, s1 = cneg;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(K + koff[jj]);
@@ -313,41 +329,66 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[jj], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[jj], s1, 0, 0, 0);
     }
-    if (need_mask) {
-      const int kb = kt * kKB + 4 * hf;
+    if (need_mask) {   // visible iff 0 <= query - key <= window
+      // (the tile's first key through readfirstlane: an opaque value, so that the compiler does not keep 32
+      // per-element induction variables alive across the loop for this rarely taken branch)
+      const int dq = qp - __builtin_amdgcn_readfirstlane(kt * kKB) - 4 * hf;
+      const uint32_t w = static_cast<uint32_t>(p.window);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int k0 = kb + 8 * (e >> 2) + (e & 3), k1 = k0 + 32;
-        s0[e] = (k0 <= qp && k0 >= qp - p.window) ? s0[e] : -INFINITY;
-        s1[e] = (k1 <= qp && k1 >= qp - p.window) ? s1[e] : -INFINITY;
+        const int off = 8 * (e >> 2) + (e & 3);
+        s0[e] = static_cast<uint32_t>(dq - off) <= w ? s0[e] : -INFINITY;
+        s1[e] = static_cast<uint32_t>(dq - off - 32) <= w ? s1[e] : -INFINITY;
       }
     }
-    float mx = fmaxf(s0[0], s1[0]);
+    // largest score above the reference, as the integer maximum of the bit patterns: exact whenever some
+    // score is positive, and <= 0 as a float otherwise (all that the test below needs)
+    int im = __float_as_int(s0[0]);
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    for (int e = 1; e < 16; ++e) im = max(im, __float_as_int(s0[e]));
+#pragma unroll
+    for (int e = 0; e < 16; ++e) im = max(im, __float_as_int(s1[e]));
     {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const auto sw = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(im), static_cast<uint32_t>(im), false,
+                                                       false);
+      im = max(static_cast<int>(sw[0]), static_cast<int>(sw[1]));
     }
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float mc = m_use * c;
-    const float alpha = __builtin_amdgcn_exp2f(m_run * c - mc);
-    float rs = 0.f;
+    const bool move = (m_ref == -INFINITY) || (__int_as_float(im) > kRescale);
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      // exact online-softmax step for the whole wave: new reference = running maximum
+      float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      s0[e] = __builtin_amdgcn_exp2f(fmaf(s0[e], c, -mc));
-      s1[e] = __builtin_amdgcn_exp2f(fmaf(s1[e], c, -mc));
-      rs += s0[e] + s1[e];
-    }
-    l_run = fmaf(l_run, alpha, rs);
-    m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float ref = (m_ref == -INFINITY) ? 0.f : m_ref;   // what the scores are relative to
+      const float m_new = fmaxf(m_ref, mx + ref);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_use);   // 0 before the first key
+      const float delta = ref - m_use;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s0[e] += delta;
+        s1[e] += delta;
+        cneg[e] = -m_use;
+      }
+      l_run *= alpha;
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[hb][e] *= alpha;
+      m_ref = m_new;
     }
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      s0[e] = __builtin_amdgcn_exp2f(s0[e]);
+      s1[e] = __builtin_amdgcn_exp2f(s1[e]);
+      rs += s0[e] + s1[e];
+    }
+    l_run += rs;
     bf16x8_t pf[4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -365,18 +406,24 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
       }
   };
 
-  gload(kt_lo);
-  lstore(0);
-  __syncthreads();
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const int buf = (kt - kt_lo) & 1;
+  // one tile: prefetch the next into registers, compute from LDS buffer `buf`, stage the next into the other
+  // buffer.  Two tiles per loop trip so that the buffer (and every LDS address) is a compile-time constant.
+  auto tile = [&](auto bufc, int kt) {
+    constexpr int buf = decltype(bufc)::value;
     const bool more = kt < kt_hi;
     if (more) gload(kt + 1);
     const int k_first = kt * kKB, k_last = k_first + kKB - 1;
     if (wave_live && k_first <= q_hi && k_last >= q_lo - p.window)
-      compute(buf, kt, k_last > q_lo || k_first < q_hi - p.window);
-    if (more) lstore(buf ^ 1);
+      compute(bufc, kt, k_last > q_lo || k_first < q_hi - p.window);
+    if (more) lstore(std::integral_constant<int, buf ^ 1>{});
     __syncthreads();
+  };
+  gload(kt_lo);
+  lstore(std::integral_constant<int, 0>{});
+  __syncthreads();
+  for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+    tile(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 <= kt_hi) tile(std::integral_constant<int, 1>{}, kt + 1);
   }
 
   if (!wave_live) return;
@@ -601,7 +648,7 @@ samba_status samba_rope(const samba_rope_args* a, void* stream) {
   if (a->struct_size != sizeof(samba_rope_args)) return SAMBA_ERR_BAD_STRUCT;
   RopeParams p{};
   int64_t nblk = 0;
-  samba_status st = token_shape(a->batch, a->seqlen, a->cu_seqlens, a->nseq, &nblk, 6, &p.per_seq);
+  samba_status st = token_shape(a->batch, a->seqlen, a->cu_seqlens, a->nseq, &nblk, kRopeShift, &p.per_seq);
   if (st != SAMBA_OK) return st;
   if (a->heads < 1 || a->head_dim < 16 || a->head_dim % 16 != 0 || a->npos < 1) return SAMBA_ERR_BAD_SHAPE;
   const int64_t tokens = static_cast<int64_t>(a->batch) * a->seqlen;

@@ -8,10 +8,13 @@ bf16, forms scores from bf16 products with fp32 accumulation, and feeds bf16 pro
 Tolerances:
   * RoPE: one bf16 rounding of the rotated value plus the fp32 roundings of the table and the products,
     |g - o| <= 2^-8 |o| + 2^-22 (|x[c]| + |x[c + hd/2]|);
-  * attention, fp32 output: per (sequence, head) max|g - o| / max|o| <= ATT_TOL.  The error is that of the
-    bf16 rotated q, k (relative 2^-9 per element, a score error of about 2^-9 |q||k| / sqrt(d) spread over
-    the keys) and of the bf16 probabilities (relative 2^-9 each); both average out over the window, leaving a
-    few 1e-3 of the output's scale at the worst element;
+  * attention, fp32 output: per (sequence, head) max|g - o| / max|o| <= ATT_TOL for scores of unit size.
+    The error is that of the bf16 operands: rotated q and k, q times log2(e)/sqrt(d) (each a relative 2^-9
+    per element, i.e. a score error of about 2^-9 |q||k| / sqrt(d) per rounding, random over the keys) and
+    the bf16 probabilities (relative 2^-9 each).  To first order the output moves by sum_j p_j ds_j
+    (v_j - o): the errors average over the window and grow with the scores' size.  Measured 2-4e-3 with
+    N(0, 1) inputs (an fp64 emulation of exactly these roundings gives the same); sharper scores get a
+    proportionally larger tolerance;
   * attention, bf16 output: one more bf16 rounding, |g - o| <= 2^-8 |o| + ATT_TOL max|o|;
   * tripwires with exact arithmetic on the device: q = 0 (every visible key weighs exactly 1, so o is an
     fp32 mean of bf16 values: error ~1e-6) pins the window's edges and the sequence boundaries, and hard
@@ -181,10 +184,12 @@ def test_swa_fwd_matches_oracle(kind, shape, H, window, out):
 
 
 def test_swa_fwd_sharp_softmax():
-    """Scores ~N(0, 16): the maximum moves often and the probabilities span many orders of magnitude."""
+    """Scores ~N(0, 16): the maximum moves often and the probabilities span many orders of magnitude.  The
+    rounding errors of the bf16 operands perturb each score in proportion to its size (to first order the
+    output moves by sum_j p_j ds_j (v_j - o)), so scores four times larger get four times the tolerance."""
     say("case: swa_fwd sharp softmax")
     g, o, b = prefill("batch", (1, 600), 2, 200, "f32", q_scale=4.0)
-    say("  error ratio %.3f" % check_att(g, o, b, "swa_fwd sharp"))
+    say("  error ratio %.3f" % check_att(g, o, b, "swa_fwd sharp", tol=4 * ATT_TOL))
 
 
 @pytest.mark.parametrize("kind,shape,window", [("batch", (2, 333), 70), ("varlen", (5, 0, 260, 1, 130), 64),
