@@ -57,6 +57,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kHD = 128;                // head size served by the attention kernels
 constexpr int kQB = 128;                // queries per prefill workgroup
 constexpr int kKB = 64;                 // keys per prefill tile
+constexpr int kKRow = kHD + 8;          // K tile row stride in LDS (bf16): 16 rows cover all banks
 constexpr float kRescale = 8.0f;        // exp2 units a score may exceed the softmax reference by
 constexpr int kRopeShift = 3;           // 8 tokens per RoPE workgroup (thousands of workgroups in flight)
 constexpr int kRopeTok = 1 << kRopeShift;
@@ -73,6 +74,11 @@ __device__ __forceinline__ rsrc_t rsrc_rows(const void* base, int rows, uint32_t
 
 __device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+// same with a wave-uniform part of the offset in the instruction's scalar offset
+__device__ __forceinline__ uint4 ld16s(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -209,15 +215,15 @@ struct SwaParams {
   float c;           // log2(e) / sqrt(head size): scores enter exp2 scaled by it
 };
 
-// V^T row swizzle: the 16-byte group g of row r is stored at g ^ vswz(r).  Rows written by one staging
-// instruction differ in r >> 3, rows read by one fragment load in r & 7; both spread.
-__device__ __forceinline__ int vswz(int r) { return (r ^ (r >> 3)) & 7; }
+// V^T row swizzle: the 16-byte group g of row r is stored at g ^ vswz(r), vswz(r) = (r ^ (r >> 3)) & 7.
+// Rows written by one staging instruction differ in r >> 3, rows read by one fragment load in r & 7; both
+// spread over the banks.  (The addresses below are this map in closed form.)
 // slot of key k inside a 64-key tile: bits 2 and 3 swapped (the score layout's key order)
 __device__ __forceinline__ int key_slot(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 template <typename Tout>
 __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKB * kHD];   // [key][hd], group g at g ^ (key & 15)
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKB * kKRow];  // [key][hd], rows padded to 272 bytes
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kHD * kKB];   // [hd][slot], group g at g ^ vswz(hd)
   const int logical = xcd_remap(blockIdx.x, p.nqb * p.heads);
   const int head = logical / p.nqb;
@@ -260,27 +266,33 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
   // staging: K rows sr + 16 r, 16-byte group sg; V keys 4 sr .. 4 sr + 3, hd 8 sg .. 8 sg + 7
   const int sr = tid >> 4, sg = tid & 15;
   uint4 kr[4], vr[4];
+  // one offset register per tensor; the row steps go in the instruction's scalar offset
+  const uint32_t gk_off = static_cast<uint32_t>(sr) * row_bytes + sg * 16;
+  const uint32_t gv_off = static_cast<uint32_t>(4 * sr) * row_bytes + sg * 16;
   auto gload = [&](int kt) {
     const int64_t tok = sb.t0 + static_cast<int64_t>(kt) * kKB;
     const int rows = (len - kt * kKB) < kKB ? len - kt * kKB : kKB;
     const rsrc_t rk = rsrc_rows(p.k + tok * p.heads * kHD + head_off, rows, row_bytes);
     const rsrc_t rv = rsrc_rows(p.v + tok * p.heads * kHD + head_off, rows, row_bytes);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) kr[r] = ld16(rk, static_cast<uint32_t>(sr + 16 * r) * row_bytes + sg * 16);
+    for (int r = 0; r < 4; ++r) kr[r] = ld16s(rk, gk_off, 16u * r * row_bytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vr[i] = ld16(rv, static_cast<uint32_t>(4 * sr + i) * row_bytes + sg * 16);
+    for (int i = 0; i < 4; ++i) vr[i] = ld16s(rv, gv_off, static_cast<uint32_t>(i) * row_bytes);
   };
+  // V^T element (row 8 sg + d, slot s) of this thread's keys: row (8 sg + d) * 64, group (s >> 3) ^ vswz(row)
+  // with vswz(8 sg + d) = (sg ^ d) & 7.  As 8 sg * 64 has no bits in 3..5, the address is vbase ^ (d << 3)
+  // plus d * 64: one XOR per row, the rest an immediate offset (no per-row address registers).
   const int vslot = key_slot(4 * sr);
+  const int vbase = 8 * sg * kKB + ((((vslot >> 3) ^ sg) & 7) << 3) + (vslot & 7);
   auto lstore = [&](auto bufc) {
     constexpr int buf = decltype(bufc)::value;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = sr + 16 * r;
-      *reinterpret_cast<uint4*>(&sK[buf][row * kHD + ((sg ^ (row & 15)) << 3)]) = kr[r];
+      *reinterpret_cast<uint4*>(&sK[buf][row * kKRow + 8 * sg]) = kr[r];
     }
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
-      const int row = 8 * sg + d;
       const int w = d >> 1;
       const uint32_t a0 = (&vr[0].x)[w], a1 = (&vr[1].x)[w], a2 = (&vr[2].x)[w], a3 = (&vr[3].x)[w];
       // bf16 number d of keys 4 sr + 0..3, packed in key order (byte select: low or high halves)
@@ -289,18 +301,16 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
       uint2 pk;
       pk.x = __builtin_amdgcn_perm(a1, a0, sel);
       pk.y = __builtin_amdgcn_perm(a3, a2, sel);
-      *reinterpret_cast<uint2*>(&sV[buf][row * kKB + (((vslot >> 3) ^ vswz(row)) << 3) + (vslot & 7)]) = pk;
+      *reinterpret_cast<uint2*>(&sV[buf][(vbase ^ (d << 3)) + d * kKB]) = pk;
     }
   };
 
-  // fragment offsets (elements) of this lane
-  int koff[8], voff[2][4];
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) koff[jj] = ql * kHD + (((2 * jj + hf) ^ (ql & 15)) << 3);
-#pragma unroll
-  for (int par = 0; par < 2; ++par)
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) voff[par][cc] = ql * kKB + (((2 * cc + hf) ^ vswz(32 * par + ql)) << 3);
+  // fragment addresses (elements) of this lane.  K rows are padded: affine in the 16-column chunk.  V^T row
+  // 32 hb + ql, slot group 2 cc + hf, is stored at group (2 cc + hf) ^ vswz(32 hb + ql), and vswz(32 hb + ql)
+  // = z ^ 4 (hb & 1) with z = (ql ^ (ql >> 3)) & 7; as ql * 64 has no bits in 3..5 the address is
+  // vtbase ^ ((2 cc ^ 4 (hb & 1)) << 3) plus hb * 32 * 64.
+  const int kbase = ql * kKRow + 8 * hf;
+  const int vtbase = ql * kKB + ((hf ^ ((ql ^ (ql >> 3)) & 7)) << 3);
 
   f32x16_t acc[4];
 #pragma unroll
@@ -324,8 +334,8 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
     f32x16_t s0 = cneg, s1 = cneg;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(K + koff[jj]);
-      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(K + koff[jj] + 32 * kHD);
+      const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(K + kbase + 16 * jj);
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(K + kbase + 32 * kKRow + 16 * jj);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[jj], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[jj], s1, 0, 0, 0);
     }
@@ -401,7 +411,8 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
     for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Vt + hb * 32 * kKB + voff[hb & 1][cc]);
+        const bf16x8_t a =
+            *reinterpret_cast<const bf16x8_t*>(Vt + hb * 32 * kKB + (vtbase ^ (((2 * cc) ^ (4 * (hb & 1))) << 3)));
         acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[cc], acc[hb], 0, 0, 0);
       }
   };
