@@ -50,8 +50,9 @@ extern "C" {
  * sequence, plus pos0[s] for sequence s when pos0 (device int32 [nseq]) is
  * given; a decode step is a batch of one-token sequences with pos0 = the
  * tokens' positions.  Positions outside [0, npos) are clamped into the table
- * (memory-safe; results for such input are unspecified).  head_dim even, a
- * multiple of 16; q/k 16-byte aligned; tables 16-byte aligned.
+ * (memory-safe; results for such input are unspecified).  head_dim a multiple
+ * of 16 up to 4096, heads * head_dim at most 2^20; q/k 16-byte aligned;
+ * tables 16-byte aligned.
  */
 typedef struct {
   uint32_t struct_size;        /* = sizeof(samba_rope_args) */

@@ -59,8 +59,6 @@ constexpr int kQB = 128;                // queries per prefill workgroup
 constexpr int kKB = 64;                 // keys per prefill tile
 constexpr int kKRow = kHD + 8;          // K tile row stride in LDS (bf16): 16 rows cover all banks
 constexpr float kRescale = 8.0f;        // exp2 units a score may exceed the softmax reference by
-constexpr int kRopeShift = 3;           // 8 tokens per RoPE workgroup (thousands of workgroups in flight)
-constexpr int kRopeTok = 1 << kRopeShift;
 
 // Resource over `rows` rows of row_bytes; rows <= 0 gives an empty resource (loads return 0, stores are
 // dropped), byte counts beyond 32 bits saturate.
@@ -75,6 +73,10 @@ __device__ __forceinline__ rsrc_t rsrc_rows(const void* base, int rows, uint32_t
 __device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st16(rsrc_t r, uint32_t off, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
 }
 // same with a wave-uniform part of the offset in the instruction's scalar offset
 __device__ __forceinline__ uint4 ld16s(rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -152,52 +154,102 @@ struct RopeParams {
   const float *cs, *sn;
   const int32_t *cu, *pos0;
   int32_t nseq, seqlen, heads, hd, npos, per_seq, total;
+  int32_t shift;   // log2 of the tokens per workgroup
+  int32_t groups;  // head groups per token (threads per token = groups x head_dim / 16)
 };
 
-__device__ __forceinline__ void rope_rows(const uint16_t* in, uint16_t* out, int64_t off, int half, const float (&c)[8],
-                                          const float (&s)[8]) {
-  const uint4 a = *reinterpret_cast<const uint4*>(in + off);
-  const uint4 b = *reinterpret_cast<const uint4*>(in + off + half);
-  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-  uint32_t ra[4], rb[4];
+// Rotate 8 pairs (x[c..c+7], x[c+half..c+half+7]) held as bf16 words a (first half) and b (second half).
+__device__ __forceinline__ void rope8(uint4& a, uint4& b, const float (&c)[8], const float (&s)[8]) {
+  uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const float x0 = bf_lo(aw[w]), x1 = bf_hi(aw[w]), y0 = bf_lo(bw[w]), y1 = bf_hi(bw[w]);
     const int i = 2 * w;
-    ra[w] = pack_bf16(fmaf(x0, c[i], -y0 * s[i]), fmaf(x1, c[i + 1], -y1 * s[i + 1]));
-    rb[w] = pack_bf16(fmaf(y0, c[i], x0 * s[i]), fmaf(y1, c[i + 1], x1 * s[i + 1]));
+    aw[w] = pack_bf16(fmaf(x0, c[i], -y0 * s[i]), fmaf(x1, c[i + 1], -y1 * s[i + 1]));
+    bw[w] = pack_bf16(fmaf(y0, c[i], x0 * s[i]), fmaf(y1, c[i + 1], x1 * s[i + 1]));
   }
-  *reinterpret_cast<uint4*>(out + off) = make_uint4(ra[0], ra[1], ra[2], ra[3]);
-  *reinterpret_cast<uint4*>(out + off + half) = make_uint4(rb[0], rb[1], rb[2], rb[3]);
+  a = make_uint4(aw[0], aw[1], aw[2], aw[3]);
+  b = make_uint4(bw[0], bw[1], bw[2], bw[3]);
 }
 
-// One workgroup per 8 tokens of one sequence; a work item is (token, head, 8 rotation pairs).
+constexpr int kRopeGroups = 8;   // head groups per token (thread (token, group, chunk)), fewer for head_dim > 512
+constexpr int kRopeBatch = 4;    // heads of a group loaded together before any store
+
+// One workgroup per 2^shift tokens of one sequence; thread (token, head group g, chunk c of 8 rotation
+// pairs) reads the token's table entries once and rotates chunk c of heads g, g + G, g + 2G, ... of q and k.
+// Every access goes through a buffer resource over the workgroup's token rows, and accesses that do not
+// exist (a head past the last, a token past the sequence's end) get an out-of-range offset: loads return
+// zeros and stores are dropped, so the code has no branches, and all loads of a batch of heads are issued
+// before its stores (in-place calls alias input and output, so the compiler could not reorder them).
+template <bool kQ, bool kK>
 __global__ __launch_bounds__(256) void rope_kernel(RopeParams p) {
-  const SeqBlock sb = locate(p.cu, p.nseq, p.total, p.seqlen, p.per_seq, blockIdx.x, kRopeShift);
-  if (sb.j < 0 || sb.j * kRopeTok >= sb.len) return;
-  const int first = sb.j * kRopeTok;
-  const int ntok = (sb.len - first) < kRopeTok ? sb.len - first : kRopeTok;
-  const int half = p.hd >> 1, cph = half >> 3, per_tok = p.heads * cph;
-  int32_t base_pos = first;
+  const SeqBlock sb = locate(p.cu, p.nseq, p.total, p.seqlen, p.per_seq, blockIdx.x, p.shift);
+  const int tpb = 1 << p.shift;
+  if (sb.j < 0 || sb.j * tpb >= sb.len) return;
+  const int first = sb.j * tpb;
+  const int ntok = (sb.len - first) < tpb ? sb.len - first : tpb;
+  const int half = p.hd >> 1, cph = half >> 3;
+  const int t = static_cast<int>(threadIdx.x);
+  const int cc = t % cph, g = (t / cph) % p.groups, tl = t / (cph * p.groups);
+  const bool live = tl < ntok;
+  int32_t pos = first + (live ? tl : 0);
   if (p.pos0) {
-    const int s = p.cu ? seq_of_block(p.cu, p.nseq, blockIdx.x, kRopeShift, p.total)
+    const int s = p.cu ? seq_of_block(p.cu, p.nseq, blockIdx.x, p.shift, p.total)
                        : static_cast<int>(blockIdx.x) / p.per_seq;
-    base_pos += p.pos0[s];
+    pos += p.pos0[s];
   }
-  for (int it = threadIdx.x; it < ntok * per_tok; it += blockDim.x) {
-    const int tl = it / per_tok, rem = it - tl * per_tok;
-    const int h = rem / cph, cc = rem - h * cph;
-    int32_t pos = base_pos + tl;
-    pos = pos < 0 ? 0 : (pos >= p.npos ? p.npos - 1 : pos);
-    float c[8], s[8];
+  pos = pos < 0 ? 0 : (pos >= p.npos ? p.npos - 1 : pos);
+  float c[8], s[8];
+  {
     const float4* tc = reinterpret_cast<const float4*>(p.cs + static_cast<int64_t>(pos) * half + 8 * cc);
     const float4* ts = reinterpret_cast<const float4*>(p.sn + static_cast<int64_t>(pos) * half + 8 * cc);
     const float4 c0 = tc[0], c1 = tc[1], s0 = ts[0], s1 = ts[1];
     c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w; c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
     s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w; s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
-    const int64_t off = ((sb.t0 + first + tl) * p.heads + h) * p.hd + 8 * cc;
-    if (p.qi) rope_rows(p.qi, p.qo, off, half, c, s);
-    if (p.ki) rope_rows(p.ki, p.ko, off, half, c, s);
+  }
+  const int64_t blk = (sb.t0 + first) * p.heads * p.hd;   // first element of the workgroup's rows
+  const uint32_t row_bytes = static_cast<uint32_t>(p.heads) * p.hd * 2u;
+  // (a tensor that is not rotated gets an empty resource over the other one's rows; it is never used)
+  const uint16_t* qi = kQ ? p.qi : p.ki;
+  uint16_t* qo = kQ ? p.qo : p.ko;
+  const uint16_t* ki = kK ? p.ki : p.qi;
+  uint16_t* ko = kK ? p.ko : p.qo;
+  const rsrc_t rqi = rsrc_rows(qi + blk, kQ ? ntok : 0, row_bytes), rqo = rsrc_rows(qo + blk, kQ ? ntok : 0, row_bytes);
+  const rsrc_t rki = rsrc_rows(ki + blk, kK ? ntok : 0, row_bytes), rko = rsrc_rows(ko + blk, kK ? ntok : 0, row_bytes);
+  // beyond any resource (a workgroup's rows span at most 32 x 2 MiB), also after adding the half-row step:
+  // loads read zeros, stores are dropped
+  constexpr uint32_t kNowhere = 0x80000000u;
+  const uint32_t base = live ? static_cast<uint32_t>(tl) * row_bytes + 16u * cc : kNowhere;
+  const uint32_t hstep = static_cast<uint32_t>(p.hd) * 2u, hb = static_cast<uint32_t>(half) * 2u;
+  for (int h0 = g; h0 < p.heads; h0 += p.groups * kRopeBatch) {
+    uint32_t off[kRopeBatch];
+    uint4 qa[kRopeBatch], qb[kRopeBatch], ka[kRopeBatch], kb[kRopeBatch];
+#pragma unroll
+    for (int u = 0; u < kRopeBatch; ++u) {
+      const int h = h0 + p.groups * u;
+      off[u] = (h < p.heads && live) ? base + static_cast<uint32_t>(h) * hstep : kNowhere;
+      if constexpr (kQ) {
+        qa[u] = ld16(rqi, off[u]);
+        qb[u] = ld16(rqi, off[u] + hb);
+      }
+      if constexpr (kK) {
+        ka[u] = ld16(rki, off[u]);
+        kb[u] = ld16(rki, off[u] + hb);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRopeBatch; ++u) {
+      if constexpr (kQ) {
+        rope8(qa[u], qb[u], c, s);
+        st16(rqo, off[u], qa[u]);
+        st16(rqo, off[u] + hb, qb[u]);
+      }
+      if constexpr (kK) {
+        rope8(ka[u], kb[u], c, s);
+        st16(rko, off[u], ka[u]);
+        st16(rko, off[u] + hb, kb[u]);
+      }
+    }
   }
 }
 
@@ -659,9 +711,18 @@ samba_status samba_rope(const samba_rope_args* a, void* stream) {
   if (a->struct_size != sizeof(samba_rope_args)) return SAMBA_ERR_BAD_STRUCT;
   RopeParams p{};
   int64_t nblk = 0;
-  samba_status st = token_shape(a->batch, a->seqlen, a->cu_seqlens, a->nseq, &nblk, kRopeShift, &p.per_seq);
+  if (a->heads < 1 || a->head_dim < 16 || a->head_dim % 16 != 0 || a->head_dim > 4096 || a->npos < 1 ||
+      static_cast<int64_t>(a->heads) * a->head_dim > (1 << 20))
+    return SAMBA_ERR_BAD_SHAPE;
+  // head groups: 8, or as many as fit 256 threads for one token (head_dim > 512); tokens per workgroup: the
+  // largest power of two whose threads fit 256
+  const int cph = a->head_dim / 16;
+  p.groups = cph * kRopeGroups <= 256 ? kRopeGroups : 256 / cph;
+  int shift = 0;
+  while ((2 << shift) * p.groups * cph <= 256) ++shift;
+  p.shift = shift;
+  samba_status st = token_shape(a->batch, a->seqlen, a->cu_seqlens, a->nseq, &nblk, shift, &p.per_seq);
   if (st != SAMBA_OK) return st;
-  if (a->heads < 1 || a->head_dim < 16 || a->head_dim % 16 != 0 || a->npos < 1) return SAMBA_ERR_BAD_SHAPE;
   const int64_t tokens = static_cast<int64_t>(a->batch) * a->seqlen;
   const size_t bytes = static_cast<size_t>(tokens) * a->heads * a->head_dim * 2;
   if (nblk == 0 || tokens == 0) return SAMBA_OK;
@@ -701,7 +762,11 @@ samba_status samba_rope(const samba_rope_args* a, void* stream) {
   p.npos = a->npos;
   p.total = a->seqlen;
   if (!p.qi && !p.ki) return SAMBA_OK;
-  hipLaunchKernelGGL(rope_kernel, dim3(static_cast<uint32_t>(nblk)), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+  const dim3 grid(static_cast<uint32_t>(nblk));
+  const hipStream_t sm = static_cast<hipStream_t>(stream);
+  if (p.qi && p.ki) hipLaunchKernelGGL((rope_kernel<true, true>), grid, dim3(256), 0, sm, p);
+  else if (p.qi) hipLaunchKernelGGL((rope_kernel<true, false>), grid, dim3(256), 0, sm, p);
+  else hipLaunchKernelGGL((rope_kernel<false, true>), grid, dim3(256), 0, sm, p);
   return hipGetLastError() == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
 }
 

@@ -389,6 +389,8 @@ ROPE_CASES = {
     "zero_heads": (lambda a: setattr(a, "heads", 0), 2),
     "head_dim_not_16": (lambda a: setattr(a, "head_dim", 72), 2),
     "zero_npos": (lambda a: setattr(a, "npos", 0), 2),
+    "head_dim_too_large": (lambda a: setattr(a, "head_dim", 4112), 2),
+    "too_many_features": (lambda a: setattr(a, "heads", 8193), 2),
     "varlen_batch": (lambda a: (setattr(a, "cu_seqlens", BASE + 6 * GB), setattr(a, "nseq", 2)), 2),
     "varlen_nseq0": (lambda a: (setattr(a, "batch", 1), setattr(a, "cu_seqlens", BASE + 6 * GB)), 2),
     "null_cos": (lambda a: setattr(a, "cos", None), 1),

@@ -120,6 +120,26 @@ def test_rope_matches_oracle(lengths):
                                                                                    kr.view(torch.int16))
 
 
+@pytest.mark.parametrize("H,hd", [(40, 64), (1, 16), (2, 1024)])
+def test_rope_other_shapes(H, hd):
+    """Head sizes other than 128 (RoPE accepts any multiple of 16) and more heads than one pass covers."""
+    say("case: rope H%d hd%d" % (H, hd))
+    T = 77
+    g = np.random.default_rng(12)
+    v = g.standard_normal((2, T, H, hd)).astype(np.float32)
+    bits = [I.bf16_bits_from_f32(x) for x in v]
+    c, s = I.rope_tables(T, hd)
+    ct, st = (torch.from_numpy(x.astype(np.float32)).to(DEV) for x in (c, s))
+    q, k = (bf16_dev(b).reshape(1, T, H, hd) for b in bits)
+    qr, kr = W.rope(q, k, ct, st)
+    torch.cuda.synchronize()
+    for g_, b in ((qr, bits[0]), (kr, bits[1])):
+        x = I.f32_from_bf16_bits(b)
+        o = O.rope(x, c, s, np.arange(T))
+        ratio = np.abs(host(g_).reshape(T, H, hd) - o) / rope_bound(x, o)
+        assert np.all(ratio <= 1.0), "worst ratio %.3f" % float(ratio.max())
+
+
 def test_rope_positions_offset():
     """A decode batch: one-token sequences at positions pos0[b] (and k only)."""
     B, H = 9, 4
