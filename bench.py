@@ -456,6 +456,7 @@ def bench_swa(steps: int = 20, warmup: int = 5):
                         "attention (Samba-3.8B layer, training shape)" % (B, L, H, hd, w),
             "steps": steps, "ms_per_layer": ms_layer, "tokens_per_s": B * L / (ms_layer * 1e-3),
             "attention_ms": ms_att, "rope_ms": ms_rope, "tflops": tf,
+            "rope_gbs": (4 * B * L * H * hd * 2 + 2 * L * (hd // 2) * 4) / (ms_rope * 1e-3) / 1e9,
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": read_swa_traffic("prefill"),
                          "kernel": "swa_fwd_kernel<bf16> (v_mfma_f32_32x32x16_bf16)", "flops_per_launch": flops,
@@ -632,6 +633,68 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
     print(json.dumps(out_d))
 
 
+SWA_PMC_RUN = ("python3 <repo>/bench.py --swa-only --swa-steps 2 --swa-decode-steps 2 --warmup 1 --copy-probe")
+
+
+def pmc_summary_swa(fetch_dir: str, write_dir: str, out: str):
+    """The attention kernels' HBM bytes per launch from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of
+    SWA_PMC_RUN, calibrated by the 512 MiB copy of the same run (as pmc_summary does for the scan)."""
+    import csv
+    import glob
+    import statistics
+
+    def per_kernel(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        vals = {}
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault((r["Kernel_Name"], int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0)),
+                                []).append(float(r["Counter_Value"]))
+        return vals
+
+    def pick(vals, part, largest=True):
+        keys = [k for k in vals if part in k[0]]
+        assert keys, part
+        return sorted(keys, key=lambda k: k[1])[-1 if largest else 0]
+
+    from selective_state_space_05_amd import inputs as I
+    wl6, wl7 = I.WORKLOADS[6], I.WORKLOADS[7]
+    B, L, H, hd, w = wl6.batch, wl6.seqlen, wl6.extra["heads"], wl6.extra["head_dim"], wl6.extra["window"]
+    Bd, Hd, hdd, wd = wl7.batch, wl7.extra["heads"], wl7.extra["head_dim"], wl7.extra["window"]
+    sel = {"prefill": ("swa_fwd_kernel<unsigned short>", True, 4 * B * L * H * hd * 2),
+           "rope_prefill": ("rope_kernel<true, true>", True, 4 * B * L * H * hd * 2 + 2 * L * hd * 4),
+           "decode": ("swa_decode_kernel<unsigned short>", True, swa_decode_bytes(Bd, Hd, hdd, wd))}
+    got = {k: {} for k in sel}
+    scales = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = per_kernel(d, counter)
+        copy = [v for k, vs in vals.items() if "copyBuffer" in k[0] for v in vs]
+        big = min(v for v in copy if v > 0.25 * max(copy))
+        scale = (512 << 20) / 1024.0 / big
+        scales[counter] = {"copy_raw_kib_per_dispatch": big, "scale": scale}
+        for name, (part, largest, _) in sel.items():
+            key = pick(vals, part, largest)
+            kib = statistics.median(vals[key])
+            got[name][counter] = {"kernel": key[0][:120], "grid": key[1], "raw_kib_per_dispatch": kib,
+                                  "bytes": kib * scale * 1024.0}
+    out_d = {"kernel_source_sha256_16": swa_hash(), "unit": "bytes per launch", "calibration": scales}
+    for name, (_, _, algorithmic) in sel.items():
+        f, wr = got[name]["FETCH_SIZE"]["bytes"], got[name]["WRITE_SIZE"]["bytes"]
+        out_d[name] = {"kernel": got[name]["FETCH_SIZE"]["kernel"], "grid": got[name]["FETCH_SIZE"]["grid"],
+                       "fetch_bytes": f, "write_bytes": wr, "bytes_per_launch": f + wr,
+                       "algorithmic_bytes_per_launch": algorithmic}
+    out_d["command"] = [
+        f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {SWA_PMC_RUN}",
+        f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {SWA_PMC_RUN}",
+        f"python bench.py --pmc-summary-swa {fetch_dir} {write_dir} {out}",
+    ]
+    out_d["note"] = ("Algorithmic bytes: prefill q, k, v read once and o written once (the window's re-reads of K "
+                     "and V are meant to hit L2); RoPE q, k read and written plus the tables; decode the window's "
+                     "cached K and V, the new q, k, v, the cache write and o.")
+    Path(out).write_text(json.dumps(out_d, indent=1) + "\n")
+    print(json.dumps(out_d))
+
+
 def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
     """Measured device-to-device copy rate (bytes read + bytes written per second, GB/s): the practical HBM
     ceiling the algorithmic rates are also compared with."""
@@ -777,9 +840,14 @@ def main():
                     help="also run a plain 512 MiB device copy (untimed), the reference kernel for HBM byte counters")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="summarise two rocprofv3 counter runs into OUT (host only; no GPU work)")
+    ap.add_argument("--pmc-summary-swa", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="the same for the attention kernels (counter runs of the --swa-only legs)")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.pmc_summary_swa:
+        pmc_summary_swa(*args.pmc_summary_swa)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1",
