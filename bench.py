@@ -314,7 +314,7 @@ def bench_proj(steps: int = 20, warmup: int = 5):
                          "algorithmic_bytes_per_call": nbytes}}
 
 
-def cpu_baseline_proj(rows: int = 64):
+def cpu_baseline_proj(rows: int = 1024):
     """The fp64 oracle's projections on `rows` tokens of the same shape (D 4096), extrapolated to TFLOP/s."""
     import numpy as np
     from oracle import oracle as O
@@ -519,7 +519,7 @@ def bench_swa_decode(steps: int = 200, warmup: int = 20):
                          "algorithmic_bytes_per_launch": nbytes}}
 
 
-def cpu_baseline_swa(rows: int = 256):
+def cpu_baseline_swa(rows: int = 2048):
     """The fp64 oracle's attention for `rows` query rows of one 4096-token sequence (all 24 heads, full
     2048-token windows), in TFLOP/s of the same algorithmic count."""
     import numpy as np
@@ -541,7 +541,7 @@ def cpu_baseline_swa(rows: int = 256):
                       "RoPE, %.1f s" % (rows, spent)}
 
 
-def cpu_baseline_swa_decode(seqs: int = 16):
+def cpu_baseline_swa_decode(seqs: int = 64):
     """The fp64 oracle's decode output (last row of a full window) for `seqs` of the 64 sequences,
     extrapolated to steps/s of the whole batch."""
     import numpy as np
