@@ -82,23 +82,26 @@ static double token_update(double* h, int64_t N, double xv, double dtv, double z
 }
 
 /*
- * Prefill over nseq sequences packed along the token axis.
+ * Prefill over nseq sequences packed along the token axis, with ngroups groups of (B, C) vectors per token.
  *   seq_start [nseq+1] : token offsets, seq_start[0] = 0, ascending; seq s owns
  *                        tokens [seq_start[s], seq_start[s+1]).
- *   x, dt, z  [T][dim] , B, C [T][dstate] , A [dim][dstate], Dskip, dt_bias [dim]
+ *   x, dt, z  [T][dim] , B, C [T][ngroups][dstate] , A [dim][dstate], Dskip, dt_bias [dim]
+ *   channel d reads the (B, C) of group d / (dim / ngroups): contiguous blocks of channels share a group
+ *   (ngroups = 1: one vector per token shared by all channels, the pages' selection)
  *   h0        [nseq][dim][dstate] or NULL (zeros)
  *   y         [T][dim] (written)
  *   h_last    [nseq][dim][dstate] or NULL (not written)
  * Returns 0, or -1 on invalid sizes / allocation failure.
  */
-int oracle_scan_fwd(int64_t nseq, const int64_t* seq_start, int64_t dim, int64_t dstate,
-                    const double* x, const double* dt, const double* z,
-                    const double* B, const double* C,
-                    const double* A, const double* Dskip, const double* dt_bias,
-                    const double* h0, double* y, double* h_last, int nthreads) {
-  if (nseq < 0 || dim < 0 || dstate < 1 || !seq_start) return -1;
+int oracle_scan_fwd_groups(int64_t nseq, const int64_t* seq_start, int64_t dim, int64_t dstate, int64_t ngroups,
+                           const double* x, const double* dt, const double* z,
+                           const double* B, const double* C,
+                           const double* A, const double* Dskip, const double* dt_bias,
+                           const double* h0, double* y, double* h_last, int nthreads) {
+  if (nseq < 0 || dim < 0 || dstate < 1 || ngroups < 1 || dim % ngroups != 0 || !seq_start) return -1;
   for (int64_t s = 0; s < nseq; ++s)
     if (seq_start[s + 1] < seq_start[s]) return -1;
+  const int64_t per_group = dim / ngroups;
   int failed = 0;
 #ifdef _OPENMP
   if (nthreads <= 0) nthreads = omp_get_max_threads();
@@ -106,13 +109,15 @@ int oracle_scan_fwd(int64_t nseq, const int64_t* seq_start, int64_t dim, int64_t
 #endif
   for (int64_t s = 0; s < nseq; ++s) {
     for (int64_t d = 0; d < dim; ++d) {
+      const int64_t g = d / per_group;
       double* h = (double*)malloc((size_t)dstate * sizeof(double));
       if (!h) { failed = 1; continue; }
       for (int64_t n = 0; n < dstate; ++n)
         h[n] = h0 ? h0[(s * dim + d) * dstate + n] : 0.0;
       for (int64_t t = seq_start[s]; t < seq_start[s + 1]; ++t) {
         y[t * dim + d] = token_update(h, dstate, x[t * dim + d], dt[t * dim + d], z[t * dim + d],
-                                      B + t * dstate, C + t * dstate, A + d * dstate,
+                                      B + (t * ngroups + g) * dstate, C + (t * ngroups + g) * dstate,
+                                      A + d * dstate,
                                       Dskip[d], dt_bias[d]);
       }
       if (h_last)
@@ -122,6 +127,16 @@ int oracle_scan_fwd(int64_t nseq, const int64_t* seq_start, int64_t dim, int64_t
   }
   (void)nthreads;
   return failed ? -1 : 0;
+}
+
+/* The pages' selection: one (B, C) pair per token shared by all channels. */
+int oracle_scan_fwd(int64_t nseq, const int64_t* seq_start, int64_t dim, int64_t dstate,
+                    const double* x, const double* dt, const double* z,
+                    const double* B, const double* C,
+                    const double* A, const double* Dskip, const double* dt_bias,
+                    const double* h0, double* y, double* h_last, int nthreads) {
+  return oracle_scan_fwd_groups(nseq, seq_start, dim, dstate, 1, x, dt, z, B, C, A, Dskip, dt_bias, h0, y,
+                                h_last, nthreads);
 }
 
 /*

@@ -61,6 +61,8 @@ def _bind(lib):
     lib.oracle_swa_rows.restype = ctypes.c_int
     lib.oracle_rope.argtypes = [I64, I64, I64, P, P, P, P, P]
     lib.oracle_rope.restype = ctypes.c_int
+    lib.oracle_scan_fwd_groups.argtypes = [I64, P, I64, I64, I64] + [P] * 11 + [ctypes.c_int]
+    lib.oracle_scan_fwd_groups.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -112,6 +114,42 @@ def scan_fwd(x, dt, z, B, C, A, D, dt_bias, h0=None, seq_start=None, nthreads: i
                              _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_last), int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_scan_fwd failed (%d)" % rc)
+    return y.reshape(shape), h_last
+
+
+def scan_fwd_groups(x, dt, z, B, C, A, D, dt_bias, h0=None, seq_start=None, nthreads: int = 0, lib=None):
+    """Prefill with G groups of (B, C) per token: B, C [T][G][N] (or [batch][L][G][N]); channel d reads
+    group d // (dim // G).  Otherwise as scan_fwd."""
+    lib = lib or load()
+    x = _f64(x)
+    shape = x.shape
+    if x.ndim == 3:
+        batch, L, dim = shape
+        if seq_start is None:
+            seq_start = np.arange(batch + 1, dtype=np.int64) * L
+        x = x.reshape(batch * L, dim)
+        dt, z = _f64(dt).reshape(batch * L, dim), _f64(z).reshape(batch * L, dim)
+        B, C = _f64(B).reshape(batch * L, *np.shape(B)[2:]), _f64(C).reshape(batch * L, *np.shape(C)[2:])
+    else:
+        dim = shape[1]
+        if seq_start is None:
+            seq_start = np.array([0, shape[0]], dtype=np.int64)
+        dt, z, B, C = _f64(dt), _f64(z), _f64(B), _f64(C)
+    A, D, dt_bias = _f64(A), _f64(D), _f64(dt_bias)
+    T = x.shape[0]
+    G, dstate = B.shape[1], B.shape[2]
+    seq_start = np.ascontiguousarray(np.asarray(seq_start, dtype=np.int64))
+    nseq = len(seq_start) - 1
+    assert seq_start[0] == 0 and seq_start[-1] == T
+    assert B.shape == C.shape == (T, G, dstate) and A.shape == (dim, dstate)
+    h0 = None if h0 is None else _f64(h0).reshape(nseq, dim, dstate)
+    y = np.empty((T, dim), dtype=np.float64)
+    h_last = np.empty((nseq, dim, dstate), dtype=np.float64)
+    rc = lib.oracle_scan_fwd_groups(nseq, _ptr(seq_start), dim, dstate, G, _ptr(x), _ptr(dt), _ptr(z), _ptr(B),
+                                    _ptr(C), _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_last),
+                                    int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_scan_fwd_groups failed (%d)" % rc)
     return y.reshape(shape), h_last
 
 
