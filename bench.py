@@ -408,6 +408,78 @@ def _timed(fn, steps: int, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def groups_slots_per_td(n: int) -> int:
+    """Algorithmic issue slots per (token, channel) of the grouped prefill with n states: per state the Δ·A
+    mul, the exp (4 slots), the Δx·B mul, the state FMA and the readout FMA (8); per (token, channel)
+    softplus and silu (2 transcendentals each), Δx, skip, gate and 4 bf16 conversions (28)."""
+    return 8 * n + 28
+
+
+def bench_groups(steps: int = 10, warmup: int = 3):
+    """samba_scan_fwd_groups on B4 L4096 D4096 with 4 (B, C) groups of 64 states (bf16 I/O)."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import scan as S
+
+    wl = I.WORKLOADS[8]
+    Bt, L, D, N, G = wl.batch, wl.seqlen, wl.dim, wl.dstate, wl.extra["ngroups"]
+    dev = torch.device("cuda:0")
+    t = I.make_groups_inputs_torch(8, Bt * L, D, G, N, dev)
+    x, dt, z = (t[k].view(Bt, L, D) for k in ("x", "dt", "z"))
+    B, C = (t[k].view(Bt, L, G, N) for k in ("B", "C"))
+    y = torch.empty_like(x)
+    hl = torch.empty(Bt, D, N, dtype=torch.float32, device=dev)
+    a = S.groups_args(x, dt, z, B, C, t["A"], t["D"], t["dt_bias"], y=y, h_last=hl)
+    lib = S.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    ref = ctypes.byref(a)
+
+    def call():
+        if lib.samba_scan_fwd_groups(ref, sh) != 0:
+            raise RuntimeError("samba_scan_fwd_groups failed")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = _timed(call, steps, stream)
+    td = Bt * L * D
+    slots = groups_slots_per_td(N) * td
+    achieved = slots / (ms * 1e-3) / 1e12
+    nbytes = td * 4 * 2 + Bt * L * G * N * 2 * 2 + D * N * 4 + D * 8 + Bt * D * N * 4
+    return {"workload": "grouped prefill B=%d L=%d D=%d, %d (B, C) groups of %d states, bf16 I/O, fp32 state"
+                        % (Bt, L, D, G, N),
+            "steps": steps, "ms_per_call": ms, "tokens_channels_per_s": td / (ms * 1e-3),
+            "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TSLOT, 2),
+                         "unit": "Tslot/s", "frac": round(achieved / VALU_PEAK_TSLOT, 4), "traffic": None,
+                         "kernel": "scan_groups_kernel<bf16,bf16,N=%d>" % N, "launch_us": round(ms * 1e3, 2),
+                         "slots_per_token_channel": groups_slots_per_td(N),
+                         "algorithmic_bytes_per_launch": nbytes}}
+
+
+def cpu_baseline_groups(seqs: int = 1, channels: int = 512):
+    """The fp64 oracle's grouped prefill on one sequence of the same shape, `channels` channels (128 per
+    group), in token·channels/s."""
+    import numpy as np
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+
+    wl = I.WORKLOADS[8]
+    L, D, N, G = wl.seqlen, wl.dim, wl.dstate, wl.extra["ngroups"]
+    inp = I.make_groups_inputs_np(8, L, D, G, N)
+    per = D // G
+    cols = np.concatenate([np.arange(g * per, g * per + channels // G) for g in range(G)])
+    lib = O.load()
+    t0 = time.perf_counter()
+    O.scan_fwd_groups(inp["x_f32"][:, cols], inp["dt_f32"][:, cols], inp["z_f32"][:, cols], inp["B_f32"],
+                      inp["C_f32"], inp["A"][cols], inp["D"][cols], inp["dt_bias"][cols], lib=lib)
+    spent = time.perf_counter() - t0
+    return {"value": L * channels / spent, "unit": "tokens*channels/s", "cores": O.max_threads(lib),
+            "kind": "oracle", "sample": "one 4096-token sequence, %d of the 4096 channels (%d per group), fp64 "
+                                        "oracle, %.1f s" % (channels, channels // G, spent)}
+
+
 def bench_swa(steps: int = 20, warmup: int = 5):
     """The sliding-window attention layer of Samba-3.8B on the training shape: batch 4 x 4096 tokens, 24 heads
     of 128, window 2048, bf16 q/k/v/o.  One layer pass = RoPE of q and k, then the attention."""
@@ -833,6 +905,9 @@ def main():
     ap.add_argument("--no-swa", action="store_true", help="skip the sliding-window attention legs")
     ap.add_argument("--swa-steps", type=int, default=20)
     ap.add_argument("--swa-decode-steps", type=int, default=200)
+    ap.add_argument("--no-groups", action="store_true", help="skip the grouped-prefill leg")
+    ap.add_argument("--groups-steps", type=int, default=10)
+    ap.add_argument("--groups-only", action="store_true", help="run only the grouped-prefill leg")
     ap.add_argument("--swa-only", action="store_true",
                     help="run only the attention legs (and the copy probe with --copy-probe): counter runs")
     ap.add_argument("--time-slices", type=int, default=0, help="force the prefill's waves per time chunk (0 = auto)")
@@ -854,6 +929,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.groups_only:
+        print(json.dumps({"groups": bench_groups(args.groups_steps, min(args.warmup, 3))}), flush=True)
+        return
     if args.swa_only:
         out = {"attention": bench_swa(args.swa_steps, min(args.warmup, 5)),
                "attention_decode": bench_swa_decode(args.swa_decode_steps, min(args.warmup, 20))}
@@ -910,6 +988,8 @@ def main():
     if not args.no_bwd:
         line["backward"] = bench_backward(args.bwd_steps)
         line["backward"]["roofline"]["traffic"] = read_traffic("backward")
+    if not args.no_groups:
+        line["groups"] = bench_groups(args.groups_steps)
     if not args.no_swa:
         line["attention"] = bench_swa(args.swa_steps)
         line["attention_decode"] = bench_swa_decode(args.swa_decode_steps)
@@ -922,6 +1002,8 @@ def main():
             line["cpu_baseline"]["backward"] = cpu_baseline_backward()
         if not args.no_proj:
             line["cpu_baseline"]["projections"] = cpu_baseline_proj()
+        if not args.no_groups:
+            line["cpu_baseline"]["groups"] = cpu_baseline_groups()
         if not args.no_swa:
             line["cpu_baseline"]["attention"] = cpu_baseline_swa()
             line["cpu_baseline"]["attention_decode"] = cpu_baseline_swa_decode()

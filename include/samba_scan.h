@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SAMBA_SCAN_ABI_VERSION 5
+#define SAMBA_SCAN_ABI_VERSION 6
 #define SAMBA_DSTATE 16
 
 typedef enum {
@@ -225,6 +225,37 @@ typedef struct {
 
 /* Enqueue the selection projections.  See samba_proj_args. */
 samba_status samba_proj(const samba_proj_args* args, void* stream);
+
+/*
+ * Grouped prefill: samba_scan_fwd generalised to ngroups (B, C) vectors per
+ * token and to state sizes 16, 32, 64, 128 or 256 (the pages' selection is
+ * the case ngroups = 1, dstate = 16; same recurrence, discretisation, skip
+ * and gate).  Channel d reads group d / (dim / ngroups): contiguous blocks of
+ * channels share a group.  B, C are [tokens][ngroups][dstate] in in_dtype;
+ * A [dim][dstate]; h0, h_last [nseq][dim][dstate] fp32; everything else as
+ * for samba_scan_fwd (batched rows or cu_seqlens, optional h0 / h_last, h_last
+ * may equal h0 exactly).  Constraints: dim divisible by ngroups and each
+ * group's dim / ngroups channels a multiple of 256 / dstate (a wave's
+ * channels share a group); per sequence tokens * dim * 4 < 2^32.  Alignment:
+ * B, C, A, h0, h_last 16 bytes; others their element size.  No time slicing:
+ * parallelism comes from sequences x channels x dstate / 4 lanes.
+ */
+typedef struct {
+  uint32_t struct_size;        /* = sizeof(samba_scan_groups_args) */
+  int32_t batch, seqlen, dim, dstate, ngroups;
+  const int32_t* cu_seqlens;   /* optional, device */
+  int32_t nseq;
+  int32_t in_dtype, y_dtype;
+  const void *x, *dt, *z;      /* [tokens][dim] */
+  const void *B, *C;           /* [tokens][ngroups][dstate] */
+  const float *A, *D, *dt_bias;
+  const float* h0;             /* optional */
+  float* h_last;               /* optional */
+  void* y;
+} samba_scan_groups_args;
+
+/* Enqueue a grouped prefill.  See samba_scan_groups_args. */
+samba_status samba_scan_fwd_groups(const samba_scan_groups_args* args, void* stream);
 
 /* Enqueue a prefill scan.  See samba_scan_fwd_args. */
 samba_status samba_scan_fwd(const samba_scan_fwd_args* args, void* stream);

@@ -12,7 +12,7 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SRCS = (PKG / "csrc" / "samba_scan.hip", PKG / "csrc" / "samba_swa.hip")
+SRCS = (PKG / "csrc" / "samba_scan.hip", PKG / "csrc" / "samba_scan_groups.hip", PKG / "csrc" / "samba_swa.hip")
 HEADERS = (ROOT / "include" / "samba_scan.h", ROOT / "include" / "samba_swa.h")
 LIB = PKG / "libsamba_scan.so"
 

@@ -5,6 +5,8 @@ scan's arithmetic, so both the GPU tests/bench and the fp64 oracle can take
 their inputs from it without sharing any compute code.
 
 Recipe (every config; sizes differ):
+  * grouped prefill: B, C ~ N(0, 1) per (token, group, state); the other
+    tensors as above with A [dim][dstate]
   * attention: q, k, v ~ N(0, 1) per (token, head, feature), rounded to bf16;
     RoPE tables cos/sin of p * 10000^(-2c / head_dim) (the layer's fixed
     parameter, computed in float64 and handed to both sides: fp64 to the
@@ -107,6 +109,9 @@ WORKLOADS = {
                 extra={"heads": 24, "head_dim": 128, "window": 2048}),
     7: Workload(7, "swa_decode B64 H24 hd128 w2048 cache 2049 bf16", 64, 1, 3072,
                 extra={"heads": 24, "head_dim": 128, "window": 2048, "cache_len": 2049, "pos": 4096}),
+    # grouped selection with a larger state: the training shape with 4 (B, C) groups of 64 states
+    8: Workload(8, "scan_fwd_groups B4 L4096 D4096 G4 N64 bf16", 4, 4096, 4096, dstate=64,
+                extra={"ngroups": 4}),
 }
 
 
@@ -313,3 +318,33 @@ def make_swa_inputs_torch(cfg_id: int, rows: int, heads: int, head_dim: int, dev
 def make_positions_np(cfg_id: int, n: int, lo: int, hi: int) -> np.ndarray:
     """n decode positions drawn uniformly from [lo, hi] (int32)."""
     return _rng(cfg_id, TENSOR_IDS["pos"]).integers(lo, hi + 1, size=n).astype(np.int32)
+
+
+# --------------------------------------------------------------------------- #
+# grouped prefill
+# --------------------------------------------------------------------------- #
+def make_groups_inputs_np(cfg_id: int, rows: int, dim: int, ngroups: int, dstate: int, in_dtype: str = "bf16") -> dict:
+    """x, dt, z [rows][dim], B, C [rows][ngroups][dstate] (device representation and *_f32), params."""
+    out = {}
+    for name, shape in (("x", (rows, dim)), ("z", (rows, dim)), ("dt", (rows, dim)),
+                        ("B", (rows, ngroups, dstate)), ("C", (rows, ngroups, dstate))):
+        v = _normal(cfg_id, name, shape)
+        if in_dtype == "bf16":
+            bits = bf16_bits_from_f32(v)
+            out[name], out[name + "_f32"] = bits, f32_from_bf16_bits(bits)
+        else:
+            out[name], out[name + "_f32"] = v, v
+    out.update(make_params(cfg_id, dim, dstate))
+    return out
+
+
+def make_groups_inputs_torch(cfg_id: int, rows: int, dim: int, ngroups: int, dstate: int, device) -> dict:
+    """Device bf16 x, dt, z [rows][dim], B, C [rows][ngroups][dstate] (+ fp32 params)."""
+    import torch
+    out = {}
+    for name, shape in (("x", (rows, dim)), ("z", (rows, dim)), ("dt", (rows, dim)),
+                        ("B", (rows, ngroups, dstate)), ("C", (rows, ngroups, dstate))):
+        out[name] = _torch_normal(torch, shape, cfg_id, TENSOR_IDS[name], device, torch.bfloat16)
+    for k, v in make_params(cfg_id, dim, dstate).items():
+        out[k] = torch.from_numpy(v).to(device)
+    return out

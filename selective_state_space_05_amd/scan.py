@@ -12,7 +12,7 @@ from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "libsamba_scan.so"
 DSTATE = 16
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 SAMBA_F32, SAMBA_BF16 = 0, 1
 STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE", 3: "SAMBA_ERR_BAD_DTYPE",
@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE"
                 7: "SAMBA_ERR_BAD_STRUCT", 8: "SAMBA_ERR_HIP", 9: "SAMBA_ERR_WORKSPACE"}
 EXPORTED = ("samba_scan_fwd", "samba_scan_step", "samba_scan_fwd_plan", "samba_scan_bwd",
             "samba_scan_bwd_workspace_size", "samba_scan_ckpt_bytes", "samba_proj", "samba_status_string",
-            "samba_scan_abi_version", "samba_rope", "samba_swa_fwd", "samba_swa_decode")
+            "samba_scan_abi_version", "samba_rope", "samba_swa_fwd", "samba_swa_decode", "samba_scan_fwd_groups")
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -57,6 +57,14 @@ class ProjArgs(ctypes.Structure):
                 ("in_dtype", _I32), ("out_dtype", _I32), ("x", _P), ("W", _P), ("dt", _P), ("B", _P), ("C", _P)]
 
 
+class GroupsArgs(ctypes.Structure):
+    """Mirror of samba_scan_groups_args."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("batch", _I32), ("seqlen", _I32), ("dim", _I32),
+                ("dstate", _I32), ("ngroups", _I32), ("cu_seqlens", _P), ("nseq", _I32), ("in_dtype", _I32),
+                ("y_dtype", _I32), ("x", _P), ("dt", _P), ("z", _P), ("B", _P), ("C", _P), ("A", _P), ("D", _P),
+                ("dt_bias", _P), ("h0", _P), ("h_last", _P), ("y", _P)]
+
+
 class SambaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -91,6 +99,8 @@ def load_library(path: Path | str | None = None):
     lib.samba_scan_ckpt_bytes.restype = ctypes.c_int
     lib.samba_proj.argtypes = [ctypes.POINTER(ProjArgs), _P]
     lib.samba_proj.restype = ctypes.c_int
+    lib.samba_scan_fwd_groups.argtypes = [ctypes.POINTER(GroupsArgs), _P]
+    lib.samba_scan_fwd_groups.restype = ctypes.c_int
     lib.samba_status_string.argtypes = [ctypes.c_int]
     lib.samba_status_string.restype = ctypes.c_char_p
     lib.samba_scan_abi_version.restype = ctypes.c_int
@@ -359,3 +369,37 @@ def proj(x, W, *, out_dtype=None, dt=None, B=None, C=None, stream=None):
     if st != 0:
         raise SambaError(st, "samba_proj")
     return dt, B, C
+
+
+def groups_args(x, dt, z, B, C, A, D, dt_bias, *, y, h0=None, h_last=None, cu_seqlens=None) -> GroupsArgs:
+    """Fill a samba_scan_groups_args: B, C [batch][L][G][N] (or [tokens][G][N] packed)."""
+    batch, seqlen, dim, nseq = _seq_shape(x, cu_seqlens)
+    a = GroupsArgs()
+    a.struct_size = ctypes.sizeof(GroupsArgs)
+    a.batch, a.seqlen, a.dim = batch, seqlen, dim
+    a.ngroups, a.dstate = B.shape[-2], B.shape[-1]
+    a.cu_seqlens, a.nseq = _ptr(cu_seqlens), (nseq if cu_seqlens is not None else 0)
+    a.in_dtype, a.y_dtype = _dtype_code(x), _dtype_code(y)
+    a.x, a.dt, a.z, a.B, a.C = _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C)
+    a.A, a.D, a.dt_bias = _ptr(A), _ptr(D), _ptr(dt_bias)
+    a.h0, a.h_last, a.y = _ptr(h0), _ptr(h_last), _ptr(y)
+    return a
+
+
+def scan_fwd_groups(x, dt, z, B, C, A, D, dt_bias, *, h0=None, h_last=None, y=None, y_dtype=None, cu_seqlens=None,
+                    return_last_state: bool = True, stream=None):
+    """Grouped prefill through samba_scan_fwd_groups: B, C [batch][L][G][N] (or [tokens][G][N]); channel d
+    reads group d // (dim // G); N in 16, 32, 64, 128, 256.  Returns (y, h_last)."""
+    import torch
+    _check_dev(x, dt, z, B, C, A, D, dt_bias, h0, h_last, y, cu_seqlens)
+    batch, seqlen, dim, nseq = _seq_shape(x, cu_seqlens)
+    N = B.shape[-1]
+    if y is None:
+        y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
+    if h_last is None and return_last_state:
+        h_last = torch.empty(nseq, dim, N, dtype=torch.float32, device=x.device)
+    a = groups_args(x, dt, z, B, C, A, D, dt_bias, y=y, h0=h0, h_last=h_last, cu_seqlens=cu_seqlens)
+    st = load_library().samba_scan_fwd_groups(ctypes.byref(a), _P(_stream_handle(stream)))
+    if st != 0:
+        raise SambaError(st, "samba_scan_fwd_groups")
+    return y, h_last

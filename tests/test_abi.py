@@ -54,7 +54,8 @@ def test_status_strings(lib):
 
 STRUCTS = (("samba_scan_fwd_args", S.FwdArgs), ("samba_scan_step_args", S.StepArgs),
            ("samba_scan_bwd_args", S.BwdArgs), ("samba_proj_args", S.ProjArgs), ("samba_rope_args", W.RopeArgs),
-           ("samba_swa_fwd_args", W.SwaFwdArgs), ("samba_swa_decode_args", W.SwaDecodeArgs))
+           ("samba_swa_fwd_args", W.SwaFwdArgs), ("samba_swa_decode_args", W.SwaDecodeArgs),
+           ("samba_scan_groups_args", S.GroupsArgs))
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -506,3 +507,50 @@ def test_swa_decode_empty_batch_is_noop(lib):
     a = dec_ok(batch=0)
     a.pos = a.q = a.k = a.v = a.k_cache = a.v_cache = a.o = None
     assert lib.samba_swa_decode(ctypes.byref(a), None) == 0
+
+
+# --------------------------------------------------------------------------- #
+# grouped prefill: validation
+# --------------------------------------------------------------------------- #
+def groups_ok(batch=2, seqlen=100, dim=64, dstate=32, ngroups=2):
+    a = S.GroupsArgs()
+    a.struct_size = ctypes.sizeof(S.GroupsArgs)
+    a.batch, a.seqlen, a.dim, a.dstate, a.ngroups = batch, seqlen, dim, dstate, ngroups
+    a.in_dtype, a.y_dtype = S.SAMBA_BF16, S.SAMBA_BF16
+    a.x, a.dt, a.z, a.B, a.C = BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB, BASE + 4 * GB
+    a.A, a.D, a.dt_bias = BASE + 5 * GB, BASE + 6 * GB, BASE + 7 * GB
+    a.h0, a.h_last, a.y = BASE + 8 * GB, BASE + 9 * GB, BASE + 10 * GB
+    return a
+
+
+GROUPS_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 4), 7),
+    "dstate_24": (lambda a: setattr(a, "dstate", 24), 6),
+    "dstate_8": (lambda a: setattr(a, "dstate", 8), 6),
+    "groups_not_dividing": (lambda a: setattr(a, "ngroups", 3), 2),
+    "group_not_whole_waves": (lambda a: (setattr(a, "dstate", 16), setattr(a, "ngroups", 8)), 2),
+    "zero_groups": (lambda a: setattr(a, "ngroups", 0), 2),
+    "neg_seqlen": (lambda a: setattr(a, "seqlen", -1), 2),
+    "in_dtype": (lambda a: setattr(a, "in_dtype", 4), 3),
+    "null_B": (lambda a: setattr(a, "B", None), 1),
+    "null_A": (lambda a: setattr(a, "A", None), 1),
+    "misaligned_C": (lambda a: setattr(a, "C", a.C + 8), 4),
+    "misaligned_h_last": (lambda a: setattr(a, "h_last", a.h_last + 4), 4),
+    "y_overlaps_B": (lambda a: setattr(a, "y", a.B + 64), 5),
+    "h_last_overlaps_h0_shifted": (lambda a: setattr(a, "h_last", a.h0 + 16), 5),
+    "varlen_batch": (lambda a: (setattr(a, "cu_seqlens", BASE + 11 * GB), setattr(a, "nseq", 3)), 2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GROUPS_CASES))
+def test_groups_rejects(lib, name):
+    a = groups_ok()
+    mutate, code = GROUPS_CASES[name]
+    mutate(a)
+    assert lib.samba_scan_fwd_groups(ctypes.byref(a), None) == code
+
+
+def test_groups_no_sequences_is_noop(lib):
+    a = groups_ok(batch=0)
+    assert lib.samba_scan_fwd_groups(ctypes.byref(a), None) == 0
+    assert lib.samba_scan_fwd_groups(None, None) == 1
