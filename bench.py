@@ -52,6 +52,14 @@ KERNEL_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_scan.hip"
 TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_fwd_step_bwd_proj.json"
 SWA_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_swa.hip"
 SWA_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_swa.json"
+GROUPS_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_scan_groups.hip"
+GROUPS_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_groups.json"
+
+
+def groups_bytes(batch: int, L: int, dim: int, ngroups: int, n: int) -> int:
+    """Algorithmic bytes of one grouped prefill: x, dt, z in and y out (bf16), B and C (bf16), A, D, dt_bias,
+    h_last out."""
+    return batch * L * dim * 4 * 2 + batch * L * ngroups * n * 2 * 2 + dim * n * 4 + dim * 8 + batch * dim * n * 4
 
 
 def visible_keys(L: int, window: int) -> int:
@@ -98,6 +106,22 @@ def kernel_hash() -> str:
 
 def swa_hash() -> str:
     return hashlib.sha256(SWA_SRC.read_bytes()).hexdigest()[:16]
+
+
+def groups_hash() -> str:
+    return hashlib.sha256(GROUPS_SRC.read_bytes()).hexdigest()[:16]
+
+
+def read_groups_traffic():
+    """HBM bytes per launch of the grouped prefill from the committed counter runs, if they were taken on
+    this kernel source."""
+    try:
+        t = json.loads(GROUPS_TRAFFIC_FILE.read_text())
+    except Exception:
+        return None
+    if t.get("kernel_source_sha256_16") != groups_hash():
+        return None
+    return t.get("groups", {}).get("bytes_per_launch")
 
 
 def read_swa_traffic(part: str):
@@ -446,14 +470,14 @@ def bench_groups(steps: int = 10, warmup: int = 3):
     td = Bt * L * D
     slots = groups_slots_per_td(N) * td
     achieved = slots / (ms * 1e-3) / 1e12
-    nbytes = td * 4 * 2 + Bt * L * G * N * 2 * 2 + D * N * 4 + D * 8 + Bt * D * N * 4
+    nbytes = groups_bytes(Bt, L, D, G, N)
     return {"workload": "grouped prefill B=%d L=%d D=%d, %d (B, C) groups of %d states, bf16 I/O, fp32 state"
                         % (Bt, L, D, G, N),
             "steps": steps, "ms_per_call": ms, "tokens_channels_per_s": td / (ms * 1e-3),
             "gbs": nbytes / (ms * 1e-3) / 1e9,
             "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TSLOT, 2),
-                         "unit": "Tslot/s", "frac": round(achieved / VALU_PEAK_TSLOT, 4), "traffic": None,
-                         "kernel": "scan_groups_kernel<bf16,bf16,N=%d>" % N, "launch_us": round(ms * 1e3, 2),
+                         "unit": "Tslot/s", "frac": round(achieved / VALU_PEAK_TSLOT, 4),
+                         "traffic": read_groups_traffic(), "kernel": "scan_groups_kernel<bf16,bf16,N=%d>" % N, "launch_us": round(ms * 1e3, 2),
                          "slots_per_token_channel": groups_slots_per_td(N),
                          "algorithmic_bytes_per_launch": nbytes}}
 
@@ -705,12 +729,14 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
     print(json.dumps(out_d))
 
 
-SWA_PMC_RUN = ("python3 <repo>/bench.py --swa-only --swa-steps 2 --swa-decode-steps 2 --warmup 1 --copy-probe")
+SWA_PMC_RUN = "python3 <repo>/bench.py --swa-only --swa-steps 2 --swa-decode-steps 2 --warmup 1 --copy-probe"
+GROUPS_PMC_RUN = "python3 <repo>/bench.py --groups-only --groups-steps 2 --warmup 1 --copy-probe"
 
 
-def pmc_summary_swa(fetch_dir: str, write_dir: str, out: str):
-    """The attention kernels' HBM bytes per launch from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of
-    SWA_PMC_RUN, calibrated by the 512 MiB copy of the same run (as pmc_summary does for the scan)."""
+def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
+    """HBM bytes per launch of the attention kernels (which = "swa") or the grouped prefill ("groups") from
+    two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), each calibrated by the 512 MiB copy of the same run (as
+    pmc_summary does for the scan)."""
     import csv
     import glob
     import statistics
@@ -724,18 +750,29 @@ def pmc_summary_swa(fetch_dir: str, write_dir: str, out: str):
                                 []).append(float(r["Counter_Value"]))
         return vals
 
-    def pick(vals, part, largest=True):
+    def pick(vals, part):
         keys = [k for k in vals if part in k[0]]
         assert keys, part
-        return sorted(keys, key=lambda k: k[1])[-1 if largest else 0]
+        return sorted(keys, key=lambda k: k[1])[-1]   # the largest launch of that kernel
 
     from selective_state_space_05_amd import inputs as I
-    wl6, wl7 = I.WORKLOADS[6], I.WORKLOADS[7]
-    B, L, H, hd, w = wl6.batch, wl6.seqlen, wl6.extra["heads"], wl6.extra["head_dim"], wl6.extra["window"]
-    Bd, Hd, hdd, wd = wl7.batch, wl7.extra["heads"], wl7.extra["head_dim"], wl7.extra["window"]
-    sel = {"prefill": ("swa_fwd_kernel<unsigned short>", True, 4 * B * L * H * hd * 2),
-           "rope_prefill": ("rope_kernel<true, true>", True, 4 * B * L * H * hd * 2 + 2 * L * hd * 4),
-           "decode": ("swa_decode_kernel<unsigned short>", True, swa_decode_bytes(Bd, Hd, hdd, wd))}
+    if which == "swa":
+        wl6, wl7 = I.WORKLOADS[6], I.WORKLOADS[7]
+        B, L, H, hd, w = wl6.batch, wl6.seqlen, wl6.extra["heads"], wl6.extra["head_dim"], wl6.extra["window"]
+        Bd, Hd, hdd, wd = wl7.batch, wl7.extra["heads"], wl7.extra["head_dim"], wl7.extra["window"]
+        sel = {"prefill": ("swa_fwd_kernel<unsigned short>", 4 * B * L * H * hd * 2),
+               "rope_prefill": ("rope_kernel<true, true>", 4 * B * L * H * hd * 2 + L * hd * 4),
+               "decode": ("swa_decode_kernel<unsigned short>", swa_decode_bytes(Bd, Hd, hdd, wd))}
+        src_hash, run, flag = swa_hash(), SWA_PMC_RUN, "--pmc-summary-swa"
+        note = ("Algorithmic bytes: prefill q, k, v read once and o written once (the window's re-reads of K and V "
+                "are meant to hit L2); RoPE q, k read and written plus the tables; decode the window's cached K "
+                "and V, the new q, k, v, the cache write and o.")
+    else:
+        wl = I.WORKLOADS[8]
+        Bt, L, D, N, G = wl.batch, wl.seqlen, wl.dim, wl.dstate, wl.extra["ngroups"]
+        sel = {"groups": ("scan_groups_kernel<unsigned short, unsigned short, 64>", groups_bytes(Bt, L, D, G, N))}
+        src_hash, run, flag = groups_hash(), GROUPS_PMC_RUN, "--pmc-summary-groups"
+        note = "Algorithmic bytes: x, dt, z read and y written once (bf16), B and C once, parameters, h_last out."
     got = {k: {} for k in sel}
     scales = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -744,25 +781,23 @@ def pmc_summary_swa(fetch_dir: str, write_dir: str, out: str):
         big = min(v for v in copy if v > 0.25 * max(copy))
         scale = (512 << 20) / 1024.0 / big
         scales[counter] = {"copy_raw_kib_per_dispatch": big, "scale": scale}
-        for name, (part, largest, _) in sel.items():
-            key = pick(vals, part, largest)
+        for name, (part, _) in sel.items():
+            key = pick(vals, part)
             kib = statistics.median(vals[key])
             got[name][counter] = {"kernel": key[0][:120], "grid": key[1], "raw_kib_per_dispatch": kib,
                                   "bytes": kib * scale * 1024.0}
-    out_d = {"kernel_source_sha256_16": swa_hash(), "unit": "bytes per launch", "calibration": scales}
-    for name, (_, _, algorithmic) in sel.items():
+    out_d = {"kernel_source_sha256_16": src_hash, "unit": "bytes per launch", "calibration": scales}
+    for name, (_, algorithmic) in sel.items():
         f, wr = got[name]["FETCH_SIZE"]["bytes"], got[name]["WRITE_SIZE"]["bytes"]
         out_d[name] = {"kernel": got[name]["FETCH_SIZE"]["kernel"], "grid": got[name]["FETCH_SIZE"]["grid"],
                        "fetch_bytes": f, "write_bytes": wr, "bytes_per_launch": f + wr,
                        "algorithmic_bytes_per_launch": algorithmic}
     out_d["command"] = [
-        f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {SWA_PMC_RUN}",
-        f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {SWA_PMC_RUN}",
-        f"python bench.py --pmc-summary-swa {fetch_dir} {write_dir} {out}",
+        f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {run}",
+        f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {run}",
+        f"python bench.py {flag} {fetch_dir} {write_dir} {out}",
     ]
-    out_d["note"] = ("Algorithmic bytes: prefill q, k, v read once and o written once (the window's re-reads of K "
-                     "and V are meant to hit L2); RoPE q, k read and written plus the tables; decode the window's "
-                     "cached K and V, the new q, k, v, the cache write and o.")
+    out_d["note"] = note
     Path(out).write_text(json.dumps(out_d, indent=1) + "\n")
     print(json.dumps(out_d))
 
@@ -917,12 +952,17 @@ def main():
                     help="summarise two rocprofv3 counter runs into OUT (host only; no GPU work)")
     ap.add_argument("--pmc-summary-swa", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="the same for the attention kernels (counter runs of the --swa-only legs)")
+    ap.add_argument("--pmc-summary-groups", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="the same for the grouped prefill (counter runs of the --groups-only leg)")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
         return
     if args.pmc_summary_swa:
-        pmc_summary_swa(*args.pmc_summary_swa)
+        _counter_summary(*args.pmc_summary_swa, which="swa")
+        return
+    if args.pmc_summary_groups:
+        _counter_summary(*args.pmc_summary_groups, which="groups")
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1",
@@ -930,7 +970,10 @@ def main():
         sys.exit(2)
 
     if args.groups_only:
-        print(json.dumps({"groups": bench_groups(args.groups_steps, min(args.warmup, 3))}), flush=True)
+        out = {"groups": bench_groups(args.groups_steps, min(args.warmup, 3))}
+        if args.copy_probe:
+            copy_probe()
+        print(json.dumps(out), flush=True)
         return
     if args.swa_only:
         out = {"attention": bench_swa(args.swa_steps, min(args.warmup, 5)),

@@ -120,7 +120,15 @@ struct GParams {
   void* y;
   const int32_t* cu;
   int32_t nseq, seqlen, dim, ngroups, total;
+  int32_t ntiles;   // channel tiles (4 waves' channels) per sequence; the grid is ntiles x nseq
 };
+
+// Block index -> logical index such that consecutive logical blocks land on the same XCD (the dispatcher
+// deals blocks round-robin over the 8 XCDs).  A bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int q = n >> 3, r = n & 7, xcd = bid & 7, slot = bid >> 3;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
 
 template <typename Tin, typename Tout, int N>
 __global__ __launch_bounds__(64 * kWaves) void scan_groups_kernel(GParams p) {
@@ -136,9 +144,13 @@ __global__ __launch_bounds__(64 * kWaves) void scan_groups_kernel(GParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ch0 = (blockIdx.x * kWaves + wave) * CPW;
+  // (channel tile, sequence) of this workgroup: consecutive tiles of a sequence on one XCD, so that its L2
+  // assembles whole lines of x, dt, z and y from the few bytes per token each wave touches
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int s = logical / p.ntiles;
+  const int tile = logical - s * p.ntiles;
+  const int ch0 = (tile * kWaves + wave) * CPW;
   if (ch0 >= p.dim) return;               // a whole wave past the last channel
-  const int s = blockIdx.y;
   int64_t t0;
   int32_t len;
   if (p.cu) {
@@ -327,7 +339,7 @@ extern "C" samba_status samba_scan_fwd_groups(const samba_scan_groups_args* a, v
   }
   const int64_t tokens = static_cast<int64_t>(a->batch) * a->seqlen;
   if (nseq == 0) return SAMBA_OK;
-  if (nseq > 65535 || static_cast<int64_t>(a->dim) * a->ngroups * N > (int64_t{1} << 28)) return SAMBA_ERR_BAD_SHAPE;
+  if (static_cast<int64_t>(a->dim) * a->ngroups * N > (int64_t{1} << 28)) return SAMBA_ERR_BAD_SHAPE;
   if (static_cast<int64_t>(a->seqlen) * a->dim * 4 >= (int64_t{1} << 32)) return SAMBA_ERR_BAD_SHAPE;
   if (!a->A || !a->D || !a->dt_bias) return SAMBA_ERR_NULL_ARG;
   if (tokens > 0 && (!a->x || !a->dt || !a->z || !a->B || !a->C || !a->y)) return SAMBA_ERR_NULL_ARG;
@@ -360,7 +372,9 @@ extern "C" samba_status samba_scan_fwd_groups(const samba_scan_groups_args* a, v
   p.ngroups = a->ngroups;
   p.total = a->seqlen;
   const int cpb = kWaves * (256 / N);
-  const dim3 grid(static_cast<uint32_t>((a->dim + cpb - 1) / cpb), static_cast<uint32_t>(nseq));
+  p.ntiles = (a->dim + cpb - 1) / cpb;
+  if (static_cast<int64_t>(p.ntiles) * nseq > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.ntiles) * nseq));
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (a->in_dtype == SAMBA_BF16)
