@@ -112,16 +112,16 @@ def groups_hash() -> str:
     return hashlib.sha256(GROUPS_SRC.read_bytes()).hexdigest()[:16]
 
 
-def read_groups_traffic():
-    """HBM bytes per launch of the grouped prefill from the committed counter runs, if they were taken on
-    this kernel source."""
+def read_groups_traffic(part: str = "groups"):
+    """HBM bytes per launch of the grouped prefill ("groups") or decode step ("decode") from the committed
+    counter runs, if they were taken on this kernel source."""
     try:
         t = json.loads(GROUPS_TRAFFIC_FILE.read_text())
     except Exception:
         return None
     if t.get("kernel_source_sha256_16") != groups_hash():
         return None
-    return t.get("groups", {}).get("bytes_per_launch")
+    return t.get(part, {}).get("bytes_per_launch")
 
 
 def read_swa_traffic(part: str):
@@ -482,6 +482,43 @@ def bench_groups(steps: int = 10, warmup: int = 3):
                          "algorithmic_bytes_per_launch": nbytes}}
 
 
+def bench_groups_step(steps: int = 200, warmup: int = 20):
+    """samba_scan_step_groups on 64 sequences x D 4096 with 4 groups of 64 states (state 64 MiB read and
+    written per step); the state comes from random values of a prefill's scale."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import scan as S
+
+    wl = I.WORKLOADS[8]
+    Bt, D, N, G = 64, wl.dim, wl.dstate, wl.extra["ngroups"]
+    dev = torch.device("cuda:0")
+    t = I.make_groups_inputs_torch(18, Bt, D, G, N, dev)
+    state = torch.from_numpy(I.make_h0(18, Bt, D, N, scale=0.5)).to(dev)
+    y = torch.empty(Bt, D, dtype=torch.bfloat16, device=dev)
+    a = S.step_groups_args(state, t["x"], t["dt"], t["z"], t["B"], t["C"], t["A"], t["D"], t["dt_bias"], y=y)
+    lib = S.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    ref = ctypes.byref(a)
+
+    def call():
+        if lib.samba_scan_step_groups(ref, sh) != 0:
+            raise RuntimeError("samba_scan_step_groups failed")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = _timed(call, steps, stream)
+    nbytes = Bt * D * N * 4 * 2 + Bt * D * 4 * 2 + Bt * G * N * 2 * 2 + D * N * 4 + D * 8
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "grouped decode step: batch %d, D %d, %d groups of %d states, bf16 I/O" % (Bt, D, G, N),
+            "steps": steps, "us_per_step": ms * 1e3, "gbs": gbs,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_groups_traffic("decode"),
+                         "kernel": "step_groups_kernel<bf16,bf16,N=%d>" % N, "launch_us": round(ms * 1e3, 2),
+                         "algorithmic_bytes_per_launch": nbytes}}
+
+
 def cpu_baseline_groups(seqs: int = 1, channels: int = 512):
     """The fp64 oracle's grouped prefill on one sequence of the same shape, `channels` channels (128 per
     group), in token·channels/s."""
@@ -730,7 +767,7 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
 
 
 SWA_PMC_RUN = "python3 <repo>/bench.py --swa-only --swa-steps 2 --swa-decode-steps 2 --warmup 1 --copy-probe"
-GROUPS_PMC_RUN = "python3 <repo>/bench.py --groups-only --groups-steps 2 --warmup 1 --copy-probe"
+GROUPS_PMC_RUN = "python3 <repo>/bench.py --groups-only --groups-steps 2 --warmup 1 --copy-probe"  # 2 + 1 prefill calls, 220 steps
 
 
 def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
@@ -770,9 +807,12 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
     else:
         wl = I.WORKLOADS[8]
         Bt, L, D, N, G = wl.batch, wl.seqlen, wl.dim, wl.dstate, wl.extra["ngroups"]
-        sel = {"groups": ("scan_groups_kernel<unsigned short, unsigned short, 64>", groups_bytes(Bt, L, D, G, N))}
+        sel = {"groups": ("scan_groups_kernel<unsigned short, unsigned short, 64>", groups_bytes(Bt, L, D, G, N)),
+               "decode": ("step_groups_kernel<unsigned short, unsigned short, 64>",
+                          64 * D * N * 8 + 64 * D * 8 + 64 * G * N * 4 + D * N * 4 + D * 8)}
         src_hash, run, flag = groups_hash(), GROUPS_PMC_RUN, "--pmc-summary-groups"
-        note = "Algorithmic bytes: x, dt, z read and y written once (bf16), B and C once, parameters, h_last out."
+        note = ("Algorithmic bytes: prefill x, dt, z read and y written once (bf16), B and C once, parameters, "
+                "h_last out; decode step the state read and written, x, dt, z in and y out, B, C, parameters.")
     got = {k: {} for k in sel}
     scales = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -970,7 +1010,7 @@ def main():
         sys.exit(2)
 
     if args.groups_only:
-        out = {"groups": bench_groups(args.groups_steps, min(args.warmup, 3))}
+        out = {"groups": bench_groups(args.groups_steps, min(args.warmup, 3)), "groups_decode": bench_groups_step()}
         if args.copy_probe:
             copy_probe()
         print(json.dumps(out), flush=True)
@@ -1033,6 +1073,7 @@ def main():
         line["backward"]["roofline"]["traffic"] = read_traffic("backward")
     if not args.no_groups:
         line["groups"] = bench_groups(args.groups_steps)
+        line["groups_decode"] = bench_groups_step()
     if not args.no_swa:
         line["attention"] = bench_swa(args.swa_steps)
         line["attention_decode"] = bench_swa_decode(args.swa_decode_steps)

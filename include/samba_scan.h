@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SAMBA_SCAN_ABI_VERSION 6
+#define SAMBA_SCAN_ABI_VERSION 7
 #define SAMBA_DSTATE 16
 
 typedef enum {
@@ -256,6 +256,27 @@ typedef struct {
 
 /* Enqueue a grouped prefill.  See samba_scan_groups_args. */
 samba_status samba_scan_fwd_groups(const samba_scan_groups_args* args, void* stream);
+
+/*
+ * Grouped decode step: samba_scan_step with ngroups (B, C) vectors per token
+ * ([batch][ngroups][dstate]) and 16, 32, 64, 128 or 256 states; state
+ * [batch][dim][dstate] fp32 read and written in place; dim divisible by
+ * ngroups.  Alignment: state and A 16 bytes, others their element size; y
+ * must not overlap the state or any input.
+ */
+typedef struct {
+  uint32_t struct_size;        /* = sizeof(samba_scan_step_groups_args) */
+  int32_t batch, dim, dstate, ngroups;
+  int32_t in_dtype, y_dtype;
+  float* state;                /* [batch][dim][dstate], in place */
+  const void *x, *dt, *z;      /* [batch][dim] */
+  const void *B, *C;           /* [batch][ngroups][dstate] */
+  const float *A, *D, *dt_bias;
+  void* y;                     /* [batch][dim] */
+} samba_scan_step_groups_args;
+
+/* Enqueue one grouped decode step.  See samba_scan_step_groups_args. */
+samba_status samba_scan_step_groups(const samba_scan_step_groups_args* args, void* stream);
 
 /* Enqueue a prefill scan.  See samba_scan_fwd_args. */
 samba_status samba_scan_fwd(const samba_scan_fwd_args* args, void* stream);

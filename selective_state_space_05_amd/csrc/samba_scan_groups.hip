@@ -298,6 +298,78 @@ __global__ __launch_bounds__(64 * kWaves) void scan_groups_kernel(GParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped decode step: one token per sequence, state [batch][dim][N] read and written in place.  Lanes as
+// in the prefill (N/4 per channel, 4 states each); the per-token scalars are recomputed by each of the
+// channel's lanes (the step streams the state: N * 8 bytes per channel against ~20 issue slots of scalars).
+// ---------------------------------------------------------------------------
+struct SParams {
+  float* state;
+  const void *x, *dt, *z, *B, *C;
+  const float *A, *Dskip, *bias;
+  void* y;
+  int32_t batch, dim, ngroups;
+};
+
+template <typename Tin, typename Tout, int N>
+__global__ __launch_bounds__(256) void step_groups_kernel(SParams p) {
+  constexpr int LPC = N / 4, CPB = 256 / LPC;   // lanes per channel, channels per workgroup
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * CPB + threadIdx.x / LPC;   // (sequence, channel)
+  const int sub = threadIdx.x % LPC;
+  const int64_t total = static_cast<int64_t>(p.batch) * p.dim;
+  const bool live = item < total;
+  const int64_t it = live ? item : total - 1;   // dead lanes mirror the last item (reads only)
+  const int b = static_cast<int>(it / p.dim), d = static_cast<int>(it - static_cast<int64_t>(b) * p.dim);
+  const int g = d / (p.dim / p.ngroups);
+  const float xv = widen(static_cast<const Tin*>(p.x)[it]);
+  const float delta = softplus_f32(widen(static_cast<const Tin*>(p.dt)[it]) + p.bias[d]);
+  const float zv = widen(static_cast<const Tin*>(p.z)[it]);
+  const int64_t bc = (static_cast<int64_t>(b) * p.ngroups + g) * N + 4 * sub;
+  float bb[4], cc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bb[i] = widen(static_cast<const Tin*>(p.B)[bc + i]);
+    cc[i] = widen(static_cast<const Tin*>(p.C)[bc + i]);
+  }
+  const float4 av = reinterpret_cast<const float4*>(p.A + static_cast<int64_t>(d) * N)[sub];
+  float4* sp = reinterpret_cast<float4*>(p.state + it * N) + sub;
+  const float4 hv = *sp;
+  const float a[4] = {av.x, av.y, av.z, av.w};
+  float h[4] = {hv.x, hv.y, hv.z, hv.w};
+  const float u = delta * xv;
+  float pr = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = fmaf(__builtin_amdgcn_exp2f(delta * a[i] * kLog2e), h[i], u * bb[i]);
+    pr = fmaf(cc[i], h[i], pr);
+  }
+  const float r = group_sum<LPC>(pr);
+  if (live) {
+    *sp = make_float4(h[0], h[1], h[2], h[3]);
+    if (sub == 0) {
+      const float yv = (r + p.Dskip[d] * xv) * silu_f32(zv);
+      if constexpr (sizeof(Tout) == 2)
+        static_cast<uint16_t*>(p.y)[it] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(yv));
+      else
+        static_cast<float*>(p.y)[it] = yv;
+    }
+  }
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_step_groups(const SParams& p, int dstate, hipStream_t s) {
+  const int64_t lanes = static_cast<int64_t>(p.batch) * p.dim * (dstate / 4);
+  const dim3 grid(static_cast<uint32_t>((lanes + 255) / 256)), block(256);
+  switch (dstate) {
+    case 16: hipLaunchKernelGGL((step_groups_kernel<Tin, Tout, 16>), grid, block, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((step_groups_kernel<Tin, Tout, 32>), grid, block, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((step_groups_kernel<Tin, Tout, 64>), grid, block, 0, s, p); break;
+    case 128: hipLaunchKernelGGL((step_groups_kernel<Tin, Tout, 128>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((step_groups_kernel<Tin, Tout, 256>), grid, block, 0, s, p); break;
+  }
+  return hipGetLastError();
+}
+
 bool aligned(const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) & (a - 1)) == 0; }
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
@@ -383,5 +455,48 @@ extern "C" samba_status samba_scan_fwd_groups(const samba_scan_groups_args* a, v
   else
     e = a->y_dtype == SAMBA_BF16 ? launch_groups<float, uint16_t>(p, N, grid, s)
                                  : launch_groups<float, float>(p, N, grid, s);
+  return e == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
+}
+
+extern "C" samba_status samba_scan_step_groups(const samba_scan_step_groups_args* a, void* stream) {
+  if (!a) return SAMBA_ERR_NULL_ARG;
+  if (a->struct_size != sizeof(samba_scan_step_groups_args)) return SAMBA_ERR_BAD_STRUCT;
+  if (a->batch < 0 || a->dim < 1 || a->ngroups < 1) return SAMBA_ERR_BAD_SHAPE;
+  const int N = a->dstate;
+  if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256) return SAMBA_ERR_UNSUPPORTED;
+  if (a->in_dtype != SAMBA_F32 && a->in_dtype != SAMBA_BF16) return SAMBA_ERR_BAD_DTYPE;
+  if (a->y_dtype != SAMBA_F32 && a->y_dtype != SAMBA_BF16) return SAMBA_ERR_BAD_DTYPE;
+  if (a->dim % a->ngroups != 0) return SAMBA_ERR_BAD_SHAPE;
+  if (static_cast<int64_t>(a->batch) * a->dim * (N / 4) > (int64_t{1} << 38)) return SAMBA_ERR_BAD_SHAPE;
+  if (a->batch == 0) return SAMBA_OK;
+  if (!a->state || !a->x || !a->dt || !a->z || !a->B || !a->C || !a->A || !a->D || !a->dt_bias || !a->y)
+    return SAMBA_ERR_NULL_ARG;
+  const size_t ie = a->in_dtype == SAMBA_BF16 ? 2 : 4, oe = a->y_dtype == SAMBA_BF16 ? 2 : 4;
+  if (!aligned(a->state, 16) || !aligned(a->A, 16) || !aligned(a->x, ie) || !aligned(a->dt, ie) ||
+      !aligned(a->z, ie) || !aligned(a->B, ie) || !aligned(a->C, ie) || !aligned(a->y, oe) || !aligned(a->D, 4) ||
+      !aligned(a->dt_bias, 4))
+    return SAMBA_ERR_MISALIGNED;
+  const size_t bd = static_cast<size_t>(a->batch) * a->dim;
+  const size_t bc = static_cast<size_t>(a->batch) * a->ngroups * N;
+  const size_t st = bd * N * 4;
+  const void* ins[8] = {a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias};
+  const size_t in_sz[8] = {bd * ie, bd * ie, bd * ie, bc * ie, bc * ie, static_cast<size_t>(a->dim) * N * 4,
+                           static_cast<size_t>(a->dim) * 4, static_cast<size_t>(a->dim) * 4};
+  for (int k = 0; k < 8; ++k)
+    if (overlap(a->state, st, ins[k], in_sz[k]) || overlap(a->y, bd * oe, ins[k], in_sz[k])) return SAMBA_ERR_ALIASING;
+  if (overlap(a->y, bd * oe, a->state, st)) return SAMBA_ERR_ALIASING;
+  SParams p{};
+  p.state = a->state;
+  p.x = a->x; p.dt = a->dt; p.z = a->z; p.B = a->B; p.C = a->C;
+  p.A = a->A; p.Dskip = a->D; p.bias = a->dt_bias; p.y = a->y;
+  p.batch = a->batch; p.dim = a->dim; p.ngroups = a->ngroups;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (a->in_dtype == SAMBA_BF16)
+    e = a->y_dtype == SAMBA_BF16 ? launch_step_groups<uint16_t, uint16_t>(p, N, s)
+                                 : launch_step_groups<uint16_t, float>(p, N, s);
+  else
+    e = a->y_dtype == SAMBA_BF16 ? launch_step_groups<float, uint16_t>(p, N, s)
+                                 : launch_step_groups<float, float>(p, N, s);
   return e == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
 }

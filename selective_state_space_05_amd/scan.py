@@ -12,7 +12,7 @@ from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "libsamba_scan.so"
 DSTATE = 16
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 SAMBA_F32, SAMBA_BF16 = 0, 1
 STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE", 3: "SAMBA_ERR_BAD_DTYPE",
@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE"
                 7: "SAMBA_ERR_BAD_STRUCT", 8: "SAMBA_ERR_HIP", 9: "SAMBA_ERR_WORKSPACE"}
 EXPORTED = ("samba_scan_fwd", "samba_scan_step", "samba_scan_fwd_plan", "samba_scan_bwd",
             "samba_scan_bwd_workspace_size", "samba_scan_ckpt_bytes", "samba_proj", "samba_status_string",
-            "samba_scan_abi_version", "samba_rope", "samba_swa_fwd", "samba_swa_decode", "samba_scan_fwd_groups")
+            "samba_scan_abi_version", "samba_rope", "samba_swa_fwd", "samba_swa_decode", "samba_scan_fwd_groups",
+            "samba_scan_step_groups")
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -65,6 +66,13 @@ class GroupsArgs(ctypes.Structure):
                 ("dt_bias", _P), ("h0", _P), ("h_last", _P), ("y", _P)]
 
 
+class StepGroupsArgs(ctypes.Structure):
+    """Mirror of samba_scan_step_groups_args."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("batch", _I32), ("dim", _I32), ("dstate", _I32),
+                ("ngroups", _I32), ("in_dtype", _I32), ("y_dtype", _I32), ("state", _P), ("x", _P), ("dt", _P),
+                ("z", _P), ("B", _P), ("C", _P), ("A", _P), ("D", _P), ("dt_bias", _P), ("y", _P)]
+
+
 class SambaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -101,6 +109,8 @@ def load_library(path: Path | str | None = None):
     lib.samba_proj.restype = ctypes.c_int
     lib.samba_scan_fwd_groups.argtypes = [ctypes.POINTER(GroupsArgs), _P]
     lib.samba_scan_fwd_groups.restype = ctypes.c_int
+    lib.samba_scan_step_groups.argtypes = [ctypes.POINTER(StepGroupsArgs), _P]
+    lib.samba_scan_step_groups.restype = ctypes.c_int
     lib.samba_status_string.argtypes = [ctypes.c_int]
     lib.samba_status_string.restype = ctypes.c_char_p
     lib.samba_scan_abi_version.restype = ctypes.c_int
@@ -403,3 +413,27 @@ def scan_fwd_groups(x, dt, z, B, C, A, D, dt_bias, *, h0=None, h_last=None, y=No
     if st != 0:
         raise SambaError(st, "samba_scan_fwd_groups")
     return y, h_last
+
+
+def step_groups_args(state, x, dt, z, B, C, A, D, dt_bias, *, y) -> StepGroupsArgs:
+    a = StepGroupsArgs()
+    a.struct_size = ctypes.sizeof(StepGroupsArgs)
+    a.batch, a.dim = x.shape
+    a.ngroups, a.dstate = B.shape[-2], B.shape[-1]
+    a.in_dtype, a.y_dtype = _dtype_code(x), _dtype_code(y)
+    a.state, a.x, a.dt, a.z, a.B, a.C = _ptr(state), _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C)
+    a.A, a.D, a.dt_bias, a.y = _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(y)
+    return a
+
+
+def scan_step_groups(state, x, dt, z, B, C, A, D, dt_bias, *, y=None, y_dtype=None, stream=None):
+    """Grouped decode step through samba_scan_step_groups: x, dt, z [batch][dim]; B, C [batch][G][N]; state
+    [batch][dim][N] fp32 updated in place.  Returns y [batch][dim]."""
+    import torch
+    _check_dev(state, x, dt, z, B, C, A, D, dt_bias, y)
+    y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device) if y is None else y
+    a = step_groups_args(state, x, dt, z, B, C, A, D, dt_bias, y=y)
+    st = load_library().samba_scan_step_groups(ctypes.byref(a), _P(_stream_handle(stream)))
+    if st != 0:
+        raise SambaError(st, "samba_scan_step_groups")
+    return y

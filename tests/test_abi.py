@@ -55,7 +55,7 @@ def test_status_strings(lib):
 STRUCTS = (("samba_scan_fwd_args", S.FwdArgs), ("samba_scan_step_args", S.StepArgs),
            ("samba_scan_bwd_args", S.BwdArgs), ("samba_proj_args", S.ProjArgs), ("samba_rope_args", W.RopeArgs),
            ("samba_swa_fwd_args", W.SwaFwdArgs), ("samba_swa_decode_args", W.SwaDecodeArgs),
-           ("samba_scan_groups_args", S.GroupsArgs))
+           ("samba_scan_groups_args", S.GroupsArgs), ("samba_scan_step_groups_args", S.StepGroupsArgs))
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -554,3 +554,39 @@ def test_groups_no_sequences_is_noop(lib):
     a = groups_ok(batch=0)
     assert lib.samba_scan_fwd_groups(ctypes.byref(a), None) == 0
     assert lib.samba_scan_fwd_groups(None, None) == 1
+
+
+def step_groups_ok(batch=4, dim=64, dstate=64, ngroups=4):
+    a = S.StepGroupsArgs()
+    a.struct_size = ctypes.sizeof(S.StepGroupsArgs)
+    a.batch, a.dim, a.dstate, a.ngroups = batch, dim, dstate, ngroups
+    a.in_dtype, a.y_dtype = S.SAMBA_BF16, S.SAMBA_F32
+    a.state, a.x, a.dt, a.z, a.B, a.C = BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB, BASE + 4 * GB, BASE + 5 * GB
+    a.A, a.D, a.dt_bias, a.y = BASE + 6 * GB, BASE + 7 * GB, BASE + 8 * GB, BASE + 9 * GB
+    return a
+
+
+STEP_GROUPS_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 4), 7),
+    "dstate_48": (lambda a: setattr(a, "dstate", 48), 6),
+    "groups_not_dividing": (lambda a: setattr(a, "ngroups", 3), 2),
+    "neg_batch": (lambda a: setattr(a, "batch", -2), 2),
+    "y_dtype": (lambda a: setattr(a, "y_dtype", 9), 3),
+    "null_state": (lambda a: setattr(a, "state", None), 1),
+    "misaligned_state": (lambda a: setattr(a, "state", a.state + 8), 4),
+    "y_overlaps_state": (lambda a: setattr(a, "y", a.state + 64), 5),
+    "state_overlaps_B": (lambda a: setattr(a, "state", a.B), 5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STEP_GROUPS_CASES))
+def test_step_groups_rejects(lib, name):
+    a = step_groups_ok()
+    mutate, code = STEP_GROUPS_CASES[name]
+    mutate(a)
+    assert lib.samba_scan_step_groups(ctypes.byref(a), None) == code
+
+
+def test_step_groups_empty_batch_is_noop(lib):
+    a = step_groups_ok(batch=0)
+    assert lib.samba_scan_step_groups(ctypes.byref(a), None) == 0

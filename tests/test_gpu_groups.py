@@ -132,3 +132,35 @@ def test_groups_full_shape_sampled():
             check_bf16_y(host(y[s, :, sl]), yo, "y s%d g%d" % (s, g))
             check_fp32(host(hl[s, sl]), ho[0], "h_last s%d g%d" % (s, g))
     say("  ok")
+
+
+@pytest.mark.parametrize("N,G,din,dout", [(16, 2, "bf16", "f32"), (64, 4, "bf16", "bf16"), (256, 1, "f32", "f32")])
+def test_step_groups_continues_prefill(N, G, din, dout):
+    """Prefill 30 tokens, then 5 grouped decode steps from its h_last: each step against the oracle's grouped
+    prefill over the whole sequence (its row for that token; the final state against its h_last)."""
+    say("case: step groups N%d G%d %s %s" % (N, G, din, dout))
+    Bt, L, steps, dim = 3, 30, 5, 64
+    n = L + steps
+    inp = I.make_groups_inputs_np(12, Bt * n, dim, G, N, in_dtype=din)
+    view = lambda k, shape: dev(inp[k], din).reshape(shape)
+    x, dt, z = (view(k, (Bt, n, dim)) for k in ("x", "dt", "z"))
+    B, C = (view(k, (Bt, n, G, N)) for k in ("B", "C"))
+    A, D, bias = (torch.from_numpy(inp[k]).to(DEV) for k in ("A", "D", "dt_bias"))
+    _, state = S.scan_fwd_groups(x[:, :L].contiguous(), dt[:, :L].contiguous(), z[:, :L].contiguous(),
+                                 B[:, :L].contiguous(), C[:, :L].contiguous(), A, D, bias)
+    od = torch.float32 if dout == "f32" else torch.bfloat16
+    ys = []
+    for t in range(L, n):
+        ys.append(S.scan_step_groups(state, x[:, t].contiguous(), dt[:, t].contiguous(), z[:, t].contiguous(),
+                                     B[:, t].contiguous(), C[:, t].contiguous(), A, D, bias, y_dtype=od))
+    torch.cuda.synchronize()
+    f = lambda k, shape: inp[k + "_f32"].reshape(shape)
+    yo, ho = O.scan_fwd_groups(f("x", (Bt, n, dim)), f("dt", (Bt, n, dim)), f("z", (Bt, n, dim)),
+                               f("B", (Bt, n, G, N)), f("C", (Bt, n, G, N)), inp["A"], inp["D"], inp["dt_bias"])
+    g = np.stack([host(y) for y in ys], axis=1)            # [Bt][steps][dim]
+    for b in range(Bt):
+        if dout == "f32":
+            check_fp32(g[b], yo[b, L:], "step y b%d" % b)
+        else:
+            check_bf16_y(g[b], yo[b, L:], "step y b%d" % b)
+        check_fp32(host(state[b]), ho[b], "state b%d" % b)
