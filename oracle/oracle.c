@@ -35,6 +35,9 @@
  * The gradients of the prefill (oracle_scan_bwd) are the reverse-mode
  * derivative of exactly that loop; the formulas stand above the function.
  *
+ * The Mamba-2 form the pages compare with (oracle_ssd: scalar decay per head,
+ * a matrix state per head) is written out the same way, as its recurrence.
+ *
  * The other layer of the hybrid, sliding-window attention (oracle_swa), is
  * the definition written out per query: rotate, score the visible keys,
  * softmax, weight the values (its reading stands above the function).
@@ -459,6 +462,59 @@ int oracle_rope(int64_t T, int64_t H, int64_t hd, const double* x, const int64_t
                   rope_sin + pos[t] * (hd / 2));
   }
   return 0;
+}
+
+/*
+ * State-space duality layer (the Mamba-2 form the pages name for comparison: page 1, 与其他混合架构对比 and
+ * 设计哲学对比, SSD / 数学对偶性).  The pages give no formula; this is the usual definition: per head h a
+ * scalar decay instead of a diagonal one, a state of P x N per head, (B, C) shared by the heads of a group.
+ *   Δ_t = softplus(dt[t][h] + dt_bias[h]),  a_t = exp(Δ_t A[h])                      (A[h] < 0)
+ *   H_t[p][n] = a_t H_{t-1}[p][n] + Δ_t x_t[p] B_t[n]                               (outer product)
+ *   y_t[p] = (sum_n H_t[p][n] C_t[n] + D[h] x_t[p]) * silu(z_t[p])    (no gate when z is NULL)
+ * x, z, y [T][H][P]; dt [T][H]; B, C [T][G][N] with head h reading group h / (H / G); A, D, dt_bias [H];
+ * h0, h_last [nseq][H][P][N].  Each (sequence, head) is one sequential loop over its tokens.
+ */
+int oracle_ssd(int64_t nseq, const int64_t* seq_start, int64_t H, int64_t P, int64_t N, int64_t G,
+               const double* x, const double* dt, const double* z, const double* B, const double* C,
+               const double* A, const double* D, const double* dt_bias, const double* h0, double* y,
+               double* h_last, int nthreads) {
+  if (nseq < 0 || H < 1 || P < 1 || N < 1 || G < 1 || H % G != 0 || !seq_start) return -1;
+  for (int64_t s = 0; s < nseq; ++s)
+    if (seq_start[s + 1] < seq_start[s]) return -1;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+#endif
+  for (int64_t s = 0; s < nseq; ++s) {
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t g = h / (H / G);
+      double* st = (double*)malloc((size_t)(P * N) * sizeof(double));
+      if (!st) { failed = 1; continue; }
+      for (int64_t k = 0; k < P * N; ++k) st[k] = h0 ? h0[(s * H + h) * P * N + k] : 0.0;
+      for (int64_t t = seq_start[s]; t < seq_start[s + 1]; ++t) {
+        const double delta = softplus(dt[t * H + h] + dt_bias[h]);
+        const double a = exp(delta * A[h]);
+        const double* xt = x + (t * H + h) * P;
+        const double* Bt = B + (t * G + g) * N;
+        const double* Ct = C + (t * G + g) * N;
+        for (int64_t p = 0; p < P; ++p) {
+          double acc = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            st[p * N + n] = a * st[p * N + n] + delta * xt[p] * Bt[n];
+            acc += st[p * N + n] * Ct[n];
+          }
+          const double out = acc + D[h] * xt[p];
+          y[(t * H + h) * P + p] = z ? out * silu(z[(t * H + h) * P + p]) : out;
+        }
+      }
+      if (h_last)
+        for (int64_t k = 0; k < P * N; ++k) h_last[(s * H + h) * P * N + k] = st[k];
+      free(st);
+    }
+  }
+  (void)nthreads;
+  return failed ? -1 : 0;
 }
 
 /* Number of OpenMP threads a call with nthreads <= 0 would use. */

@@ -63,6 +63,8 @@ def _bind(lib):
     lib.oracle_rope.restype = ctypes.c_int
     lib.oracle_scan_fwd_groups.argtypes = [I64, P, I64, I64, I64] + [P] * 11 + [ctypes.c_int]
     lib.oracle_scan_fwd_groups.restype = ctypes.c_int
+    lib.oracle_ssd.argtypes = [I64, P, I64, I64, I64, I64] + [P] * 11 + [ctypes.c_int]
+    lib.oracle_ssd.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -269,6 +271,43 @@ def rope(x, rope_cos, rope_sin, positions, lib=None):
     if rc != 0:
         raise RuntimeError("oracle_rope failed (%d)" % rc)
     return out
+
+
+def ssd(x, dt, B, C, A, D, dt_bias, z=None, h0=None, seq_start=None, nthreads: int = 0, lib=None):
+    """State-space duality layer in fp64 (its recurrence).  x [T][H][P] (or [batch][L][H][P]), dt [T][H],
+    B, C [T][G][N], A, D, dt_bias [H], z like x or None, h0 [nseq][H][P][N] or None.
+    Returns (y like x, h_last [nseq][H][P][N])."""
+    lib = lib or load()
+    x = _f64(x)
+    shape = x.shape
+    if x.ndim == 4:
+        b, L, H, P = shape
+        if seq_start is None:
+            seq_start = np.arange(b + 1, dtype=np.int64) * L
+        x = x.reshape(b * L, H, P)
+        dt = _f64(dt).reshape(b * L, H)
+        B, C = _f64(B).reshape(b * L, *np.shape(B)[2:]), _f64(C).reshape(b * L, *np.shape(C)[2:])
+        z = None if z is None else _f64(z).reshape(b * L, H, P)
+    else:
+        H, P = shape[1], shape[2]
+        if seq_start is None:
+            seq_start = np.array([0, shape[0]], dtype=np.int64)
+        dt, B, C = _f64(dt), _f64(B), _f64(C)
+        z = None if z is None else _f64(z)
+    T = x.shape[0]
+    G, N = B.shape[1], B.shape[2]
+    A, D, dt_bias = _f64(A), _f64(D), _f64(dt_bias)
+    seq_start = np.ascontiguousarray(np.asarray(seq_start, dtype=np.int64))
+    nseq = len(seq_start) - 1
+    assert seq_start[0] == 0 and seq_start[-1] == T and dt.shape == (T, H) and C.shape == B.shape == (T, G, N)
+    h0 = None if h0 is None else _f64(h0).reshape(nseq, H, P, N)
+    y = np.empty((T, H, P))
+    h_last = np.empty((nseq, H, P, N))
+    rc = lib.oracle_ssd(nseq, _ptr(seq_start), H, P, N, G, _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C), _ptr(A),
+                        _ptr(D), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_last), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_ssd failed (%d)" % rc)
+    return y.reshape(shape), h_last
 
 
 def scan_step(state, x, dt, z, B, C, A, D, dt_bias, nthreads: int = 0, lib=None):
