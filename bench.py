@@ -54,6 +54,8 @@ SWA_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_swa.hip"
 SWA_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_swa.json"
 GROUPS_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_scan_groups.hip"
 GROUPS_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_groups.json"
+SSD_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_ssd.hip"
+SSD_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_ssd.json"
 
 
 def groups_bytes(batch: int, L: int, dim: int, ngroups: int, n: int) -> int:
@@ -122,6 +124,22 @@ def read_groups_traffic(part: str = "groups"):
     if t.get("kernel_source_sha256_16") != groups_hash():
         return None
     return t.get(part, {}).get("bytes_per_launch")
+
+
+def ssd_hash() -> str:
+    return hashlib.sha256(SSD_SRC.read_bytes()).hexdigest()[:16]
+
+
+def read_ssd_traffic():
+    """HBM bytes per launch of the SSD prefill from the committed counter runs, if they were taken on this
+    kernel source."""
+    try:
+        t = json.loads(SSD_TRAFFIC_FILE.read_text())
+    except Exception:
+        return None
+    if t.get("kernel_source_sha256_16") != ssd_hash():
+        return None
+    return t.get("ssd", {}).get("bytes_per_launch")
 
 
 def read_swa_traffic(part: str):
@@ -539,6 +557,82 @@ def cpu_baseline_groups(seqs: int = 1, channels: int = 512):
     return {"value": L * channels / spent, "unit": "tokens*channels/s", "cores": O.max_threads(lib),
             "kind": "oracle", "sample": "one 4096-token sequence, %d of the 4096 channels (%d per group), fp64 "
                                         "oracle, %.1f s" % (channels, channels // G, spent)}
+
+
+def ssd_bytes(batch: int, L: int, heads: int, hd: int, ngroups: int, n: int) -> int:
+    """Algorithmic bytes of one SSD prefill: x, z read and y written (bf16), dt (bf16), B and C (bf16),
+    A, D, dt_bias, h_last out (fp32)."""
+    T = batch * L
+    return T * heads * hd * 2 * 3 + T * heads * 2 + T * ngroups * n * 2 * 2 + heads * 12 + batch * heads * hd * n * 4
+
+
+def ssd_flops(batch: int, L: int, heads: int, hd: int, n: int, q: int = 64) -> int:
+    """Algorithmic flops of the chunked form per token and head: C Bᵀ (2qn), the masked product with x (2qP),
+    the readout of the entering state (2nP) and the state update (2nP); full chunks, no split operands."""
+    return batch * L * heads * (2 * q * n + 2 * q * hd + 4 * n * hd)
+
+
+def bench_ssd(steps: int = 20, warmup: int = 5):
+    """samba_ssd_fwd on B4 L4096 with 64 heads of 64, one (B, C) group of 128 states, gated, bf16 I/O."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import ssd as SD
+
+    wl = I.WORKLOADS[9]
+    Bt, L, H, P, N, G = (wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.dstate,
+                         wl.extra["ngroups"])
+    dev = torch.device("cuda:0")
+    t = I.make_ssd_inputs_torch(9, Bt * L, H, G, N, dev)
+    x, z = (t[k].view(Bt, L, H, P) for k in ("x", "z"))
+    dt = t["dt"].view(Bt, L, H)
+    B, C = (t[k].view(Bt, L, G, N) for k in ("B", "C"))
+    y = torch.empty_like(x)
+    hl = torch.empty(Bt, H, P, N, dtype=torch.float32, device=dev)
+    a = SD.fwd_args(x, dt, B, C, t["A"], t["D"], t["dt_bias"], y=y, z=z, h_last=hl)
+    lib = SD.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    ref = ctypes.byref(a)
+
+    def call():
+        if lib.samba_ssd_fwd(ref, sh) != 0:
+            raise RuntimeError("samba_ssd_fwd failed")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = _timed(call, steps, stream)
+    nbytes = ssd_bytes(Bt, L, H, P, G, N)
+    flops = ssd_flops(Bt, L, H, P, N)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "SSD prefill B=%d L=%d, %d heads of %d, %d (B, C) group of %d states, gated, bf16 I/O, "
+                        "fp32 state" % (Bt, L, H, P, G, N),
+            "steps": steps, "ms_per_call": ms, "tokens_per_s": Bt * L / (ms * 1e-3), "gbs": gbs,
+            "mfma_tflops": round(tf, 1), "mfma_frac_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_ssd_traffic(),
+                         "kernel": "ssd_fwd_kernel<bf16,N=%d,gate>" % N, "launch_us": round(ms * 1e3, 2),
+                         "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops}}
+
+
+def cpu_baseline_ssd():
+    """The fp64 oracle's SSD recurrence on the whole workload (4 sequences of 4096 tokens, 64 heads), in
+    tokens/s like the GPU leg."""
+    import numpy as np
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+
+    wl = I.WORKLOADS[9]
+    Bt, L, H, N, G = wl.batch, wl.seqlen, wl.extra["heads"], wl.dstate, wl.extra["ngroups"]
+    inp = I.make_ssd_inputs_np(9, Bt * L, H, G, N)
+    lib = O.load()
+    t0 = time.perf_counter()
+    O.ssd(inp["x_f32"], inp["dt_f32"], inp["B_f32"], inp["C_f32"], inp["A"], inp["D"], inp["dt_bias"],
+          z=inp["z_f32"], seq_start=np.arange(Bt + 1, dtype=np.int64) * L, lib=lib)
+    spent = time.perf_counter() - t0
+    return {"value": Bt * L / spent, "unit": "tokens/s", "cores": O.max_threads(lib), "kind": "oracle",
+            "sample": "the whole workload (%d x %d tokens, %d heads), fp64 oracle, %.1f s" % (Bt, L, H, spent)}
 
 
 def bench_swa(steps: int = 20, warmup: int = 5):
@@ -983,6 +1077,9 @@ def main():
     ap.add_argument("--no-groups", action="store_true", help="skip the grouped-prefill leg")
     ap.add_argument("--groups-steps", type=int, default=10)
     ap.add_argument("--groups-only", action="store_true", help="run only the grouped-prefill leg")
+    ap.add_argument("--no-ssd", action="store_true", help="skip the state-space duality leg")
+    ap.add_argument("--ssd-steps", type=int, default=20)
+    ap.add_argument("--ssd-only", action="store_true", help="run only the state-space duality leg")
     ap.add_argument("--swa-only", action="store_true",
                     help="run only the attention legs (and the copy probe with --copy-probe): counter runs")
     ap.add_argument("--time-slices", type=int, default=0, help="force the prefill's waves per time chunk (0 = auto)")
@@ -1011,6 +1108,12 @@ def main():
 
     if args.groups_only:
         out = {"groups": bench_groups(args.groups_steps, min(args.warmup, 3)), "groups_decode": bench_groups_step()}
+        if args.copy_probe:
+            copy_probe()
+        print(json.dumps(out), flush=True)
+        return
+    if args.ssd_only:
+        out = {"ssd": bench_ssd(args.ssd_steps, min(args.warmup, 5))}
         if args.copy_probe:
             copy_probe()
         print(json.dumps(out), flush=True)
@@ -1074,6 +1177,8 @@ def main():
     if not args.no_groups:
         line["groups"] = bench_groups(args.groups_steps)
         line["groups_decode"] = bench_groups_step()
+    if not args.no_ssd:
+        line["ssd"] = bench_ssd(args.ssd_steps)
     if not args.no_swa:
         line["attention"] = bench_swa(args.swa_steps)
         line["attention_decode"] = bench_swa_decode(args.swa_decode_steps)
@@ -1088,6 +1193,8 @@ def main():
             line["cpu_baseline"]["projections"] = cpu_baseline_proj()
         if not args.no_groups:
             line["cpu_baseline"]["groups"] = cpu_baseline_groups()
+        if not args.no_ssd:
+            line["cpu_baseline"]["ssd"] = cpu_baseline_ssd()
         if not args.no_swa:
             line["cpu_baseline"]["attention"] = cpu_baseline_swa()
             line["cpu_baseline"]["attention_decode"] = cpu_baseline_swa_decode()

@@ -1,0 +1,68 @@
+/*
+ * samba_ssd.h -- C ABI of the MI355X (gfx950) state-space duality layer: the
+ * Mamba-2 form that page "SAMBA混合注意力状态空间模型" (metaphor-xennon.pages.dev)
+ * compares Samba with (与其他混合架构对比 and 设计哲学对比: SSD, 状态空间对偶).
+ * The pages name the form and give no formula; this library takes its usual
+ * definition, in the conventions of samba_scan.h:
+ *     Δ_t = softplus(dt[t][h] + dt_bias[h]),  a_t = exp(Δ_t A[h])    (A[h] < 0)
+ *     H_t = a_t H_{t-1} + Δ_t x_t B_tᵀ          (H: head_dim x dstate per head)
+ *     y_t = (H_t C_t + D[h] x_t) * silu(z_t)     (no gate when z is NULL)
+ * i.e. a scalar decay per head (instead of the diagonal A[d][n] of the
+ * selective scan) and a matrix state per head; the (B, C) of group g serve
+ * heads g*heads/ngroups .. (g+1)*heads/ngroups - 1.  With a scalar decay the
+ * prefill is computed in chunks of 64 tokens as dense products on the matrix
+ * cores: inside a chunk y = (L ∘ C Bᵀ) x with the decay mask L, across chunks
+ * through the carried state.
+ *
+ * Layout: x, z, y [tokens][heads][head_dim]; dt [tokens][heads]; B, C
+ * [tokens][ngroups][dstate]; A, D, dt_bias fp32 [heads]; h0, h_last fp32
+ * [nseq][heads][head_dim][dstate].  Tokens: batch * seqlen rows (sequence b
+ * in rows b*seqlen ..), or packed sequences given by cu_seqlens as for
+ * samba_scan_fwd (out-of-range offsets clamped on the device).
+ * Types: x, dt, z, B, C bf16; y bf16 (round to nearest even) or fp32; the
+ * state fp32.  Arithmetic: bf16 products with fp32 accumulation, where every
+ * operand that is not an input (the masked C Bᵀ, the state, the decay-weighted
+ * x) enters as a pair of bf16 values whose sum carries 16 significant bits.
+ * Supported: head_dim 64, dstate 64 or 128, heads a multiple of ngroups.
+ * Alignment: x, B, C, h0, h_last 16 bytes; z 8; y 8 (bf16) or 16 (fp32);
+ * dt 2; A, D, dt_bias 4.  y and h_last must not overlap any input, except
+ * h_last == h0 exactly (the final state written in place over the initial).
+ *
+ * Ownership, asynchrony and errors as for samba_scan.h: device pointers owned
+ * by the caller, nothing allocated or kept, validation before anything is
+ * enqueued, kernels enqueued on `stream` (hipStream_t as void*, NULL = the
+ * default stream), status codes from samba_status.
+ */
+#ifndef SAMBA_SSD_H
+#define SAMBA_SSD_H
+
+#include "samba_scan.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  uint32_t struct_size;        /* = sizeof(samba_ssd_args) */
+  int32_t batch, seqlen;
+  int32_t heads, head_dim, dstate, ngroups;
+  const int32_t* cu_seqlens;   /* optional, device int32 [nseq + 1] (batch must be 1) */
+  int32_t nseq;
+  int32_t y_dtype;             /* samba_dtype of y */
+  const void* x;               /* bf16 [tokens][heads][head_dim] */
+  const void* dt;              /* bf16 [tokens][heads] */
+  const void* z;               /* bf16 [tokens][heads][head_dim], optional */
+  const void *B, *C;           /* bf16 [tokens][ngroups][dstate] */
+  const float *A, *D, *dt_bias;  /* [heads] */
+  const float* h0;             /* optional [nseq][heads][head_dim][dstate] */
+  float* h_last;               /* optional, same shape */
+  void* y;                     /* [tokens][heads][head_dim] */
+} samba_ssd_args;
+
+samba_status samba_ssd_fwd(const samba_ssd_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAMBA_SSD_H */

@@ -112,6 +112,10 @@ WORKLOADS = {
     # grouped selection with a larger state: the training shape with 4 (B, C) groups of 64 states
     8: Workload(8, "scan_fwd_groups B4 L4096 D4096 G4 N64 bf16", 4, 4096, 4096, dstate=64,
                 extra={"ngroups": 4}),
+    # the state-space duality form on the training shape: the inner width 4096 as 64 heads of 64, one
+    # (B, C) group of 128 states
+    9: Workload(9, "ssd_fwd B4 L4096 H64 P64 N128 G1 bf16", 4, 4096, 4096, dstate=128,
+                extra={"heads": 64, "head_dim": 64, "ngroups": 1}),
 }
 
 
@@ -348,3 +352,47 @@ def make_groups_inputs_torch(cfg_id: int, rows: int, dim: int, ngroups: int, dst
     for k, v in make_params(cfg_id, dim, dstate).items():
         out[k] = torch.from_numpy(v).to(device)
     return out
+
+
+# --------------------------------------------------------------------------- #
+# state-space duality layer: per-head parameters, [tokens][heads][head_dim] activations
+# --------------------------------------------------------------------------- #
+def make_ssd_params(cfg_id: int, heads: int) -> dict:
+    """A [heads] = -exp(U(0, log 16)), D [heads] ~ U(0, 1), dt_bias [heads] = log(expm1(U(1e-3, 1e-1)))."""
+    u = _rng(cfg_id, TENSOR_IDS["dt_init"]).uniform(1e-3, 1e-1, size=heads)
+    dt_bias = np.log(np.expm1(u)).astype(np.float32)
+    A = (-np.exp(_rng(cfg_id, TENSOR_IDS["A"]).uniform(0.0, math.log(16.0), size=heads))).astype(np.float32)
+    D = _rng(cfg_id, TENSOR_IDS["D"]).uniform(0.0, 1.0, size=heads).astype(np.float32)
+    return {"A": A, "D": D, "dt_bias": dt_bias}
+
+
+def _ssd_shapes(rows, heads, head_dim, ngroups, dstate):
+    return (("x", (rows, heads, head_dim)), ("z", (rows, heads, head_dim)), ("dt", (rows, heads)),
+            ("B", (rows, ngroups, dstate)), ("C", (rows, ngroups, dstate)))
+
+
+def make_ssd_inputs_np(cfg_id: int, rows: int, heads: int, ngroups: int, dstate: int, head_dim: int = 64) -> dict:
+    """bf16 bits of x, z [rows][heads][head_dim], dt [rows][heads], B, C [rows][ngroups][dstate] (and *_f32,
+    their exact fp32 values), all N(0, 1); params as make_ssd_params."""
+    out = {}
+    for name, shape in _ssd_shapes(rows, heads, head_dim, ngroups, dstate):
+        bits = bf16_bits_from_f32(_normal(cfg_id, name, shape))
+        out[name], out[name + "_f32"] = bits, f32_from_bf16_bits(bits)
+    out.update(make_ssd_params(cfg_id, heads))
+    return out
+
+
+def make_ssd_inputs_torch(cfg_id: int, rows: int, heads: int, ngroups: int, dstate: int, device,
+                          head_dim: int = 64) -> dict:
+    """The same tensors generated on the device (bf16; fp32 params)."""
+    import torch
+    out = {}
+    for name, shape in _ssd_shapes(rows, heads, head_dim, ngroups, dstate):
+        out[name] = _torch_normal(torch, shape, cfg_id, TENSOR_IDS[name], device, torch.bfloat16)
+    for k, v in make_ssd_params(cfg_id, heads).items():
+        out[k] = torch.from_numpy(v).to(device)
+    return out
+
+
+def make_ssd_h0(cfg_id: int, nseq: int, heads: int, dstate: int, head_dim: int = 64, scale: float = 1.0):
+    return (scale * _rng(cfg_id, TENSOR_IDS["h0"]).standard_normal((nseq, heads, head_dim, dstate))).astype(np.float32)

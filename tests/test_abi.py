@@ -12,6 +12,7 @@ from pathlib import Path
 import pytest
 
 from selective_state_space_05_amd import scan as S
+from selective_state_space_05_amd import ssd as D
 from selective_state_space_05_amd import swa as W
 
 ROOT = Path(__file__).resolve().parents[1]
@@ -21,6 +22,7 @@ HEADERS = sorted((ROOT / "include").glob("*.h"))
 
 @pytest.fixture(scope="module")
 def lib():
+    D.load_library()
     return W.load_library()
 
 
@@ -55,13 +57,14 @@ def test_status_strings(lib):
 STRUCTS = (("samba_scan_fwd_args", S.FwdArgs), ("samba_scan_step_args", S.StepArgs),
            ("samba_scan_bwd_args", S.BwdArgs), ("samba_proj_args", S.ProjArgs), ("samba_rope_args", W.RopeArgs),
            ("samba_swa_fwd_args", W.SwaFwdArgs), ("samba_swa_decode_args", W.SwaDecodeArgs),
-           ("samba_scan_groups_args", S.GroupsArgs), ("samba_scan_step_groups_args", S.StepGroupsArgs))
+           ("samba_scan_groups_args", S.GroupsArgs), ("samba_scan_step_groups_args", S.StepGroupsArgs),
+           ("samba_ssd_args", D.SsdArgs))
 
 
 def test_struct_layout_matches_header(tmp_path):
     """Compile a C probe against the header and compare sizeof/offsetof with the ctypes mirrors."""
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "samba_scan.h"', '#include "samba_swa.h"',
-             'int main(void) {']
+             '#include "samba_ssd.h"', 'int main(void) {']
     for cname, py in STRUCTS:
         lines.append('printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
         for f, _ in py._fields_:
@@ -590,3 +593,56 @@ def test_step_groups_rejects(lib, name):
 def test_step_groups_empty_batch_is_noop(lib):
     a = step_groups_ok(batch=0)
     assert lib.samba_scan_step_groups(ctypes.byref(a), None) == 0
+
+
+# --------------------------------------------------------------------------- #
+# state-space duality prefill: validation
+# --------------------------------------------------------------------------- #
+def ssd_ok(batch=2, seqlen=100, heads=8, dstate=128, ngroups=2):
+    a = D.SsdArgs()
+    a.struct_size = ctypes.sizeof(D.SsdArgs)
+    a.batch, a.seqlen, a.heads, a.head_dim, a.dstate, a.ngroups = batch, seqlen, heads, 64, dstate, ngroups
+    a.y_dtype = S.SAMBA_BF16
+    a.x, a.dt, a.z, a.B, a.C = BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB, BASE + 4 * GB
+    a.A, a.D, a.dt_bias = BASE + 5 * GB, BASE + 6 * GB, BASE + 7 * GB
+    a.h0, a.h_last, a.y = BASE + 8 * GB, BASE + 9 * GB, BASE + 10 * GB
+    return a
+
+
+SSD_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 4), 7),
+    "head_dim_128": (lambda a: setattr(a, "head_dim", 128), 6),
+    "dstate_16": (lambda a: setattr(a, "dstate", 16), 6),
+    "dstate_256": (lambda a: setattr(a, "dstate", 256), 6),
+    "groups_not_dividing": (lambda a: setattr(a, "ngroups", 3), 2),
+    "zero_heads": (lambda a: setattr(a, "heads", 0), 2),
+    "neg_seqlen": (lambda a: setattr(a, "seqlen", -1), 2),
+    "y_dtype": (lambda a: setattr(a, "y_dtype", 7), 3),
+    "null_x": (lambda a: setattr(a, "x", None), 1),
+    "null_A": (lambda a: setattr(a, "A", None), 1),
+    "misaligned_x": (lambda a: setattr(a, "x", a.x + 8), 4),
+    "misaligned_z": (lambda a: setattr(a, "z", a.z + 4), 4),
+    "misaligned_h0": (lambda a: setattr(a, "h0", a.h0 + 8), 4),
+    "misaligned_y_f32": (lambda a: (setattr(a, "y_dtype", S.SAMBA_F32), setattr(a, "y", a.y + 8)), 4),
+    "y_overlaps_x": (lambda a: setattr(a, "y", a.x + 128), 5),
+    "y_overlaps_z": (lambda a: setattr(a, "y", a.z), 5),
+    "h_last_overlaps_B": (lambda a: setattr(a, "h_last", a.B + 256), 5),
+    "h_last_overlaps_h0_shifted": (lambda a: setattr(a, "h_last", a.h0 + 16), 5),
+    "varlen_batch": (lambda a: (setattr(a, "cu_seqlens", BASE + 11 * GB), setattr(a, "nseq", 3)), 2),
+    "offsets_past_32_bits": (lambda a: (setattr(a, "seqlen", 1 << 20), setattr(a, "heads", 64),
+                                        setattr(a, "ngroups", 1)), 2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SSD_CASES))
+def test_ssd_rejects(lib, name):
+    a = ssd_ok()
+    mutate, code = SSD_CASES[name]
+    mutate(a)
+    assert lib.samba_ssd_fwd(ctypes.byref(a), None) == code
+
+
+def test_ssd_noops(lib):
+    a = ssd_ok(batch=0)
+    assert lib.samba_ssd_fwd(ctypes.byref(a), None) == 0
+    assert lib.samba_ssd_fwd(None, None) == 1

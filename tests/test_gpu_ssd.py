@@ -1,0 +1,153 @@
+"""GPU parity of the state-space duality prefill (samba_ssd_fwd through the C ABI) against the fp64 oracle
+(oracle_ssd, pinned in tests/test_oracle_ssd_pins.py).
+
+Tolerance reading as for the selective scan (tests/parity.py): fp32 outputs per sequence within the 2e-3
+contract and the 1e-4 tripwire, bf16 y one bf16 rounding on top per (sequence, channel).  The tripwire holds
+because every operand the kernel builds (the masked C Bᵀ, the state, the decay-weighted x) enters the bf16
+products as a hi + lo pair carrying 16 significant bits: a numpy model of the chunked products gives about
+4e-6 of the output's scale with the pairs and 2e-3 without them.
+
+Cases: both state sizes, fp32 and bf16 y, with and without gate, h0 given and h_last written in place over
+it, a ragged last chunk, one-token and one-chunk sequences, packed sequences with empty ones, batched rows,
+a slowly decaying head (long memory), a call chained through h_last, determinism, and the benchmark's shape
+(B4 L4096 H64 P64 N128 G1) on sampled (sequence, head) pairs.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from selective_state_space_05_amd import inputs as I
+from selective_state_space_05_amd import ssd as S
+from tests.parity import check_bf16_y, check_fp32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+CASES = [
+    # lengths, heads, G, N, y dtype, gate, h0
+    ((200,), 4, 2, 64, "f32", True, True),
+    ((200,), 4, 2, 128, "bf16", False, False),
+    ((130, 130, 130), 2, 1, 128, "f32", True, True),      # batched rows
+    ((0, 70, 1, 0, 129), 2, 2, 64, "f32", True, True),   # packed, with empty sequences
+    ((64,), 2, 1, 128, "bf16", True, False),              # exactly one chunk
+    ((1, 1), 2, 2, 64, "f32", True, True),                # one token each (batched)
+    ((333,), 6, 3, 128, "f32", False, True),
+]
+
+
+def run_case(lengths, heads, G, N, yd, gate, with_h0, cfg=9, params=None):
+    T = sum(lengths)
+    nseq = len(lengths)
+    inp = I.make_ssd_inputs_np(cfg, T, heads, G, N)
+    if params:
+        inp.update(params)
+    h0 = I.make_ssd_h0(cfg, nseq, heads, N, scale=0.5) if with_h0 else None
+    packed = len(set(lengths)) > 1 or 0 in lengths
+    x, z, dt, B, C = (bf16_dev(inp[k]) for k in ("x", "z", "dt", "B", "C"))
+    A, D, bias = (torch.from_numpy(np.asarray(inp[k], dtype=np.float32)).to(DEV) for k in ("A", "D", "dt_bias"))
+    od = torch.float32 if yd == "f32" else torch.bfloat16
+    h0d = None if h0 is None else torch.from_numpy(h0).to(DEV)
+    cu = torch.from_numpy(I.cu_from_lengths(lengths)).to(DEV) if packed else None
+    if not packed:
+        L = lengths[0]
+        x, z = (t.reshape(nseq, L, heads, 64) for t in (x, z))
+        dt = dt.reshape(nseq, L, heads)
+        B, C = (t.reshape(nseq, L, G, N) for t in (B, C))
+    y, hl = S.ssd_fwd(x, dt, B, C, A, D, bias, z=z if gate else None, h0=h0d, h_last=h0d, y_dtype=od,
+                      cu_seqlens=cu)
+    torch.cuda.synchronize()
+    bounds = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    yo, ho = O.ssd(inp["x_f32"], inp["dt_f32"], inp["B_f32"], inp["C_f32"], inp["A"], inp["D"], inp["dt_bias"],
+                   z=inp["z_f32"] if gate else None, h0=h0, seq_start=bounds)
+    return host(y).reshape(T, heads * 64), yo.reshape(T, heads * 64), host(hl), ho, bounds
+
+
+def check(y, yo, hl, ho, b, yd):
+    ey = check_fp32(y, yo, "y", b) if yd == "f32" else check_bf16_y(y, yo, "y", b)
+    eh = 0.0
+    for s in range(len(b) - 1):
+        eh = max(eh, check_fp32(hl[s], ho[s], "h_last s%d" % s))
+    say("  y %.2e h_last %.2e" % (ey, eh))
+
+
+@pytest.mark.parametrize("lengths,heads,G,N,yd,gate,with_h0", CASES)
+def test_ssd_matches_oracle(lengths, heads, G, N, yd, gate, with_h0):
+    say("case: ssd", lengths, "heads", heads, "G", G, "N", N, yd, "gate" if gate else "", "h0" if with_h0 else "")
+    y, yo, hl, ho, b = run_case(lengths, heads, G, N, yd, gate, with_h0)
+    check(y, yo, hl, ho, b, yd)
+
+
+def test_ssd_long_memory():
+    """Decays close to 1 (A = -0.02 and -0.5, Δ up to 0.1): the carried state dominates the output."""
+    say("case: ssd long memory")
+    params = {"A": np.array([-0.02, -0.5], dtype=np.float32)}
+    y, yo, hl, ho, b = run_case((500,), 2, 1, 128, "f32", True, True, params=params)
+    check(y, yo, hl, ho, b, "f32")
+
+
+def test_ssd_chained_equals_one_pass():
+    """Two calls over 150 + 107 tokens, h_last of the first as h0 of the second, against one call."""
+    say("case: ssd chained")
+    heads, G, N, L1, L2 = 4, 2, 128, 150, 107
+    inp = I.make_ssd_inputs_np(10, L1 + L2, heads, G, N)
+    x, z, dt, B, C = (bf16_dev(inp[k]) for k in ("x", "z", "dt", "B", "C"))
+    A, D, bias = (torch.from_numpy(inp[k]).to(DEV) for k in ("A", "D", "dt_bias"))
+    y, hl = S.ssd_fwd(x, dt, B, C, A, D, bias, z=z, y_dtype=torch.float32)
+    y1, h1 = S.ssd_fwd(x[:L1], dt[:L1], B[:L1], C[:L1], A, D, bias, z=z[:L1], y_dtype=torch.float32)
+    y2, h2 = S.ssd_fwd(x[L1:], dt[L1:], B[L1:], C[L1:], A, D, bias, z=z[L1:], h0=h1, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yo, ho = O.ssd(inp["x_f32"], inp["dt_f32"], inp["B_f32"], inp["C_f32"], inp["A"], inp["D"], inp["dt_bias"],
+                   z=inp["z_f32"])
+    T = L1 + L2
+    check_fp32(host(torch.cat([y1, y2])).reshape(T, -1), yo.reshape(T, -1), "chained y")
+    check_fp32(host(h2), ho, "chained h_last")
+    check_fp32(host(y).reshape(T, -1), yo.reshape(T, -1), "one-pass y")
+    check_fp32(host(hl), ho, "one-pass h_last")
+
+
+def test_ssd_deterministic():
+    heads, G, N, L = 4, 1, 128, 300
+    t = I.make_ssd_inputs_torch(11, L, heads, G, N, DEV)
+    args = (t["x"], t["dt"], t["B"], t["C"], t["A"], t["D"], t["dt_bias"])
+    y1, h1 = S.ssd_fwd(*args, z=t["z"])
+    y2, h2 = S.ssd_fwd(*args, z=t["z"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)) and torch.equal(h1, h2)
+
+
+def test_ssd_full_shape_sampled():
+    """B4 L4096 H64 P64 N128 G1 (the benchmark's launch): two heads of two sequences against the oracle
+    (heads are independent given their group's B and C)."""
+    wl = I.WORKLOADS[9]
+    Bt, L, H, N, G = wl.batch, wl.seqlen, wl.extra["heads"], wl.dstate, wl.extra["ngroups"]
+    say("case: ssd full shape B%d L%d H%d N%d G%d" % (Bt, L, H, N, G))
+    t = I.make_ssd_inputs_torch(9, Bt * L, H, G, N, DEV)
+    x, z = (t[k].view(Bt, L, H, 64) for k in ("x", "z"))
+    dt = t["dt"].view(Bt, L, H)
+    B, C = (t[k].view(Bt, L, G, N) for k in ("B", "C"))
+    y, hl = S.ssd_fwd(x, dt, B, C, t["A"], t["D"], t["dt_bias"], z=z)
+    torch.cuda.synchronize()
+    for s, h in ((0, 5), (3, 62)):
+        hs = slice(h, h + 1)
+        yo, ho = O.ssd(host(x[s, :, hs]), host(dt[s, :, hs]), host(B[s]), host(C[s]), host(t["A"][hs]),
+                       host(t["D"][hs]), host(t["dt_bias"][hs]), z=host(z[s, :, hs]))
+        check_bf16_y(host(y[s, :, h]), yo[:, 0], "y s%d h%d" % (s, h))
+        check_fp32(host(hl[s, h]), ho[0, 0], "h_last s%d h%d" % (s, h))
+    say("  ok")
