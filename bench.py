@@ -589,6 +589,7 @@ def bench_ssd(steps: int = 20, warmup: int = 5):
     y = torch.empty_like(x)
     hl = torch.empty(Bt, H, P, N, dtype=torch.float32, device=dev)
     a = SD.fwd_args(x, dt, B, C, t["A"], t["D"], t["dt_bias"], y=y, z=z, h_last=hl)
+    ws = SD.attach_workspace(a, dev)
     lib = SD.load_library()
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
@@ -602,6 +603,7 @@ def bench_ssd(steps: int = 20, warmup: int = 5):
         call()
     torch.cuda.synchronize()
     ms = _timed(call, steps, stream)
+    del ws
     nbytes = ssd_bytes(Bt, L, H, P, G, N)
     flops = ssd_flops(Bt, L, H, P, N)
     gbs = nbytes / (ms * 1e-3) / 1e9

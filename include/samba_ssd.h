@@ -28,6 +28,14 @@
  * dt 2; A, D, dt_bias 4.  y and h_last must not overlap any input, except
  * h_last == h0 exactly (the final state written in place over the initial).
  *
+ * Workspace: the products C Bᵀ of each chunk depend on the group only, not on
+ * the head, so each call first writes them, once per (chunk, group), into a
+ * caller-owned device workspace of samba_ssd_workspace_size() bytes (256-byte
+ * aligned; 12 KiB per chunk slot and group, about 3 MiB for 4 x 4096 tokens
+ * and one group), which the prefill kernel then reads.  Calls that overlap in
+ * time must use different workspaces; the workspace may not overlap any input
+ * or output (SAMBA_ERR_ALIASING); NULL or too small is SAMBA_ERR_WORKSPACE.
+ *
  * Ownership, asynchrony and errors as for samba_scan.h: device pointers owned
  * by the caller, nothing allocated or kept, validation before anything is
  * enqueued, kernels enqueued on `stream` (hipStream_t as void*, NULL = the
@@ -57,7 +65,13 @@ typedef struct {
   const float* h0;             /* optional [nseq][heads][head_dim][dstate] */
   float* h_last;               /* optional, same shape */
   void* y;                     /* [tokens][heads][head_dim] */
+  void* workspace;             /* device, samba_ssd_workspace_size() bytes */
+  size_t workspace_bytes;
 } samba_ssd_args;
+
+/* Host-only: bytes of workspace samba_ssd_fwd needs for these sizes (0 when
+ * there are no tokens); validates the sizes like samba_ssd_fwd. */
+samba_status samba_ssd_workspace_size(const samba_ssd_args* args, size_t* bytes);
 
 samba_status samba_ssd_fwd(const samba_ssd_args* args, void* stream);
 

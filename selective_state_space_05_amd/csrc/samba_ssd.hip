@@ -2,10 +2,14 @@
 // "SAMBA混合注意力状态空间模型" compares Samba with, 与其他混合架构对比): a scalar decay per head and a
 // head_dim x dstate state per head, so that a chunk of tokens is a handful of dense products.
 //
-// One workgroup (4 waves) owns one (sequence, head) and walks its tokens in chunks of Q = 64, the fp32
-// state carried in registers from chunk to chunk.  With la_t = log2e * A * sum_{r<=t} Δ_r inside the chunk,
-// w_s = 2^(la_end - la_s) Δ_s and the entering state H (P x N):
-//   (a) Sᵀ[s][t] = sum_n B[s][n] C[t][n]                       MFMA, K = N
+// Two kernels per call:
+//   * ssd_cb_kernel computes, once per (chunk, group), the three nonzero 32x32 tiles of Sᵀ = B Cᵀ (the
+//     (B, C) of a group serve every head of the group) into the caller's workspace, each tile stored as
+//     the accumulator image its consumer loads (16 floats per lane);
+//   * ssd_fwd_kernel: one workgroup (8 waves) per (sequence, head) walks the tokens in chunks of Q = 64, the
+//     fp32 state carried in registers from chunk to chunk.
+// With la_t = log2e * A * sum_{r<=t} Δ_r inside the chunk, w_s = 2^(la_end - la_s) Δ_s and the entering
+// state H (P x N), per chunk:
 //   (b) Mᵀ[s][t] = Sᵀ[s][t] 2^(la_t - la_s) Δ_s  (s <= t, else 0), + D on the diagonal (the skip)
 //   (c) Yᵀ[p][t] = sum_s X[s][p] Mᵀ[s][t]                      MFMA, K = Q
 //   (d)         + 2^(la_t) sum_n H[p][n] C[t][n]               MFMA, K = N
@@ -14,19 +18,26 @@
 // The operands built here rather than read (M, H, w X) are split into bf16 hi + lo pairs, two MFMAs each:
 // one bf16 rounding of them alone costs about 2e-3 of the output's scale, the pair about 1e-6.
 //
-// Wave roles (32x32 tiles, v_mfma_f32_32x32x16_bf16): wave w holds p-tile a = w & 1 of the state and its
-// n-tiles of half hb = w >> 1, and finishes the output tile (p-tile a, t-tile hb).  Products are laid out
-// so that one product's accumulators are the next one's operand without a trip through LDS:
-//   * Sᵀ's accumulator rows s are the contraction index of (c): a lane's 8 elements of a 16-wide step
-//     are s = 16kk + 8(j/4) + 4hi + j%4, and X is read from LDS in that order;
-//   * the state lives as Hᵀ accumulators (lane = column p), which are (d)'s A operand in the same way,
-//     with C read in the matching n order.
-// (d) over a wave's half of the states leaves partial sums for both t-tiles; the half for the other
-// t-tile goes to the partner wave through LDS.  Chunk inputs are loaded one chunk ahead into registers and
-// staged into LDS (C and B row-major, B and X transposed); Δ, la and w are computed by wave 0.
+// Roles (32x32 tiles, v_mfma_f32_32x32x16_bf16, two waves per SIMD):
+//   * state waves 0 .. 3: wave k holds p-tile a = k & 1 of the state for half hb = k >> 1 of the n-tiles
+//     as Hᵀ accumulators and finishes the output tile (p-tile a, t-tile hb).  Products are laid out so
+//     that one product's accumulators are the next one's operand: Sᵀ's accumulator rows s are the
+//     contraction index of (c) (a lane's 8 elements of a 16-wide step are s = 16kk + 8(j/4) + 4hi + j%4,
+//     and X is read from LDS in that order), and the Hᵀ accumulators (lane = column p) are (d)'s A operand
+//     the same way, with C read in the matching n order.  (d) over a wave's half of the states gives
+//     partial sums for both t-tiles; the other t-tile's goes to the partner wave through LDS;
+//   * helper waves 4 .. 7 load C, B, X, z and Δ through a ring of two register sets and stage them into
+//     LDS (C and z row-major, B and X transposed, each store a run of consecutive words across the lanes);
+//     one of them computes Δ, la and w with a DPP prefix sum; they store bf16 y, which the state waves
+//     stage in LDS, as whole 128-byte lines one chunk later.  (z and y in the state waves' own
+//     layout would be 8-byte pieces of 32 rows per instruction, which costs more than the arithmetic.)
+// The inputs are staged in two alternating LDS buffers, so the helpers fill chunk c + 1's while the state
+// waves compute chunk c: two barriers per chunk (partial sums exchanged; chunk done and next one staged).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "samba_ssd.h"
 
@@ -45,6 +56,9 @@ constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kQ = 64;                   // tokens per chunk
 constexpr int kP = 64;                   // head size
 constexpr int kTRow = kQ + 8;            // row stride (bf16) of the transposed tiles in LDS
+// a buffer offset past every resource here (a sequence's rows of any tensor span less than 2^31 bytes):
+// accesses at it read 0 and write nothing
+constexpr uint32_t kNowhere = 0x80000000u;
 
 __device__ __forceinline__ rsrc_t rsrc_bytes(const void* base, int64_t bytes) {
   const uint32_t b = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : static_cast<uint32_t>(bytes));
@@ -107,148 +121,383 @@ struct SsdParams {
   const float *A, *Dskip, *bias, *h0;
   float* h_last;
   void* y;
+  float* ws;                                        // Sᵀ tile images [slot][group][3][64][16]
   const int32_t* cu;
-  int32_t nseq, seqlen, heads, ngroups, total;
+  int32_t nseq, seqlen, heads, ngroups, total, nch;   // nch: chunks per batched sequence
 };
 
+constexpr int kWaves = 8;                // 4 state waves + 4 helper waves
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileFloats = 64 * 16;     // one 32x32 accumulator image
+
+__device__ __forceinline__ int32_t cu_at(const int32_t* cu, int s, int32_t total) {
+  const int32_t v = cu[s];
+  return v < 0 ? 0 : (v > total ? total : v);
+}
+// (first token, length) of sequence s and the workspace slot of its first chunk: batched sequences own nch
+// slots each; packed sequence s owns slots (cu[s] >> 6) + s .. (these ranges never overlap and all lie below
+// (total >> 6) + nseq)
+struct SeqInfo {
+  int64_t t0;
+  int32_t len, slot0;
+};
+__device__ __forceinline__ SeqInfo seq_info(const SsdParams& p, int s) {
+  SeqInfo r;
+  if (p.cu) {
+    const int32_t b = cu_at(p.cu, s, p.total), e0 = cu_at(p.cu, s + 1, p.total);
+    const int32_t e = e0 < b ? b : e0;
+    r.t0 = b;
+    r.len = e - b;
+    r.slot0 = (b >> 6) + s;
+  } else {
+    r.t0 = static_cast<int64_t>(s) * p.seqlen;
+    r.len = p.seqlen;
+    r.slot0 = s * p.nch;
+  }
+  return r;
+}
+
+// Sᵀ tiles (s-tile, t-tile) = (0, 0), (0, 1), (1, 1) of one (chunk, group): one wave per tile, operands read
+// straight from B and C (rows past the sequence read as 0).  Block b is (slot b / G, group b % G); slots of
+// no chunk (between packed sequences) return at once.
 template <int N>
-struct Smem {
-  static constexpr int kRow = N + 8;                // row stride (bf16) of the row-major tiles
+__global__ __launch_bounds__(192) void ssd_cb_kernel(SsdParams p) {
+  const int G = p.ngroups;
+  const int slot = static_cast<int>(blockIdx.x) / G, g = static_cast<int>(blockIdx.x) - slot * G;
+  int s, c;
+  if (p.cu) {
+    // the last sequence whose first slot is <= slot (first slots ascend with s)
+    int lo = 0, hi = p.nseq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((cu_at(p.cu, mid, p.total) >> 6) + mid <= slot) lo = mid;
+      else hi = mid;
+    }
+    s = lo;
+  } else {
+    s = slot / p.nch;
+  }
+  const SeqInfo si = seq_info(p, s);
+  c = slot - si.slot0;
+  if (c < 0 || c * kQ >= si.len) return;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  const int tile = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int m_si = tile == 2 ? 1 : 0, m_tb = tile == 0 ? 0 : 1;
+  const uint32_t rowbc = static_cast<uint32_t>(G) * N * 2;
+  const int64_t gb = static_cast<int64_t>(g) * N;
+  const int64_t bcb = (static_cast<int64_t>(si.len) * G * N - gb) * 2;
+  const rsrc_t rb = rsrc_bytes(static_cast<const uint16_t*>(p.B) + si.t0 * G * N + gb, bcb);
+  const rsrc_t rc = rsrc_bytes(static_cast<const uint16_t*>(p.C) + si.t0 * G * N + gb, bcb);
+  const uint32_t ob = static_cast<uint32_t>(c * kQ + 32 * m_si + l32) * rowbc + 16 * hi;
+  const uint32_t oc = static_cast<uint32_t>(c * kQ + 32 * m_tb + l32) * rowbc + 16 * hi;
+  uint4 bv[N / 16], cv[N / 16];
+#pragma unroll
+  for (int kk = 0; kk < N / 16; ++kk) {
+    bv[kk] = ld16(rb, ob + 32 * kk);
+    cv[kk] = ld16(rc, oc + 32 * kk);
+  }
+  f32x16_t acc = f32x16_t{};
+#pragma unroll
+  for (int kk = 0; kk < N / 16; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bv[kk]),
+                                                  __builtin_bit_cast(bf16x8_t, cv[kk]), acc, 0, 0, 0);
+  float4* dst = reinterpret_cast<float4*>(p.ws + ((static_cast<int64_t>(slot) * G + g) * 3 + tile) * kTileFloats) +
+                lane * 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dst[q] = make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+}
+
+// One chunk's staged inputs and its M tiles; two of them alternate between consecutive chunks.
+template <int N>
+struct Stage {
+  static constexpr int kRow = N + 8;                // row stride (bf16) of C
   uint16_t c[kQ * kRow];                            // C [t][n]
-  uint16_t b[kQ * kRow];                            // B [s][n]
   uint16_t bt[N * kTRow];                           // B transposed [n][s]
   uint16_t xt[kP * kTRow];                          // X transposed [p][s]
+  bf16x8_t m[3][2][2][64];                          // M tiles (0,0), (0,1), (1,1): [tile][kk][hi/lo][lane]
   float dl[kQ], la[kQ], w[kQ];                      // Δ_s, la_s (log2 units), w_s
+};
+constexpr int kYRow = kP + 4;                        // row stride (floats) of the staged output
+template <int N>
+struct Smem {
+  Stage<N> st[2];                                   // chunk c uses st[c & 1]
+  float yf[kQ * kYRow];                             // the chunk's output before the gate [t][p]
   float4 xch[4][4][64];                             // (d) partial sums for the partner wave
+  float hs[4][2][kQ];                               // each helper wave's own la, Δ of the chunk it prepares
 };
 
-// The chunk loop of one wave; HB (the wave's state half and output t-tile) is a template argument so that
-// every register array is indexed by constants.
-template <typename Tout, int N, bool kGate, int HB>
-__device__ __forceinline__ void ssd_wave(const SsdParams& p, Smem<N>& sm, int s, int h, int64_t t0, int32_t len) {
-  constexpr int kRow = Smem<N>::kRow;
-  constexpr int NTW = N / 64;             // state n-tiles per wave
-  constexpr int NPR = N / 8;              // 16-byte pieces per B / C row
-  constexpr int RPL = N / 32;             // B rows per lane (transposed staging), C pieces per lane
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// Per-workgroup views of one (sequence, head): rows past the sequence read as 0 and are not written.
+struct Ctx {
+  rsrc_t rx, rz, ry, rdt, rb, rc;
+  uint32_t rowx, rowbc;                             // bytes per token of x (bf16) and of B, C
+  int64_t st_off0;                                  // offset of this (sequence, head)'s state
+  const float* ws;                                  // this group's first chunk's tiles
+  int64_t ws_stride;                                // floats from one chunk's tiles to the next's
+  int32_t len, H;
+  float A2, Dh, bias;
+};
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or0(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, true));
+}
+// inclusive prefix sum over the 64 lanes: shifts within rows of 16, then the row totals carried forward
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp_or0<0x111, 0xF>(v);   // row_shr:1
+  v += dpp_or0<0x112, 0xF>(v);   // row_shr:2
+  v += dpp_or0<0x114, 0xF>(v);   // row_shr:4
+  v += dpp_or0<0x118, 0xF>(v);   // row_shr:8
+  v += dpp_or0<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_or0<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Helper waves (h = 0 .. 3).  While the state waves compute chunk c, the helpers
+//   1. finish chunk c - 1: its staged output times silu(z), as bf16 or fp32 whole-line stores;
+//   2. stage chunk c + 1 (loaded two chunks earlier into a ring of two register sets) into its LDS stage:
+//      C as row-major pieces, B and X as pairs of rows at one 8-column run (so that the transposed stores
+//      of consecutive lanes are consecutive words); every helper computes Δ, la and w of the chunk with a
+//      DPP prefix sum (helper 0 publishes them, the others keep their own copy for step 3);
+//   3. helpers 0 .. 2 turn the chunk's Sᵀ tile h (loaded from the workspace two chunks earlier) into M
+//      = Sᵀ 2^(la_t - la_s) Δ_s (s <= t), + D on the diagonal, published as bf16 hi + lo operand images;
+//   4. load chunk c + 3 and the workspace tile of chunk c + 3.
+template <typename Tout, int N, bool kGate>
+__device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
+  constexpr int kRow = Stage<N>::kRow;
+  constexpr int NPR = N / 8;              // 16-byte pieces per C row
+  constexpr int PC = N / 32;              // C pieces per helper thread
+  constexpr int NB = N / 64;              // B passes (8-column runs 8 (c + 8 i))
+  const int t = static_cast<int>(threadIdx.x) - 256;
+  const int lane = t & 63, l32 = lane & 31, hi = lane >> 5;
+  const int hw = __builtin_amdgcn_readfirstlane(t >> 6);   // helper index
+  const int r = t & 31, cg = t >> 5;      // row pair, 8-column run
+  // M tile of this helper: (s-tile, t-tile) = (0, 0), (0, 1), (1, 1); helper 3 has none
+  const int m_si = hw == 2 ? 1 : 0, m_tb = hw == 0 ? 0 : 1;
+  const int tile = hw < 3 ? hw : 2;       // (helper 3 loads a tile it does not use: no branch around loads)
+  struct Set {
+    uint4 cr[PC], br[NB][2], xr[2], zr[2];
+    uint16_t dtr;
+  } set[2];
+  uint4 zring[2][2];                      // z of the chunk being finished and of the next one
+  f32x16_t sring[2];                      // Sᵀ tiles two chunks ahead
+  // z and output pieces: row t / 8 + 32 q, 8-column run t % 8
+  const int zrow = t >> 3, zcol = 8 * (t & 7);
+  const int nchunks = (cx.len + kQ - 1) / kQ;
+  auto load = [&](auto kset, int c) {
+    Set& st = set[decltype(kset)::value];
+    const int c0 = c * kQ;
+#pragma unroll
+    for (int i = 0; i < PC; ++i) {
+      const int id = i * 256 + t;
+      st.cr[i] = ld16(cx.rc, static_cast<uint32_t>(c0 + id / NPR) * cx.rowbc + (id % NPR) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        st.br[i][k] = ld16(cx.rb, static_cast<uint32_t>(c0 + 2 * r + k) * cx.rowbc + (8 * (cg + 8 * i)) * 2);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      st.xr[k] = ld16(cx.rx, static_cast<uint32_t>(c0 + 2 * r + k) * cx.rowx + (8 * cg) * 2);
+    if constexpr (kGate) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        st.zr[k] = ld16(cx.rz, static_cast<uint32_t>(c0 + zrow + 32 * k) * cx.rowx + zcol * 2);
+    }
+    st.dtr = __builtin_amdgcn_raw_buffer_load_b16(cx.rdt, static_cast<uint32_t>(c0 + lane) * cx.H * 2, 0, 0);
+    // the chunk's Sᵀ tile (the last chunk's past the sequence: a padding chunk's M is the skip alone)
+    const int cs = c < nchunks ? c : nchunks - 1;
+    const float4* q = reinterpret_cast<const float4*>(cx.ws + cs * cx.ws_stride + tile * kTileFloats) + lane * 4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 v = q[k];
+      sring[decltype(kset)::value][4 * k] = v.x;
+      sring[decltype(kset)::value][4 * k + 1] = v.y;
+      sring[decltype(kset)::value][4 * k + 2] = v.z;
+      sring[decltype(kset)::value][4 * k + 3] = v.w;
+    }
+  };
+  auto prepare = [&](auto kset, int c) {
+    constexpr int K = decltype(kset)::value;
+    const Set& st = set[K];
+    Stage<N>& g = sm.st[K];
+    const int c0 = c * kQ;
+#pragma unroll
+    for (int i = 0; i < PC; ++i) {
+      const int id = i * 256 + t;
+      *reinterpret_cast<uint4*>(&g.c[(id / NPR) * kRow + (id % NPR) * 8]) = st.cr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t w0 = word(st.br[i][0], j / 2), w1 = word(st.br[i][1], j / 2);
+        *reinterpret_cast<uint32_t*>(&g.bt[(8 * (cg + 8 * i) + j) * kTRow + 2 * r]) =
+            (j & 1) ? highs(w0, w1) : lows(w0, w1);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w0 = word(st.xr[0], j / 2), w1 = word(st.xr[1], j / 2);
+      *reinterpret_cast<uint32_t*>(&g.xt[(8 * cg + j) * kTRow + 2 * r]) = (j & 1) ? highs(w0, w1) : lows(w0, w1);
+    }
+    zring[K][0] = st.zr[0];
+    zring[K][1] = st.zr[1];
+    // Δ, la (inclusive prefix sum of Δ A log2e) and w = 2^(la_end - la) Δ; tokens past the sequence get
+    // Δ = 0 (no decay, no input)
+    const float dlt = c0 + lane < cx.len ? softplus_f32(widen(st.dtr) + cx.bias) : 0.0f;
+    const float l = wave_prefix_sum(dlt * cx.A2);
+    if (hw == 0) {
+      const float l_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 63));
+      g.dl[lane] = dlt;
+      g.la[lane] = l;
+      g.w[lane] = __builtin_amdgcn_exp2f(l_end - l) * dlt;
+    }
+    if (hw < 3) {
+      sm.hs[hw][0][lane] = l;
+      sm.hs[hw][1][lane] = dlt;
+      wave_sync();
+      const int t_own = 32 * m_tb + l32;
+      const float la_t = sm.hs[hw][0][t_own];
+      f32x16_t m = sring[K];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int s0 = 32 * m_si + 8 * q + 4 * hi;
+        const float4 las = *reinterpret_cast<const float4*>(&sm.hs[hw][0][s0]);
+        const float4 dls = *reinterpret_cast<const float4*>(&sm.hs[hw][1][s0]);
+        const float lv[4] = {las.x, las.y, las.z, las.w}, dv[4] = {dls.x, dls.y, dls.z, dls.w};
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int sv = s0 + rr;
+          float v = sv <= t_own ? m[4 * q + rr] * __builtin_amdgcn_exp2f(la_t - lv[rr]) * dv[rr] : 0.0f;
+          v += sv == t_own ? cx.Dh : 0.0f;
+          m[4 * q + rr] = v;
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t mh, ml;
+        split8(m, 8 * kk, mh, ml);
+        g.m[hw][kk][0][lane] = mh;
+        g.m[hw][kk][1][lane] = ml;
+      }
+    }
+  };
+  // chunk k's output (k < 0: nothing, the stores go nowhere), z from the ring slot of k
+  auto finish = [&](auto kz, int k) {
+    constexpr int K = decltype(kz)::value;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = zrow + 32 * q;
+      const float4 v0 = *reinterpret_cast<const float4*>(&sm.yf[row * kYRow + zcol]);
+      const float4 v1 = *reinterpret_cast<const float4*>(&sm.yf[row * kYRow + zcol + 4]);
+      float yv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      if constexpr (kGate) {
+        const uint4 zv = zring[K][q];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t zw = word(zv, j / 2);
+          yv[j] *= silu_f32(__uint_as_float((j & 1) ? (zw & 0xffff0000u) : (zw << 16)));
+        }
+      }
+      const uint32_t off0 = k >= 0 ? static_cast<uint32_t>(k * kQ + row) * cx.H * kP * sizeof(Tout) : kNowhere;
+      if constexpr (sizeof(Tout) == 2) {
+        u32x4_t w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(yv[2 * j]))) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(yv[2 * j + 1]))) << 16);
+        __builtin_amdgcn_raw_buffer_store_b128(w, cx.ry, off0 + (k >= 0 ? zcol * 2 : 0), 0, 0);
+      } else {
+        const u32x4_t w0 = {__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]), __float_as_uint(yv[3])};
+        const u32x4_t w1 = {__float_as_uint(yv[4]), __float_as_uint(yv[5]), __float_as_uint(yv[6]), __float_as_uint(yv[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(w0, cx.ry, off0 + (k >= 0 ? zcol * 4 : 0), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(w1, cx.ry, off0 + (k >= 0 ? zcol * 4 + 16 : 16), 0, 0);
+      }
+    }
+  };
+  // An even number of chunks (the state waves pad the same way; a chunk past the sequence reads zeros and
+  // changes nothing), and no load or store behind a data-dependent branch inside the loop, so that the
+  // compiler's wait counts keep the other register set's loads in flight.
+  const int npad = (nchunks + 1) & ~1;
+  if (nchunks > 0) {
+    load(std::integral_constant<int, 0>{}, 0);
+    load(std::integral_constant<int, 1>{}, 1);
+    prepare(std::integral_constant<int, 0>{}, 0);
+    load(std::integral_constant<int, 0>{}, 2);
+  }
+  __syncthreads();   // chunk 0 staged
+  auto body = [&](auto knext, int c) {
+    finish(knext, c - 1);   // chunk c - 1's z sits in the slot that chunk c + 1's takes next
+    prepare(knext, c + 1);
+    load(knext, c + 3);
+    __syncthreads();   // X1: the state waves' partial sums
+    __syncthreads();   // X2: chunk c computed, chunk c + 1 prepared
+  };
+  for (int c = 0; c < npad; c += 2) {
+    body(std::integral_constant<int, 1>{}, c);
+    body(std::integral_constant<int, 0>{}, c + 1);
+  }
+  if (npad > 0) finish(std::integral_constant<int, 1>{}, npad - 1);
+}
+
+// State wave k (0 .. 3): p-tile a = k & 1, n-tiles of half HB = k >> 1 (element e of tile nt: n = 32 nt +
+// 8 (e / 4) + 4 hi + e % 4, p = 32 a + lane % 32); finishes the output tile (a, HB) up to the gate.
+template <int N, int HB>
+__device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const float* h0, float* h_last) {
+  constexpr int NTW = N / 64;
+  constexpr int kRow = Stage<N>::kRow;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int a = wave & 1;
-  const int H = p.heads;
-  const int g = h / (H / p.ngroups);
-  const int p_own = 32 * a + l32;         // this lane's column of the state and of Yᵀ
+  const int p_own = 32 * a + l32;
+  const int t_own = 32 * HB + l32;
+  const int64_t st_off = cx.st_off0 + static_cast<int64_t>(p_own) * N;
 
-  const float A2 = p.A[h] * kLog2e;
-  const float Dh = p.Dskip[h];
-  const float bias = p.bias[h];
-
-  // per-(sequence, head) views; rows past the sequence read as 0 and are not written
-  const uint32_t rowx = static_cast<uint32_t>(H) * kP * 2;          // bytes per token of x, z (bf16)
-  const uint32_t rowbc = static_cast<uint32_t>(p.ngroups) * N * 2;  // bytes per token of B, C
-  const int64_t hx = static_cast<int64_t>(h) * kP;
-  const rsrc_t rx = rsrc_bytes(static_cast<const uint16_t*>(p.x) + t0 * H * kP + hx,
-                               (static_cast<int64_t>(len) * H * kP - hx) * 2);
-  const rsrc_t rz = kGate ? rsrc_bytes(static_cast<const uint16_t*>(p.z) + t0 * H * kP + hx,
-                                       (static_cast<int64_t>(len) * H * kP - hx) * 2)
-                          : rsrc_bytes(nullptr, 0);
-  const rsrc_t ry = rsrc_bytes(static_cast<Tout*>(p.y) + t0 * H * kP + hx,
-                               (static_cast<int64_t>(len) * H * kP - hx) * static_cast<int64_t>(sizeof(Tout)));
-  const rsrc_t rdt = rsrc_bytes(static_cast<const uint16_t*>(p.dt) + t0 * H + h,
-                                (static_cast<int64_t>(len) * H - h) * 2);
-  const int64_t gb = static_cast<int64_t>(g) * N;
-  const int64_t bcb = (static_cast<int64_t>(len) * p.ngroups * N - gb) * 2;
-  const rsrc_t rb = rsrc_bytes(static_cast<const uint16_t*>(p.B) + t0 * p.ngroups * N + gb, bcb);
-  const rsrc_t rc = rsrc_bytes(static_cast<const uint16_t*>(p.C) + t0 * p.ngroups * N + gb, bcb);
-
-  // the state: NTW accumulator tiles Hᵀ[n][p], n-tile HB * NTW + i; element e is
-  // n = 32 nt + 8 (e / 4) + 4 hi + e % 4, p = p_own
   f32x16_t hst[NTW];
-  const int64_t st_off = ((static_cast<int64_t>(s) * H + h) * kP + p_own) * N;
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
     const int nt = HB * NTW + i;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (p.h0) v = *reinterpret_cast<const float4*>(p.h0 + st_off + 32 * nt + 8 * q + 4 * hi);
+      if (h0) v = *reinterpret_cast<const float4*>(h0 + st_off + 32 * nt + 8 * q + 4 * hi);
       hst[i][4 * q] = v.x; hst[i][4 * q + 1] = v.y; hst[i][4 * q + 2] = v.z; hst[i][4 * q + 3] = v.w;
     }
   }
+  // an even number of chunks, as the helper waves run (a padding chunk has Δ = 0 and x = 0: it leaves the
+  // state alone and its output goes past the sequence)
+  const int npad = ((cx.len + kQ - 1) / kQ + 1) & ~1;
+  __syncthreads();   // chunk 0 staged
 
-  // staging assignment: C pieces (row-major), B rows (RPL consecutive rows, one 8-column run), X rows
-  const int bcol = 8 * (tid % NPR), brow = RPL * (tid / NPR);
-  const int xcol = 8 * (tid % 8), xrow = 2 * (tid / 8);
-  uint4 cr[RPL], br[RPL], xr[2];
-  uint16_t dtr = 0;
-  auto load_chunk = [&](int c0) {
+  auto chunk = [&](auto kbuf) {
+    const Stage<N>& g = sm.st[decltype(kbuf)::value];
+    // operands of (d): C in the state accumulators' n order, both t-tiles; of (c): X in M's s order
+    bf16x8_t cop[2][NTW][2], xop[HB + 1][2];
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      const int id = i * 256 + tid;
-      cr[i] = ld16(rc, static_cast<uint32_t>(c0 + id / NPR) * rowbc + (id % NPR) * 16);
-      br[i] = ld16(rb, static_cast<uint32_t>(c0 + brow + i) * rowbc + bcol * 2);
-    }
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) xr[i] = ld16(rx, static_cast<uint32_t>(c0 + xrow + i) * rowx + xcol * 2);
-    if (wave == 0) dtr = __builtin_amdgcn_raw_buffer_load_b16(rdt, static_cast<uint32_t>(c0 + lane) * H * 2, 0, 0);
-  };
-
-  const int nchunks = (len + kQ - 1) / kQ;
-  if (nchunks > 0) load_chunk(0);
-  for (int c = 0; c < nchunks; ++c) {
-    const int c0 = c * kQ;
-    __syncthreads();   // every wave is done with the previous chunk's LDS
+      for (int i = 0; i < NTW; ++i)
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      const int id = i * 256 + tid;
-      *reinterpret_cast<uint4*>(&sm.c[(id / NPR) * kRow + (id % NPR) * 8]) = cr[i];
-      *reinterpret_cast<uint4*>(&sm.b[(brow + i) * kRow + bcol]) = br[i];
-    }
-    // B transposed: column n = bcol + j, rows brow .. brow + RPL - 1
+        for (int kk = 0; kk < 2; ++kk) {
+          const uint16_t* row = &g.c[(32 * tb + l32) * kRow + 32 * (HB * NTW + i) + 16 * kk + 4 * hi];
+          cop[tb][i][kk] = cat4(row, row + 8);
+        }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t v[RPL / 2];
+    for (int si = 0; si <= HB; ++si)
 #pragma unroll
-      for (int r = 0; r < RPL / 2; ++r) {
-        const uint32_t w0 = word(br[2 * r], j / 2), w1 = word(br[2 * r + 1], j / 2);
-        v[r] = (j & 1) ? highs(w0, w1) : lows(w0, w1);
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint16_t* row = &g.xt[p_own * kTRow + 32 * si + 16 * kk + 4 * hi];
+        xop[si][kk] = cat4(row, row + 8);
       }
-      uint16_t* dst = &sm.bt[(bcol + j) * kTRow + brow];
-      if constexpr (RPL == 4) *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{v[0], v[1]};
-      else *reinterpret_cast<uint32_t*>(dst) = v[0];
-    }
-    // X transposed: column p = xcol + j, rows xrow, xrow + 1
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w0 = word(xr[0], j / 2), w1 = word(xr[1], j / 2);
-      *reinterpret_cast<uint32_t*>(&sm.xt[(xcol + j) * kTRow + xrow]) = (j & 1) ? highs(w0, w1) : lows(w0, w1);
-    }
-    if (wave == 0) {
-      // Δ, la (inclusive prefix sum of Δ A log2e over the chunk) and w = 2^(la_end - la) Δ; tokens past the
-      // sequence get Δ = 0 (no decay, no input)
-      const float dlt = c0 + lane < len ? softplus_f32(widen(dtr) + bias) : 0.0f;
-      float la = dlt * A2;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float v = __shfl_up(la, off, 64);
-        la = lane >= off ? la + v : la;
-      }
-      const float la_end = __shfl(la, 63, 64);
-      sm.dl[lane] = dlt;
-      sm.la[lane] = la;
-      sm.w[lane] = __builtin_amdgcn_exp2f(la_end - la) * dlt;
-    }
-    __syncthreads();
-    if (c + 1 < nchunks) load_chunk(c0 + kQ);
-
-    // z of this chunk for the output tile (p-tile a, t-tile HB): 4 runs of 4 columns
-    u32x2_t zr[4];
-    const int t_own = 32 * HB + l32;
-    if constexpr (kGate) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        zr[q] = __builtin_amdgcn_raw_buffer_load_b64(rz, static_cast<uint32_t>(c0 + t_own) * rowx +
-                                                             (32 * a + 8 * q + 4 * hi) * 2, 0, 0);
-    }
+    const float la_t = g.la[t_own];
+    const float decay = __builtin_amdgcn_exp2f(g.la[kQ - 1]);
 
     // (d) partial sums over this wave's states, both t-tiles, from the entering state
     f32x16_t yo[2];
@@ -256,80 +505,41 @@ __device__ __forceinline__ void ssd_wave(const SsdParams& p, Smem<N>& sm, int s,
     yo[1] = f32x16_t{};
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
-      const int nt = HB * NTW + i;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bf16x8_t hh, hl;
         split8(hst[i], 8 * kk, hh, hl);
-        const int n0 = 32 * nt + 16 * kk + 4 * hi;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-          const uint16_t* row = &sm.c[(32 * tb + l32) * kRow];
-          const bf16x8_t cop = cat4(row + n0, row + n0 + 8);
-          yo[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hh, cop, yo[tb], 0, 0, 0);
-          yo[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hl, cop, yo[tb], 0, 0, 0);
+          yo[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hh, cop[tb][i][kk], yo[tb], 0, 0, 0);
+          yo[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hl, cop[tb][i][kk], yo[tb], 0, 0, 0);
         }
       }
     }
-    // the other t-tile's partial goes to the partner wave (same p-tile, other state half)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       sm.xch[wave][q][lane] = make_float4(yo[1 - HB][4 * q], yo[1 - HB][4 * q + 1], yo[1 - HB][4 * q + 2],
                                           yo[1 - HB][4 * q + 3]);
 
-    // (a) Sᵀ tiles (s-tile si, t-tile HB) for si <= HB, then (b) M as bf16 hi + lo operands
-    f32x16_t sacc[HB + 1];
-#pragma unroll
-    for (int si = 0; si <= HB; ++si) sacc[si] = f32x16_t{};
-#pragma unroll
-    for (int kk = 0; kk < N / 16; ++kk) {
-      const bf16x8_t cop = *reinterpret_cast<const bf16x8_t*>(&sm.c[t_own * kRow + 16 * kk + 8 * hi]);
-#pragma unroll
-      for (int si = 0; si <= HB; ++si) {
-        const bf16x8_t bop = *reinterpret_cast<const bf16x8_t*>(&sm.b[(32 * si + l32) * kRow + 16 * kk + 8 * hi]);
-        sacc[si] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, cop, sacc[si], 0, 0, 0);
-      }
-    }
-    const float la_t = sm.la[t_own];
+    // (c) Yᵀ = X M over the s-tiles up to HB, M from the helpers' images
     f32x16_t yd = f32x16_t{};
 #pragma unroll
-    for (int si = 0; si <= HB; ++si) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int s0 = 32 * si + 8 * q + 4 * hi;
-        const float4 las = *reinterpret_cast<const float4*>(&sm.la[s0]);
-        const float4 dls = *reinterpret_cast<const float4*>(&sm.dl[s0]);
-        const float lv[4] = {las.x, las.y, las.z, las.w}, dv[4] = {dls.x, dls.y, dls.z, dls.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int sv = s0 + r;
-          float m = sv <= t_own ? sacc[si][4 * q + r] * __builtin_amdgcn_exp2f(la_t - lv[r]) * dv[r] : 0.0f;
-          m += sv == t_own ? Dh : 0.0f;
-          sacc[si][4 * q + r] = m;
-        }
-      }
-      // (c) Yᵀ += X M over this s-tile (X read in the accumulator's s order)
+    for (int si = 0; si <= HB; ++si)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bf16x8_t mh, ml;
-        split8(sacc[si], 8 * kk, mh, ml);
-        const uint16_t* row = &sm.xt[p_own * kTRow + 32 * si + 16 * kk + 4 * hi];
-        const bf16x8_t xop = cat4(row, row + 8);
-        yd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xop, mh, yd, 0, 0, 0);
-        yd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xop, ml, yd, 0, 0, 0);
+        yd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xop[si][kk], g.m[si + HB][kk][0][lane], yd, 0, 0, 0);
+        yd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xop[si][kk], g.m[si + HB][kk][1][lane], yd, 0, 0, 0);
       }
-    }
 
-    // (e) the state update: Hᵀ = 2^(la_end) Hᵀ + Bᵀ (w X), w X as a bf16 hi + lo pair
-    const float decay = __builtin_amdgcn_exp2f(sm.la[kQ - 1]);
+    // (e) Hᵀ = 2^(la_end) Hᵀ + Bᵀ (w X), w X as a bf16 hi + lo pair
 #pragma unroll
     for (int i = 0; i < NTW; ++i) hst[i] *= decay;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int s0 = 16 * kk + 8 * hi;
-      const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(&sm.xt[p_own * kTRow + s0]);
-      const float4 w0 = *reinterpret_cast<const float4*>(&sm.w[s0]);
-      const float4 w1 = *reinterpret_cast<const float4*>(&sm.w[s0 + 4]);
+      const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(&g.xt[p_own * kTRow + s0]);
+      const float4 w0 = *reinterpret_cast<const float4*>(&g.w[s0]);
+      const float4 w1 = *reinterpret_cast<const float4*>(&g.w[s0 + 4]);
       const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       bf16x8_t xh, xl;
 #pragma unroll
@@ -341,80 +551,79 @@ __device__ __forceinline__ void ssd_wave(const SsdParams& p, Smem<N>& sm, int s,
       }
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
-        const int nt = HB * NTW + i;
-        const bf16x8_t bop = *reinterpret_cast<const bf16x8_t*>(&sm.bt[(32 * nt + l32) * kTRow + s0]);
+        const bf16x8_t bop = *reinterpret_cast<const bf16x8_t*>(&g.bt[(32 * (HB * NTW + i) + l32) * kTRow + s0]);
         hst[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, xh, hst[i], 0, 0, 0);
         hst[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, xl, hst[i], 0, 0, 0);
       }
     }
 
-    __syncthreads();   // the partner's partial sums are in LDS
+    __syncthreads();   // X1: the partner's partial sums are in LDS
     const float eo = __builtin_amdgcn_exp2f(la_t);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 o = sm.xch[wave ^ 2][q][lane];
-      const float ov[4] = {o.x, o.y, o.z, o.w};
-      float yv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) yv[r] = fmaf(eo, yo[HB][4 * q + r] + ov[r], yd[4 * q + r]);
-      if constexpr (kGate) {
-        const uint32_t zw[2] = {zr[q][0], zr[q][1]};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t zb = (r & 1) ? (zw[r / 2] & 0xffff0000u) : (zw[r / 2] << 16);
-          yv[r] *= silu_f32(__uint_as_float(zb));
-        }
-      }
-      const uint32_t off = static_cast<uint32_t>(c0 + t_own) * H * kP * sizeof(Tout) +
-                           (32 * a + 8 * q + 4 * hi) * sizeof(Tout);
-      if constexpr (sizeof(Tout) == 2) {
-        const u32x2_t v = {static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(yv[0]))) |
-                               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(yv[1]))) << 16),
-                           static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(yv[2]))) |
-                               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(yv[3]))) << 16)};
-        __builtin_amdgcn_raw_buffer_store_b64(v, ry, off, 0, 0);
-      } else {
-        const u32x4_t v = {__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]),
-                           __float_as_uint(yv[3])};
-        __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
-      }
+      const float4 v = make_float4(fmaf(eo, yo[HB][4 * q] + o.x, yd[4 * q]), fmaf(eo, yo[HB][4 * q + 1] + o.y, yd[4 * q + 1]),
+                                   fmaf(eo, yo[HB][4 * q + 2] + o.z, yd[4 * q + 2]),
+                                   fmaf(eo, yo[HB][4 * q + 3] + o.w, yd[4 * q + 3]));
+      *reinterpret_cast<float4*>(&sm.yf[t_own * kYRow + 32 * a + 8 * q + 4 * hi]) = v;
     }
+    __syncthreads();   // X2: chunk computed (output staged), the next chunk prepared
+  };
+  for (int c = 0; c < npad; c += 2) {
+    chunk(std::integral_constant<int, 0>{});
+    chunk(std::integral_constant<int, 1>{});
   }
 
-  if (p.h_last) {
+  if (h_last) {
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
       const int nt = HB * NTW + i;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(p.h_last + st_off + 32 * nt + 8 * q + 4 * hi) =
+        *reinterpret_cast<float4*>(h_last + st_off + 32 * nt + 8 * q + 4 * hi) =
             make_float4(hst[i][4 * q], hst[i][4 * q + 1], hst[i][4 * q + 2], hst[i][4 * q + 3]);
     }
   }
 }
 
 template <typename Tout, int N, bool kGate>
-__global__ __launch_bounds__(256, 1) void ssd_fwd_kernel(SsdParams p) {
+__global__ __launch_bounds__(kThreads, 1) void ssd_fwd_kernel(SsdParams p) {
   __shared__ __attribute__((aligned(16))) Smem<N> sm;
   const int nblk = static_cast<int>(gridDim.x);
   const int logical = xcd_remap(static_cast<int>(blockIdx.x), nblk);
   const int s = logical / p.heads;
   const int h = logical - s * p.heads;
-  int64_t t0;
-  int32_t len;
-  if (p.cu) {
-    int32_t b = p.cu[s], e = p.cu[s + 1];
-    b = b < 0 ? 0 : (b > p.total ? p.total : b);
-    e = e < b ? b : (e > p.total ? p.total : e);
-    t0 = b;
-    len = e - b;
-  } else {
-    t0 = static_cast<int64_t>(s) * p.seqlen;
-    len = p.seqlen;
-  }
-  const int hb = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 7);
-  if (hb == 0) ssd_wave<Tout, N, kGate, 0>(p, sm, s, h, t0, len);
-  else ssd_wave<Tout, N, kGate, 1>(p, sm, s, h, t0, len);
+  const SeqInfo si = seq_info(p, s);
+  const int H = p.heads;
+  const int G = p.ngroups;
+  const int g = h / (H / G);
+  Ctx cx;
+  cx.len = si.len;
+  cx.H = H;
+  cx.A2 = p.A[h] * kLog2e;
+  cx.Dh = p.Dskip[h];
+  cx.bias = p.bias[h];
+  cx.rowx = static_cast<uint32_t>(H) * kP * 2;
+  cx.rowbc = static_cast<uint32_t>(G) * N * 2;
+  const int64_t t0 = si.t0;
+  const int64_t hx = static_cast<int64_t>(h) * kP;
+  const int64_t xb = (static_cast<int64_t>(si.len) * H * kP - hx);
+  cx.rx = rsrc_bytes(static_cast<const uint16_t*>(p.x) + t0 * H * kP + hx, xb * 2);
+  cx.rz = kGate ? rsrc_bytes(static_cast<const uint16_t*>(p.z) + t0 * H * kP + hx, xb * 2) : rsrc_bytes(nullptr, 0);
+  cx.ry = rsrc_bytes(static_cast<Tout*>(p.y) + t0 * H * kP + hx, xb * static_cast<int64_t>(sizeof(Tout)));
+  cx.rdt = rsrc_bytes(static_cast<const uint16_t*>(p.dt) + t0 * H + h, (static_cast<int64_t>(si.len) * H - h) * 2);
+  const int64_t gb = static_cast<int64_t>(g) * N;
+  const int64_t bcb = (static_cast<int64_t>(si.len) * G * N - gb) * 2;
+  cx.rb = rsrc_bytes(static_cast<const uint16_t*>(p.B) + t0 * G * N + gb, bcb);
+  cx.rc = rsrc_bytes(static_cast<const uint16_t*>(p.C) + t0 * G * N + gb, bcb);
+  cx.st_off0 = (static_cast<int64_t>(s) * H + h) * kP * N;
+  cx.ws_stride = static_cast<int64_t>(G) * 3 * kTileFloats;
+  cx.ws = p.ws + (static_cast<int64_t>(si.slot0) * G + g) * 3 * kTileFloats;
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  if (wave >= 4) helper_wave<Tout, N, kGate>(cx, sm);
+  else if (wave >= 2) state_wave<N, 1>(cx, sm, p.h0, p.h_last);
+  else state_wave<N, 0>(cx, sm, p.h0, p.h_last);
 }
 
 bool aligned(const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) & (a - 1)) == 0; }
@@ -425,36 +634,66 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 template <typename Tout, int N>
-hipError_t launch_ssd(const SsdParams& p, bool gate, dim3 grid, hipStream_t s) {
-  const dim3 block(256);
+hipError_t launch_ssd(const SsdParams& p, bool gate, int64_t nslots, int64_t nblocks, hipStream_t s) {
+  if (nslots > 0)
+    hipLaunchKernelGGL((ssd_cb_kernel<N>), dim3(static_cast<uint32_t>(nslots * p.ngroups)), dim3(192), 0, s, p);
+  const dim3 grid(static_cast<uint32_t>(nblocks)), block(kThreads);
   if (gate) hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, true>), grid, block, 0, s, p);
   else hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
-}  // namespace
-
-extern "C" samba_status samba_ssd_fwd(const samba_ssd_args* a, void* stream) {
+// sequences, chunk slots and workspace bytes of a validated call
+struct Plan {
+  int64_t nseq, tokens, nch, nslots;
+  size_t ws_bytes;
+};
+samba_status plan_ssd(const samba_ssd_args* a, Plan* pl) {
   if (!a) return SAMBA_ERR_NULL_ARG;
   if (a->struct_size != sizeof(samba_ssd_args)) return SAMBA_ERR_BAD_STRUCT;
   if (a->batch < 0 || a->seqlen < 0 || a->heads < 1 || a->ngroups < 1 || a->nseq < 0) return SAMBA_ERR_BAD_SHAPE;
   if (a->head_dim != kP || (a->dstate != 64 && a->dstate != 128)) return SAMBA_ERR_UNSUPPORTED;
   if (a->heads % a->ngroups != 0) return SAMBA_ERR_BAD_SHAPE;
   if (a->y_dtype != SAMBA_F32 && a->y_dtype != SAMBA_BF16) return SAMBA_ERR_BAD_DTYPE;
-  int64_t nseq;
   if (a->cu_seqlens) {
     if (a->batch != 1 || a->nseq < 1) return SAMBA_ERR_BAD_SHAPE;
-    nseq = a->nseq;
+    pl->nseq = a->nseq;
   } else {
-    nseq = a->batch;
+    pl->nseq = a->batch;
   }
-  const int64_t tokens = static_cast<int64_t>(a->batch) * a->seqlen;
-  if (nseq == 0) return SAMBA_OK;
+  pl->tokens = static_cast<int64_t>(a->batch) * a->seqlen;
+  pl->nch = (static_cast<int64_t>(a->seqlen) + kQ - 1) / kQ;
+  pl->nslots = a->cu_seqlens ? (pl->tokens >> 6) + pl->nseq : pl->nseq * pl->nch;
   const int N = a->dstate;
-  // 32-bit buffer offsets: a sequence's rows of y (fp32) and of B / C
-  if (tokens * a->heads * kP * 4 >= (int64_t{1} << 32)) return SAMBA_ERR_BAD_SHAPE;
-  if (tokens * a->ngroups * N * 2 >= (int64_t{1} << 32)) return SAMBA_ERR_BAD_SHAPE;
-  if (nseq * a->heads > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  // 32-bit buffer offsets: the kernels address up to two chunks past a sequence's end (reads of zeros,
+  // dropped writes), so a sequence's rows of y (fp32) and of B / C stay below 2^31 bytes and 128 rows below
+  // 2^31 bytes more, which keeps every such offset below 2^32 and kNowhere past every sequence
+  if (a->heads > 65536) return SAMBA_ERR_BAD_SHAPE;
+  if (pl->tokens * a->heads * kP * 4 >= (int64_t{1} << 31)) return SAMBA_ERR_BAD_SHAPE;
+  if (pl->tokens * a->ngroups * N * 2 >= (int64_t{1} << 31)) return SAMBA_ERR_BAD_SHAPE;
+  if (pl->nseq * a->heads > 0x7fffffff || pl->nslots * a->ngroups > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
+  pl->ws_bytes = pl->tokens > 0 ? static_cast<size_t>(pl->nslots) * a->ngroups * 3 * kTileFloats * 4 : 0;
+  return SAMBA_OK;
+}
+
+}  // namespace
+
+extern "C" samba_status samba_ssd_workspace_size(const samba_ssd_args* a, size_t* bytes) {
+  if (!bytes) return SAMBA_ERR_NULL_ARG;
+  Plan pl;
+  const samba_status st = plan_ssd(a, &pl);
+  if (st != SAMBA_OK) return st;
+  *bytes = pl.nseq == 0 ? 0 : pl.ws_bytes;
+  return SAMBA_OK;
+}
+
+extern "C" samba_status samba_ssd_fwd(const samba_ssd_args* a, void* stream) {
+  Plan pl;
+  const samba_status st0 = plan_ssd(a, &pl);
+  if (st0 != SAMBA_OK) return st0;
+  if (pl.nseq == 0) return SAMBA_OK;
+  const int N = a->dstate;
+  const int64_t tokens = pl.tokens;
   if (!a->A || !a->D || !a->dt_bias) return SAMBA_ERR_NULL_ARG;
   if (tokens > 0 && (!a->x || !a->dt || !a->B || !a->C || !a->y)) return SAMBA_ERR_NULL_ARG;
   const size_t oe = a->y_dtype == SAMBA_BF16 ? 2 : 4;
@@ -462,36 +701,46 @@ extern "C" samba_status samba_ssd_fwd(const samba_ssd_args* a, void* stream) {
       !aligned(a->h_last, 16) || !aligned(a->z, 8) || !aligned(a->y, 4 * oe) || !aligned(a->dt, 2) ||
       !aligned(a->A, 4) || !aligned(a->D, 4) || !aligned(a->dt_bias, 4))
     return SAMBA_ERR_MISALIGNED;
+  if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned(a->workspace, 256)))
+    return SAMBA_ERR_WORKSPACE;
   const size_t thp = static_cast<size_t>(tokens) * a->heads * kP;
   const size_t tbc = static_cast<size_t>(tokens) * a->ngroups * N * 2;
-  const size_t st = static_cast<size_t>(nseq) * a->heads * kP * N * 4;
+  const size_t st = static_cast<size_t>(pl.nseq) * a->heads * kP * N * 4;
   const size_t hv = static_cast<size_t>(a->heads) * 4;
   const void* ins[11] = {a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias, a->h0, a->cu_seqlens, nullptr};
   const size_t in_sz[11] = {thp * 2, static_cast<size_t>(tokens) * a->heads * 2, thp * 2, tbc, tbc, hv, hv, hv, st,
-                            a->cu_seqlens ? (static_cast<size_t>(nseq) + 1) * 4 : 0, 0};
+                            a->cu_seqlens ? (static_cast<size_t>(pl.nseq) + 1) * 4 : 0, 0};
   for (int k = 0; k < 10; ++k) {
     if (overlap(a->y, thp * oe, ins[k], in_sz[k])) return SAMBA_ERR_ALIASING;
     if (a->h_last && !(k == 8 && a->h_last == a->h0) && overlap(a->h_last, st, ins[k], in_sz[k]))
       return SAMBA_ERR_ALIASING;
+    if (overlap(a->workspace, pl.ws_bytes, ins[k], in_sz[k])) return SAMBA_ERR_ALIASING;
   }
   if (overlap(a->y, thp * oe, a->h_last, st)) return SAMBA_ERR_ALIASING;
+  if (overlap(a->workspace, pl.ws_bytes, a->y, thp * oe) || overlap(a->workspace, pl.ws_bytes, a->h_last, st))
+    return SAMBA_ERR_ALIASING;
 
   SsdParams p{};
   p.x = a->x; p.dt = a->dt; p.z = a->z; p.B = a->B; p.C = a->C;
   p.A = a->A; p.Dskip = a->D; p.bias = a->dt_bias; p.h0 = a->h0; p.h_last = a->h_last; p.y = a->y;
+  p.ws = static_cast<float*>(a->workspace);
   p.cu = a->cu_seqlens;
-  p.nseq = static_cast<int32_t>(nseq);
+  p.nseq = static_cast<int32_t>(pl.nseq);
   p.seqlen = a->seqlen;
   p.heads = a->heads;
   p.ngroups = a->ngroups;
   p.total = a->seqlen;
-  const dim3 grid(static_cast<uint32_t>(nseq * a->heads));
+  p.nch = static_cast<int32_t>(pl.nch);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool gate = a->z != nullptr;
+  const int64_t nblocks = pl.nseq * a->heads;
+  const int64_t nslots = tokens > 0 ? pl.nslots : 0;
   hipError_t e;
-  if (a->y_dtype == SAMBA_BF16)
-    e = N == 64 ? launch_ssd<uint16_t, 64>(p, gate, grid, s) : launch_ssd<uint16_t, 128>(p, gate, grid, s);
-  else
-    e = N == 64 ? launch_ssd<float, 64>(p, gate, grid, s) : launch_ssd<float, 128>(p, gate, grid, s);
+  // (no tokens: no chunk, no workspace read; every sequence's h_last is its h0, or zero)
+  if (a->y_dtype == SAMBA_BF16) {
+    e = N == 64 ? launch_ssd<uint16_t, 64>(p, gate, nslots, nblocks, s) : launch_ssd<uint16_t, 128>(p, gate, nslots, nblocks, s);
+  } else {
+    e = N == 64 ? launch_ssd<float, 64>(p, gate, nslots, nblocks, s) : launch_ssd<float, 128>(p, gate, nslots, nblocks, s);
+  }
   return e == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
 }

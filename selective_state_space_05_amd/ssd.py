@@ -26,7 +26,8 @@ class SsdArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("batch", _I32), ("seqlen", _I32), ("heads", _I32),
                 ("head_dim", _I32), ("dstate", _I32), ("ngroups", _I32), ("cu_seqlens", _P), ("nseq", _I32),
                 ("y_dtype", _I32), ("x", _P), ("dt", _P), ("z", _P), ("B", _P), ("C", _P), ("A", _P), ("D", _P),
-                ("dt_bias", _P), ("h0", _P), ("h_last", _P), ("y", _P)]
+                ("dt_bias", _P), ("h0", _P), ("h_last", _P), ("y", _P), ("workspace", _P),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 _bound = set()
@@ -38,6 +39,8 @@ def load_library(path=None):
     if id(lib) not in _bound:
         lib.samba_ssd_fwd.argtypes = [ctypes.POINTER(SsdArgs), _P]
         lib.samba_ssd_fwd.restype = ctypes.c_int
+        lib.samba_ssd_workspace_size.argtypes = [ctypes.POINTER(SsdArgs), ctypes.POINTER(ctypes.c_size_t)]
+        lib.samba_ssd_workspace_size.restype = ctypes.c_int
         _bound.add(id(lib))
     return lib
 
@@ -51,6 +54,27 @@ def _shape(x, cu_seqlens):
     if x.dim() == 3:
         return 1, x.shape[0], x.shape[1], x.shape[2], (1 if cu_seqlens is None else cu_seqlens.numel() - 1)
     raise ValueError("x must be [batch][seqlen][heads][head_dim] or [tokens][heads][head_dim]")
+
+
+def workspace_bytes(a: SsdArgs) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().samba_ssd_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    if st != 0:
+        raise SambaError(st, "samba_ssd_workspace_size")
+    return n.value
+
+
+def attach_workspace(a: SsdArgs, device, workspace=None):
+    """Give the args a workspace of the size the call needs (a new uint8 device tensor unless one is passed);
+    returns the tensor, which must outlive the call."""
+    import torch
+    need = workspace_bytes(a)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if workspace.numel() < need:
+        raise ValueError("workspace too small: %d < %d bytes" % (workspace.numel(), need))
+    a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    return workspace
 
 
 def fwd_args(x, dt, B, C, A, D, dt_bias, *, y, z=None, h0=None, h_last=None, cu_seqlens=None) -> SsdArgs:
@@ -68,10 +92,11 @@ def fwd_args(x, dt, B, C, A, D, dt_bias, *, y, z=None, h0=None, h_last=None, cu_
 
 
 def ssd_fwd(x, dt, B, C, A, D, dt_bias, *, z=None, h0=None, h_last=None, y=None, y_dtype=None, cu_seqlens=None,
-            return_last_state: bool = True, stream=None):
+            return_last_state: bool = True, workspace=None, stream=None):
     """Chunked SSD prefill through samba_ssd_fwd.  x bf16 [batch][L][heads][64] (or [tokens][heads][64]);
     dt bf16 [.., heads]; B, C bf16 [.., ngroups][dstate] with dstate 64 or 128; z optional (no gate when
-    None).  Returns (y, h_last) with h_last fp32 [nseq][heads][64][dstate]."""
+    None); workspace: a uint8 device tensor of at least samba_ssd_workspace_size() bytes (allocated per call
+    when None).  Returns (y, h_last) with h_last fp32 [nseq][heads][64][dstate]."""
     import torch
     _check_dev(x, dt, z, B, C, A, D, dt_bias, h0, h_last, y, cu_seqlens)
     batch, seqlen, heads, hd, nseq = _shape(x, cu_seqlens)
@@ -81,7 +106,9 @@ def ssd_fwd(x, dt, B, C, A, D, dt_bias, *, z=None, h0=None, h_last=None, y=None,
     if h_last is None and return_last_state:
         h_last = torch.empty(nseq, heads, hd, N, dtype=torch.float32, device=x.device)
     a = fwd_args(x, dt, B, C, A, D, dt_bias, y=y, z=z, h0=h0, h_last=h_last, cu_seqlens=cu_seqlens)
+    ws = attach_workspace(a, x.device, workspace)
     st = load_library().samba_ssd_fwd(ctypes.byref(a), _P(_stream_handle(stream)))
+    del ws   # torch reuses the freed block only for later work on this stream, which runs after the call
     if st != 0:
         raise SambaError(st, "samba_ssd_fwd")
     return y, h_last

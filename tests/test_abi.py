@@ -606,7 +606,26 @@ def ssd_ok(batch=2, seqlen=100, heads=8, dstate=128, ngroups=2):
     a.x, a.dt, a.z, a.B, a.C = BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB, BASE + 4 * GB
     a.A, a.D, a.dt_bias = BASE + 5 * GB, BASE + 6 * GB, BASE + 7 * GB
     a.h0, a.h_last, a.y = BASE + 8 * GB, BASE + 9 * GB, BASE + 10 * GB
+    a.workspace, a.workspace_bytes = BASE + 12 * GB, GB
     return a
+
+
+def ssd_ws(lib, a):
+    n = ctypes.c_size_t(0)
+    assert lib.samba_ssd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0
+    return n.value
+
+
+@pytest.mark.parametrize("batch,seqlen,G,varlen", [(2, 100, 2, False), (4, 4096, 1, False), (1, 1000, 4, True),
+                                                   (3, 0, 1, False)])
+def test_ssd_workspace_size(lib, batch, seqlen, G, varlen):
+    """12 KiB per (chunk slot, group): batched sequences own ceil(L / 64) slots each, packed streams
+    tokens / 64 + nseq slots; no tokens, no workspace."""
+    a = ssd_ok(batch=batch, seqlen=seqlen, heads=4 * G, ngroups=G)
+    if varlen:
+        a.cu_seqlens, a.nseq = BASE + 11 * GB, 5
+    slots = (batch * seqlen) // 64 + 5 if varlen else batch * -(-seqlen // 64)
+    assert ssd_ws(lib, a) == (slots * G * 12288 if batch * seqlen else 0)
 
 
 SSD_CASES = {
@@ -629,8 +648,15 @@ SSD_CASES = {
     "h_last_overlaps_B": (lambda a: setattr(a, "h_last", a.B + 256), 5),
     "h_last_overlaps_h0_shifted": (lambda a: setattr(a, "h_last", a.h0 + 16), 5),
     "varlen_batch": (lambda a: (setattr(a, "cu_seqlens", BASE + 11 * GB), setattr(a, "nseq", 3)), 2),
-    "offsets_past_32_bits": (lambda a: (setattr(a, "seqlen", 1 << 20), setattr(a, "heads", 64),
+    "offsets_past_31_bits": (lambda a: (setattr(a, "seqlen", 1 << 19), setattr(a, "heads", 64),
                                         setattr(a, "ngroups", 1)), 2),
+    "too_many_heads": (lambda a: (setattr(a, "seqlen", 1), setattr(a, "batch", 1), setattr(a, "heads", 1 << 17),
+                                  setattr(a, "ngroups", 1)), 2),
+    "null_workspace": (lambda a: setattr(a, "workspace", None), 9),
+    "small_workspace": (lambda a: setattr(a, "workspace_bytes", 4096), 9),
+    "misaligned_workspace": (lambda a: setattr(a, "workspace", a.workspace + 128), 9),
+    "workspace_overlaps_y": (lambda a: setattr(a, "workspace", a.y), 5),
+    "workspace_overlaps_C": (lambda a: setattr(a, "workspace", a.C + 256), 5),
 }
 
 
@@ -646,3 +672,7 @@ def test_ssd_noops(lib):
     a = ssd_ok(batch=0)
     assert lib.samba_ssd_fwd(ctypes.byref(a), None) == 0
     assert lib.samba_ssd_fwd(None, None) == 1
+    n = ctypes.c_size_t(7)
+    assert lib.samba_ssd_workspace_size(None, ctypes.byref(n)) == 1
+    assert lib.samba_ssd_workspace_size(ctypes.byref(a), None) == 1
+    assert lib.samba_ssd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == 0
