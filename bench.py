@@ -614,7 +614,8 @@ def bench_ssd(steps: int = 20, warmup: int = 5):
             "mfma_tflops": round(tf, 1), "mfma_frac_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_ssd_traffic(),
-                         "kernel": "ssd_fwd_kernel<bf16,N=%d,gate>" % N, "launch_us": round(ms * 1e3, 2),
+                         "kernel": "ssd_cb_kernel<%d> + ssd_fwd_kernel<bf16,N=%d,gate> (one call)" % (N, N),
+                         "launch_us": round(ms * 1e3, 2),
                          "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops}}
 
 
@@ -863,11 +864,13 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
 
 
 SWA_PMC_RUN = "python3 <repo>/bench.py --swa-only --swa-steps 2 --swa-decode-steps 2 --warmup 1 --copy-probe"
-GROUPS_PMC_RUN = "python3 <repo>/bench.py --groups-only --groups-steps 2 --warmup 1 --copy-probe"  # 2 + 1 prefill calls, 220 steps
+GROUPS_PMC_RUN = "python3 <repo>/bench.py --groups-only --groups-steps 2 --warmup 1 --copy-probe"
+SSD_PMC_RUN = "python3 <repo>/bench.py --ssd-only --ssd-steps 2 --warmup 1 --copy-probe"  # 2 + 1 prefill calls, 220 steps
 
 
 def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
-    """HBM bytes per launch of the attention kernels (which = "swa") or the grouped prefill ("groups") from
+    """HBM bytes per launch of the attention kernels (which = "swa"), the grouped prefill ("groups") or the SSD
+    prefill ("ssd") from
     two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), each calibrated by the 512 MiB copy of the same run (as
     pmc_summary does for the scan)."""
     import csv
@@ -900,6 +903,15 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
         note = ("Algorithmic bytes: prefill q, k, v read once and o written once (the window's re-reads of K and V "
                 "are meant to hit L2); RoPE q, k read and written plus the tables; decode the window's cached K "
                 "and V, the new q, k, v, the cache write and o.")
+    elif which == "ssd":
+        wl = I.WORKLOADS[9]
+        Bt, L, H, P, N, G = (wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.dstate,
+                             wl.extra["ngroups"])
+        sel = {"ssd": ("ssd_fwd_kernel<unsigned short, 128, true>", ssd_bytes(Bt, L, H, P, G, N))}
+        src_hash, run, flag = ssd_hash(), SSD_PMC_RUN, "--pmc-summary-ssd"
+        note = ("Algorithmic bytes: x, z read and y written once (bf16), dt, B and C once, parameters, h_last "
+                "out. The workspace of C B^T tiles (3 MiB, written by the small pre-pass kernel and read from L2) "
+                "is not counted in the algorithmic bytes.")
     else:
         wl = I.WORKLOADS[8]
         Bt, L, D, N, G = wl.batch, wl.seqlen, wl.dim, wl.dstate, wl.extra["ngroups"]
@@ -1093,6 +1105,8 @@ def main():
                     help="the same for the attention kernels (counter runs of the --swa-only legs)")
     ap.add_argument("--pmc-summary-groups", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="the same for the grouped prefill (counter runs of the --groups-only leg)")
+    ap.add_argument("--pmc-summary-ssd", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="the same for the SSD prefill (counter runs of the --ssd-only leg)")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
@@ -1102,6 +1116,9 @@ def main():
         return
     if args.pmc_summary_groups:
         _counter_summary(*args.pmc_summary_groups, which="groups")
+        return
+    if args.pmc_summary_ssd:
+        _counter_summary(*args.pmc_summary_ssd, which="ssd")
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1",

@@ -8,7 +8,9 @@ The oracle writes the layer as its recurrence (a scalar decay per head, a P x N 
     dim = heads * P channels, each head's P channels reading its group's (B, C);
   * carrying h_last into h0 over a split, packed sequences against separate calls, batched rows against
     packed ones;
-  * planted mistakes in the recurrence and its indexing are rejected by the quadratic form.
+  * planted mistakes in the recurrence and its indexing are rejected by the quadratic form;
+  * with a unit step (Δ = 1) and A = ln γ per head the layer is multi-scale retention, checked against the
+    retention's parallel form.
 """
 import shutil
 
@@ -183,3 +185,29 @@ def test_ssd_mutant_is_caught(tmp_path, name):
         yq, hq = quadratic_form(p)
         bad |= rel_err(y[seq_start[i]:seq_start[i + 1]], yq) > 1e-6 or rel_err(hl[i], hq) > 1e-6
     assert bad, "quadratic form did not reject mutant " + name
+
+
+def retention_parallel(q, k, v, gammas):
+    """Multi-scale retention in its parallel form (the hackernoon page "Microsoft's Samba Model Redefines
+    Long-Context Learning for AI", §2, names Multi-Scale Retention and GLA as substitutes for the Mamba
+    layer; the form is the retention paper's): per head, O = (Q Kᵀ ∘ Γ) V with Γ[t][s] = γ^(t - s), s <= t."""
+    L, H, _ = v.shape
+    o = np.zeros_like(v)
+    idx = np.arange(L)
+    for h in range(H):
+        gam = np.where(idx[:, None] >= idx[None, :], gammas[h] ** (idx[:, None] - idx[None, :]).astype(float), 0.0)
+        o[:, h] = ((q[:, h] @ k[:, h].T) * gam) @ v[:, h]
+    return o
+
+
+def test_retention_is_ssd_with_unit_step():
+    """Δ = softplus(0 + ln(e - 1)) = 1 and A = ln γ make the layer multi-scale retention: state S_t =
+    γ S_{t-1} + k_t v_tᵀ read out by q_t (B = k, C = q per head, x = v, no skip, no gate), with RetNet's
+    decays γ_h = 1 - 2^(-5-h)."""
+    g = np.random.default_rng(60)
+    L, H, P, N = 45, 4, 3, 5
+    q, k = g.standard_normal((L, H, N)), g.standard_normal((L, H, N))
+    v = g.standard_normal((L, H, P))
+    gammas = 1.0 - 2.0 ** (-5.0 - np.arange(H))
+    y, _ = O.ssd(v, np.zeros((L, H)), k, q, np.log(gammas), np.zeros(H), np.full(H, np.log(np.e - 1.0)))
+    assert rel_err(y, retention_parallel(q, k, v, gammas)) < 1e-12
