@@ -35,8 +35,9 @@
  * The gradients of the prefill (oracle_scan_bwd) are the reverse-mode
  * derivative of exactly that loop; the formulas stand above the function.
  *
- * The Mamba-2 form the pages compare with (oracle_ssd: scalar decay per head,
- * a matrix state per head) is written out the same way, as its recurrence.
+ * Gated linear attention (oracle_gla: a decay per key dimension and token) and
+ * the Mamba-2 form the pages compare with (oracle_ssd: scalar decay per head,
+ * a matrix state per head) are written out the same way, as their recurrences.
  *
  * The other layer of the hybrid, sliding-window attention (oracle_swa), is
  * the definition written out per query: rotate, score the visible keys,
@@ -510,6 +511,53 @@ int oracle_ssd(int64_t nseq, const int64_t* seq_start, int64_t H, int64_t P, int
       }
       if (h_last)
         for (int64_t k = 0; k < P * N; ++k) h_last[(s * H + h) * P * N + k] = st[k];
+      free(st);
+    }
+  }
+  (void)nthreads;
+  return failed ? -1 : 0;
+}
+
+/*
+ * Gated linear attention (the hackernoon page, §2, names GLA with Multi-Scale Retention as substitutes for
+ * the Mamba layer; the recurrence is the GLA paper's): per head h a key-by-value state S with a decay per key
+ * dimension that depends on the token,
+ *   S_t[n][p] = exp(gk[t][h][n]) S_{t-1}[n][p] + k[t][h][n] v[t][h][p],   o[t][h][p] = sum_n q[t][h][n] S_t[n][p]
+ * q, k, gk [T][H][N] (gk = log of the decay, <= 0), v, o [T][H][P], h0, h_last [nseq][H][P][N] (the state
+ * stored value-major, S^T).  Each (sequence, head, value column p) is one sequential loop over its tokens.
+ */
+int oracle_gla(int64_t nseq, const int64_t* seq_start, int64_t H, int64_t P, int64_t N, const double* q,
+               const double* k, const double* v, const double* gk, const double* h0, double* o,
+               double* h_last, int nthreads) {
+  if (nseq < 0 || H < 1 || P < 1 || N < 1 || !seq_start) return -1;
+  for (int64_t s = 0; s < nseq; ++s)
+    if (seq_start[s + 1] < seq_start[s]) return -1;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(nthreads) reduction(| : failed)
+#endif
+  for (int64_t s = 0; s < nseq; ++s) {
+    for (int64_t h = 0; h < H; ++h) {
+      double* st = (double*)malloc((size_t)(P * N) * sizeof(double));
+      if (!st) { failed = 1; continue; }
+      for (int64_t i = 0; i < P * N; ++i) st[i] = h0 ? h0[(s * H + h) * P * N + i] : 0.0;
+      for (int64_t t = seq_start[s]; t < seq_start[s + 1]; ++t) {
+        const double* qt = q + (t * H + h) * N;
+        const double* kt = k + (t * H + h) * N;
+        const double* gt = gk + (t * H + h) * N;
+        for (int64_t p = 0; p < P; ++p) {
+          const double vp = v[(t * H + h) * P + p];
+          double acc = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            st[p * N + n] = exp(gt[n]) * st[p * N + n] + kt[n] * vp;
+            acc += qt[n] * st[p * N + n];
+          }
+          o[(t * H + h) * P + p] = acc;
+        }
+      }
+      if (h_last)
+        for (int64_t i = 0; i < P * N; ++i) h_last[(s * H + h) * P * N + i] = st[i];
       free(st);
     }
   }

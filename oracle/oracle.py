@@ -65,6 +65,8 @@ def _bind(lib):
     lib.oracle_scan_fwd_groups.restype = ctypes.c_int
     lib.oracle_ssd.argtypes = [I64, P, I64, I64, I64, I64] + [P] * 11 + [ctypes.c_int]
     lib.oracle_ssd.restype = ctypes.c_int
+    lib.oracle_gla.argtypes = [I64, P, I64, I64, I64] + [P] * 7 + [ctypes.c_int]
+    lib.oracle_gla.restype = ctypes.c_int
     lib.oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -308,6 +310,38 @@ def ssd(x, dt, B, C, A, D, dt_bias, z=None, h0=None, seq_start=None, nthreads: i
     if rc != 0:
         raise RuntimeError("oracle_ssd failed (%d)" % rc)
     return y.reshape(shape), h_last
+
+
+def gla(q, k, v, gk, h0=None, seq_start=None, nthreads: int = 0, lib=None):
+    """Gated linear attention in fp64 (its recurrence).  q, k, gk [T][H][N] (or [batch][L][H][N]), v [T][H][P],
+    h0 [nseq][H][P][N] or None.  Returns (o like v, h_last [nseq][H][P][N])."""
+    lib = lib or load()
+    v = _f64(v)
+    shape = v.shape
+    if v.ndim == 4:
+        b, L, H, P = shape
+        if seq_start is None:
+            seq_start = np.arange(b + 1, dtype=np.int64) * L
+        v = v.reshape(b * L, H, P)
+        q, k, gk = (_f64(a).reshape(b * L, H, -1) for a in (q, k, gk))
+    else:
+        H, P = shape[1], shape[2]
+        if seq_start is None:
+            seq_start = np.array([0, shape[0]], dtype=np.int64)
+        q, k, gk = _f64(q), _f64(k), _f64(gk)
+    T, N = v.shape[0], q.shape[2]
+    assert q.shape == k.shape == gk.shape == (T, H, N)
+    seq_start = np.ascontiguousarray(np.asarray(seq_start, dtype=np.int64))
+    nseq = len(seq_start) - 1
+    assert seq_start[0] == 0 and seq_start[-1] == T
+    h0 = None if h0 is None else _f64(h0).reshape(nseq, H, P, N)
+    o = np.empty((T, H, P))
+    h_last = np.empty((nseq, H, P, N))
+    rc = lib.oracle_gla(nseq, _ptr(seq_start), H, P, N, _ptr(q), _ptr(k), _ptr(v), _ptr(gk), _ptr(h0), _ptr(o),
+                        _ptr(h_last), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_gla failed (%d)" % rc)
+    return o.reshape(shape), h_last
 
 
 def scan_step(state, x, dt, z, B, C, A, D, dt_bias, nthreads: int = 0, lib=None):
