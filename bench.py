@@ -56,6 +56,8 @@ GROUPS_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_scan_groups
 GROUPS_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_groups.json"
 SSD_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_ssd.hip"
 SSD_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_ssd.json"
+GLA_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_gla.hip"
+GLA_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_gla.json"
 
 
 def groups_bytes(batch: int, L: int, dim: int, ngroups: int, n: int) -> int:
@@ -124,6 +126,22 @@ def read_groups_traffic(part: str = "groups"):
     if t.get("kernel_source_sha256_16") != groups_hash():
         return None
     return t.get(part, {}).get("bytes_per_launch")
+
+
+def gla_hash() -> str:
+    return hashlib.sha256(GLA_SRC.read_bytes()).hexdigest()[:16]
+
+
+def read_gla_traffic():
+    """HBM bytes per launch of the GLA kernel from the committed counter runs, if they were taken on this
+    kernel source."""
+    try:
+        t = json.loads(GLA_TRAFFIC_FILE.read_text())
+    except Exception:
+        return None
+    if t.get("kernel_source_sha256_16") != gla_hash():
+        return None
+    return t.get("gla", {}).get("bytes_per_launch")
 
 
 def ssd_hash() -> str:
@@ -638,6 +656,81 @@ def cpu_baseline_ssd():
             "sample": "the whole workload (%d x %d tokens, %d heads), fp64 oracle, %.1f s" % (Bt, L, H, spent)}
 
 
+def gla_bytes(batch: int, L: int, heads: int, n: int, pv: int) -> int:
+    """Algorithmic bytes of one GLA call: q, k, gk and v read, o written once (bf16), h_last out (fp32)."""
+    T = batch * L
+    return T * heads * (3 * n + 2 * pv) * 2 + batch * heads * pv * n * 4
+
+
+def gla_slots(batch: int, L: int, heads: int, n: int, pv: int) -> int:
+    """Algorithmic issue slots of the recurrence: per (token, value column, key) the decay multiply, the
+    k v FMA and the readout FMA (3); per (token, head, key) the decay exp (4) and its scaling (1)."""
+    T = batch * L
+    return T * heads * pv * n * 3 + T * heads * n * 5
+
+
+def bench_gla(steps: int = 5, warmup: int = 2):
+    """samba_gla_fwd on B4 L4096 with 4 heads, keys 256, values 512 (bf16 I/O, fp32 state)."""
+    import torch
+    from selective_state_space_05_amd import gla as GL
+    from selective_state_space_05_amd import inputs as I
+
+    wl = I.WORKLOADS[10]
+    Bt, L, H, N, P = wl.batch, wl.seqlen, wl.extra["heads"], wl.dstate, wl.extra["head_dim"]
+    dev = torch.device("cuda:0")
+    t = I.make_gla_inputs_torch(10, Bt * L, H, N, P, dev)
+    q, k, gk = (t[n].view(Bt, L, H, N) for n in ("q", "k", "gk"))
+    v = t["v"].view(Bt, L, H, P)
+    o = torch.empty_like(v)
+    hl = torch.empty(Bt, H, P, N, dtype=torch.float32, device=dev)
+    a = GL.fwd_args(q, k, v, gk, o=o, h_last=hl)
+    lib = GL.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    ref = ctypes.byref(a)
+
+    def call():
+        if lib.samba_gla_fwd(ref, sh) != 0:
+            raise RuntimeError("samba_gla_fwd failed")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = _timed(call, steps, stream)
+    slots = gla_slots(Bt, L, H, N, P)
+    achieved = slots / (ms * 1e-3) / 1e12
+    nbytes = gla_bytes(Bt, L, H, N, P)
+    return {"workload": "GLA B=%d L=%d, %d heads, keys %d, values %d, bf16 I/O, fp32 state" % (Bt, L, H, N, P),
+            "steps": steps, "ms_per_call": ms, "tokens_per_s": Bt * L / (ms * 1e-3),
+            "token_columns_per_s": Bt * L * H * P / (ms * 1e-3), "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TSLOT, 2),
+                         "unit": "Tslot/s", "frac": round(achieved / VALU_PEAK_TSLOT, 4),
+                         "traffic": read_gla_traffic(), "kernel": "gla_fwd_kernel<bf16,bf16,N=%d>" % N, "launch_us": round(ms * 1e3, 2),
+                         "algorithmic_slots_per_launch": slots, "algorithmic_bytes_per_launch": nbytes}}
+
+
+def cpu_baseline_gla(columns: int = 32):
+    """The fp64 oracle's GLA on the workload's 4 sequences and 4 heads, `columns` of the 512 value columns,
+    in token·columns/s (the GPU figure is token_columns_per_s).  The oracle runs one thread per (sequence,
+    head): 16 at most."""
+    import numpy as np
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+
+    wl = I.WORKLOADS[10]
+    Bt, L, H, N, P = wl.batch, wl.seqlen, wl.extra["heads"], wl.dstate, wl.extra["head_dim"]
+    inp = I.make_gla_inputs_np(10, Bt * L, H, N, P)
+    lib = O.load()
+    t0 = time.perf_counter()
+    O.gla(inp["q_f32"], inp["k_f32"], np.ascontiguousarray(inp["v_f32"][:, :, :columns]), inp["gk_f32"],
+          seq_start=np.arange(Bt + 1, dtype=np.int64) * L, lib=lib)
+    spent = time.perf_counter() - t0
+    return {"value": Bt * L * H * columns / spent, "unit": "token*columns/s",
+            "cores": min(O.max_threads(lib), Bt * H), "kind": "oracle",
+            "sample": "4 sequences of 4096 tokens, 4 heads, %d of the 512 value columns, fp64 oracle, %.1f s"
+                      % (columns, spent)}
+
+
 def bench_swa(steps: int = 20, warmup: int = 5):
     """The sliding-window attention layer of Samba-3.8B on the training shape: batch 4 x 4096 tokens, 24 heads
     of 128, window 2048, bf16 q/k/v/o.  One layer pass = RoPE of q and k, then the attention."""
@@ -865,12 +958,13 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
 
 SWA_PMC_RUN = "python3 <repo>/bench.py --swa-only --swa-steps 2 --swa-decode-steps 2 --warmup 1 --copy-probe"
 GROUPS_PMC_RUN = "python3 <repo>/bench.py --groups-only --groups-steps 2 --warmup 1 --copy-probe"
-SSD_PMC_RUN = "python3 <repo>/bench.py --ssd-only --ssd-steps 2 --warmup 1 --copy-probe"  # 2 + 1 prefill calls, 220 steps
+SSD_PMC_RUN = "python3 <repo>/bench.py --ssd-only --ssd-steps 2 --warmup 1 --copy-probe"
+GLA_PMC_RUN = "python3 <repo>/bench.py --gla-only --gla-steps 2 --warmup 1 --copy-probe"  # 2 + 1 prefill calls, 220 steps
 
 
 def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
-    """HBM bytes per launch of the attention kernels (which = "swa"), the grouped prefill ("groups") or the SSD
-    prefill ("ssd") from
+    """HBM bytes per launch of the attention kernels (which = "swa"), the grouped prefill ("groups"), the SSD
+    prefill ("ssd") or gated linear attention ("gla") from
     two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), each calibrated by the 512 MiB copy of the same run (as
     pmc_summary does for the scan)."""
     import csv
@@ -903,6 +997,12 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
         note = ("Algorithmic bytes: prefill q, k, v read once and o written once (the window's re-reads of K and V "
                 "are meant to hit L2); RoPE q, k read and written plus the tables; decode the window's cached K "
                 "and V, the new q, k, v, the cache write and o.")
+    elif which == "gla":
+        wl = I.WORKLOADS[10]
+        Bt, L, H, N, P = wl.batch, wl.seqlen, wl.extra["heads"], wl.dstate, wl.extra["head_dim"]
+        sel = {"gla": ("gla_fwd_kernel<unsigned short, unsigned short, 256>", gla_bytes(Bt, L, H, N, P))}
+        src_hash, run, flag = gla_hash(), GLA_PMC_RUN, "--pmc-summary-gla"
+        note = "Algorithmic bytes: q, k, gk and v read and o written once (bf16), h_last out."
     elif which == "ssd":
         wl = I.WORKLOADS[9]
         Bt, L, H, P, N, G = (wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.dstate,
@@ -1094,6 +1194,9 @@ def main():
     ap.add_argument("--no-ssd", action="store_true", help="skip the state-space duality leg")
     ap.add_argument("--ssd-steps", type=int, default=20)
     ap.add_argument("--ssd-only", action="store_true", help="run only the state-space duality leg")
+    ap.add_argument("--no-gla", action="store_true", help="skip the gated linear attention leg")
+    ap.add_argument("--gla-steps", type=int, default=5)
+    ap.add_argument("--gla-only", action="store_true", help="run only the gated linear attention leg")
     ap.add_argument("--swa-only", action="store_true",
                     help="run only the attention legs (and the copy probe with --copy-probe): counter runs")
     ap.add_argument("--time-slices", type=int, default=0, help="force the prefill's waves per time chunk (0 = auto)")
@@ -1107,6 +1210,8 @@ def main():
                     help="the same for the grouped prefill (counter runs of the --groups-only leg)")
     ap.add_argument("--pmc-summary-ssd", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="the same for the SSD prefill (counter runs of the --ssd-only leg)")
+    ap.add_argument("--pmc-summary-gla", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="the same for gated linear attention (counter runs of the --gla-only leg)")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
@@ -1120,6 +1225,9 @@ def main():
     if args.pmc_summary_ssd:
         _counter_summary(*args.pmc_summary_ssd, which="ssd")
         return
+    if args.pmc_summary_gla:
+        _counter_summary(*args.pmc_summary_gla, which="gla")
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1",
               file=sys.stderr)
@@ -1127,6 +1235,12 @@ def main():
 
     if args.groups_only:
         out = {"groups": bench_groups(args.groups_steps, min(args.warmup, 3)), "groups_decode": bench_groups_step()}
+        if args.copy_probe:
+            copy_probe()
+        print(json.dumps(out), flush=True)
+        return
+    if args.gla_only:
+        out = {"gla": bench_gla(args.gla_steps, min(args.warmup, 2))}
         if args.copy_probe:
             copy_probe()
         print(json.dumps(out), flush=True)
@@ -1198,6 +1312,8 @@ def main():
         line["groups_decode"] = bench_groups_step()
     if not args.no_ssd:
         line["ssd"] = bench_ssd(args.ssd_steps)
+    if not args.no_gla:
+        line["gla"] = bench_gla(args.gla_steps)
     if not args.no_swa:
         line["attention"] = bench_swa(args.swa_steps)
         line["attention_decode"] = bench_swa_decode(args.swa_decode_steps)
@@ -1214,6 +1330,8 @@ def main():
             line["cpu_baseline"]["groups"] = cpu_baseline_groups()
         if not args.no_ssd:
             line["cpu_baseline"]["ssd"] = cpu_baseline_ssd()
+        if not args.no_gla:
+            line["cpu_baseline"]["gla"] = cpu_baseline_gla()
         if not args.no_swa:
             line["cpu_baseline"]["attention"] = cpu_baseline_swa()
             line["cpu_baseline"]["attention_decode"] = cpu_baseline_swa_decode()

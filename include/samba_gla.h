@@ -1,0 +1,58 @@
+/*
+ * samba_gla.h -- C ABI of the MI355X (gfx950) gated linear attention layer,
+ * which the hackernoon page "Microsoft's Samba Model Redefines Long-Context
+ * Learning for AI" (§2) names, with Multi-Scale Retention, as a substitute
+ * for the Mamba layer.  The page gives no formula; this library computes the
+ * GLA paper's recurrence, per head h, with a decay per key dimension that
+ * depends on the token:
+ *     S_t[n][p] = exp(gk[t][h][n]) S_{t-1}[n][p] + k[t][h][n] v[t][h][p]
+ *     o[t][h][p] = sum_n q[t][h][n] S_t[n][p]
+ * gk is the log of the decay (<= 0; the gate's projection and any 1/sqrt(d)
+ * scaling of q are the caller's).  The output normalisation and gate that
+ * follow in the GLA layer are separate layers.
+ *
+ * Layout: q, k, gk [tokens][heads][dstate] (dstate = the key size N);
+ * v, o [tokens][heads][head_dim] (head_dim = the value size P); h0, h_last
+ * fp32 [nseq][heads][head_dim][dstate] (the state stored value-major).
+ * Tokens: batch * seqlen rows, or packed sequences given by cu_seqlens as for
+ * samba_scan_fwd.  q, k, v, gk share in_dtype (bf16 or fp32); o is y_dtype;
+ * the state and all arithmetic are fp32.  Supported: dstate 16, 32, 64, 128
+ * or 256, head_dim a multiple of 8 (16 at dstate 16), heads * head_dim * 4 * tokens
+ * of a sequence below 2^32.  Alignment: h0, h_last 16 bytes; q, k, gk 16
+ * bytes; v, o their element size.  o and h_last must not overlap any input,
+ * except h_last == h0 exactly (the final state written in place).
+ *
+ * Computed as the recurrence (a diagonal scan per (head, value column), the
+ * key dimension split over dstate / 4 lanes), which is exact and needs no
+ * workspace; ownership, asynchrony and errors as for samba_scan.h.
+ */
+#ifndef SAMBA_GLA_H
+#define SAMBA_GLA_H
+
+#include "samba_scan.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  uint32_t struct_size;        /* = sizeof(samba_gla_args) */
+  int32_t batch, seqlen;
+  int32_t heads, head_dim, dstate;
+  const int32_t* cu_seqlens;   /* optional, device int32 [nseq + 1] (batch must be 1) */
+  int32_t nseq;
+  int32_t in_dtype, y_dtype;   /* samba_dtype values */
+  const void *q, *k, *gk;      /* [tokens][heads][dstate] */
+  const void* v;               /* [tokens][heads][head_dim] */
+  const float* h0;             /* optional [nseq][heads][head_dim][dstate] */
+  float* h_last;               /* optional, same shape */
+  void* o;                     /* [tokens][heads][head_dim] */
+} samba_gla_args;
+
+samba_status samba_gla_fwd(const samba_gla_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAMBA_GLA_H */

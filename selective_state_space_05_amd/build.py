@@ -13,8 +13,9 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 SRCS = (PKG / "csrc" / "samba_scan.hip", PKG / "csrc" / "samba_scan_groups.hip", PKG / "csrc" / "samba_swa.hip",
-        PKG / "csrc" / "samba_ssd.hip")
-HEADERS = (ROOT / "include" / "samba_scan.h", ROOT / "include" / "samba_swa.h", ROOT / "include" / "samba_ssd.h")
+        PKG / "csrc" / "samba_ssd.hip", PKG / "csrc" / "samba_gla.hip")
+HEADERS = (ROOT / "include" / "samba_scan.h", ROOT / "include" / "samba_swa.h", ROOT / "include" / "samba_ssd.h",
+           ROOT / "include" / "samba_gla.h")
 LIB = PKG / "libsamba_scan.so"
 
 HIPCC_FLAGS = [

@@ -42,7 +42,7 @@ import numpy as np
 SEED_ROOT = 20240611
 TENSOR_IDS = {"x": 0, "z": 1, "dt": 2, "dt_init": 3, "A": 4, "B": 5, "C": 6, "D": 7,
               "lengths": 8, "h0": 9, "dy": 10, "dh_last": 11, "W_sel": 12, "q": 13, "k": 14, "v": 15,
-              "pos": 16}
+              "pos": 16, "gk": 17}
 ROPE_BASE = 10000.0
 DECODE_RING_BASE = 100
 DSTATE = 16
@@ -116,6 +116,10 @@ WORKLOADS = {
     # (B, C) group of 128 states
     9: Workload(9, "ssd_fwd B4 L4096 H64 P64 N128 G1 bf16", 4, 4096, 4096, dstate=128,
                 extra={"heads": 64, "head_dim": 64, "ngroups": 1}),
+    # gated linear attention at the GLA paper's 1.3B shape on the training shape: model width 2048, 4 heads,
+    # key size 256 (half the width over 4 heads), value size 512
+    10: Workload(10, "gla_fwd B4 L4096 H4 K256 V512 bf16", 4, 4096, 2048, dstate=256,
+                 extra={"heads": 4, "head_dim": 512}),
 }
 
 
@@ -396,3 +400,40 @@ def make_ssd_inputs_torch(cfg_id: int, rows: int, heads: int, ngroups: int, dsta
 
 def make_ssd_h0(cfg_id: int, nseq: int, heads: int, dstate: int, head_dim: int = 64, scale: float = 1.0):
     return (scale * _rng(cfg_id, TENSOR_IDS["h0"]).standard_normal((nseq, heads, head_dim, dstate))).astype(np.float32)
+
+
+# --------------------------------------------------------------------------- #
+# gated linear attention: q, k, log decay gk [tokens][heads][N], v [tokens][heads][P]
+# --------------------------------------------------------------------------- #
+def _gla_values(cfg_id: int, rows: int, heads: int, dstate: int, head_dim: int) -> dict:
+    """fp32 values before the bf16 rounding: q ~ N(0,1)/sqrt(N), k, v ~ N(0,1), gk = logsigmoid(N(0,1)) / 16
+    (the GLA paper's gate with temperature 16: decays in (0, 1), mostly close to 1)."""
+    q = _normal(cfg_id, "q", (rows, heads, dstate)) / np.float32(math.sqrt(dstate))
+    k = _normal(cfg_id, "k", (rows, heads, dstate))
+    v = _normal(cfg_id, "v", (rows, heads, head_dim))
+    g = _normal(cfg_id, "gk", (rows, heads, dstate)).astype(np.float64)
+    gk = (-np.logaddexp(0.0, -g) / 16.0).astype(np.float32)
+    return {"q": q, "k": k, "v": v, "gk": gk}
+
+
+def make_gla_inputs_np(cfg_id: int, rows: int, heads: int, dstate: int, head_dim: int, in_dtype: str = "bf16") -> dict:
+    """q, k, gk [rows][heads][dstate], v [rows][heads][head_dim]: device representation and *_f32 (exact values)."""
+    out = {}
+    for name, v in _gla_values(cfg_id, rows, heads, dstate, head_dim).items():
+        if in_dtype == "bf16":
+            bits = bf16_bits_from_f32(v)
+            out[name], out[name + "_f32"] = bits, f32_from_bf16_bits(bits)
+        else:
+            out[name], out[name + "_f32"] = v, v
+    return out
+
+
+def make_gla_inputs_torch(cfg_id: int, rows: int, heads: int, dstate: int, head_dim: int, device) -> dict:
+    """The same distributions generated on the device (bf16)."""
+    import torch
+    q = _torch_normal(torch, (rows, heads, dstate), cfg_id, TENSOR_IDS["q"], device, torch.float32)
+    k = _torch_normal(torch, (rows, heads, dstate), cfg_id, TENSOR_IDS["k"], device, torch.bfloat16)
+    v = _torch_normal(torch, (rows, heads, head_dim), cfg_id, TENSOR_IDS["v"], device, torch.bfloat16)
+    g = _torch_normal(torch, (rows, heads, dstate), cfg_id, TENSOR_IDS["gk"], device, torch.float32)
+    return {"q": (q / math.sqrt(dstate)).to(torch.bfloat16), "k": k, "v": v,
+            "gk": (torch.nn.functional.logsigmoid(g) / 16.0).to(torch.bfloat16)}

@@ -1,6 +1,6 @@
 """Python binding of libsamba_scan.so (the C ABI in include/samba_scan.h; the
 attention entry points of include/samba_swa.h are bound in swa.py, the state-space
-duality prefill of include/samba_ssd.h in ssd.py).
+duality prefill of include/samba_ssd.h in ssd.py, gated linear attention of include/samba_gla.h in gla.py).
 
 Argument marshalling only: every step of the scan runs in the HIP kernels of
 the shared library.  torch provides device memory and the current stream.  If
@@ -13,7 +13,7 @@ from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "libsamba_scan.so"
 DSTATE = 16
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 SAMBA_F32, SAMBA_BF16 = 0, 1
 STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE", 3: "SAMBA_ERR_BAD_DTYPE",
@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE"
 EXPORTED = ("samba_scan_fwd", "samba_scan_step", "samba_scan_fwd_plan", "samba_scan_bwd",
             "samba_scan_bwd_workspace_size", "samba_scan_ckpt_bytes", "samba_proj", "samba_status_string",
             "samba_scan_abi_version", "samba_rope", "samba_swa_fwd", "samba_swa_decode", "samba_scan_fwd_groups",
-            "samba_scan_step_groups", "samba_ssd_fwd", "samba_ssd_workspace_size")
+            "samba_scan_step_groups", "samba_ssd_fwd", "samba_ssd_workspace_size",
+            "samba_gla_fwd")
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32

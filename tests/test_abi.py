@@ -12,6 +12,7 @@ from pathlib import Path
 import pytest
 
 from selective_state_space_05_amd import scan as S
+from selective_state_space_05_amd import gla as GL
 from selective_state_space_05_amd import ssd as D
 from selective_state_space_05_amd import swa as W
 
@@ -23,6 +24,7 @@ HEADERS = sorted((ROOT / "include").glob("*.h"))
 @pytest.fixture(scope="module")
 def lib():
     D.load_library()
+    GL.load_library()
     return W.load_library()
 
 
@@ -58,13 +60,13 @@ STRUCTS = (("samba_scan_fwd_args", S.FwdArgs), ("samba_scan_step_args", S.StepAr
            ("samba_scan_bwd_args", S.BwdArgs), ("samba_proj_args", S.ProjArgs), ("samba_rope_args", W.RopeArgs),
            ("samba_swa_fwd_args", W.SwaFwdArgs), ("samba_swa_decode_args", W.SwaDecodeArgs),
            ("samba_scan_groups_args", S.GroupsArgs), ("samba_scan_step_groups_args", S.StepGroupsArgs),
-           ("samba_ssd_args", D.SsdArgs))
+           ("samba_ssd_args", D.SsdArgs), ("samba_gla_args", GL.GlaArgs))
 
 
 def test_struct_layout_matches_header(tmp_path):
     """Compile a C probe against the header and compare sizeof/offsetof with the ctypes mirrors."""
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "samba_scan.h"', '#include "samba_swa.h"',
-             '#include "samba_ssd.h"', 'int main(void) {']
+             '#include "samba_ssd.h"', '#include "samba_gla.h"', 'int main(void) {']
     for cname, py in STRUCTS:
         lines.append('printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
         for f, _ in py._fields_:
@@ -676,3 +678,53 @@ def test_ssd_noops(lib):
     assert lib.samba_ssd_workspace_size(None, ctypes.byref(n)) == 1
     assert lib.samba_ssd_workspace_size(ctypes.byref(a), None) == 1
     assert lib.samba_ssd_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == 0
+
+
+# --------------------------------------------------------------------------- #
+# gated linear attention: validation
+# --------------------------------------------------------------------------- #
+def gla_ok(batch=2, seqlen=100, heads=4, head_dim=64, dstate=128):
+    a = GL.GlaArgs()
+    a.struct_size = ctypes.sizeof(GL.GlaArgs)
+    a.batch, a.seqlen, a.heads, a.head_dim, a.dstate = batch, seqlen, heads, head_dim, dstate
+    a.in_dtype, a.y_dtype = S.SAMBA_BF16, S.SAMBA_F32
+    a.q, a.k, a.gk, a.v = BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB
+    a.h0, a.h_last, a.o = BASE + 4 * GB, BASE + 5 * GB, BASE + 6 * GB
+    return a
+
+
+GLA_CASES = {
+    "struct_size": (lambda a: setattr(a, "struct_size", 4), 7),
+    "dstate_48": (lambda a: setattr(a, "dstate", 48), 6),
+    "dstate_512": (lambda a: setattr(a, "dstate", 512), 6),
+    "head_dim_not_whole_waves": (lambda a: setattr(a, "head_dim", 3), 2),
+    "zero_heads": (lambda a: setattr(a, "heads", 0), 2),
+    "neg_seqlen": (lambda a: setattr(a, "seqlen", -1), 2),
+    "in_dtype": (lambda a: setattr(a, "in_dtype", 5), 3),
+    "null_gk": (lambda a: setattr(a, "gk", None), 1),
+    "misaligned_q": (lambda a: setattr(a, "q", a.q + 8), 4),
+    "misaligned_h0": (lambda a: setattr(a, "h0", a.h0 + 4), 4),
+    "o_overlaps_v": (lambda a: setattr(a, "o", a.v + 64), 5),
+    "h_last_overlaps_k": (lambda a: setattr(a, "h_last", a.k), 5),
+    "h_last_overlaps_h0_shifted": (lambda a: setattr(a, "h_last", a.h0 + 16), 5),
+    "varlen_batch": (lambda a: (setattr(a, "cu_seqlens", BASE + 11 * GB), setattr(a, "nseq", 3)), 2),
+    "offsets_past_32_bits": (lambda a: (setattr(a, "seqlen", 1 << 22), setattr(a, "heads", 16)), 2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GLA_CASES))
+def test_gla_rejects(lib, name):
+    a = gla_ok()
+    mutate, code = GLA_CASES[name]
+    mutate(a)
+    assert lib.samba_gla_fwd(ctypes.byref(a), None) == code
+
+
+def test_gla_noops(lib):
+    a = gla_ok(batch=0)
+    assert lib.samba_gla_fwd(ctypes.byref(a), None) == 0
+    assert lib.samba_gla_fwd(None, None) == 1
+    a = gla_ok()
+    a.h_last = a.h0                     # in place is allowed
+    a.batch = 0
+    assert lib.samba_gla_fwd(ctypes.byref(a), None) == 0
