@@ -17,7 +17,7 @@
  * Tokens: batch * seqlen rows, or packed sequences given by cu_seqlens as for
  * samba_scan_fwd.  q, k, v, gk share in_dtype (bf16 or fp32); o is y_dtype;
  * the state and all arithmetic are fp32.  Supported: dstate 16, 32, 64, 128
- * or 256, head_dim a multiple of 8 (16 at dstate 16), heads * head_dim * 4 * tokens
+ * or 256, head_dim a multiple of 16 (32 at dstate 32, 64 at dstate 16), heads * head_dim * 4 * tokens
  * of a sequence below 2^32.  Alignment: h0, h_last 16 bytes; q, k, gk 16
  * bytes; v, o their element size.  o and h_last must not overlap any input,
  * except h_last == h0 exactly (the final state written in place).

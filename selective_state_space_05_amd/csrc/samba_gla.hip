@@ -2,15 +2,15 @@
 // Samba Model Redefines Long-Context Learning for AI", §2, names as a substitute for the Mamba layer), computed
 // as its recurrence: per head, S_t = diag(exp(gk_t)) S_{t-1} + k_tᵀ v_t, o_t = q_t S_t.
 //
-// The recurrence is a diagonal scan per (head, value column) over the key dimension.  A lane holds 4 key
-// dimensions of C = N / 32 value columns (N / 4 lanes cover the keys, so a wave covers 8 columns of one head),
-// and tokens advance 8 at a time.  The wave stages the chunk's k, q and the decay exp(gk) (computed once per
-// (token, key dimension)) and the 8 columns' v into its own LDS region; every lane runs the 8 updates of its
-// C x 4 states (one multiply and one FMA each) and keeps its partial readouts, C x 8 of them; once per chunk
-// those are reduced over the N / 4 lanes of the keys by a reduce-scatter (v_permlane32_swap and
-// v_permlane16_swap, then LDS swizzles and DPP), after which each lane holds the sum of exactly one
-// (column, token).  The staging is shared by 8 columns and the cross-lane work is one reduce-scatter per
-// chunk rather than a butterfly per token.  No workspace and no workgroup barrier.
+// The recurrence is a diagonal scan per (head, value column) over the key dimension.  A lane holds 4 keys of
+// C value columns (N / 4 lanes cover the keys; C = N / 64 from 64 keys up, so a wave covers 4 columns and a
+// workgroup of 4 waves 16 columns of one head), and tokens advance 16 at a time (8 below 64 keys).  The
+// workgroup stages the chunk's k, q and the decay exp(gk) (once per (token, key)) and its columns' v into
+// LDS, shared by its 4 waves; every lane runs the chunk's updates of its C x 4 states (one multiply and one
+// FMA each) and keeps its partial readouts, C x kT of them; those are reduced over the N / 4 lanes of the
+// keys by one reduce-scatter per chunk (v_permlane32_swap and v_permlane16_swap, then LDS swizzles and DPP),
+// after which each lane holds the sum of exactly one (column, token).  Two barriers per chunk, no workspace;
+// LDS 49 KiB at 256 keys, so three workgroups fit a CU.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -145,30 +145,43 @@ __device__ __forceinline__ void reduce_scatter(float (&v)[K], int lane) {
   }
 }
 
+// Chunk and lane shape per key size N: a lane holds 4 keys of C value columns; tokens advance kT at a time so
+// that the C x kT partial readouts of a lane reduce to whole sums over the N / 4 lanes of the keys.
+template <int N>
+struct GlaShape {
+  static constexpr int kT = N >= 64 ? 16 : 8;            // tokens per chunk
+  static constexpr int LPC = N / 4;                      // lanes per column group
+  static constexpr int GPW = 64 / LPC;                   // column groups per wave
+  static constexpr int C = N >= 64 ? N / 64 : 1;         // value columns per lane
+  static constexpr int CPW = GPW * C;                    // value columns per wave: 4 (8 at N = 32, 16 at 16)
+  static constexpr int CPB = CPW * kWaves;               // value columns per workgroup
+  static constexpr int K = C * kT;                       // partial readouts per lane per chunk
+  static constexpr int R = K / LPC;                      // sums per lane after the reduction
+  static constexpr int VPT = kT * N / 256 > 2 ? kT * N / 256 : 2;   // k, q, gk elements a staging thread moves
+  static constexpr int NST = kT * N / VPT;               // staging threads
+  static constexpr int VV = kT * CPB / 256;              // v elements per thread
+  static_assert(K % LPC == 0 && R >= 1 && VV >= 1 && NST % 64 == 0, "chunk shape");
+};
+
 template <typename Tin, typename Tout, int N>
 __global__ __launch_bounds__(64 * kWaves) void gla_fwd_kernel(GlaParams p) {
-  constexpr int LPC = N / 4;              // lanes per column group (4 key dimensions each)
-  constexpr int GPW = 64 / LPC;           // column groups per wave
-  constexpr int C = N >= 32 ? N / 32 : 1; // value columns per group
-  constexpr int CPW = GPW * C;            // value columns per wave: 8 (16 at N = 16)
-  constexpr int K = C * kTK;              // readout partial sums per lane per chunk
-  constexpr int R = K / LPC;              // sums per lane after the reduction: 1 (2 at N = 16)
-  constexpr int VPL = kTK * N / 64;       // k, q, gk elements each lane stages per chunk
+  using S = GlaShape<N>;
+  constexpr int kT = S::kT, LPC = S::LPC, C = S::C, CPW = S::CPW, CPB = S::CPB, K = S::K, R = S::R;
+  constexpr int VPT = S::VPT, NST = S::NST, VV = S::VV;
   constexpr int ES = sizeof(Tin);
-  constexpr int NW = (VPL * ES + 3) / 4;  // 32-bit words per lane per tensor per chunk
-  constexpr int VV = kTK * CPW / 64;      // v elements each lane stages per chunk
-  static_assert(VPL * ES >= 4, "staging runs of at least one word");
-  static_assert(K % LPC == 0 && CPW * kTK == 64 * VV, "chunk shape");
-  __shared__ __attribute__((aligned(16))) float s_kqd[kWaves][3][kTK][N];   // k, q, decay
-  __shared__ __attribute__((aligned(16))) float s_v[kWaves][kTK][CPW];      // v [token][column]
+  constexpr int NW = (VPT * ES + 3) / 4;  // 32-bit words per staging thread per tensor per chunk
+  static_assert(VPT * ES >= 4, "staging runs of at least one word");
+  // the chunk's k, q and decay exp(gk) of the workgroup's head, and v of its columns, shared by its 4 waves
+  __shared__ __attribute__((aligned(16))) float s_kqd[3][kT][N];
+  __shared__ __attribute__((aligned(16))) float s_v[kT][CPB];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int s = logical / p.ntiles;
   const int tile = logical - s * p.ntiles;
-  const int ch0 = (tile * kWaves + wave) * CPW;
-  if (ch0 >= p.dim) return;               // a whole wave past the last column
+  const int colb = tile * CPB;            // the workgroup's first column (head_dim is a multiple of CPB)
   int64_t t0;
   int32_t len;
   if (p.cu) {
@@ -181,9 +194,10 @@ __global__ __launch_bounds__(64 * kWaves) void gla_fwd_kernel(GlaParams p) {
     t0 = static_cast<int64_t>(s) * p.seqlen;
     len = p.seqlen;
   }
-  const int hd = ch0 / p.head_dim;        // the wave's head (head_dim is a multiple of CPW)
+  const int hd = colb / p.head_dim;
   const int sub = lane % LPC, grp = lane / LPC;
-  const int col0 = ch0 + grp * C;         // this lane's first column
+  const int cw0 = wave * CPW + grp * C;   // this lane's first column inside the workgroup
+  const int col0 = colb + cw0;
 
   // this lane's states S[4 sub + i][column col0 + c]
   float h[C][4];
@@ -199,7 +213,8 @@ __global__ __launch_bounds__(64 * kWaves) void gla_fwd_kernel(GlaParams p) {
   }
   const uint32_t row_bytes = static_cast<uint32_t>(p.dim) * ES;
   const uint32_t kq_row = static_cast<uint32_t>(p.heads) * N * ES;
-  const int e0 = lane * VPL;               // staging run: token e0 / N, key dimensions e0 % N .. + VPL
+  const bool stager = tid < NST;          // whole waves (NST is a multiple of 64)
+  const int e0 = tid * VPT;               // staging run: token e0 / N, keys e0 % N .. + VPT
   const int st_j = e0 / N, st_n = e0 % N;
 
   // chunk loads into registers (rows past the sequence read as 0: k = v = 0 and decay exp(0) = 1 leave the
@@ -209,21 +224,23 @@ __global__ __launch_bounds__(64 * kWaves) void gla_fwd_kernel(GlaParams p) {
   auto load_chunk = [&](int c0) {
     const int64_t tok = t0 + c0;
     const int rows = len - c0;
-    const int64_t remain = static_cast<int64_t>(rows < kTK ? rows : kTK);
+    const int64_t remain = static_cast<int64_t>(rows < kT ? rows : kT);
     const rsrc_t rv = rsrc_bytes(static_cast<const Tin*>(p.v) + tok * p.dim, remain * row_bytes);
 #pragma unroll
     for (int k = 0; k < VV; ++k) {
-      const int i = lane + 64 * k;         // token i / CPW, column i % CPW of the wave
-      ld_elem(rv, static_cast<uint32_t>(i / CPW) * row_bytes + static_cast<uint32_t>(ch0 + i % CPW) * ES, vv[k]);
+      const int i = tid + 256 * k;         // token i / CPB, column i % CPB of the workgroup
+      ld_elem(rv, static_cast<uint32_t>(i / CPB) * row_bytes + static_cast<uint32_t>(colb + i % CPB) * ES, vv[k]);
     }
-    const int64_t kbase = (tok * p.heads + hd) * N;
-    const rsrc_t rk = rsrc_bytes(static_cast<const Tin*>(p.k) + kbase, remain * kq_row);
-    const rsrc_t rq = rsrc_bytes(static_cast<const Tin*>(p.q) + kbase, remain * kq_row);
-    const rsrc_t rg = rsrc_bytes(static_cast<const Tin*>(p.gk) + kbase, remain * kq_row);
-    const uint32_t koff = static_cast<uint32_t>(st_j) * kq_row + static_cast<uint32_t>(st_n) * ES;
-    ld_words<NW>(rk, koff, kw);
-    ld_words<NW>(rq, koff, qw);
-    ld_words<NW>(rg, koff, gw);
+    if (stager) {
+      const int64_t kbase = (tok * p.heads + hd) * N;
+      const rsrc_t rk = rsrc_bytes(static_cast<const Tin*>(p.k) + kbase, remain * kq_row);
+      const rsrc_t rq = rsrc_bytes(static_cast<const Tin*>(p.q) + kbase, remain * kq_row);
+      const rsrc_t rg = rsrc_bytes(static_cast<const Tin*>(p.gk) + kbase, remain * kq_row);
+      const uint32_t koff = static_cast<uint32_t>(st_j) * kq_row + static_cast<uint32_t>(st_n) * ES;
+      ld_words<NW>(rk, koff, kw);
+      ld_words<NW>(rq, koff, qw);
+      ld_words<NW>(rg, koff, gw);
+    }
   };
   auto widen_word = [&](const uint32_t (&w)[NW], int i) -> float {
     if constexpr (ES == 2) return (i & 1) ? __uint_as_float(w[i >> 1] & 0xffff0000u) : __uint_as_float(w[i >> 1] << 16);
@@ -233,58 +250,55 @@ __global__ __launch_bounds__(64 * kWaves) void gla_fwd_kernel(GlaParams p) {
   const rsrc_t ro = rsrc_bytes(static_cast<Tout*>(p.o) + t0 * p.dim, static_cast<int64_t>(len) * p.dim *
                                                                       static_cast<int64_t>(sizeof(Tout)));
   if (len > 0) load_chunk(0);
-  for (int c0 = 0; c0 < len; c0 += kTK) {
-    // publish this chunk: k, q and the decay exp(gk) (once per (token, key dimension)), and v
-    float* sk = &s_kqd[wave][0][st_j][st_n];
-    float* sq = &s_kqd[wave][1][st_j][st_n];
-    float* sd = &s_kqd[wave][2][st_j][st_n];
+  for (int c0 = 0; c0 < len; c0 += kT) {
+    // publish this chunk: k, q and the decay exp(gk) (once per (token, key)), and v
+    if (stager) {
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      sk[i] = widen_word(kw, i);
-      sq[i] = widen_word(qw, i);
-      sd[i] = __builtin_amdgcn_exp2f(widen_word(gw, i) * kLog2e);
+      for (int i = 0; i < VPT; ++i) {
+        s_kqd[0][st_j][st_n + i] = widen_word(kw, i);
+        s_kqd[1][st_j][st_n + i] = widen_word(qw, i);
+        s_kqd[2][st_j][st_n + i] = __builtin_amdgcn_exp2f(widen_word(gw, i) * kLog2e);
+      }
     }
 #pragma unroll
     for (int k = 0; k < VV; ++k) {
-      const int i = lane + 64 * k;
-      s_v[wave][i / CPW][i % CPW] = widen(vv[k]);
+      const int i = tid + 256 * k;
+      s_v[i / CPB][i % CPB] = widen(vv[k]);
     }
-    wave_sync();
-    if (c0 + kTK < len) load_chunk(c0 + kTK);
-    // the chunk's 8 updates of this lane's C x 4 states; partial readouts over its 4 key dimensions
+    __syncthreads();   // chunk staged
+    if (c0 + kT < len) load_chunk(c0 + kT);
+    // the chunk's kT updates of this lane's C x 4 states; partial readouts over its 4 keys
     float part[K];
 #pragma unroll
-    for (int j = 0; j < kTK; ++j) {
-      const float4 k4 = reinterpret_cast<const float4*>(&s_kqd[wave][0][j][0])[sub];
-      const float4 q4 = reinterpret_cast<const float4*>(&s_kqd[wave][1][j][0])[sub];
-      const float4 d4 = reinterpret_cast<const float4*>(&s_kqd[wave][2][j][0])[sub];
+    for (int j = 0; j < kT; ++j) {
+      const float4 k4 = reinterpret_cast<const float4*>(&s_kqd[0][j][0])[sub];
+      const float4 q4 = reinterpret_cast<const float4*>(&s_kqd[1][j][0])[sub];
+      const float4 d4 = reinterpret_cast<const float4*>(&s_kqd[2][j][0])[sub];
       const float kk[4] = {k4.x, k4.y, k4.z, k4.w}, qq[4] = {q4.x, q4.y, q4.z, q4.w};
       const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-      float vc[C];
-#pragma unroll
-      for (int c = 0; c < C; ++c) vc[c] = s_v[wave][j][grp * C + c];
 #pragma unroll
       for (int c = 0; c < C; ++c) {
+        const float vc = s_v[j][cw0 + c];
         float pr = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          h[c][i] = fmaf(dd[i], h[c][i], vc[c] * kk[i]);
+          h[c][i] = fmaf(dd[i], h[c][i], vc * kk[i]);
           pr = fmaf(qq[i], h[c][i], pr);
         }
-        part[c * kTK + j] = pr;
+        part[c * kT + j] = pr;
       }
     }
+    __syncthreads();   // every wave is done with the chunk's LDS
     // sums over the group's LPC lanes: lane l keeps partial indices r + R (l % LPC) = (column, token)
     reduce_scatter<LPC, K>(part, lane);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int idx = r + R * sub;
-      const int c = idx / kTK, j = idx % kTK;
+      const int c = idx / kT, j = idx % kT;
       st_elem(ro, (static_cast<uint32_t>(c0 + j) * p.dim + static_cast<uint32_t>(col0 + c)) *
                       static_cast<uint32_t>(sizeof(Tout)),
               part[r], static_cast<Tout*>(nullptr));
     }
-    wave_sync();   // the next chunk overwrites this wave's LDS
   }
   if (p.h_last) {
 #pragma unroll
@@ -324,8 +338,9 @@ extern "C" samba_status samba_gla_fwd(const samba_gla_args* a, void* stream) {
   if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256) return SAMBA_ERR_UNSUPPORTED;
   if (a->in_dtype != SAMBA_F32 && a->in_dtype != SAMBA_BF16) return SAMBA_ERR_BAD_DTYPE;
   if (a->y_dtype != SAMBA_F32 && a->y_dtype != SAMBA_BF16) return SAMBA_ERR_BAD_DTYPE;
-  // a wave's value columns (8; 16 at dstate 16) share a head
-  if (a->head_dim % (N == 16 ? 16 : 8) != 0) return SAMBA_ERR_BAD_SHAPE;
+  // a workgroup's value columns (16; 32 at dstate 32, 64 at dstate 16) share a head
+  const int cpb = N == 16 ? 64 : (N == 32 ? 32 : 16);
+  if (a->head_dim % cpb != 0) return SAMBA_ERR_BAD_SHAPE;
   int64_t nseq;
   if (a->cu_seqlens) {
     if (a->batch != 1 || a->nseq < 1) return SAMBA_ERR_BAD_SHAPE;
@@ -367,7 +382,6 @@ extern "C" samba_status samba_gla_fwd(const samba_gla_args* a, void* stream) {
   p.head_dim = a->head_dim;
   p.dim = static_cast<int32_t>(dim);
   p.total = a->seqlen;
-  const int cpb = kWaves * (N == 16 ? 16 : 8);
   p.ntiles = static_cast<int32_t>((dim + cpb - 1) / cpb);
   if (static_cast<int64_t>(p.ntiles) * nseq > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.ntiles) * nseq));

@@ -40,12 +40,12 @@ def host(t):
 
 CASES = [
     # lengths, heads, N (keys), P (values), in, out, h0
-    ((100,), 2, 16, 16, "bf16", "f32", True),
-    ((77, 77), 2, 64, 8, "bf16", "bf16", False),
-    ((0, 41, 1, 0, 64), 2, 32, 16, "bf16", "f32", True),
-    ((50,), 1, 256, 8, "f32", "f32", True),
-    ((33, 33, 33), 3, 128, 8, "bf16", "f32", True),
-    ((130,), 2, 256, 16, "bf16", "bf16", True),
+    ((100,), 2, 16, 64, "bf16", "f32", True),
+    ((77, 77), 2, 64, 16, "bf16", "bf16", False),
+    ((0, 41, 1, 0, 64), 2, 32, 32, "bf16", "f32", True),
+    ((50,), 1, 256, 16, "f32", "f32", True),
+    ((33, 33, 33), 3, 128, 16, "bf16", "f32", True),
+    ((130,), 2, 256, 32, "bf16", "bf16", True),
 ]
 
 
@@ -91,13 +91,13 @@ def test_gla_matches_oracle(lengths, H, N, P, din, dout, with_h0):
 def test_gla_strong_decay():
     """Gates 16x the recipe's (decays down to ~e^-3 per token): the state forgets within a few tokens."""
     say("case: gla strong decay")
-    o, oo, hl, ho, b = run_case((120,), 2, 64, 8, "bf16", "f32", True, gk_scale=16.0)
+    o, oo, hl, ho, b = run_case((120,), 2, 64, 16, "bf16", "f32", True, gk_scale=16.0)
     check(o, oo, hl, ho, b, "f32")
 
 
 def test_gla_chained_and_deterministic():
     say("case: gla chained")
-    H, N, P, L1, L2 = 2, 128, 8, 45, 38
+    H, N, P, L1, L2 = 2, 128, 16, 45, 38
     inp = I.make_gla_inputs_np(11, L1 + L2, H, N, P)
     q, k, gk, v = (dev(inp[n], "bf16") for n in ("q", "k", "gk", "v"))
     o, hl = G.gla_fwd(q, k, v, gk, y_dtype=torch.float32)
