@@ -211,3 +211,19 @@ def test_retention_is_ssd_with_unit_step():
     gammas = 1.0 - 2.0 ** (-5.0 - np.arange(H))
     y, _ = O.ssd(v, np.zeros((L, H)), k, q, np.log(gammas), np.zeros(H), np.full(H, np.log(np.e - 1.0)))
     assert rel_err(y, retention_parallel(q, k, v, gammas)) < 1e-12
+
+
+def test_golden_regression_ssd_and_gla(oracle_lib):
+    """Regression fixture written by tests/golden/make_golden.py from oracle/ only (catches accidental changes
+    to the oracle; the pins above are what tie it to the definitions)."""
+    import json
+    from pathlib import Path
+    data = json.loads((Path(__file__).resolve().parent / "golden" / "oracle_variants_small.json").read_text())
+    ss = np.array(data["seq_start"], dtype=np.int64)
+    a = {k: np.array(v, dtype=np.float64) for k, v in data["ssd"]["inputs"].items()}
+    y, h = O.ssd(a["x"], a["dt"], a["B"], a["C"], a["A"], a["D"], a["dt_bias"], z=a["z"], h0=a["h0"], seq_start=ss,
+                 lib=oracle_lib)
+    assert rel_err(y, np.array(data["ssd"]["y"])) < 1e-13 and rel_err(h, np.array(data["ssd"]["h_last"])) < 1e-13
+    g = {k: np.array(v, dtype=np.float64) for k, v in data["gla"]["inputs"].items()}
+    o, hg = O.gla(g["q"], g["k"], g["v"], g["gk"], h0=g["h0"], seq_start=ss, lib=oracle_lib)
+    assert rel_err(o, np.array(data["gla"]["o"])) < 1e-13 and rel_err(hg, np.array(data["gla"]["h_last"])) < 1e-13
