@@ -133,3 +133,21 @@ def test_gla_full_shape_sampled():
             check_bf16_y(host(o[s, :, h, cols]), oo[:, 0], "o s%d h%d" % (s, h))
             check_fp32(host(hl[s, h, cols]), ho[0, 0], "h_last s%d h%d" % (s, h))
     say("  ok")
+
+
+def test_gla_no_tokens_carries_h0():
+    say("case: gla no tokens")
+    H, N, P = 2, 64, 16
+    h0 = torch.from_numpy((0.5 * np.random.default_rng(13).standard_normal((3, H, P, N))).astype(np.float32)).to(DEV)
+    q = torch.zeros(3, 0, H, N, dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros(3, 0, H, P, dtype=torch.bfloat16, device=DEV)
+    _, hl = G.gla_fwd(q, q, v, q, h0=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(hl, h0)
+
+
+def test_gla_one_past_a_chunk():
+    """17 and 33 tokens at 256 keys (16-token chunks) and 9 at 32 keys (8-token chunks)."""
+    for L, N, P in ((17, 256, 16), (33, 256, 16), (9, 32, 32)):
+        say("case: gla L%d N%d" % (L, N))
+        check(*run_case((L,), 2, N, P, "bf16", "f32", True), "f32")

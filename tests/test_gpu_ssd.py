@@ -176,3 +176,26 @@ def test_retention_configuration():
     check_fp32(host(y).reshape(L, -1), yo.reshape(L, -1), "retention y")
     check_fp32(host(hl), ho, "retention state")
     say("  ok")
+
+
+def test_ssd_no_tokens_carries_h0():
+    """Batched sequences of length 0: no chunk and no workspace; h_last is h0 exactly (and zero without h0)."""
+    say("case: ssd no tokens")
+    H, G, N = 4, 2, 64
+    h0 = torch.from_numpy(I.make_ssd_h0(12, 3, H, N, scale=0.5)).to(DEV)
+    x = torch.zeros(3, 0, H, 64, dtype=torch.bfloat16, device=DEV)
+    dt = torch.zeros(3, 0, H, dtype=torch.bfloat16, device=DEV)
+    B = torch.zeros(3, 0, G, N, dtype=torch.bfloat16, device=DEV)
+    p = I.make_ssd_params(12, H)
+    A, D, bias = (torch.from_numpy(p[k]).to(DEV) for k in ("A", "D", "dt_bias"))
+    _, hl = S.ssd_fwd(x, dt, B, B, A, D, bias, h0=h0)
+    _, hz = S.ssd_fwd(x, dt, B, B, A, D, bias)
+    torch.cuda.synchronize()
+    assert torch.equal(hl, h0) and not torch.any(hz)
+
+
+def test_ssd_one_past_a_chunk():
+    """65 tokens (one full chunk and one token), 129 tokens: the padding chunk and the partial last chunk."""
+    for L in (65, 129):
+        say("case: ssd L%d" % L)
+        check(*run_case((L,), 2, 1, 128, "f32", True, True), "f32")
