@@ -1081,6 +1081,16 @@ def copy_probe(nbytes: int = 512 << 20, reps: int = 3):
     torch.cuda.synchronize()
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(max_oracle_s: float = 30.0):
     """The fp64 oracle on the same long-prompt workload: the 8 chained 16384-token
     calls (h0 -> h_last carried between calls) over all 4096 channels, with
@@ -1109,10 +1119,21 @@ def cpu_baseline(max_oracle_s: float = 30.0):
         if spent * (done + 1) / done > max_oracle_s:
             break
     gbs = done * prefill_bytes(cl, D) / spent / 1e9
+    # the same oracle on one core, over the first call's first 256 channels
+    inp = I.make_fwd_inputs_torch(3, cl, D, "cpu", tensor_offset=0)
+    c1 = 256
+    x, dt, z = (inp[k][:, :c1].double().numpy().copy() for k in ("x", "dt", "z"))
+    Bm, Cm = (inp[k].double().numpy() for k in ("B", "C"))
+    t0 = time.perf_counter()
+    O.scan_fwd(x, dt, z, Bm, Cm, P["A"][:c1], P["D"][:c1], P["dt_bias"][:c1], nthreads=1, lib=lib)
+    one = time.perf_counter() - t0
     return {"value": gbs, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": "%d of the 8 chained 16384-token calls of the 131072-token prompt, all 4096 channels, "
                       "fp64 oracle (OpenMP over channels), %.1f s of oracle time" % (done, spent),
-            "tokens_channels_per_s": done * cl * D / spent}
+            "tokens_channels_per_s": done * cl * D / spent,
+            "one_core": {"tokens_channels_per_s": cl * c1 / one,
+                         "sample": "first 16384-token call, 256 channels, 1 thread, %.2f s" % one},
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
 
 
 def cpu_baseline_backward(max_oracle_s: float = 30.0):
