@@ -370,7 +370,7 @@ def bench_proj(steps: int = 20, warmup: int = 5):
             "steps": steps, "ms_per_call": ms, "tflops": tf, "tokens_per_s": T / (ms * 1e-3),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": "proj_kernel<bf16> (v_mfma_f32_32x32x16_bf16)", "flops_per_call": flops,
+                         "kernel": "proj_dma_kernel<bf16, BK=64, 2 stages, 2x4 waves> (v_mfma_f32_32x32x16_bf16, operands loaded straight into LDS)", "flops_per_call": flops,
                          "algorithmic_bytes_per_call": nbytes}}
 
 
@@ -917,7 +917,7 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
 
     sel = {"fwd": ("scan_fwd_kernel", "16, 1, 8, false>"), "step": ("scan_step_kernel<unsigned short, unsigned short",),
            "ckpt": ("scan_fwd_kernel", ", true>"), "bwd": ("scan_bwd_kernel<",), "finish": ("scan_bwd_finish_kernel",),
-           "proj": ("proj_kernel<unsigned short",)}
+           "proj": ("proj_dma_kernel<unsigned short",)}
     got = {k: {} for k in sel}
     scales = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):

@@ -209,10 +209,13 @@ samba_status samba_scan_bwd(const samba_scan_bwd_args* args, void* stream);
  * as a linear layer stores its weight): Linear_Δ (dim rows, full rank), then
  * Linear_B, then Linear_C.  No bias (τ_Δ's bias is dt_bias of the scan).
  * x [tokens][dim] and W are bf16 (in_dtype must be SAMBA_BF16), 16-byte
- * aligned, dim a multiple of 8; dt [tokens][dim], B and C [tokens][dstate]
+ * aligned, dim a multiple of 8 and below 2^22; dt [tokens][dim], B and C [tokens][dstate]
  * are written in out_dtype (bf16 round to nearest even, or fp32), aligned to
  * their element size, and must not overlap x, W or each other.  The outputs
- * feed samba_scan_fwd / samba_scan_bwd directly (same layouts).
+ * feed samba_scan_fwd / samba_scan_bwd directly (same layouts).  bf16
+ * results go out as 16-byte chunks where dt (and B, C with dstate a multiple
+ * of 8) are 16-byte aligned, element by element otherwise; the result is the
+ * same either way.
  */
 typedef struct {
   uint32_t struct_size;        /* = sizeof(samba_proj_args) */

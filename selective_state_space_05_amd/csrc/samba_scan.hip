@@ -33,6 +33,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "samba_scan.h"
 
@@ -1102,22 +1103,32 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepParams p) {
 // ---------------------------------------------------------------------------
 // Selection projections: [dt_raw | B | C] = x W^T, one bf16 GEMM on the matrix
 // cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  x [T][dim] and W
-// [dim + 2N][dim] are both K-contiguous.  A workgroup computes a BM x BN output
-// tile; each of its waves owns a block of 32 x 32 MFMA tiles (the launch
-// configuration is fixed below).  K advances 64 at a time through double-buffered LDS
-// tiles (rows padded to 144 bytes so that the 16-byte fragment reads of 8
-// consecutive rows hit distinct banks); the next step's global loads are
-// issued before the current step's MFMAs.  Tiles are ordered in groups of 8
-// row tiles so that workgroups running together on one XCD share their A and
-// B tiles in L2.  Operand layouts (checked on the device): lane l holds
-// A[l % 32][8 (l / 32) + 0..7] and B[8 (l / 32) + 0..7][l % 32]; result
-// element e of lane l is D[8 (e / 4) + 4 (l / 32) + e % 4][l % 32].
+// [dim + 2N][dim] are both K-contiguous.  A workgroup computes a 256 x 256
+// output tile with WM x WN waves, each owning a block of 32 x 32 MFMA tiles.
+// Operand tiles go from memory straight into LDS (buffer_load_dwordx4 ... lds:
+// the 64 lanes of a wave fill 1 KiB of LDS, lane l at byte 16 l), so no VGPRs
+// hold prefetched data; K advances BK per step through a ring of S stages.
+// The LDS image of a 256 x BK operand tile is row-major with 2 BK bytes per
+// row, its 16-byte chunks permuted per row (logical chunk c of row r sits at
+// position c ^ swz(r)) so that fragment reads are free of bank conflicts.  The
+// compiler does not track these LDS writes, so the waits are explicit: before
+// step s each wave waits for its own loads of stage s (vmcnt), then a barrier
+// publishes every wave's loads and frees the buffer that step s - 1 read,
+// which the loads of stage s + S - 1 then refill.  Inside a step the fragments
+// of the next 16-wide K slice are read while the MFMAs of this one run.
+// Out-of-range rows, and chunks past the K tail, read as zero (the resource
+// bounds, and an offset past them).  A wave whose output columns lie beyond
+// the last one skips their MFMAs (the ragged last column tile).  bf16 results
+// leave through LDS as 16-byte row chunks, fp32 results element-wise.  Tiles
+// are ordered in groups of 8 row tiles so that workgroups running together on
+// one XCD share their A and B tiles in L2.  Operand layouts (checked on the
+// device): lane l holds A[l % 32][8 (l / 32) + 0..7] and B[8 (l / 32) +
+// 0..7][l % 32]; result element e of lane l is D[8 (e / 4) + 4 (l / 32) + e %
+// 4][l % 32].
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kPK = 64;
-constexpr int kPRow = kPK + 8;      // LDS row stride in bf16 (144 bytes)
 constexpr int kPGroup = 8;          // row tiles per ordering group
 
 struct ProjParams {
@@ -1125,6 +1136,7 @@ struct ProjParams {
   const uint16_t* W;    // [nout][dim]
   void *dt, *B, *C;
   int32_t T, dim, dstate, nout, mtiles, ntiles, nblocks;
+  int32_t vec_dt, vec_bc;  // bf16 results may leave as 16-byte chunks (alignment, dstate % 8 == 0)
 };
 
 template <typename Tout>
@@ -1135,29 +1147,70 @@ __device__ __forceinline__ void proj_store(const ProjParams& p, int t, int j, fl
   else st_out(static_cast<Tout*>(p.C), static_cast<int64_t>(t) * p.dstate + (j - p.dim - p.dstate), v);
 }
 
-// Output tile BM x BN per workgroup of WM x WN waves; each wave owns a (BM/WM) x (BN/WN) block of
-// 32 x 32 MFMA tiles.
-template <typename Tout, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjParams p) {
-  constexpr int kThreads = 64 * WM * WN;
-  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;       // MFMA tiles per wave
-  constexpr int CA = BM * (kPK / 8) / kThreads;             // 16-byte chunks per thread per K step
-  constexpr int CW = BN * (kPK / 8) / kThreads;
-  static_assert(CA * kThreads == BM * kPK / 8 && CW * kThreads == BN * kPK / 8, "tile / thread mismatch");
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kPRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][BN * kPRow];
+// Tile configuration (build-time): K step, ring stages, waves per tile (WM x WN).  Measured on
+// 16384 x 4096 -> 4128: 64 / 2 / 2 x 4 at 0.48-0.51 ms, against 32 / 4 / 2 x 4 (0.53-0.56), 64 / 2 / 2 x 2
+// (0.53-0.57) and 32 / 4 / 2 x 2 (0.55-0.59).
+#ifndef SAMBA_PROJ_BK
+#define SAMBA_PROJ_BK 64
+#endif
+#ifndef SAMBA_PROJ_STAGES
+#define SAMBA_PROJ_STAGES 2
+#endif
+#ifndef SAMBA_PROJ_WM
+#define SAMBA_PROJ_WM 2
+#endif
+#ifndef SAMBA_PROJ_WN
+#define SAMBA_PROJ_WN 4
+#endif
+constexpr int kDBK = SAMBA_PROJ_BK, kDS = SAMBA_PROJ_STAGES, kDWM = SAMBA_PROJ_WM, kDWN = SAMBA_PROJ_WN;
+
+// Chunk permutation of tile row r.  gfx950's LDS serves a 16-byte-per-lane read to 16 lanes per cycle
+// over 64 banks (256 bytes), and the 16 lanes of a fragment read are 16 consecutive rows: with 128-byte
+// rows, rows r and r + 8 must land in different 16-byte bank groups as well as rows r .. r + 7.
+template <int BK>
+__device__ __forceinline__ int proj_swz(int r) { return BK == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3); }
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// one wave-wide 16-byte-per-lane load from a buffer resource straight into LDS at `lds` + 16 lane
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+template <typename Tout, int BK, int S, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void proj_dma_kernel(ProjParams p) {
+  constexpr int kW = WM * WN;
+  constexpr int BM = 256, BN = 256;
+  constexpr int RM = BM / WM, RN = BN / WN;   // a wave's output block
+  constexpr int TM = RM / 32, TN = RN / 32;   // MFMA tiles per wave
+  constexpr int kRowB = BK * 2;               // bytes per LDS tile row
+  constexpr int kCh = BK / 8;                 // 16-byte chunks per row
+  constexpr int kRPL = 64 / kCh;              // rows filled by one wave load
+  constexpr int kTileB = BM * kRowB;
+  constexpr int kStageB = 2 * kTileB;
+  constexpr int kLPT = BM / kRPL / kW;        // loads per wave per operand tile
+  constexpr int kL = 2 * kLPT;                // loads per wave per stage
+  constexpr int kEpRow = RN * 2 + 16;         // bf16 epilogue staging row (padded)
+  constexpr int kEpB = RM * kEpRow;
+  constexpr int kLdsB = (S * kStageB > kW * kEpB) ? S * kStageB : kW * kEpB;
+  static_assert(kLPT * kRPL * kW == BM && BM == BN, "loads per wave");
+  static_assert(S >= 2 && (S - 2) * kL < 64, "stages");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kLdsB];
+
   const int logical = xcd_remap(blockIdx.x, p.nblocks);
-  // grouped order: kPGroup row tiles x all column tiles per group
   const int per_group = kPGroup * p.ntiles;
   const int grp = logical / per_group;
   const int first_m = grp * kPGroup;
   const int gm = (p.mtiles - first_m) < kPGroup ? (p.mtiles - first_m) : kPGroup;
   const int within = logical - grp * per_group;
-  const int mt = first_m + within % gm;
-  const int nt = within / gm;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m0 = (first_m + within % gm) * BM, n0 = (within / gm) * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int wm = wave / WN, wn = wave % WN;
 
   const uint32_t row_bytes = static_cast<uint32_t>(p.dim) * 2u;
@@ -1165,42 +1218,38 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjParams p) {
                                    static_cast<uint32_t>(p.dim));
   const rsrc_t rw = make_rsrc_rows(p.W + static_cast<int64_t>(n0) * p.dim, p.nout - n0 < BN ? p.nout - n0 : BN,
                                    static_cast<uint32_t>(p.dim));
-  // this thread's 16-byte chunks of each tile: chunk q -> row q / 8, 8 bf16 at column 8 (q % 8)
-  const int c8 = (tid & 7) * 8;
-  uint32_t gA[CA], gW[CW];
-  int lA[CA], lW[CW];
+  // this lane's share of a wave load: row rl of the 1 KiB block, physical chunk pc holding logical chunk lc
+  static_assert(kW % 2 == 0, "the row parity of 8-row blocks is the wave's");
+  const int rl = lane / kCh, pc = lane % kCh;
+  const int lc = pc ^ proj_swz<BK>(kRPL * wave + rl);
+  const uint32_t vlane = static_cast<uint32_t>(rl) * row_bytes + static_cast<uint32_t>(lc) * 16u;
+  uint32_t voff[kLPT];   // load q of this wave fills rows kRPL (wave + kW q) ..
 #pragma unroll
-  for (int r = 0; r < CA; ++r) {
-    const int row = (tid + kThreads * r) >> 3;
-    gA[r] = static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(c8) * 2u;
-    lA[r] = row * kPRow + c8;
-  }
+  for (int q = 0; q < kLPT; ++q) voff[q] = vlane + static_cast<uint32_t>(kRPL * (wave + kW * q)) * row_bytes;
+
+  // issue the loads of the stage at K offset k0 into ring slot `slot`; chunks at or past dim get an offset
+  // past the resource (read as zero): only the last stage of a ragged K has any
+  auto load_stage = [&](int k0, int slot) {
+    const uint32_t kill = (k0 + 8 * lc < p.dim) ? 0u : 0x80000000u;
+    unsigned char* base = smem + slot * kStageB;
 #pragma unroll
-  for (int r = 0; r < CW; ++r) {
-    const int row = (tid + kThreads * r) >> 3;
-    gW[r] = static_cast<uint32_t>(row) * row_bytes + static_cast<uint32_t>(c8) * 2u;
-    lW[r] = row * kPRow + c8;
-  }
-  uint4 ra[CA], rb[CW];
-  auto gload = [&](int k0) {
-    const bool in = k0 + c8 < p.dim;   // K tail: chunks past dim read as zeros
-#pragma unroll
-    for (int r = 0; r < CA; ++r) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, gA[r] + static_cast<uint32_t>(k0) * 2u, 0, 0);
-      ra[r] = in ? make_uint4(v[0], v[1], v[2], v[3]) : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int r = 0; r < CW; ++r) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rw, gW[r] + static_cast<uint32_t>(k0) * 2u, 0, 0);
-      rb[r] = in ? make_uint4(v[0], v[1], v[2], v[3]) : make_uint4(0u, 0u, 0u, 0u);
+    for (int q = 0; q < kLPT; ++q) {
+      const int blk = (wave + kW * q) * 1024;
+      dma16(rx, base + blk, voff[q] | kill, k0 * 2);
+      dma16(rw, base + kTileB + blk, voff[q] | kill, k0 * 2);
     }
   };
-  auto lstore = [&](int buf) {
+
+  // fragment offsets within a stage: A rows wm RM + 32 i + lane % 32, B rows wn RN + 32 j + lane % 32,
+  // logical chunk 2 kk + lane / 32 of each
+  const int fr = lane & 31, fh = lane >> 5;
+  int aoff[BK / 16], boff[BK / 16];
 #pragma unroll
-    for (int r = 0; r < CA; ++r) *reinterpret_cast<uint4*>(&sA[buf][lA[r]]) = ra[r];
-#pragma unroll
-    for (int r = 0; r < CW; ++r) *reinterpret_cast<uint4*>(&sW[buf][lW[r]]) = rb[r];
-  };
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    const int ph = ((2 * kk + fh) ^ proj_swz<BK>(fr)) * 16;
+    aoff[kk] = (wm * RM + fr) * kRowB + ph;
+    boff[kk] = kTileB + (wn * RN + fr) * kRowB + ph;
+  }
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -1210,49 +1259,132 @@ __global__ __launch_bounds__(64 * WM * WN) void proj_kernel(ProjParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = (p.dim + kPK - 1) / kPK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int fr = lane & 31, fk = (lane >> 5) * 8;   // fragment row and k offset of this lane
-  const int arow = (BM / WM) * wm + fr, brow = (BN / WN) * wn + fr;
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) gload((ks + 1) * kPK);
+  const int nk = (p.dim + BK - 1) / BK;
+  // MFMA tiles of this wave that hold output columns (wave-uniform)
+  const int live = p.nout - (n0 + wn * RN);
+  const int jm = live <= 0 ? 0 : (live >= RN ? TN : (live + 31) / 32);
+
+  auto main_loop = [&](auto jm_c) {
+    constexpr int JM = decltype(jm_c)::value;
+    constexpr int KK = BK / 16;
 #pragma unroll
-    for (int kk = 0; kk < kPK / 16; ++kk) {
-      bf16x8_t a[TM], b[TN];
+    for (int st = 0; st < S - 1; ++st)
+      if (st < nk) load_stage(st * BK, st);
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks + S - 2 < nk) wait_vmcnt<(S - 2) * kL>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const int nxt = ks + S - 1;
+      if (nxt < nk) load_stage(nxt * BK, nxt % S);
+      const unsigned char* base = smem + (ks % S) * kStageB;
+      // fragments of slice kk + 1 are read while the MFMAs of slice kk run
+      bf16x8_t a[2][TM], b[2][TN > 0 ? TN : 1];
+      auto rd = [&](int kk, int sl) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][(arow + 32 * i) * kPRow + 16 * kk + fk]);
+        for (int i = 0; i < TM; ++i) a[sl][i] = *reinterpret_cast<const bf16x8_t*>(base + aoff[kk] + 32 * i * kRowB);
+#pragma unroll
+        for (int j = 0; j < JM; ++j) b[sl][j] = *reinterpret_cast<const bf16x8_t*>(base + boff[kk] + 32 * j * kRowB);
+      };
+      if constexpr (JM > 0) {
+        rd(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 1 < KK) rd(kk + 1, (kk + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < JM; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
+        }
+        // issue order: the ring loads, slice 0's fragments, then per slice one fragment read of the next
+        // slice after every few MFMAs
+        constexpr int kRd = TM + JM, kMf = TM * JM;
+        constexpr int kPer = kMf / kRd > 0 ? kMf / kRd : 1;
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 * kLPT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);
+#pragma unroll
+        for (int kk = 0; kk + 1 < KK; ++kk) {
+#pragma unroll
+          for (int r = 0; r < kRd; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if constexpr (kMf > kPer * kRd) __builtin_amdgcn_sched_group_barrier(0x008, kMf - kPer * kRd, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if (jm == TN) main_loop(std::integral_constant<int, TN>());
+  else if (jm == 0) main_loop(std::integral_constant<int, 0>());
+  else if (jm == 1) main_loop(std::integral_constant<int, 1>());
+  else if (jm == 2) main_loop(std::integral_constant<int, (TN > 2 ? 2 : TN)>());
+  else main_loop(std::integral_constant<int, (TN > 3 ? 3 : TN)>());
+
+  // element e of lane l: row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32 of its 32 x 32 tile
+  if constexpr (sizeof(Tout) == 4) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(&sW[buf][(brow + 32 * j) * kPRow + 16 * kk + fk]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int e = 0; e < 16; ++e) {
+          const int m = wm * RM + 32 * i + 8 * (e >> 2) + 4 * fh + (e & 3);
+          const int n = wn * RN + 32 * j + fr;
+          proj_store<Tout>(p, m0 + m, n0 + n, acc[i][j][e]);
+        }
+  } else {
+    __syncthreads();  // every wave is done reading the operand ring
+    unsigned char* ep = smem + wave * kEpB;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (ks + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
-  }
-  // epilogue: element e of lane l is row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32 of its block
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = (BM / WM) * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int n = (BN / WN) * wn + 32 * j + (lane & 31);
-        proj_store<Tout>(p, m0 + m, n0 + n, acc[i][j][e]);
+        for (int e = 0; e < 16; ++e) {
+          const int m = 32 * i + 8 * (e >> 2) + 4 * fh + (e & 3);
+          const int n = 32 * j + fr;
+          *reinterpret_cast<uint16_t*>(ep + m * kEpRow + n * 2) = f32_to_bf16(acc[i][j][e]);
+        }
+    wave_lds_sync();
+    // read back 16-byte row chunks: RN / 8 chunks per row, 64 lanes per pass
+    constexpr int kCPR = RN / 8;
+    constexpr int kRPP = 64 / kCPR;
+    const int cr = lane / kCPR, cc = lane % kCPR;
+#pragma unroll 4
+    for (int r0 = 0; r0 < RM; r0 += kRPP) {
+      const int m = m0 + wm * RM + r0 + cr;
+      const int n = n0 + wn * RN + 8 * cc;
+      const uint4 v = *reinterpret_cast<const uint4*>(ep + (r0 + cr) * kEpRow + cc * 16);
+      if (m >= p.T || n >= p.nout) continue;
+      uint16_t* dst = nullptr;   // a 16-byte aligned destination for the whole chunk, when there is one
+      if (n < p.dim) {
+        if (p.vec_dt) dst = static_cast<uint16_t*>(p.dt) + static_cast<int64_t>(m) * p.dim + n;
+      } else if (p.vec_bc) {
+        const int cb = n - p.dim;
+        dst = cb < p.dstate ? static_cast<uint16_t*>(p.B) + static_cast<int64_t>(m) * p.dstate + cb
+                            : static_cast<uint16_t*>(p.C) + static_cast<int64_t>(m) * p.dstate + (cb - p.dstate);
       }
+      if (dst) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint16_t bits = static_cast<uint16_t>(u & 1 ? (w4[u >> 1] >> 16) : (w4[u >> 1] & 0xffffu));
+          const int j = n + u;
+          if (j >= p.nout) break;
+          if (j < p.dim) static_cast<uint16_t*>(p.dt)[static_cast<int64_t>(m) * p.dim + j] = bits;
+          else if (j < p.dim + p.dstate) static_cast<uint16_t*>(p.B)[static_cast<int64_t>(m) * p.dstate + (j - p.dim)] = bits;
+          else static_cast<uint16_t*>(p.C)[static_cast<int64_t>(m) * p.dstate + (j - p.dim - p.dstate)] = bits;
+        }
+      }
+    }
+  }
 }
 
-// 256 x 256 tiles, 8 waves of 128 x 64 (4 x 2 MFMA tiles each): 0.75 KiB of LDS fragment reads per MFMA,
-// 144 KiB of double-buffered LDS (one workgroup per CU, two waves per SIMD).  Measured against 128 x 128 /
-// 4 waves and 256 x 128 / 4 waves on 16384 x 4096 x 4128: 0.630 ms vs 0.655 and 0.770 ms.
-constexpr int kPM = 256, kPN = 256, kPWM = 2, kPWN = 4;
 
 // ---------------------------------------------------------------------------
 // host side
@@ -1660,7 +1792,8 @@ samba_status samba_proj(const samba_proj_args* a, void* stream) {
   if (a->struct_size != sizeof(samba_proj_args)) return SAMBA_ERR_BAD_STRUCT;
   if (a->in_dtype != SAMBA_BF16 || !dtype_ok(a->out_dtype)) return SAMBA_ERR_BAD_DTYPE;
   if (a->tokens < 0 || a->dim < 8 || a->dstate < 1) return SAMBA_ERR_BAD_SHAPE;
-  if (a->dim % 8 != 0) return SAMBA_ERR_BAD_SHAPE;
+  // dim % 8: 16-byte operand chunks; dim < 2^22: byte offsets within a 256-row tile stay below 2^31
+  if (a->dim % 8 != 0 || a->dim >= (1 << 22)) return SAMBA_ERR_BAD_SHAPE;
   const int64_t nout = static_cast<int64_t>(a->dim) + 2 * static_cast<int64_t>(a->dstate);
   if (nout > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
   if (!a->W) return SAMBA_ERR_NULL_ARG;
@@ -1685,17 +1818,19 @@ samba_status samba_proj(const samba_proj_args* a, void* stream) {
   p.W = static_cast<const uint16_t*>(a->W);
   p.dt = a->dt; p.B = a->B; p.C = a->C;
   p.T = a->tokens; p.dim = a->dim; p.dstate = a->dstate; p.nout = static_cast<int32_t>(nout);
-  p.mtiles = (a->tokens + kPM - 1) / kPM;
-  p.ntiles = static_cast<int32_t>((nout + kPN - 1) / kPN);
+  p.mtiles = (a->tokens + 255) / 256;
+  p.ntiles = static_cast<int32_t>((nout + 255) / 256);
   const int64_t nblocks = static_cast<int64_t>(p.mtiles) * p.ntiles;
   if (nblocks > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
   p.nblocks = static_cast<int32_t>(nblocks);
+  p.vec_dt = aligned(a->dt, 16);
+  p.vec_bc = a->dstate % 8 == 0 && aligned(a->B, 16) && aligned(a->C, 16);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 block(64 * kPWM * kPWN);
+  const dim3 block(64 * kDWM * kDWN);
   if (a->out_dtype == SAMBA_BF16)
-    hipLaunchKernelGGL((proj_kernel<uint16_t, kPM, kPN, kPWM, kPWN>), dim3(p.nblocks), block, 0, s, p);
+    hipLaunchKernelGGL((proj_dma_kernel<uint16_t, kDBK, kDS, kDWM, kDWN>), dim3(p.nblocks), block, 0, s, p);
   else
-    hipLaunchKernelGGL((proj_kernel<float, kPM, kPN, kPWM, kPWN>), dim3(p.nblocks), block, 0, s, p);
+    hipLaunchKernelGGL((proj_dma_kernel<float, kDBK, kDS, kDWM, kDWN>), dim3(p.nblocks), block, 0, s, p);
   return hipGetLastError() == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
 }
 

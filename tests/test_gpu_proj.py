@@ -55,6 +55,33 @@ def test_proj_small(T, dim, out):
         say("  %s: %.2e" % (name, e))
 
 
+@pytest.mark.parametrize("T,dim,N,out,shift", [(300, 296, 16, "bf16", 0), (130, 304, 8, "bf16", 0),
+                                               (200, 136, 5, "bf16", 1), (70, 64, 3, "f32", 1),
+                                               (513, 520, 16, "bf16", 1)])
+def test_proj_ragged_columns_and_layouts(T, dim, N, out, shift):
+    """Last column tile 72 and 64 wide (a wave computes 3 or 2 of its 4 column blocks), a state size that
+    is not a multiple of 8 and outputs that start one element past a 16-byte boundary (element-wise
+    result stores)."""
+    say("case: proj T%d dim%d N%d out %s shift %d" % (T, dim, N, out, shift))
+    inp = I.make_fwd_inputs_np(2, T, dim, in_dtype="bf16")
+    w = I.make_proj_weight_np(2, dim, dstate=N)
+    od = torch.float32 if out == "f32" else torch.bfloat16
+
+    def buf(n):
+        return torch.full((n + shift,), float("nan"), dtype=od, device=DEV)[shift:]
+
+    dt, B, C = buf(T * dim).view(T, dim), buf(T * N).view(T, N), buf(T * N).view(T, N)
+    S.proj(bf16_dev(inp["x"]).reshape(T, dim), bf16_dev(w["W"]).reshape(-1, dim), dt=dt, B=B, C=C)
+    torch.cuda.synchronize()
+    odt, oB, oC = O.proj(inp["x_f32"].reshape(T, dim), w["W_f32"], dstate=N)
+    for name, g, o in (("dt", dt, odt), ("B", B, oB), ("C", C, oC)):
+        if out == "f32":
+            e = check_fp32(host(g), o, "proj " + name, trip=PROJ_TRIP)
+        else:
+            e = check_bf16_y(host(g), o, "proj " + name)
+        say("  %s: %.2e" % (name, e))
+
+
 def test_proj_full_shape_sampled_rows():
     """16384 tokens x 4096 channels (the long-prompt chunk), every output feature of 96 sampled tokens."""
     T, dim = 16384, 4096
