@@ -684,6 +684,7 @@ def bench_gla(steps: int = 5, warmup: int = 2):
     o = torch.empty_like(v)
     hl = torch.empty(Bt, H, P, N, dtype=torch.float32, device=dev)
     a = GL.fwd_args(q, k, v, gk, o=o, h_last=hl)
+    ws = GL.attach_workspace(a, dev)   # noqa: F841 (kept alive for the calls)
     lib = GL.load_library()
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)

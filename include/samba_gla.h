@@ -47,7 +47,13 @@ typedef struct {
   const float* h0;             /* optional [nseq][heads][head_dim][dstate] */
   float* h_last;               /* optional, same shape */
   void* o;                     /* [tokens][heads][head_dim] */
+  void* workspace;             /* device, samba_gla_workspace_size() bytes (chunked form only) */
+  size_t workspace_bytes;
 } samba_gla_args;
+
+/* Host-only: bytes of workspace samba_gla_fwd needs for these sizes (0 for the
+ * recurrent form, and when there are no tokens); validates like samba_gla_fwd. */
+samba_status samba_gla_workspace_size(const samba_gla_args* args, size_t* bytes);
 
 samba_status samba_gla_fwd(const samba_gla_args* args, void* stream);
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SAMBA_SCAN_ABI_VERSION 10
+#define SAMBA_SCAN_ABI_VERSION 11
 #define SAMBA_DSTATE 16
 
 typedef enum {
@@ -59,7 +59,7 @@ typedef enum {
   SAMBA_ERR_UNSUPPORTED = 6,   /* dstate != 16, or time_slices not 0/1/2/4/8/16 */
   SAMBA_ERR_BAD_STRUCT = 7,    /* struct_size does not match this header */
   SAMBA_ERR_HIP = 8,           /* the HIP runtime refused the launch */
-  SAMBA_ERR_WORKSPACE = 9      /* workspace NULL, too small or misaligned (backward, SSD prefill) */
+  SAMBA_ERR_WORKSPACE = 9      /* workspace NULL or too small (backward, SSD prefill, chunked GLA) */
 } samba_status;
 
 typedef enum { SAMBA_F32 = 0, SAMBA_BF16 = 1 } samba_dtype;

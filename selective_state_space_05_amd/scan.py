@@ -13,7 +13,7 @@ from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "libsamba_scan.so"
 DSTATE = 16
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 SAMBA_F32, SAMBA_BF16 = 0, 1
 STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE", 3: "SAMBA_ERR_BAD_DTYPE",
@@ -23,7 +23,7 @@ EXPORTED = ("samba_scan_fwd", "samba_scan_step", "samba_scan_fwd_plan", "samba_s
             "samba_scan_bwd_workspace_size", "samba_scan_ckpt_bytes", "samba_proj", "samba_status_string",
             "samba_scan_abi_version", "samba_rope", "samba_swa_fwd", "samba_swa_decode", "samba_scan_fwd_groups",
             "samba_scan_step_groups", "samba_ssd_fwd", "samba_ssd_workspace_size",
-            "samba_gla_fwd")
+            "samba_gla_fwd", "samba_gla_workspace_size")
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32

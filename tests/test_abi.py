@@ -690,10 +690,20 @@ def gla_ok(batch=2, seqlen=100, heads=4, head_dim=64, dstate=128):
     a.in_dtype, a.y_dtype = S.SAMBA_BF16, S.SAMBA_F32
     a.q, a.k, a.gk, a.v = BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB
     a.h0, a.h_last, a.o = BASE + 4 * GB, BASE + 5 * GB, BASE + 6 * GB
+    a.workspace, a.workspace_bytes = BASE + 7 * GB, GB
     return a
 
 
+def gla_ws_bytes(nslots, heads, dstate):
+    # per (chunk slot, head): scaled q and k as bf16 hi + lo planes, A hi + lo, e^{b_64}
+    return nslots * heads * (4 * 64 * dstate * 2 + 2 * 64 * 64 * 2 + 4 * dstate)
+
+
 GLA_CASES = {
+    "workspace_null": (lambda a: setattr(a, "workspace", None), 9),
+    "workspace_small": (lambda a: setattr(a, "workspace_bytes", gla_ws_bytes(4, 4, 128) - 1), 9),
+    "workspace_misaligned": (lambda a: setattr(a, "workspace", a.workspace + 128), 4),
+    "workspace_overlaps_o": (lambda a: setattr(a, "workspace", a.o), 5),
     "struct_size": (lambda a: setattr(a, "struct_size", 4), 7),
     "dstate_48": (lambda a: setattr(a, "dstate", 48), 6),
     "dstate_512": (lambda a: setattr(a, "dstate", 512), 6),
@@ -718,6 +728,24 @@ def test_gla_rejects(lib, name):
     mutate, code = GLA_CASES[name]
     mutate(a)
     assert lib.samba_gla_fwd(ctypes.byref(a), None) == code
+
+
+def test_gla_workspace_size(lib):
+    n = ctypes.c_size_t(0)
+    a = gla_ok()                       # bf16, 128 keys, 64 values: the chunked form, 2 x 2 chunks
+    assert lib.samba_gla_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == gla_ws_bytes(4, 4, 128)
+    a = gla_ok(dstate=256, seqlen=64)
+    assert lib.samba_gla_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == gla_ws_bytes(2, 4, 256)
+    a.cu_seqlens, a.nseq, a.batch, a.seqlen = BASE + 11 * GB, 3, 1, 1000   # packed: tokens / 64 + nseq slots
+    assert lib.samba_gla_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == gla_ws_bytes(15 + 3, 4, 256)
+    for mutate in (lambda a: setattr(a, "in_dtype", S.SAMBA_F32), lambda a: setattr(a, "dstate", 64),
+                   lambda a: setattr(a, "head_dim", 48), lambda a: setattr(a, "batch", 0)):
+        a = gla_ok()
+        mutate(a)                      # the recurrent form (or no tokens): no workspace
+        assert lib.samba_gla_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == 0
+    a = gla_ok(dstate=48)
+    assert lib.samba_gla_workspace_size(ctypes.byref(a), ctypes.byref(n)) == 6
+    assert lib.samba_gla_workspace_size(ctypes.byref(gla_ok()), None) == 1
 
 
 def test_gla_noops(lib):

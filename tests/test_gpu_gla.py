@@ -1,12 +1,13 @@
 """GPU parity of gated linear attention (samba_gla_fwd through the C ABI) against the fp64 oracle (oracle_gla,
 pinned in tests/test_oracle_gla_pins.py).
 
-Tolerance reading as for the selective scan (tests/parity.py): the kernel is the recurrence in fp32 (no
-bf16 products), so fp32 outputs per sequence meet the 2e-3 contract and the 1e-4 tripwire; bf16 o gets one
-bf16 rounding on top per (sequence, column).  Cases: every key size (16 .. 256), fp32 and bf16 inputs and
+Tolerance reading as for the selective scan (tests/parity.py): the recurrence runs in fp32 (no bf16
+products), and the chunked form feeds the matrix cores bf16 hi + lo pairs (16 significant bits) for every
+operand that is not an input, so fp32 outputs per sequence meet the 2e-3 contract and the 1e-4 tripwire;
+bf16 o gets one bf16 rounding on top per (sequence, column).  Cases: every key size (16 .. 256), fp32 and bf16 inputs and
 outputs, h0 given and h_last written in place over it, packed sequences with empty ones, ragged chunks,
 strongly decaying gates, a chained call, determinism, and the benchmark's shape (B4 L4096, 4 heads, keys
-256, values 512) on sampled value columns of every head.
+256, values 512) on sampled value columns of every head; each in the recurrent and the chunked form.
 """
 import sys
 
@@ -46,6 +47,11 @@ CASES = [
     ((50,), 1, 256, 16, "f32", "f32", True),
     ((33, 33, 33), 3, 128, 16, "bf16", "f32", True),
     ((130,), 2, 256, 32, "bf16", "bf16", True),
+    # the chunked form (bf16 inputs, 128 or 256 keys, values a multiple of 32): 64-token chunks
+    ((64, 0, 129, 1, 200), 2, 128, 32, "bf16", "f32", True),
+    ((65,), 3, 256, 64, "bf16", "f32", True),
+    ((300,), 1, 128, 96, "bf16", "bf16", False),
+    ((128, 128), 2, 256, 32, "bf16", "f32", False),
 ]
 
 
@@ -88,16 +94,21 @@ def test_gla_matches_oracle(lengths, H, N, P, din, dout, with_h0):
     check(*run_case(lengths, H, N, P, din, dout, with_h0), dout)
 
 
-def test_gla_strong_decay():
-    """Gates 16x the recipe's (decays down to ~e^-3 per token): the state forgets within a few tokens."""
-    say("case: gla strong decay")
-    o, oo, hl, ho, b = run_case((120,), 2, 64, 16, "bf16", "f32", True, gk_scale=16.0)
+@pytest.mark.parametrize("N,P,scale", [(64, 16, 16.0), (256, 32, 16.0), (128, 32, 120.0)])
+def test_gla_strong_decay(N, P, scale):
+    """Gates 16x the recipe's (decays down to ~e^-3 per token): the state forgets within a few tokens, and in
+    the chunked form the decay across a 64-token chunk spans tens of e-folds.  At 120x a 32-token half spans
+    more than the 64 e-folds across which the intra-chunk matrix is formed from factored decays, so those
+    blocks take the exact term-by-term form."""
+    say("case: gla strong decay N%d P%d x%g" % (N, P, scale))
+    o, oo, hl, ho, b = run_case((150,), 2, N, P, "bf16", "f32", True, gk_scale=scale)
     check(o, oo, hl, ho, b, "f32")
 
 
-def test_gla_chained_and_deterministic():
-    say("case: gla chained")
-    H, N, P, L1, L2 = 2, 128, 16, 45, 38
+@pytest.mark.parametrize("N,P,L1,L2", [(128, 16, 45, 38), (256, 32, 70, 60)])
+def test_gla_chained_and_deterministic(N, P, L1, L2):
+    say("case: gla chained N%d P%d" % (N, P))
+    H = 2
     inp = I.make_gla_inputs_np(11, L1 + L2, H, N, P)
     q, k, gk, v = (dev(inp[n], "bf16") for n in ("q", "k", "gk", "v"))
     o, hl = G.gla_fwd(q, k, v, gk, y_dtype=torch.float32)
@@ -135,9 +146,10 @@ def test_gla_full_shape_sampled():
     say("  ok")
 
 
-def test_gla_no_tokens_carries_h0():
-    say("case: gla no tokens")
-    H, N, P = 2, 64, 16
+@pytest.mark.parametrize("N,P", [(64, 16), (128, 32)])
+def test_gla_no_tokens_carries_h0(N, P):
+    say("case: gla no tokens N%d P%d" % (N, P))
+    H = 2
     h0 = torch.from_numpy((0.5 * np.random.default_rng(13).standard_normal((3, H, P, N))).astype(np.float32)).to(DEV)
     q = torch.zeros(3, 0, H, N, dtype=torch.bfloat16, device=DEV)
     v = torch.zeros(3, 0, H, P, dtype=torch.bfloat16, device=DEV)
@@ -147,7 +159,8 @@ def test_gla_no_tokens_carries_h0():
 
 
 def test_gla_one_past_a_chunk():
-    """17 and 33 tokens at 256 keys (16-token chunks) and 9 at 32 keys (8-token chunks)."""
-    for L, N, P in ((17, 256, 16), (33, 256, 16), (9, 32, 32)):
+    """17 and 33 tokens at 256 keys (16-token chunks) and 9 at 32 keys (8-token chunks) in the recurrence;
+    65 and 1 tokens in the chunked form (64-token chunks)."""
+    for L, N, P in ((17, 256, 16), (33, 256, 16), (9, 32, 32), (65, 256, 32), (1, 128, 32)):
         say("case: gla L%d N%d" % (L, N))
         check(*run_case((L,), 2, N, P, "bf16", "f32", True), "f32")
