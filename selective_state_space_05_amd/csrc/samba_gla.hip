@@ -461,18 +461,27 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaChunkParams p) {
   const int64_t bytes = static_cast<int64_t>(nv - 1) * rowb + N * 2;   // rows past the chunk's tokens read 0
   const rsrc_t rq = rsrc_bytes(p.q + e0, bytes), rk = rsrc_bytes(p.k + e0, bytes), rg = rsrc_bytes(p.gk + e0, bytes);
   if (tid < 2) sWide[tid] = 0;
+  // q, k and gk rows (gk widened to fp32 in place of b)
+#pragma unroll 2
   for (int i = tid; i < kCQ * N / 8; i += 256) {
     const int t = i / (N / 8), c8 = i - t * (N / 8);
     const uint32_t off = static_cast<uint32_t>(t) * rowb + 16u * c8;
     const auto a = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
     const auto b = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+    const auto g = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0);
     *reinterpret_cast<uint4*>(&sQ[t * kQR + 8 * c8]) = make_uint4(a[0], a[1], a[2], a[3]);
     *reinterpret_cast<uint4*>(&sK[t * kQR + 8 * c8]) = make_uint4(b[0], b[1], b[2], b[3]);
+    float* gb = &sB[t * kBR + 8 * c8];
+    *reinterpret_cast<float4*>(gb) = make_float4(__uint_as_float(g[0] << 16), __uint_as_float(g[0] & 0xffff0000u),
+                                                 __uint_as_float(g[1] << 16), __uint_as_float(g[1] & 0xffff0000u));
+    *reinterpret_cast<float4*>(gb + 4) = make_float4(__uint_as_float(g[2] << 16), __uint_as_float(g[2] & 0xffff0000u),
+                                                     __uint_as_float(g[3] << 16), __uint_as_float(g[3] & 0xffff0000u));
   }
-  if (tid < N) {   // inclusive cumulative sum of gk over the tokens, one key per thread
+  __syncthreads();
+  if (tid < N) {   // inclusive cumulative sum over the tokens, one key per thread, in place
     float acc = 0.f;
     for (int t = 0; t < kCQ; ++t) {
-      acc += bf16f(__builtin_amdgcn_raw_buffer_load_b16(rg, static_cast<uint32_t>(t) * rowb + 2u * tid, 0, 0));
+      acc += sB[t * kBR + tid];
       sB[t * kBR + tid] = acc;
     }
   }
@@ -699,8 +708,11 @@ __global__ __launch_bounds__(64 * (N / 32)) void gla_chunk_kernel(GlaChunkParams
     put_g(0, gw0);
   }
   // one chunk; the parity of c (which LDS buffer and register set) is a compile-time constant
-  auto step = [&](int c, auto bufc) {
+  // TTc: the token tile of this wave's share of A V (waves 0 .. NW / 2 - 1 take tile 0): a compile-time
+  // constant, so that the accumulator it feeds is chosen without selects
+  auto step = [&](int c, auto bufc, auto ttc) {
     constexpr int buf = decltype(bufc)::value;
+    constexpr int TTc = decltype(ttc)::value;
     __syncthreads();   // v of chunk c staged; the previous chunk's partial outputs consumed
     // next chunk's v and operands (the last chunk reloads its own: no branch around the loads)
     const int cn = c + 1 < nch ? c + 1 : c, cnn = c + 2 < nch ? c + 2 : cn;
@@ -735,15 +747,10 @@ __global__ __launch_bounds__(64 * (N / 32)) void gla_chunk_kernel(GlaChunkParams
     }
 #pragma unroll
     for (int u = 0; u < Ops::kAV; ++u) {
-      const int pr = Ops::kAV * wave + u, tt = pr >> 2, kk = pr & 3;
-      // (tt is wave-uniform: pick the accumulator without indexing by it)
-      if (tt == 0) {
-        op[0] = mfma(cur.ah[u], vf[kk], op[0]);
-        op[0] = mfma(cur.al[u], vf[kk], op[0]);
-      } else {
-        op[1] = mfma(cur.ah[u], vf[kk], op[1]);
-        op[1] = mfma(cur.al[u], vf[kk], op[1]);
-      }
+      const int kk = (Ops::kAV * wave + u) & 3;   // (its v fragment read again: kk is not a constant)
+      const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(&sVt[buf][l32 * kVtRow + 16 * kk + 8 * hi]);
+      op[TTc] = mfma(cur.ah[u], va, op[TTc]);
+      op[TTc] = mfma(cur.al[u], va, op[TTc]);
     }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -792,10 +799,15 @@ __global__ __launch_bounds__(64 * (N / 32)) void gla_chunk_kernel(GlaChunkParams
     }
     cur = nxt;
   };
-  for (int c = 0; c < nch; c += 2) {
-    step(c, std::integral_constant<int, 0>());
-    if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>());
-  }
+  auto run = [&](auto ttc) {
+    for (int c = 0; c < nch; c += 2) {
+      step(c, std::integral_constant<int, 0>(), ttc);
+      if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>(), ttc);
+    }
+  };
+  // (both halves of the workgroup run the same barriers)
+  if (wave < NW / 2) run(std::integral_constant<int, 0>());
+  else run(std::integral_constant<int, 1>());
   if (p.h_last) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
