@@ -141,7 +141,7 @@ def read_gla_traffic():
         return None
     if t.get("kernel_source_sha256_16") != gla_hash():
         return None
-    return t.get("gla", {}).get("bytes_per_launch")
+    return t.get("gla_call", {}).get("bytes_per_call")
 
 
 def ssd_hash() -> str:
@@ -662,11 +662,11 @@ def gla_bytes(batch: int, L: int, heads: int, n: int, pv: int) -> int:
     return T * heads * (3 * n + 2 * pv) * 2 + batch * heads * pv * n * 4
 
 
-def gla_slots(batch: int, L: int, heads: int, n: int, pv: int) -> int:
-    """Algorithmic issue slots of the recurrence: per (token, value column, key) the decay multiply, the
-    k v FMA and the readout FMA (3); per (token, head, key) the decay exp (4) and its scaling (1)."""
+def gla_flops(batch: int, L: int, heads: int, n: int, pv: int, chunk: int = 64) -> int:
+    """Algorithmic flops of the chunked form: per token and head the inter-chunk readout and the state update
+    (2 N P each), the intra-chunk A V and A (causal: half of 2 C P and 2 C N)."""
     T = batch * L
-    return T * heads * pv * n * 3 + T * heads * n * 5
+    return T * heads * (4 * n * pv + chunk * pv + chunk * n)
 
 
 def bench_gla(steps: int = 5, warmup: int = 2):
@@ -698,16 +698,22 @@ def bench_gla(steps: int = 5, warmup: int = 2):
         call()
     torch.cuda.synchronize()
     ms = _timed(call, steps, stream)
-    slots = gla_slots(Bt, L, H, N, P)
-    achieved = slots / (ms * 1e-3) / 1e12
     nbytes = gla_bytes(Bt, L, H, N, P)
+    flops = gla_flops(Bt, L, H, N, P)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    # roofline of the chunked form: flops / bytes = ~150 flop/B, below the chip's 2.5 PFLOP/s / 8 TB/s = 312
+    # flop/B ridge, so the call is bound by HBM on the roofline (its actual limits are the workspace round
+    # trip and the per-chunk dependency chain: see the kernel notes)
     return {"workload": "GLA B=%d L=%d, %d heads, keys %d, values %d, bf16 I/O, fp32 state" % (Bt, L, H, N, P),
             "steps": steps, "ms_per_call": ms, "tokens_per_s": Bt * L / (ms * 1e-3),
-            "token_columns_per_s": Bt * L * H * P / (ms * 1e-3), "gbs": nbytes / (ms * 1e-3) / 1e9,
-            "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TSLOT, 2),
-                         "unit": "Tslot/s", "frac": round(achieved / VALU_PEAK_TSLOT, 4),
-                         "traffic": read_gla_traffic(), "kernel": "gla_fwd_kernel<bf16,bf16,N=%d>" % N, "launch_us": round(ms * 1e3, 2),
-                         "algorithmic_slots_per_launch": slots, "algorithmic_bytes_per_launch": nbytes}}
+            "token_columns_per_s": Bt * L * H * P / (ms * 1e-3), "gbs": gbs, "tflops": tflops,
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_gla_traffic(),
+                         "kernel": "gla_prep_kernel<256> + gla_chunk_kernel<bf16,256> (one call, chunked form)",
+                         "launch_us": round(ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes,
+                         "algorithmic_flops_per_launch": flops}}
 
 
 def cpu_baseline_gla(columns: int = 32):
@@ -945,6 +951,9 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
                           "algorithmic_bytes_per_call": bwd_bytes(4 * 4096, 4096, 4)},
              "projections": entry("proj", (16384 * 4096 + 4128 * 4096 + 16384 * 4128) * 2)}
     out_d["backward"]["bytes_per_call"] = sum(v["bytes_per_launch"] for v in out_d["backward"]["kernels"].values())
+    if which == "gla":
+        out_d["gla_call"] = {"bytes_per_call": sum(out_d[k]["bytes_per_launch"] for k in sel),
+                             "algorithmic_bytes_per_call": sum(out_d[k]["algorithmic_bytes_per_launch"] for k in sel)}
     out_d["command"] = [
         f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {PMC_RUN}",
         f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {PMC_RUN}",
@@ -1001,9 +1010,13 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
     elif which == "gla":
         wl = I.WORKLOADS[10]
         Bt, L, H, N, P = wl.batch, wl.seqlen, wl.extra["heads"], wl.dstate, wl.extra["head_dim"]
-        sel = {"gla": ("gla_fwd_kernel<unsigned short, unsigned short, 256>", gla_bytes(Bt, L, H, N, P))}
+        T = Bt * L
+        sel = {"gla_prep": ("gla_prep_kernel<256>", T * H * 3 * N * 2),
+               "gla_chunk": ("gla_chunk_kernel<unsigned short, 256>", gla_bytes(Bt, L, H, N, P) - T * H * 3 * N * 2)}
         src_hash, run, flag = gla_hash(), GLA_PMC_RUN, "--pmc-summary-gla"
-        note = "Algorithmic bytes: q, k, gk and v read and o written once (bf16), h_last out."
+        note = ("Algorithmic bytes: q, k, gk (the prep kernel) and v read and o written once (bf16), h_last out "
+                "(the chunk kernel). The workspace the prep kernel writes and the chunk kernel reads (145 KiB per "
+                "(chunk, head), 152 MB here) is not counted in the algorithmic bytes.")
     elif which == "ssd":
         wl = I.WORKLOADS[9]
         Bt, L, H, P, N, G = (wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.dstate,
@@ -1041,6 +1054,9 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
         out_d[name] = {"kernel": got[name]["FETCH_SIZE"]["kernel"], "grid": got[name]["FETCH_SIZE"]["grid"],
                        "fetch_bytes": f, "write_bytes": wr, "bytes_per_launch": f + wr,
                        "algorithmic_bytes_per_launch": algorithmic}
+    if which == "gla":
+        out_d["gla_call"] = {"bytes_per_call": sum(out_d[k]["bytes_per_launch"] for k in sel),
+                             "algorithmic_bytes_per_call": sum(out_d[k]["algorithmic_bytes_per_launch"] for k in sel)}
     out_d["command"] = [
         f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {run}",
         f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {run}",

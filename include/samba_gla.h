@@ -22,9 +22,23 @@
  * bytes; v, o their element size.  o and h_last must not overlap any input,
  * except h_last == h0 exactly (the final state written in place).
  *
- * Computed as the recurrence (a diagonal scan per (head, value column), the
- * key dimension split over dstate / 4 lanes), which is exact and needs no
- * workspace; ownership, asynchrony and errors as for samba_scan.h.
+ * Two forms.  bf16 inputs with dstate 128 or 256 and head_dim a multiple of
+ * 32 run the chunked form (the GLA paper's, §3 and §4.2): 64-token chunks
+ * whose inter-chunk, intra-chunk and state products run on the matrix cores,
+ * with every operand that is not an input as a bf16 hi + lo pair (16
+ * significant bits; outputs within a few 1e-6 of the recurrence's scale).
+ * Each call first writes, per (64-token chunk slot, head), the decayed q and
+ * k, the chunk's decay and its intra-chunk matrix into a caller-owned device
+ * workspace of samba_gla_workspace_size() bytes (256-byte aligned; 145 KiB
+ * per slot and head at dstate 256; slots as for the SSD layer: nch per
+ * batched sequence, tokens / 64 + nseq in all when packed), which the chunk
+ * kernel then reads.  Calls that overlap in time need different workspaces;
+ * it may not overlap any input or output (SAMBA_ERR_ALIASING); NULL or too
+ * small is SAMBA_ERR_WORKSPACE.  For these calls v must also be 16-byte
+ * aligned and o 8-byte (bf16) or 16-byte (fp32) aligned.  The other shapes
+ * run the recurrence in fp32 (a diagonal scan per (head, value column), the
+ * key dimension split over dstate / 4 lanes) and need no workspace.
+ * Ownership, asynchrony and errors as for samba_scan.h.
  */
 #ifndef SAMBA_GLA_H
 #define SAMBA_GLA_H

@@ -1,6 +1,8 @@
 // samba_gla.hip -- gfx950 (MI355X) gated linear attention (the GLA layer that the hackernoon page "Microsoft's
-// Samba Model Redefines Long-Context Learning for AI", §2, names as a substitute for the Mamba layer), computed
-// as its recurrence: per head, S_t = diag(exp(gk_t)) S_{t-1} + k_tᵀ v_t, o_t = q_t S_t.
+// Samba Model Redefines Long-Context Learning for AI", §2, names as a substitute for the Mamba layer): per
+// head, S_t = diag(exp(gk_t)) S_{t-1} + k_tᵀ v_t, o_t = q_t S_t.  Two forms: the chunked form on the matrix
+// cores (bf16 inputs, 128 or 256 keys, values a multiple of 32; see the chunked-form section below) and the
+// recurrence (every other shape), which follows.
 //
 // The recurrence is a diagonal scan per (head, value column) over the key dimension.  A lane holds 4 keys of
 // C value columns (N / 4 lanes cover the keys; C = N / 64 from 64 keys up, so a wave covers 4 columns and a
@@ -417,7 +419,7 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 // 32-token half of a chunk whose gates sum to more than this falls back to the exact pairwise form.
 constexpr float kSpanMax = 64.f;
 
-// Prep kernel: block = (slot, head), 4 waves; slots between packed sequences return at once.
+// Prep kernel: block = (slot, head), 8 waves; slots between packed sequences return at once.
 //   * b = inclusive cumulative sum of gk over the chunk's 64 tokens (tokens past the sequence add 0);
 //   * scaled q and kᵀ and e^{b_64}, elementwise, straight into their workspace fragments;
 //   * A in 32 x 32 tiles (GLA paper, §4.2, secondary chunking): with m the decay at the start of a token
@@ -427,7 +429,8 @@ constexpr float kSpanMax = 64.f;
 //     48 MFMAs (bf16 hi + lo factors) per tile.  A half whose span exceeds kSpanMax for some key is
 //     recomputed exactly, Σ_n q_tn k_sn e^{b_tn − b_sn} term by term.
 template <int N>
-__global__ __launch_bounds__(256) void gla_prep_kernel(GlaChunkParams p) {
+__global__ __launch_bounds__(512) void gla_prep_kernel(GlaChunkParams p) {
+  constexpr int kT = 512;
   using W = ChunkWs<N>;
   constexpr int kQR = N + 8;   // LDS row strides (padded so that 16 consecutive rows hit distinct banks)
   constexpr int kBR = N + 4;
@@ -463,7 +466,7 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaChunkParams p) {
   if (tid < 2) sWide[tid] = 0;
   // q, k and gk rows (gk widened to fp32 in place of b)
 #pragma unroll 2
-  for (int i = tid; i < kCQ * N / 8; i += 256) {
+  for (int i = tid; i < kCQ * N / 8; i += kT) {
     const int t = i / (N / 8), c8 = i - t * (N / 8);
     const uint32_t off = static_cast<uint32_t>(t) * rowb + 16u * c8;
     const auto a = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
@@ -478,23 +481,33 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaChunkParams p) {
                                                      __uint_as_float(g[3] << 16), __uint_as_float(g[3] & 0xffff0000u));
   }
   __syncthreads();
-  if (tid < N) {   // inclusive cumulative sum over the tokens, one key per thread, in place
+  // inclusive cumulative sum over the tokens, in place: two threads per key (tokens 0..31 and 32..63), then the
+  // second adds the first's total
+  const int cn = tid % N, ch = tid / N;
+  if (tid < 2 * N) {
     float acc = 0.f;
-    for (int t = 0; t < kCQ; ++t) {
-      acc += sB[t * kBR + tid];
-      sB[t * kBR + tid] = acc;
+#pragma unroll 8
+    for (int t = 32 * ch; t < 32 * ch + 32; ++t) {
+      acc += sB[t * kBR + cn];
+      sB[t * kBR + cn] = acc;
     }
   }
   __syncthreads();
+  if (tid < 2 * N && ch == 1) {
+    const float b31 = sB[31 * kBR + cn];
+#pragma unroll 8
+    for (int t = 32; t < kCQ; ++t) sB[t * kBR + cn] += b31;
+  }
+  __syncthreads();
   unsigned char* ws = p.ws + (static_cast<int64_t>(slot) * p.heads + h) * W::kBytes;
-  for (int n = tid; n < N; n += 256) {
+  for (int n = tid; n < N; n += kT) {
     const float b31 = sB[31 * kBR + n], b63 = sB[(kCQ - 1) * kBR + n];
     reinterpret_cast<float*>(ws + W::kG)[n] = __builtin_amdgcn_exp2f(b63 * kLog2e);
     if (-b31 > kSpanMax) sWide[0] = 1;
     if (b31 - b63 > kSpanMax) sWide[1] = 1;
   }
   // q ⊙ e^{b_t} at contraction positions: 8 positions per item
-  for (int i = tid; i < kCQ * N / 8; i += 256) {
+  for (int i = tid; i < kCQ * N / 8; i += kT) {
     const int t = i / (N / 8), p8 = i - t * (N / 8);
     uint16_t hv[8], lv[8];
 #pragma unroll
@@ -507,7 +520,7 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaChunkParams p) {
     *reinterpret_cast<uint4*>(ws + W::qs(t >> 5, p8 >> 2, (p8 >> 1) & 1, 1) + ln) = pack8(lv);
   }
   // (k ⊙ e^{b_64 − b_s})ᵀ: 8 tokens of one key per item
-  for (int i = tid; i < N * kCQ / 8; i += 256) {
+  for (int i = tid; i < N * kCQ / 8; i += kT) {
     const int n = i % N, tb = i / N;
     const float be = sB[(kCQ - 1) * kBR + n];
     uint16_t hv[8], lv[8];
@@ -551,7 +564,7 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaChunkParams p) {
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     if (!sWide[hf]) continue;   // (block-uniform)
-    for (int i = tid; i < 32 * 32; i += 256) {
+    for (int i = tid; i < 32 * 32; i += kT) {
       const int tl = i >> 5, sl = i & 31;
       if (sl > tl) continue;
       const int t = 32 * hf + tl, sj = 32 * hf + sl;
@@ -564,7 +577,7 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(GlaChunkParams p) {
   }
   __syncthreads();
   // A fragments: item (tt, kk, lane) holds row 32 tt + l % 32, key tokens 16 kk + 8 (l / 32) + 0..7
-  for (int i = tid; i < 2 * 4 * 64; i += 256) {
+  for (int i = tid; i < 2 * 4 * 64; i += kT) {
     const int ln = i & 63, kk = (i >> 6) & 3, tt = i >> 8;
     const int tl = ln & 31, s0 = 16 * kk + 8 * (ln >> 5);
     const int sb = s0 >> 5;
@@ -607,7 +620,7 @@ __global__ __launch_bounds__(64 * (N / 32)) void gla_chunk_kernel(GlaChunkParams
   constexpr int kThreads = 64 * NW;
   constexpr int kVE = kCQ * 32 / kThreads;      // v elements of a chunk per thread (8 or 4)
   __shared__ __attribute__((aligned(16))) uint16_t sVt[2][32 * kVtRow];   // the chunk's v, [value][token]
-  __shared__ __attribute__((aligned(16))) float sO[NW][kCQ * 32];         // partial outputs, [token][value]
+  __shared__ __attribute__((aligned(16))) float sO[2][NW][kCQ * 32];      // partial outputs, [token][value]
   __shared__ __attribute__((aligned(16))) float sG[2][N];                  // the chunk's e^{b_64}
   const int logical = xcd_remap(blockIdx.x, p.nblocks);
   const int vt = logical % p.vtiles, sh = logical / p.vtiles;
@@ -710,10 +723,36 @@ __global__ __launch_bounds__(64 * (N / 32)) void gla_chunk_kernel(GlaChunkParams
   // one chunk; the parity of c (which LDS buffer and register set) is a compile-time constant
   // TTc: the token tile of this wave's share of A V (waves 0 .. NW / 2 - 1 take tile 0): a compile-time
   // constant, so that the accumulator it feeds is chosen without selects
+  // chunk c's outputs: the sum of the waves' partials in buffer ob, rounded and stored
+  auto reduce_store = [&](int c, int ob) {
+    const int nv = (cs.len - c * kCQ) < kCQ ? cs.len - c * kCQ : kCQ;
+    for (int i = tid; i < kCQ * 8; i += kThreads) {
+      const int t = i >> 3, q4 = i & 7;
+      if (t >= nv) continue;
+      float4 a = *reinterpret_cast<const float4*>(&sO[ob][0][t * 32 + 4 * q4]);
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        const float4 b = *reinterpret_cast<const float4*>(&sO[ob][w][t * 32 + 4 * q4]);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      const int64_t oe = (cs.t0 + static_cast<int64_t>(c) * kCQ + t) * p.heads * p.head_dim +
+                         static_cast<int64_t>(h) * p.head_dim + v0 + 4 * q4;
+      if constexpr (sizeof(Tout) == 2) {
+        const uint2 w2 = make_uint2(bf16r(a.x) | (static_cast<uint32_t>(bf16r(a.y)) << 16),
+                                    bf16r(a.z) | (static_cast<uint32_t>(bf16r(a.w)) << 16));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + oe) = w2;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.o) + oe) = a;
+      }
+    }
+  };
+  // One barrier per chunk: at the top of chunk c, its v and e^{b_64} are staged and every wave's partial
+  // outputs of chunk c - 1 are in LDS; they are summed and stored during chunk c, and their buffer is
+  // written again only in chunk c + 1, after the next barrier.
   auto step = [&](int c, auto bufc, auto ttc) {
     constexpr int buf = decltype(bufc)::value;
     constexpr int TTc = decltype(ttc)::value;
-    __syncthreads();   // v of chunk c staged; the previous chunk's partial outputs consumed
+    __syncthreads();
     // next chunk's v and operands (the last chunk reloads its own: no branch around the loads)
     const int cn = c + 1 < nch ? c + 1 : c, cnn = c + 2 < nch ? c + 2 : cn;
     // issue order = wait order: this chunk's kᵀ (needed first of these), then chunk c + 2's v and e^{b_64}
@@ -755,7 +794,8 @@ __global__ __launch_bounds__(64 * (N / 32)) void gla_chunk_kernel(GlaChunkParams
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sO[wave][(32 * tt + 8 * (e >> 2) + 4 * hi + (e & 3)) * 32 + l32] = op[tt][e];
+      for (int e = 0; e < 16; ++e) sO[buf][wave][(32 * tt + 8 * (e >> 2) + 4 * hi + (e & 3)) * 32 + l32] = op[tt][e];
+    if (c > 0) reduce_store(c - 1, buf ^ 1);
     // state: S ← diag(e^{b_64}) S + (k ⊙ e^{b_64 − b})ᵀ V
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -776,27 +816,6 @@ __global__ __launch_bounds__(64 * (N / 32)) void gla_chunk_kernel(GlaChunkParams
     }
     put_v(buf ^ 1, vw_next);   // (chunk c + 1's buffers were last read in chunk c - 1)
     put_g(buf ^ 1, gw_next);
-    __syncthreads();      // every wave's partial outputs are in LDS
-    const int nv = (cs.len - c * kCQ) < kCQ ? cs.len - c * kCQ : kCQ;
-    for (int i = tid; i < kCQ * 8; i += kThreads) {
-      const int t = i >> 3, q4 = i & 7;
-      if (t >= nv) continue;
-      float4 a = *reinterpret_cast<const float4*>(&sO[0][t * 32 + 4 * q4]);
-#pragma unroll
-      for (int w = 1; w < NW; ++w) {
-        const float4 b = *reinterpret_cast<const float4*>(&sO[w][t * 32 + 4 * q4]);
-        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-      }
-      const int64_t oe = (cs.t0 + static_cast<int64_t>(c) * kCQ + t) * p.heads * p.head_dim +
-                         static_cast<int64_t>(h) * p.head_dim + v0 + 4 * q4;
-      if constexpr (sizeof(Tout) == 2) {
-        const uint2 w2 = make_uint2(bf16r(a.x) | (static_cast<uint32_t>(bf16r(a.y)) << 16),
-                                    bf16r(a.z) | (static_cast<uint32_t>(bf16r(a.w)) << 16));
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + oe) = w2;
-      } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(p.o) + oe) = a;
-      }
-    }
     cur = nxt;
   };
   auto run = [&](auto ttc) {
@@ -808,6 +827,10 @@ __global__ __launch_bounds__(64 * (N / 32)) void gla_chunk_kernel(GlaChunkParams
   // (both halves of the workgroup run the same barriers)
   if (wave < NW / 2) run(std::integral_constant<int, 0>());
   else run(std::integral_constant<int, 1>());
+  if (nch > 0) {
+    __syncthreads();
+    reduce_store(nch - 1, (nch - 1) & 1);
+  }
   if (p.h_last) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -885,11 +908,11 @@ hipError_t launch_chunked(const GlaChunkParams& p, int N, int64_t nslots, hipStr
   // (no tokens: no prep, and the chunk kernel only carries h0 to h_last)
   if (N == 256) {
     if (nslots > 0)
-      hipLaunchKernelGGL((gla_prep_kernel<256>), dim3(static_cast<uint32_t>(nslots * p.heads)), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((gla_prep_kernel<256>), dim3(static_cast<uint32_t>(nslots * p.heads)), dim3(512), 0, s, p);
     hipLaunchKernelGGL((gla_chunk_kernel<Tout, 256>), dim3(static_cast<uint32_t>(p.nblocks)), dim3(64 * 8), 0, s, p);
   } else {
     if (nslots > 0)
-      hipLaunchKernelGGL((gla_prep_kernel<128>), dim3(static_cast<uint32_t>(nslots * p.heads)), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((gla_prep_kernel<128>), dim3(static_cast<uint32_t>(nslots * p.heads)), dim3(512), 0, s, p);
     hipLaunchKernelGGL((gla_chunk_kernel<Tout, 128>), dim3(static_cast<uint32_t>(p.nblocks)), dim3(64 * 4), 0, s, p);
   }
   return hipGetLastError();
