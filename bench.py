@@ -1267,7 +1267,7 @@ def main():
         _counter_summary(*args.pmc_summary_gla, which="gla")
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only (this build has no multi-GPU path); run with --gpus 1",
+        print("bench.py measures one GPU only (the library has no multi-GPU path); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
