@@ -9,11 +9,11 @@
 //
 // Prefill design (FlashAttention-2's online softmax, laid out for CDNA4's
 // 64-wide waves and v_mfma_f32_32x32x16_bf16):
-//   * a workgroup of 4 waves owns 128 consecutive queries of one head; each
+//   * a workgroup of 8 waves owns 256 consecutive queries of one head; each
 //     wave owns 32 of them and keeps their rotated q (32 x 128 bf16) in
 //     registers for the whole key loop;
 //   * keys advance 64 at a time through double-buffered LDS tiles (K as
-//     [key][hd], V transposed as [hd][key]), all 256 threads staging;
+//     [key][hd], V transposed as [hd][key]), half the waves staging K and half V;
 //   * scores are formed transposed, S^T = K Q^T, so that every lane holds one
 //     query's scores for 16 of each 32 keys: the row maximum is a reduction
 //     inside the lane plus one exchange with the lane 32 away, and the running
@@ -55,7 +55,9 @@ using rsrc_t = __amdgpu_buffer_rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped, unswizzled) buffer
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kHD = 128;                // head size served by the attention kernels
-constexpr int kQB = 128;                // queries per prefill workgroup
+constexpr int kQB = 256;                // queries per prefill workgroup (8 waves of 32)
+constexpr int kQBShift = 8;             // log2(kQB)
+constexpr int kSwaThreads = 512;
 constexpr int kKB = 64;                 // keys per prefill tile
 constexpr int kKRow = kHD + 8;          // K tile row stride in LDS (bf16): 16 rows cover all banks
 constexpr float kRescale = 8.0f;        // exp2 units a score may exceed the softmax reference by
@@ -274,12 +276,12 @@ struct SwaParams {
 __device__ __forceinline__ int key_slot(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 template <typename Tout>
-__global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
+__global__ __launch_bounds__(kSwaThreads, 1) void swa_fwd_kernel(SwaParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKB * kKRow];  // [key][hd], rows padded to 272 bytes
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kHD * kKB];   // [hd][slot], group g at g ^ vswz(hd)
   const int logical = xcd_remap(blockIdx.x, p.nqb * p.heads);
   const int head = logical / p.nqb;
-  const SeqBlock sb = locate(p.cu, p.nseq, p.total, p.seqlen, p.per_seq, logical - head * p.nqb, 7);
+  const SeqBlock sb = locate(p.cu, p.nseq, p.total, p.seqlen, p.per_seq, logical - head * p.nqb, kQBShift);
   if (sb.j < 0 || sb.j * kQB >= sb.len) return;   // the whole workgroup leaves together
   const int len = sb.len;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -315,45 +317,48 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
     }
   }
 
-  // staging: K rows sr + 16 r, 16-byte group sg; V keys 4 sr .. 4 sr + 3, hd 8 sg .. 8 sg + 7
-  const int sr = tid >> 4, sg = tid & 15;
-  uint4 kr[4], vr[4];
-  // one offset register per tensor; the row steps go in the instruction's scalar offset
-  const uint32_t gk_off = static_cast<uint32_t>(sr) * row_bytes + sg * 16;
-  const uint32_t gv_off = static_cast<uint32_t>(4 * sr) * row_bytes + sg * 16;
-  auto gload = [&](int kt) {
+  // staging: waves 4..7 load K (rows sr + 16 r, 16-byte group sg), waves 0..3 load V (keys 4 sr .. 4 sr + 3,
+  // hd 8 sg .. 8 sg + 7), four 16-byte pieces per thread either way
+  const bool stage_k = wave >= 4;
+  const int st = stage_k ? tid - 256 : tid;
+  const int sr = st >> 4, sg = st & 15;
+  uint4 sv0[4], sv1[4];   // two register sets: the tile after next is loaded while the next one is stored
+  // one offset register; the row steps go in the instruction's scalar offset
+  const uint32_t g_off = (stage_k ? static_cast<uint32_t>(sr) : static_cast<uint32_t>(4 * sr)) * row_bytes + sg * 16;
+  const uint32_t g_step = stage_k ? 16u * row_bytes : row_bytes;
+  auto gload = [&](int kt, uint4 (&sv)[4]) {
     const int64_t tok = sb.t0 + static_cast<int64_t>(kt) * kKB;
     const int rows = (len - kt * kKB) < kKB ? len - kt * kKB : kKB;
-    const rsrc_t rk = rsrc_rows(p.k + tok * p.heads * kHD + head_off, rows, row_bytes);
-    const rsrc_t rv = rsrc_rows(p.v + tok * p.heads * kHD + head_off, rows, row_bytes);
+    const rsrc_t rs = rsrc_rows((stage_k ? p.k : p.v) + tok * p.heads * kHD + head_off, rows, row_bytes);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) kr[r] = ld16s(rk, gk_off, 16u * r * row_bytes);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vr[i] = ld16s(rv, gv_off, static_cast<uint32_t>(i) * row_bytes);
+    for (int i = 0; i < 4; ++i) sv[i] = ld16s(rs, g_off, static_cast<uint32_t>(i) * g_step);
   };
   // V^T element (row 8 sg + d, slot s) of this thread's keys: row (8 sg + d) * 64, group (s >> 3) ^ vswz(row)
   // with vswz(8 sg + d) = (sg ^ d) & 7.  As 8 sg * 64 has no bits in 3..5, the address is vbase ^ (d << 3)
   // plus d * 64: one XOR per row, the rest an immediate offset (no per-row address registers).
   const int vslot = key_slot(4 * sr);
   const int vbase = 8 * sg * kKB + ((((vslot >> 3) ^ sg) & 7) << 3) + (vslot & 7);
-  auto lstore = [&](auto bufc) {
+  auto lstore = [&](auto bufc, const uint4 (&sv)[4]) {
     constexpr int buf = decltype(bufc)::value;
+    if (stage_k) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = sr + 16 * r;
-      *reinterpret_cast<uint4*>(&sK[buf][row * kKRow + 8 * sg]) = kr[r];
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int row = sr + 16 * r;
+        *reinterpret_cast<uint4*>(&sK[buf][row * kKRow + 8 * sg]) = sv[r];
+      }
+    } else {
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const int w = d >> 1;
-      const uint32_t a0 = (&vr[0].x)[w], a1 = (&vr[1].x)[w], a2 = (&vr[2].x)[w], a3 = (&vr[3].x)[w];
-      // bf16 number d of keys 4 sr + 0..3, packed in key order (byte select: low or high halves)
-      constexpr uint32_t kLoHalves = 0x05040100u, kHiHalves = 0x07060302u;
-      const uint32_t sel = (d & 1) ? kHiHalves : kLoHalves;
-      uint2 pk;
-      pk.x = __builtin_amdgcn_perm(a1, a0, sel);
-      pk.y = __builtin_amdgcn_perm(a3, a2, sel);
-      *reinterpret_cast<uint2*>(&sV[buf][(vbase ^ (d << 3)) + d * kKB]) = pk;
+      for (int d = 0; d < 8; ++d) {
+        const int w = d >> 1;
+        const uint32_t a0 = (&sv[0].x)[w], a1 = (&sv[1].x)[w], a2 = (&sv[2].x)[w], a3 = (&sv[3].x)[w];
+        // bf16 number d of keys 4 sr + 0..3, packed in key order (byte select: low or high halves)
+        constexpr uint32_t kLoHalves = 0x05040100u, kHiHalves = 0x07060302u;
+        const uint32_t sel = (d & 1) ? kHiHalves : kLoHalves;
+        uint2 pk;
+        pk.x = __builtin_amdgcn_perm(a1, a0, sel);
+        pk.y = __builtin_amdgcn_perm(a3, a2, sel);
+        *reinterpret_cast<uint2*>(&sV[buf][(vbase ^ (d << 3)) + d * kKB]) = pk;
+      }
     }
   };
 
@@ -471,18 +476,26 @@ __global__ __launch_bounds__(256, 2) void swa_fwd_kernel(SwaParams p) {
 
   // one tile: prefetch the next into registers, compute from LDS buffer `buf`, stage the next into the other
   // buffer.  Two tiles per loop trip so that the buffer (and every LDS address) is a compile-time constant.
+  // Tile kt (LDS buffer buf, the parity of kt - kt_lo): register set buf ^ 1 holds tile kt + 1 (loaded one
+  // tile earlier), and set buf takes tile kt + 2 (the last tile is reloaded past the end: no branch around
+  // the loads); compute from LDS, then store tile kt + 1 into the other buffer.
   auto tile = [&](auto bufc, int kt) {
     constexpr int buf = decltype(bufc)::value;
-    const bool more = kt < kt_hi;
-    if (more) gload(kt + 1);
+    const int k2 = kt + 2 <= kt_hi ? kt + 2 : kt_hi;
+    if constexpr (buf == 0) gload(k2, sv0);
+    else gload(k2, sv1);
     const int k_first = kt * kKB, k_last = k_first + kKB - 1;
     if (wave_live && k_first <= q_hi && k_last >= q_lo - p.window)
       compute(bufc, kt, k_last > q_lo || k_first < q_hi - p.window);
-    if (more) lstore(std::integral_constant<int, buf ^ 1>{});
+    if (kt < kt_hi) {
+      if constexpr (buf == 0) lstore(std::integral_constant<int, 1>{}, sv1);
+      else lstore(std::integral_constant<int, 0>{}, sv0);
+    }
     __syncthreads();
   };
-  gload(kt_lo);
-  lstore(std::integral_constant<int, 0>{});
+  gload(kt_lo, sv0);
+  gload(kt_lo + 1 <= kt_hi ? kt_lo + 1 : kt_hi, sv1);
+  lstore(std::integral_constant<int, 0>{}, sv0);
   __syncthreads();
   for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
     tile(std::integral_constant<int, 0>{}, kt);
@@ -775,7 +788,7 @@ samba_status samba_swa_fwd(const samba_swa_fwd_args* a, void* stream) {
   if (a->struct_size != sizeof(samba_swa_fwd_args)) return SAMBA_ERR_BAD_STRUCT;
   SwaParams p{};
   int64_t nqb = 0;
-  samba_status st = token_shape(a->batch, a->seqlen, a->cu_seqlens, a->nseq, &nqb, 7, &p.per_seq);
+  samba_status st = token_shape(a->batch, a->seqlen, a->cu_seqlens, a->nseq, &nqb, kQBShift, &p.per_seq);
   if (st != SAMBA_OK) return st;
   if (a->heads < 1 || a->heads > 4096 || a->window < 0) return SAMBA_ERR_BAD_SHAPE;
   if (a->head_dim != kHD) return SAMBA_ERR_UNSUPPORTED;
@@ -806,8 +819,8 @@ samba_status samba_swa_fwd(const samba_swa_fwd_args* a, void* stream) {
   p.c = kLog2e / sqrtf(static_cast<float>(kHD));
   const dim3 grid(static_cast<uint32_t>(nqb * a->heads));
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a->out_dtype == SAMBA_BF16) hipLaunchKernelGGL(swa_fwd_kernel<uint16_t>, grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(swa_fwd_kernel<float>, grid, dim3(256), 0, s, p);
+  if (a->out_dtype == SAMBA_BF16) hipLaunchKernelGGL(swa_fwd_kernel<uint16_t>, grid, dim3(kSwaThreads), 0, s, p);
+  else hipLaunchKernelGGL(swa_fwd_kernel<float>, grid, dim3(kSwaThreads), 0, s, p);
   return hipGetLastError() == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
 }
 
