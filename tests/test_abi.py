@@ -348,6 +348,7 @@ PROJ_CASES = {
     "f32_inputs": (lambda a: setattr(a, "in_dtype", S.SAMBA_F32), 3),
     "out_dtype": (lambda a: setattr(a, "out_dtype", 9), 3),
     "dim_not_multiple_of_8": (lambda a: setattr(a, "dim", 60), 2),
+    "dim_2_pow_22": (lambda a: setattr(a, "dim", 1 << 22), 2),   # 256-row tile byte offsets past 2^31
     "neg_tokens": (lambda a: setattr(a, "tokens", -1), 2),
     "zero_dstate": (lambda a: setattr(a, "dstate", 0), 2),
     "null_W": (lambda a: setattr(a, "W", None), 1),
