@@ -217,11 +217,9 @@ struct Stage {
   bf16x8_t m[3][2][2][64];                          // M tiles (0,0), (0,1), (1,1): [tile][kk][hi/lo][lane]
   float dl[kQ], la[kQ], w[kQ];                      // Δ_s, la_s (log2 units), w_s
 };
-constexpr int kYRow = kP + 4;                        // row stride (floats) of the staged output
 template <int N>
 struct Smem {
   Stage<N> st[2];                                   // chunk c uses st[c & 1]
-  float yf[kQ * kYRow];                             // the chunk's output before the gate [t][p]
   float4 xch[4][4][64];                             // (d) partial sums for the partner wave
   float hs[4][2][kQ];                               // each helper wave's own la, Δ of the chunk it prepares
 };
@@ -267,7 +265,7 @@ __device__ __forceinline__ void wave_sync() {
 //   3. helpers 0 .. 2 turn the chunk's Sᵀ tile h (loaded from the workspace two chunks earlier) into M
 //      = Sᵀ 2^(la_t - la_s) Δ_s (s <= t), + D on the diagonal, published as bf16 hi + lo operand images;
 //   4. load chunk c + 3 and the workspace tile of chunk c + 3.
-template <typename Tout, int N, bool kGate>
+template <int N>
 __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
   constexpr int kRow = Stage<N>::kRow;
   constexpr int NPR = N / 8;              // 16-byte pieces per C row
@@ -281,13 +279,11 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
   const int m_si = hw == 2 ? 1 : 0, m_tb = hw == 0 ? 0 : 1;
   const int tile = hw < 3 ? hw : 2;       // (helper 3 loads a tile it does not use: no branch around loads)
   struct Set {
-    uint4 cr[PC], br[NB][2], xr[2], zr[2];
+    uint4 cr[PC], br[NB][2], xr[2];
     uint16_t dtr;
   } set[2];
-  uint4 zring[2][2];                      // z of the chunk being finished and of the next one
   f32x16_t sring[2];                      // Sᵀ tiles two chunks ahead
   // z and output pieces: row t / 8 + 32 q, 8-column run t % 8
-  const int zrow = t >> 3, zcol = 8 * (t & 7);
   const int nchunks = (cx.len + kQ - 1) / kQ;
   auto load = [&](auto kset, int c) {
     Set& st = set[decltype(kset)::value];
@@ -305,11 +301,6 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
 #pragma unroll
     for (int k = 0; k < 2; ++k)
       st.xr[k] = ld16(cx.rx, static_cast<uint32_t>(c0 + 2 * r + k) * cx.rowx + (8 * cg) * 2);
-    if constexpr (kGate) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        st.zr[k] = ld16(cx.rz, static_cast<uint32_t>(c0 + zrow + 32 * k) * cx.rowx + zcol * 2);
-    }
     st.dtr = __builtin_amdgcn_raw_buffer_load_b16(cx.rdt, static_cast<uint32_t>(c0 + lane) * cx.H * 2, 0, 0);
     // the chunk's Sᵀ tile (the last chunk's past the sequence: a padding chunk's M is the skip alone)
     const int cs = c < nchunks ? c : nchunks - 1;
@@ -347,8 +338,6 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
       const uint32_t w0 = word(st.xr[0], j / 2), w1 = word(st.xr[1], j / 2);
       *reinterpret_cast<uint32_t*>(&g.xt[(8 * cg + j) * kTRow + 2 * r]) = (j & 1) ? highs(w0, w1) : lows(w0, w1);
     }
-    zring[K][0] = st.zr[0];
-    zring[K][1] = st.zr[1];
     // Δ, la (inclusive prefix sum of Δ A log2e) and w = 2^(la_end - la) Δ; tokens past the sequence get
     // Δ = 0 (no decay, no input)
     const float dlt = c0 + lane < cx.len ? softplus_f32(widen(st.dtr) + cx.bias) : 0.0f;
@@ -389,39 +378,6 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
       }
     }
   };
-  // chunk k's output (k < 0: nothing, the stores go nowhere), z from the ring slot of k
-  auto finish = [&](auto kz, int k) {
-    constexpr int K = decltype(kz)::value;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = zrow + 32 * q;
-      const float4 v0 = *reinterpret_cast<const float4*>(&sm.yf[row * kYRow + zcol]);
-      const float4 v1 = *reinterpret_cast<const float4*>(&sm.yf[row * kYRow + zcol + 4]);
-      float yv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      if constexpr (kGate) {
-        const uint4 zv = zring[K][q];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t zw = word(zv, j / 2);
-          yv[j] *= silu_f32(__uint_as_float((j & 1) ? (zw & 0xffff0000u) : (zw << 16)));
-        }
-      }
-      const uint32_t off0 = k >= 0 ? static_cast<uint32_t>(k * kQ + row) * cx.H * kP * sizeof(Tout) : kNowhere;
-      if constexpr (sizeof(Tout) == 2) {
-        u32x4_t w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          w[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(yv[2 * j]))) |
-                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(yv[2 * j + 1]))) << 16);
-        __builtin_amdgcn_raw_buffer_store_b128(w, cx.ry, off0 + (k >= 0 ? zcol * 2 : 0), 0, 0);
-      } else {
-        const u32x4_t w0 = {__float_as_uint(yv[0]), __float_as_uint(yv[1]), __float_as_uint(yv[2]), __float_as_uint(yv[3])};
-        const u32x4_t w1 = {__float_as_uint(yv[4]), __float_as_uint(yv[5]), __float_as_uint(yv[6]), __float_as_uint(yv[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(w0, cx.ry, off0 + (k >= 0 ? zcol * 4 : 0), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(w1, cx.ry, off0 + (k >= 0 ? zcol * 4 + 16 : 16), 0, 0);
-      }
-    }
-  };
   // An even number of chunks (the state waves pad the same way; a chunk past the sequence reads zeros and
   // changes nothing), and no load or store behind a data-dependent branch inside the loop, so that the
   // compiler's wait counts keep the other register set's loads in flight.
@@ -434,7 +390,6 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
   }
   __syncthreads();   // chunk 0 staged
   auto body = [&](auto knext, int c) {
-    finish(knext, c - 1);   // chunk c - 1's z sits in the slot that chunk c + 1's takes next
     prepare(knext, c + 1);
     load(knext, c + 3);
     __syncthreads();   // X1: the state waves' partial sums
@@ -444,12 +399,12 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
     body(std::integral_constant<int, 1>{}, c);
     body(std::integral_constant<int, 0>{}, c + 1);
   }
-  if (npad > 0) finish(std::integral_constant<int, 1>{}, npad - 1);
 }
 
 // State wave k (0 .. 3): p-tile a = k & 1, n-tiles of half HB = k >> 1 (element e of tile nt: n = 32 nt +
-// 8 (e / 4) + 4 hi + e % 4, p = 32 a + lane % 32); finishes the output tile (a, HB) up to the gate.
-template <int N, int HB>
+// 8 (e / 4) + 4 hi + e % 4, p = 32 a + lane % 32); finishes the output tile (a, HB): sums it with the
+// partner's partial sums, applies the gate (z loaded one chunk ahead) and stores it.
+template <typename Tout, int N, int HB, bool kGate>
 __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const float* h0, float* h_last) {
   constexpr int NTW = N / 64;
   constexpr int kRow = Stage<N>::kRow;
@@ -476,8 +431,27 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
   const int npad = ((cx.len + kQ - 1) / kQ + 1) & ~1;
   __syncthreads();   // chunk 0 staged
 
+  // z and y pieces of this lane: token t_own, channels 32 a + 8 q + 4 hi + 0..3 (q = 0..3); z of the next
+  // chunk is loaded while this one computes (register set kbuf ^ 1)
+  uint2 zr0[4], zr1[4];
+  auto load_z = [&](int c, uint2 (&zr)[4]) {
+    if constexpr (kGate) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+            cx.rz, static_cast<uint32_t>(c * kQ + t_own) * cx.rowx + (32 * a + 8 * q + 4 * hi) * 2, 0, 0);
+        zr[q] = make_uint2(v[0], v[1]);
+      }
+    }
+  };
+  const uint32_t rowy = static_cast<uint32_t>(cx.H) * kP * sizeof(Tout);
+  load_z(0, zr0);
+  int cc = 0;   // the chunk being computed
   auto chunk = [&](auto kbuf) {
-    const Stage<N>& g = sm.st[decltype(kbuf)::value];
+    constexpr int KB = decltype(kbuf)::value;
+    const Stage<N>& g = sm.st[KB];
+    if constexpr (KB == 0) load_z(cc + 1, zr1);
+    else load_z(cc + 1, zr0);
     // operands of (d): C in the state accumulators' n order, both t-tiles; of (c): X in M's s order
     bf16x8_t cop[2][NTW][2], xop[HB + 1][2];
 #pragma unroll
@@ -559,15 +533,34 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
 
     __syncthreads();   // X1: the partner's partial sums are in LDS
     const float eo = __builtin_amdgcn_exp2f(la_t);
+    const uint2* zr = KB == 0 ? zr0 : zr1;
+    // (the stores of a padding chunk past the sequence fall outside the output resource)
+    const uint32_t yrow = static_cast<uint32_t>(cc * kQ + t_own) * rowy;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 o = sm.xch[wave ^ 2][q][lane];
-      const float4 v = make_float4(fmaf(eo, yo[HB][4 * q] + o.x, yd[4 * q]), fmaf(eo, yo[HB][4 * q + 1] + o.y, yd[4 * q + 1]),
-                                   fmaf(eo, yo[HB][4 * q + 2] + o.z, yd[4 * q + 2]),
-                                   fmaf(eo, yo[HB][4 * q + 3] + o.w, yd[4 * q + 3]));
-      *reinterpret_cast<float4*>(&sm.yf[t_own * kYRow + 32 * a + 8 * q + 4 * hi]) = v;
+      float v[4] = {fmaf(eo, yo[HB][4 * q] + o.x, yd[4 * q]), fmaf(eo, yo[HB][4 * q + 1] + o.y, yd[4 * q + 1]),
+                    fmaf(eo, yo[HB][4 * q + 2] + o.z, yd[4 * q + 2]), fmaf(eo, yo[HB][4 * q + 3] + o.w, yd[4 * q + 3])};
+      if constexpr (kGate) {
+        const uint32_t zw[2] = {zr[q].x, zr[q].y};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          v[j] *= silu_f32(__uint_as_float((j & 1) ? (zw[j >> 1] & 0xffff0000u) : (zw[j >> 1] << 16)));
+      }
+      const uint32_t off = yrow + (32 * a + 8 * q + 4 * hi) * static_cast<uint32_t>(sizeof(Tout));
+      if constexpr (sizeof(Tout) == 2) {
+        const u32x2_t w = {static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[0]))) |
+                               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[1]))) << 16),
+                           static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2]))) |
+                               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[3]))) << 16)};
+        __builtin_amdgcn_raw_buffer_store_b64(w, cx.ry, off, 0, 0);
+      } else {
+        const u32x4_t w = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, cx.ry, off, 0, 0);
+      }
     }
-    __syncthreads();   // X2: chunk computed (output staged), the next chunk prepared
+    ++cc;
+    __syncthreads();   // X2: chunk computed, the next chunk prepared
   };
   for (int c = 0; c < npad; c += 2) {
     chunk(std::integral_constant<int, 0>{});
@@ -621,9 +614,9 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_fwd_kernel(SsdParams p) {
   cx.ws = p.ws + (static_cast<int64_t>(si.slot0) * G + g) * 3 * kTileFloats;
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  if (wave >= 4) helper_wave<Tout, N, kGate>(cx, sm);
-  else if (wave >= 2) state_wave<N, 1>(cx, sm, p.h0, p.h_last);
-  else state_wave<N, 0>(cx, sm, p.h0, p.h_last);
+  if (wave >= 4) helper_wave<N>(cx, sm);
+  else if (wave >= 2) state_wave<Tout, N, 1, kGate>(cx, sm, p.h0, p.h_last);
+  else state_wave<Tout, N, 0, kGate>(cx, sm, p.h0, p.h_last);
 }
 
 bool aligned(const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) & (a - 1)) == 0; }
