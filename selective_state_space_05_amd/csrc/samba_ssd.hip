@@ -20,17 +20,18 @@
 //
 // Roles (32x32 tiles, v_mfma_f32_32x32x16_bf16, two waves per SIMD):
 //   * state waves 0 .. 3: wave k holds p-tile a = k & 1 of the state for half hb = k >> 1 of the n-tiles
-//     as Hᵀ accumulators and finishes the output tile (p-tile a, t-tile hb).  Products are laid out so
+//     as Hᵀ accumulators and finishes the output tile (p-tile a, t-tile hb): the partner's partial sums,
+//     the gate (z loaded one chunk ahead in the wave's own layout) and the store.  Products are laid out so
 //     that one product's accumulators are the next one's operand: Sᵀ's accumulator rows s are the
 //     contraction index of (c) (a lane's 8 elements of a 16-wide step are s = 16kk + 8(j/4) + 4hi + j%4,
 //     and X is read from LDS in that order), and the Hᵀ accumulators (lane = column p) are (d)'s A operand
 //     the same way, with C read in the matching n order.  (d) over a wave's half of the states gives
 //     partial sums for both t-tiles; the other t-tile's goes to the partner wave through LDS;
-//   * helper waves 4 .. 7 load C, B, X, z and Δ through a ring of two register sets and stage them into
-//     LDS (C and z row-major, B and X transposed, each store a run of consecutive words across the lanes);
-//     one of them computes Δ, la and w with a DPP prefix sum; they store bf16 y, which the state waves
-//     stage in LDS, as whole 128-byte lines one chunk later.  (z and y in the state waves' own
-//     layout would be 8-byte pieces of 32 rows per instruction, which costs more than the arithmetic.)
+//   * helper waves 4 .. 7 load C, B, X and Δ through a ring of two register sets and stage them into
+//     LDS (C row-major, B and X transposed, each store a run of consecutive words across the lanes);
+//     each computes Δ, la and w with a DPP prefix sum, and three of them build the chunk's masked M tiles.
+//     (z and y in the state waves' layout are 8-byte pieces of 32 rows per instruction; staging y through
+//     LDS for whole-line stores by the helpers measured no faster.)
 // The inputs are staged in two alternating LDS buffers, so the helpers fill chunk c + 1's while the state
 // waves compute chunk c: two barriers per chunk (partial sums exchanged; chunk done and next one staged).
 #include <hip/hip_runtime.h>
@@ -257,14 +258,13 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // Helper waves (h = 0 .. 3).  While the state waves compute chunk c, the helpers
-//   1. finish chunk c - 1: its staged output times silu(z), as bf16 or fp32 whole-line stores;
-//   2. stage chunk c + 1 (loaded two chunks earlier into a ring of two register sets) into its LDS stage:
+//   1. stage chunk c + 1 (loaded two chunks earlier into a ring of two register sets) into its LDS stage:
 //      C as row-major pieces, B and X as pairs of rows at one 8-column run (so that the transposed stores
 //      of consecutive lanes are consecutive words); every helper computes Δ, la and w of the chunk with a
-//      DPP prefix sum (helper 0 publishes them, the others keep their own copy for step 3);
-//   3. helpers 0 .. 2 turn the chunk's Sᵀ tile h (loaded from the workspace two chunks earlier) into M
+//      DPP prefix sum (helper 0 publishes them, the others keep their own copy for step 2);
+//   2. helpers 0 .. 2 turn the chunk's Sᵀ tile h (loaded from the workspace two chunks earlier) into M
 //      = Sᵀ 2^(la_t - la_s) Δ_s (s <= t), + D on the diagonal, published as bf16 hi + lo operand images;
-//   4. load chunk c + 3 and the workspace tile of chunk c + 3.
+//   3. load chunk c + 3 and the workspace tile of chunk c + 3.
 template <int N>
 __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
   constexpr int kRow = Stage<N>::kRow;
@@ -283,7 +283,6 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
     uint16_t dtr;
   } set[2];
   f32x16_t sring[2];                      // Sᵀ tiles two chunks ahead
-  // z and output pieces: row t / 8 + 32 q, 8-column run t % 8
   const int nchunks = (cx.len + kQ - 1) / kQ;
   auto load = [&](auto kset, int c) {
     Set& st = set[decltype(kset)::value];
