@@ -419,27 +419,34 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 // 32-token half of a chunk whose gates sum to more than this falls back to the exact pairwise form.
 constexpr float kSpanMax = 64.f;
 
-// Prep kernel: block = (slot, head), 8 waves; slots between packed sequences return at once.
+// Prep kernel: block = (slot, head), 8 waves; slots between packed sequences return at once.  The keys go
+// through in passes of 128 (one for N = 128, two for N = 256), which keeps the LDS footprint near 80 KiB so
+// that two blocks share a CU.  Per pass:
 //   * b = inclusive cumulative sum of gk over the chunk's 64 tokens (tokens past the sequence add 0);
 //   * scaled q and kᵀ and e^{b_64}, elementwise, straight into their workspace fragments;
-//   * A in 32 x 32 tiles (GLA paper, §4.2, secondary chunking): with m the decay at the start of a token
-//     half, A_ts = Σ_n (q_tn e^{b_tn − m_n}) (k_sn e^{m_n − b_sn}).  The block below the diagonal (queries in
-//     the second half, keys in the first) takes m = b_31, where both factors are ≤ 1; the two diagonal
-//     blocks take m at their half's start, where the key factor is ≤ e^{span of the half}: one wave and
-//     48 MFMAs (bf16 hi + lo factors) per tile.  A half whose span exceeds kSpanMax for some key is
-//     recomputed exactly, Σ_n q_tn k_sn e^{b_tn − b_sn} term by term.
+//   * the pass's keys' share of A in 32 x 32 tiles (GLA paper, §4.2, secondary chunking): with m the decay at
+//     the start of a token half, A_ts = Σ_n (q_tn e^{b_tn − m_n}) (k_sn e^{m_n − b_sn}).  The block below the
+//     diagonal (queries in the second half, keys in the first) takes m = b_31, where both factors are ≤ 1;
+//     the two diagonal blocks take m at their half's start, where the key factor is ≤ e^{span of the half}:
+//     one wave and 24 MFMAs (bf16 hi + lo factors) per tile and pass, accumulated across the passes.  For a
+//     diagonal block whose half spans more than kSpanMax for some key of the pass, that pass's terms are
+//     taken exactly instead, Σ_n q_tn k_sn e^{b_tn − b_sn} term by term (A is a sum over keys, so each pass
+//     may take either form).
 template <int N>
 __global__ __launch_bounds__(512) void gla_prep_kernel(GlaChunkParams p) {
   constexpr int kT = 512;
+  constexpr int KP = 128;        // keys per pass
+  constexpr int NP = N / KP;     // passes
+  static_assert(N % KP == 0, "whole passes");
   using W = ChunkWs<N>;
-  constexpr int kQR = N + 8;   // LDS row strides (padded so that 16 consecutive rows hit distinct banks)
-  constexpr int kBR = N + 4;
+  constexpr int kQR = KP + 8;    // LDS row strides (padded so that 16 consecutive rows hit distinct banks)
+  constexpr int kBR = KP + 4;
   constexpr int kAR = 33;
   __shared__ __attribute__((aligned(16))) uint16_t sQ[kCQ * kQR];
   __shared__ __attribute__((aligned(16))) uint16_t sK[kCQ * kQR];
   __shared__ __attribute__((aligned(16))) float sB[kCQ * kBR];
   __shared__ float sA[3][32 * kAR];   // A tiles (0,0), (1,0), (1,1) as [query][key token]
-  __shared__ int sWide[2];            // half h spans more than kSpanMax for some key
+  __shared__ int sWide[2];            // half h spans more than kSpanMax for some key of the pass
   const int slot = static_cast<int>(blockIdx.x) / p.heads, h = static_cast<int>(blockIdx.x) - slot * p.heads;
   int s;
   if (p.cu) {
@@ -463,135 +470,163 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(GlaChunkParams p) {
   const int64_t e0 = (cs.t0 + static_cast<int64_t>(c) * kCQ) * p.heads * N + static_cast<int64_t>(h) * N;
   const int64_t bytes = static_cast<int64_t>(nv - 1) * rowb + N * 2;   // rows past the chunk's tokens read 0
   const rsrc_t rq = rsrc_bytes(p.q + e0, bytes), rk = rsrc_bytes(p.k + e0, bytes), rg = rsrc_bytes(p.gk + e0, bytes);
-  if (tid < 2) sWide[tid] = 0;
-  // q, k and gk rows (gk widened to fp32 in place of b)
-#pragma unroll 2
-  for (int i = tid; i < kCQ * N / 8; i += kT) {
-    const int t = i / (N / 8), c8 = i - t * (N / 8);
-    const uint32_t off = static_cast<uint32_t>(t) * rowb + 16u * c8;
-    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-    const auto b = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-    const auto g = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0);
-    *reinterpret_cast<uint4*>(&sQ[t * kQR + 8 * c8]) = make_uint4(a[0], a[1], a[2], a[3]);
-    *reinterpret_cast<uint4*>(&sK[t * kQR + 8 * c8]) = make_uint4(b[0], b[1], b[2], b[3]);
-    float* gb = &sB[t * kBR + 8 * c8];
-    *reinterpret_cast<float4*>(gb) = make_float4(__uint_as_float(g[0] << 16), __uint_as_float(g[0] & 0xffff0000u),
-                                                 __uint_as_float(g[1] << 16), __uint_as_float(g[1] & 0xffff0000u));
-    *reinterpret_cast<float4*>(gb + 4) = make_float4(__uint_as_float(g[2] << 16), __uint_as_float(g[2] & 0xffff0000u),
-                                                     __uint_as_float(g[3] << 16), __uint_as_float(g[3] & 0xffff0000u));
-  }
-  __syncthreads();
-  // inclusive cumulative sum over the tokens, in place: two threads per key (tokens 0..31 and 32..63), then the
-  // second adds the first's total
-  const int cn = tid % N, ch = tid / N;
-  if (tid < 2 * N) {
-    float acc = 0.f;
-#pragma unroll 8
-    for (int t = 32 * ch; t < 32 * ch + 32; ++t) {
-      acc += sB[t * kBR + cn];
-      sB[t * kBR + cn] = acc;
-    }
-  }
-  __syncthreads();
-  if (tid < 2 * N && ch == 1) {
-    const float b31 = sB[31 * kBR + cn];
-#pragma unroll 8
-    for (int t = 32; t < kCQ; ++t) sB[t * kBR + cn] += b31;
-  }
-  __syncthreads();
   unsigned char* ws = p.ws + (static_cast<int64_t>(slot) * p.heads + h) * W::kBytes;
-  for (int n = tid; n < N; n += kT) {
-    const float b31 = sB[31 * kBR + n], b63 = sB[(kCQ - 1) * kBR + n];
-    reinterpret_cast<float*>(ws + W::kG)[n] = __builtin_amdgcn_exp2f(b63 * kLog2e);
-    if (-b31 > kSpanMax) sWide[0] = 1;
-    if (b31 - b63 > kSpanMax) sWide[1] = 1;
-  }
-  // q ⊙ e^{b_t} at contraction positions: 8 positions per item
-  for (int i = tid; i < kCQ * N / 8; i += kT) {
-    const int t = i / (N / 8), p8 = i - t * (N / 8);
-    uint16_t hv[8], lv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = (p8 & ~1) * 8 + swap23(8 * (p8 & 1) + j);
-      hilo(bf16f(sQ[t * kQR + n]) * __builtin_amdgcn_exp2f(sB[t * kBR + n] * kLog2e), hv[j], lv[j]);
-    }
-    const int ln = 16 * (32 * (p8 & 1) + (t & 31));
-    *reinterpret_cast<uint4*>(ws + W::qs(t >> 5, p8 >> 2, (p8 >> 1) & 1, 0) + ln) = pack8(hv);
-    *reinterpret_cast<uint4*>(ws + W::qs(t >> 5, p8 >> 2, (p8 >> 1) & 1, 1) + ln) = pack8(lv);
-  }
-  // (k ⊙ e^{b_64 − b_s})ᵀ: 8 tokens of one key per item
-  for (int i = tid; i < N * kCQ / 8; i += kT) {
-    const int n = i % N, tb = i / N;
-    const float be = sB[(kCQ - 1) * kBR + n];
-    uint16_t hv[8], lv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = 8 * tb + j;
-      hilo(bf16f(sK[t * kQR + n]) * __builtin_amdgcn_exp2f((be - sB[t * kBR + n]) * kLog2e), hv[j], lv[j]);
-    }
-    const int ln = 16 * (32 * (tb & 1) + (n & 31));
-    *reinterpret_cast<uint4*>(ws + W::kt(n >> 5, tb >> 1, 0) + ln) = pack8(hv);
-    *reinterpret_cast<uint4*>(ws + W::kt(n >> 5, tb >> 1, 1) + ln) = pack8(lv);
-  }
   // A tiles on the matrix cores: wave 0 → (0,0) with m = 0, wave 1 → (1,0) and wave 2 → (1,1) with m = b_31
-  if (wave < 3) {
-    const int tt = wave == 0 ? 0 : 1, sb = wave == 2 ? 1 : 0;
-    const bool ref31 = wave != 0;
-    const int tq = 32 * tt + l32, tk = 32 * sb + l32;
-    f32x16_t acc = f32x16_t{};
-    for (int kk = 0; kk < N / 16; ++kk) {
-      const int n0 = 16 * kk + 8 * hl;
-      bf16x8_t ah, al, bh, bl;
+  const int tt = wave == 0 ? 0 : 1, sb = wave == 2 ? 1 : 0;
+  const bool ref31 = wave != 0;
+  const int diag = wave == 0 ? 0 : 1;   // the half of a diagonal tile (waves 0 and 2)
+  const int tq = 32 * tt + l32, tk = 32 * sb + l32;
+  f32x16_t acc = f32x16_t{};
+  float ex[2][2] = {{0.f, 0.f}, {0.f, 0.f}};   // exact diagonal terms of wide passes: [half][item]
+  bool wide_any[2] = {false, false};
+  for (int ps = 0; ps < NP; ++ps) {
+    const int nb = KP * ps;   // first key of the pass
+    if (ps > 0) __syncthreads();   // the previous pass is done with LDS
+    if (tid < 2) sWide[tid] = 0;
+    // q, k and gk rows (gk widened to fp32 in place of b)
+#pragma unroll 2
+    for (int i = tid; i < kCQ * KP / 8; i += kT) {
+      const int t = i / (KP / 8), c8 = i - t * (KP / 8);
+      const uint32_t off = static_cast<uint32_t>(t) * rowb + 2u * nb + 16u * c8;
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
+      const auto g = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0);
+      *reinterpret_cast<uint4*>(&sQ[t * kQR + 8 * c8]) = make_uint4(a[0], a[1], a[2], a[3]);
+      *reinterpret_cast<uint4*>(&sK[t * kQR + 8 * c8]) = make_uint4(b[0], b[1], b[2], b[3]);
+      float* gb = &sB[t * kBR + 8 * c8];
+      *reinterpret_cast<float4*>(gb) = make_float4(__uint_as_float(g[0] << 16), __uint_as_float(g[0] & 0xffff0000u),
+                                                   __uint_as_float(g[1] << 16), __uint_as_float(g[1] & 0xffff0000u));
+      *reinterpret_cast<float4*>(gb + 4) = make_float4(__uint_as_float(g[2] << 16), __uint_as_float(g[2] & 0xffff0000u),
+                                                       __uint_as_float(g[3] << 16), __uint_as_float(g[3] & 0xffff0000u));
+    }
+    __syncthreads();
+    // inclusive cumulative sum over the tokens, in place: two threads per key (tokens 0..31 and 32..63), then
+    // the second adds the first's total
+    const int cn = tid % KP, ch = tid / KP;
+    if (tid < 2 * KP) {
+      float run = 0.f;
+#pragma unroll 8
+      for (int t = 32 * ch; t < 32 * ch + 32; ++t) {
+        run += sB[t * kBR + cn];
+        sB[t * kBR + cn] = run;
+      }
+    }
+    __syncthreads();
+    if (tid < 2 * KP && ch == 1) {
+      const float b31 = sB[31 * kBR + cn];
+#pragma unroll 8
+      for (int t = 32; t < kCQ; ++t) sB[t * kBR + cn] += b31;
+    }
+    __syncthreads();
+    for (int n = tid; n < KP; n += kT) {
+      const float b31 = sB[31 * kBR + n], b63 = sB[(kCQ - 1) * kBR + n];
+      reinterpret_cast<float*>(ws + W::kG)[nb + n] = __builtin_amdgcn_exp2f(b63 * kLog2e);
+      if (-b31 > kSpanMax) sWide[0] = 1;
+      if (b31 - b63 > kSpanMax) sWide[1] = 1;
+    }
+    // q ⊙ e^{b_t} at contraction positions: 8 positions per item
+    for (int i = tid; i < kCQ * KP / 8; i += kT) {
+      const int t = i / (KP / 8), p8 = i - t * (KP / 8);
+      const int pg = p8 + nb / 8;   // position group among all N keys
+      uint16_t hv[8], lv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int n = n0 + j;
-        const float m = ref31 ? sB[31 * kBR + n] : 0.f;
-        const float x = bf16f(sQ[tq * kQR + n]) * __builtin_amdgcn_exp2f((sB[tq * kBR + n] - m) * kLog2e);
-        const float y = bf16f(sK[tk * kQR + n]) * __builtin_amdgcn_exp2f((m - sB[tk * kBR + n]) * kLog2e);
-        const __bf16 xh = static_cast<__bf16>(x), yh = static_cast<__bf16>(y);
-        ah[j] = xh; al[j] = static_cast<__bf16>(x - static_cast<float>(xh));
-        bh[j] = yh; bl[j] = static_cast<__bf16>(y - static_cast<float>(yh));
+        const int n = (p8 & ~1) * 8 + swap23(8 * (p8 & 1) + j);
+        hilo(bf16f(sQ[t * kQR + n]) * __builtin_amdgcn_exp2f(sB[t * kBR + n] * kLog2e), hv[j], lv[j]);
       }
-      acc = mfma(ah, bh, acc);
-      acc = mfma(ah, bl, acc);
-      acc = mfma(al, bh, acc);
+      const int ln = 16 * (32 * (p8 & 1) + (t & 31));
+      *reinterpret_cast<uint4*>(ws + W::qs(t >> 5, pg >> 2, (pg >> 1) & 1, 0) + ln) = pack8(hv);
+      *reinterpret_cast<uint4*>(ws + W::qs(t >> 5, pg >> 2, (pg >> 1) & 1, 1) + ln) = pack8(lv);
     }
+    // (k ⊙ e^{b_64 − b_s})ᵀ: 8 tokens of one key per item
+    for (int i = tid; i < KP * kCQ / 8; i += kT) {
+      const int n = i % KP, tb = i / KP;
+      const int ng = nb + n;
+      const float be = sB[(kCQ - 1) * kBR + n];
+      uint16_t hv[8], lv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = 8 * tb + j;
+        hilo(bf16f(sK[t * kQR + n]) * __builtin_amdgcn_exp2f((be - sB[t * kBR + n]) * kLog2e), hv[j], lv[j]);
+      }
+      const int ln = 16 * (32 * (tb & 1) + (ng & 31));
+      *reinterpret_cast<uint4*>(ws + W::kt(ng >> 5, tb >> 1, 0) + ln) = pack8(hv);
+      *reinterpret_cast<uint4*>(ws + W::kt(ng >> 5, tb >> 1, 1) + ln) = pack8(lv);
+    }
+    __syncthreads();   // the pass's span flags
+    const bool w0 = sWide[0] != 0, w1 = sWide[1] != 0;   // (block-uniform)
+    wide_any[0] = wide_any[0] || w0;
+    wide_any[1] = wide_any[1] || w1;
+    if (wave < 3 && !(wave != 1 && (diag == 0 ? w0 : w1))) {
+      for (int kk = 0; kk < KP / 16; ++kk) {
+        const int n0 = 16 * kk + 8 * hl;
+        bf16x8_t ah, al, bh, bl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int n = n0 + j;
+          const float m = ref31 ? sB[31 * kBR + n] : 0.f;
+          const float x = bf16f(sQ[tq * kQR + n]) * __builtin_amdgcn_exp2f((sB[tq * kBR + n] - m) * kLog2e);
+          const float y = bf16f(sK[tk * kQR + n]) * __builtin_amdgcn_exp2f((m - sB[tk * kBR + n]) * kLog2e);
+          const __bf16 xh = static_cast<__bf16>(x), yh = static_cast<__bf16>(y);
+          ah[j] = xh; al[j] = static_cast<__bf16>(x - static_cast<float>(xh));
+          bh[j] = yh; bl[j] = static_cast<__bf16>(y - static_cast<float>(yh));
+        }
+        acc = mfma(ah, bh, acc);
+        acc = mfma(ah, bl, acc);
+        acc = mfma(al, bh, acc);
+      }
+    }
+    // a diagonal tile whose half spans too much in this pass: its exact terms
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      if (!(hf == 0 ? w0 : w1)) continue;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = tid + kT * r;
+        const int tl = i >> 5, sl = i & 31;
+        if (sl > tl) continue;
+        const int t = 32 * hf + tl, sj = 32 * hf + sl;
+        float a = 0.f;
+        for (int n = 0; n < KP; ++n)
+          a = fmaf(bf16f(sQ[t * kQR + n]) * bf16f(sK[sj * kQR + n]),
+                   __builtin_amdgcn_exp2f((sB[t * kBR + n] - sB[sj * kBR + n]) * kLog2e), a);
+        ex[hf][r] += a;
+      }
+    }
+  }
+  if (wave < 3) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) sA[wave][(8 * (e >> 2) + 4 * hl + (e & 3)) * kAR + l32] = acc[e];
   }
   __syncthreads();
-  // a diagonal tile whose half spans too much: exact terms (tile 0 for half 0, tile 2 for half 1)
+  // add the exact terms of the wide passes (each item belongs to one thread)
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    if (!sWide[hf]) continue;   // (block-uniform)
-    for (int i = tid; i < 32 * 32; i += kT) {
+    if (!wide_any[hf]) continue;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = tid + kT * r;
       const int tl = i >> 5, sl = i & 31;
-      if (sl > tl) continue;
-      const int t = 32 * hf + tl, sj = 32 * hf + sl;
-      float a = 0.f;
-      for (int n = 0; n < N; ++n)
-        a = fmaf(bf16f(sQ[t * kQR + n]) * bf16f(sK[sj * kQR + n]),
-                 __builtin_amdgcn_exp2f((sB[t * kBR + n] - sB[sj * kBR + n]) * kLog2e), a);
-      sA[2 * hf][tl * kAR + sl] = a;
+      if (sl <= tl) sA[2 * hf][tl * kAR + sl] += ex[hf][r];
     }
   }
   __syncthreads();
   // A fragments: item (tt, kk, lane) holds row 32 tt + l % 32, key tokens 16 kk + 8 (l / 32) + 0..7
   for (int i = tid; i < 2 * 4 * 64; i += kT) {
-    const int ln = i & 63, kk = (i >> 6) & 3, tt = i >> 8;
+    const int ln = i & 63, kk = (i >> 6) & 3, ft = i >> 8;
     const int tl = ln & 31, s0 = 16 * kk + 8 * (ln >> 5);
-    const int sb = s0 >> 5;
+    const int fb = s0 >> 5;
     uint16_t hv[8], lv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int sl = (s0 & 31) + j;
       float a = 0.f;
-      if (tt == 1 && sb == 0) a = sA[1][tl * kAR + sl];
-      else if (tt == sb && sl <= tl) a = sA[2 * tt][tl * kAR + sl];
+      if (ft == 1 && fb == 0) a = sA[1][tl * kAR + sl];
+      else if (ft == fb && sl <= tl) a = sA[2 * ft][tl * kAR + sl];
       hilo(a, hv[j], lv[j]);
     }
-    *reinterpret_cast<uint4*>(ws + W::am(tt, kk, 0) + 16 * ln) = pack8(hv);
-    *reinterpret_cast<uint4*>(ws + W::am(tt, kk, 1) + 16 * ln) = pack8(lv);
+    *reinterpret_cast<uint4*>(ws + W::am(ft, kk, 0) + 16 * ln) = pack8(hv);
+    *reinterpret_cast<uint4*>(ws + W::am(ft, kk, 1) + 16 * ln) = pack8(lv);
   }
 }
 

@@ -59,8 +59,8 @@ def run_case(lengths, H, N, P, din, dout, with_h0, cfg=10, gk_scale=1.0):
     T = sum(lengths)
     nseq = len(lengths)
     inp = I.make_gla_inputs_np(cfg, T, H, N, P, in_dtype=din)
-    if gk_scale != 1.0:
-        g = (inp["gk_f32"] * gk_scale).astype(np.float32)
+    if not np.all(np.asarray(gk_scale) == 1.0):
+        g = (inp["gk_f32"] * np.asarray(gk_scale, dtype=np.float32)).astype(np.float32)
         inp["gk"] = I.bf16_bits_from_f32(g) if din == "bf16" else g
         inp["gk_f32"] = I.f32_from_bf16_bits(inp["gk"]) if din == "bf16" else g
     h0 = (0.5 * np.random.default_rng(cfg).standard_normal((nseq, H, P, N))).astype(np.float32) if with_h0 else None
@@ -94,7 +94,7 @@ def test_gla_matches_oracle(lengths, H, N, P, din, dout, with_h0):
     check(*run_case(lengths, H, N, P, din, dout, with_h0), dout)
 
 
-@pytest.mark.parametrize("N,P,scale", [(64, 16, 16.0), (256, 32, 16.0), (128, 32, 120.0)])
+@pytest.mark.parametrize("N,P,scale", [(64, 16, 16.0), (256, 32, 16.0), (128, 32, 120.0), (256, 32, 120.0)])
 def test_gla_strong_decay(N, P, scale):
     """Gates 16x the recipe's (decays down to ~e^-3 per token): the state forgets within a few tokens, and in
     the chunked form the decay across a 64-token chunk spans tens of e-folds.  At 120x a 32-token half spans
@@ -102,6 +102,17 @@ def test_gla_strong_decay(N, P, scale):
     blocks take the exact term-by-term form."""
     say("case: gla strong decay N%d P%d x%g" % (N, P, scale))
     o, oo, hl, ho, b = run_case((150,), 2, N, P, "bf16", "f32", True, gk_scale=scale)
+    check(o, oo, hl, ho, b, "f32")
+
+
+@pytest.mark.parametrize("wide", ["first", "second"])
+def test_gla_strong_decay_in_one_key_pass(wide):
+    """Keys 256 in the chunked form go through in two passes of 128; gates 120x the recipe's on one pass's keys
+    only, so that pass takes the exact form of the diagonal blocks of A and the other the factored one."""
+    say("case: gla strong decay on the %s 128 keys" % wide)
+    scale = np.ones(256, dtype=np.float32)
+    scale[slice(0, 128) if wide == "first" else slice(128, 256)] = 120.0
+    o, oo, hl, ho, b = run_case((150,), 2, 256, 32, "bf16", "f32", True, gk_scale=scale)
     check(o, oo, hl, ho, b, "f32")
 
 
