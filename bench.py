@@ -577,11 +577,12 @@ def cpu_baseline_groups(seqs: int = 1, channels: int = 512):
                                         "oracle, %.1f s" % (channels, channels // G, spent)}
 
 
-def ssd_bytes(batch: int, L: int, heads: int, hd: int, ngroups: int, n: int) -> int:
-    """Algorithmic bytes of one SSD prefill: x, z read and y written (bf16), dt (bf16), B and C (bf16),
-    A, D, dt_bias, h_last out (fp32)."""
+def ssd_bytes(batch: int, L: int, heads: int, hd: int, ngroups: int, n: int, gated: bool = True) -> int:
+    """Algorithmic bytes of one SSD prefill: x (and z when gated) read and y written (bf16), dt (bf16), B and C
+    (bf16), A, D, dt_bias, h_last out (fp32)."""
     T = batch * L
-    return T * heads * hd * 2 * 3 + T * heads * 2 + T * ngroups * n * 2 * 2 + heads * 12 + batch * heads * hd * n * 4
+    return (T * heads * hd * 2 * (3 if gated else 2) + T * heads * 2 + T * ngroups * n * 2 * 2 + heads * 12 +
+            batch * heads * hd * n * 4)
 
 
 def ssd_flops(batch: int, L: int, heads: int, hd: int, n: int, q: int = 64) -> int:
@@ -633,6 +634,55 @@ def bench_ssd(steps: int = 20, warmup: int = 5):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_ssd_traffic(),
                          "kernel": "ssd_cb_kernel<%d> + ssd_fwd_kernel<bf16,N=%d,gate> (one call)" % (N, N),
+                         "launch_us": round(ms * 1e3, 2),
+                         "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops}}
+
+
+def bench_retention(steps: int = 20, warmup: int = 5):
+    """Multi-scale retention through samba_ssd_fwd: B4 L4096, 32 heads of 64 values with 128 keys each (one
+    (k, q) group per head: B = k, C = q, x = v), Δ = 1, A = ln γ_h, no skip, no gate, bf16 I/O."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import ssd as SD
+
+    wl = I.WORKLOADS[11]
+    Bt, L, H, P, N, G = (wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.dstate,
+                         wl.extra["ngroups"])
+    dev = torch.device("cuda:0")
+    t = I.make_ssd_inputs_torch(11, Bt * L, H, G, N, dev)
+    rp = {k: torch.from_numpy(v).to(dev) for k, v in I.make_retention_params(H).items()}
+    x = t["x"].view(Bt, L, H, P)
+    dt = torch.zeros(Bt, L, H, dtype=torch.bfloat16, device=dev)
+    B, C = (t[k].view(Bt, L, G, N) for k in ("B", "C"))
+    y = torch.empty_like(x)
+    hl = torch.empty(Bt, H, P, N, dtype=torch.float32, device=dev)
+    a = SD.fwd_args(x, dt, B, C, rp["A"], rp["D"], rp["dt_bias"], y=y, h_last=hl)
+    ws = SD.attach_workspace(a, dev)
+    lib = SD.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    ref = ctypes.byref(a)
+
+    def call():
+        if lib.samba_ssd_fwd(ref, sh) != 0:
+            raise RuntimeError("samba_ssd_fwd failed")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = _timed(call, steps, stream)
+    del ws
+    nbytes = ssd_bytes(Bt, L, H, P, G, N, gated=False)
+    flops = ssd_flops(Bt, L, H, P, N)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": "multi-scale retention B=%d L=%d, %d heads of %d values and %d keys (one (k, q) group per "
+                        "head), no gate, bf16 I/O, fp32 state" % (Bt, L, H, P, N),
+            "steps": steps, "ms_per_call": ms, "tokens_per_s": Bt * L / (ms * 1e-3), "gbs": gbs,
+            "mfma_tflops": round(tf, 1), "mfma_frac_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "ssd_cb_kernel<%d> + ssd_fwd_kernel<bf16,N=%d,no gate> (one call)" % (N, N),
                          "launch_us": round(ms * 1e3, 2),
                          "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops}}
 
@@ -1350,6 +1400,7 @@ def main():
         line["groups_decode"] = bench_groups_step()
     if not args.no_ssd:
         line["ssd"] = bench_ssd(args.ssd_steps)
+        line["retention"] = bench_retention(args.ssd_steps)
     if not args.no_gla:
         line["gla"] = bench_gla(args.gla_steps)
     if not args.no_swa:

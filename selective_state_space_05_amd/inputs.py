@@ -120,6 +120,11 @@ WORKLOADS = {
     # key size 256 (half the width over 4 heads), value size 512
     10: Workload(10, "gla_fwd B4 L4096 H4 K256 V512 bf16", 4, 4096, 2048, dstate=256,
                  extra={"heads": 4, "head_dim": 512}),
+    # multi-scale retention through the state-space duality entry point on the training shape: width 2048
+    # as 32 heads of 64 values, 128 keys per head (one (k, q) group per head), Δ = 1, A = ln γ_h, no skip
+    # and no gate (make_retention_params)
+    11: Workload(11, "retention B4 L4096 H32 P64 N128 G32 bf16", 4, 4096, 2048, dstate=128,
+                 extra={"heads": 32, "head_dim": 64, "ngroups": 32}),
 }
 
 
@@ -368,6 +373,14 @@ def make_ssd_params(cfg_id: int, heads: int) -> dict:
     A = (-np.exp(_rng(cfg_id, TENSOR_IDS["A"]).uniform(0.0, math.log(16.0), size=heads))).astype(np.float32)
     D = _rng(cfg_id, TENSOR_IDS["D"]).uniform(0.0, 1.0, size=heads).astype(np.float32)
     return {"A": A, "D": D, "dt_bias": dt_bias}
+
+
+def make_retention_params(heads: int) -> dict:
+    """Multi-scale retention as the duality form's parameters: decay γ_h = 1 - 2^(-5-h) per head (A = ln γ_h),
+    Δ = 1 (dt = 0 with dt_bias = ln(e - 1), whose softplus is 1), no skip (D = 0)."""
+    gam = 1.0 - 2.0 ** (-5.0 - np.arange(heads, dtype=np.float64))
+    return {"A": np.log(gam).astype(np.float32), "D": np.zeros(heads, dtype=np.float32),
+            "dt_bias": np.full(heads, math.log(math.e - 1.0), dtype=np.float32)}
 
 
 def _ssd_shapes(rows, heads, head_dim, ngroups, dstate):

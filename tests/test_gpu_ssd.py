@@ -153,6 +153,29 @@ def test_ssd_full_shape_sampled():
     say("  ok")
 
 
+def test_retention_full_shape_sampled():
+    """Multi-scale retention at the benchmark's launch (B4 L4096, 32 heads of 64 values, 128 keys per head, one
+    (k, q) group per head, no gate, bf16 y): two heads of two sequences against the oracle."""
+    wl = I.WORKLOADS[11]
+    Bt, L, H, P, N, G = (wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.dstate,
+                         wl.extra["ngroups"])
+    say("case: retention full shape B%d L%d H%d N%d G%d" % (Bt, L, H, N, G))
+    t = I.make_ssd_inputs_torch(11, Bt * L, H, G, N, DEV)
+    rp = I.make_retention_params(H)
+    x = t["x"].view(Bt, L, H, P)
+    dt = torch.zeros(Bt, L, H, dtype=torch.bfloat16, device=DEV)
+    B, C = (t[k].view(Bt, L, G, N) for k in ("B", "C"))
+    y, hl = S.ssd_fwd(x, dt, B, C, *(torch.from_numpy(rp[k]).to(DEV) for k in ("A", "D", "dt_bias")))
+    torch.cuda.synchronize()
+    for s, h in ((0, 0), (3, 31)):
+        hs = slice(h, h + 1)
+        yo, ho = O.ssd(host(x[s, :, hs]), np.zeros((L, 1)), host(B[s, :, hs]), host(C[s, :, hs]), rp["A"][hs],
+                       rp["D"][hs], rp["dt_bias"][hs])
+        check_bf16_y(host(y[s, :, h]), yo[:, 0], "y s%d h%d" % (s, h))
+        check_fp32(host(hl[s, h]), ho[0, 0], "h_last s%d h%d" % (s, h))
+    say("  ok")
+
+
 def test_retention_configuration():
     """Multi-scale retention through the same entry point: dt = 0 with bias ln(e - 1) (Δ = 1), A = ln γ_h with
     γ_h = 1 - 2^(-5-h), one (k, q) group per head (B = k, C = q), x = v, no skip, no gate; against the oracle
