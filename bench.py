@@ -1071,7 +1071,7 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
         wl = I.WORKLOADS[9]
         Bt, L, H, P, N, G = (wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.dstate,
                              wl.extra["ngroups"])
-        sel = {"ssd": ("ssd_fwd_kernel<unsigned short, 128, true>", ssd_bytes(Bt, L, H, P, G, N))}
+        sel = {"ssd": ("ssd_fwd_kernel<unsigned short, 128, true, false>", ssd_bytes(Bt, L, H, P, G, N))}
         src_hash, run, flag = ssd_hash(), SSD_PMC_RUN, "--pmc-summary-ssd"
         note = ("Algorithmic bytes: x, z read and y written once (bf16), dt, B and C once, parameters, h_last "
                 "out. The workspace of C B^T tiles (3 MiB, written by the small pre-pass kernel and read from L2) "
@@ -1282,6 +1282,8 @@ def main():
     ap.add_argument("--no-ssd", action="store_true", help="skip the state-space duality leg")
     ap.add_argument("--ssd-steps", type=int, default=20)
     ap.add_argument("--ssd-only", action="store_true", help="run only the state-space duality leg")
+    ap.add_argument("--retention-only", action="store_true",
+                    help="run only the multi-scale retention leg (the duality entry point)")
     ap.add_argument("--no-gla", action="store_true", help="skip the gated linear attention leg")
     ap.add_argument("--gla-steps", type=int, default=5)
     ap.add_argument("--gla-only", action="store_true", help="run only the gated linear attention leg")
@@ -1332,6 +1334,9 @@ def main():
         if args.copy_probe:
             copy_probe()
         print(json.dumps(out), flush=True)
+        return
+    if args.retention_only:
+        print(json.dumps({"retention": bench_retention(args.ssd_steps, min(args.warmup, 5))}), flush=True)
         return
     if args.ssd_only:
         out = {"ssd": bench_ssd(args.ssd_steps, min(args.warmup, 5))}

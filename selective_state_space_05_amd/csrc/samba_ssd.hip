@@ -38,6 +38,7 @@
 
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "samba_ssd.h"
@@ -578,13 +579,29 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
   }
 }
 
-template <typename Tout, int N, bool kGate>
+// A state wave of the value tile that its workgroup leaves to the other one (kSplit): it only takes part in
+// the barriers, as many as a computing state wave does.
+__device__ __forceinline__ void idle_state_wave(const Ctx& cx) {
+  const int npad = ((cx.len + kQ - 1) / kQ + 1) & ~1;
+  __syncthreads();   // chunk 0 staged
+  for (int c = 0; c < npad; ++c) {
+    __syncthreads();   // X1
+    __syncthreads();   // X2
+  }
+}
+
+// kSplit: the head's two 32-column value tiles go to two workgroups (when one workgroup per (sequence, head)
+// would leave at least half of the CUs idle); both stage the chunk and build M, and each runs the state
+// waves of its own tile.
+template <typename Tout, int N, bool kGate, bool kSplit>
 __global__ __launch_bounds__(kThreads, 1) void ssd_fwd_kernel(SsdParams p) {
   __shared__ __attribute__((aligned(16))) Smem<N> sm;
   const int nblk = static_cast<int>(gridDim.x);
   const int logical = xcd_remap(static_cast<int>(blockIdx.x), nblk);
-  const int s = logical / p.heads;
-  const int h = logical - s * p.heads;
+  const int sh = kSplit ? (logical >> 1) : logical;   // (the two halves of a head are neighbours: same XCD)
+  const int pa = kSplit ? (logical & 1) : 0;
+  const int s = sh / p.heads;
+  const int h = sh - s * p.heads;
   const SeqInfo si = seq_info(p, s);
   const int H = p.heads;
   const int G = p.ngroups;
@@ -614,6 +631,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_fwd_kernel(SsdParams p) {
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   if (wave >= 4) helper_wave<N>(cx, sm);
+  else if (kSplit && (wave & 1) != pa) idle_state_wave(cx);
   else if (wave >= 2) state_wave<Tout, N, 1, kGate>(cx, sm, p.h0, p.h_last);
   else state_wave<Tout, N, 0, kGate>(cx, sm, p.h0, p.h_last);
 }
@@ -626,13 +644,39 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 template <typename Tout, int N>
-hipError_t launch_ssd(const SsdParams& p, bool gate, int64_t nslots, int64_t nblocks, hipStream_t s) {
+hipError_t launch_ssd(const SsdParams& p, bool gate, bool split, int64_t nslots, int64_t nblocks, hipStream_t s) {
   if (nslots > 0)
     hipLaunchKernelGGL((ssd_cb_kernel<N>), dim3(static_cast<uint32_t>(nslots * p.ngroups)), dim3(192), 0, s, p);
-  const dim3 grid(static_cast<uint32_t>(nblocks)), block(kThreads);
-  if (gate) hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, false>), grid, block, 0, s, p);
+  const dim3 grid(static_cast<uint32_t>(split ? 2 * nblocks : nblocks)), block(kThreads);
+  if (gate) {
+    if (split) hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, true, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, true, false>), grid, block, 0, s, p);
+  } else {
+    if (split) hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, false, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, false, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
+}
+
+// compute units of the current device (256 when the runtime cannot tell)
+int ssd_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // sequences, chunk slots and workspace bytes of a validated call
@@ -727,12 +771,16 @@ extern "C" samba_status samba_ssd_fwd(const samba_ssd_args* a, void* stream) {
   const bool gate = a->z != nullptr;
   const int64_t nblocks = pl.nseq * a->heads;
   const int64_t nslots = tokens > 0 ? pl.nslots : 0;
+  // value columns over two workgroups per head when that still fits the CUs in one round
+  const bool split = nblocks > 0 && 2 * nblocks <= ssd_cu_count();
   hipError_t e;
   // (no tokens: no chunk, no workspace read; every sequence's h_last is its h0, or zero)
   if (a->y_dtype == SAMBA_BF16) {
-    e = N == 64 ? launch_ssd<uint16_t, 64>(p, gate, nslots, nblocks, s) : launch_ssd<uint16_t, 128>(p, gate, nslots, nblocks, s);
+    e = N == 64 ? launch_ssd<uint16_t, 64>(p, gate, split, nslots, nblocks, s)
+                : launch_ssd<uint16_t, 128>(p, gate, split, nslots, nblocks, s);
   } else {
-    e = N == 64 ? launch_ssd<float, 64>(p, gate, nslots, nblocks, s) : launch_ssd<float, 128>(p, gate, nslots, nblocks, s);
+    e = N == 64 ? launch_ssd<float, 64>(p, gate, split, nslots, nblocks, s)
+                : launch_ssd<float, 128>(p, gate, split, nslots, nblocks, s);
   }
   return e == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
 }
