@@ -996,17 +996,22 @@ __global__ __launch_bounds__(256) void scan_bwd_finish_kernel(const float* dbc, 
                                                               float* dA, float* dD, float* dbias, int64_t total_tokens,
                                                               int32_t ntiles, int32_t nseq, int32_t dim) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t n1 = total_tokens * 32;
-  if (idx < n1) {
-    float acc = 0.f;
-    for (int t = 0; t < ntiles; ++t) acc += dbc[static_cast<int64_t>(t) * n1 + idx];
-    const int64_t row = idx >> 5;
-    const int o = static_cast<int>(idx & 31);
-    if (o < 16) dB[row * 16 + o] = acc;
-    else dC[row * 16 + (o - 16)] = acc;
+  const int64_t n4 = total_tokens * 8;   // 4 consecutive outputs of one row per thread (16-byte loads)
+  if (idx < n4) {
+    const float4* src = reinterpret_cast<const float4*>(dbc) + idx;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int t = 0; t < ntiles; ++t) {   // (each output still sums its tiles in order 0, 1, ..)
+      const float4 v = src[static_cast<int64_t>(t) * n4];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const int64_t row = idx >> 3;
+    const int o = 4 * static_cast<int>(idx & 7);
+    float4* dst = reinterpret_cast<float4*>((o < 16 ? dB : dC) + row * 16 + (o & 15));
+    *dst = acc;
     return;
   }
-  const int64_t i2 = idx - n1;
+  const int64_t i2 = idx - n4;
   if (i2 >= static_cast<int64_t>(dim) * 18) return;
   const int64_t dd = i2 / 18;
   const int q = static_cast<int>(i2 - dd * 18);
@@ -1778,7 +1783,7 @@ samba_status samba_scan_bwd(const samba_scan_bwd_args* args, void* stream) {
     const hipError_t e = bf ? launch_bwd_kernel<uint16_t>(pl, s) : launch_bwd_kernel<float>(pl, s);
     if (e != hipSuccess) return SAMBA_ERR_HIP;
   }
-  const int64_t nout = pl.tokens * 32 + static_cast<int64_t>(args->dim) * 18;
+  const int64_t nout = pl.tokens * 8 + static_cast<int64_t>(args->dim) * 18;
   const int64_t blocks = (nout + 255) / 256;
   if (blocks > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(scan_bwd_finish_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, pl.prm.dbc,
