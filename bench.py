@@ -1001,9 +1001,6 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
                           "algorithmic_bytes_per_call": bwd_bytes(4 * 4096, 4096, 4)},
              "projections": entry("proj", (16384 * 4096 + 4128 * 4096 + 16384 * 4128) * 2)}
     out_d["backward"]["bytes_per_call"] = sum(v["bytes_per_launch"] for v in out_d["backward"]["kernels"].values())
-    if which == "gla":
-        out_d["gla_call"] = {"bytes_per_call": sum(out_d[k]["bytes_per_launch"] for k in sel),
-                             "algorithmic_bytes_per_call": sum(out_d[k]["algorithmic_bytes_per_launch"] for k in sel)}
     out_d["command"] = [
         f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {PMC_RUN}",
         f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {PMC_RUN}",
