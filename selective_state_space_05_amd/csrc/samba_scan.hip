@@ -366,7 +366,7 @@ __device__ __forceinline__ int64_t ckpt_slot(int64_t start, int s, int j) { retu
 // token of each sequence to p.ckpt (the backward's recomputation points).
 // ---------------------------------------------------------------------------
 template <typename Tin, typename Tout, int W, int TPW, int K, bool kCkpt = false>
-__global__ __launch_bounds__(64 * W * TPW) void scan_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) {   // (4 waves per SIMD: <= 128 VGPRs)
   static_assert(W == 1 || TPW == 1, "time slices and tile packing are exclusive");
   static_assert(K == 8 || K == 16, "slice length");
   constexpr int kWaves = W * TPW;
