@@ -132,6 +132,29 @@ def test_ssd_deterministic():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)) and torch.equal(h1, h2)
 
 
+def test_ssd_split_value_tiles_match_one_workgroup():
+    """A head's two 32-column value tiles go to two workgroups when (sequences x heads) is at most half the CU
+    count: 32 sequences x 4 heads take that path, 33 x 4 the one-workgroup path; the first 32 sequences'
+    outputs and states must agree bit for bit (same arithmetic per tile)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    heads, G, N, L = 4, 2, 128, 130
+    n_split = cus // 2 // heads            # largest batch that still splits
+    say("case: ssd split vs one workgroup: %d and %d sequences x %d heads (%d CUs)" % (n_split, n_split + 1, heads, cus))
+    t = I.make_ssd_inputs_torch(21, (n_split + 1) * L, heads, G, N, DEV)
+    x, z = (t[k].view(n_split + 1, L, heads, 64) for k in ("x", "z"))
+    dt = t["dt"].view(n_split + 1, L, heads)
+    B, C = (t[k].view(n_split + 1, L, G, N) for k in ("B", "C"))
+    par = (t["A"], t["D"], t["dt_bias"])
+    y1, h1 = S.ssd_fwd(x[:n_split], dt[:n_split], B[:n_split], C[:n_split], *par, z=z[:n_split])
+    y2, h2 = S.ssd_fwd(x, dt, B, C, *par, z=z)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2[:n_split].view(torch.int16))
+    assert torch.equal(h1, h2[:n_split])
+    yo, ho = O.ssd(host(x[0]), host(dt[0]), host(B[0]), host(C[0]), *(host(v) for v in par), z=host(z[0]))
+    check_bf16_y(host(y1[0]).reshape(L, -1), yo.reshape(L, -1), "y s0")
+    check_fp32(host(h1[0]), ho[0], "h_last s0")
+
+
 def test_ssd_full_shape_sampled():
     """B4 L4096 H64 P64 N128 G1 (the benchmark's launch): two heads of two sequences against the oracle
     (heads are independent given their group's B and C)."""
