@@ -250,12 +250,11 @@ struct LaneCtx {
   int bc_lds;               // float index of those values in an LDS [K][16] tile
 };
 
-// Issue the loads of the slice starting at token row t0 (all buffer loads).
+// Issue the loads of the slice starting at token row t0 (all buffer loads); rem = tokens of the sequence
+// from t0 on (wave-uniform, 32-bit: a sequence is < 2^31 tokens; 0 or less past its end).
 template <typename Tin, typename Tout, int K>
-__device__ __forceinline__ void load_raw(const FwdParams& p, const LaneCtx<Tin, Tout, K>& L, int64_t t0,
+__device__ __forceinline__ void load_raw(const FwdParams& p, const LaneCtx<Tin, Tout, K>& L, int64_t t0, int rem,
                                          RawSlice<Tin, K>& r) {
-  // tokens left in this sequence (wave-uniform; a sequence is < 2^31 tokens)
-  const int rem = static_cast<int>(L.end - t0 > 0x7fffffff ? 0x7fffffff : (L.end - t0 < 0 ? 0 : L.end - t0));
   const int64_t row0 = t0 * p.dim;
   const uint32_t dim = static_cast<uint32_t>(p.dim);
   const rsrc_t rx = make_rsrc_rows(static_cast<const Tin*>(p.x) + row0, rem, dim);
@@ -452,7 +451,7 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
     auto step = [&](int i0, const RawSlice<Tin, K>& cur, RawSlice<Tin, K>& nxt) {
       const int64_t t0 = L.start + i0;
       const int nv = ntok - i0 < K ? ntok - i0 : K;
-      load_raw<Tin, Tout, K>(p, L, t0 + K, nxt);
+      load_raw<Tin, Tout, K>(p, L, t0 + K, ntok - i0 - K, nxt);
       stage_bc<Tin, Tout, K>(cur, L, sB, sC);
       float xv[K / 4], zv[K / 4], dl[K / 4], uu[K / 4];
       decode_raw<Tin, Tout, K>(cur, L, nv, xv, zv, dl, uu);
@@ -493,7 +492,7 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
       wave_lds_sync();
     };
     RawSlice<Tin, K> ra, rb;
-    load_raw<Tin, Tout, K>(p, L, L.start, ra);
+    load_raw<Tin, Tout, K>(p, L, L.start, ntok, ra);
     for (int i0 = 0; i0 < ntok; i0 += 2 * K) {
       step(i0, ra, rb);
       if (i0 + K < ntok) step(i0 + K, rb, ra);
@@ -516,7 +515,7 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
       const int i0 = my0 + ci * chunk;
       const int64_t t0 = L.start + i0;
       const int nv = ntok - i0 <= 0 ? 0 : (ntok - i0 < K ? ntok - i0 : K);
-      load_raw<Tin, Tout, K>(p, L, t0 + chunk, nxt);  // prefetch this wave's slice of the next chunk
+      load_raw<Tin, Tout, K>(p, L, t0 + chunk, ntok - i0 - chunk, nxt);  // prefetch this wave's slice of the next chunk
       stage_bc<Tin, Tout, K>(cur, L, sB, sC);
       float xv[K / 4], zv[K / 4], dl[K / 4], uu[K / 4];
       decode_raw<Tin, Tout, K>(cur, L, nv, xv, zv, dl, uu);
@@ -612,7 +611,7 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
     };
 
     RawSlice<Tin, K> ra, rb;
-    load_raw<Tin, Tout, K>(p, L, L.start + my0, ra);
+    load_raw<Tin, Tout, K>(p, L, L.start + my0, ntok - my0, ra);
     for (int ci = 0; ci < nchunks; ci += 2) {
       chunk_step(ci, ra, rb);
       if (ci + 1 < nchunks) chunk_step(ci + 1, rb, ra);
