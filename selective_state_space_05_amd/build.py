@@ -1,5 +1,6 @@
 """Builds libsamba_scan.so in-tree with hipcc for gfx950 (the scan and the
-sliding-window attention kernels, one library).
+sliding-window attention kernels, one library), and libsamba_probe.so (the
+ALU issue-rate probes the benchmark measures the prefill's ceiling with).
 
 Usage:  python -m selective_state_space_05_amd.build   (always recompiles)
 """
@@ -17,6 +18,8 @@ SRCS = (PKG / "csrc" / "samba_scan.hip", PKG / "csrc" / "samba_scan_groups.hip",
 HEADERS = (ROOT / "include" / "samba_scan.h", ROOT / "include" / "samba_swa.h", ROOT / "include" / "samba_ssd.h",
            ROOT / "include" / "samba_gla.h")
 LIB = PKG / "libsamba_scan.so"
+PROBE_SRC = PKG / "csrc" / "samba_probe.hip"
+PROBE_LIB = PKG / "libsamba_probe.so"
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -37,14 +40,21 @@ def hipcc() -> str:
     raise FileNotFoundError("hipcc not found")
 
 
-def build(out: Path = LIB, extra=()) -> Path:
-    """Compile the HIP library (kernels + C ABI) into `out`."""
+def _compile(srcs, out: Path, extra=()) -> Path:
     tmp = out.with_suffix(".so.tmp%d" % os.getpid())
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", str(ROOT / "include"), "-o", str(tmp), *(str(p) for p in SRCS)]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", str(ROOT / "include"), "-o", str(tmp), *(str(p) for p in srcs)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
     os.replace(tmp, out)
+    return out
+
+
+def build(out: Path = LIB, extra=(), probe: bool = True) -> Path:
+    """Compile the HIP library (kernels + C ABI) into `out`, and the ALU probe library beside it."""
+    _compile(SRCS, out, extra)
+    if probe:
+        _compile((PROBE_SRC,), PROBE_LIB, extra)
     return out
 
 

@@ -343,7 +343,7 @@ def scan_bwd(x, dt, z, B, C, A, D, dt_bias, dy, *, h0=None, dh_last=None, cu_seq
     out["ddt_bias"] = torch.empty(dim, dtype=torch.float32, device=dev)
     out["dh0"] = torch.empty((nseq, dim, DSTATE), dtype=torch.float32, device=dev) if want_dh0 else None
     a = bwd_args(x, dt, z, B, C, A, D, dt_bias, dy, h0=h0, dh_last=dh_last, cu_seqlens=cu_seqlens,
-                 time_slices=time_slices, h_ckpt=h_ckpt, **out)
+                 workspace=workspace, time_slices=time_slices, h_ckpt=h_ckpt, **out)
     if workspace is None:
         workspace = torch.empty(max(bwd_workspace_bytes(a), 1), dtype=torch.uint8, device=dev)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()

@@ -33,8 +33,38 @@ def norm_err(g, o) -> float:
     return diff / scale
 
 
+# Per-(sequence, channel) diagnostic: the same error with each column normalised by its own largest oracle
+# magnitude, so that a channel of small scale cannot hide under the largest channel of the sequence.
+# Columns below this fraction of the sequence's largest magnitude are left out (their own scale is then
+# rounding noise of the inputs, not a signal the contract speaks of).
+CHANNEL_FLOOR = 1e-3
+LAST_CHANNEL_ERR = {}
+
+
+def channel_err(g, o, seq_bounds=None) -> float:
+    """Worst per-(sequence, column) normalised error of 2-D [rows][columns] arrays (0 for other shapes)."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    if o.ndim != 2 or o.shape[1] < 2 or o.size == 0:
+        return 0.0
+    parts = [(0, len(o))] if seq_bounds is None else list(zip(seq_bounds[:-1], seq_bounds[1:]))
+    worst = 0.0
+    for a, b in parts:
+        if b <= a:
+            continue
+        oo, gg = o[a:b], g[a:b]
+        colmax = np.max(np.abs(oo), axis=0)
+        keep = colmax > CHANNEL_FLOOR * max(float(np.max(colmax)), 1e-300)
+        if not np.any(keep):
+            continue
+        e = np.max(np.abs(gg[:, keep] - oo[:, keep]), axis=0) / colmax[keep]
+        worst = max(worst, float(np.max(e)))
+    return worst
+
+
 def check_fp32(g, o, what: str, seq_bounds=None, trip: float = TRIP) -> float:
-    """fp32 output: per-sequence normalised error <= contract (and <= trip)."""
+    """fp32 output: per-sequence normalised error <= contract (and <= trip); for [rows][columns] outputs the
+    per-(sequence, column) diagnostic must also meet the contract."""
     g = np.asarray(g, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
     assert np.all(np.isfinite(g)), what + ": non-finite GPU output"
@@ -45,6 +75,9 @@ def check_fp32(g, o, what: str, seq_bounds=None, trip: float = TRIP) -> float:
         worst = max(worst, e)
     assert worst <= CONTRACT, "%s: normalised error %.3e > contract %.1e" % (what, worst, CONTRACT)
     assert worst <= trip, "%s: normalised error %.3e > tripwire %.1e" % (what, worst, trip)
+    ce = channel_err(g, o, seq_bounds)
+    LAST_CHANNEL_ERR[what] = ce
+    assert ce <= CONTRACT, "%s: per-(sequence, channel) error %.3e > contract %.1e" % (what, ce, CONTRACT)
     return worst
 
 

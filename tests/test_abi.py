@@ -18,7 +18,8 @@ from selective_state_space_05_amd import swa as W
 
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "samba_scan.h"
-HEADERS = sorted((ROOT / "include").glob("*.h"))
+PROBE_HEADER = ROOT / "include" / "samba_probe.h"
+HEADERS = sorted(h for h in (ROOT / "include").glob("*.h") if h != PROBE_HEADER)
 
 
 @pytest.fixture(scope="module")
@@ -28,9 +29,9 @@ def lib():
     return W.load_library()
 
 
-def header_functions():
+def header_functions(headers=HEADERS):
     names = set()
-    for h in HEADERS:
+    for h in headers:
         txt = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
         names |= set(re.findall(r"\b(samba_\w+)\s*\(", txt))
     return sorted(names)
@@ -41,6 +42,23 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(S.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_probe_library_exports_its_header():
+    """libsamba_probe.so (the ALU issue-rate probes) exports every function samba_probe.h declares."""
+    from selective_state_space_05_amd import probe as PR
+    plib = PR.load_library()
+    names = header_functions([PROBE_HEADER])
+    assert names == ["samba_probe_alu", "samba_probe_instructions_per_round"]
+    for n in names:
+        assert hasattr(plib, n), n
+    assert PR.instructions_per_round("fmac_vop2") == 16 and PR.instructions_per_round("fma_vop3") == 32
+    assert PR.instructions_per_round("mix_4fmac_1exp") == 80
+    assert plib.samba_probe_instructions_per_round(99) == 0
+    # bad arguments are refused on the host, before any HIP call
+    assert plib.samba_probe_alu(0, 0, 1, ctypes.c_void_p(64), None) == 1
+    assert plib.samba_probe_alu(0, 1, 1, None, None) == 1
+    assert plib.samba_probe_alu(99, 1, 1, ctypes.c_void_p(64), None) == 1
 
 
 def test_abi_version_and_state_size(lib):
