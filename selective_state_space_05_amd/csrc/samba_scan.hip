@@ -372,8 +372,8 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
   __shared__ float4 s_bc[kWaves][2][K * kN / 4];                   // per-wave staged B, C (fp32)
   __shared__ float4 s_du[kWaves][K / 4][kCPW][2];                  // per-wave (Δ, Δx) of each group's 4 tokens
   __shared__ float s_red[kWaves][kCPW * kRedRow];                  // per-wave readout partials of one group
-  __shared__ float4 s_agg[(W > 1) ? 2 : 1][W][2][64];              // slice (P, H) pairs, double buffered
-  __shared__ float4 s_carry[(W > 1) ? 2 : 1][64];                  // chunk carry, double buffered
+  __shared__ float4 s_agg[(W > 1) ? W : 1][2][64];                // slice (P, H) pairs of the current chunk
+  __shared__ float4 s_cin[(W > 1) ? W : 1][64];                    // each slice's carry-in, from the fold waves
 
   // wave index, declared wave-uniform so that everything derived from it lives in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -507,11 +507,32 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
     constexpr int chunk = W * K;
     const int nchunks = (ntok + chunk - 1) / chunk;
     const int my0 = wave * K;  // this wave's slice in chunk 0, relative to the sequence start
-    // the carry into chunk 0 is h0: seed the "previous chunk" carry slot with it
-    if (wave == W - 1) s_carry[1][L.lane] = make_float4(L.hinit[0], L.hinit[1], L.hinit[2], L.hinit[3]);
+
+    // Carry fold.  The chunk's 64 lanes x 4 states = 256 independent chains are shared out over the first
+    // kFoldWaves waves (one per SIMD where W >= 4): thread t of fold wave f owns the kChainsPerThread chains
+    // k = (f * kChainsPerThread + q) * 64 + t, i.e. float k of a [64 lanes][4 states] row, so that a fold
+    // wave's LDS accesses are contiguous.  Each chain keeps the running carry (the state entering the
+    // chunk) in a register: it starts as h0 and after every chunk becomes the state leaving it.
+    constexpr int kFoldWaves = W < 4 ? W : 4;
+    constexpr int kChainsPerThread = 4 / kFoldWaves;
+    constexpr int kFoldGroup = 4;   // slices whose (P, H) are read together: bounds the fold's extra registers
+    const bool folder = wave < kFoldWaves;
+    // element of h0 / h_last [nseq][dim][16] of chain q of this thread, or -1 (not a fold thread, or past
+    // the last channel)
+    auto chain_off = [&](int q) -> int64_t {
+      const int k = (wave * kChainsPerThread + q) * 64 + L.lane;   // float index in a [64][4] row
+      const int cl = k >> 2, st = 4 * (cl & 3) + (k & 3);           // lane of the row, state of the chain
+      const int dch = tile * kCPW + (cl >> 2);
+      return (folder && dch < p.dim) ? (static_cast<int64_t>(s) * p.dim + dch) * kN + st : -1;
+    };
+    float carry[kChainsPerThread];
+#pragma unroll
+    for (int q = 0; q < kChainsPerThread; ++q) {
+      const int64_t off = chain_off(q);
+      carry[q] = (off >= 0 && p.h0) ? p.h0[off] : 0.f;
+    }
 
     auto chunk_step = [&](int ci, const RawSlice<Tin, K>& cur, RawSlice<Tin, K>& nxt) {
-      const int buf = ci & 1;
       const int i0 = my0 + ci * chunk;
       const int64_t t0 = L.start + i0;
       const int nv = ntok - i0 <= 0 ? 0 : (ntok - i0 < K ? ntok - i0 : K);
@@ -554,27 +575,46 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
 #pragma unroll
       for (int j = 0; j < K / 4; ++j) sd += dl[j];
       sd = quad_allsum(sd);
-      s_agg[buf][wave][0][L.lane] = make_float4(__builtin_amdgcn_exp2f(L.A2[0] * sd), __builtin_amdgcn_exp2f(L.A2[1] * sd),
-                                                __builtin_amdgcn_exp2f(L.A2[2] * sd), __builtin_amdgcn_exp2f(L.A2[3] * sd));
-      s_agg[buf][wave][1][L.lane] = make_float4(H[0], H[1], H[2], H[3]);
+      s_agg[wave][0][L.lane] = make_float4(__builtin_amdgcn_exp2f(L.A2[0] * sd), __builtin_amdgcn_exp2f(L.A2[1] * sd),
+                                           __builtin_amdgcn_exp2f(L.A2[2] * sd), __builtin_amdgcn_exp2f(L.A2[3] * sd));
+      s_agg[wave][1][L.lane] = make_float4(H[0], H[1], H[2], H[3]);
       __syncthreads();
 
-      // carry-in of this slice: chunk carry folded through the earlier slices
+      // fold: every slice's carry-in, from the chunk carry through the slices before it (all reads issued
+      // first, then one dependent FMA per slice); the result of the last slice is the next chunk's carry
+      if (folder) {
+        const float* aggf = reinterpret_cast<const float*>(s_agg);
+        float* cinf = reinterpret_cast<float*>(s_cin);
+#pragma unroll
+        for (int q = 0; q < kChainsPerThread; ++q) {
+          const int k = (wave * kChainsPerThread + q) * 64 + L.lane;
+          float c = carry[q];
+#pragma unroll
+          for (int g0 = 0; g0 < W; g0 += kFoldGroup) {
+            constexpr int G = W < kFoldGroup ? W : kFoldGroup;
+            float Pv[G], Hv[G];
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+              Pv[u] = aggf[((g0 + u) * 2 + 0) * 256 + k];
+              Hv[u] = aggf[((g0 + u) * 2 + 1) * 256 + k];
+            }
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+              cinf[(g0 + u) * 256 + k] = c;
+              c = fmaf(Pv[u], c, Hv[u]);
+            }
+          }
+          carry[q] = c;
+        }
+      }
+      __syncthreads();
+
+      // phase 3: replay the slice from its carry-in, read out, gate, store
       float hin[kSPL];
       {
-        const float4 cr = s_carry[buf ^ 1][L.lane];
+        const float4 cr = s_cin[wave][L.lane];
         hin[0] = cr.x; hin[1] = cr.y; hin[2] = cr.z; hin[3] = cr.w;
       }
-      for (int w2 = 0; w2 < wave; ++w2) {
-        const float4 P = s_agg[buf][w2][0][L.lane];
-        const float4 Hs = s_agg[buf][w2][1][L.lane];
-        hin[0] = fmaf(P.x, hin[0], Hs.x);
-        hin[1] = fmaf(P.y, hin[1], Hs.y);
-        hin[2] = fmaf(P.z, hin[2], Hs.z);
-        hin[3] = fmaf(P.w, hin[3], Hs.w);
-      }
-
-      // phase 3: replay the slice from the true carry-in, read out, gate, store
       const rsrc_t ry = make_rsrc_rows(kCkpt ? yout : yout + t0 * p.dim, kCkpt ? 0 : ntok - i0,
                                        static_cast<uint32_t>(p.dim));
       if (kCkpt || p.ckpt) {
@@ -606,7 +646,6 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
           }
         }
       }
-      if (wave == W - 1) s_carry[buf][L.lane] = make_float4(h[0], h[1], h[2], h[3]);
       wave_lds_sync();
     };
 
@@ -616,9 +655,15 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
       chunk_step(ci, ra, rb);
       if (ci + 1 < nchunks) chunk_step(ci + 1, rb, ra);
     }
-    if (wave == W - 1 && p.h_last && L.dvalid)
-      reinterpret_cast<float4*>(p.h_last + (static_cast<int64_t>(s) * p.dim + L.d) * kN)[L.g] =
-          make_float4(h[0], h[1], h[2], h[3]);
+    // the state leaving the sequence is the fold's carry after the last chunk (also for a chained call's
+    // next h0, so that chunk-aligned chained calls reproduce a single pass bit for bit)
+    if (p.h_last) {
+#pragma unroll
+      for (int q = 0; q < kChainsPerThread; ++q) {
+        const int64_t off = chain_off(q);
+        if (off >= 0) p.h_last[off] = carry[q];
+      }
+    }
   }
 }
 
