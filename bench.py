@@ -249,7 +249,8 @@ def bench_prefill(steps: int, warmup: int, time_slices: int = 0):
         "launch_ms": launch_ms,
         "launch_td": cl * D,
         "bytes_per_launch": prefill_bytes(cl, D),
-        "plan": {"time_slices": plan[0], "workgroups": plan[1], "threads_per_workgroup": plan[2]},
+        "plan": {"time_slices": plan[0], "workgroups": plan[1], "threads_per_workgroup": plan[2],
+                 "lanes_per_channel": plan[3]},
         "call_us": {"median": per_call[len(per_call) // 2], "min": per_call[0], "calls": len(per_call)},
     }
 
@@ -1114,6 +1115,13 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
     print(json.dumps(out_d))
 
 
+def kernel_name(plan) -> str:
+    """The prefill kernel a launch plan runs (bf16 in, bf16 out)."""
+    if plan["lanes_per_channel"] == 8:
+        return "scan_split8_kernel<bf16,bf16,W=%d> (8 lanes per channel)" % plan["time_slices"]
+    return "scan_fwd_kernel<bf16,bf16,W=%d> (4 lanes per channel)" % plan["time_slices"]
+
+
 def copy_ceiling(nbytes: int = 1 << 30, reps: int = 10) -> float:
     """Measured device-to-device copy rate (bytes read + bytes written per second, GB/s): the practical HBM
     ceiling the algorithmic rates are also compared with."""
@@ -1380,7 +1388,7 @@ def main():
         "call_us": pf["call_us"],
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_PEAK_TSLOT, 2),
                      "unit": "Tslot/s", "frac": round(achieved / VALU_PEAK_TSLOT, 4),
-                     "traffic": traffic, "kernel": "scan_fwd_kernel<bf16,bf16,W=%d>" % pf["plan"]["time_slices"],
+                     "traffic": traffic, "kernel": kernel_name(pf["plan"]),
                      "launch_us": round(pf["launch_ms"] * 1e3, 2), "slots_per_token_channel": SLOTS_PER_TD,
                      "algorithmic_bytes_per_launch": pf["bytes_per_launch"]},
     }

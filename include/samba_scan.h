@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SAMBA_SCAN_ABI_VERSION 11
+#define SAMBA_SCAN_ABI_VERSION 12
 #define SAMBA_DSTATE 16
 
 typedef enum {
@@ -86,10 +86,17 @@ typedef enum { SAMBA_F32 = 0, SAMBA_BF16 = 1 } samba_dtype;
  * of one channel tile (1, 2, 4, 8 or 16); other values force it (testing and
  * tuning; results agree to fp32 rounding, and are bitwise reproducible for a
  * given choice).
+ * lanes_per_channel: 0 lets the library choose how many lanes share one
+ * channel's 16 states in a time-split launch: 4 (16-channel tiles) or 8
+ * (8-channel tiles: twice the workgroups, for few sequences); other values
+ * force it.  8 needs time_slices 0 or >= 2 and no h_ckpt (else
+ * SAMBA_ERR_UNSUPPORTED); h_ckpt always runs the 4-lane kernel.
  *
  * h_ckpt (optional output, fp32, 16-byte aligned): the state before every 8th
  * token of each sequence, for a later samba_scan_bwd of the same inputs (a
- * training forward keeps them instead of the backward recomputing them).  The
+ * training forward keeps them instead of the backward recomputing them).  A
+ * call with h_ckpt runs the 4-lane kernel: y and h_last equal, bit for bit,
+ * those of the same call without h_ckpt and lanes_per_channel = 4.  The
  * state before token 8j of sequence s (first token row start_s) is slot
  * floor(start_s / 8) + s + j of an array [slots][dim][16], slots = tokens / 8 +
  * nseq + 1 (samba_scan_ckpt_bytes); slots no sequence uses are not written.
@@ -109,6 +116,7 @@ typedef struct {
   float* h_last;               /* optional */
   void* y;
   float* h_ckpt;               /* optional: states every 8 tokens, for the backward */
+  int32_t lanes_per_channel;   /* 0 = automatic; 4 or 8 force the kernel (see above) */
 } samba_scan_fwd_args;
 
 /*
@@ -290,10 +298,12 @@ samba_status samba_scan_step(const samba_scan_step_args* args, void* stream);
 /*
  * Host-only: validate `args` and report the launch the library would make on
  * the current device (time slices per channel tile, workgroups, threads per
- * workgroup).  Enqueues nothing.  Any of the out pointers may be NULL.
+ * workgroup, lanes per channel).  Enqueues nothing.  Any of the out pointers
+ * may be NULL.
  */
 samba_status samba_scan_fwd_plan(const samba_scan_fwd_args* args, int32_t* time_slices,
-                                 int32_t* workgroups, int32_t* threads_per_workgroup);
+                                 int32_t* workgroups, int32_t* threads_per_workgroup,
+                                 int32_t* lanes_per_channel);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* samba_status_string(int status);

@@ -668,6 +668,263 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
 }
 
 // ---------------------------------------------------------------------------
+// Prefill, time-sliced, eight lanes per channel.  Lane (c, g) of a wave owns
+// states 2g and 2g+1 of channel c, so a wave covers 8 channels and the
+// workgroup an 8-channel tile; each wave's slice is 16 tokens, which keeps the
+// same 2 x 16 x 2 replay registers per lane as the quad variant's 8 tokens x
+// 4 states.  Halving the channels per workgroup doubles the workgroups: with
+// one or few sequences that fills twice the CUs, or puts two independent
+// workgroups on each CU, so one workgroup's barriers and LDS round trips are
+// covered by the other's work.  Per lane the scalar work is the same two
+// tokens per slice (g and g + 8).  No checkpoint variant.
+// ---------------------------------------------------------------------------
+constexpr int kCPW8 = 8;      // channels per wave (and per tile)
+constexpr int kK8 = 16;       // tokens per slice
+constexpr int kRedRow8 = 72;  // floats per channel row of the readout partials: 8 tokens x 8 lanes + 8
+constexpr int kDuRow8 = kK8 / 2 + 1;  // float4 per channel row of the (Δ, Δx) pairs: 8 used + 1 (bank spread)
+
+template <typename Tin>
+struct RawSlice8 {
+  static constexpr int kWords = static_cast<int>(sizeof(Tin));  // 4 B (and 4 C) values per lane, as words
+  Tin x[2], dt[2], z[2];
+  uint32_t bw[kWords], cw[kWords];
+};
+
+// Sum over the 8 lanes of each octet (two quad exchanges, then each half-row's mirror image)
+__device__ __forceinline__ float octet_allsum(float v) {
+  v += qperm<kQXor1>(v);
+  v += qperm<kQXor2>(v);
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  return v;
+}
+
+template <typename Tin>
+__device__ __forceinline__ void widen4(const uint32_t (&w)[RawSlice8<Tin>::kWords], float4& v) {
+  if constexpr (sizeof(Tin) == 2) {
+    v = make_float4(bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1]));
+  } else {
+    v = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3]));
+  }
+}
+
+template <typename Tin, typename Tout, int W>
+__global__ __launch_bounds__(64 * W, 4) void scan_split8_kernel(FwdParams p) {   // (<= 128 VGPRs)
+  static_assert(W >= 2 && W <= 16, "time slices");
+  constexpr int K = kK8;
+  __shared__ float4 s_bc[W][2][K * kN / 4];        // B, C rows [K][16] of each wave's slice (fp32)
+  __shared__ float4 s_du[W][kCPW8][kDuRow8];       // (Δ, Δx) of each channel's K tokens, two tokens per float4
+  __shared__ float s_red[W][kCPW8 * kRedRow8];     // readout partials [channel][token][lane]
+  __shared__ float2 s_agg[W][2][64];               // slice (P, H) pairs of the current chunk
+  __shared__ float2 s_cin[W][64];                  // each slice's carry-in, from the fold waves
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int logical = xcd_remap(blockIdx.x, p.nblocks);
+  const int s = logical / p.ngroups;
+  const int tile = logical - s * p.ngroups;
+  const int lane = threadIdx.x & 63, g = lane & 7, c = lane >> 3;
+  const int d = tile * kCPW8 + c;
+  const bool dvalid = d < p.dim;
+  const int dc = dvalid ? d : p.dim - 1;
+  int64_t start, end;
+  if (p.cu) {
+    int64_t a = p.cu[s], b = p.cu[s + 1];
+    a = a < 0 ? 0 : (a > p.total_tokens ? p.total_tokens : a);
+    b = b < a ? a : (b > p.total_tokens ? p.total_tokens : b);
+    start = a;
+    end = b;
+  } else {
+    start = static_cast<int64_t>(s) * p.seqlen;
+    end = start + p.seqlen;
+  }
+  float A2[2];
+  {
+    const float2 a2 = reinterpret_cast<const float2*>(p.A + static_cast<int64_t>(dc) * kN)[g];
+    A2[0] = a2.x * kLog2e;
+    A2[1] = a2.y * kLog2e;
+  }
+  const float dsk = p.Dskip[dc], bias = p.bias[dc];
+  const uint32_t dim = static_cast<uint32_t>(p.dim);
+  uint32_t in_off[2], out_off[2];  // byte offsets of tokens g and g + 8 of this lane's channel from a slice's first row
+  {
+    const uint32_t e0 = static_cast<uint32_t>(g) * dim + static_cast<uint32_t>(d);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      in_off[j] = (e0 + static_cast<uint32_t>(j) * 8u * dim) * static_cast<uint32_t>(sizeof(Tin));
+      out_off[j] = (e0 + static_cast<uint32_t>(j) * 8u * dim) * static_cast<uint32_t>(sizeof(Tout));
+    }
+  }
+  const uint32_t bc_off = static_cast<uint32_t>(lane) * 4u * static_cast<uint32_t>(sizeof(Tin));  // 4 of the slice's K x 16 values
+  Tout* const yout = static_cast<Tout*>(p.y);
+
+  const int ntok = static_cast<int>(end - start);   // 32-bit loop bookkeeping (a sequence is < 2^31 tokens)
+  constexpr int chunk = W * K;
+  const int nchunks = (ntok + chunk - 1) / chunk;
+  const int my0 = wave * K;
+
+  // Carry fold: the chunk's 64 lanes x 2 states = 128 chains, one per thread of the first two waves
+  // (chain k is float k of a [64 lanes][2 states] row); the chunk carry stays in that thread's register.
+  const bool folder = wave < 2;
+  auto chain_off = [&]() -> int64_t {
+    const int k = wave * 64 + lane;
+    const int cl = k >> 1;
+    const int dch = tile * kCPW8 + (cl >> 3);
+    return (folder && dch < p.dim) ? (static_cast<int64_t>(s) * p.dim + dch) * kN + 2 * (cl & 7) + (k & 1) : -1;
+  };
+  float carry;
+  {
+    const int64_t off = chain_off();
+    carry = (off >= 0 && p.h0) ? p.h0[off] : 0.f;
+  }
+
+  auto load8 = [&](int64_t t0, int rem, RawSlice8<Tin>& r) {
+    const int64_t row0 = t0 * p.dim;
+    const rsrc_t rx = make_rsrc_rows(static_cast<const Tin*>(p.x) + row0, rem, dim);
+    const rsrc_t rd = make_rsrc_rows(static_cast<const Tin*>(p.dt) + row0, rem, dim);
+    const rsrc_t rz = make_rsrc_rows(static_cast<const Tin*>(p.z) + row0, rem, dim);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bload(rx, in_off[j], r.x[j]);
+      bload(rd, in_off[j], r.dt[j]);
+      bload(rz, in_off[j], r.z[j]);
+    }
+    const rsrc_t rb = make_rsrc_rows(static_cast<const Tin*>(p.B) + t0 * kN, rem, kN);
+    const rsrc_t rc = make_rsrc_rows(static_cast<const Tin*>(p.C) + t0 * kN, rem, kN);
+    bload_words(rb, bc_off, r.bw);
+    bload_words(rc, bc_off, r.cw);
+  };
+
+  const float2* sB2 = reinterpret_cast<const float2*>(s_bc[wave][0]);
+  const float2* sC2 = reinterpret_cast<const float2*>(s_bc[wave][1]);
+  float* red = s_red[wave] + c * kRedRow8;
+
+  auto chunk_step = [&](int ci, const RawSlice8<Tin>& cur, RawSlice8<Tin>& nxt) {
+    const int i0 = my0 + ci * chunk;
+    const int64_t t0 = start + i0;
+    const int nv = ntok - i0 <= 0 ? 0 : (ntok - i0 < K ? ntok - i0 : K);
+    load8(t0 + chunk, ntok - i0 - chunk, nxt);   // this wave's slice of the next chunk
+    {
+      float4 v;
+      widen4<Tin>(cur.bw, v);
+      s_bc[wave][0][lane] = v;
+      widen4<Tin>(cur.cw, v);
+      s_bc[wave][1][lane] = v;
+    }
+    float xv[2], zv[2], dl[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool ok = dvalid && (g + 8 * j) < nv;
+      xv[j] = widen(cur.x[j]);
+      zv[j] = widen(cur.z[j]);
+      const float delta = softplus_f32(widen(cur.dt[j]) + bias);
+      dl[j] = ok ? delta : 0.0f;
+      reinterpret_cast<float2*>(s_du[wave][c])[g + 8 * j] = make_float2(dl[j], ok ? delta * xv[j] : 0.0f);
+    }
+    wave_lds_sync();
+
+    // phase 1: local scan of the slice from zero; keep Ā and B̄x in registers
+    float ak[K][2], bk[K][2];
+    float H[2];
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 4) {
+      const float4 du01 = s_du[wave][c][k0 / 2], du23 = s_du[wave][c][k0 / 2 + 1];
+      const float dq[4] = {du01.x, du01.z, du23.x, du23.z};
+      const float uq[4] = {du01.y, du01.w, du23.y, du23.w};
+      float2 bq[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bq[r] = sB2[(k0 + r) * 8 + g];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int k = k0 + r;
+        ak[k][0] = __builtin_amdgcn_exp2f(dq[r] * A2[0]);
+        ak[k][1] = __builtin_amdgcn_exp2f(dq[r] * A2[1]);
+        bk[k][0] = uq[r] * bq[r].x;
+        bk[k][1] = uq[r] * bq[r].y;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) H[i] = (k == 0) ? bk[0][i] : fmaf(ak[k][i], H[i], bk[k][i]);
+      }
+    }
+    // product of the slice's Ā = exp(A * sum of the slice's Δ)
+    const float sd = octet_allsum(dl[0] + dl[1]);
+    s_agg[wave][0][lane] = make_float2(__builtin_amdgcn_exp2f(A2[0] * sd), __builtin_amdgcn_exp2f(A2[1] * sd));
+    s_agg[wave][1][lane] = make_float2(H[0], H[1]);
+    __syncthreads();
+
+    // fold: every slice's carry-in (all four slices of a group read first, then one FMA per slice)
+    if (folder) {
+      const float* aggf = reinterpret_cast<const float*>(s_agg);
+      float* cinf = reinterpret_cast<float*>(s_cin);
+      const int k = wave * 64 + lane;
+      float cc = carry;
+#pragma unroll
+      for (int g0 = 0; g0 < W; g0 += 4) {
+        constexpr int G = W < 4 ? W : 4;
+        float Pv[G], Hv[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+          Pv[u] = aggf[((g0 + u) * 2 + 0) * 128 + k];
+          Hv[u] = aggf[((g0 + u) * 2 + 1) * 128 + k];
+        }
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+          cinf[(g0 + u) * 128 + k] = cc;
+          cc = fmaf(Pv[u], cc, Hv[u]);
+        }
+      }
+      carry = cc;
+    }
+    __syncthreads();
+
+    // phase 3: replay the slice from its carry-in, read out, gate, store
+    float h[2];
+    {
+      const float2 cr = s_cin[wave][lane];
+      h[0] = cr.x;
+      h[1] = cr.y;
+    }
+    const rsrc_t ry = make_rsrc_rows(yout + t0 * p.dim, ntok - i0, dim);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      float pr[8];
+      float2 cq[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) cq[q] = sC2[(8 * jj + q) * 8 + g];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int k = 8 * jj + q;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) h[i] = fmaf(ak[k][i], h[i], bk[k][i]);
+        pr[q] = fmaf(cq[q].y, h[1], cq[q].x * h[0]);
+      }
+      // transposed sum over the octet: lane g writes its partial of token q at [q][g] and reads the
+      // eight partials of token g (rows of 72 floats put the 64 single-float writes on distinct banks)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) red[q * 8 + g] = pr[q];
+      wave_lds_sync();
+      const float4 v0 = reinterpret_cast<const float4*>(red + g * 8)[0];
+      const float4 v1 = reinterpret_cast<const float4*>(red + g * 8)[1];
+      const float yraw = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w));
+      if (g + 8 * jj < nv) {
+        const float yv = (yraw + dsk * xv[jj]) * silu_f32(zv[jj]);
+        if (dvalid) bstore(ry, out_off[jj], yv, static_cast<Tout*>(nullptr));
+      }
+    }
+    wave_lds_sync();
+  };
+
+  RawSlice8<Tin> ra, rb;
+  load8(start + my0, ntok - my0, ra);
+  for (int ci = 0; ci < nchunks; ci += 2) {
+    chunk_step(ci, ra, rb);
+    if (ci + 1 < nchunks) chunk_step(ci + 1, rb, ra);
+  }
+  // the state leaving the sequence is the fold's carry after the last chunk
+  if (p.h_last) {
+    const int64_t off = chain_off();
+    if (off >= 0) p.h_last[off] = carry;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Backward (gradients of the prefill).  Per sequence and channel the adjoint
 // g_t = dr_t C_t + Ā_{t+1} g_{t+1} runs from the last token to the first, and
 // every gradient term of token t needs g_t together with the forward states
@@ -1478,7 +1735,7 @@ bool dtype_ok(int32_t dt) { return dt == SAMBA_F32 || dt == SAMBA_BF16; }
 int slice_tokens(int W) { return W >= 2 ? 8 : 16; }
 
 struct FwdPlan {
-  int W, tpw, threads, grid;
+  int W, tpw, lanes, threads, grid;   // lanes: per channel, 4 (scan_fwd_kernel) or 8 (scan_split8_kernel)
   int64_t nseq;
   FwdParams prm;
 };
@@ -1497,12 +1754,31 @@ int choose_time_slices(int64_t nseq, int64_t ntiles, int64_t tokens, int wmax, i
   return W;
 }
 
+int slice_tokens8(int) { return kK8; }
+
+// lanes: 0 (choose), 4 or 8 lanes per channel; ckpt: checkpoints requested (the 8-lane kernel has none).
+// Automatic choice: the quad kernel's plan, unless it splits time and its (sequence, 16-channel tile)
+// workgroups would not exceed the CUs; then 8-channel tiles double the workgroups (twice the CUs busy, or
+// two independent workgroups per CU) at the same work per (token, channel).
 samba_status make_fwd_plan(const void* x, const void* dt, const void* z, const void* B, const void* C, const float* A,
                            const float* D, const float* bias, const float* h0, const int32_t* cu, int64_t nseq,
-                           int32_t batch, int32_t seqlen, int32_t dim, int ts, FwdPlan* plan) {
+                           int32_t batch, int32_t seqlen, int32_t dim, int ts, int lanes, bool ckpt, FwdPlan* plan) {
   const int64_t tokens = static_cast<int64_t>(batch) * seqlen;
-  const int ntiles = (dim + kCPW - 1) / kCPW;
-  const int W = ts ? ts : choose_time_slices(nseq, ntiles, tokens, 16, slice_tokens);
+  const int ntiles16 = (dim + kCPW - 1) / kCPW, ntiles8 = (dim + kCPW8 - 1) / kCPW8;
+  if (lanes == 0) {
+    lanes = 4;
+    const int Wq = ts ? ts : choose_time_slices(nseq, ntiles16, tokens, 16, slice_tokens);
+    const int W8 = ts ? ts : choose_time_slices(nseq, ntiles8, tokens, 16, slice_tokens8);
+    if (!ckpt && Wq >= 2 && W8 >= 2 && nseq * ntiles16 <= device_cu_count()) lanes = 8;
+  }
+  if (lanes == 8 && (ckpt || ts == 1)) return SAMBA_ERR_UNSUPPORTED;
+  const int ntiles = lanes == 8 ? ntiles8 : ntiles16;
+  int W = ts;
+  if (!W) {
+    W = lanes == 8 ? choose_time_slices(nseq, ntiles, tokens, 16, slice_tokens8)
+                   : choose_time_slices(nseq, ntiles, tokens, 16, slice_tokens);
+    if (lanes == 8 && W < 2) W = 2;   // (forced 8 lanes on a sequence too short to split: two slices)
+  }
   const int tpw = (W == 1) ? 4 : 1;
   const int ngroups = (ntiles + tpw - 1) / tpw;
   FwdParams& p = plan->prm;
@@ -1522,6 +1798,7 @@ samba_status make_fwd_plan(const void* x, const void* dt, const void* z, const v
   p.nblocks = static_cast<int32_t>(nblocks);
   plan->W = W;
   plan->tpw = tpw;
+  plan->lanes = lanes;
   plan->threads = 64 * W * tpw;
   plan->grid = static_cast<int>(nblocks);
   plan->nseq = nseq;
@@ -1536,6 +1813,9 @@ samba_status validate_fwd(const samba_scan_fwd_args* a, FwdPlan* plan) {
   if (a->batch < 0 || a->seqlen < 0 || a->dim < 1) return SAMBA_ERR_BAD_SHAPE;
   const int ts = a->time_slices;
   if (!(ts == 0 || ts == 1 || ts == 2 || ts == 4 || ts == 8 || ts == 16)) return SAMBA_ERR_UNSUPPORTED;
+  const int lanes = a->lanes_per_channel;
+  if (!(lanes == 0 || lanes == 4 || lanes == 8)) return SAMBA_ERR_UNSUPPORTED;
+  if (lanes == 8 && (ts == 1 || a->h_ckpt)) return SAMBA_ERR_UNSUPPORTED;
   int64_t nseq = a->batch;
   if (a->cu_seqlens) {
     if (a->batch != 1 || a->nseq < 1) return SAMBA_ERR_BAD_SHAPE;
@@ -1575,12 +1855,21 @@ samba_status validate_fwd(const samba_scan_fwd_args* a, FwdPlan* plan) {
 
   if (!plan) return SAMBA_OK;
   return make_fwd_plan(a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias, a->h0, a->cu_seqlens, nseq,
-                       a->batch, a->seqlen, a->dim, ts, plan);
+                       a->batch, a->seqlen, a->dim, ts, lanes, a->h_ckpt != nullptr, plan);
 }
 
 template <typename Tin, typename Tout>
 hipError_t launch_fwd(const FwdPlan& pl, hipStream_t st) {
   const dim3 grid(pl.grid), block(pl.threads);
+  if (pl.lanes == 8) {
+    switch (pl.W) {
+      case 2: hipLaunchKernelGGL((scan_split8_kernel<Tin, Tout, 2>), grid, block, 0, st, pl.prm); break;
+      case 4: hipLaunchKernelGGL((scan_split8_kernel<Tin, Tout, 4>), grid, block, 0, st, pl.prm); break;
+      case 8: hipLaunchKernelGGL((scan_split8_kernel<Tin, Tout, 8>), grid, block, 0, st, pl.prm); break;
+      default: hipLaunchKernelGGL((scan_split8_kernel<Tin, Tout, 16>), grid, block, 0, st, pl.prm); break;
+    }
+    return hipGetLastError();
+  }
   switch (pl.W) {
     case 1: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 1, 4, 16>), grid, block, 0, st, pl.prm); break;
     case 2: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 2, 1, 8>), grid, block, 0, st, pl.prm); break;
@@ -1696,7 +1985,7 @@ samba_status validate_bwd(const samba_scan_bwd_args* a, BwdPlan* plan) {
 
   // checkpoint pass: the forward kernel's checkpoint variant, its own launch plan
   st = make_fwd_plan(a->x, a->dt, a->z, a->B, a->C, a->A, a->D, a->dt_bias, a->h0, a->cu_seqlens, nseq, a->batch,
-                     a->seqlen, a->dim, 0, &pl->ck);
+                     a->seqlen, a->dim, 0, 4, true, &pl->ck);
   if (st != SAMBA_OK) return st;
   char* ws = static_cast<char*>(a->workspace);
   float* ckpt = a->h_ckpt ? const_cast<float*>(a->h_ckpt) : reinterpret_cast<float*>(ws);
@@ -1785,10 +2074,11 @@ samba_status samba_scan_fwd(const samba_scan_fwd_args* args, void* stream) {
 }
 
 samba_status samba_scan_fwd_plan(const samba_scan_fwd_args* args, int32_t* time_slices, int32_t* workgroups,
-                                 int32_t* threads_per_workgroup) {
+                                 int32_t* threads_per_workgroup, int32_t* lanes_per_channel) {
   FwdPlan pl;
   const samba_status st = validate_fwd(args, &pl);
   if (st != SAMBA_OK) return st;
+  if (lanes_per_channel) *lanes_per_channel = pl.lanes;
   if (time_slices) *time_slices = pl.W;
   if (workgroups) *workgroups = pl.grid;
   if (threads_per_workgroup) *threads_per_workgroup = pl.threads;

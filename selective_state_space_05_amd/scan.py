@@ -13,7 +13,7 @@ from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "libsamba_scan.so"
 DSTATE = 16
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 SAMBA_F32, SAMBA_BF16 = 0, 1
 STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE", 3: "SAMBA_ERR_BAD_DTYPE",
@@ -34,7 +34,8 @@ class FwdArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("batch", _I32), ("seqlen", _I32), ("dim", _I32),
                 ("dstate", _I32), ("cu_seqlens", _P), ("nseq", _I32), ("in_dtype", _I32), ("y_dtype", _I32),
                 ("time_slices", _I32), ("x", _P), ("dt", _P), ("z", _P), ("B", _P), ("C", _P), ("A", _P),
-                ("D", _P), ("dt_bias", _P), ("h0", _P), ("h_last", _P), ("y", _P), ("h_ckpt", _P)]
+                ("D", _P), ("dt_bias", _P), ("h0", _P), ("h_last", _P), ("y", _P), ("h_ckpt", _P),
+                ("lanes_per_channel", _I32)]
 
 
 class StepArgs(ctypes.Structure):
@@ -99,7 +100,7 @@ def load_library(path: Path | str | None = None):
     lib.samba_scan_step.argtypes = [ctypes.POINTER(StepArgs), _P]
     lib.samba_scan_step.restype = ctypes.c_int
     lib.samba_scan_fwd_plan.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(_I32), ctypes.POINTER(_I32),
-                                        ctypes.POINTER(_I32)]
+                                        ctypes.POINTER(_I32), ctypes.POINTER(_I32)]
     lib.samba_scan_fwd_plan.restype = ctypes.c_int
     lib.samba_scan_bwd.argtypes = [ctypes.POINTER(BwdArgs), _P]
     lib.samba_scan_bwd.restype = ctypes.c_int
@@ -185,7 +186,7 @@ def alloc_ckpt(x, cu_seqlens=None):
 
 
 def fwd_args(x, dt, z, B, C, A, D, dt_bias, *, y, h0=None, h_last=None, cu_seqlens=None,
-             time_slices: int = 0, h_ckpt=None) -> FwdArgs:
+             time_slices: int = 0, h_ckpt=None, lanes_per_channel: int = 0) -> FwdArgs:
     """Fill a samba_scan_fwd_args from tensors (shapes as in scan_fwd)."""
     if x.dim() == 3:
         batch, seqlen, dim = x.shape
@@ -210,11 +211,13 @@ def fwd_args(x, dt, z, B, C, A, D, dt_bias, *, y, h0=None, h_last=None, cu_seqle
     a.A, a.D, a.dt_bias = _ptr(A), _ptr(D), _ptr(dt_bias)
     a.h0, a.h_last, a.y = _ptr(h0), _ptr(h_last), _ptr(y)
     a.h_ckpt = _ptr(h_ckpt)
+    a.lanes_per_channel = int(lanes_per_channel)
     return a
 
 
 def scan_fwd(x, dt, z, B, C, A, D, dt_bias, *, h0=None, h_last=None, y=None, return_last_state: bool = True,
-             cu_seqlens=None, y_dtype=None, time_slices: int = 0, h_ckpt=None, stream=None):
+             cu_seqlens=None, y_dtype=None, time_slices: int = 0, h_ckpt=None, lanes_per_channel: int = 0,
+             stream=None):
     """Selective-scan prefill through samba_scan_fwd.
 
     x, dt, z : [batch][seqlen][dim]  (or [tokens][dim] with cu_seqlens)   bf16 or fp32
@@ -223,6 +226,7 @@ def scan_fwd(x, dt, z, B, C, A, D, dt_bias, *, h0=None, h_last=None, y=None, ret
     h0       : [nseq][dim][16] fp32 or None (zeros)
     cu_seqlens: int32 [nseq+1] device tensor of packed sequence offsets, or None
     h_ckpt   : optional output from alloc_ckpt(x, cu_seqlens): states every 8 tokens, for scan_bwd
+    time_slices, lanes_per_channel: 0 = the library's launch plan; other values force it (see the header)
     Returns (y, h_last); h_last is None when neither given nor requested.
     """
     import torch
@@ -234,22 +238,24 @@ def scan_fwd(x, dt, z, B, C, A, D, dt_bias, *, h0=None, h_last=None, y=None, ret
             cu_seqlens.numel() - 1 if cu_seqlens is not None else 1)
         h_last = torch.empty((nseq, x.shape[-1], DSTATE), dtype=torch.float32, device=x.device)
     a = fwd_args(x, dt, z, B, C, A, D, dt_bias, y=y, h0=h0, h_last=h_last, cu_seqlens=cu_seqlens,
-                 time_slices=time_slices, h_ckpt=h_ckpt)
+                 time_slices=time_slices, h_ckpt=h_ckpt, lanes_per_channel=lanes_per_channel)
     st = load_library().samba_scan_fwd(ctypes.byref(a), _P(_stream_handle(stream)))
     if st != 0:
         raise SambaError(st, "samba_scan_fwd")
     return y, h_last
 
 
-def fwd_plan(x, dt, z, B, C, A, D, dt_bias, *, y, h0=None, h_last=None, cu_seqlens=None, time_slices: int = 0):
-    """(time_slices, workgroups, threads_per_workgroup) the library would launch."""
+def fwd_plan(x, dt, z, B, C, A, D, dt_bias, *, y, h0=None, h_last=None, cu_seqlens=None, time_slices: int = 0,
+             lanes_per_channel: int = 0, h_ckpt=None):
+    """(time_slices, workgroups, threads_per_workgroup, lanes_per_channel) the library would launch."""
     a = fwd_args(x, dt, z, B, C, A, D, dt_bias, y=y, h0=h0, h_last=h_last, cu_seqlens=cu_seqlens,
-                 time_slices=time_slices)
-    w, g, t = _I32(), _I32(), _I32()
-    st = load_library().samba_scan_fwd_plan(ctypes.byref(a), ctypes.byref(w), ctypes.byref(g), ctypes.byref(t))
+                 time_slices=time_slices, lanes_per_channel=lanes_per_channel, h_ckpt=h_ckpt)
+    w, g, t, q = _I32(), _I32(), _I32(), _I32()
+    st = load_library().samba_scan_fwd_plan(ctypes.byref(a), ctypes.byref(w), ctypes.byref(g), ctypes.byref(t),
+                                            ctypes.byref(q))
     if st != 0:
         raise SambaError(st, "samba_scan_fwd_plan")
-    return w.value, g.value, t.value
+    return w.value, g.value, t.value, q.value
 
 
 def step_args(state, x, dt, z, B, C, A, D, dt_bias, *, y) -> StepArgs:

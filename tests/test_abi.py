@@ -130,10 +130,10 @@ def step_ok(batch=4, dim=64):
     return a
 
 
-def plan(lib, a):
-    w, g, t = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    st = lib.samba_scan_fwd_plan(ctypes.byref(a), ctypes.byref(w), ctypes.byref(g), ctypes.byref(t))
-    return st, w.value, g.value, t.value
+def plan(lib, a, with_lanes=False):
+    w, g, t, q = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = lib.samba_scan_fwd_plan(ctypes.byref(a), ctypes.byref(w), ctypes.byref(g), ctypes.byref(t), ctypes.byref(q))
+    return (st, w.value, g.value, t.value, q.value) if with_lanes else (st, w.value, g.value, t.value)
 
 
 FWD_CASES = {
@@ -223,9 +223,36 @@ def test_step_empty_batch_is_noop(lib):
 # launch plan (host logic; falls back to 256 CUs when no device is visible)
 # --------------------------------------------------------------------------- #
 def test_plan_low_parallelism_splits_time(lib):
+    """One long sequence: 8-channel tiles (512 workgroups, two per CU) of 8 slices of 16 tokens."""
     a = fwd_ok(batch=1, seqlen=16384, dim=4096)
-    st, w, g, t = plan(lib, a)
-    assert st == 0 and w == 16 and g == 256 and t == 1024
+    assert plan(lib, a, True) == (0, 8, 512, 512, 8)
+    a.lanes_per_channel = 4     # the 16-channel-tile kernel: one 16-wave workgroup per tile
+    assert plan(lib, a, True) == (0, 16, 256, 1024, 4)
+
+
+def test_plan_half_gpu_shape_uses_eight_lanes(lib):
+    """B1 L4096 D2048: 128 sixteen-channel tiles would leave half of 256 CUs idle; 256 eight-channel tiles."""
+    a = fwd_ok(batch=1, seqlen=4096, dim=2048)
+    assert plan(lib, a, True) == (0, 16, 256, 1024, 8)
+
+
+def test_plan_eight_lanes_rules(lib):
+    a = fwd_ok(batch=1, seqlen=1000, dim=100)
+    a.lanes_per_channel = 8
+    for ts in (2, 4, 8, 16):
+        a.time_slices = ts
+        assert plan(lib, a, True) == (0, ts, 13, 64 * ts, 8)
+    a.time_slices = 1                       # no sequential 8-lane kernel
+    assert plan(lib, a)[0] == 6 and lib.samba_scan_fwd(ctypes.byref(a), None) == 6
+    a.time_slices = 0
+    a.h_ckpt = BASE + 12 * (1 << 30)        # checkpoints come from the 4-lane kernel only
+    assert plan(lib, a)[0] == 6
+    a.lanes_per_channel = 0                 # automatic: checkpoints keep 4 lanes
+    assert plan(lib, a, True)[4] == 4
+    a.h_ckpt = None
+    for bad in (1, 2, 3, 16, -4):
+        a.lanes_per_channel = bad
+        assert plan(lib, a)[0] == 6 and lib.samba_scan_fwd(ctypes.byref(a), None) == 6
 
 
 def test_plan_batched_runs_sequential(lib):
@@ -238,14 +265,21 @@ def test_plan_short_sequences_limit_slices(lib):
     """Time is split only into slices (8 tokens each) that the average sequence fills at least twice over."""
     for seqlen, want in ((12, 1), (20, 2), (40, 4)):
         a = fwd_ok(batch=1, seqlen=seqlen, dim=64)
+        a.lanes_per_channel = 4
         st, w, g, t = plan(lib, a)
         assert st == 0 and w == want, (seqlen, w)
+    # automatic lanes: 8 only where 16-token slices still split the sequence at least twice
+    for seqlen, want in ((12, (1, 4)), (20, (2, 4)), (40, (2, 8)), (100, (2, 8)))[:3]:
+        a = fwd_ok(batch=1, seqlen=seqlen, dim=64)
+        st, w, g, t, q = plan(lib, a, True)
+        assert st == 0 and (w, q) == want, (seqlen, w, q)
 
 
 def test_plan_forced_slices(lib):
     for ts in (1, 2, 4, 8, 16):
         a = fwd_ok(batch=1, seqlen=1000, dim=100)
         a.time_slices = ts
+        a.lanes_per_channel = 4
         st, w, g, t = plan(lib, a)
         assert st == 0 and w == ts
         assert g == (7 if ts > 1 else 2) and t == (64 * ts if ts > 1 else 256)

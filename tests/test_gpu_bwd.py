@@ -23,7 +23,7 @@ import torch
 from oracle import oracle as O
 from selective_state_space_05_amd import inputs as I
 from selective_state_space_05_amd import scan as S
-from tests.parity import check_bf16_y, check_fp32
+from tests.parity import check_bf16_y, check_fp32, norm_err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -189,7 +189,8 @@ def test_bwd_full_training_shape():
 
 @pytest.mark.parametrize("lengths", [None, [37, 0, 100, 8, 1, 0, 64]])
 def test_forward_checkpoints_feed_the_backward(lengths):
-    """samba_scan_fwd with h_ckpt: y and h_last unchanged (bitwise); every checkpoint is the oracle's state
+    """samba_scan_fwd with h_ckpt: y and h_last bitwise those of the same (4-lane) launch plan without
+    checkpoints, and within fp32 rounding of the automatic plan; every checkpoint is the oracle's state
     before that token; the backward fed these checkpoints equals the self-contained backward (bitwise)."""
     D, cfg = 40, 0
     if lengths is None:
@@ -210,13 +211,15 @@ def test_forward_checkpoints_feed_the_backward(lengths):
     A, Dv, bias = (torch.from_numpy(inp[k]).to(DEV) for k in ("A", "D", "dt_bias"))
     cu = torch.from_numpy(seq_start.astype(np.int32)).to(DEV) if lengths is not None else None
     h0t, dhl = torch.from_numpy(h0).to(DEV), torch.from_numpy(ex["dh_last"]).to(DEV)
-    y1, hl1 = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=h0t, cu_seqlens=cu)
+    y1, hl1 = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=h0t, cu_seqlens=cu, lanes_per_channel=4)
+    y0, hl0 = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=h0t, cu_seqlens=cu)
     ck = S.alloc_ckpt(x, cu)
     y2, hl2 = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=h0t, cu_seqlens=cu, h_ckpt=ck)
     g1 = S.scan_bwd(x, dt, z, B, C, A, Dv, bias, dy, h0=h0t, dh_last=dhl, cu_seqlens=cu)
     g2 = S.scan_bwd(x, dt, z, B, C, A, Dv, bias, dy, h0=h0t, dh_last=dhl, cu_seqlens=cu, h_ckpt=ck)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(hl1, hl2)
+    assert norm_err(host(hl0), host(hl2)) < 1e-5 and norm_err(host(y0), host(y2)) < 1e-2
     for k, v in g1.items():
         assert torch.equal(v, g2[k]), "backward with forward checkpoints differs: " + k
     ckh = host(ck)

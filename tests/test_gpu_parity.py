@@ -37,7 +37,7 @@ def host(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_case(batch, L, D, in_dtype="bf16", y_dtype="f32", ts=0, h0_scale=0.0, cfg=0, dt_override=None):
+def run_case(batch, L, D, in_dtype="bf16", y_dtype="f32", ts=0, h0_scale=0.0, cfg=0, dt_override=None, lanes=0):
     """Build a seeded host-sized case, run GPU and oracle, return both."""
     rows = batch * L
     inp = I.make_fwd_inputs_np(cfg, rows, D, in_dtype=in_dtype)
@@ -52,7 +52,7 @@ def run_case(batch, L, D, in_dtype="bf16", y_dtype="f32", ts=0, h0_scale=0.0, cf
     A, Dv, bias = (torch.from_numpy(inp[k]).to(DEV) for k in ("A", "D", "dt_bias"))
     h0_t = torch.from_numpy(h0).to(DEV) if h0 is not None else None
     ydt = torch.float32 if y_dtype == "f32" else torch.bfloat16
-    y, hl = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=h0_t, y_dtype=ydt, time_slices=ts)
+    y, hl = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=h0_t, y_dtype=ydt, time_slices=ts, lanes_per_channel=lanes)
     torch.cuda.synchronize()
     yo, ho = O.scan_fwd(inp["x_f32"].reshape(shp), inp["dt_f32"].reshape(shp), inp["z_f32"].reshape(shp),
                         inp["B_f32"].reshape(batch, L, 16), inp["C_f32"].reshape(batch, L, 16), inp["A"], inp["D"],
@@ -94,10 +94,14 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("lanes", [4, 8])
 @pytest.mark.parametrize("batch,L,D,ind,yd,ts,h0s", SMALL)
-def test_small(batch, L, D, ind, yd, ts, h0s):
-    say("case batch=%d L=%d D=%d in=%s y=%s slices=%d h0=%g" % (batch, L, D, ind, yd, ts, h0s))
-    r = run_case(batch, L, D, ind, yd, ts, h0s)
+def test_small(batch, L, D, ind, yd, ts, h0s, lanes):
+    """Every case through the 4-lane kernel and, where time is split, the 8-lane kernel (8-channel tiles)."""
+    if lanes == 8 and ts == 1:
+        pytest.skip("the 8-lane kernel only splits time (a sequential plan has 4 lanes per channel)")
+    say("case batch=%d L=%d D=%d in=%s y=%s slices=%d h0=%g lanes=%d" % (batch, L, D, ind, yd, ts, h0s, lanes))
+    r = run_case(batch, L, D, ind, yd, ts, h0s, lanes=lanes if ts != 1 else 0)
     check_case(r, batch, L, yd, "B%d L%d D%d" % (batch, L, D))
 
 
@@ -117,20 +121,22 @@ def test_empty_sequence_copies_carry():
 
 
 def test_time_slices_agree():
-    """Every slicing of the time axis gives the same result to fp32 rounding."""
+    """Every slicing of the time axis, with 4 or 8 lanes per channel, gives the same result to fp32 rounding."""
     outs = {}
-    for ts in (1, 2, 4, 8, 16):
-        outs[ts] = run_case(1, 2000, 64, "bf16", "f32", ts, 1.0, cfg=1)
+    outs[(1, 4)] = run_case(1, 2000, 64, "bf16", "f32", 1, 1.0, cfg=1)
     for ts in (2, 4, 8, 16):
-        assert norm_err(outs[ts]["y"], outs[1]["y"]) < 1e-5
-        assert norm_err(outs[ts]["h"], outs[1]["h"]) < 1e-5
+        for lanes in (4, 8):
+            outs[(ts, lanes)] = run_case(1, 2000, 64, "bf16", "f32", ts, 1.0, cfg=1, lanes=lanes)
+    for key, r in outs.items():
+        assert norm_err(r["y"], outs[(1, 4)]["y"]) < 1e-5, key
+        assert norm_err(r["h"], outs[(1, 4)]["h"]) < 1e-5, key
 
 
 def test_delta_to_zero_carry_pin():
     """dt_raw = -40 makes Δ ~ 1e-18: h_last must equal h0 and y_t = (C_t.h0 + D x_t) silu(z_t).
     Away from the first token only a correct carry (across slices, chunks and waves) gives this."""
-    for ts in (1, 8, 16):
-        r = run_case(2, 1000, 32, "bf16", "f32", ts, 1.0, dt_override=-40.0)
+    for ts, lanes in ((1, 0), (8, 4), (16, 4), (2, 8), (8, 8), (16, 8)):
+        r = run_case(2, 1000, 32, "bf16", "f32", ts, 1.0, dt_override=-40.0, lanes=lanes)
         inp, h0 = r["inp"], r["h0"]
         C = inp["C_f32"].reshape(2, 1000, 16).astype(np.float64)
         x = inp["x_f32"].reshape(2, 1000, 32).astype(np.float64)
@@ -141,7 +147,8 @@ def test_delta_to_zero_carry_pin():
         check_case(r, 2, 1000, "f32", "dt->0 slices=%d" % ts)
 
 
-def test_slow_decay_chained_calls():
+@pytest.mark.parametrize("lanes", [4, 8])
+def test_slow_decay_chained_calls(lanes):
     """Long memory (Δ = 1e-3, A = -1): 4 chained calls of 1024 tokens == one call == oracle."""
     D, L, parts = 64, 4096, 4
     inp = I.make_fwd_inputs_np(3, L, D)
@@ -152,7 +159,7 @@ def test_slow_decay_chained_calls():
     x, dt, z = (dev_in(inp[k], "bf16").reshape(1, L, D) for k in ("x", "dt", "z"))
     B, C = (dev_in(inp[k], "bf16").reshape(1, L, 16) for k in ("B", "C"))
     A_t, D_t, b_t = torch.from_numpy(A).to(DEV), torch.from_numpy(inp["D"]).to(DEV), torch.from_numpy(bias).to(DEV)
-    y1, h1 = S.scan_fwd(x, dt, z, B, C, A_t, D_t, b_t, y_dtype=torch.float32, time_slices=8)
+    y1, h1 = S.scan_fwd(x, dt, z, B, C, A_t, D_t, b_t, y_dtype=torch.float32, time_slices=8, lanes_per_channel=lanes)
     h = None
     ys = []
     n = L // parts
@@ -160,7 +167,7 @@ def test_slow_decay_chained_calls():
         sl = slice(i * n, (i + 1) * n)
         yi, h = S.scan_fwd(x[:, sl].contiguous(), dt[:, sl].contiguous(), z[:, sl].contiguous(),
                            B[:, sl].contiguous(), C[:, sl].contiguous(), A_t, D_t, b_t, h0=h,
-                           y_dtype=torch.float32, time_slices=8)
+                           y_dtype=torch.float32, time_slices=8, lanes_per_channel=lanes)
         ys.append(yi)
     torch.cuda.synchronize()
     assert torch.equal(torch.cat(ys, 1), y1) and torch.equal(h, h1)
@@ -194,14 +201,16 @@ def test_varlen_small_with_empty_sequences():
     x, dt, z = (dev_in(inp[k], "bf16") for k in ("x", "dt", "z"))
     B, C = (dev_in(inp[k], "bf16") for k in ("B", "C"))
     A, Dv, bias = (torch.from_numpy(inp[k]).to(DEV) for k in ("A", "D", "dt_bias"))
-    for ts in (0, 1, 4, 16):
+    for ts, lanes in ((0, 0), (1, 0), (4, 4), (16, 4), (4, 8), (16, 8)):
         y, hl = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=torch.from_numpy(h0).to(DEV),
-                           cu_seqlens=torch.from_numpy(cu).to(DEV), y_dtype=torch.float32, time_slices=ts)
+                           cu_seqlens=torch.from_numpy(cu).to(DEV), y_dtype=torch.float32, time_slices=ts,
+                           lanes_per_channel=lanes)
         torch.cuda.synchronize()
         yo, ho = O.scan_fwd(inp["x_f32"], inp["dt_f32"], inp["z_f32"], inp["B_f32"], inp["C_f32"], inp["A"],
                             inp["D"], inp["dt_bias"], h0=h0, seq_start=cu.astype(np.int64))
-        check_fp32(host(y), yo, "varlen y ts=%d" % ts, cu)
-        check_fp32(host(hl).reshape(len(lens), -1), ho.reshape(len(lens), -1), "varlen h_last ts=%d" % ts)
+        check_fp32(host(y), yo, "varlen y ts=%d lanes=%d" % (ts, lanes), cu)
+        check_fp32(host(hl).reshape(len(lens), -1), ho.reshape(len(lens), -1),
+                   "varlen h_last ts=%d lanes=%d" % (ts, lanes))
         assert np.array_equal(host(hl)[0], h0[0]) and np.array_equal(host(hl)[4], h0[4])
 
 

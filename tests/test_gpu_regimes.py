@@ -67,11 +67,11 @@ def with_dt(inp, bits, f32):
 # --------------------------------------------------------------------------- #
 # large Δ: prefill, decode step, backward, grouped prefill
 # --------------------------------------------------------------------------- #
-@pytest.mark.parametrize("ts", [1, 8, 16])
+@pytest.mark.parametrize("ts,lanes", [(1, 0), (8, 4), (16, 4), (8, 8), (16, 8)])
 @pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
-def test_large_delta_prefill(ts, in_dtype):
+def test_large_delta_prefill(ts, lanes, in_dtype):
     batch, L, D = 2, 700, 48
-    say("case: large-delta prefill slices=%d in=%s" % (ts, in_dtype))
+    say("case: large-delta prefill slices=%d lanes=%d in=%s" % (ts, lanes, in_dtype))
     rows = batch * L
     inp = I.make_fwd_inputs_np(5, rows, D, in_dtype=in_dtype)
     inp = with_dt(inp, *large_dt(51, (rows, D), in_dtype))
@@ -83,7 +83,7 @@ def test_large_delta_prefill(ts, in_dtype):
     B, C = (dev_in(inp[k], in_dtype).reshape(batch, L, 16) for k in ("B", "C"))
     A, Dv, bias = (torch.from_numpy(inp[k]).to(DEV) for k in ("A", "D", "dt_bias"))
     y, hl = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=torch.from_numpy(h0).to(DEV), y_dtype=torch.float32,
-                       time_slices=ts)
+                       time_slices=ts, lanes_per_channel=lanes)
     torch.cuda.synchronize()
     yo, ho = O.scan_fwd(inp["x_f32"].reshape(shp), inp["dt_f32"].reshape(shp), inp["z_f32"].reshape(shp),
                         inp["B_f32"].reshape(batch, L, 16), inp["C_f32"].reshape(batch, L, 16), inp["A"], inp["D"],
@@ -171,10 +171,10 @@ def test_large_delta_groups(N):
 # --------------------------------------------------------------------------- #
 # memoryless limit: Ā -> 0, closed form
 # --------------------------------------------------------------------------- #
-@pytest.mark.parametrize("ts", [1, 8, 16])
-def test_memoryless_limit_closed_form(ts):
+@pytest.mark.parametrize("ts,lanes", [(1, 0), (8, 4), (16, 4), (8, 8), (16, 8)])
+def test_memoryless_limit_closed_form(ts, lanes):
     batch, L, D = 2, 500, 32
-    say("case: memoryless limit slices=%d" % ts)
+    say("case: memoryless limit slices=%d lanes=%d" % (ts, lanes))
     rows = batch * L
     inp = I.make_fwd_inputs_np(9, rows, D, in_dtype="bf16")
     bits = I.bf16_bits_from_f32(np.full((rows, D), 50.0, np.float32))
@@ -186,7 +186,7 @@ def test_memoryless_limit_closed_form(ts):
     B, C = (dev_in(inp[k], "bf16").reshape(batch, L, 16) for k in ("B", "C"))
     A, Dv, bias = (torch.from_numpy(inp[k]).to(DEV) for k in ("A", "D", "dt_bias"))
     y, hl = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=torch.from_numpy(h0).to(DEV), y_dtype=torch.float32,
-                       time_slices=ts)
+                       time_slices=ts, lanes_per_channel=lanes)
     torch.cuda.synchronize()
     delta = np.log1p(np.exp(50.0 + inp["dt_bias"].astype(np.float64)))       # [D], >= 43
     xv = inp["x_f32"].reshape(shp).astype(np.float64)
