@@ -1758,8 +1758,10 @@ int slice_tokens8(int) { return kK8; }
 
 // lanes: 0 (choose), 4 or 8 lanes per channel; ckpt: checkpoints requested (the 8-lane kernel has none).
 // Automatic choice: the quad kernel's plan, unless it splits time and its (sequence, 16-channel tile)
-// workgroups would not exceed the CUs; then 8-channel tiles double the workgroups (twice the CUs busy, or
-// two independent workgroups per CU) at the same work per (token, channel).
+// workgroups would leave at least half of the CUs idle; then 8-channel tiles double the workgroups at the
+// same work per (token, channel).  (With one 16-wave workgroup per CU already, two 8-channel workgroups
+// per CU measured slower than the 4-lane kernel: its instructions per (token, channel) are the same, its
+// memory rows half as wide.)
 samba_status make_fwd_plan(const void* x, const void* dt, const void* z, const void* B, const void* C, const float* A,
                            const float* D, const float* bias, const float* h0, const int32_t* cu, int64_t nseq,
                            int32_t batch, int32_t seqlen, int32_t dim, int ts, int lanes, bool ckpt, FwdPlan* plan) {
@@ -1769,7 +1771,7 @@ samba_status make_fwd_plan(const void* x, const void* dt, const void* z, const v
     lanes = 4;
     const int Wq = ts ? ts : choose_time_slices(nseq, ntiles16, tokens, 16, slice_tokens);
     const int W8 = ts ? ts : choose_time_slices(nseq, ntiles8, tokens, 16, slice_tokens8);
-    if (!ckpt && Wq >= 2 && W8 >= 2 && nseq * ntiles16 <= device_cu_count()) lanes = 8;
+    if (!ckpt && Wq >= 2 && W8 >= 2 && 2 * nseq * ntiles16 <= device_cu_count()) lanes = 8;
   }
   if (lanes == 8 && (ckpt || ts == 1)) return SAMBA_ERR_UNSUPPORTED;
   const int ntiles = lanes == 8 ? ntiles8 : ntiles16;

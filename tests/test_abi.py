@@ -223,11 +223,11 @@ def test_step_empty_batch_is_noop(lib):
 # launch plan (host logic; falls back to 256 CUs when no device is visible)
 # --------------------------------------------------------------------------- #
 def test_plan_low_parallelism_splits_time(lib):
-    """One long sequence: 8-channel tiles (512 workgroups, two per CU) of 8 slices of 16 tokens."""
+    """One long sequence of 4096 channels: one 16-wave workgroup per 16-channel tile (256 on 256 CUs)."""
     a = fwd_ok(batch=1, seqlen=16384, dim=4096)
-    assert plan(lib, a, True) == (0, 8, 512, 512, 8)
-    a.lanes_per_channel = 4     # the 16-channel-tile kernel: one 16-wave workgroup per tile
     assert plan(lib, a, True) == (0, 16, 256, 1024, 4)
+    a.lanes_per_channel = 8     # forced: 8-channel tiles, two 8-wave workgroups per CU
+    assert plan(lib, a, True) == (0, 8, 512, 512, 8)
 
 
 def test_plan_half_gpu_shape_uses_eight_lanes(lib):
