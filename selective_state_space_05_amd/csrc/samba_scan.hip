@@ -14,19 +14,23 @@
 // fp32, so the per-lane work is only the recurrence itself.  The per-token
 // scalar work of a channel (softplus, skip, gate, conversions, load and store)
 // is spread over the quad: lane g of a quad owns tokens t with t % 4 == g of
-// each group of four, and broadcasts Δ and Δx to its quad with DPP.  The four
-// lanes' partial readouts are summed with a transposed quad reduction so that
-// each lane ends with the finished y of its own token.
+// each group of four, and shares Δ and Δx with its quad through LDS.  The four
+// lanes' partial readouts are summed with a transposed quad reduction (through
+// LDS in the sequential kernel, in registers with DPP in the time-split one) so
+// that each lane ends with the finished y of its own token.
 //
 // Prefill parallelism: (sequence x 16-channel tile) workgroups; when that is
 // too few to fill 256 CUs, W waves of a workgroup split each time chunk of
-// W*16 tokens into W slices.  Each wave runs its slice from a zero state,
+// W*8 tokens into W slices of 8 tokens.  Each wave runs its slice from a zero state,
 // keeping every Ā and B̄x it computed in registers and publishing the slice's
 // (product of Ā, local end state) pair through LDS; after one barrier each
 // wave folds its predecessors' pairs into its carry-in and replays the slice
-// from the registers (two FMAs per state and token, no second exp).  The carry
-// between chunks goes through LDS as well.  No state crosses workgroups, so no
-// workspace and no inter-workgroup synchronisation is needed.
+// from the registers (two FMAs per state and token, no second exp).  The
+// carry-ins come from up to four fold waves between two barriers; the chunk
+// carry stays in the fold threads' registers.  With very few (sequence, tile)
+// pairs a variant with 8 lanes per channel (8-channel tiles) doubles the
+// workgroups.  No state crosses workgroups, so no workspace and no
+// inter-workgroup synchronisation is needed.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -641,7 +645,8 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
         }
         if constexpr (!kCkpt) {
           if (4 * j < nv) {
-            const float yraw = quad_transpose_sum_lds(s_red[wave], L.c, L.g, pr[0], pr[1], pr[2], pr[3]);
+            // (in registers: measured faster here than the LDS transposed sum the sequential path uses)
+            const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
             store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
           }
         }
@@ -2222,7 +2227,9 @@ const char* samba_status_string(int status) {
     case SAMBA_ERR_UNSUPPORTED: return "unsupported configuration (dstate must be 16; time_slices 0/1/2/4/8/16)";
     case SAMBA_ERR_BAD_STRUCT: return "argument struct size mismatch (header/library version skew)";
     case SAMBA_ERR_HIP: return "HIP runtime error at launch";
-    case SAMBA_ERR_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
+    case SAMBA_ERR_WORKSPACE:
+      return "workspace NULL, too small or not 256-byte aligned (no-allocation entry: needs more than its static "
+             "scratch)";
     default: return "unknown status";
   }
 }
