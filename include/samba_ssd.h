@@ -75,6 +75,22 @@ samba_status samba_ssd_workspace_size(const samba_ssd_args* args, size_t* bytes)
 
 samba_status samba_ssd_fwd(const samba_ssd_args* args, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): samba_ssd_fwd with the C Bᵀ tiles in a static scratch array of
+ * SAMBA_SSD_SCRATCH_BYTES that the library holds on each GPU it runs on (until the process ends), instead
+ * of a caller workspace.  Same arguments, results bit for bit those of samba_ssd_fwd; args->workspace and
+ * workspace_bytes are ignored.  A call whose samba_ssd_workspace_size() exceeds SAMBA_SSD_SCRATCH_BYTES
+ * (16 MiB: 1365 chunk slots x groups of 12 KiB, e.g. 87,360 tokens with one group) is refused with
+ * SAMBA_ERR_WORKSPACE before anything is enqueued.  The call allocates nothing: on its first use on a
+ * device it looks up that device's copy of the array (SAMBA_ERR_HIP if that fails).  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller.  The array needs no clearing: each call writes every tile it
+ * reads before reading it.
+ */
+#define SAMBA_SSD_SCRATCH_BYTES (16u << 20)
+samba_status samba_ssd_fwd_noalloc(const samba_ssd_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

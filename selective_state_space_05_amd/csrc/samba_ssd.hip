@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "samba_ssd.h"
@@ -723,7 +724,46 @@ extern "C" samba_status samba_ssd_workspace_size(const samba_ssd_args* a, size_t
   return SAMBA_OK;
 }
 
-extern "C" samba_status samba_ssd_fwd(const samba_ssd_args* a, void* stream) {
+namespace {
+
+// Scratch of the no-allocation entry point: a file-scope device array, one copy per GPU, holding the
+// C Bᵀ tiles that samba_ssd_fwd writes into the caller's workspace.  Host code never passes the array's
+// name to a kernel (on the host it is a stand-in, not a device address): it uses the address that
+// hipGetSymbolAddress returned for the device, kept per device below.
+constexpr size_t kSsdScratchBytes = SAMBA_SSD_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kSsdScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch array's device address on the current device, looked up once per device (with that device
+// current) and kept; nullptr if the lookup fails.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_addr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
+}
+
+// The prefill with the C Bᵀ tiles in `ws` (ws_bytes usable), which is either the caller's workspace
+// (samba_ssd_fwd) or this device's scratch array (samba_ssd_fwd_noalloc).
+samba_status ssd_fwd_impl(const samba_ssd_args* a, void* ws, size_t ws_bytes, bool caller_ws, void* stream) {
   Plan pl;
   const samba_status st0 = plan_ssd(a, &pl);
   if (st0 != SAMBA_OK) return st0;
@@ -737,8 +777,7 @@ extern "C" samba_status samba_ssd_fwd(const samba_ssd_args* a, void* stream) {
       !aligned(a->h_last, 16) || !aligned(a->z, 8) || !aligned(a->y, 4 * oe) || !aligned(a->dt, 2) ||
       !aligned(a->A, 4) || !aligned(a->D, 4) || !aligned(a->dt_bias, 4))
     return SAMBA_ERR_MISALIGNED;
-  if (pl.ws_bytes > 0 && (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned(a->workspace, 256)))
-    return SAMBA_ERR_WORKSPACE;
+  if (pl.ws_bytes > 0 && (!ws || ws_bytes < pl.ws_bytes || !aligned(ws, 256))) return SAMBA_ERR_WORKSPACE;
   const size_t thp = static_cast<size_t>(tokens) * a->heads * kP;
   const size_t tbc = static_cast<size_t>(tokens) * a->ngroups * N * 2;
   const size_t st = static_cast<size_t>(pl.nseq) * a->heads * kP * N * 4;
@@ -750,16 +789,16 @@ extern "C" samba_status samba_ssd_fwd(const samba_ssd_args* a, void* stream) {
     if (overlap(a->y, thp * oe, ins[k], in_sz[k])) return SAMBA_ERR_ALIASING;
     if (a->h_last && !(k == 8 && a->h_last == a->h0) && overlap(a->h_last, st, ins[k], in_sz[k]))
       return SAMBA_ERR_ALIASING;
-    if (overlap(a->workspace, pl.ws_bytes, ins[k], in_sz[k])) return SAMBA_ERR_ALIASING;
+    if (caller_ws && overlap(ws, pl.ws_bytes, ins[k], in_sz[k])) return SAMBA_ERR_ALIASING;
   }
   if (overlap(a->y, thp * oe, a->h_last, st)) return SAMBA_ERR_ALIASING;
-  if (overlap(a->workspace, pl.ws_bytes, a->y, thp * oe) || overlap(a->workspace, pl.ws_bytes, a->h_last, st))
+  if (caller_ws && (overlap(ws, pl.ws_bytes, a->y, thp * oe) || overlap(ws, pl.ws_bytes, a->h_last, st)))
     return SAMBA_ERR_ALIASING;
 
   SsdParams p{};
   p.x = a->x; p.dt = a->dt; p.z = a->z; p.B = a->B; p.C = a->C;
   p.A = a->A; p.Dskip = a->D; p.bias = a->dt_bias; p.h0 = a->h0; p.h_last = a->h_last; p.y = a->y;
-  p.ws = static_cast<float*>(a->workspace);
+  p.ws = static_cast<float*>(ws);
   p.cu = a->cu_seqlens;
   p.nseq = static_cast<int32_t>(pl.nseq);
   p.seqlen = a->seqlen;
@@ -783,4 +822,25 @@ extern "C" samba_status samba_ssd_fwd(const samba_ssd_args* a, void* stream) {
                 : launch_ssd<float, 128>(p, gate, split, nslots, nblocks, s);
   }
   return e == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" samba_status samba_ssd_fwd(const samba_ssd_args* a, void* stream) {
+  if (!a) return SAMBA_ERR_NULL_ARG;
+  return ssd_fwd_impl(a, a->workspace, a->workspace_bytes, true, stream);
+}
+
+extern "C" samba_status samba_ssd_fwd_noalloc(const samba_ssd_args* a, void* stream) {
+  Plan pl;
+  const samba_status st = plan_ssd(a, &pl);
+  if (st != SAMBA_OK) return st;
+  if (pl.nseq == 0) return SAMBA_OK;
+  if (pl.ws_bytes > kSsdScratchBytes) return SAMBA_ERR_WORKSPACE;   // beyond the static scratch: refused
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    ws = scratch_address();
+    if (!ws) return SAMBA_ERR_HIP;
+  }
+  return ssd_fwd_impl(a, ws, kSsdScratchBytes, false, stream);
 }

@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "SAMBA_OK", 1: "SAMBA_ERR_NULL_ARG", 2: "SAMBA_ERR_BAD_SHAPE"
 EXPORTED = ("samba_scan_fwd", "samba_scan_step", "samba_scan_fwd_plan", "samba_scan_bwd",
             "samba_scan_bwd_workspace_size", "samba_scan_ckpt_bytes", "samba_proj", "samba_status_string",
             "samba_scan_abi_version", "samba_rope", "samba_swa_fwd", "samba_swa_decode", "samba_scan_fwd_groups",
-            "samba_scan_step_groups", "samba_ssd_fwd", "samba_ssd_workspace_size",
+            "samba_scan_step_groups", "samba_ssd_fwd", "samba_ssd_workspace_size", "samba_ssd_fwd_noalloc",
             "samba_gla_fwd", "samba_gla_workspace_size")
 
 _P = ctypes.c_void_p

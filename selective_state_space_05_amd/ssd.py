@@ -41,6 +41,8 @@ def load_library(path=None):
         lib.samba_ssd_fwd.restype = ctypes.c_int
         lib.samba_ssd_workspace_size.argtypes = [ctypes.POINTER(SsdArgs), ctypes.POINTER(ctypes.c_size_t)]
         lib.samba_ssd_workspace_size.restype = ctypes.c_int
+        lib.samba_ssd_fwd_noalloc.argtypes = [ctypes.POINTER(SsdArgs), _P]
+        lib.samba_ssd_fwd_noalloc.restype = ctypes.c_int
         _bound.add(id(lib))
     return lib
 
@@ -111,4 +113,22 @@ def ssd_fwd(x, dt, B, C, A, D, dt_bias, *, z=None, h0=None, h_last=None, y=None,
     del ws   # torch reuses the freed block only for later work on this stream, which runs after the call
     if st != 0:
         raise SambaError(st, "samba_ssd_fwd")
+    return y, h_last
+
+
+SCRATCH_BYTES = 16 << 20   # SAMBA_SSD_SCRATCH_BYTES
+
+
+def ssd_fwd_noalloc(x, dt, B, C, A, D, dt_bias, *, z=None, h0=None, h_last=None, y=None, cu_seqlens=None,
+                    stream=None):
+    """samba_ssd_fwd_noalloc: as ssd_fwd, but the library's static per-GPU scratch holds the C Bᵀ tiles
+    (no workspace; calls needing more than SCRATCH_BYTES are refused).  y and h_last must be given here
+    (this wrapper allocates nothing either)."""
+    _check_dev(x, dt, z, B, C, A, D, dt_bias, h0, h_last, y, cu_seqlens)
+    if y is None:
+        raise ValueError("ssd_fwd_noalloc takes a preallocated y")
+    a = fwd_args(x, dt, B, C, A, D, dt_bias, y=y, z=z, h0=h0, h_last=h_last, cu_seqlens=cu_seqlens)
+    st = load_library().samba_ssd_fwd_noalloc(ctypes.byref(a), _P(_stream_handle(stream)))
+    if st != 0:
+        raise SambaError(st, "samba_ssd_fwd_noalloc")
     return y, h_last

@@ -1,0 +1,71 @@
+"""The SSD prefill's no-allocation entry point (samba_ssd_fwd_noalloc, include/samba_ssd.h) against
+samba_ssd_fwd with a caller workspace: bit for bit, on two calls in a row (the second smaller, so that
+it runs over the scratch the first one left), and the refusal of a call that needs more scratch than the
+static array holds (checked on the host, nothing enqueued)."""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from selective_state_space_05_amd import inputs as I
+from selective_state_space_05_amd import ssd as SD
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def case(cfg, lengths, heads, G, N, gate, y_dtype):
+    T = int(sum(lengths))
+    inp = I.make_ssd_inputs_np(cfg, T, heads, G, N)
+    x, z, dt, B, C = (bf(inp[k]) for k in ("x", "z", "dt", "B", "C"))
+    A, D, bias = (torch.from_numpy(np.asarray(inp[k], dtype=np.float32)).to(DEV) for k in ("A", "D", "dt_bias"))
+    cu = torch.from_numpy(I.cu_from_lengths(lengths)).to(DEV) if len(lengths) > 1 else None
+    h0 = torch.from_numpy(I.make_ssd_h0(cfg, len(lengths), heads, N, scale=0.5)).to(DEV)
+    return dict(x=x, dt=dt, B=B, C=C, A=A, D=D, dt_bias=bias, z=z if gate else None, h0=h0, cu=cu, T=T,
+                heads=heads, N=N, y_dtype=y_dtype)
+
+
+def run_both(c):
+    kw = dict(z=c["z"], h0=c["h0"], cu_seqlens=c["cu"])
+    args = (c["x"], c["dt"], c["B"], c["C"], c["A"], c["D"], c["dt_bias"])
+    y1, h1 = SD.ssd_fwd(*args, y_dtype=c["y_dtype"], **kw)
+    y2 = torch.empty_like(y1)
+    h2 = torch.empty_like(h1)
+    SD.ssd_fwd_noalloc(*args, y=y2, h_last=h2, **kw)
+    torch.cuda.synchronize()
+    return (y1, h1), (y2, h2)
+
+
+def test_noalloc_matches_workspace_entry_twice():
+    # first call: 4 x 1024 tokens, 8 heads, 2 groups of 128 states (scratch 4 * 16 * 2 * 12 KiB = 1.5 MiB)
+    big = case(30, (1024, 1024, 1024, 1024), 8, 2, 128, True, torch.float32)
+    say("case: noalloc big", big["T"], "tokens")
+    (y1, h1), (y2, h2) = run_both(big)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    # second, smaller call right after: packed ragged sequences, one group of 64 states, bf16 y
+    small = case(31, (130, 0, 77, 1), 4, 1, 64, False, torch.bfloat16)
+    say("case: noalloc small", small["T"], "tokens")
+    (y1, h1), (y2, h2) = run_both(small)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    assert torch.isfinite(y2.float()).all() and torch.isfinite(h2).all()
+
+
+def test_noalloc_refuses_beyond_scratch():
+    # 16 groups of 128 states over 8192 tokens need 128 slots x 16 groups x 12 KiB = 24 MiB > 16 MiB
+    c = case(32, (8192,), 16, 16, 128, False, torch.float32)
+    a = SD.fwd_args(c["x"], c["dt"], c["B"], c["C"], c["A"], c["D"], c["dt_bias"],
+                    y=torch.empty(c["T"], 16, 64, device=DEV))
+    assert SD.workspace_bytes(a) > SD.SCRATCH_BYTES
+    st = SD.load_library().samba_ssd_fwd_noalloc(ctypes.byref(a), None)
+    assert st == 9   # SAMBA_ERR_WORKSPACE, nothing enqueued
