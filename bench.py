@@ -10,6 +10,11 @@ token, parameters, carry in and out).  The streaming decode (batch 64, D 4096,
 a 2048-token prefill) is reported in the same line under "decode", and the
 backward on the training shape (batch 4 x 4096 tokens, D 4096: gradients of
 every input, forward states recomputed inside the call) under "backward".
+The other prefill configurations (B1 L4096 D2048; a packed 32768-token stream
+of 512..4096-token sequences), the complexity checks (prefill time against L,
+decode-step time against the tokens before it), a decode over 24 independent
+states (384 MiB, beyond the last-level cache) and the measured ALU issue rates
+that give the prefill's ceiling are reported beside them.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
 """
@@ -158,6 +163,21 @@ def read_ssd_traffic():
     if t.get("kernel_source_sha256_16") != ssd_hash():
         return None
     return t.get("ssd", {}).get("bytes_per_launch")
+
+
+RETENTION_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_retention.json"
+
+
+def read_retention_traffic():
+    """HBM bytes per retention call (pre-pass + prefill) from the committed counter runs, if they were taken on
+    this kernel source."""
+    try:
+        t = json.loads(RETENTION_TRAFFIC_FILE.read_text())
+    except Exception:
+        return None
+    if t.get("kernel_source_sha256_16") != ssd_hash():
+        return None
+    return t.get("retention_call", {}).get("bytes_per_call")
 
 
 def read_swa_traffic(part: str):
@@ -682,7 +702,7 @@ def bench_retention(steps: int = 20, warmup: int = 5):
             "steps": steps, "ms_per_call": ms, "tokens_per_s": Bt * L / (ms * 1e-3), "gbs": gbs,
             "mfma_tflops": round(tf, 1), "mfma_frac_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_retention_traffic(),
                          "kernel": "ssd_cb_kernel<%d> + ssd_fwd_kernel<bf16,N=%d,no gate> (one call)" % (N, N),
                          "launch_us": round(ms * 1e3, 2),
                          "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops}}
@@ -945,6 +965,278 @@ def cpu_baseline_swa_decode(seqs: int = 64):
                       "extrapolated to the batch; %.2f s" % (seqs, spent)}
 
 
+# --------------------------------------------------------------------------- #
+# measured ALU ceiling (libsamba_probe.so: issue rates of the instruction forms the prefill is made of)
+# --------------------------------------------------------------------------- #
+PROBE_BLOCKS, PROBE_ITERS = 2048, 2048   # 8 waves per SIMD on 256 CUs, 0.3 to 1 ms per probe launch
+# The prefill's algorithmic operations per (token, channel), by the instruction form that executes them:
+# two-source multiplies (Δ*A and Δx*B per state, and the 11 other plain ops), fused multiply-adds (state
+# update and readout per state), transcendentals (16 exp for Ā, 2 for softplus, 2 for silu).
+PREFILL_MUL_PER_TD, PREFILL_FMA_PER_TD = 32 + (VALU_PER_TD - 64), 32
+
+
+def alu_ceiling():
+    """Issue rates measured on this GPU with the library's build flags, and the prefill ceiling they give:
+    (t, d)/s = 1 / (n_mul / R_mul + n_fma / R_fma + n_trans / R_exp), R in lane operations per second (the
+    faster of the two FMA forms), i.e. perfect issue of exactly the algorithmic operations."""
+    import torch
+    from selective_state_space_05_amd import probe as PR
+    s = torch.cuda.current_stream()
+    out = torch.empty(PROBE_BLOCKS * 256, device="cuda:0")
+    for _ in range(3):   # settle the clocks
+        PR.launch("fmac_vop2", PROBE_BLOCKS, PROBE_ITERS, out, s)
+    rates = {}
+    for kind in PR.KINDS:
+        PR.launch(kind, PROBE_BLOCKS, 64, out, s)
+        ms = _timed(lambda: PR.launch(kind, PROBE_BLOCKS, PROBE_ITERS, out, s), 3, s)
+        instr = PROBE_BLOCKS * 4 * PROBE_ITERS * PR.instructions_per_round(kind)   # wave-wide instructions
+        rates[kind] = {"tlane_ops_per_s": round(instr * 64 / (ms * 1e-3) / 1e12, 2),
+                       "cycles_per_wave_instruction_at_2p4ghz": round(1024 * 2.4e9 * ms * 1e-3 / instr, 2)}
+    r_mul = rates["mul_vop2"]["tlane_ops_per_s"] * 1e12
+    r_fma = max(rates["fmac_vop2"]["tlane_ops_per_s"], rates["fma_vop3"]["tlane_ops_per_s"]) * 1e12
+    r_exp = rates["exp"]["tlane_ops_per_s"] * 1e12
+    td_s = 1.0 / (PREFILL_MUL_PER_TD / r_mul + PREFILL_FMA_PER_TD / r_fma + TRANS_PER_TD / r_exp)
+    per_td = prefill_bytes(16384, 4096) / (16384 * 4096)
+    return {"rates": rates, "probe": "%d workgroups x 256 threads, %d rounds of 16 independent instructions "
+                                     "per thread (32 for VOP3 fma, 80 for the mix)" % (PROBE_BLOCKS, PROBE_ITERS),
+            "prefill_ceiling_td_per_s": td_s, "prefill_ceiling_gbs": td_s * per_td / 1e9,
+            "prefill_ceiling_hbm_frac": td_s * per_td / 1e9 / HBM_PEAK_GBS,
+            "ops_per_td": {"mul": PREFILL_MUL_PER_TD, "fma": PREFILL_FMA_PER_TD, "trans": TRANS_PER_TD},
+            "trans_cost_in_mul_slots": round(r_mul / r_exp, 2),
+            "note": "transcendentals and other VALU ops measured not to overlap (the 4:1 mix costs the sum)"}
+
+
+VALU_COUNTER_FILE = ROOT / "profiles" / "valu_counters_prefill.json"
+
+
+def read_valu_counters():
+    """Executed VALU / transcendental instructions per (token, channel) of the long-prompt prefill kernel from
+    the committed counter run, if it was taken on this kernel source."""
+    try:
+        t = json.loads(VALU_COUNTER_FILE.read_text())
+    except Exception:
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return t.get("forward")
+
+
+# --------------------------------------------------------------------------- #
+# the other prefill configurations, complexity checks, decode over many states
+# --------------------------------------------------------------------------- #
+def _prefill_leg(name, launch_args, td, nbytes, steps, warmup, plan):
+    """Time calls cycling over `launch_args` (one FwdArgs per input set); roofline against the VALU slot
+    peak, GB/s against HBM."""
+    import torch
+    from selective_state_space_05_amd import scan as S
+    lib = S.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    refs = [ctypes.byref(a) for a in launch_args]
+
+    def call(i=[0]):
+        st = lib.samba_scan_fwd(refs[i[0] % len(refs)], sh)
+        i[0] += 1
+        if st != 0:
+            raise S.SambaError(st, "samba_scan_fwd")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = _timed(call, steps, stream)
+    slots = SLOTS_PER_TD * td / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": name, "steps": steps, "ms_per_call": ms, "gbs": gbs, "tokens_channels_per_s": td / (ms * 1e-3),
+            "hbm_frac": gbs / HBM_PEAK_GBS, "input_sets": len(refs),
+            "plan": {"time_slices": plan[0], "workgroups": plan[1], "threads_per_workgroup": plan[2],
+                     "lanes_per_channel": plan[3]},
+            "roofline": {"bound": "alu", "achieved": round(slots, 3), "peak": round(VALU_PEAK_TSLOT, 2),
+                         "unit": "Tslot/s", "frac": round(slots / VALU_PEAK_TSLOT, 4), "traffic": None,
+                         "kernel": kernel_name({"time_slices": plan[0], "lanes_per_channel": plan[3]}),
+                         "algorithmic_bytes_per_launch": nbytes}}
+
+
+def bench_cfg1(steps: int = 40, warmup: int = 8, sets: int = 4):
+    """B1 L4096 D2048, bf16 I/O, y and h_last out.  One call's 67.6 MB fits the 256 MB last-level cache,
+    so the calls cycle over `sets` distinct input sets (270 MB together) and each call reads from HBM."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import scan as S
+    W = I.WORKLOADS[1]
+    L, D = W.seqlen, W.dim
+    dev = torch.device("cuda:0")
+    args, keep = [], []
+    for k in range(sets):
+        inp = I.make_fwd_inputs_torch(1, L, D, dev, tensor_offset=k)
+        y = torch.empty(1, L, D, dtype=torch.bfloat16, device=dev)
+        hl = torch.empty(1, D, 16, device=dev)
+        keep.append((inp, y, hl))
+        args.append(S.fwd_args(*(inp[n].view(1, L, -1) for n in ("x", "dt", "z", "B", "C")), inp["A"], inp["D"],
+                               inp["dt_bias"], y=y, h_last=hl))
+    inp, y, hl = keep[0]
+    plan = S.fwd_plan(*(inp[n].view(1, L, -1) for n in ("x", "dt", "z", "B", "C")), inp["A"], inp["D"], inp["dt_bias"],
+                      y=y, h_last=hl)
+    return _prefill_leg("prefill B1 L4096 D2048 N16 bf16 (y and h_last out)", args, L * D,
+                        prefill_bytes(L, D, h0=False), steps, warmup, plan)
+
+
+def bench_cfg2(steps: int = 10, warmup: int = 3):
+    """Packed variable-length stream: T = 32768 tokens of lengths U(512, 4096), D 4096, bf16, state reset at
+    every sequence start (no h0), one h_last row per sequence."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import scan as S
+    W = I.WORKLOADS[2]
+    T, D = W.varlen_total, W.dim
+    dev = torch.device("cuda:0")
+    lens = I.varlen_lengths(2, T)
+    cu = torch.from_numpy(I.cu_from_lengths(lens)).to(dev)
+    inp = I.make_fwd_inputs_torch(2, T, D, dev)
+    y = torch.empty(T, D, dtype=torch.bfloat16, device=dev)
+    hl = torch.empty(len(lens), D, 16, device=dev)
+    ins = [inp[n] for n in ("x", "dt", "z", "B", "C", "A", "D", "dt_bias")]
+    a = S.fwd_args(*ins, y=y, h_last=hl, cu_seqlens=cu)
+    plan = S.fwd_plan(*ins, y=y, h_last=hl, cu_seqlens=cu)
+    nbytes = prefill_bytes(T, D, h0=False, h_last=False) + len(lens) * D * 16 * 4
+    out = _prefill_leg("prefill packed T=32768 (%d sequences of 512..4096) D4096 N16 bf16, resets at sequence "
+                       "starts" % len(lens), [a], T * D, nbytes, steps, warmup, plan)
+    out["sequences"] = int(len(lens))
+    return out
+
+
+def bench_complexity():
+    """Linear time in L (prefill, one sequence, D 4096, L = 4K / 16K / 64K) and constant time per decode
+    step (B64 D4096: the same steps after a 0-token and after a 2048-token prefill)."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import scan as S
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    D = 4096
+    pre = {}
+    for L in (4096, 16384, 65536):
+        inp = I.make_fwd_inputs_torch(3, L, D, dev)
+        y = torch.empty(1, L, D, dtype=torch.bfloat16, device=dev)
+        ins = [inp[n].view(1, L, -1) for n in ("x", "dt", "z", "B", "C")] + [inp["A"], inp["D"], inp["dt_bias"]]
+        call = lambda: S.scan_fwd(*ins, y=y, return_last_state=False)
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        ms = _timed(call, 5, stream)
+        pre[L] = {"us_per_call": ms * 1e3, "ns_per_token": ms * 1e6 / L,
+                  "plan": S.fwd_plan(*ins, y=y)}
+        del inp, y, ins
+    ref = pre[16384]["ns_per_token"]
+    for L in pre:
+        pre[L]["per_token_vs_16k"] = pre[L]["ns_per_token"] / ref
+    Bt = 64
+    W = I.WORKLOADS[4]
+    p = I.make_fwd_inputs_torch(4, Bt * W.seqlen, D, dev)
+    A, Dv, bias = p["A"], p["D"], p["dt_bias"]
+    _, st2048 = S.scan_fwd(*(p[n].view(Bt, W.seqlen, -1) for n in ("x", "dt", "z", "B", "C")), A, Dv, bias)
+    del p
+    rg = I.make_step_ring_torch(4, 16, Bt, D, dev)
+    ys = torch.empty(Bt, D, dtype=torch.bfloat16, device=dev)
+    dec = {}
+    for name, st in (("after_0_tokens", torch.zeros(Bt, D, 16, device=dev)), ("after_2048_tokens", st2048)):
+        i = [0]
+
+        def step():
+            r = i[0] % 16
+            i[0] += 1
+            S.scan_step(st, rg["x"][r], rg["dt"][r], rg["z"][r], rg["B"][r], rg["C"][r], A, Dv, bias, y=ys)
+
+        for _ in range(32):
+            step()
+        torch.cuda.synchronize()
+        dec[name] = {"us_per_step": _timed(step, 400, stream) * 1e3}
+    dec["ratio"] = dec["after_2048_tokens"]["us_per_step"] / dec["after_0_tokens"]["us_per_step"]
+    return {"prefill_time_vs_L": {str(k): v for k, v in pre.items()}, "decode_step_vs_prior_tokens": dec,
+            "note": "per-token prefill time flat in L means linear time; decode step time independent of the "
+                    "tokens already consumed means a constant-size state (page 1, 推理效率)"}
+
+
+def bench_decode_states(nstates: int = 24, rounds: int = 100):
+    """Decode over `nstates` independent batch-64 states (16 MiB each, 384 MiB together, more than the
+    256 MB last-level cache), step k on state k % nstates, as one token through a stack of layers: every
+    step's state comes from HBM, unlike the single in-place state of the streaming-decode leg."""
+    import torch
+    from selective_state_space_05_amd import inputs as I
+    from selective_state_space_05_amd import scan as S
+    dev = torch.device("cuda:0")
+    Bt, D = 64, 4096
+    p = I.make_params(4, D)
+    A, Dv, bias = (torch.from_numpy(p[k]).to(dev) for k in ("A", "D", "dt_bias"))
+    states = [torch.zeros(Bt, D, 16, device=dev) for _ in range(nstates)]
+    rg = I.make_step_ring_torch(4, nstates, Bt, D, dev)
+    ys = torch.empty(nstates, Bt, D, dtype=torch.bfloat16, device=dev)
+    lib = S.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    args = [S.step_args(states[k], rg["x"][k], rg["dt"][k], rg["z"][k], rg["B"][k], rg["C"][k], A, Dv, bias,
+                        y=ys[k]) for k in range(nstates)]
+    refs = [ctypes.byref(a) for a in args]
+
+    def one_round():
+        for r in refs:
+            if lib.samba_scan_step(r, sh) != 0:
+                raise RuntimeError("samba_scan_step failed")
+
+    for _ in range(3):
+        one_round()
+    torch.cuda.synchronize()
+    us = _timed(one_round, rounds, stream) * 1e3 / nstates
+    gbs = decode_bytes(Bt, D) / (us * 1e-6) / 1e9
+    return {"states": nstates, "state_mib_total": nstates * Bt * D * 16 * 4 / 2 ** 20, "us_per_step": us,
+            "steps_per_s": 1e6 / us, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "scan_step_kernel<bf16,bf16>"}}
+
+
+def cpu_baseline_cfg1():
+    """The oracle on the whole B1 L4096 D2048 call (all host cores)."""
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+    W = I.WORKLOADS[1]
+    L, D = W.seqlen, W.dim
+    lib = O.load()
+    inp = I.make_fwd_inputs_torch(1, L, D, "cpu")
+    P = I.make_params(1, D)
+    arr = [inp[k].double().numpy() for k in ("x", "dt", "z", "B", "C")]
+    t0 = time.perf_counter()
+    O.scan_fwd(*arr, P["A"], P["D"], P["dt_bias"], lib=lib)
+    dt_s = time.perf_counter() - t0
+    return {"value": prefill_bytes(L, D, h0=False) / dt_s / 1e9, "unit": "GB/s", "cores": O.max_threads(lib),
+            "kind": "oracle", "tokens_channels_per_s": L * D / dt_s,
+            "sample": "the whole call (4096 tokens x 2048 channels), %.2f s" % dt_s}
+
+
+def cpu_baseline_cfg2(channels: int = 512):
+    """The oracle on every sequence of the packed stream, over `channels` of the 4096 channels (rate per
+    (token, channel) extrapolates to the whole)."""
+    import numpy as np
+    from oracle import oracle as O
+    from selective_state_space_05_amd import inputs as I
+    W = I.WORKLOADS[2]
+    T, D = W.varlen_total, W.dim
+    lib = O.load()
+    lens = I.varlen_lengths(2, T)
+    ss = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    inp = I.make_fwd_inputs_torch(2, T, D, "cpu")
+    P = I.make_params(2, D)
+    x, dt, z = (inp[k][:, :channels].double().numpy().copy() for k in ("x", "dt", "z"))
+    Bm, Cm = (inp[k].double().numpy() for k in ("B", "C"))
+    t0 = time.perf_counter()
+    O.scan_fwd(x, dt, z, Bm, Cm, P["A"][:channels], P["D"][:channels], P["dt_bias"][:channels], seq_start=ss, lib=lib)
+    dt_s = time.perf_counter() - t0
+    td_s = T * channels / dt_s
+    per_td = (prefill_bytes(T, D, h0=False, h_last=False) + len(lens) * D * 64) / (T * D)
+    return {"value": td_s * per_td / 1e9, "unit": "GB/s", "cores": O.max_threads(lib), "kind": "oracle",
+            "tokens_channels_per_s": td_s,
+            "sample": "all %d sequences (32768 tokens), %d of 4096 channels, %.2f s" % (len(lens), channels, dt_s)}
+
+
 PMC_RUN = ("python3 <repo>/bench.py --steps 1 --warmup 0 --decode-steps 256 --no-cpu --bwd-steps 1 "
            "--proj-steps 1 --copy-probe")
 
@@ -974,6 +1266,8 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
         return keys[0]
 
     sel = {"fwd": ("scan_fwd_kernel", "16, 1, 8, false>"), "step": ("scan_step_kernel<unsigned short, unsigned short",),
+           "cfg1": ("scan_split8_kernel<unsigned short, unsigned short, 16>",),
+           "cfg2": ("scan_fwd_kernel", "unsigned short, 1, 4, 16, false>"),
            "ckpt": ("scan_fwd_kernel", ", true>"), "bwd": ("scan_bwd_kernel<",), "finish": ("scan_bwd_finish_kernel",),
            "proj": ("proj_dma_kernel<unsigned short",)}
     got = {k: {} for k in sel}
@@ -1000,7 +1294,9 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
              "decode_step": entry("step", decode_bytes(64, 4096)),
              "backward": {"kernels": {n: entry(n, None) for n in ("ckpt", "bwd", "finish")},
                           "algorithmic_bytes_per_call": bwd_bytes(4 * 4096, 4096, 4)},
-             "projections": entry("proj", (16384 * 4096 + 4128 * 4096 + 16384 * 4128) * 2)}
+             "projections": entry("proj", (16384 * 4096 + 4128 * 4096 + 16384 * 4128) * 2),
+             "cfg1": entry("cfg1", prefill_bytes(4096, 2048, h0=False)),
+             "cfg2": entry("cfg2", None)}
     out_d["backward"]["bytes_per_call"] = sum(v["bytes_per_launch"] for v in out_d["backward"]["kernels"].values())
     out_d["command"] = [
         f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {PMC_RUN}",
@@ -1017,7 +1313,67 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
 SWA_PMC_RUN = "python3 <repo>/bench.py --swa-only --swa-steps 2 --swa-decode-steps 2 --warmup 1 --copy-probe"
 GROUPS_PMC_RUN = "python3 <repo>/bench.py --groups-only --groups-steps 2 --warmup 1 --copy-probe"
 SSD_PMC_RUN = "python3 <repo>/bench.py --ssd-only --ssd-steps 2 --warmup 1 --copy-probe"
+RETENTION_PMC_RUN = "python3 <repo>/bench.py --retention-only --ssd-steps 2 --warmup 1 --copy-probe"
 GLA_PMC_RUN = "python3 <repo>/bench.py --gla-only --gla-steps 2 --warmup 1 --copy-probe"  # 2 + 1 prefill calls, 220 steps
+
+
+VALU_PMC_RUN = ("python3 <repo>/bench.py --steps 1 --warmup 0 --no-decode --no-cpu --no-bwd --no-proj --no-swa "
+                "--no-groups --no-ssd --no-gla --no-cfg --no-alu --copy-probe")
+VALU_PASSES = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_INSTS_LDS "
+               "SQ_INSTS_SALU SQ_BUSY_CYCLES",
+               "SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS "
+               "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_VALU2")
+
+
+def valu_summary(dir_a: str, dir_b: str, out: str):
+    """Turn the two SQ counter passes (VALU_PASSES, each a rocprofv3 --pmc run of VALU_RUN) into per
+    (token, channel) executed instruction counts of the long-prompt prefill kernel and its wave-time split.
+    Values are medians over that kernel's dispatches; instruction counts are wave-wide (x 64 lanes)."""
+    import csv
+    import glob
+    import statistics
+
+    vals = {}
+    for d in (dir_a, dir_b):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        per = {}
+        for r in csv.DictReader(open(f)):
+            k = r["Kernel_Name"]
+            if "scan_fwd_kernel" in k and "16, 1, 8, false>" in k:
+                per.setdefault((r["Dispatch_Id"], r["Counter_Name"]), 0.0)
+                per[(r["Dispatch_Id"], r["Counter_Name"])] += float(r["Counter_Value"])
+                kernel = k
+        for (disp, c), v in per.items():
+            vals.setdefault(c, []).append(v)
+    med = {c: statistics.median(v) for c, v in vals.items()}
+    td = 16384 * 4096
+    valu = med["SQ_INSTS_VALU"] * 64 / td
+    trans = med["SQ_INSTS_VALU_TRANS_F32"] * 64 / td
+    wc = med["SQ_WAVE_CYCLES"]
+    fw = {"forward": {
+        "kernel": kernel[:120], "dispatches": len(vals["SQ_INSTS_VALU"]), "tokens_channels_per_launch": td,
+        "valu_lane_ops_per_td": round(valu, 2), "trans_lane_ops_per_td": round(trans, 2),
+        "executed_slots_per_td": round(valu - trans + TRANS_SLOTS * trans, 1),
+        "algorithmic_slots_per_td": SLOTS_PER_TD,
+        "lds_wave_instructions_per_td": round(med["SQ_INSTS_LDS"] / td, 4),
+        "salu_wave_instructions_per_td": round(med["SQ_INSTS_SALU"] / td, 4),
+        "wave_time": {"waiting_on_dependencies": round(med["SQ_WAIT_ANY"] / wc, 3),
+                      "issuing": round(med["SQ_ACTIVE_INST_ANY"] / wc, 3),
+                      "waiting_for_issue": round(med["SQ_WAIT_INST_ANY"] / wc, 3),
+                      "valu_active": round(med["SQ_ACTIVE_INST_VALU"] / wc, 3)},
+        "lds_bank_conflict_cycles_over_lds_active": round(med["SQ_LDS_BANK_CONFLICT"] / max(med["SQ_LDS_IDX_ACTIVE"], 1.0),
+                                                          4),
+        "raw_medians": med}}
+    out_d = {"kernel_source_sha256_16": kernel_hash(), **fw}
+    out_d["command"] = [
+        f"cd /tmp && rocprofv3 --pmc {VALU_PASSES[0]} --output-format csv -d <repo>/{dir_a} -o p -- {VALU_PMC_RUN}",
+        f"cd /tmp && rocprofv3 --pmc {VALU_PASSES[1]} --output-format csv -d <repo>/{dir_b} -o p -- {VALU_PMC_RUN}",
+        f"python bench.py --valu-summary {dir_a} {dir_b} {out}"]
+    out_d["note"] = ("SQ_INSTS_VALU counts every VALU instruction (transcendentals included); executed slots count a "
+                     "transcendental as %d, as the algorithmic count does. wave_time fractions are the SQ wave-cycle "
+                     "counters over SQ_WAVE_CYCLES (quad-cycle units cancel)." % TRANS_SLOTS)
+    Path(out).write_text(json.dumps(out_d, indent=1) + "\n")
+    print(json.dumps(out_d))
 
 
 def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
@@ -1074,6 +1430,18 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
         note = ("Algorithmic bytes: x, z read and y written once (bf16), dt, B and C once, parameters, h_last "
                 "out. The workspace of C B^T tiles (3 MiB, written by the small pre-pass kernel and read from L2) "
                 "is not counted in the algorithmic bytes.")
+    elif which == "retention":
+        wl = I.WORKLOADS[11]
+        Bt, L, H, P, N, G = (wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.dstate,
+                             wl.extra["ngroups"])
+        # the retention leg runs the unsplit or split prefill depending on the CU count: match either
+        sel = {"cb": ("ssd_cb_kernel<128>", Bt * L * G * N * 2 * 2),
+               "ssd": ("ssd_fwd_kernel<unsigned short, 128, false",
+                       ssd_bytes(Bt, L, H, P, G, N, gated=False) - Bt * L * G * N * 2 * 2)}
+        src_hash, run, flag = ssd_hash(), RETENTION_PMC_RUN, "--pmc-summary-retention"
+        note = ("Algorithmic bytes: the C B^T pre-pass reads B and C once; the prefill reads x (v) and writes y "
+                "once (bf16), parameters, h_last out.  The pre-pass's C B^T tiles (12 KiB per 64-token chunk and "
+                "group, 101 MB with a group per head) are written and read back, not counted as algorithmic.")
     else:
         wl = I.WORKLOADS[8]
         Bt, L, D, N, G = wl.batch, wl.seqlen, wl.dim, wl.dstate, wl.extra["ngroups"]
@@ -1102,9 +1470,10 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
         out_d[name] = {"kernel": got[name]["FETCH_SIZE"]["kernel"], "grid": got[name]["FETCH_SIZE"]["grid"],
                        "fetch_bytes": f, "write_bytes": wr, "bytes_per_launch": f + wr,
                        "algorithmic_bytes_per_launch": algorithmic}
-    if which == "gla":
-        out_d["gla_call"] = {"bytes_per_call": sum(out_d[k]["bytes_per_launch"] for k in sel),
-                             "algorithmic_bytes_per_call": sum(out_d[k]["algorithmic_bytes_per_launch"] for k in sel)}
+    if which in ("gla", "retention"):
+        out_d[which + "_call"] = {"bytes_per_call": sum(out_d[k]["bytes_per_launch"] for k in sel),
+                                  "algorithmic_bytes_per_call": sum(out_d[k]["algorithmic_bytes_per_launch"]
+                                                                    for k in sel)}
     out_d["command"] = [
         f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/{fetch_dir} -o p -- {run}",
         f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/{write_dir} -o p -- {run}",
@@ -1295,6 +1664,9 @@ def main():
     ap.add_argument("--swa-only", action="store_true",
                     help="run only the attention legs (and the copy probe with --copy-probe): counter runs")
     ap.add_argument("--time-slices", type=int, default=0, help="force the prefill's waves per time chunk (0 = auto)")
+    ap.add_argument("--no-cfg", action="store_true",
+                    help="skip the B1 L4096 D2048 and packed T=32768 prefill legs and the complexity checks")
+    ap.add_argument("--no-alu", action="store_true", help="skip the ALU issue-rate probes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (untimed), the reference kernel for HBM byte counters")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
@@ -1305,11 +1677,18 @@ def main():
                     help="the same for the grouped prefill (counter runs of the --groups-only leg)")
     ap.add_argument("--pmc-summary-ssd", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="the same for the SSD prefill (counter runs of the --ssd-only leg)")
+    ap.add_argument("--valu-summary", nargs=3, metavar=("PASS_A_DIR", "PASS_B_DIR", "OUT"),
+                    help="per-(token, channel) VALU counters of the prefill kernel from the two SQ passes")
+    ap.add_argument("--pmc-summary-retention", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="the same for the retention configuration (counter runs of the --retention-only leg)")
     ap.add_argument("--pmc-summary-gla", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="the same for gated linear attention (counter runs of the --gla-only leg)")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.valu_summary:
+        valu_summary(*args.valu_summary)
         return
     if args.pmc_summary_swa:
         _counter_summary(*args.pmc_summary_swa, which="swa")
@@ -1322,6 +1701,9 @@ def main():
         return
     if args.pmc_summary_gla:
         _counter_summary(*args.pmc_summary_gla, which="gla")
+        return
+    if args.pmc_summary_retention:
+        _counter_summary(*args.pmc_summary_retention, which="retention")
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only (the library has no multi-GPU path); run with --gpus 1",
@@ -1341,7 +1723,10 @@ def main():
         print(json.dumps(out), flush=True)
         return
     if args.retention_only:
-        print(json.dumps({"retention": bench_retention(args.ssd_steps, min(args.warmup, 5))}), flush=True)
+        out = {"retention": bench_retention(args.ssd_steps, min(args.warmup, 5))}
+        if args.copy_probe:
+            copy_probe()
+        print(json.dumps(out), flush=True)
         return
     if args.ssd_only:
         out = {"ssd": bench_ssd(args.ssd_steps, min(args.warmup, 5))}
@@ -1364,6 +1749,9 @@ def main():
         copy_probe()
     achieved = SLOTS_PER_TD * pf["launch_td"] / (pf["launch_ms"] * 1e-3) / 1e12
     traffic = read_traffic()
+    # (counter runs skip the ALU probes and the complexity checks: their launches would mix into the medians)
+    alu = None if (args.no_alu or args.copy_probe) else alu_ceiling()
+    valu = read_valu_counters()
     line = {
         "metric": METRIC,
         "value": round(pf["gbs"], 2),
@@ -1392,13 +1780,35 @@ def main():
                      "launch_us": round(pf["launch_ms"] * 1e3, 2), "slots_per_token_channel": SLOTS_PER_TD,
                      "algorithmic_bytes_per_launch": pf["bytes_per_launch"]},
     }
+    rf = line["roofline"]
+    launch_td_s = pf["launch_td"] / (pf["launch_ms"] * 1e-3)
+    rf["hbm_frac_of_launch"] = round(pf["bytes_per_launch"] / (pf["launch_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    if alu:
+        rf["measured_ceiling_td_per_s"] = alu["prefill_ceiling_td_per_s"]
+        rf["frac_of_measured_ceiling"] = round(launch_td_s / alu["prefill_ceiling_td_per_s"], 4)
+        line["alu_ceiling"] = alu
+    if valu:
+        rf["executed_per_td"] = {k: valu[k] for k in ("valu_lane_ops_per_td", "trans_lane_ops_per_td",
+                                                       "executed_slots_per_td") if k in valu}
+        rf["executed_over_algorithmic_slots"] = round(valu["executed_slots_per_td"] / SLOTS_PER_TD, 3)
     if not args.no_decode:
         dec = bench_decode(args.decode_steps)
         dec["roofline"] = {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4), "traffic": read_traffic("decode_step"),
                            "kernel": "scan_step_kernel<bf16,bf16>"}
         dec["copy_frac"] = dec["gbs"] / ceiling if ceiling else None
+        dec["note"] = ("one 16 MiB state read and written in place by every step: it stays in the 256 MB last-level "
+                       "cache, so these bytes are cache-assisted; decode_many_states is the HBM-bound variant")
         line["decode"] = dec
+    if not args.no_decode and not args.copy_probe:
+        line["decode_many_states"] = bench_decode_states()
+    if not args.no_cfg:
+        line["cfg1"] = bench_cfg1()
+        line["cfg1"]["roofline"]["traffic"] = read_traffic("cfg1")
+        line["cfg2"] = bench_cfg2()
+        line["cfg2"]["roofline"]["traffic"] = read_traffic("cfg2")
+        if not args.copy_probe:
+            line["complexity"] = bench_complexity()
     if not args.no_proj:
         line["projections"] = bench_proj(args.proj_steps)
         line["projections"]["roofline"]["traffic"] = read_traffic("projections")
@@ -1421,6 +1831,9 @@ def main():
         line["cpu_baseline"] = cpu_baseline()
         if not args.no_decode:
             line["cpu_baseline"]["decode"] = cpu_baseline_decode()
+        if not args.no_cfg:
+            line["cpu_baseline"]["cfg1"] = cpu_baseline_cfg1()
+            line["cpu_baseline"]["cfg2"] = cpu_baseline_cfg2()
         if not args.no_bwd:
             line["cpu_baseline"]["backward"] = cpu_baseline_backward()
         if not args.no_proj:
