@@ -58,5 +58,31 @@ def build(out: Path = LIB, extra=(), probe: bool = True) -> Path:
     return out
 
 
+# Host-side sanitizers only: the device code is built as usual; -Xarch_host applies each flag to the host
+# compilation (validation, launch plans, the C ABI), which the ABI tests then exercise.
+SANITIZER_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libasan"]
+
+
+def asan_runtime() -> Path:
+    """The clang AddressSanitizer runtime a process must preload to load the sanitized library."""
+    cands = sorted(Path("/opt/rocm/llvm/lib/clang").glob("*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not cands:
+        raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under /opt/rocm/llvm/lib/clang")
+    return cands[-1]
+
+
+def build_sanitized(out: Path) -> Path:
+    """libsamba_scan.so with AddressSanitizer and UndefinedBehaviorSanitizer on its host code, at `out`."""
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + SANITIZER_FLAGS
+    tmp = Path(out).with_suffix(".so.tmp%d" % os.getpid())
+    cmd = [hipcc(), *flags, "-I", str(ROOT / "include"), "-o", str(tmp), *(str(p) for p in SRCS)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+    os.replace(tmp, out)
+    return Path(out)
+
+
 if __name__ == "__main__":
     print(build(), file=sys.stderr)

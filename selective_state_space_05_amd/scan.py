@@ -83,13 +83,17 @@ class SambaError(RuntimeError):
 
 
 _lib = None
+_libs_by_path = {}
 
 
 def load_library(path: Path | str | None = None):
-    """Load libsamba_scan.so; raises (no fallback) if it is absent or stale."""
+    """Load libsamba_scan.so (or the library at `path`, one shared handle per path, so that the other
+    bindings' signatures land on the same object); raises (no fallback) if it is absent or stale."""
     global _lib
     if _lib is not None and path is None:
         return _lib
+    if path is not None and str(Path(path).resolve()) in _libs_by_path:
+        return _libs_by_path[str(Path(path).resolve())]
     p = Path(path) if path is not None else LIB_PATH
     if not p.exists():
         raise ImportError("libsamba_scan.so not built at %s: run __graft_entry__.build() or "
@@ -121,6 +125,8 @@ def load_library(path: Path | str | None = None):
         raise ImportError("libsamba_scan.so ABI %d != binding ABI %d" % (lib.samba_scan_abi_version(), ABI_VERSION))
     if path is None:
         _lib = lib
+    else:
+        _libs_by_path[str(Path(path).resolve())] = lib
     return lib
 
 

@@ -5,6 +5,7 @@ returns its documented status here without a device.  Pointers are fake,
 never-dereferenced addresses.
 """
 import ctypes
+import os
 import re
 import subprocess
 from pathlib import Path
@@ -22,11 +23,15 @@ PROBE_HEADER = ROOT / "include" / "samba_probe.h"
 HEADERS = sorted(h for h in (ROOT / "include").glob("*.h") if h != PROBE_HEADER)
 
 
+# tests/test_abi_sanitized.py runs this file against a host-sanitized build of the library
+LIB_OVERRIDE = os.environ.get("SAMBA_ABI_TEST_LIBRARY")
+
+
 @pytest.fixture(scope="module")
 def lib():
-    D.load_library()
-    GL.load_library()
-    return W.load_library()
+    D.load_library(LIB_OVERRIDE)
+    GL.load_library(LIB_OVERRIDE)
+    return W.load_library(LIB_OVERRIDE)
 
 
 def header_functions(headers=HEADERS):
