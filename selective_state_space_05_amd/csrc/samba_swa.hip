@@ -300,21 +300,14 @@ __global__ __launch_bounds__(kSwaThreads, 1) void swa_fwd_kernel(SwaParams p) {
   const bool wave_live = q_lo < len;
   const int q_hi = wave_live ? ((len - q_lo) < 32 ? len - 1 : q_lo + 31) : q_lo;
   const int qp = q_lo + ql;   // this lane's query
-  // q fragments, multiplied by log2(e) / sqrt(head size) and rounded to bf16: scores come out in exp2 units
+  // q fragments as stored (bf16): the scale log2(e) / sqrt(head size) is applied to the fp32 scores
   bf16x8_t qf[8];
   {
     const rsrc_t rq = rsrc_rows(p.q + (sb.t0 + q_lo) * p.heads * kHD + head_off, wave_live ? q_hi - q_lo + 1 : 0,
                                 row_bytes);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const uint4 w = ld16(rq, static_cast<uint32_t>(ql) * row_bytes + (16 * jj + 8 * hf) * 2);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qf[jj][2 * i] = static_cast<__bf16>(bf_lo(ws[i]) * p.c);
-        qf[jj][2 * i + 1] = static_cast<__bf16>(bf_hi(ws[i]) * p.c);
-      }
-    }
+    for (int jj = 0; jj < 8; ++jj)
+      qf[jj] = __builtin_bit_cast(bf16x8_t, ld16(rq, static_cast<uint32_t>(ql) * row_bytes + (16 * jj + 8 * hf) * 2));
   }
 
   // staging: waves 4..7 load K (rows sr + 16 r, 16-byte group sg), waves 0..3 load V (keys 4 sr .. 4 sr + 3,
@@ -374,27 +367,33 @@ __global__ __launch_bounds__(kSwaThreads, 1) void swa_fwd_kernel(SwaParams p) {
   for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[hb][e] = 0.f;
-  // Softmax reference per lane (exp2 units): the scores of a tile are formed relative to it (the MFMA
-  // accumulators start at -m_ref), and it is moved only when a score exceeds it by more than kRescale (or
+  // Softmax reference per lane (exp2 units): the scores of a tile are formed relative to it (scaled score
+  // minus m_ref, one fp32 fma each), and it is moved only when a score exceeds it by more than kRescale (or
   // before the lane has seen any key), so the rescaling of the output is rare.  Any reference gives the same
   // result once the output is divided by the sum; keeping the maximum within 2^kRescale of it bounds the
   // probabilities by 2^kRescale and keeps the largest one >= 1.
   float m_ref = -INFINITY, l_run = 0.f;
-  f32x16_t cneg;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) cneg[e] = 0.f;
+  float mneg = 0.f;   // -m_ref, or 0 before the first key
+  const float sc = p.c;
 
   auto compute = [&](auto bufc, int kt, bool need_mask) {
     constexpr int buf = decltype(bufc)::value;
     const uint16_t* K = sK[buf];
     const uint16_t* Vt = sV[buf];
-    f32x16_t s0 = cneg, s1 = cneg;
+    f32x16_t s0, s1;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s0[e] = s1[e] = 0.f;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(K + kbase + 16 * jj);
       const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(K + kbase + 32 * kKRow + 16 * jj);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[jj], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[jj], s1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {   // exp2 units, relative to the reference
+      s0[e] = fmaf(s0[e], sc, mneg);
+      s1[e] = fmaf(s1[e], sc, mneg);
     }
     if (need_mask) {   // visible iff 0 <= query - key <= window
       // (the tile's first key through readfirstlane: an opaque value, so that the compiler does not keep 32
@@ -439,8 +438,8 @@ __global__ __launch_bounds__(kSwaThreads, 1) void swa_fwd_kernel(SwaParams p) {
       for (int e = 0; e < 16; ++e) {
         s0[e] += delta;
         s1[e] += delta;
-        cneg[e] = -m_use;
       }
+      mneg = -m_use;
       l_run *= alpha;
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb)
@@ -448,14 +447,11 @@ __global__ __launch_bounds__(kSwaThreads, 1) void swa_fwd_kernel(SwaParams p) {
         for (int e = 0; e < 16; ++e) acc[hb][e] *= alpha;
       m_ref = m_new;
     }
-    float rs = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       s0[e] = __builtin_amdgcn_exp2f(s0[e]);
       s1[e] = __builtin_amdgcn_exp2f(s1[e]);
-      rs += s0[e] + s1[e];
     }
-    l_run += rs;
     bf16x8_t pf[4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -463,6 +459,18 @@ __global__ __launch_bounds__(kSwaThreads, 1) void swa_fwd_kernel(SwaParams p) {
       pf[1][i] = static_cast<__bf16>(s0[8 + i]);
       pf[2][i] = static_cast<__bf16>(s1[i]);
       pf[3][i] = static_cast<__bf16>(s1[8 + i]);
+    }
+    // the denominator sums the same bf16 probabilities the P.V product weighs the values with, so the output
+    // stays a convex combination of the values (a dominant key returns its value exactly)
+    {
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4_t w = __builtin_bit_cast(u32x4_t, pf[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rs[j] += bf_lo(w[j]) + bf_hi(w[j]);
+      }
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb)

@@ -3,19 +3,25 @@ C ABI) against the fp64 oracle (oracle_swa / oracle_rope, pinned in tests/test_o
 
 Both sides take the same bf16 q, k, v and the same RoPE table (fp64 for the oracle, its fp32 rounding for the
 library).  The oracle rotates and attends in fp64; the library rotates in fp32, rounds the rotated q and k to
-bf16, forms scores from bf16 products with fp32 accumulation, and feeds bf16 probabilities to the P.V product.
+bf16 (samba_rope's output), forms scores from bf16 products with fp32 accumulation, scales them in fp32, and
+feeds bf16 probabilities to the P.V product (the denominator sums those same bf16 values).
 
 Tolerances:
   * RoPE: one bf16 rounding of the rotated value plus the fp32 roundings of the table and the products,
     |g - o| <= 2^-8 |o| + 2^-22 (|x[c]| + |x[c + hd/2]|);
-  * attention, fp32 output: per (sequence, head) max|g - o| / max|o| <= ATT_TOL for scores of unit size.
-    The error is that of the bf16 operands: rotated q and k, q times log2(e)/sqrt(d) (each a relative 2^-9
-    per element, i.e. a score error of about 2^-9 |q||k| / sqrt(d) per rounding, random over the keys) and
-    the bf16 probabilities (relative 2^-9 each).  To first order the output moves by sum_j p_j ds_j
-    (v_j - o): the errors average over the window and grow with the scores' size.  Measured 2-4e-3 with
-    N(0, 1) inputs (an fp64 emulation of exactly these roundings gives the same); sharper scores get a
-    proportionally larger tolerance;
-  * attention, bf16 output: one more bf16 rounding, |g - o| <= 2^-8 |o| + ATT_TOL max|o|;
+  * attention entry points alone (q and k given in bf16, no RoPE): per (sequence, head)
+    max|g - o| / max|o| <= CORE_TOL = 2e-3.  The only rounding left in the prefill is that of the bf16
+    probabilities (relative 2^-9 each; the output is a convex combination of the values with weights perturbed
+    by at most 2^-8 relative), measured 0.7-1.3e-3 with N(0, 1) inputs and scores four times larger; the
+    decode keeps fp32 probabilities (error ~1e-7);
+  * RoPE then attention, fp32 output: per (sequence, head) max|g - o| / max|o| <= ATT_TOL = 5e-3 for scores
+    of unit size.  On top of the above, the bf16 rotated q and k (a relative 2^-9 per element each, i.e. a
+    score error of about 2^-9 |q||k| / sqrt(d), random over the keys) move the output by sum_j p_j ds_j
+    (v_j - o) to first order: the errors grow with the scores' size.  Measured 1.7-3.5e-3 with N(0, 1)
+    inputs; scores four times larger get four times the tolerance (measured 8e-3).  A single decoded row
+    over a 24-key window, normalised by its own largest element, averages over few keys: ROW_TOL = 1e-2
+    there (measured up to 7.3e-3);
+  * attention, bf16 output: one more bf16 rounding, |g - o| <= 2^-8 |o| + tol max|o|;
   * tripwires with exact arithmetic on the device: q = 0 (every visible key weighs exactly 1, so o is an
     fp32 mean of bf16 values: error ~1e-6) pins the window's edges and the sequence boundaries, and hard
     attention (one key scores ~300 above the rest) returns that key's value exactly.
@@ -33,7 +39,9 @@ from selective_state_space_05_amd import swa as W
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 HD = 128
-ATT_TOL = 1e-2
+ATT_TOL = 5e-3
+ROW_TOL = 1e-2
+CORE_TOL = 2e-3
 EXACT_TOL = 1e-5
 
 
@@ -203,6 +211,45 @@ def test_swa_fwd_matches_oracle(kind, shape, H, window, out):
     say("  error ratio %.3f" % r)
 
 
+def prefill_core(case_kind, shape, H, window, out, q_scale=1.0):
+    """samba_swa_fwd alone on bf16 q, k, v taken as already rotated, against the oracle's attention without
+    RoPE on the same values."""
+    if case_kind == "batch":
+        batch, L = shape
+        lengths = [L] * batch
+    else:
+        lengths = list(shape)
+    T = sum(lengths)
+    inp = I.make_swa_inputs_np(13, T, H, HD, q_scale=q_scale)
+    q, k, v = (bf16_dev(inp[n]) for n in ("q", "k", "v"))
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    if case_kind == "batch":
+        q, k, v = (t.reshape(batch, L, H, HD) for t in (q, k, v))
+        o = W.swa_fwd(q, k, v, window, out_dtype=od)
+    else:
+        cu = torch.from_numpy(I.cu_from_lengths(lengths)).to(DEV)
+        o = W.swa_fwd(q, k, v, window, cu_seqlens=cu, out_dtype=od)
+    torch.cuda.synchronize()
+    b = seq_bounds(lengths)
+    oo = O.swa(inp["q_f32"], inp["k_f32"], inp["v_f32"], window, seq_start=b)
+    return host(o).reshape(T, H, HD), oo, b
+
+
+@pytest.mark.parametrize("kind,shape,H,window,out", PREFILL_CASES)
+def test_swa_fwd_core_matches_oracle(kind, shape, H, window, out):
+    """The attention entry point on its own: q and k enter in bf16 as given, so the only roundings left are
+    the bf16 probabilities of the P.V product and fp32 accumulation; held to CORE_TOL."""
+    say("case: swa_fwd core", kind, shape, "H", H, "w", window, out)
+    g, o, b = prefill_core(kind, shape, H, window, out)
+    say("  error ratio %.3f" % check_att(g, o, b, "swa_fwd core", out=out, tol=CORE_TOL))
+
+
+def test_swa_fwd_core_sharp_softmax():
+    say("case: swa_fwd core sharp softmax")
+    g, o, b = prefill_core("batch", (1, 600), 2, 200, "f32", q_scale=4.0)
+    say("  error ratio %.3f" % check_att(g, o, b, "swa_fwd core sharp", tol=CORE_TOL))
+
+
 def test_swa_fwd_sharp_softmax():
     """Scores ~N(0, 16): the maximum moves often and the probabilities span many orders of magnitude.  The
     rounding errors of the bf16 operands perturb each score in proportion to its size (to first order the
@@ -327,6 +374,32 @@ def test_swa_decode_matches_oracle(window, cache_len, out):
         assert torch.equal(vc[b, :, slot].view(torch.int16), vn[b].view(torch.int16))
 
 
+def test_swa_decode_core_matches_oracle():
+    """The decode entry point on its own: q, k and the cache hold bf16 values taken as already rotated; the
+    probabilities stay fp32, so only fp32 rounding is left."""
+    say("case: swa_decode core")
+    H, window, cache_len = 2, 40, 57
+    pos = np.array([0, 5, 40, 41, 100, 333], dtype=np.int32)
+    B = len(pos)
+    kc = torch.zeros(B, H, cache_len, HD, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    qn, kn, vn, want = [], [], [], []
+    for b in range(B):
+        n = int(pos[b]) + 1
+        inp = I.make_swa_inputs_np(200 + b, n, H, HD)
+        qd, kd, vd = (bf16_dev(inp[x]).reshape(n, H, HD) for x in ("q", "k", "v"))
+        fill_cache(kd, vd, n - 1, cache_len, kc, vc, b)
+        qn.append(qd[n - 1])
+        kn.append(kd[n - 1])
+        vn.append(vd[n - 1])
+        want.append(O.swa(inp["q_f32"], inp["k_f32"], inp["v_f32"], window, rows=[n - 1])[n - 1])
+    qn, kn, vn = (torch.stack(x).contiguous() for x in (qn, kn, vn))
+    o = W.swa_decode(qn, kn, vn, kc, vc, torch.from_numpy(pos).to(DEV), window, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    r = check_att(host(o).reshape(B, H, HD), np.stack(want), np.arange(B + 1), "swa_decode core", tol=CORE_TOL)
+    say("  error ratio %.3f" % r)
+
+
 def test_swa_decode_steps_continue_prefill():
     """Prefill 50 tokens, fill the ring from the prefill's rotated keys, then 12 decode steps; every step's
     output against the oracle's row of the whole sequence (the ring wraps during the steps)."""
@@ -345,7 +418,7 @@ def test_swa_decode_steps_continue_prefill():
         o = W.swa_decode(qr[0, t:t + 1].contiguous(), kr[0, t:t + 1].contiguous(), v[0, t:t + 1].contiguous(), kc,
                          vc, pos, window, out_dtype=torch.float32)
         torch.cuda.synchronize()
-        check_att(host(o).reshape(1, H, HD), oo[t:t + 1], np.array([0, 1]), "decode step %d" % t)
+        check_att(host(o).reshape(1, H, HD), oo[t:t + 1], np.array([0, 1]), "decode step %d" % t, tol=ROW_TOL)
 
 
 def test_swa_decode_full_shape_sampled():
