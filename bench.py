@@ -169,7 +169,7 @@ RETENTION_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_retention.json"
 
 
 def read_retention_traffic():
-    """HBM bytes per retention call (pre-pass + prefill) from the committed counter runs, if they were taken on
+    """HBM bytes per retention call (one prefill launch) from the committed counter runs, if they were taken on
     this kernel source."""
     try:
         t = json.loads(RETENTION_TRAFFIC_FILE.read_text())
@@ -612,8 +612,40 @@ def ssd_flops(batch: int, L: int, heads: int, hd: int, n: int, q: int = 64) -> i
     return batch * L * heads * (2 * q * n + 2 * q * hd + 4 * n * hd)
 
 
+def _ssd_timed(forms, steps: int, warmup: int, rounds: int = 3):
+    """ms per samba_ssd_fwd call for each args object in `forms` (a workspace attached where its form needs
+    one): `rounds` rounds of `steps` calls of each in turn, after `warmup` calls of each; the median round."""
+    import statistics
+    import torch
+    from selective_state_space_05_amd import ssd as SD
+
+    dev = torch.device("cuda:0")
+    lib = SD.load_library()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    wss = [SD.attach_workspace(a, dev) for a in forms]
+
+    def caller(a):
+        ref = ctypes.byref(a)
+
+        def call():
+            if lib.samba_ssd_fwd(ref, sh) != 0:
+                raise RuntimeError("samba_ssd_fwd failed")
+        return call
+
+    calls = [caller(a) for a in forms]
+    for c in calls:
+        for _ in range(warmup):
+            c()
+    torch.cuda.synchronize()
+    per = [[_timed(c, steps, stream) for c in calls] for _ in range(rounds)]
+    del wss
+    return [statistics.median(r[i] for r in per) for i in range(len(forms))]
+
+
 def bench_ssd(steps: int = 20, warmup: int = 5):
-    """samba_ssd_fwd on B4 L4096 with 64 heads of 64, one (B, C) group of 128 states, gated, bf16 I/O."""
+    """samba_ssd_fwd on B4 L4096 with 64 heads of 64, one (B, C) group of 128 states, gated, bf16 I/O: the
+    default form (C B^T inside the prefill kernel) and the pre-pass form, timed in alternating rounds."""
     import torch
     from selective_state_space_05_amd import inputs as I
     from selective_state_space_05_amd import ssd as SD
@@ -628,22 +660,8 @@ def bench_ssd(steps: int = 20, warmup: int = 5):
     B, C = (t[k].view(Bt, L, G, N) for k in ("B", "C"))
     y = torch.empty_like(x)
     hl = torch.empty(Bt, H, P, N, dtype=torch.float32, device=dev)
-    a = SD.fwd_args(x, dt, B, C, t["A"], t["D"], t["dt_bias"], y=y, z=z, h_last=hl)
-    ws = SD.attach_workspace(a, dev)
-    lib = SD.load_library()
-    stream = torch.cuda.current_stream()
-    sh = ctypes.c_void_p(stream.cuda_stream)
-    ref = ctypes.byref(a)
-
-    def call():
-        if lib.samba_ssd_fwd(ref, sh) != 0:
-            raise RuntimeError("samba_ssd_fwd failed")
-
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    ms = _timed(call, steps, stream)
-    del ws
+    mk = lambda mode: SD.fwd_args(x, dt, B, C, t["A"], t["D"], t["dt_bias"], y=y, z=z, h_last=hl, cb_mode=mode)
+    ms, ms_pre = _ssd_timed([mk(SD.CB_AUTO), mk(SD.CB_PREPASS)], steps, warmup)
     nbytes = ssd_bytes(Bt, L, H, P, G, N)
     flops = ssd_flops(Bt, L, H, P, N)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -652,16 +670,18 @@ def bench_ssd(steps: int = 20, warmup: int = 5):
                         "fp32 state" % (Bt, L, H, P, G, N),
             "steps": steps, "ms_per_call": ms, "tokens_per_s": Bt * L / (ms * 1e-3), "gbs": gbs,
             "mfma_tflops": round(tf, 1), "mfma_frac_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "ms_per_call_cb_prepass": ms_pre,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_ssd_traffic(),
-                         "kernel": "ssd_cb_kernel<%d> + ssd_fwd_kernel<bf16,N=%d,gate> (one call)" % (N, N),
+                         "kernel": "ssd_fwd_kernel<bf16,N=%d,gate>, C B^T in kernel (one launch)" % N,
                          "launch_us": round(ms * 1e3, 2),
                          "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops}}
 
 
 def bench_retention(steps: int = 20, warmup: int = 5):
     """Multi-scale retention through samba_ssd_fwd: B4 L4096, 32 heads of 64 values with 128 keys each (one
-    (k, q) group per head: B = k, C = q, x = v), Δ = 1, A = ln γ_h, no skip, no gate, bf16 I/O."""
+    (k, q) group per head: B = k, C = q, x = v), Δ = 1, A = ln γ_h, no skip, no gate, bf16 I/O; the default
+    form and the pre-pass form, timed in alternating rounds."""
     import torch
     from selective_state_space_05_amd import inputs as I
     from selective_state_space_05_amd import ssd as SD
@@ -677,22 +697,8 @@ def bench_retention(steps: int = 20, warmup: int = 5):
     B, C = (t[k].view(Bt, L, G, N) for k in ("B", "C"))
     y = torch.empty_like(x)
     hl = torch.empty(Bt, H, P, N, dtype=torch.float32, device=dev)
-    a = SD.fwd_args(x, dt, B, C, rp["A"], rp["D"], rp["dt_bias"], y=y, h_last=hl)
-    ws = SD.attach_workspace(a, dev)
-    lib = SD.load_library()
-    stream = torch.cuda.current_stream()
-    sh = ctypes.c_void_p(stream.cuda_stream)
-    ref = ctypes.byref(a)
-
-    def call():
-        if lib.samba_ssd_fwd(ref, sh) != 0:
-            raise RuntimeError("samba_ssd_fwd failed")
-
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    ms = _timed(call, steps, stream)
-    del ws
+    mk = lambda mode: SD.fwd_args(x, dt, B, C, rp["A"], rp["D"], rp["dt_bias"], y=y, h_last=hl, cb_mode=mode)
+    ms, ms_pre = _ssd_timed([mk(SD.CB_AUTO), mk(SD.CB_PREPASS)], steps, warmup)
     nbytes = ssd_bytes(Bt, L, H, P, G, N, gated=False)
     flops = ssd_flops(Bt, L, H, P, N)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -701,9 +707,10 @@ def bench_retention(steps: int = 20, warmup: int = 5):
                         "head), no gate, bf16 I/O, fp32 state" % (Bt, L, H, P, N),
             "steps": steps, "ms_per_call": ms, "tokens_per_s": Bt * L / (ms * 1e-3), "gbs": gbs,
             "mfma_tflops": round(tf, 1), "mfma_frac_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "ms_per_call_cb_prepass": ms_pre,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_retention_traffic(),
-                         "kernel": "ssd_cb_kernel<%d> + ssd_fwd_kernel<bf16,N=%d,no gate> (one call)" % (N, N),
+                         "kernel": "ssd_fwd_kernel<bf16,N=%d,no gate>, C B^T in kernel (one launch)" % N,
                          "launch_us": round(ms * 1e3, 2),
                          "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops}}
 
@@ -1395,7 +1402,8 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
         return vals
 
     def pick(vals, part):
-        keys = [k for k in vals if part in k[0]]
+        parts = part if isinstance(part, tuple) else (part,)   # every piece must be in the kernel's name
+        keys = [k for k in vals if all(q in k[0] for q in parts)]
         assert keys, part
         return sorted(keys, key=lambda k: k[1])[-1]   # the largest launch of that kernel
 
@@ -1425,23 +1433,22 @@ def _counter_summary(fetch_dir: str, write_dir: str, out: str, which: str):
         wl = I.WORKLOADS[9]
         Bt, L, H, P, N, G = (wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.dstate,
                              wl.extra["ngroups"])
-        sel = {"ssd": ("ssd_fwd_kernel<unsigned short, 128, true, false>", ssd_bytes(Bt, L, H, P, G, N))}
+        # (the default form: C B^T inside the prefill kernel, the last template argument)
+        sel = {"ssd": ("ssd_fwd_kernel<unsigned short, 128, true, false, true>", ssd_bytes(Bt, L, H, P, G, N))}
         src_hash, run, flag = ssd_hash(), SSD_PMC_RUN, "--pmc-summary-ssd"
         note = ("Algorithmic bytes: x, z read and y written once (bf16), dt, B and C once, parameters, h_last "
-                "out. The workspace of C B^T tiles (3 MiB, written by the small pre-pass kernel and read from L2) "
-                "is not counted in the algorithmic bytes.")
+                "out. C B^T is formed inside the prefill kernel (no workspace).")
     elif which == "retention":
         wl = I.WORKLOADS[11]
         Bt, L, H, P, N, G = (wl.batch, wl.seqlen, wl.extra["heads"], wl.extra["head_dim"], wl.dstate,
                              wl.extra["ngroups"])
-        # the retention leg runs the unsplit or split prefill depending on the CU count: match either
-        sel = {"cb": ("ssd_cb_kernel<128>", Bt * L * G * N * 2 * 2),
-               "ssd": ("ssd_fwd_kernel<unsigned short, 128, false",
-                       ssd_bytes(Bt, L, H, P, G, N, gated=False) - Bt * L * G * N * 2 * 2)}
+        # the retention leg runs the unsplit or split prefill depending on the CU count: match either, in the
+        # default form (C B^T inside the prefill kernel: the last template argument)
+        sel = {"ssd": (("ssd_fwd_kernel<unsigned short, 128, false, ", ", true>("),
+                       ssd_bytes(Bt, L, H, P, G, N, gated=False))}
         src_hash, run, flag = ssd_hash(), RETENTION_PMC_RUN, "--pmc-summary-retention"
-        note = ("Algorithmic bytes: the C B^T pre-pass reads B and C once; the prefill reads x (v) and writes y "
-                "once (bf16), parameters, h_last out.  The pre-pass's C B^T tiles (12 KiB per 64-token chunk and "
-                "group, 101 MB with a group per head) are written and read back, not counted as algorithmic.")
+        note = ("Algorithmic bytes: B, C (k, q) and x (v) read and y written once (bf16), parameters, h_last out. "
+                "C B^T is formed inside the prefill kernel: one launch per call, no workspace.")
     else:
         wl = I.WORKLOADS[8]
         Bt, L, D, N, G = wl.batch, wl.seqlen, wl.dim, wl.dstate, wl.extra["ngroups"]

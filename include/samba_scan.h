@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define SAMBA_SCAN_ABI_VERSION 12
+#define SAMBA_SCAN_ABI_VERSION 13
 #define SAMBA_DSTATE 16
 
 typedef enum {

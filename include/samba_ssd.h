@@ -28,13 +28,15 @@
  * dt 2; A, D, dt_bias 4.  y and h_last must not overlap any input, except
  * h_last == h0 exactly (the final state written in place over the initial).
  *
- * Workspace: the products C Bᵀ of each chunk depend on the group only, not on
- * the head, so each call first writes them, once per (chunk, group), into a
- * caller-owned device workspace of samba_ssd_workspace_size() bytes (256-byte
- * aligned; 12 KiB per chunk slot and group, about 3 MiB for 4 x 4096 tokens
- * and one group), which the prefill kernel then reads.  Calls that overlap in
- * time must use different workspaces; the workspace may not overlap any input
- * or output (SAMBA_ERR_ALIASING); NULL or too small is SAMBA_ERR_WORKSPACE.
+ * Workspace: none by default.  The products C Bᵀ of each chunk are formed by
+ * the prefill kernel itself (cb_mode below).  With cb_mode
+ * SAMBA_SSD_CB_PREPASS a first kernel writes them, once per (chunk, group),
+ * into a caller-owned device workspace of samba_ssd_workspace_size() bytes
+ * (256-byte aligned; 12 KiB per chunk slot and group, about 3 MiB for
+ * 4 x 4096 tokens and one group), which the prefill kernel then reads.  Calls
+ * that overlap in time must use different workspaces; the workspace may not
+ * overlap any input or output (SAMBA_ERR_ALIASING); NULL or too small is
+ * SAMBA_ERR_WORKSPACE.  Without a workspace (size 0) the pointer is ignored.
  *
  * Ownership, asynchrony and errors as for samba_scan.h: device pointers owned
  * by the caller, nothing allocated or kept, validation before anything is
@@ -67,7 +69,16 @@ typedef struct {
   void* y;                     /* [tokens][heads][head_dim] */
   void* workspace;             /* device, samba_ssd_workspace_size() bytes */
   size_t workspace_bytes;
+  int32_t cb_mode;             /* samba_ssd_cb_mode: where C Bᵀ is formed (0 = the library chooses) */
 } samba_ssd_args;
+
+/* Where the products C Bᵀ are formed.  SAMBA_SSD_CB_PREPASS: a first kernel writes them once per (chunk,
+ * group) into the workspace and the prefill reads them back (shared by the heads of a group).
+ * SAMBA_SSD_CB_IN_KERNEL: the prefill kernel's helper waves form each chunk's tiles on the matrix cores
+ * from B and C as they stream by (per head; no workspace: samba_ssd_workspace_size() is 0).  Both give
+ * bit for bit the same results.  SAMBA_SSD_CB_AUTO takes the in-kernel form.  Other values:
+ * SAMBA_ERR_UNSUPPORTED. */
+enum samba_ssd_cb_mode { SAMBA_SSD_CB_AUTO = 0, SAMBA_SSD_CB_PREPASS = 1, SAMBA_SSD_CB_IN_KERNEL = 2 };
 
 /* Host-only: bytes of workspace samba_ssd_fwd needs for these sizes (0 when
  * there are no tokens); validates the sizes like samba_ssd_fwd. */
@@ -77,10 +88,12 @@ samba_status samba_ssd_fwd(const samba_ssd_args* args, void* stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid allocation): samba_ssd_fwd with the C Bᵀ tiles in a static scratch array of
- * SAMBA_SSD_SCRATCH_BYTES that the library holds on each GPU it runs on (until the process ends), instead
- * of a caller workspace.  Same arguments, results bit for bit those of samba_ssd_fwd; args->workspace and
- * workspace_bytes are ignored.  A call whose samba_ssd_workspace_size() exceeds SAMBA_SSD_SCRATCH_BYTES
+ * harnesses that forbid allocation): samba_ssd_fwd with the C Bᵀ tiles of the pre-pass form
+ * (SAMBA_SSD_CB_PREPASS) in a static scratch array of SAMBA_SSD_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on (until the process ends), instead of a caller workspace; the default form needs no
+ * scratch and the call then only enqueues the prefill.  Same arguments, results bit for bit those of
+ * samba_ssd_fwd; args->workspace and workspace_bytes are ignored.  A pre-pass call whose
+ * samba_ssd_workspace_size() exceeds SAMBA_SSD_SCRATCH_BYTES
  * (16 MiB: 1365 chunk slots x groups of 12 KiB, e.g. 87,360 tokens with one group) is refused with
  * SAMBA_ERR_WORKSPACE before anything is enqueued.  The call allocates nothing: on its first use on a
  * device it looks up that device's copy of the array (SAMBA_ERR_HIP if that fails).  Every call on one

@@ -2,12 +2,12 @@
 // "SAMBA混合注意力状态空间模型" compares Samba with, 与其他混合架构对比): a scalar decay per head and a
 // head_dim x dstate state per head, so that a chunk of tokens is a handful of dense products.
 //
-// Two kernels per call:
-//   * ssd_cb_kernel computes, once per (chunk, group), the three nonzero 32x32 tiles of Sᵀ = B Cᵀ (the
-//     (B, C) of a group serve every head of the group) into the caller's workspace, each tile stored as
-//     the accumulator image its consumer loads (16 floats per lane);
-//   * ssd_fwd_kernel: one workgroup (8 waves) per (sequence, head) walks the tokens in chunks of Q = 64, the
-//     fp32 state carried in registers from chunk to chunk.
+// ssd_fwd_kernel: one workgroup (8 waves) per (sequence, head) walks the tokens in chunks of Q = 64, the
+// fp32 state carried in registers from chunk to chunk.  The three nonzero 32x32 tiles of Sᵀ = B Cᵀ of each
+// chunk are formed by the kernel's helper waves from B and C staged row-major in LDS (the default), or, in
+// the pre-pass form, by ssd_cb_kernel once per (chunk, group) (the (B, C) of a group serve every head of
+// the group) into the caller's workspace, each tile stored as the accumulator image its consumer loads (16
+// floats per lane).  Both forms run the same MFMA sequence: bit for bit the same tiles.
 // With la_t = log2e * A * sum_{r<=t} Δ_r inside the chunk, w_s = 2^(la_end - la_s) Δ_s and the entering
 // state H (P x N), per chunk:
 //   (b) Mᵀ[s][t] = Sᵀ[s][t] 2^(la_t - la_s) Δ_s  (s <= t, else 0), + D on the diagonal (the skip)
@@ -29,7 +29,9 @@
 //     partial sums for both t-tiles; the other t-tile's goes to the partner wave through LDS;
 //   * helper waves 4 .. 7 load C, B, X and Δ through a ring of two register sets and stage them into
 //     LDS (C row-major, B and X transposed, each store a run of consecutive words across the lanes);
-//     each computes Δ, la and w with a DPP prefix sum, and three of them build the chunk's masked M tiles.
+//     each computes Δ, la and w with a DPP prefix sum, and three of them build the chunk's masked M tiles
+//     (in the default form between the two barriers of the chunk before, once every helper has staged B
+//     and C, each from its own Sᵀ tile formed on the matrix cores).
 //     (z and y in the state waves' layout are 8-byte pieces of 32 rows per instruction; staging y through
 //     LDS for whole-line stores by the helpers measured no faster.)
 // The inputs are staged in two alternating LDS buffers, so the helpers fill chunk c + 1's while the state
@@ -132,6 +134,7 @@ struct SsdParams {
 constexpr int kWaves = 8;                // 4 state waves + 4 helper waves
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileFloats = 64 * 16;     // one 32x32 accumulator image
+constexpr bool kCbInAuto = true;         // SAMBA_SSD_CB_AUTO: C Bᵀ inside the prefill kernel
 
 __device__ __forceinline__ int32_t cu_at(const int32_t* cu, int s, int32_t total) {
   const int32_t v = cu[s];
@@ -223,6 +226,7 @@ struct Stage {
 template <int N>
 struct Smem {
   Stage<N> st[2];                                   // chunk c uses st[c & 1]
+  uint16_t brm[kQ * Stage<N>::kRow];                // B [s][n] of the chunk being prepared (C Bᵀ in kernel)
   float4 xch[4][4][64];                             // (d) partial sums for the partner wave
   float hs[4][2][kQ];                               // each helper wave's own la, Δ of the chunk it prepares
 };
@@ -253,6 +257,10 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ float uniform(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -267,7 +275,7 @@ __device__ __forceinline__ void wave_sync() {
 //   2. helpers 0 .. 2 turn the chunk's Sᵀ tile h (loaded from the workspace two chunks earlier) into M
 //      = Sᵀ 2^(la_t - la_s) Δ_s (s <= t), + D on the diagonal, published as bf16 hi + lo operand images;
 //   3. load chunk c + 3 and the workspace tile of chunk c + 3.
-template <int N>
+template <int N, bool kCbIn>
 __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
   constexpr int kRow = Stage<N>::kRow;
   constexpr int NPR = N / 8;              // 16-byte pieces per C row
@@ -284,7 +292,7 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
     uint4 cr[PC], br[NB][2], xr[2];
     uint16_t dtr;
   } set[2];
-  f32x16_t sring[2];                      // Sᵀ tiles two chunks ahead
+  f32x16_t sring[2];                      // Sᵀ tiles two chunks ahead (from the workspace)
   const int nchunks = (cx.len + kQ - 1) / kQ;
   auto load = [&](auto kset, int c) {
     Set& st = set[decltype(kset)::value];
@@ -303,16 +311,45 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
     for (int k = 0; k < 2; ++k)
       st.xr[k] = ld16(cx.rx, static_cast<uint32_t>(c0 + 2 * r + k) * cx.rowx + (8 * cg) * 2);
     st.dtr = __builtin_amdgcn_raw_buffer_load_b16(cx.rdt, static_cast<uint32_t>(c0 + lane) * cx.H * 2, 0, 0);
-    // the chunk's Sᵀ tile (the last chunk's past the sequence: a padding chunk's M is the skip alone)
-    const int cs = c < nchunks ? c : nchunks - 1;
-    const float4* q = reinterpret_cast<const float4*>(cx.ws + cs * cx.ws_stride + tile * kTileFloats) + lane * 4;
+    if constexpr (!kCbIn) {
+      // the chunk's Sᵀ tile (the last chunk's past the sequence: a padding chunk's M is the skip alone)
+      const int cs = c < nchunks ? c : nchunks - 1;
+      const float4* q = reinterpret_cast<const float4*>(cx.ws + cs * cx.ws_stride + tile * kTileFloats) + lane * 4;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float4 v = q[k];
-      sring[decltype(kset)::value][4 * k] = v.x;
-      sring[decltype(kset)::value][4 * k + 1] = v.y;
-      sring[decltype(kset)::value][4 * k + 2] = v.z;
-      sring[decltype(kset)::value][4 * k + 3] = v.w;
+      for (int k = 0; k < 4; ++k) {
+        const float4 v = q[k];
+        sring[decltype(kset)::value][4 * k] = v.x;
+        sring[decltype(kset)::value][4 * k + 1] = v.y;
+        sring[decltype(kset)::value][4 * k + 2] = v.z;
+        sring[decltype(kset)::value][4 * k + 3] = v.w;
+      }
+    }
+  };
+  // M = Sᵀ 2^(la_t - la_s) Δ_s (s <= t), + D on the diagonal, from the helper's Sᵀ tile and its own copy
+  // of the chunk's la and Δ, published as bf16 hi + lo operand images
+  auto build_m = [&](Stage<N>& g, f32x16_t m) {
+    const int t_own = 32 * m_tb + l32;
+    const float la_t = sm.hs[hw][0][t_own];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int s0 = 32 * m_si + 8 * q + 4 * hi;
+      const float4 las = *reinterpret_cast<const float4*>(&sm.hs[hw][0][s0]);
+      const float4 dls = *reinterpret_cast<const float4*>(&sm.hs[hw][1][s0]);
+      const float lv[4] = {las.x, las.y, las.z, las.w}, dv[4] = {dls.x, dls.y, dls.z, dls.w};
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int sv = s0 + rr;
+        float v = sv <= t_own ? m[4 * q + rr] * __builtin_amdgcn_exp2f(la_t - lv[rr]) * dv[rr] : 0.0f;
+        v += sv == t_own ? cx.Dh : 0.0f;
+        m[4 * q + rr] = v;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t mh, ml;
+      split8(m, 8 * kk, mh, ml);
+      g.m[hw][kk][0][lane] = mh;
+      g.m[hw][kk][1][lane] = ml;
     }
   };
   auto prepare = [&](auto kset, int c) {
@@ -349,51 +386,60 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
       g.la[lane] = l;
       g.w[lane] = __builtin_amdgcn_exp2f(l_end - l) * dlt;
     }
+    if constexpr (kCbIn) {
+      // B row-major as well, for the C Bᵀ tile that the helpers form after the next barrier
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          *reinterpret_cast<uint4*>(&sm.brm[(2 * r + k) * kRow + 8 * (cg + 8 * i)]) = st.br[i][k];
+    }
     if (hw < 3) {
       sm.hs[hw][0][lane] = l;
       sm.hs[hw][1][lane] = dlt;
       wave_sync();
-      const int t_own = 32 * m_tb + l32;
-      const float la_t = sm.hs[hw][0][t_own];
-      f32x16_t m = sring[K];
+      if constexpr (!kCbIn) build_m(g, sring[K]);
+    }
+  };
+  // C Bᵀ formed here: the helper's tile of chunk c from B and C row-major in LDS (staged by all helpers
+  // before the last barrier), the same MFMA sequence as the pre-pass kernel (bit for bit the same tile;
+  // rows past the sequence were staged as 0: a padding chunk's M is the skip alone)
+  auto form_m = [&](auto kset) {
+    Stage<N>& g = sm.st[decltype(kset)::value];
+    if (hw < 3) {
+      f32x16_t m = f32x16_t{};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int s0 = 32 * m_si + 8 * q + 4 * hi;
-        const float4 las = *reinterpret_cast<const float4*>(&sm.hs[hw][0][s0]);
-        const float4 dls = *reinterpret_cast<const float4*>(&sm.hs[hw][1][s0]);
-        const float lv[4] = {las.x, las.y, las.z, las.w}, dv[4] = {dls.x, dls.y, dls.z, dls.w};
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int sv = s0 + rr;
-          float v = sv <= t_own ? m[4 * q + rr] * __builtin_amdgcn_exp2f(la_t - lv[rr]) * dv[rr] : 0.0f;
-          v += sv == t_own ? cx.Dh : 0.0f;
-          m[4 * q + rr] = v;
-        }
+      for (int kk = 0; kk < N / 16; ++kk) {
+        const bf16x8_t bo = *reinterpret_cast<const bf16x8_t*>(&sm.brm[(32 * m_si + l32) * kRow + 8 * hi + 16 * kk]);
+        const bf16x8_t co = *reinterpret_cast<const bf16x8_t*>(&g.c[(32 * m_tb + l32) * kRow + 8 * hi + 16 * kk]);
+        m = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo, co, m, 0, 0, 0);
       }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8_t mh, ml;
-        split8(m, 8 * kk, mh, ml);
-        g.m[hw][kk][0][lane] = mh;
-        g.m[hw][kk][1][lane] = ml;
-      }
+      build_m(g, m);
     }
   };
   // An even number of chunks (the state waves pad the same way; a chunk past the sequence reads zeros and
   // changes nothing), and no load or store behind a data-dependent branch inside the loop, so that the
   // compiler's wait counts keep the other register set's loads in flight.
   const int npad = (nchunks + 1) & ~1;
+  // With C Bᵀ formed here, the M tiles of chunk c + 1 are built between the two barriers of chunk c (after
+  // every helper has staged B and C of chunk c + 1, before the state waves need them), and those of chunk 0
+  // behind one more barrier.
   if (nchunks > 0) {
     load(std::integral_constant<int, 0>{}, 0);
     load(std::integral_constant<int, 1>{}, 1);
     prepare(std::integral_constant<int, 0>{}, 0);
     load(std::integral_constant<int, 0>{}, 2);
   }
+  if constexpr (kCbIn) {
+    __syncthreads();   // chunk 0's B and C staged
+    if (nchunks > 0) form_m(std::integral_constant<int, 0>{});
+  }
   __syncthreads();   // chunk 0 staged
   auto body = [&](auto knext, int c) {
     prepare(knext, c + 1);
     load(knext, c + 3);
     __syncthreads();   // X1: the state waves' partial sums
+    if constexpr (kCbIn) form_m(knext);
     __syncthreads();   // X2: chunk c computed, chunk c + 1 prepared
   };
   for (int c = 0; c < npad; c += 2) {
@@ -405,7 +451,7 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
 // State wave k (0 .. 3): p-tile a = k & 1, n-tiles of half HB = k >> 1 (element e of tile nt: n = 32 nt +
 // 8 (e / 4) + 4 hi + e % 4, p = 32 a + lane % 32); finishes the output tile (a, HB): sums it with the
 // partner's partial sums, applies the gate (z loaded one chunk ahead) and stores it.
-template <typename Tout, int N, int HB, bool kGate>
+template <typename Tout, int N, int HB, bool kGate, bool kCbIn>
 __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const float* h0, float* h_last) {
   constexpr int NTW = N / 64;
   constexpr int kRow = Stage<N>::kRow;
@@ -430,6 +476,7 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
   // an even number of chunks, as the helper waves run (a padding chunk has Δ = 0 and x = 0: it leaves the
   // state alone and its output goes past the sequence)
   const int npad = ((cx.len + kQ - 1) / kQ + 1) & ~1;
+  if constexpr (kCbIn) __syncthreads();   // chunk 0's B and C staged (the helpers then form its M)
   __syncthreads();   // chunk 0 staged
 
   // z and y pieces of this lane: token t_own, channels 32 a + 8 q + 4 hi + 0..3 (q = 0..3); z of the next
@@ -582,8 +629,10 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
 
 // A state wave of the value tile that its workgroup leaves to the other one (kSplit): it only takes part in
 // the barriers, as many as a computing state wave does.
+template <bool kCbIn>
 __device__ __forceinline__ void idle_state_wave(const Ctx& cx) {
   const int npad = ((cx.len + kQ - 1) / kQ + 1) & ~1;
+  if constexpr (kCbIn) __syncthreads();   // chunk 0's B and C staged
   __syncthreads();   // chunk 0 staged
   for (int c = 0; c < npad; ++c) {
     __syncthreads();   // X1
@@ -594,15 +643,18 @@ __device__ __forceinline__ void idle_state_wave(const Ctx& cx) {
 // kSplit: the head's two 32-column value tiles go to two workgroups (when one workgroup per (sequence, head)
 // would leave at least half of the CUs idle); both stage the chunk and build M, and each runs the state
 // waves of its own tile.
-template <typename Tout, int N, bool kGate, bool kSplit>
+template <typename Tout, int N, bool kGate, bool kSplit, bool kCbIn>
 __global__ __launch_bounds__(kThreads, 1) void ssd_fwd_kernel(SsdParams p) {
   __shared__ __attribute__((aligned(16))) Smem<N> sm;
   const int nblk = static_cast<int>(gridDim.x);
   const int logical = xcd_remap(static_cast<int>(blockIdx.x), nblk);
   const int sh = kSplit ? (logical >> 1) : logical;   // (the two halves of a head are neighbours: same XCD)
   const int pa = kSplit ? (logical & 1) : 0;
-  const int s = sh / p.heads;
-  const int h = sh - s * p.heads;
+  // (sequence, head) and the head's parameters through readfirstlane: scalar loads.  A per-lane load issued
+  // before the chunk loop leaves the compiler unsure whether it is still in flight inside the loop, and it
+  // then waits for every outstanding load (prefetches included) at each use.
+  const int s = __builtin_amdgcn_readfirstlane(sh / p.heads);
+  const int h = __builtin_amdgcn_readfirstlane(sh - s * p.heads);
   const SeqInfo si = seq_info(p, s);
   const int H = p.heads;
   const int G = p.ngroups;
@@ -610,9 +662,9 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_fwd_kernel(SsdParams p) {
   Ctx cx;
   cx.len = si.len;
   cx.H = H;
-  cx.A2 = p.A[h] * kLog2e;
-  cx.Dh = p.Dskip[h];
-  cx.bias = p.bias[h];
+  cx.A2 = uniform(p.A[h] * kLog2e);
+  cx.Dh = uniform(p.Dskip[h]);
+  cx.bias = uniform(p.bias[h]);
   cx.rowx = static_cast<uint32_t>(H) * kP * 2;
   cx.rowbc = static_cast<uint32_t>(G) * N * 2;
   const int64_t t0 = si.t0;
@@ -628,13 +680,13 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_fwd_kernel(SsdParams p) {
   cx.rc = rsrc_bytes(static_cast<const uint16_t*>(p.C) + t0 * G * N + gb, bcb);
   cx.st_off0 = (static_cast<int64_t>(s) * H + h) * kP * N;
   cx.ws_stride = static_cast<int64_t>(G) * 3 * kTileFloats;
-  cx.ws = p.ws + (static_cast<int64_t>(si.slot0) * G + g) * 3 * kTileFloats;
+  cx.ws = kCbIn ? nullptr : p.ws + (static_cast<int64_t>(si.slot0) * G + g) * 3 * kTileFloats;
 
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  if (wave >= 4) helper_wave<N>(cx, sm);
-  else if (kSplit && (wave & 1) != pa) idle_state_wave(cx);
-  else if (wave >= 2) state_wave<Tout, N, 1, kGate>(cx, sm, p.h0, p.h_last);
-  else state_wave<Tout, N, 0, kGate>(cx, sm, p.h0, p.h_last);
+  if (wave >= 4) helper_wave<N, kCbIn>(cx, sm);
+  else if (kSplit && (wave & 1) != pa) idle_state_wave<kCbIn>(cx);
+  else if (wave >= 2) state_wave<Tout, N, 1, kGate, kCbIn>(cx, sm, p.h0, p.h_last);
+  else state_wave<Tout, N, 0, kGate, kCbIn>(cx, sm, p.h0, p.h_last);
 }
 
 bool aligned(const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) & (a - 1)) == 0; }
@@ -644,17 +696,28 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-template <typename Tout, int N>
-hipError_t launch_ssd(const SsdParams& p, bool gate, bool split, int64_t nslots, int64_t nblocks, hipStream_t s) {
-  if (nslots > 0)
-    hipLaunchKernelGGL((ssd_cb_kernel<N>), dim3(static_cast<uint32_t>(nslots * p.ngroups)), dim3(192), 0, s, p);
+template <typename Tout, int N, bool kCbIn>
+void launch_fwd(const SsdParams& p, bool gate, bool split, int64_t nblocks, hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>(split ? 2 * nblocks : nblocks)), block(kThreads);
   if (gate) {
-    if (split) hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, true, false>), grid, block, 0, s, p);
+    if (split) hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, true, true, kCbIn>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, true, false, kCbIn>), grid, block, 0, s, p);
   } else {
-    if (split) hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, false, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, false, false>), grid, block, 0, s, p);
+    if (split) hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, false, true, kCbIn>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((ssd_fwd_kernel<Tout, N, false, false, kCbIn>), grid, block, 0, s, p);
+  }
+}
+
+// cb_in: C Bᵀ formed inside the prefill kernel (no pre-pass, no workspace)
+template <typename Tout, int N>
+hipError_t launch_ssd(const SsdParams& p, bool gate, bool split, bool cb_in, int64_t nslots, int64_t nblocks,
+                      hipStream_t s) {
+  if (cb_in) {
+    launch_fwd<Tout, N, true>(p, gate, split, nblocks, s);
+  } else {
+    if (nslots > 0)
+      hipLaunchKernelGGL((ssd_cb_kernel<N>), dim3(static_cast<uint32_t>(nslots * p.ngroups)), dim3(192), 0, s, p);
+    launch_fwd<Tout, N, false>(p, gate, split, nblocks, s);
   }
   return hipGetLastError();
 }
@@ -683,6 +746,7 @@ int ssd_cu_count() {
 // sequences, chunk slots and workspace bytes of a validated call
 struct Plan {
   int64_t nseq, tokens, nch, nslots;
+  bool cb_in;        // C Bᵀ inside the prefill kernel
   size_t ws_bytes;
 };
 samba_status plan_ssd(const samba_ssd_args* a, Plan* pl) {
@@ -709,7 +773,10 @@ samba_status plan_ssd(const samba_ssd_args* a, Plan* pl) {
   if (pl->tokens * a->heads * kP * 4 >= (int64_t{1} << 31)) return SAMBA_ERR_BAD_SHAPE;
   if (pl->tokens * a->ngroups * N * 2 >= (int64_t{1} << 31)) return SAMBA_ERR_BAD_SHAPE;
   if (pl->nseq * a->heads > 0x7fffffff || pl->nslots * a->ngroups > 0x7fffffff) return SAMBA_ERR_BAD_SHAPE;
-  pl->ws_bytes = pl->tokens > 0 ? static_cast<size_t>(pl->nslots) * a->ngroups * 3 * kTileFloats * 4 : 0;
+  if (a->cb_mode != SAMBA_SSD_CB_AUTO && a->cb_mode != SAMBA_SSD_CB_PREPASS && a->cb_mode != SAMBA_SSD_CB_IN_KERNEL)
+    return SAMBA_ERR_UNSUPPORTED;
+  pl->cb_in = a->cb_mode == SAMBA_SSD_CB_IN_KERNEL || (a->cb_mode == SAMBA_SSD_CB_AUTO && kCbInAuto);
+  pl->ws_bytes = pl->tokens > 0 && !pl->cb_in ? static_cast<size_t>(pl->nslots) * a->ngroups * 3 * kTileFloats * 4 : 0;
   return SAMBA_OK;
 }
 
@@ -727,9 +794,9 @@ extern "C" samba_status samba_ssd_workspace_size(const samba_ssd_args* a, size_t
 namespace {
 
 // Scratch of the no-allocation entry point: a file-scope device array, one copy per GPU, holding the
-// C Bᵀ tiles that samba_ssd_fwd writes into the caller's workspace.  Host code never passes the array's
-// name to a kernel (on the host it is a stand-in, not a device address): it uses the address that
-// hipGetSymbolAddress returned for the device, kept per device below.
+// C Bᵀ tiles that the pre-pass form of samba_ssd_fwd writes into the caller's workspace.  Host code never
+// passes the array's name to a kernel (on the host it is a stand-in, not a device address): it uses the
+// address that hipGetSymbolAddress returned for the device, kept per device below.
 constexpr size_t kSsdScratchBytes = SAMBA_SSD_SCRATCH_BYTES;
 static __device__ __align__(256) unsigned char scratch[kSsdScratchBytes];
 
@@ -815,11 +882,11 @@ samba_status ssd_fwd_impl(const samba_ssd_args* a, void* ws, size_t ws_bytes, bo
   hipError_t e;
   // (no tokens: no chunk, no workspace read; every sequence's h_last is its h0, or zero)
   if (a->y_dtype == SAMBA_BF16) {
-    e = N == 64 ? launch_ssd<uint16_t, 64>(p, gate, split, nslots, nblocks, s)
-                : launch_ssd<uint16_t, 128>(p, gate, split, nslots, nblocks, s);
+    e = N == 64 ? launch_ssd<uint16_t, 64>(p, gate, split, pl.cb_in, nslots, nblocks, s)
+                : launch_ssd<uint16_t, 128>(p, gate, split, pl.cb_in, nslots, nblocks, s);
   } else {
-    e = N == 64 ? launch_ssd<float, 64>(p, gate, split, nslots, nblocks, s)
-                : launch_ssd<float, 128>(p, gate, split, nslots, nblocks, s);
+    e = N == 64 ? launch_ssd<float, 64>(p, gate, split, pl.cb_in, nslots, nblocks, s)
+                : launch_ssd<float, 128>(p, gate, split, pl.cb_in, nslots, nblocks, s);
   }
   return e == hipSuccess ? SAMBA_OK : SAMBA_ERR_HIP;
 }

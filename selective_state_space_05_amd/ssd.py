@@ -27,7 +27,11 @@ class SsdArgs(ctypes.Structure):
                 ("head_dim", _I32), ("dstate", _I32), ("ngroups", _I32), ("cu_seqlens", _P), ("nseq", _I32),
                 ("y_dtype", _I32), ("x", _P), ("dt", _P), ("z", _P), ("B", _P), ("C", _P), ("A", _P), ("D", _P),
                 ("dt_bias", _P), ("h0", _P), ("h_last", _P), ("y", _P), ("workspace", _P),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("cb_mode", _I32)]
+
+
+# samba_ssd_cb_mode: where C Bᵀ is formed
+CB_AUTO, CB_PREPASS, CB_IN_KERNEL = 0, 1, 2
 
 
 _bound = set()
@@ -79,7 +83,8 @@ def attach_workspace(a: SsdArgs, device, workspace=None):
     return workspace
 
 
-def fwd_args(x, dt, B, C, A, D, dt_bias, *, y, z=None, h0=None, h_last=None, cu_seqlens=None) -> SsdArgs:
+def fwd_args(x, dt, B, C, A, D, dt_bias, *, y, z=None, h0=None, h_last=None, cu_seqlens=None,
+             cb_mode: int = CB_AUTO) -> SsdArgs:
     batch, seqlen, heads, hd, nseq = _shape(x, cu_seqlens)
     a = SsdArgs()
     a.struct_size = ctypes.sizeof(SsdArgs)
@@ -90,15 +95,17 @@ def fwd_args(x, dt, B, C, A, D, dt_bias, *, y, z=None, h0=None, h_last=None, cu_
     a.x, a.dt, a.z, a.B, a.C = _ptr(x), _ptr(dt), _ptr(z), _ptr(B), _ptr(C)
     a.A, a.D, a.dt_bias = _ptr(A), _ptr(D), _ptr(dt_bias)
     a.h0, a.h_last, a.y = _ptr(h0), _ptr(h_last), _ptr(y)
+    a.cb_mode = cb_mode
     return a
 
 
 def ssd_fwd(x, dt, B, C, A, D, dt_bias, *, z=None, h0=None, h_last=None, y=None, y_dtype=None, cu_seqlens=None,
-            return_last_state: bool = True, workspace=None, stream=None):
+            return_last_state: bool = True, workspace=None, cb_mode: int = CB_AUTO, stream=None):
     """Chunked SSD prefill through samba_ssd_fwd.  x bf16 [batch][L][heads][64] (or [tokens][heads][64]);
     dt bf16 [.., heads]; B, C bf16 [.., ngroups][dstate] with dstate 64 or 128; z optional (no gate when
     None); workspace: a uint8 device tensor of at least samba_ssd_workspace_size() bytes (allocated per call
-    when None).  Returns (y, h_last) with h_last fp32 [nseq][heads][64][dstate]."""
+    when None and needed); cb_mode: CB_AUTO, CB_PREPASS or CB_IN_KERNEL.  Returns (y, h_last) with h_last
+    fp32 [nseq][heads][64][dstate]."""
     import torch
     _check_dev(x, dt, z, B, C, A, D, dt_bias, h0, h_last, y, cu_seqlens)
     batch, seqlen, heads, hd, nseq = _shape(x, cu_seqlens)
@@ -107,7 +114,8 @@ def ssd_fwd(x, dt, B, C, A, D, dt_bias, *, z=None, h0=None, h_last=None, y=None,
         y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
     if h_last is None and return_last_state:
         h_last = torch.empty(nseq, heads, hd, N, dtype=torch.float32, device=x.device)
-    a = fwd_args(x, dt, B, C, A, D, dt_bias, y=y, z=z, h0=h0, h_last=h_last, cu_seqlens=cu_seqlens)
+    a = fwd_args(x, dt, B, C, A, D, dt_bias, y=y, z=z, h0=h0, h_last=h_last, cu_seqlens=cu_seqlens,
+                 cb_mode=cb_mode)
     ws = attach_workspace(a, x.device, workspace)
     st = load_library().samba_ssd_fwd(ctypes.byref(a), _P(_stream_handle(stream)))
     del ws   # torch reuses the freed block only for later work on this stream, which runs after the call
@@ -120,14 +128,15 @@ SCRATCH_BYTES = 16 << 20   # SAMBA_SSD_SCRATCH_BYTES
 
 
 def ssd_fwd_noalloc(x, dt, B, C, A, D, dt_bias, *, z=None, h0=None, h_last=None, y=None, cu_seqlens=None,
-                    stream=None):
+                    cb_mode: int = CB_AUTO, stream=None):
     """samba_ssd_fwd_noalloc: as ssd_fwd, but the library's static per-GPU scratch holds the C Bᵀ tiles
     (no workspace; calls needing more than SCRATCH_BYTES are refused).  y and h_last must be given here
     (this wrapper allocates nothing either)."""
     _check_dev(x, dt, z, B, C, A, D, dt_bias, h0, h_last, y, cu_seqlens)
     if y is None:
         raise ValueError("ssd_fwd_noalloc takes a preallocated y")
-    a = fwd_args(x, dt, B, C, A, D, dt_bias, y=y, z=z, h0=h0, h_last=h_last, cu_seqlens=cu_seqlens)
+    a = fwd_args(x, dt, B, C, A, D, dt_bias, y=y, z=z, h0=h0, h_last=h_last, cu_seqlens=cu_seqlens,
+                 cb_mode=cb_mode)
     st = load_library().samba_ssd_fwd_noalloc(ctypes.byref(a), _P(_stream_handle(stream)))
     if st != 0:
         raise SambaError(st, "samba_ssd_fwd_noalloc")

@@ -679,17 +679,24 @@ def ssd_ws(lib, a):
 @pytest.mark.parametrize("batch,seqlen,G,varlen", [(2, 100, 2, False), (4, 4096, 1, False), (1, 1000, 4, True),
                                                    (3, 0, 1, False)])
 def test_ssd_workspace_size(lib, batch, seqlen, G, varlen):
-    """12 KiB per (chunk slot, group): batched sequences own ceil(L / 64) slots each, packed streams
-    tokens / 64 + nseq slots; no tokens, no workspace."""
+    """With the C Bᵀ pre-pass, 12 KiB per (chunk slot, group): batched sequences own ceil(L / 64) slots
+    each, packed streams tokens / 64 + nseq slots; no tokens, no workspace.  Formed inside the prefill
+    kernel (and by default), none."""
     a = ssd_ok(batch=batch, seqlen=seqlen, heads=4 * G, ngroups=G)
     if varlen:
         a.cu_seqlens, a.nseq = BASE + 11 * GB, 5
     slots = (batch * seqlen) // 64 + 5 if varlen else batch * -(-seqlen // 64)
+    a.cb_mode = D.CB_PREPASS
     assert ssd_ws(lib, a) == (slots * G * 12288 if batch * seqlen else 0)
+    for mode in (D.CB_IN_KERNEL, D.CB_AUTO):
+        a.cb_mode = mode
+        assert ssd_ws(lib, a) == 0
 
 
 SSD_CASES = {
     "struct_size": (lambda a: setattr(a, "struct_size", 4), 7),
+    "cb_mode": (lambda a: setattr(a, "cb_mode", 3), 6),
+    "cb_mode_negative": (lambda a: setattr(a, "cb_mode", -1), 6),
     "head_dim_128": (lambda a: setattr(a, "head_dim", 128), 6),
     "dstate_16": (lambda a: setattr(a, "dstate", 16), 6),
     "dstate_256": (lambda a: setattr(a, "dstate", 256), 6),
@@ -723,6 +730,8 @@ SSD_CASES = {
 @pytest.mark.parametrize("name", sorted(SSD_CASES))
 def test_ssd_rejects(lib, name):
     a = ssd_ok()
+    if "workspace" in name:
+        a.cb_mode = D.CB_PREPASS   # (the only form that takes a workspace)
     mutate, code = SSD_CASES[name]
     mutate(a)
     assert lib.samba_ssd_fwd(ctypes.byref(a), None) == code

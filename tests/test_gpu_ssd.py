@@ -94,6 +94,24 @@ def test_ssd_matches_oracle(lengths, heads, G, N, yd, gate, with_h0):
     check(y, yo, hl, ho, b, yd)
 
 
+@pytest.mark.parametrize("lengths,heads,G,N,yd,gate,with_h0", CASES)
+def test_ssd_cb_forms_bitwise_equal(lengths, heads, G, N, yd, gate, with_h0):
+    """C Bᵀ from the pre-pass (through the workspace) and formed inside the prefill kernel: the same tiles
+    from the same MFMA sequence, so y and h_last agree bit for bit (the oracle tests run the default form)."""
+    say("case: ssd C B^T forms", lengths, "heads", heads, "G", G, "N", N, yd)
+    T = sum(lengths)
+    t = I.make_ssd_inputs_torch(14, T, heads, G, N, DEV)
+    cu = torch.from_numpy(I.cu_from_lengths(lengths)).to(DEV) if len(lengths) > 1 else None
+    h0 = torch.from_numpy(I.make_ssd_h0(14, len(lengths), heads, N, scale=0.5)).to(DEV) if with_h0 else None
+    od = torch.float32 if yd == "f32" else torch.bfloat16
+    args = (t["x"], t["dt"], t["B"], t["C"], t["A"], t["D"], t["dt_bias"])
+    kw = dict(z=t["z"] if gate else None, h0=h0, y_dtype=od, cu_seqlens=cu)
+    y1, h1 = S.ssd_fwd(*args, cb_mode=S.CB_PREPASS, **kw)
+    y2, h2 = S.ssd_fwd(*args, cb_mode=S.CB_IN_KERNEL, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)) and torch.equal(h1, h2)
+
+
 def test_ssd_long_memory():
     """Decays close to 1 (A = -0.02 and -0.5, Δ up to 0.1): the carried state dominates the output."""
     say("case: ssd long memory")

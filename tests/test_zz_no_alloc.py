@@ -1,7 +1,8 @@
 """The SSD prefill's no-allocation entry point (samba_ssd_fwd_noalloc, include/samba_ssd.h) against
-samba_ssd_fwd with a caller workspace: bit for bit, on two calls in a row (the second smaller, so that
-it runs over the scratch the first one left), and the refusal of a call that needs more scratch than the
-static array holds (checked on the host, nothing enqueued)."""
+samba_ssd_fwd with a caller workspace, both with the C Bᵀ pre-pass (the form that uses the scratch): bit for
+bit, on two calls in a row (the second smaller, so that it runs over the scratch the first one left), and
+the refusal of a call that needs more scratch than the static array holds (checked on the host, nothing
+enqueued).  With C Bᵀ formed inside the prefill kernel no scratch is needed: the same call then runs."""
 import ctypes
 import sys
 
@@ -36,8 +37,8 @@ def case(cfg, lengths, heads, G, N, gate, y_dtype):
                 heads=heads, N=N, y_dtype=y_dtype)
 
 
-def run_both(c):
-    kw = dict(z=c["z"], h0=c["h0"], cu_seqlens=c["cu"])
+def run_both(c, cb_mode=SD.CB_PREPASS):
+    kw = dict(z=c["z"], h0=c["h0"], cu_seqlens=c["cu"], cb_mode=cb_mode)
     args = (c["x"], c["dt"], c["B"], c["C"], c["A"], c["D"], c["dt_bias"])
     y1, h1 = SD.ssd_fwd(*args, y_dtype=c["y_dtype"], **kw)
     y2 = torch.empty_like(y1)
@@ -65,7 +66,11 @@ def test_noalloc_refuses_beyond_scratch():
     # 16 groups of 128 states over 8192 tokens need 128 slots x 16 groups x 12 KiB = 24 MiB > 16 MiB
     c = case(32, (8192,), 16, 16, 128, False, torch.float32)
     a = SD.fwd_args(c["x"], c["dt"], c["B"], c["C"], c["A"], c["D"], c["dt_bias"],
-                    y=torch.empty(c["T"], 16, 64, device=DEV))
+                    y=torch.empty(c["T"], 16, 64, device=DEV), cb_mode=SD.CB_PREPASS)
     assert SD.workspace_bytes(a) > SD.SCRATCH_BYTES
     st = SD.load_library().samba_ssd_fwd_noalloc(ctypes.byref(a), None)
     assert st == 9   # SAMBA_ERR_WORKSPACE, nothing enqueued
+    # formed inside the prefill kernel, the same call needs no scratch and runs
+    say("case: noalloc in-kernel C B^T", c["T"], "tokens")
+    (y1, h1), (y2, h2) = run_both(c, SD.CB_IN_KERNEL)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
