@@ -143,6 +143,22 @@ __device__ __forceinline__ float quad_allsum(float v) {
   return v;
 }
 
+// rotation by N lanes within each row of 16 lanes
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + N, 0xF, 0xF, true));
+}
+// reduce-scatter steps: lanes 0..31 get lo + lo of the lane 32 above, lanes 32..63 hi + hi of the lane 32
+// below; likewise over rows of 16 (even rows keep lo, odd rows hi)
+__device__ __forceinline__ float swap32_sum(float lo, float hi) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+__device__ __forceinline__ float swap16_sum(float lo, float hi) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -156,6 +172,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // last token makes ragged tails free of per-lane predicates.
 // ---------------------------------------------------------------------------
 using rsrc_t = __amdgpu_buffer_rsrc_t;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped, unswizzled) buffer
 
 template <typename T>
@@ -956,10 +973,6 @@ __global__ __launch_bounds__(64 * W, 4) void scan_split8_kernel(FwdParams p) {  
 // ---------------------------------------------------------------------------
 constexpr int kBK = 8;      // tokens per backward slice = checkpoint interval
 constexpr int kParW = 20;   // per-sequence partial row: dA[16], dD, ddt_bias, 2 pad (16-byte rows)
-// dB/dC channel-sum scratch: dB of channel c at [16c, 16c+16), dC at kDbcOff + 16c.  Each lane's float4
-// writes are contiguous across the wave, and the 16-float shift of the dC block puts a half-wave's reads
-// of dB (lanes 0..15) and dC (lanes 16..31) on different banks.
-constexpr int kDbcOff = kCPW * kN + 16;
 
 struct BwdParams {
   const void *x, *dt, *z, *B, *C, *dy;
@@ -982,7 +995,6 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
   __shared__ float4 s_bc[W][2][K * kN / 4];   // B, C rows of the slice (fp32)
   __shared__ float4 s_sc[W][K][kCPW];         // per token and channel: (Δ, Δx, dr, 0), masked
   __shared__ float4 s_tok[W][K / 4][64];      // this lane's tokens: (x, dy, sigmoid(v), silu'(z))
-  __shared__ float s_red[W][kDbcOff + kCPW * kN];   // one token's dB [channel][16], then dC [channel][16]
   __shared__ float4 s_agg[W][2][64];          // slice (P, Ĝ); after the last chunk: per-wave parameter sums
   __shared__ float4 s_carry[2][64];           // adjoint entering a chunk from the right, double buffered
 
@@ -1024,7 +1036,6 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
   float* sC = reinterpret_cast<float*>(s_bc[wave][1]);
   const float4* sB4 = s_bc[wave][0];
   const float4* sC4 = s_bc[wave][1];
-  float* red = s_red[wave];
 
   // adjoint entering the sequence's last token from the right: dh_last
   float gh[kSPL] = {0.f, 0.f, 0.f, 0.f};
@@ -1168,8 +1179,10 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
     // ---- reverse sweep: every gradient term
     const int prow = rem < 0 ? 0 : rem;
     const rsrc_t rbc = make_rsrc_rows(p.dbc + (static_cast<int64_t>(tile) * p.total_tokens + t0) * 32, prow, 32u);
-    const int half = lane >> 5, o = lane & 31;
-    const int obase = (o >> 4) * kDbcOff + (o & 15);   // output o = kind * 16 + n
+    // after the channel reduction below, lanes with channel bits 2..3 clear write outputs 16 (lane bit 5) +
+    // 4 g + 2 (lane bit 4) + 0..1 of the token's row (kind dB / dC, then the state)
+    const bool dbc_writer = (lane & 12) == 0;
+    const uint32_t dbc_off = static_cast<uint32_t>(16 * (lane >> 5) + 4 * g + 2 * ((lane >> 4) & 1)) * 4u;
     float sau_t[K / 4], sgb_t[K / 4];
     // one token k of the reverse sweep, with Ā_k, h_{k-1} and h_k; returns its (Σ g A2 Ā h_{k-1}, Σ g B) partials
     auto rev_token = [&](int k, const float (&a)[kSPL], const float (&hprev)[kSPL], const float (&hc)[kSPL],
@@ -1192,19 +1205,22 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
         dcv[i] = sc.z * hc[i];
         gh[i] = a[i] * gi;
       }
-      // this token's dB / dC summed over the wave's 16 channels: lanes 0..31 take channels 0..7 and
-      // lanes 32..63 channels 8..15 of output (lane & 31); one lane swap adds the halves
-      *reinterpret_cast<float4*>(red + c * kN + 4 * g) = make_float4(db[0], db[1], db[2], db[3]);
-      *reinterpret_cast<float4*>(red + kDbcOff + c * kN + 4 * g) = make_float4(dcv[0], dcv[1], dcv[2], dcv[3]);
-      wave_lds_sync();
-      float acc = 0.f;
+      // this token's dB / dC summed over the wave's 16 channels (lane bits 2..5), in registers: a
+      // reduce-scatter over bit 5 (the lower half keeps dB, the upper dC) and bit 4 (states 0, 1 of the
+      // lane's four, or 2, 3), then rotations within each row of 16 lanes add over bits 2 and 3
+      float u[4], w[2];
 #pragma unroll
-      for (int c2 = 0; c2 < kCPW / 2; ++c2) acc += red[obase + (8 * half + c2) * kN];
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc), __float_as_uint(acc), false, false);
-      acc += __uint_as_float(sw[1]);   // lanes 0..31: + the value of lane + 32
-      if (half == 0)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rbc, static_cast<uint32_t>((k * 32 + o) * 4),
-                                              0, 0);
+      for (int i = 0; i < 4; ++i) u[i] = swap32_sum(db[i], dcv[i]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        w[i] = swap16_sum(u[i], u[i + 2]);
+        w[i] += row_ror<4>(w[i]);
+        w[i] += row_ror<8>(w[i]);
+      }
+      if (dbc_writer) {
+        const u32x2_t wv = {__float_as_uint(w[0]), __float_as_uint(w[1])};
+        __builtin_amdgcn_raw_buffer_store_b64(wv, rbc, static_cast<uint32_t>(k * 32 * 4) + dbc_off, 0, 0);
+      }
     };
     static_assert(H == 4, "one quad group per half");
     // second half (tokens K-1 .. H) from the registers
