@@ -991,9 +991,10 @@ struct BwdParams {
 template <typename T, int W>
 __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
   constexpr int K = kBK;
-  // LDS, per wave (9 KiB) plus 2 KiB per workgroup: four 4-wave workgroups fit a CU.
+  // LDS, per wave (7.1 KiB) plus 2 KiB per workgroup: 30.5 KiB for 4 waves.
   __shared__ float4 s_bc[W][2][K * kN / 4];   // B, C rows of the slice (fp32)
-  __shared__ float4 s_sc[W][K][kCPW];         // per token and channel: (Δ, Δx, dr, 0), masked
+  __shared__ float4 s_sc[W][K][kCPW + 1];     // per token and channel: (Δ, Δx, dr, 0), masked (rows padded:
+                                              // the four tokens of a lane quad land on different banks)
   __shared__ float4 s_tok[W][K / 4][64];      // this lane's tokens: (x, dy, sigmoid(v), silu'(z))
   __shared__ float4 s_agg[W][2][64];          // slice (P, Ĝ); after the last chunk: per-wave parameter sums
   __shared__ float4 s_carry[2][64];           // adjoint entering a chunk from the right, double buffered
