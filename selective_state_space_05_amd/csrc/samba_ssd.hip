@@ -272,9 +272,12 @@ __device__ __forceinline__ void wave_sync() {
 //      C as row-major pieces, B and X as pairs of rows at one 8-column run (so that the transposed stores
 //      of consecutive lanes are consecutive words); every helper computes Δ, la and w of the chunk with a
 //      DPP prefix sum (helper 0 publishes them, the others keep their own copy for step 2);
-//   2. helpers 0 .. 2 turn the chunk's Sᵀ tile h (loaded from the workspace two chunks earlier) into M
-//      = Sᵀ 2^(la_t - la_s) Δ_s (s <= t), + D on the diagonal, published as bf16 hi + lo operand images;
-//   3. load chunk c + 3 and the workspace tile of chunk c + 3.
+//   2. helpers 0 .. 2 turn the chunk's Sᵀ tile h into M = Sᵀ 2^(la_t - la_s) Δ_s (s <= t), + D on the
+//      diagonal, published as bf16 hi + lo operand images.  In the pre-pass form the tile was loaded from
+//      the workspace two chunks earlier and M is built right away; by default (kCbIn) every helper also
+//      stages B row-major, and after the next barrier (once all of B and C are staged) helpers 0 .. 2 form
+//      their tiles on the matrix cores from LDS and build M;
+//   3. load chunk c + 3 (and, in the pre-pass form, its workspace tile).
 template <int N, bool kCbIn>
 __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
   constexpr int kRow = Stage<N>::kRow;
