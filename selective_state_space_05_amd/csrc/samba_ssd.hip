@@ -103,6 +103,15 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int k) {
   return k == 0 ? v.x : (k == 1 ? v.y : (k == 2 ? v.z : v.w));
 }
 
+// Position (bf16 units) of token s in row `row` of a transposed tile (B as [n][s], X as [p][s]): the row's
+// eight 16-byte groups of tokens are XOR-permuted by bits 4-5 of the row index.  The helpers write a token pair
+// of eight rows per lane group (their loads read whole rows of B and X), the state waves read eight tokens of
+// one row per lane (consecutive rows across lanes); with the permutation both are free of bank conflicts on
+// the 64 four-byte banks, and a group stays whole, so the operand reads stay single 16-byte reads.
+__device__ __forceinline__ int tpos(int row, int s) {
+  return row * kTRow + 8 * ((s >> 3) ^ (2 * ((row >> 4) & 3))) + (s & 7);
+}
+
 // two 4-element runs of a bf16 row as one 8-element operand
 __device__ __forceinline__ bf16x8_t cat4(const uint16_t* p0, const uint16_t* p1) {
   const bf16x4_t u = *reinterpret_cast<const bf16x4_t*>(p0);
@@ -228,7 +237,7 @@ struct Smem {
   Stage<N> st[2];                                   // chunk c uses st[c & 1]
   uint16_t brm[kQ * Stage<N>::kRow];                // B [s][n] of the chunk being prepared (C Bᵀ in kernel)
   float4 xch[4][4][64];                             // (d) partial sums for the partner wave
-  float hs[4][2][kQ];                               // each helper wave's own la, Δ of the chunk it prepares
+  float hs[4][2][kQ];                               // (pre-pass form) each helper's own la, Δ of its chunk
 };
 
 // Per-workgroup views of one (sequence, head): rows past the sequence read as 0 and are not written.
@@ -269,9 +278,11 @@ __device__ __forceinline__ void wave_sync() {
 
 // Helper waves (h = 0 .. 3).  While the state waves compute chunk c, the helpers
 //   1. stage chunk c + 1 (loaded two chunks earlier into a ring of two register sets) into its LDS stage:
-//      C as row-major pieces, B and X as pairs of rows at one 8-column run (so that the transposed stores
-//      of consecutive lanes are consecutive words); every helper computes Δ, la and w of the chunk with a
-//      DPP prefix sum (helper 0 publishes them, the others keep their own copy for step 2);
+//      C as row-major pieces, B and X transposed (each lane holds a 16-byte piece of two consecutive rows
+//      and stores token pairs; eight lanes read one 128-byte row segment, so the loads are whole cache
+//      lines, and the transposed rows are permuted by tpos so the stores are free of bank conflicts); helper
+//      0 computes Δ, la and w of the chunk with a DPP prefix sum and publishes them (in the pre-pass form
+//      helpers 1 .. 2 compute their own copy for step 2, which comes before the barrier);
 //   2. helpers 0 .. 2 turn the chunk's Sᵀ tile h into M = Sᵀ 2^(la_t - la_s) Δ_s (s <= t), + D on the
 //      diagonal, published as bf16 hi + lo operand images.  In the pre-pass form the tile was loaded from
 //      the workspace two chunks earlier and M is built right away; by default (kCbIn) every helper also
@@ -283,11 +294,13 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
   constexpr int kRow = Stage<N>::kRow;
   constexpr int NPR = N / 8;              // 16-byte pieces per C row
   constexpr int PC = N / 32;              // C pieces per helper thread
-  constexpr int NB = N / 64;              // B passes (8-column runs 8 (c + 8 i))
+  constexpr int NB = N / 64;              // B passes (16-byte pieces pc + 8 i of a row)
   const int t = static_cast<int>(threadIdx.x) - 256;
   const int lane = t & 63, l32 = lane & 31, hi = lane >> 5;
   const int hw = __builtin_amdgcn_readfirstlane(t >> 6);   // helper index
-  const int r = t & 31, cg = t >> 5;      // row pair, 8-column run
+  // B and X loads: token pair rr (rows 2 rr, 2 rr + 1), 16-byte piece pc; one load instruction reads eight whole
+  // 128-byte row segments
+  const int rr = 8 * hw + (lane >> 3), pc = lane & 7;
   // M tile of this helper: (s-tile, t-tile) = (0, 0), (0, 1), (1, 1); helper 3 has none
   const int m_si = hw == 2 ? 1 : 0, m_tb = hw == 0 ? 0 : 1;
   const int tile = hw < 3 ? hw : 2;       // (helper 3 loads a tile it does not use: no branch around loads)
@@ -309,11 +322,14 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
     for (int i = 0; i < NB; ++i)
 #pragma unroll
       for (int k = 0; k < 2; ++k)
-        st.br[i][k] = ld16(cx.rb, static_cast<uint32_t>(c0 + 2 * r + k) * cx.rowbc + (8 * (cg + 8 * i)) * 2);
+        st.br[i][k] = ld16(cx.rb, static_cast<uint32_t>(c0 + 2 * rr + k) * cx.rowbc + (pc + 8 * i) * 16);
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      st.xr[k] = ld16(cx.rx, static_cast<uint32_t>(c0 + 2 * r + k) * cx.rowx + (8 * cg) * 2);
-    st.dtr = __builtin_amdgcn_raw_buffer_load_b16(cx.rdt, static_cast<uint32_t>(c0 + lane) * cx.H * 2, 0, 0);
+      st.xr[k] = ld16(cx.rx, static_cast<uint32_t>(c0 + 2 * rr + k) * cx.rowx + pc * 16);
+    // Δ: with C Bᵀ formed here only helper 0 needs it (the others read its la and Δ from the stage after the
+    // next barrier) and the others read one row
+    const int dtok = (kCbIn && hw != 0) ? 0 : lane;
+    st.dtr = __builtin_amdgcn_raw_buffer_load_b16(cx.rdt, static_cast<uint32_t>(c0 + dtok) * cx.H * 2, 0, 0);
     if constexpr (!kCbIn) {
       // the chunk's Sᵀ tile (the last chunk's past the sequence: a padding chunk's M is the skip alone)
       const int cs = c < nchunks ? c : nchunks - 1;
@@ -328,21 +344,40 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
       }
     }
   };
-  // M = Sᵀ 2^(la_t - la_s) Δ_s (s <= t), + D on the diagonal, from the helper's Sᵀ tile and its own copy
-  // of the chunk's la and Δ, published as bf16 hi + lo operand images
-  auto build_m = [&](Stage<N>& g, f32x16_t m) {
-    const int t_own = 32 * m_tb + l32;
-    const float la_t = sm.hs[hw][0][t_own];
+  // M = Sᵀ 2^(la_t - la_s) Δ_s (s <= t), + D on the diagonal, from the helper's Sᵀ tile and the chunk's la
+  // and Δ, published as bf16 hi + lo operand images.  The la and Δ values are read into
+  // registers first (before the product that feeds M, when it is formed here) and the causal mask is a
+  // select, so that no LDS read waits inside the mask.
+  struct Decay {
+    float la_t;
+    float4 las[4], dls[4];
+  };
+  // (la and Δ: helper 0's, in the stage, when C Bᵀ is formed after the barrier; the helper's own otherwise)
+  auto load_decay = [&](const Stage<N>& g) {
+    const float* la = kCbIn ? g.la : sm.hs[hw][0];
+    const float* dl = kCbIn ? g.dl : sm.hs[hw][1];
+    Decay d;
+    d.la_t = la[32 * m_tb + l32];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int s0 = 32 * m_si + 8 * q + 4 * hi;
-      const float4 las = *reinterpret_cast<const float4*>(&sm.hs[hw][0][s0]);
-      const float4 dls = *reinterpret_cast<const float4*>(&sm.hs[hw][1][s0]);
-      const float lv[4] = {las.x, las.y, las.z, las.w}, dv[4] = {dls.x, dls.y, dls.z, dls.w};
+      d.las[q] = *reinterpret_cast<const float4*>(&la[s0]);
+      d.dls[q] = *reinterpret_cast<const float4*>(&dl[s0]);
+    }
+    return d;
+  };
+  auto build_m = [&](Stage<N>& g, f32x16_t m, const Decay& d) {
+    const int t_own = 32 * m_tb + l32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int s0 = 32 * m_si + 8 * q + 4 * hi;
+      const float lv[4] = {d.las[q].x, d.las[q].y, d.las[q].z, d.las[q].w};
+      const float dv[4] = {d.dls[q].x, d.dls[q].y, d.dls[q].z, d.dls[q].w};
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int sv = s0 + rr;
-        float v = sv <= t_own ? m[4 * q + rr] * __builtin_amdgcn_exp2f(la_t - lv[rr]) * dv[rr] : 0.0f;
+        const float e = __builtin_amdgcn_exp2f(d.la_t - lv[rr]);   // (> 1 above the diagonal: masked)
+        float v = sv <= t_own ? m[4 * q + rr] * e * dv[rr] : 0.0f;
         v += sv == t_own ? cx.Dh : 0.0f;
         m[4 * q + rr] = v;
       }
@@ -370,19 +405,21 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t w0 = word(st.br[i][0], j / 2), w1 = word(st.br[i][1], j / 2);
-        *reinterpret_cast<uint32_t*>(&g.bt[(8 * (cg + 8 * i) + j) * kTRow + 2 * r]) =
-            (j & 1) ? highs(w0, w1) : lows(w0, w1);
+        *reinterpret_cast<uint32_t*>(&g.bt[tpos(8 * (pc + 8 * i) + j, 2 * rr)]) = (j & 1) ? highs(w0, w1) : lows(w0, w1);
       }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t w0 = word(st.xr[0], j / 2), w1 = word(st.xr[1], j / 2);
-      *reinterpret_cast<uint32_t*>(&g.xt[(8 * cg + j) * kTRow + 2 * r]) = (j & 1) ? highs(w0, w1) : lows(w0, w1);
+      *reinterpret_cast<uint32_t*>(&g.xt[tpos(8 * pc + j, 2 * rr)]) = (j & 1) ? highs(w0, w1) : lows(w0, w1);
     }
     // Δ, la (inclusive prefix sum of Δ A log2e) and w = 2^(la_end - la) Δ; tokens past the sequence get
     // Δ = 0 (no decay, no input)
-    const float dlt = c0 + lane < cx.len ? softplus_f32(widen(st.dtr) + cx.bias) : 0.0f;
-    const float l = wave_prefix_sum(dlt * cx.A2);
+    float dlt = 0.0f, l = 0.0f;
+    if (!kCbIn || hw == 0) {
+      dlt = c0 + lane < cx.len ? softplus_f32(widen(st.dtr) + cx.bias) : 0.0f;
+      l = wave_prefix_sum(dlt * cx.A2);
+    }
     if (hw == 0) {
       const float l_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 63));
       g.dl[lane] = dlt;
@@ -395,13 +432,15 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
       for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int k = 0; k < 2; ++k)
-          *reinterpret_cast<uint4*>(&sm.brm[(2 * r + k) * kRow + 8 * (cg + 8 * i)]) = st.br[i][k];
+          *reinterpret_cast<uint4*>(&sm.brm[(2 * rr + k) * kRow + 8 * (pc + 8 * i)]) = st.br[i][k];
     }
-    if (hw < 3) {
-      sm.hs[hw][0][lane] = l;
-      sm.hs[hw][1][lane] = dlt;
-      wave_sync();
-      if constexpr (!kCbIn) build_m(g, sring[K]);
+    if constexpr (!kCbIn) {
+      if (hw < 3) {
+        sm.hs[hw][0][lane] = l;
+        sm.hs[hw][1][lane] = dlt;
+        wave_sync();
+        build_m(g, sring[K], load_decay(g));
+      }
     }
   };
   // C Bᵀ formed here: the helper's tile of chunk c from B and C row-major in LDS (staged by all helpers
@@ -410,14 +449,17 @@ __device__ __forceinline__ void helper_wave(const Ctx& cx, Smem<N>& sm) {
   auto form_m = [&](auto kset) {
     Stage<N>& g = sm.st[decltype(kset)::value];
     if (hw < 3) {
-      f32x16_t m = f32x16_t{};
+      const Decay d = load_decay(g);
+      bf16x8_t bo[N / 16], co[N / 16];
 #pragma unroll
       for (int kk = 0; kk < N / 16; ++kk) {
-        const bf16x8_t bo = *reinterpret_cast<const bf16x8_t*>(&sm.brm[(32 * m_si + l32) * kRow + 8 * hi + 16 * kk]);
-        const bf16x8_t co = *reinterpret_cast<const bf16x8_t*>(&g.c[(32 * m_tb + l32) * kRow + 8 * hi + 16 * kk]);
-        m = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo, co, m, 0, 0, 0);
+        bo[kk] = *reinterpret_cast<const bf16x8_t*>(&sm.brm[(32 * m_si + l32) * kRow + 8 * hi + 16 * kk]);
+        co[kk] = *reinterpret_cast<const bf16x8_t*>(&g.c[(32 * m_tb + l32) * kRow + 8 * hi + 16 * kk]);
       }
-      build_m(g, m);
+      f32x16_t m = f32x16_t{};
+#pragma unroll
+      for (int kk = 0; kk < N / 16; ++kk) m = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bo[kk], co[kk], m, 0, 0, 0);
+      build_m(g, m, d);
     }
   };
   // An even number of chunks (the state waves pad the same way; a chunk past the sequence reads zeros and
@@ -518,8 +560,8 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
     for (int si = 0; si <= HB; ++si)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint16_t* row = &g.xt[p_own * kTRow + 32 * si + 16 * kk + 4 * hi];
-        xop[si][kk] = cat4(row, row + 8);
+        const int s = 32 * si + 16 * kk + 4 * hi;
+        xop[si][kk] = cat4(&g.xt[tpos(p_own, s)], &g.xt[tpos(p_own, s + 8)]);
       }
     const float la_t = g.la[t_own];
     const float decay = __builtin_amdgcn_exp2f(g.la[kQ - 1]);
@@ -562,7 +604,7 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int s0 = 16 * kk + 8 * hi;
-      const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(&g.xt[p_own * kTRow + s0]);
+      const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(&g.xt[tpos(p_own, s0)]);
       const float4 w0 = *reinterpret_cast<const float4*>(&g.w[s0]);
       const float4 w1 = *reinterpret_cast<const float4*>(&g.w[s0 + 4]);
       const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -576,7 +618,7 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
       }
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
-        const bf16x8_t bop = *reinterpret_cast<const bf16x8_t*>(&g.bt[(32 * (HB * NTW + i) + l32) * kTRow + s0]);
+        const bf16x8_t bop = *reinterpret_cast<const bf16x8_t*>(&g.bt[tpos(32 * (HB * NTW + i) + l32, s0)]);
         hst[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, xh, hst[i], 0, 0, 0);
         hst[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, xl, hst[i], 0, 0, 0);
       }
