@@ -53,6 +53,8 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 using rsrc_t = __amdgpu_buffer_rsrc_t;
 
 constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped, unswizzled) buffer
@@ -119,15 +121,23 @@ __device__ __forceinline__ bf16x8_t cat4(const uint16_t* p0, const uint16_t* p1)
   return __builtin_shufflevector(u, v, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// a and b rounded to bf16 (to nearest even) by one paired conversion, a in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+// bf16 hi + lo of a and b: hi = bf16(v), lo = bf16(v - hi), each a packed pair (one conversion per pair)
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
 // the 8 accumulator elements e0 .. e0 + 7 as a bf16 hi + lo pair
 __device__ __forceinline__ void split8(const f32x16_t& acc, int e0, bf16x8_t& hi, bf16x8_t& lo) {
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float v = acc[e0 + j];
-    const __bf16 h = static_cast<__bf16>(v);
-    hi[j] = h;
-    lo[j] = static_cast<__bf16>(v - static_cast<float>(h));
-  }
+  for (int j = 0; j < 4; ++j) split2(acc[e0 + 2 * j], acc[e0 + 2 * j + 1], h[j], l[j]);
+  hi = __builtin_bit_cast(bf16x8_t, u32x4_t{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8_t, u32x4_t{l[0], l[1], l[2], l[3]});
 }
 
 struct SsdParams {
@@ -608,14 +618,13 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
       const float4 w0 = *reinterpret_cast<const float4*>(&g.w[s0]);
       const float4 w1 = *reinterpret_cast<const float4*>(&g.w[s0 + 4]);
       const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      bf16x8_t xh, xl;
+      uint32_t xhw[4], xlw[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = static_cast<float>(xv[j]) * wv[j];
-        const __bf16 hv = static_cast<__bf16>(v);
-        xh[j] = hv;
-        xl[j] = static_cast<__bf16>(v - static_cast<float>(hv));
-      }
+      for (int j = 0; j < 4; ++j)
+        split2(static_cast<float>(xv[2 * j]) * wv[2 * j], static_cast<float>(xv[2 * j + 1]) * wv[2 * j + 1], xhw[j],
+               xlw[j]);
+      const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, u32x4_t{xhw[0], xhw[1], xhw[2], xhw[3]});
+      const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, u32x4_t{xlw[0], xlw[1], xlw[2], xlw[3]});
 #pragma unroll
       for (int i = 0; i < NTW; ++i) {
         const bf16x8_t bop = *reinterpret_cast<const bf16x8_t*>(&g.bt[tpos(32 * (HB * NTW + i) + l32, s0)]);
@@ -642,10 +651,7 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
       }
       const uint32_t off = yrow + (32 * a + 8 * q + 4 * hi) * static_cast<uint32_t>(sizeof(Tout));
       if constexpr (sizeof(Tout) == 2) {
-        const u32x2_t w = {static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[0]))) |
-                               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[1]))) << 16),
-                           static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[2]))) |
-                               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[3]))) << 16)};
+        const u32x2_t w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         __builtin_amdgcn_raw_buffer_store_b64(w, cx.ry, off, 0, 0);
       } else {
         const u32x4_t w = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
