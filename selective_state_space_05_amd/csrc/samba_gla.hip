@@ -330,6 +330,8 @@ __global__ __launch_bounds__(64 * kWaves) void gla_fwd_kernel(GlaParams p) {
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kCQ = 64;        // tokens per chunk
 constexpr int kVtRow = 72;     // LDS row of the transposed v tile (bf16): 64 tokens + 8 (16 rows on distinct banks)
 
@@ -386,29 +388,33 @@ __device__ __forceinline__ ChunkSeq chunk_seq(const GlaChunkParams& p, int s) {
 }
 
 __device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
-__device__ __forceinline__ uint16_t bf16r(float v) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
-// v as hi + lo bf16 (hi = v rounded, lo = the remainder rounded)
-__device__ __forceinline__ void hilo(float v, uint16_t& h, uint16_t& l) {
-  const __bf16 b = static_cast<__bf16>(v);
-  h = __builtin_bit_cast(uint16_t, b);
-  l = bf16r(v - static_cast<float>(b));
+// a and b rounded to bf16 (to nearest even) by one paired conversion, a in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
-__device__ __forceinline__ uint4 pack8(const uint16_t (&e)[8]) {
-  return make_uint4(e[0] | (static_cast<uint32_t>(e[1]) << 16), e[2] | (static_cast<uint32_t>(e[3]) << 16),
-                    e[4] | (static_cast<uint32_t>(e[5]) << 16), e[6] | (static_cast<uint32_t>(e[7]) << 16));
+// a and b as hi + lo bf16 (hi = v rounded, lo = the remainder rounded), each a packed pair
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+// v[0 .. 7] as hi + lo bf16, element j in half j % 2 of word j / 2
+__device__ __forceinline__ void hilo8(const float (&v)[8], uint4& h, uint4& l) {
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) split2(v[2 * j], v[2 * j + 1], hw[j], lw[j]);
+  h = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  l = make_uint4(lw[0], lw[1], lw[2], lw[3]);
 }
 // key at contraction position p of a 16-key group (and back: the map is its own inverse)
 __device__ __forceinline__ int swap23(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
 // the 8 accumulator elements e0 .. e0 + 7 as a bf16 hi + lo pair
 __device__ __forceinline__ void split8(const f32x16_t& acc, int e0, bf16x8_t& hi, bf16x8_t& lo) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float v = acc[e0 + j];
-    const __bf16 b = static_cast<__bf16>(v);
-    hi[j] = b;
-    lo[j] = static_cast<__bf16>(v - static_cast<float>(b));
-  }
+  const float v[8] = {acc[e0], acc[e0 + 1], acc[e0 + 2], acc[e0 + 3], acc[e0 + 4], acc[e0 + 5], acc[e0 + 6], acc[e0 + 7]};
+  uint4 h, l;
+  hilo8(v, h, l);
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  lo = __builtin_bit_cast(bf16x8_t, l);
 }
 __device__ __forceinline__ bf16x8_t ldop(const unsigned char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
@@ -528,30 +534,34 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(GlaChunkParams p) {
     for (int i = tid; i < kCQ * KP / 8; i += kT) {
       const int t = i / (KP / 8), p8 = i - t * (KP / 8);
       const int pg = p8 + nb / 8;   // position group among all N keys
-      uint16_t hv[8], lv[8];
+      float v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int n = (p8 & ~1) * 8 + swap23(8 * (p8 & 1) + j);
-        hilo(bf16f(sQ[t * kQR + n]) * __builtin_amdgcn_exp2f(sB[t * kBR + n] * kLog2e), hv[j], lv[j]);
+        v[j] = bf16f(sQ[t * kQR + n]) * __builtin_amdgcn_exp2f(sB[t * kBR + n] * kLog2e);
       }
+      uint4 hq, lq;
+      hilo8(v, hq, lq);
       const int ln = 16 * (32 * (p8 & 1) + (t & 31));
-      *reinterpret_cast<uint4*>(ws + W::qs(t >> 5, pg >> 2, (pg >> 1) & 1, 0) + ln) = pack8(hv);
-      *reinterpret_cast<uint4*>(ws + W::qs(t >> 5, pg >> 2, (pg >> 1) & 1, 1) + ln) = pack8(lv);
+      *reinterpret_cast<uint4*>(ws + W::qs(t >> 5, pg >> 2, (pg >> 1) & 1, 0) + ln) = hq;
+      *reinterpret_cast<uint4*>(ws + W::qs(t >> 5, pg >> 2, (pg >> 1) & 1, 1) + ln) = lq;
     }
     // (k ⊙ e^{b_64 − b_s})ᵀ: 8 tokens of one key per item
     for (int i = tid; i < KP * kCQ / 8; i += kT) {
       const int n = i % KP, tb = i / KP;
       const int ng = nb + n;
       const float be = sB[(kCQ - 1) * kBR + n];
-      uint16_t hv[8], lv[8];
+      float v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int t = 8 * tb + j;
-        hilo(bf16f(sK[t * kQR + n]) * __builtin_amdgcn_exp2f((be - sB[t * kBR + n]) * kLog2e), hv[j], lv[j]);
+        v[j] = bf16f(sK[t * kQR + n]) * __builtin_amdgcn_exp2f((be - sB[t * kBR + n]) * kLog2e);
       }
+      uint4 hk, lk;
+      hilo8(v, hk, lk);
       const int ln = 16 * (32 * (tb & 1) + (ng & 31));
-      *reinterpret_cast<uint4*>(ws + W::kt(ng >> 5, tb >> 1, 0) + ln) = pack8(hv);
-      *reinterpret_cast<uint4*>(ws + W::kt(ng >> 5, tb >> 1, 1) + ln) = pack8(lv);
+      *reinterpret_cast<uint4*>(ws + W::kt(ng >> 5, tb >> 1, 0) + ln) = hk;
+      *reinterpret_cast<uint4*>(ws + W::kt(ng >> 5, tb >> 1, 1) + ln) = lk;
     }
     __syncthreads();   // the pass's span flags
     const bool w0 = sWide[0] != 0, w1 = sWide[1] != 0;   // (block-uniform)
@@ -560,17 +570,19 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(GlaChunkParams p) {
     if (wave < 3 && !(wave != 1 && (diag == 0 ? w0 : w1))) {
       for (int kk = 0; kk < KP / 16; ++kk) {
         const int n0 = 16 * kk + 8 * hl;
-        bf16x8_t ah, al, bh, bl;
+        float xs[8], ys[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int n = n0 + j;
           const float m = ref31 ? sB[31 * kBR + n] : 0.f;
-          const float x = bf16f(sQ[tq * kQR + n]) * __builtin_amdgcn_exp2f((sB[tq * kBR + n] - m) * kLog2e);
-          const float y = bf16f(sK[tk * kQR + n]) * __builtin_amdgcn_exp2f((m - sB[tk * kBR + n]) * kLog2e);
-          const __bf16 xh = static_cast<__bf16>(x), yh = static_cast<__bf16>(y);
-          ah[j] = xh; al[j] = static_cast<__bf16>(x - static_cast<float>(xh));
-          bh[j] = yh; bl[j] = static_cast<__bf16>(y - static_cast<float>(yh));
+          xs[j] = bf16f(sQ[tq * kQR + n]) * __builtin_amdgcn_exp2f((sB[tq * kBR + n] - m) * kLog2e);
+          ys[j] = bf16f(sK[tk * kQR + n]) * __builtin_amdgcn_exp2f((m - sB[tk * kBR + n]) * kLog2e);
         }
+        uint4 xh, xl, yh, yl;
+        hilo8(xs, xh, xl);
+        hilo8(ys, yh, yl);
+        const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, xh), al = __builtin_bit_cast(bf16x8_t, xl);
+        const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, yh), bl = __builtin_bit_cast(bf16x8_t, yl);
         acc = mfma(ah, bh, acc);
         acc = mfma(ah, bl, acc);
         acc = mfma(al, bh, acc);
@@ -616,17 +628,19 @@ __global__ __launch_bounds__(512) void gla_prep_kernel(GlaChunkParams p) {
     const int ln = i & 63, kk = (i >> 6) & 3, ft = i >> 8;
     const int tl = ln & 31, s0 = 16 * kk + 8 * (ln >> 5);
     const int fb = s0 >> 5;
-    uint16_t hv[8], lv[8];
+    float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int sl = (s0 & 31) + j;
       float a = 0.f;
       if (ft == 1 && fb == 0) a = sA[1][tl * kAR + sl];
       else if (ft == fb && sl <= tl) a = sA[2 * ft][tl * kAR + sl];
-      hilo(a, hv[j], lv[j]);
+      v[j] = a;
     }
-    *reinterpret_cast<uint4*>(ws + W::am(ft, kk, 0) + 16 * ln) = pack8(hv);
-    *reinterpret_cast<uint4*>(ws + W::am(ft, kk, 1) + 16 * ln) = pack8(lv);
+    uint4 ha, la;
+    hilo8(v, ha, la);
+    *reinterpret_cast<uint4*>(ws + W::am(ft, kk, 0) + 16 * ln) = ha;
+    *reinterpret_cast<uint4*>(ws + W::am(ft, kk, 1) + 16 * ln) = la;
   }
 }
 
@@ -773,8 +787,7 @@ __global__ __launch_bounds__(64 * (N / 32)) void gla_chunk_kernel(GlaChunkParams
       const int64_t oe = (cs.t0 + static_cast<int64_t>(c) * kCQ + t) * p.heads * p.head_dim +
                          static_cast<int64_t>(h) * p.head_dim + v0 + 4 * q4;
       if constexpr (sizeof(Tout) == 2) {
-        const uint2 w2 = make_uint2(bf16r(a.x) | (static_cast<uint32_t>(bf16r(a.y)) << 16),
-                                    bf16r(a.z) | (static_cast<uint32_t>(bf16r(a.w)) << 16));
+        const uint2 w2 = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + oe) = w2;
       } else {
         *reinterpret_cast<float4*>(static_cast<float*>(p.o) + oe) = a;
