@@ -27,11 +27,13 @@
 //     and X is read from LDS in that order), and the Hᵀ accumulators (lane = column p) are (d)'s A operand
 //     the same way, with C read in the matching n order.  (d) over a wave's half of the states gives
 //     partial sums for both t-tiles; the other t-tile's goes to the partner wave through LDS;
-//   * helper waves 4 .. 7 load C, B, X and Δ through a ring of two register sets and stage them into
-//     LDS (C row-major, B and X transposed, each store a run of consecutive words across the lanes);
-//     each computes Δ, la and w with a DPP prefix sum, and three of them build the chunk's masked M tiles
-//     (in the default form between the two barriers of the chunk before, once every helper has staged B
-//     and C, each from its own Sᵀ tile formed on the matrix cores).
+//   * helper waves 4 .. 7 load C, B, X and Δ through a ring of two register sets (every load instruction
+//     reads whole 128-byte row segments) and stage them into LDS (C row-major; B and X transposed into
+//     tiles whose 16-byte token groups are permuted by row, so that both the transposing stores and the
+//     state waves' operand reads are free of bank conflicts); helper 0 computes Δ, la and w with a DPP
+//     prefix sum, and three helpers build the chunk's masked M tiles (in the default form between the two
+//     barriers of the chunk before, once every helper has staged B and C, each from its own Sᵀ tile formed
+//     on the matrix cores).
 //     (z and y in the state waves' layout are 8-byte pieces of 32 rows per instruction; staging y through
 //     LDS for whole-line stores by the helpers measured no faster.)
 // The inputs are staged in two alternating LDS buffers, so the helpers fill chunk c + 1's while the state
