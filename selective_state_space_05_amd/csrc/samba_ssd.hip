@@ -610,30 +610,36 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
         yd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xop[si][kk], g.m[si + HB][kk][1][lane], yd, 0, 0, 0);
       }
 
-    // (e) Hᵀ = 2^(la_end) Hᵀ + Bᵀ (w X), w X as a bf16 hi + lo pair
+    // (e) Hᵀ = 2^(la_end) Hᵀ + Bᵀ (w X), w X as a bf16 hi + lo pair.  It reads only this chunk's stage,
+    // which stays valid until the second barrier: with a gate it runs before the first barrier (the gated
+    // epilogue fills the wait for the helpers' M tiles), without one after the epilogue (which is then
+    // short, and the state waves would wait there instead).
+    auto update_state = [&]() {
 #pragma unroll
-    for (int i = 0; i < NTW; ++i) hst[i] *= decay;
+      for (int i = 0; i < NTW; ++i) hst[i] *= decay;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int s0 = 16 * kk + 8 * hi;
-      const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(&g.xt[tpos(p_own, s0)]);
-      const float4 w0 = *reinterpret_cast<const float4*>(&g.w[s0]);
-      const float4 w1 = *reinterpret_cast<const float4*>(&g.w[s0 + 4]);
-      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      uint32_t xhw[4], xlw[4];
+      for (int kk = 0; kk < 4; ++kk) {
+        const int s0 = 16 * kk + 8 * hi;
+        const bf16x8_t xv = *reinterpret_cast<const bf16x8_t*>(&g.xt[tpos(p_own, s0)]);
+        const float4 w0 = *reinterpret_cast<const float4*>(&g.w[s0]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&g.w[s0 + 4]);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        uint32_t xhw[4], xlw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        split2(static_cast<float>(xv[2 * j]) * wv[2 * j], static_cast<float>(xv[2 * j + 1]) * wv[2 * j + 1], xhw[j],
-               xlw[j]);
-      const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, u32x4_t{xhw[0], xhw[1], xhw[2], xhw[3]});
-      const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, u32x4_t{xlw[0], xlw[1], xlw[2], xlw[3]});
+        for (int j = 0; j < 4; ++j)
+          split2(static_cast<float>(xv[2 * j]) * wv[2 * j], static_cast<float>(xv[2 * j + 1]) * wv[2 * j + 1], xhw[j],
+                 xlw[j]);
+        const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, u32x4_t{xhw[0], xhw[1], xhw[2], xhw[3]});
+        const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, u32x4_t{xlw[0], xlw[1], xlw[2], xlw[3]});
 #pragma unroll
-      for (int i = 0; i < NTW; ++i) {
-        const bf16x8_t bop = *reinterpret_cast<const bf16x8_t*>(&g.bt[tpos(32 * (HB * NTW + i) + l32, s0)]);
-        hst[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, xh, hst[i], 0, 0, 0);
-        hst[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, xl, hst[i], 0, 0, 0);
+        for (int i = 0; i < NTW; ++i) {
+          const bf16x8_t bop = *reinterpret_cast<const bf16x8_t*>(&g.bt[tpos(32 * (HB * NTW + i) + l32, s0)]);
+          hst[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, xh, hst[i], 0, 0, 0);
+          hst[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, xl, hst[i], 0, 0, 0);
+        }
       }
-    }
+    };
+    if constexpr (kGate) update_state();
 
     __syncthreads();   // X1: the partner's partial sums are in LDS
     const float eo = __builtin_amdgcn_exp2f(la_t);
@@ -660,6 +666,7 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
         __builtin_amdgcn_raw_buffer_store_b128(w, cx.ry, off, 0, 0);
       }
     }
+    if constexpr (!kGate) update_state();
     ++cc;
     __syncthreads();   // X2: chunk computed, the next chunk prepared
   };
