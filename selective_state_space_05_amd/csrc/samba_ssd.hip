@@ -611,9 +611,9 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
       }
 
     // (e) Hᵀ = 2^(la_end) Hᵀ + Bᵀ (w X), w X as a bf16 hi + lo pair.  It reads only this chunk's stage,
-    // which stays valid until the second barrier: with a gate it runs before the first barrier (the gated
-    // epilogue fills the wait for the helpers' M tiles), without one after the epilogue (which is then
-    // short, and the state waves would wait there instead).
+    // which stays valid until the second barrier.  Before the first barrier, except without a gate when the
+    // helpers form the M tiles between the two: the ungated epilogue is short, and the state waves would
+    // wait there for the helpers instead.
     auto update_state = [&]() {
 #pragma unroll
       for (int i = 0; i < NTW; ++i) hst[i] *= decay;
@@ -639,7 +639,8 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
         }
       }
     };
-    if constexpr (kGate) update_state();
+    constexpr bool kLate = !kGate && kCbIn;
+    if constexpr (!kLate) update_state();
 
     __syncthreads();   // X1: the partner's partial sums are in LDS
     const float eo = __builtin_amdgcn_exp2f(la_t);
@@ -666,7 +667,7 @@ __device__ __forceinline__ void state_wave(const Ctx& cx, Smem<N>& sm, const flo
         __builtin_amdgcn_raw_buffer_store_b128(w, cx.ry, off, 0, 0);
       }
     }
-    if constexpr (!kGate) update_state();
+    if constexpr (kLate) update_state();
     ++cc;
     __syncthreads();   // X2: chunk computed, the next chunk prepared
   };
