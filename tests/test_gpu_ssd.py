@@ -120,6 +120,27 @@ def test_ssd_long_memory():
     check(y, yo, hl, ho, b, "f32")
 
 
+def test_ssd_strong_decay():
+    """Δ of 15-28 (dt_raw + bias past the softplus identity switch at 20) with A = -8 and -30: the decay
+    underflows to 0 within a token, so every exponent difference inside a chunk's M is far outside the fp32
+    range (masked entries overflow, unmasked ones underflow) and the state is memoryless.  Against the oracle,
+    and both C Bᵀ forms bit for bit."""
+    say("case: ssd strong decay")
+    heads, G, N = 2, 1, 128
+    params = {"A": np.array([-8.0, -30.0], dtype=np.float32), "dt_bias": np.array([18.0, 24.0], dtype=np.float32)}
+    y, yo, hl, ho, b = run_case((200,), heads, G, N, "f32", True, True, params=params)
+    assert np.isfinite(y).all() and np.isfinite(hl).all()
+    check(y, yo, hl, ho, b, "f32")
+    inp = I.make_ssd_inputs_np(9, 200, heads, G, N)
+    x, z, dt, B, C = (bf16_dev(inp[k]).view(1, 200, *inp[k].shape[1:]) for k in ("x", "z", "dt", "B", "C"))
+    A, D, bias = (torch.from_numpy(np.asarray(v, dtype=np.float32)).to(DEV)
+                  for v in (params["A"], inp["D"], params["dt_bias"]))
+    outs = [S.ssd_fwd(x, dt, B, C, A, D, bias, z=z, y_dtype=torch.float32, cb_mode=m)
+            for m in (S.CB_PREPASS, S.CB_IN_KERNEL)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
 def test_ssd_chained_equals_one_pass():
     """Two calls over 150 + 107 tokens, h_last of the first as h0 of the second, against one call."""
     say("case: ssd chained")
