@@ -49,6 +49,7 @@ CASES = [
     ((64,), 2, 1, 128, "bf16", True, False),              # exactly one chunk
     ((1, 1), 2, 2, 64, "f32", True, True),                # one token each (batched)
     ((333,), 6, 3, 128, "f32", False, True),
+    ((150, 77), 3, 1, 64, "f32", False, True),            # no gate at N = 64, packed
 ]
 
 
