@@ -11,8 +11,8 @@
 //     lane) and the per-token scalars are computed once per (token, channel) by one lane of the channel
 //     (softplus, Δx, published to LDS; gate and skip kept for the output);
 //   * every lane then runs the 8 state updates of its 4 states with Δ, Δx, B, C from LDS, and the
-//     channel's partial readouts are summed over its N / 4 lanes by a butterfly (DPP within a quad, LDS
-//     swizzles beyond, the lane-32 swap for 256 states);
+//     channel's partial readouts are summed over its N / 4 lanes by a butterfly (DPP within a 16-lane row,
+//     the lane-16 and lane-32 swaps across rows for 128 and 256 states: no LDS round trip per token);
 //   * the lane that computed a token's scalars forms and stores its output.
 // The next chunk's loads are issued before the current chunk's arithmetic.  No state crosses waves: no
 // workspace and no workgroup barrier (each wave has its own LDS region).
@@ -87,19 +87,20 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-// XOR-k exchange within 32 lanes (k < 32) through the LDS swizzle unit (bit mode: and 0x1f, xor k)
-template <int K>
-__device__ __forceinline__ float swz_xor(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (K << 10)));
-}
-// sum over the LPC consecutive lanes of a channel, in every one of them
+// sum over the LPC consecutive lanes of a channel, in every one of them.  Each step adds the partner
+// group's partial sum: after the quad steps a lane's 8-lane partner quad is its mirror in the half row,
+// its 16-lane partner half the mirror in the row; across rows the permlane swaps give every lane both
+// halves of a 32- or 64-lane group.
 template <int LPC>
 __device__ __forceinline__ float group_sum(float v) {
   v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
   v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  if constexpr (LPC >= 8) v += swz_xor<4>(v);
-  if constexpr (LPC >= 16) v += swz_xor<8>(v);
-  if constexpr (LPC >= 32) v += swz_xor<16>(v);
+  if constexpr (LPC >= 8) v += dpp<0x141>(v);   // row_half_mirror
+  if constexpr (LPC >= 16) v += dpp<0x140>(v);  // row_mirror
+  if constexpr (LPC >= 32) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   if constexpr (LPC >= 64) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
