@@ -72,26 +72,12 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-// XOR-k exchange within 32 lanes (k < 32) through the LDS swizzle unit (bit mode: and 0x1f, xor k)
-template <int K>
-__device__ __forceinline__ float swz_xor(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (K << 10)));
+// the value of lane l ^ 4 (within rows of 16 lanes), from two row rotations (a rotation right by r gives lane
+// l the value of lane l - r mod 16): no LDS round trip
+__device__ __forceinline__ float xor4(float v, bool bit4) {
+  const float from_below = dpp<0x124>(v), from_above = dpp<0x12C>(v);   // row_ror:4 (l - 4), row_ror:12 (l + 4)
+  return bit4 ? from_below : from_above;
 }
-// sum over the LPC consecutive lanes of a channel, in every one of them
-template <int LPC>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  if constexpr (LPC >= 8) v += swz_xor<4>(v);
-  if constexpr (LPC >= 16) v += swz_xor<8>(v);
-  if constexpr (LPC >= 32) v += swz_xor<16>(v);
-  if constexpr (LPC >= 64) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  }
-  return v;
-}
-
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -128,7 +114,8 @@ __device__ __forceinline__ float rs_step(float lo, float hi, bool upper) {
   } else {
     const float send = upper ? lo : hi, keep = upper ? hi : lo;
     float got;
-    if constexpr (M == 8 || M == 4) got = swz_xor<M>(send);
+    if constexpr (M == 8) got = dpp<0x128>(send);        // row_ror:8 (lane l - 8 mod 16 = l ^ 8)
+    else if constexpr (M == 4) got = xor4(send, upper);
     else if constexpr (M == 2) got = dpp<0x4E>(send);   // quad_perm [2,3,0,1]
     else got = dpp<0xB1>(send);                         // quad_perm [1,0,3,2]
     return keep + got;
