@@ -15,9 +15,9 @@
 // scalar work of a channel (softplus, skip, gate, conversions, load and store)
 // is spread over the quad: lane g of a quad owns tokens t with t % 4 == g of
 // each group of four, and shares Δ and Δx with its quad through LDS.  The four
-// lanes' partial readouts are summed with a transposed quad reduction (through
-// LDS in the sequential kernel, in registers with DPP in the time-split one) so
-// that each lane ends with the finished y of its own token.
+// lanes' partial readouts are summed with a transposed quad reduction in
+// registers (DPP quad permutes) so that each lane ends with the finished y of
+// its own token.
 //
 // Prefill parallelism: (sequence x 16-channel tile) workgroups; when that is
 // too few to fill 256 CUs, W waves of a workgroup split each time chunk of
@@ -116,25 +116,6 @@ __device__ __forceinline__ float quad_transpose_sum(float p0, float p1, float p2
   const bool odd = (g & 1) != 0;
   const float k = odd ? r1 : r0, s = odd ? r0 : r1;
   return k + qperm<kQXor1>(s);
-}
-
-// Same result through LDS (no DPP, no selects): lane g stores its partial of
-// token q at red[c][q][g], then reads the four partials of token g.  A
-// channel's row is 20 floats (16 used), so the four single-float writes of a
-// wave hit 32 distinct banks.
-constexpr int kRedRow = 20;
-__device__ __forceinline__ float quad_transpose_sum_lds(float* red, int c, int g, float p0, float p1, float p2,
-                                                        float p3) {
-  float* row = red + c * kRedRow;
-  row[0 * 4 + g] = p0;
-  row[1 * 4 + g] = p1;
-  row[2 * 4 + g] = p2;
-  row[3 * 4 + g] = p3;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const float4 v = reinterpret_cast<const float4*>(row)[g];
-  return (v.x + v.y) + (v.z + v.w);
 }
 
 __device__ __forceinline__ float quad_allsum(float v) {
@@ -392,7 +373,6 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
   constexpr int kWaves = W * TPW;
   __shared__ float4 s_bc[kWaves][2][K * kN / 4];                   // per-wave staged B, C (fp32)
   __shared__ float4 s_du[kWaves][K / 4][kCPW][2];                  // per-wave (Δ, Δx) of each group's 4 tokens
-  __shared__ float s_red[kWaves][kCPW * kRedRow];                  // per-wave readout partials of one group
   __shared__ float4 s_agg[(W > 1) ? W : 1][2][64];                // slice (P, H) pairs of the current chunk
   __shared__ float4 s_cin[(W > 1) ? W : 1][64];                    // each slice's carry-in, from the fold waves
 
@@ -506,7 +486,7 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
           pr[q] = fmaf(cv[q].w, h[3], fmaf(cv[q].z, h[2], fmaf(cv[q].y, h[1], cv[q].x * h[0])));
         }
         if constexpr (!kCkpt) {
-          const float yraw = quad_transpose_sum_lds(s_red[wave], L.c, L.g, pr[0], pr[1], pr[2], pr[3]);
+          const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
           store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
         }
       }
@@ -702,7 +682,6 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
 // ---------------------------------------------------------------------------
 constexpr int kCPW8 = 8;      // channels per wave (and per tile)
 constexpr int kK8 = 16;       // tokens per slice
-constexpr int kRedRow8 = 72;  // floats per channel row of the readout partials: 8 tokens x 8 lanes + 8
 constexpr int kDuRow8 = kK8 / 2 + 1;  // float4 per channel row of the (Δ, Δx) pairs: 8 used + 1 (bank spread)
 
 template <typename Tin>
@@ -735,7 +714,6 @@ __global__ __launch_bounds__(64 * W, 4) void scan_split8_kernel(FwdParams p) {  
   constexpr int K = kK8;
   __shared__ float4 s_bc[W][2][K * kN / 4];        // B, C rows [K][16] of each wave's slice (fp32)
   __shared__ float4 s_du[W][kCPW8][kDuRow8];       // (Δ, Δx) of each channel's K tokens, two tokens per float4
-  __shared__ float s_red[W][kCPW8 * kRedRow8];     // readout partials [channel][token][lane]
   __shared__ float2 s_agg[W][2][64];               // slice (P, H) pairs of the current chunk
   __shared__ float2 s_cin[W][64];                  // each slice's carry-in, from the fold waves
 
@@ -817,7 +795,6 @@ __global__ __launch_bounds__(64 * W, 4) void scan_split8_kernel(FwdParams p) {  
 
   const float2* sB2 = reinterpret_cast<const float2*>(s_bc[wave][0]);
   const float2* sC2 = reinterpret_cast<const float2*>(s_bc[wave][1]);
-  float* red = s_red[wave] + c * kRedRow8;
 
   auto chunk_step = [&](int ci, const RawSlice8<Tin>& cur, RawSlice8<Tin>& nxt) {
     const int i0 = my0 + ci * chunk;
@@ -917,14 +894,22 @@ __global__ __launch_bounds__(64 * W, 4) void scan_split8_kernel(FwdParams p) {  
         for (int i = 0; i < 2; ++i) h[i] = fmaf(ak[k][i], h[i], bk[k][i]);
         pr[q] = fmaf(cq[q].y, h[1], cq[q].x * h[0]);
       }
-      // transposed sum over the octet: lane g writes its partial of token q at [q][g] and reads the
-      // eight partials of token g (rows of 72 floats put the 64 single-float writes on distinct banks)
+      // transposed sum over the octet (a half row) by a reduce-scatter on DPP: lane g keeps the tokens
+      // whose index matches it in bit 2, then bit 1, then bit 0, adding its partner's share each time (the
+      // partner 7 - g across the half row, then g ^ 2, then g ^ 1); lane g ends with token g's sum
+      const bool b2 = (g & 4) != 0, b1 = (g & 2) != 0, b0 = (g & 1) != 0;
+      float s4[4], s2[2];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) red[q * 8 + g] = pr[q];
-      wave_lds_sync();
-      const float4 v0 = reinterpret_cast<const float4*>(red + g * 8)[0];
-      const float4 v1 = reinterpret_cast<const float4*>(red + g * 8)[1];
-      const float yraw = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w));
+      for (int k = 0; k < 4; ++k) {
+        const float keep = b2 ? pr[k + 4] : pr[k], send = b2 ? pr[k] : pr[k + 4];
+        s4[k] = keep + qperm<0x141>(send);   // row_half_mirror
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float keep = b1 ? s4[k + 2] : s4[k], send = b1 ? s4[k] : s4[k + 2];
+        s2[k] = keep + qperm<kQXor2>(send);
+      }
+      const float yraw = (b0 ? s2[1] : s2[0]) + qperm<kQXor1>(b0 ? s2[0] : s2[1]);
       if (g + 8 * jj < nv) {
         const float yv = (yraw + dsk * xv[jj]) * silu_f32(zv[jj]);
         if (dvalid) bstore(ry, out_off[jj], yv, static_cast<Tout*>(nullptr));
