@@ -78,6 +78,8 @@ typedef enum { SAMBA_F32 = 0, SAMBA_BF16 = 1 } samba_dtype;
  * Out-of-range or descending offsets are clamped into [0, seqlen] on the
  * device (memory-safe; results for such input are unspecified).
  *
+ * Sizes: 1 <= dim < 2^24 (SAMBA_ERR_BAD_SHAPE otherwise: the kernels address
+ * a lane's elements within a slice of token rows with 32-bit byte offsets).
  * Pointers: x, dt, z, B, C, y may be NULL only when there are no tokens.
  * Alignment: B, C, A, h0, h_last 16 bytes; x, dt, z, y, D, dt_bias their
  * element size.  h_last may equal h0 exactly (in-place carry); any other
@@ -157,7 +159,7 @@ typedef struct {
  * both sides the two routes give bitwise the same gradients).
  *
  * Shapes and dtypes: x, dt, z, B, C, cu_seqlens, A, D, dt_bias, h0 exactly as
- * for samba_scan_fwd (in_dtype).  dy [tokens][dim] and the outputs dx, ddt, dz
+ * for samba_scan_fwd (in_dtype; also 1 <= dim < 2^24).  dy [tokens][dim] and the outputs dx, ddt, dz
  * [tokens][dim] have in_dtype too.  dB, dC [tokens][16], dA [dim][16], dD,
  * ddt_bias [dim] are fp32 and are overwritten (not accumulated).  dh_last
  * (input) and dh0 (output) are fp32 [nseq][dim][16] and optional (NULL:
@@ -196,7 +198,7 @@ typedef struct {
 } samba_scan_bwd_args;
 
 /* Host-only: bytes of the h_ckpt array for these sizes (nseq = batch without cu_seqlens):
- * (batch * seqlen / 8 + nseq + 1) * dim * 16 * 4. */
+ * (batch * seqlen / 8 + nseq + 1) * dim * 16 * 4; dim must satisfy the prefill's bound. */
 samba_status samba_scan_ckpt_bytes(int32_t batch, int32_t seqlen, int32_t nseq, int32_t dim, size_t* bytes);
 
 /* Host-only: bytes of workspace samba_scan_bwd needs for these sizes and for whether h_ckpt is given

@@ -46,6 +46,10 @@ namespace {
 constexpr int kN = 16;         // states per channel
 constexpr int kSPL = 4;        // states per lane
 constexpr int kCPW = 16;       // channels per wave
+// Prefill and backward kernels address a lane's elements inside a slice (up to 16 token rows of x, dt, z, y,
+// and a channel's 16-state checkpoint row) with 32-bit byte offsets of at most 64 * dim; this bound keeps
+// them below 2^30.
+constexpr int32_t kMaxDim = 1 << 24;
 #ifndef SAMBA_STEP_QPT
 #define SAMBA_STEP_QPT 4
 #endif
@@ -1819,7 +1823,7 @@ samba_status validate_fwd(const samba_scan_fwd_args* a, FwdPlan* plan) {
   if (a->struct_size != sizeof(samba_scan_fwd_args)) return SAMBA_ERR_BAD_STRUCT;
   if (a->dstate != kN) return SAMBA_ERR_UNSUPPORTED;
   if (!dtype_ok(a->in_dtype) || !dtype_ok(a->y_dtype)) return SAMBA_ERR_BAD_DTYPE;
-  if (a->batch < 0 || a->seqlen < 0 || a->dim < 1) return SAMBA_ERR_BAD_SHAPE;
+  if (a->batch < 0 || a->seqlen < 0 || a->dim < 1 || a->dim >= kMaxDim) return SAMBA_ERR_BAD_SHAPE;
   const int ts = a->time_slices;
   if (!(ts == 0 || ts == 1 || ts == 2 || ts == 4 || ts == 8 || ts == 16)) return SAMBA_ERR_UNSUPPORTED;
   const int lanes = a->lanes_per_channel;
@@ -1937,7 +1941,7 @@ samba_status bwd_shape(const samba_scan_bwd_args* a, int64_t* nseq) {
   if (a->struct_size != sizeof(samba_scan_bwd_args)) return SAMBA_ERR_BAD_STRUCT;
   if (a->dstate != kN) return SAMBA_ERR_UNSUPPORTED;
   if (!dtype_ok(a->in_dtype)) return SAMBA_ERR_BAD_DTYPE;
-  if (a->batch < 0 || a->seqlen < 0 || a->dim < 1) return SAMBA_ERR_BAD_SHAPE;
+  if (a->batch < 0 || a->seqlen < 0 || a->dim < 1 || a->dim >= kMaxDim) return SAMBA_ERR_BAD_SHAPE;
   const int ts = a->time_slices;
   if (!(ts == 0 || ts == 1 || ts == 2 || ts == 4 || ts == 8)) return SAMBA_ERR_UNSUPPORTED;
   *nseq = a->batch;
@@ -2107,7 +2111,7 @@ samba_status samba_scan_bwd_workspace_size(const samba_scan_bwd_args* args, size
 
 samba_status samba_scan_ckpt_bytes(int32_t batch, int32_t seqlen, int32_t nseq, int32_t dim, size_t* bytes) {
   if (!bytes) return SAMBA_ERR_NULL_ARG;
-  if (batch < 0 || seqlen < 0 || nseq < 0 || dim < 1) return SAMBA_ERR_BAD_SHAPE;
+  if (batch < 0 || seqlen < 0 || nseq < 0 || dim < 1 || dim >= kMaxDim) return SAMBA_ERR_BAD_SHAPE;
   *bytes = ckpt_bytes(static_cast<int64_t>(batch) * seqlen, nseq, dim);
   return SAMBA_OK;
 }

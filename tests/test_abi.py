@@ -149,6 +149,7 @@ FWD_CASES = {
     "neg_batch": (lambda a: setattr(a, "batch", -1), 2),
     "neg_seqlen": (lambda a: setattr(a, "seqlen", -5), 2),
     "zero_dim": (lambda a: setattr(a, "dim", 0), 2),
+    "dim_2_pow_24": (lambda a: setattr(a, "dim", 1 << 24), 2),   # slice byte offsets must stay in 32 bits
     "time_slices": (lambda a: setattr(a, "time_slices", 3), 6),
     "time_slices_32": (lambda a: setattr(a, "time_slices", 32), 6),
     "null_x": (lambda a: setattr(a, "x", None), 1),
@@ -189,6 +190,11 @@ def test_fwd_in_place_carry_allowed(lib):
     a = fwd_ok()
     a.h_last = a.h0
     assert plan(lib, a)[0] == 0
+
+
+def test_fwd_largest_dim_accepted(lib):
+    """dim = 2^24 - 1 is the largest the prefill takes (one token: every buffer fits its 1 GiB slot)."""
+    assert plan(lib, fwd_ok(batch=1, seqlen=1, dim=(1 << 24) - 1))[0] == 0
 
 
 def test_fwd_no_tokens_allows_null_token_pointers(lib):
@@ -333,6 +339,7 @@ BWD_CASES = {
     "dstate": (lambda a: setattr(a, "dstate", 4), 6),
     "in_dtype": (lambda a: setattr(a, "in_dtype", 2), 3),
     "neg_seqlen": (lambda a: setattr(a, "seqlen", -1), 2),
+    "dim_2_pow_24": (lambda a: setattr(a, "dim", 1 << 24), 2),
     "time_slices_16": (lambda a: setattr(a, "time_slices", 16), 6),
     "time_slices_3": (lambda a: setattr(a, "time_slices", 3), 6),
     "null_dy": (lambda a: setattr(a, "dy", None), 1),
@@ -369,6 +376,7 @@ def test_ckpt_bytes(lib):
         assert lib.samba_scan_ckpt_bytes(batch, seqlen, nseq, dim, ctypes.byref(n)) == 0
         assert n.value == (batch * seqlen // 8 + nseq + 1) * dim * 64
     assert lib.samba_scan_ckpt_bytes(1, 8, 1, 0, ctypes.byref(n)) == 2
+    assert lib.samba_scan_ckpt_bytes(1, 8, 1, 1 << 24, ctypes.byref(n)) == 2
     assert lib.samba_scan_ckpt_bytes(1, 8, 1, 8, None) == 1
 
 
