@@ -53,7 +53,9 @@ SLOTS_PER_TD = VALU_PER_TD + TRANS_SLOTS * TRANS_PER_TD
 BWD_VALU_PER_TD = 16 * 15 + 20
 BWD_TRANS_PER_TD = 16 + 6
 BWD_SLOTS_PER_TD = BWD_VALU_PER_TD + TRANS_SLOTS * BWD_TRANS_PER_TD
-KERNEL_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_scan.hip"
+# the scan's kernels: samba_scan.hip, the prefill kernel's header and its separately scheduled copy
+KERNEL_SRCS = tuple(ROOT / "selective_state_space_05_amd" / "csrc" / n
+                    for n in ("samba_scan.hip", "samba_scan_fwd.h", "samba_scan_fwd_ilp.hip"))
 TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_fwd_step_bwd_proj.json"
 SWA_SRC = ROOT / "selective_state_space_05_amd" / "csrc" / "samba_swa.hip"
 SWA_TRAFFIC_FILE = ROOT / "profiles" / "hbm_traffic_swa.json"
@@ -110,7 +112,13 @@ def decode_bytes(batch: int, dim: int, n: int = 16) -> int:
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(KERNEL_SRC.read_bytes()).hexdigest()[:16]
+    """Source key of the scan's counter summaries: its sources and the per-source compiler flags."""
+    from selective_state_space_05_amd import build as _build
+    h = hashlib.sha256()
+    for src in KERNEL_SRCS:
+        h.update(src.read_bytes())
+    h.update(repr(sorted((k.name, v) for k, v in _build.SRC_FLAGS.items() if k in KERNEL_SRCS)).encode())
+    return h.hexdigest()[:16]
 
 
 def swa_hash() -> str:
