@@ -132,6 +132,40 @@ def test_time_slices_agree():
         assert norm_err(r["h"], outs[(1, 4)]["h"]) < 1e-5, key
 
 
+@pytest.mark.parametrize("ts", [1, 8, 16])
+@pytest.mark.parametrize("in_dtype,y_dtype", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16"), ("f32", "f32")])
+def test_scheduled_copies_agree(ts, in_dtype, y_dtype):
+    """At 1, 8 and 16 time slices a call without h_ckpt runs the prefill kernel's separately scheduled copy,
+    the same call with h_ckpt the library's other copy: y and h_last must be bitwise the same, and match
+    the oracle (several tiles, a ragged channel tile and a ragged last chunk)."""
+    batch, L, D, cfg = 2, 333, 72, 2
+    say("case: scheduled copies, W=%d %s -> %s" % (ts, in_dtype, y_dtype))
+    rows = batch * L
+    inp = I.make_fwd_inputs_np(cfg, rows, D, in_dtype=in_dtype)
+    h0 = I.make_h0(cfg, batch, D, scale=1.0)
+    shp = (batch, L, D)
+    x, dt, z = (dev_in(inp[k], in_dtype).reshape(shp) for k in ("x", "dt", "z"))
+    B, C = (dev_in(inp[k], in_dtype).reshape(batch, L, 16) for k in ("B", "C"))
+    A, Dv, bias = (torch.from_numpy(inp[k]).to(DEV) for k in ("A", "D", "dt_bias"))
+    h0_t = torch.from_numpy(h0).to(DEV)
+    ydt = torch.float32 if y_dtype == "f32" else torch.bfloat16
+    y1, hl1 = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=h0_t, y_dtype=ydt, time_slices=ts, lanes_per_channel=4)
+    ck = S.alloc_ckpt(x, None)
+    y2, hl2 = S.scan_fwd(x, dt, z, B, C, A, Dv, bias, h0=h0_t, y_dtype=ydt, time_slices=ts, lanes_per_channel=4,
+                         h_ckpt=ck)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(hl1, hl2)
+    yo, ho = O.scan_fwd(inp["x_f32"].reshape(shp), inp["dt_f32"].reshape(shp), inp["z_f32"].reshape(shp),
+                        inp["B_f32"].reshape(batch, L, 16), inp["C_f32"].reshape(batch, L, 16), inp["A"], inp["D"],
+                        inp["dt_bias"], h0=h0)
+    bounds = np.arange(batch + 1, dtype=np.int64) * L
+    if y_dtype == "f32":
+        check_fp32(host(y1).reshape(rows, D), yo.reshape(rows, D), "y", bounds)
+    else:
+        check_bf16_y(host(y1).reshape(rows, D), yo.reshape(rows, D), "y", bounds)
+    check_fp32(host(hl1).reshape(batch, -1), ho.reshape(batch, -1), "h_last")
+
+
 def test_delta_to_zero_carry_pin():
     """dt_raw = -40 makes Δ ~ 1e-18: h_last must equal h0 and y_t = (C_t.h0 + D x_t) silu(z_t).
     Away from the first token only a correct carry (across slices, chunks and waves) gives this."""
