@@ -1202,8 +1202,27 @@ def bench_decode_states(nstates: int = 24, rounds: int = 100):
     torch.cuda.synchronize()
     us = _timed(one_round, rounds, stream) * 1e3 / nstates
     gbs = decode_bytes(Bt, D) / (us * 1e-6) / 1e9
+
+    # reference at the same size: a device copy of each 16 MiB state into a second ring of 24 (16 MiB read
+    # from HBM and 16 MiB written per copy, as a step reads and writes its state), timed the same way
+    dst = [torch.empty_like(t) for t in states]
+
+    def copy_round():
+        for k in range(nstates):
+            dst[k].copy_(states[k])
+
+    for _ in range(3):
+        copy_round()
+    torch.cuda.synchronize()
+    copy_us = _timed(copy_round, rounds, stream) * 1e3 / nstates
+    copy_gbs = 2 * states[0].numel() * 4 / (copy_us * 1e-6) / 1e9
+    del dst
     return {"states": nstates, "state_mib_total": nstates * Bt * D * 16 * 4 / 2 ** 20, "us_per_step": us,
             "steps_per_s": 1e6 / us, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "same_size_copy": {"us": copy_us, "gbs": copy_gbs,
+                               "note": "device copy of one 16 MiB state into another buffer, rotating over "
+                                       "%d states like the steps" % nstates},
+            "frac_of_same_size_copy": gbs / copy_gbs,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "kernel": "scan_step_kernel<bf16,bf16>"}}
