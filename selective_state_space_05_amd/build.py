@@ -15,8 +15,8 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SRCS = (PKG / "csrc" / "samba_scan.hip", PKG / "csrc" / "samba_scan_fwd_ilp.hip", PKG / "csrc" / "samba_scan_groups.hip",
-        PKG / "csrc" / "samba_swa.hip", PKG / "csrc" / "samba_ssd.hip", PKG / "csrc" / "samba_gla.hip")
+SRCS = tuple(PKG / "csrc" / n for n in ("samba_scan.hip", "samba_scan_fwd_ilp.hip", "samba_scan_groups.hip",
+                                         "samba_swa.hip", "samba_ssd.hip", "samba_gla.hip"))
 # Flags for single sources: the inference copy of the prefill kernel is scheduled by LLVM's max-ILP machine
 # scheduler (same instructions, another order; measured faster for those launch plans only).
 SRC_FLAGS = {PKG / "csrc" / "samba_scan_fwd_ilp.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
@@ -57,11 +57,12 @@ def _compile(srcs, out: Path, extra=()) -> Path:
     """Each source to an object (with its SRC_FLAGS), compiled in parallel, then linked into `out`."""
     tmp = out.with_suffix(".so.tmp%d" % os.getpid())
     with tempfile.TemporaryDirectory(prefix="samba_build_") as objdir:
+        objs = [Path(objdir) / ("%d_%s.o" % (i, Path(src).stem)) for i, src in enumerate(srcs)]
         jobs = [[hipcc(), *COMPILE_FLAGS, *extra, *SRC_FLAGS.get(Path(src), ()), "-I", ROOT / "include", "-c",
-                 "-o", Path(objdir) / ("%d_%s.o" % (i, Path(src).stem)), src] for i, src in enumerate(srcs)]
+                 "-o", obj, src] for obj, src in zip(objs, srcs)]
         with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 8)) as pool:
             list(pool.map(_run, jobs))
-        _run([hipcc(), *LINK_FLAGS, "-o", tmp, *(job[job.index("-o") + 1] for job in jobs)])
+        _run([hipcc(), *LINK_FLAGS, "-o", tmp, *objs])
     os.replace(tmp, out)
     return out
 
@@ -89,7 +90,8 @@ def asan_runtime() -> Path:
 
 
 def build_sanitized(out: Path) -> Path:
-    """libsamba_scan.so with AddressSanitizer and UndefinedBehaviorSanitizer on its host code, at `out`."""
+    """libsamba_scan.so with AddressSanitizer and UndefinedBehaviorSanitizer on its host code, at `out` (one
+    hipcc command; without SRC_FLAGS, which only order the device instructions)."""
     flags = [f for f in HIPCC_FLAGS if f != "-O3"] + SANITIZER_FLAGS
     tmp = Path(out).with_suffix(".so.tmp%d" % os.getpid())
     cmd = [hipcc(), *flags, "-I", str(ROOT / "include"), "-o", str(tmp), *(str(p) for p in SRCS)]
