@@ -46,6 +46,9 @@ constexpr int kSPL = 4;        // states per lane
 constexpr int kCPW = 16;       // channels per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
+// Byte offset that every slice-sized y resource ends before (a slice is at most 16 rows of dim < 2^24 fp32
+// values, < 2^30 bytes): a lane past the last channel stores there, and the hardware drops the store.
+constexpr uint32_t kDropOffset = 0x40000000u;
 
 // ---------------------------------------------------------------------------
 // element access and conversion
@@ -226,7 +229,7 @@ struct LaneCtx {
   float dsk, bias;
   float hinit[kSPL];
   uint32_t in_off[K / 4];   // byte offsets of this lane's x/dt/z elements from a slice's first row
-  uint32_t out_off[K / 4];  // same for y
+  uint32_t out_off[K / 4];  // same for y (kDropOffset for a lane past the last channel: its stores are dropped)
   uint32_t bc_off;          // byte offset of this lane's B/C values from a slice's first row
   int bc_lds;               // float index of those values in an LDS [K][16] tile
 };
@@ -325,13 +328,15 @@ __device__ __forceinline__ int slice_len(int64_t rem) {
   return rem <= 0 ? 0 : (rem < K ? static_cast<int>(rem) : K);
 }
 
-// y of token 4j+g: skip, gate, round, store (tokens past the sequence end are
-// outside the resource and dropped by the hardware).
+// y of token 4j+g: skip, gate, round, store.  No branch: tokens past the sequence end are outside ry (which
+// covers the slice's valid rows only) and lanes past the last channel store at kDropOffset; the hardware
+// drops both.  With no branch around the stores the count of memory operations in flight is fixed, so the
+// next slice's wait for its own loads need not wait for these stores as well.
 template <typename Tin, typename Tout, int K>
 __device__ __forceinline__ void store_y(const LaneCtx<Tin, Tout, K>& L, rsrc_t ry, int j, float yraw, float xr,
                                         float zr) {
   const float yv = (yraw + L.dsk * xr) * silu_f32(zr);
-  if (L.dvalid) bstore(ry, L.out_off[j], yv, static_cast<Tout*>(nullptr));
+  bstore(ry, L.out_off[j], yv, static_cast<Tout*>(nullptr));
 }
 
 // Checkpoint slot of the state before token 8*j of the sequence that starts
@@ -344,8 +349,9 @@ __device__ __forceinline__ int64_t ckpt_slot(int64_t start, int s, int j) { retu
 // scan); TPW = channel tiles per workgroup (W == 1 only); K = tokens per wave
 // slice (8 or 16).  kCkpt: instead of y, write the state before every 8th
 // token of each sequence to p.ckpt (the backward's recomputation points).
+// kNoCkpt: the launch never passes p.ckpt (inference), so its checks compile out.
 // ---------------------------------------------------------------------------
-template <typename Tin, typename Tout, int W, int TPW, int K, bool kCkpt = false>
+template <typename Tin, typename Tout, int W, int TPW, int K, bool kCkpt = false, bool kNoCkpt = false>
 __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) {   // (4 waves per SIMD: <= 128 VGPRs)
   static_assert(W == 1 || TPW == 1, "time slices and tile packing are exclusive");
   static_assert(K == 8 || K == 16, "slice length");
@@ -375,7 +381,8 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
 #pragma unroll
     for (int j = 0; j < K / 4; ++j) {
       L.in_off[j] = (e0 + static_cast<uint32_t>(j) * 4u * dim) * static_cast<uint32_t>(sizeof(Tin));
-      L.out_off[j] = (e0 + static_cast<uint32_t>(j) * 4u * dim) * static_cast<uint32_t>(sizeof(Tout));
+      L.out_off[j] = L.dvalid ? (e0 + static_cast<uint32_t>(j) * 4u * dim) * static_cast<uint32_t>(sizeof(Tout))
+                              : kDropOffset;
     }
     constexpr int E = K / 4, lanes_per_row = kN / E;
     L.bc_lds = (L.lane / lanes_per_row) * kN + (L.lane % lanes_per_row) * E;
@@ -436,16 +443,17 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
       float xv[K / 4], zv[K / 4], dl[K / 4], uu[K / 4];
       decode_raw<Tin, Tout, K>(cur, L, nv, xv, zv, dl, uu);
       publish_du<K>(s_du[wave], L.c, L.g, dl, uu);
-      // (the checkpoint variant writes no y: an empty resource)
-      const rsrc_t ry = make_rsrc_rows(kCkpt ? yout : yout + t0 * p.dim, kCkpt ? 0 : ntok - i0,
+      // y of this slice only (the checkpoint variant writes none: an empty resource); nv rows are at most
+      // 16 * dim * 4 bytes < 2^30 (dim < 2^24), so a lane past the last channel stores beyond the resource
+      const rsrc_t ry = make_rsrc_rows(kCkpt ? yout : yout + t0 * p.dim, kCkpt ? 0 : __builtin_amdgcn_readfirstlane(nv),
                                        static_cast<uint32_t>(p.dim));
-      if (kCkpt || p.ckpt) put_ckpt(i0, h);
+      if (kCkpt || (!kNoCkpt && p.ckpt)) put_ckpt(i0, h);
       wave_lds_sync();
 #pragma unroll
       for (int j = 0; j < K / 4; ++j) {
-        if (4 * j >= nv) break;
+        // (groups past the sequence end run on with Δ = 0, which leaves the state exactly as it is)
         if constexpr (K == 16) {
-          if ((kCkpt || p.ckpt) && j == 2) put_ckpt(i0 + 8, h);
+          if ((kCkpt || (!kNoCkpt && p.ckpt)) && j == 2 && nv > 8) put_ckpt(i0 + 8, h);
         }
         float4 bv[4], cv[4];
         float dk[4], uk[4];
@@ -465,6 +473,7 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
           pr[q] = fmaf(cv[q].w, h[3], fmaf(cv[q].z, h[2], fmaf(cv[q].y, h[1], cv[q].x * h[0])));
         }
         if constexpr (!kCkpt) {
+          // stored without a branch, as in the time-split path below
           const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
           store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
         }
@@ -595,9 +604,13 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
         const float4 cr = s_cin[wave][L.lane];
         hin[0] = cr.x; hin[1] = cr.y; hin[2] = cr.z; hin[3] = cr.w;
       }
-      const rsrc_t ry = make_rsrc_rows(kCkpt ? yout : yout + t0 * p.dim, kCkpt ? 0 : ntok - i0,
+      // The inference copy (kNoCkpt) stores y without a branch (store_y): its resource covers this slice's
+      // valid rows only (nv is wave-uniform).  The other copy keeps the branches, with which it compiles
+      // without spills.
+      const rsrc_t ry = make_rsrc_rows(kCkpt ? yout : yout + t0 * p.dim,
+                                       kCkpt ? 0 : (kNoCkpt ? __builtin_amdgcn_readfirstlane(nv) : ntok - i0),
                                        static_cast<uint32_t>(p.dim));
-      if (kCkpt || p.ckpt) {
+      if (kCkpt || (!kNoCkpt && p.ckpt)) {
         if (nv > 0) put_ckpt(i0, hin);
       }
 #pragma unroll
@@ -605,7 +618,7 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
 #pragma unroll
       for (int j = 0; j < K / 4; ++j) {
         if constexpr (K == 16) {
-          if ((kCkpt || p.ckpt) && j == 2 && nv > 8) put_ckpt(i0 + 8, h);
+          if ((kCkpt || (!kNoCkpt && p.ckpt)) && j == 2 && nv > 8) put_ckpt(i0 + 8, h);
         }
         float pr[4];
         float4 cq[4];
@@ -619,11 +632,14 @@ __global__ __launch_bounds__(64 * W * TPW, 4) void scan_fwd_kernel(FwdParams p) 
           for (int i = 0; i < kSPL; ++i) h[i] = fmaf(ak[k][i], h[i], bk[k][i]);
           pr[q] = fmaf(cv.w, h[3], fmaf(cv.z, h[2], fmaf(cv.y, h[1], cv.x * h[0])));
         }
-        if constexpr (!kCkpt) {
+        if constexpr (kNoCkpt) {
+          const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
+          store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
+        } else if constexpr (!kCkpt) {
           if (4 * j < nv) {
-            // (in registers: measured faster here than the LDS transposed sum the sequential path uses)
             const float yraw = quad_transpose_sum(pr[0], pr[1], pr[2], pr[3], L.g);
-            store_y<Tin, Tout, K>(L, ry, j, yraw, xv[j], zv[j]);
+            const float yv = (yraw + L.dsk * xv[j]) * silu_f32(zv[j]);
+            if (L.dvalid) bstore(ry, L.out_off[j], yv, static_cast<Tout*>(nullptr));
           }
         }
       }

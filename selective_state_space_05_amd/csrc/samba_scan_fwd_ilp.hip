@@ -4,7 +4,8 @@
 //
 // The build compiles this file alone with LLVM's max-ILP machine scheduler (-amdgpu-sched-strategy=max-ilp).
 // The scheduler only orders instructions; every arithmetic operation is the same, so y and h_last are
-// bitwise those of samba_scan.hip's copy.  Measured on MI355X in alternating rounds: the 16384-token launch
+// bitwise those of samba_scan.hip's copy (this copy is also built without the checkpoint branches, which an
+// inference launch never takes).  Measured on MI355X in alternating rounds: the 16384-token launch
 // at D 4096 (16 slices) 2.6-4 % faster, 8 slices 1 %, the sequential kernel 1-5 %; with checkpoint writes,
 // at 4 slices, and for the backward, grouped, SSD and 8-lane kernels the default scheduler measured faster,
 // so those stay in samba_scan.hip.
@@ -17,9 +18,9 @@ namespace {
 template <typename Tin, typename Tout>
 hipError_t launch_typed(int W, dim3 grid, dim3 block, const FwdParams& p, hipStream_t st) {
   switch (W) {
-    case 1: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 1, 4, 16>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 8, 1, 8>), grid, block, 0, st, p); break;
-    case 16: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 16, 1, 8>), grid, block, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 1, 4, 16, false, true>), grid, block, 0, st, p); break;
+    case 8: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 8, 1, 8, false, true>), grid, block, 0, st, p); break;
+    case 16: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 16, 1, 8, false, true>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
