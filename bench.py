@@ -1299,10 +1299,13 @@ def pmc_summary(fetch_dir: str, write_dir: str, out: str):
         assert len(keys) == 1, (parts, keys)
         return keys[0]
 
-    sel = {"fwd": ("scan_fwd_kernel", "16, 1, 8, false>"), "step": ("scan_step_kernel<unsigned short, unsigned short",),
+    # (the inference launches run the copy instantiated with kNoCkpt: names end in "false, true>"; the
+    # checkpoint pass is the kCkpt variant: "true, false>")
+    sel = {"fwd": ("scan_fwd_kernel", "16, 1, 8, false, true>"),
+           "step": ("scan_step_kernel<unsigned short, unsigned short",),
            "cfg1": ("scan_split8_kernel<unsigned short, unsigned short, 16>",),
-           "cfg2": ("scan_fwd_kernel", "unsigned short, 1, 4, 16, false>"),
-           "ckpt": ("scan_fwd_kernel", ", true>"), "bwd": ("scan_bwd_kernel<",), "finish": ("scan_bwd_finish_kernel",),
+           "cfg2": ("scan_fwd_kernel", "unsigned short, 1, 4, 16, false, true>"),
+           "ckpt": ("scan_fwd_kernel", ", true, false>"), "bwd": ("scan_bwd_kernel<",), "finish": ("scan_bwd_finish_kernel",),
            "proj": ("proj_dma_kernel<unsigned short",)}
     got = {k: {} for k in sel}
     scales = {}
@@ -1373,7 +1376,7 @@ def valu_summary(dir_a: str, dir_b: str, out: str):
         per = {}
         for r in csv.DictReader(open(f)):
             k = r["Kernel_Name"]
-            if "scan_fwd_kernel" in k and "16, 1, 8, false>" in k:
+            if "scan_fwd_kernel" in k and "16, 1, 8, false, true>" in k:
                 per.setdefault((r["Dispatch_Id"], r["Counter_Name"]), 0.0)
                 per[(r["Dispatch_Id"], r["Counter_Name"])] += float(r["Counter_Value"])
                 kernel = k
