@@ -421,6 +421,45 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
   float dAacc[kSPL] = {0.f, 0.f, 0.f, 0.f};
   float dDacc = 0.f, dbacc = 0.f;
 
+  // ---- loads of one slice: this lane's tokens of x, dt, z, dy; the slice's B, C; the checkpoint.  They are
+  // issued one chunk ahead (the loop's iteration `it` loads iteration it + 1's slice), so that their latency
+  // hides behind a whole chunk of work.  Past the first chunk of the sequence (it >= nchunks) every resource
+  // is empty and based at the tensor's start: the loads read 0 and touch no memory.
+  struct BwdRaw {
+    T xr[K / 4], dtr[K / 4], zr[K / 4], dyr[K / 4];
+    uint32_t bw[RawSlice<T, K>::kWords], cw[RawSlice<T, K>::kWords];
+    uint32_t hk[kSPL];
+  };
+  auto load_slice = [&](int it_l, BwdRaw& r) {
+    const bool live = it_l < nchunks;
+    const int i0l = (nchunks - 1 - it_l) * chunk + wave * K;
+    const int reml = live ? ntok - i0l : 0;
+    const int64_t t0l = live ? start + i0l : 0;
+    const int64_t row0l = t0l * p.dim;
+    const rsrc_t rx = make_rsrc_rows(static_cast<const T*>(p.x) + row0l, reml, dim);
+    const rsrc_t rd = make_rsrc_rows(static_cast<const T*>(p.dt) + row0l, reml, dim);
+    const rsrc_t rz = make_rsrc_rows(static_cast<const T*>(p.z) + row0l, reml, dim);
+    const rsrc_t ry = make_rsrc_rows(static_cast<const T*>(p.dy) + row0l, reml, dim);
+#pragma unroll
+    for (int j = 0; j < K / 4; ++j) {
+      bload(rx, in_off[j], r.xr[j]);
+      bload(rd, in_off[j], r.dtr[j]);
+      bload(rz, in_off[j], r.zr[j]);
+      bload(ry, in_off[j], r.dyr[j]);
+    }
+    const rsrc_t rb = make_rsrc_rows(static_cast<const T*>(p.B) + t0l * kN, reml, kN);
+    const rsrc_t rc = make_rsrc_rows(static_cast<const T*>(p.C) + t0l * kN, reml, kN);
+    bload_words(rb, bc_off, r.bw);
+    bload_words(rc, bc_off, r.cw);
+    // checkpoint row of this slice (an empty resource past the sequence end: reads give 0)
+    const rsrc_t rk = make_rsrc_rows(live ? p.ckpt + ckpt_slot(start, s, i0l >> 3) * p.dim * kN : p.ckpt,
+                                     reml > 0 ? 1 : 0, dim * kN);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ck_off, 0, 0);
+    r.hk[0] = v[0]; r.hk[1] = v[1]; r.hk[2] = v[2]; r.hk[3] = v[3];
+  };
+  BwdRaw nxt;
+  load_slice(0, nxt);
+
   for (int it = 0; it < nchunks; ++it) {
     const int ci = nchunks - 1 - it;
     const int buf = it & 1;
@@ -430,34 +469,16 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
     const int64_t t0 = start + i0;
     const int64_t row0 = t0 * p.dim;
 
-    // ---- loads: this lane's tokens of x, dt, z, dy; the slice's B, C; the checkpoint
-    T xr[K / 4], dtr[K / 4], zr[K / 4], dyr[K / 4];
-    uint32_t bw[RawSlice<T, K>::kWords], cw[RawSlice<T, K>::kWords];
-    {
-      const rsrc_t rx = make_rsrc_rows(static_cast<const T*>(p.x) + row0, rem, dim);
-      const rsrc_t rd = make_rsrc_rows(static_cast<const T*>(p.dt) + row0, rem, dim);
-      const rsrc_t rz = make_rsrc_rows(static_cast<const T*>(p.z) + row0, rem, dim);
-      const rsrc_t ry = make_rsrc_rows(static_cast<const T*>(p.dy) + row0, rem, dim);
-#pragma unroll
-      for (int j = 0; j < K / 4; ++j) {
-        bload(rx, in_off[j], xr[j]);
-        bload(rd, in_off[j], dtr[j]);
-        bload(rz, in_off[j], zr[j]);
-        bload(ry, in_off[j], dyr[j]);
-      }
-      const rsrc_t rb = make_rsrc_rows(static_cast<const T*>(p.B) + t0 * kN, rem, kN);
-      const rsrc_t rc = make_rsrc_rows(static_cast<const T*>(p.C) + t0 * kN, rem, kN);
-      bload_words(rb, bc_off, bw);
-      bload_words(rc, bc_off, cw);
-    }
-    float hs[kSPL];
-    {
-      // checkpoint row of this slice (an empty resource past the sequence end: reads give 0)
-      const rsrc_t rk = make_rsrc_rows(p.ckpt + ckpt_slot(start, s, i0 >> 3) * p.dim * kN, nv > 0 ? 1 : 0, dim * kN);
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ck_off, 0, 0);
-      hs[0] = __uint_as_float(v[0]); hs[1] = __uint_as_float(v[1]);
-      hs[2] = __uint_as_float(v[2]); hs[3] = __uint_as_float(v[3]);
-    }
+    const BwdRaw cur = nxt;
+    load_slice(it + 1, nxt);
+    const T(&xr)[K / 4] = cur.xr;
+    const T(&dtr)[K / 4] = cur.dtr;
+    const T(&zr)[K / 4] = cur.zr;
+    const T(&dyr)[K / 4] = cur.dyr;
+    const uint32_t(&bw)[RawSlice<T, K>::kWords] = cur.bw;
+    const uint32_t(&cw)[RawSlice<T, K>::kWords] = cur.cw;
+    float hs[kSPL] = {__uint_as_float(cur.hk[0]), __uint_as_float(cur.hk[1]), __uint_as_float(cur.hk[2]),
+                      __uint_as_float(cur.hk[3])};
     {
       float v[K / 4];
       widen_words<T, K>(bw, v);
