@@ -359,7 +359,7 @@ struct BwdParams {
 };
 
 template <typename T, int W>
-__global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * W, 3) void scan_bwd_kernel(BwdParams p) {   // (3 waves per SIMD: <= 168 VGPRs)
   constexpr int K = kBK;
   // LDS, per wave (7.1 KiB) plus 2 KiB per workgroup: 30.5 KiB for 4 waves.
   __shared__ float4 s_bc[W][2][K * kN / 4];   // B, C rows of the slice (fp32)
@@ -457,10 +457,9 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, ck_off, 0, 0);
     r.hk[0] = v[0]; r.hk[1] = v[1]; r.hk[2] = v[2]; r.hk[3] = v[3];
   };
-  BwdRaw nxt;
-  load_slice(0, nxt);
-
-  for (int it = 0; it < nchunks; ++it) {
+  // one chunk of the sweep; `cur` holds its loaded slice, and it loads the next chunk's slice into `nxt` (the
+  // loop runs the body twice per step with the two register sets swapped, so no copy waits for the loads)
+  auto chunk_body = [&](int it, const BwdRaw& cur, BwdRaw& nxt) {
     const int ci = nchunks - 1 - it;
     const int buf = it & 1;
     const int i0 = ci * chunk + wave * K;
@@ -469,7 +468,6 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
     const int64_t t0 = start + i0;
     const int64_t row0 = t0 * p.dim;
 
-    const BwdRaw cur = nxt;
     load_slice(it + 1, nxt);
     const T(&xr)[K / 4] = cur.xr;
     const T(&dtr)[K / 4] = cur.dtr;
@@ -676,6 +674,12 @@ __global__ __launch_bounds__(64 * W) void scan_bwd_kernel(BwdParams p) {
     }
     if (wave == 0) s_carry[buf][lane] = make_float4(gh[0], gh[1], gh[2], gh[3]);
     wave_lds_sync();
+    };
+  BwdRaw ra, rb;
+  load_slice(0, ra);
+  for (int it = 0; it < nchunks; it += 2) {
+    chunk_body(it, ra, rb);
+    if (it + 1 < nchunks) chunk_body(it + 1, rb, ra);
   }
 
   // ---- end of the sequence: dh0 (wave 0 holds the adjoint leaving the first token), parameter partials
