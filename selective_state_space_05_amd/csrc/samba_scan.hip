@@ -1289,7 +1289,7 @@ hipError_t launch_fwd(const FwdPlan& pl, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  if (pl.prm.ckpt == nullptr && (pl.W == 1 || pl.W == 8 || pl.W == 16))   // the copy in samba_scan_fwd_ilp.hip
+  if (pl.prm.ckpt == nullptr && (pl.W == 1 || pl.W == 4 || pl.W == 8 || pl.W == 16))   // the copy in samba_scan_fwd_ilp.hip
     return samba_fwd::launch_fwd_ilp(sizeof(Tin) == 2, sizeof(Tout) == 2, pl.W, grid, block, pl.prm, st);
   switch (pl.W) {
     case 1: hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, 1, 4, 16>), grid, block, 0, st, pl.prm); break;

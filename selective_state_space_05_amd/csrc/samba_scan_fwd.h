@@ -31,7 +31,7 @@ struct FwdParams {
   int32_t nblocks;       // nseq * ngroups
 };
 
-// Launches scan_fwd_kernel<Tin, Tout, W, TPW, K> (no checkpoint variant) for W = 1 (TPW 4, K 16), 8 or 16
+// Launches scan_fwd_kernel<Tin, Tout, W, TPW, K> (no checkpoint variant) for W = 1 (TPW 4, K 16), 4, 8 or 16
 // (TPW 1, K 8) from the copy compiled in samba_scan_fwd_ilp.hip; in_bf16 / out_bf16 select Tin / Tout
 // (bf16 or fp32).  Returns hipErrorInvalidValue for any other W, else the launch status.
 __attribute__((visibility("hidden"))) hipError_t launch_fwd_ilp(bool in_bf16, bool out_bf16, int W, dim3 grid,

@@ -132,10 +132,10 @@ def test_time_slices_agree():
         assert norm_err(r["h"], outs[(1, 4)]["h"]) < 1e-5, key
 
 
-@pytest.mark.parametrize("ts", [1, 8, 16])
+@pytest.mark.parametrize("ts", [1, 4, 8, 16])
 @pytest.mark.parametrize("in_dtype,y_dtype", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "bf16"), ("f32", "f32")])
 def test_scheduled_copies_agree(ts, in_dtype, y_dtype):
-    """At 1, 8 and 16 time slices a call without h_ckpt runs the prefill kernel's separately scheduled copy,
+    """At 1, 4, 8 and 16 time slices a call without h_ckpt runs the prefill kernel's separately scheduled copy,
     the same call with h_ckpt the library's other copy: y and h_last must be bitwise the same, and match
     the oracle (several tiles, a ragged channel tile and a ragged last chunk)."""
     batch, L, D, cfg = 2, 333, 72, 2
